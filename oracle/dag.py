@@ -1,0 +1,204 @@
+"""Plain-Python DAG model of the deterministic backward (the oracle's copy).
+
+TEST INFRASTRUCTURE ONLY: imported by tests, never by the product path.  The
+product's C++ critical-path calculator is checked against this module.
+
+The model is the one the explainer sets up ("Technisches Resuemee" 2.1) and
+the authors' abstract names: the backward pass of deterministic attention
+is a directed acyclic graph whose nodes are compute phases (one KV tile
+meeting one Q block) and reduction phases (adding that item's dQ partial into
+the Q block's accumulator); edges are data dependencies plus the mandatory
+accumulation order; the quantity to minimise is the length of the critical
+path; and the work of one KV tile runs as one uninterrupted chain on one
+processor.  Concretely, for a launch with P processor slots:
+
+* item (kv, q) of a unit gives two nodes, C (weight c_diag on a causal
+  diagonal item, else c_full) and R (weight r), with edge C -> R;
+* consecutive items of a unit are chained R -> C, and consecutive units on
+  one slot are chained last R -> first C;
+* for a deterministic schedule, R of the contributor ranked k-1 for Q block
+  q precedes R of the contributor ranked k, with latency h (the hand-off);
+* start(x) = max over in-edges (finish(pred) + latency), finish = start +
+  weight; the makespan is the largest finish (the critical-path length).
+
+Slots take units in one of two ways (this project's reading of how a
+persistent grid runs the explainer's "one KV tile per SM" chains):
+* "dynamic": units in head-major order go to whichever slot frees first
+  (ties to the lowest slot) - used when every order edge points to an
+  earlier unit (NAIVE, DESCENDING, ATOMIC);
+* "static": head-aligned rounds, slot = u mod P' with P' the largest
+  multiple of the units per head not above P - used for SHIFT, whose order
+  edges point to later units of the same head.
+
+Lemma 1 of the explainer (2.2 B): adding a zero-weight edge u -> v keeps the
+critical path when depth(u) <= depth(v).  Read with depth(u) = earliest
+finish of u and depth(v) = earliest start of v, this is checked by
+``lemma1_preserves``.
+"""
+from __future__ import annotations
+
+from . import schedules as S
+
+
+def item_cost(kv, q, causal, cost):
+    c_full, c_diag = cost[0], cost[1]
+    return c_diag if (causal and kv == q) else c_full
+
+
+def longest_path(weights, edges):
+    """weights: list of node weights; edges: list of (u, v, latency).
+
+    Returns (start, finish) lists, or raises ValueError on a cycle.
+    Plain Kahn topological order, then one relaxation pass.
+    """
+    n = len(weights)
+    succ = [[] for _ in range(n)]
+    indeg = [0] * n
+    for u, v, lat in edges:
+        succ[u].append((v, lat))
+        indeg[v] += 1
+    order = [i for i in range(n) if indeg[i] == 0]
+    head = 0
+    while head < len(order):
+        u = order[head]
+        head += 1
+        for v, _ in succ[u]:
+            indeg[v] -= 1
+            if indeg[v] == 0:
+                order.append(v)
+    if len(order) != n:
+        raise ValueError("cycle in dependency graph")
+    start = [0.0] * n
+    finish = [0.0] * n
+    for u in order:
+        finish[u] = start[u] + weights[u]
+        for v, lat in succ[u]:
+            if finish[u] + lat > start[v]:
+                start[v] = finish[u] + lat
+    return start, finish
+
+
+def _policy(schedule):
+    return "static" if schedule == S.SHIFT else "dynamic"
+
+
+def realize(schedule, n, causal, heads, slots, cost):
+    """Assign units to slots and build the graph.
+
+    Returns dict with 'weights', 'edges', 'assign' (unit -> slot),
+    'units' (global unit list of item lists, each item (head, kv, q)) and
+    for the dynamic policy the times of the event simulation used to decide
+    the assignment ('sim_finish').
+    """
+    per_head = S.units(schedule, n, causal)
+    U = len(per_head)
+    ranks = S.rank_table(schedule, n, causal)
+    glob = []
+    for hd in range(heads):
+        for items in per_head:
+            glob.append([(hd, kv, q) for kv, q in items])
+    # node ids: for unit u item k -> C = 2*idx, R = 2*idx + 1
+    idx_of = {}
+    weights = []
+    for u, items in enumerate(glob):
+        for k, (hd, kv, q) in enumerate(items):
+            idx_of[(u, k)] = len(weights) // 2
+            weights.append(item_cost(kv, q, causal, cost))
+            weights.append(cost[2])
+    r_node = {}
+    for u, items in enumerate(glob):
+        for k, (hd, kv, q) in enumerate(items):
+            r_node[(hd, kv, q)] = 2 * idx_of[(u, k)] + 1
+    order_edges = []
+    if ranks is not None:
+        for hd in range(heads):
+            for q in range(n):
+                chain = sorted((ranks[q][kv], kv) for kv in range(n) if ranks[q][kv] is not None)
+                for (r0, kv0), (r1, kv1) in zip(chain, chain[1:]):
+                    order_edges.append((r_node[(hd, kv0, q)], r_node[(hd, kv1, q)], cost[3]))
+
+    policy = _policy(schedule)
+    assign = [None] * len(glob)
+    sim_finish = None
+    if policy == "static":
+        if U > slots:
+            raise ValueError("static policy needs a whole head of units resident")
+        p_eff = (slots // U) * U
+        for u in range(len(glob)):
+            assign[u] = u % p_eff
+    else:
+        # Event simulation: every order edge points to an earlier unit, so
+        # units can be timed in grab order.
+        free = [0.0] * slots
+        r_fin = {}
+        for u, items in enumerate(glob):
+            s = min(range(slots), key=lambda i: (free[i], i))
+            assign[u] = s
+            t = free[s]
+            for k, (hd, kv, q) in enumerate(items):
+                c = item_cost(kv, q, causal, cost)
+                t_c = t + c
+                t_r = t_c
+                if ranks is not None and ranks[q][kv] > 0:
+                    prev = [kv2 for kv2 in range(n) if ranks[q][kv2] == ranks[q][kv] - 1][0]
+                    t_r = max(t_r, r_fin[(hd, prev, q)] + cost[3])
+                t = t_r + cost[2]
+                r_fin[(hd, kv, q)] = t
+            free[s] = t
+        sim_finish = max(free) if glob else 0.0
+
+    edges = list(order_edges)
+    last_on_slot = {}
+    for u, items in enumerate(glob):
+        for k in range(len(items)):
+            c_id = 2 * idx_of[(u, k)]
+            edges.append((c_id, c_id + 1, 0.0))
+            if k > 0:
+                edges.append((2 * idx_of[(u, k - 1)] + 1, c_id, 0.0))
+        s = assign[u]
+        if s in last_on_slot and items:
+            edges.append((last_on_slot[s], 2 * idx_of[(u, 0)], 0.0))
+        if items:
+            last_on_slot[s] = 2 * idx_of[(u, len(items) - 1)] + 1
+    return {"weights": weights, "edges": edges, "assign": assign, "units": glob,
+            "sim_finish": sim_finish, "policy": policy, "n_order": len(order_edges)}
+
+
+def predict(schedule, n, causal, heads, slots, cost):
+    """Returns (makespan, total_wait, max_slot_idle, lower_bound).
+
+    total_wait: summed time R nodes spend held by their order edge beyond
+    what their own chain allows; max_slot_idle: largest (makespan - busy)
+    over slots; lower_bound: max(total work / slots, longest single unit)."""
+    g = realize(schedule, n, causal, heads, slots, cost)
+    start, finish = longest_path(g["weights"], g["edges"])
+    makespan = max(finish) if finish else 0.0
+    # time each R node could start from its own chain alone (order edges
+    # excluded); the excess of its actual start is time spent waiting
+    chain_ready = [0.0] * len(g["weights"])
+    for i, (u, v, lat) in enumerate(g["edges"]):
+        if i >= g["n_order"]:
+            chain_ready[v] = max(chain_ready[v], finish[u] + lat)
+    total_wait = 0.0
+    for i in range(1, len(g["weights"]), 2):
+        total_wait += start[i] - chain_ready[i]
+    busy = [0.0] * slots
+    for u, items in enumerate(g["units"]):
+        for hd, kv, q in items:
+            busy[g["assign"][u]] += item_cost(kv, q, causal, cost) + cost[2]
+    max_idle = max(makespan - b for b in busy) if slots else 0.0
+    longest_unit = max((sum(item_cost(kv, q, causal, cost) + cost[2] for _, kv, q in items)
+                        for items in g["units"]), default=0.0)
+    lower = max(sum(busy) / slots, longest_unit)
+    return makespan, total_wait, max_idle, lower
+
+
+def lemma1_preserves(weights, edges, u, v):
+    """Adds a zero-weight, zero-latency edge u -> v and reports
+    (condition, preserved): condition is finish(u) <= start(v) in the
+    original graph; preserved is whether the makespan is unchanged."""
+    start, finish = longest_path(weights, edges)
+    before = max(finish)
+    start2, finish2 = longest_path(weights, edges + [(u, v, 0.0)])
+    after = max(finish2)
+    return finish[u] <= start[v], after == before
