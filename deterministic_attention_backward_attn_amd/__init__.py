@@ -1,0 +1,247 @@
+"""Deterministic attention backward for MI355X (gfx950): Python binding.
+
+Thin marshalling over the C ABI in include/dash_attn.h (libdash_attn.so).
+Tensors are torch tensors on the GPU, used only as device memory; every
+step of the computation runs in the library's HIP kernels on the caller's
+current stream.  The host-only calls (schedule tables, DAG prediction,
+longest path) take and return plain Python / numpy values.
+
+Public calls (same names as the C entry points, without the prefix):
+  attn_fwd, attn_bwd_preprocess, attn_bwd_workspace_size, attn_bwd,
+  attn_bwd_status, backward (preprocess + bwd), schedule_tables,
+  schedule_predict, dag_longest_path, litmus_ordered_add.
+"""
+from __future__ import annotations
+
+import ctypes
+
+import numpy as np
+
+from ._lib import DTYPES, SCHEDULES, DashError, Debug, Desc, check, header_symbols, load
+
+__all__ = [
+    "DashError", "SCHEDULES", "attn_fwd", "attn_bwd_preprocess", "attn_bwd_workspace_size",
+    "attn_bwd", "attn_bwd_status", "backward", "schedule_tables", "schedule_predict",
+    "dag_longest_path", "litmus_ordered_add", "tile", "subtile", "header_symbols", "load",
+]
+
+
+# ----------------------------------------------------------------- helpers
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dtype_code(t):
+    torch = _torch()
+    if t.dtype == torch.float32:
+        return DTYPES["f32"]
+    if t.dtype == torch.bfloat16:
+        return DTYPES["bf16"]
+    raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
+
+
+def _desc_from(q, causal: bool, scale) -> Desc:
+    if q.dim() != 4:
+        raise ValueError("expected a [B, H, N, d] tensor")
+    B, H, N, d = (int(x) for x in q.shape)
+    return Desc(B, H, N, d, _dtype_code(q), 1 if causal else 0,
+                float(scale) if scale is not None else 0.0)
+
+
+def _desc(B, H, N, d, dtype: str, causal: bool, scale=None) -> Desc:
+    return Desc(B, H, N, d, DTYPES[dtype], 1 if causal else 0,
+                float(scale) if scale is not None else 0.0)
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensor must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensor must be contiguous")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream=None):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _sched(schedule) -> int:
+    if isinstance(schedule, int):
+        return schedule
+    try:
+        return SCHEDULES[schedule]
+    except KeyError:
+        raise ValueError(f"unknown schedule {schedule!r}; one of {sorted(SCHEDULES)}") from None
+
+
+def _same_shape(ref, *ts):
+    for t in ts:
+        if tuple(t.shape) != tuple(ref.shape) or t.dtype != ref.dtype or t.device != ref.device:
+            raise ValueError("tensors must share shape, dtype and device")
+
+
+# ------------------------------------------------------------------ device
+
+def tile(B, H, N, d, dtype="bf16") -> int:
+    lib = load()
+    return int(lib.dash_attn_tile(ctypes.byref(_desc(B, H, N, d, dtype, False))))
+
+
+def subtile(B, H, N, d, dtype="bf16") -> int:
+    lib = load()
+    return int(lib.dash_attn_bwd_subtile(ctypes.byref(_desc(B, H, N, d, dtype, False))))
+
+
+def attn_fwd(q, k, v, causal: bool = False, scale=None, stream=None):
+    """Returns (o, lse): o like q, lse float32 [B, H, N]."""
+    torch = _torch()
+    lib = load()
+    _same_shape(q, k, v)
+    desc = _desc_from(q, causal, scale)
+    o = torch.empty_like(q)
+    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    check(lib.dash_attn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                            _stream(stream)), "dash_attn_fwd")
+    return o, lse
+
+
+def attn_bwd_preprocess(o, do, stream=None):
+    """delta = rowsum(dO * O) in float32 [B, H, N]."""
+    torch = _torch()
+    lib = load()
+    _same_shape(o, do)
+    desc = _desc_from(o, False, None)
+    delta = torch.empty(o.shape[:3], dtype=torch.float32, device=o.device)
+    check(lib.dash_attn_bwd_preprocess(ctypes.byref(desc), _ptr(o), _ptr(do), _ptr(delta),
+                                       _stream(stream)), "dash_attn_bwd_preprocess")
+    return delta
+
+
+def attn_bwd_workspace_size(B, H, N, d, dtype="bf16", causal=False, schedule="naive") -> int:
+    lib = load()
+    out = ctypes.c_size_t(0)
+    check(lib.dash_attn_bwd_workspace_size(ctypes.byref(_desc(B, H, N, d, dtype, causal)),
+                                           _sched(schedule), ctypes.byref(out)),
+          "dash_attn_bwd_workspace_size")
+    return int(out.value)
+
+
+def alloc_workspace(q, causal=False, schedule="naive"):
+    torch = _torch()
+    B, H, N, d = (int(x) for x in q.shape)
+    dt = "f32" if q.dtype == torch.float32 else "bf16"
+    n = attn_bwd_workspace_size(B, H, N, d, dt, causal, schedule)
+    return torch.empty(n, dtype=torch.uint8, device=q.device)
+
+
+def attn_bwd(q, k, v, do, lse, delta, *, schedule="naive", causal=False, scale=None,
+             workspace=None, out=None, debug=None, stream=None):
+    """Returns (dq, dk, dv).  `workspace`: uint8 GPU tensor of at least
+    attn_bwd_workspace_size bytes (allocated if None).  `out`: optional
+    preallocated (dq, dk, dv).  `debug`: optional dict with keys spin_limit,
+    jitter_seed, poison_q (1-based, 0 = off), partials (float32 tensor)."""
+    torch = _torch()
+    lib = load()
+    _same_shape(q, k, v, do)
+    desc = _desc_from(q, causal, scale)
+    if workspace is None:
+        workspace = alloc_workspace(q, causal, schedule)
+    if out is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    else:
+        dq, dk, dv = out
+        _same_shape(q, dq, dk, dv)
+    for t, shp in ((lse, q.shape[:3]), (delta, q.shape[:3])):
+        if t.dtype != torch.float32 or tuple(t.shape) != tuple(shp):
+            raise ValueError("lse and delta must be float32 [B, H, N]")
+    args = [ctypes.byref(desc), _sched(schedule), _ptr(q), _ptr(k), _ptr(v), _ptr(do), _ptr(lse),
+            _ptr(delta), _ptr(dq), _ptr(dk), _ptr(dv), _ptr(workspace),
+            ctypes.c_size_t(workspace.numel() * workspace.element_size())]
+    if debug is None:
+        check(lib.dash_attn_bwd(*args, _stream(stream)), "dash_attn_bwd")
+    else:
+        dbg = Debug(int(debug.get("spin_limit", 0)), int(debug.get("jitter_seed", 0)),
+                    int(debug.get("poison_q", 0)),
+                    _ptr(debug["partials"]) if debug.get("partials") is not None else None)
+        check(lib.dash_attn_bwd_debug(*args, ctypes.byref(dbg), _stream(stream)),
+              "dash_attn_bwd_debug")
+    return dq, dk, dv
+
+
+def attn_bwd_status(workspace, stream=None):
+    """Synchronizes the stream and raises DashError if an ordered add timed out."""
+    lib = load()
+    check(lib.dash_attn_bwd_status(_ptr(workspace), _stream(stream)), "dash_attn_bwd_status")
+
+
+def backward(q, k, v, o, do, lse, *, schedule="naive", causal=False, scale=None,
+             workspace=None, stream=None):
+    """preprocess + bwd: returns (dq, dk, dv)."""
+    delta = attn_bwd_preprocess(o, do, stream=stream)
+    return attn_bwd(q, k, v, do, lse, delta, schedule=schedule, causal=causal, scale=scale,
+                    workspace=workspace, stream=stream)
+
+
+def litmus_ordered_add(turn, values, acc, counters, spin_limit=0, stream=None):
+    """Device litmus of the ordered hand-off (see the C header)."""
+    lib = load()
+    W, L = (int(x) for x in values.shape)
+    check(lib.dash_litmus_ordered_add(W, L, _ptr(turn), _ptr(values), _ptr(acc), _ptr(counters),
+                                      int(spin_limit), _stream(stream)),
+          "dash_litmus_ordered_add")
+
+
+# --------------------------------------------------------------- host only
+
+def schedule_tables(n: int, causal: bool, schedule):
+    """Returns (units, rank): units = list of [(kv, q), ...] per unit,
+    rank = int32 array [n, n] (rank[q, kv], -1 where absent)."""
+    lib = load()
+    cap = max(1, n * n)
+    n_units = ctypes.c_int32(0)
+    off = (ctypes.c_int32 * (n + 1))()
+    kv = (ctypes.c_int32 * cap)()
+    qq = (ctypes.c_int32 * cap)()
+    rank = (ctypes.c_int32 * cap)()
+    check(lib.dash_schedule_tables(n, 1 if causal else 0, _sched(schedule), ctypes.byref(n_units),
+                                   off, kv, qq, rank), "dash_schedule_tables")
+    units = []
+    for u in range(n_units.value):
+        units.append([(kv[i], qq[i]) for i in range(off[u], off[u + 1])])
+    return units, np.frombuffer(rank, dtype=np.int32).reshape(n, n).copy()
+
+
+def schedule_predict(n: int, causal: bool, schedule, heads: int, slots: int, cost):
+    """Returns (makespan, total_wait, max_slot_idle, lower_bound)."""
+    lib = load()
+    c = (ctypes.c_double * 4)(*[float(x) for x in cost])
+    out = (ctypes.c_double * 4)()
+    check(lib.dash_schedule_predict(n, 1 if causal else 0, _sched(schedule), heads, slots, c, out),
+          "dash_schedule_predict")
+    return tuple(out)
+
+
+def dag_longest_path(weights, edges):
+    """weights: node weights; edges: (src, dst, latency) triples.
+    Returns (start, finish) numpy arrays."""
+    lib = load()
+    w = np.ascontiguousarray(weights, dtype=np.float64)
+    e = list(edges)
+    src = np.ascontiguousarray([x[0] for x in e], dtype=np.int32)
+    dst = np.ascontiguousarray([x[1] for x in e], dtype=np.int32)
+    lat = np.ascontiguousarray([x[2] for x in e], dtype=np.float64)
+    start = np.zeros_like(w)
+    finish = np.zeros_like(w)
+    dp = ctypes.POINTER(ctypes.c_double)
+    ip = ctypes.POINTER(ctypes.c_int32)
+    check(lib.dash_dag_longest_path(len(w), w.ctypes.data_as(dp), len(e), src.ctypes.data_as(ip),
+                                    dst.ctypes.data_as(ip), lat.ctypes.data_as(dp),
+                                    start.ctypes.data_as(dp), finish.ctypes.data_as(dp)),
+          "dash_dag_longest_path")
+    return start, finish

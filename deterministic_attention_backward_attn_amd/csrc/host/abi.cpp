@@ -1,0 +1,372 @@
+// C ABI of the library: argument checks, workspace layout, the per-device
+// schedule-table cache, and the launch sequence of the backward.
+#include <hip/hip_runtime.h>
+
+#include <cmath>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <tuple>
+#include <vector>
+
+#include "../../../include/dash_attn.h"
+#include "../kernels/launch.hpp"
+#include "dag.hpp"
+#include "schedule.hpp"
+
+namespace {
+
+using dash::Sched;
+using dash::Tables;
+
+constexpr size_t kHeaderBytes = 256;   // [0] status, [1] work counter
+constexpr uint32_t kDefaultSpin = 1u << 21;  // polls before giving up (seconds)
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+bool sched_ok(int s) { return s >= DASH_SCHED_ATOMIC && s <= DASH_SCHED_SHIFT; }
+
+dash_status check_desc(const dash_attn_desc* d) {
+  if (!d) return DASH_ERR_INVALID_ARG;
+  if (d->B < 1 || d->H < 1 || d->N < 1 || d->d < 1) return DASH_ERR_INVALID_ARG;
+  if (d->dtype != DASH_F32 && d->dtype != DASH_BF16) return DASH_ERR_INVALID_ARG;
+  if (d->causal != 0 && d->causal != 1) return DASH_ERR_INVALID_ARG;
+  if (!std::isfinite(d->softmax_scale)) return DASH_ERR_INVALID_ARG;
+  if (d->d != 64 && d->d != 128) return DASH_ERR_UNSUPPORTED;
+  const int tile = d->dtype == DASH_BF16 ? 128 : 64;
+  if (d->N % tile) return DASH_ERR_UNSUPPORTED;
+  // row indices (head * N + row) and unit counts are 32-bit on the device
+  const long long heads = (long long)d->B * d->H;
+  if (heads * d->N >= (1LL << 31) || d->N / tile > 32767) return DASH_ERR_UNSUPPORTED;
+  return DASH_OK;
+}
+
+float scale_of(const dash_attn_desc* d) {
+  return d->softmax_scale > 0.f ? d->softmax_scale : 1.0f / std::sqrt((float)d->d);
+}
+
+struct WsLayout {
+  size_t counters_off, counters_words, acc_off, total;
+};
+
+WsLayout layout(const dash_attn_desc* d) {
+  int bc = 0, br = 0;
+  dash::bwd_tiles(d->dtype, d->d, &bc, &br);
+  WsLayout w;
+  const size_t heads = (size_t)d->B * d->H;
+  w.counters_off = kHeaderBytes;
+  w.counters_words = heads * (size_t)(d->N / br);
+  w.acc_off = align256(w.counters_off + 4 * w.counters_words);
+  w.total = w.acc_off + 4 * heads * (size_t)d->N * d->d;
+  return w;
+}
+
+// ----------------------------------------------------------- table cache
+
+struct DevTables {
+  Tables host;
+  int* d_unit_off = nullptr;
+  int2* d_items = nullptr;
+};
+
+std::mutex g_mu;
+std::map<std::tuple<int, int, int, int>, DevTables> g_tables;  // (device, n, causal, sched)
+std::map<std::tuple<int, int, int, int, int>, int> g_coresident;  // (device, dtype, d, causal, ordered)
+
+dash_status get_tables(int dev, int n, bool causal, Sched s, const DevTables** out) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  auto key = std::make_tuple(dev, n, (int)causal, (int)s);
+  auto it = g_tables.find(key);
+  if (it != g_tables.end()) {
+    *out = &it->second;
+    return DASH_OK;
+  }
+  DevTables dt;
+  if (!dash::build_tables(n, causal, s, dt.host)) return DASH_ERR_UNSUPPORTED;
+  if (dash::validate_tables(dt.host)[0] != '\0') return DASH_ERR_SCHEDULE_INVALID;
+  const Tables& t = dt.host;
+  std::vector<int2> items(t.items());
+  for (int i = 0; i < t.items(); ++i) {
+    items[i].x = t.kv[i] | (t.q[i] << 16);
+    items[i].y = t.ordered() ? t.rank[(size_t)t.q[i] * n + t.kv[i]] : 0;
+  }
+  if (hipMalloc(&dt.d_unit_off, sizeof(int) * t.unit_off.size()) != hipSuccess) return DASH_ERR_HIP;
+  if (hipMalloc(&dt.d_items, sizeof(int2) * (items.empty() ? 1 : items.size())) != hipSuccess) {
+    (void)hipFree(dt.d_unit_off);
+    return DASH_ERR_HIP;
+  }
+  if (hipMemcpy(dt.d_unit_off, t.unit_off.data(), sizeof(int) * t.unit_off.size(),
+                hipMemcpyHostToDevice) != hipSuccess ||
+      hipMemcpy(dt.d_items, items.data(), sizeof(int2) * items.size(), hipMemcpyHostToDevice) !=
+          hipSuccess) {
+    (void)hipFree(dt.d_unit_off);
+    (void)hipFree(dt.d_items);
+    return DASH_ERR_HIP;
+  }
+  auto res = g_tables.emplace(key, std::move(dt));
+  *out = &res.first->second;
+  return DASH_OK;
+}
+
+dash_status get_coresident(int dev, int dtype, int d, bool causal, bool ordered, int* blocks) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  auto key = std::make_tuple(dev, dtype, d, (int)causal, (int)ordered);
+  auto it = g_coresident.find(key);
+  if (it != g_coresident.end()) {
+    *blocks = it->second;
+    return DASH_OK;
+  }
+  int b = 0;
+  if (dash::bwd_max_coresident(dtype, d, causal, ordered, &b) != hipSuccess || b < 1)
+    return DASH_ERR_HIP;
+  g_coresident[key] = b;
+  *blocks = b;
+  return DASH_OK;
+}
+
+dash_status run_bwd(const dash_attn_desc* desc, dash_schedule schedule, const void* q,
+                    const void* k, const void* v, const void* dout, const float* lse,
+                    const float* delta, void* dq, void* dk, void* dv, void* workspace,
+                    size_t workspace_bytes, const dash_bwd_debug* dbg, void* stream) {
+  dash_status st = check_desc(desc);
+  if (st != DASH_OK) return st;
+  if (!sched_ok(schedule)) return DASH_ERR_INVALID_ARG;
+  if (!q || !k || !v || !dout || !lse || !delta || !dq || !dk || !dv || !workspace)
+    return DASH_ERR_INVALID_ARG;
+  const WsLayout w = layout(desc);
+  if (workspace_bytes < w.total || ((uintptr_t)workspace & 255u)) return DASH_ERR_WORKSPACE;
+  int bc = 0, br = 0;
+  dash::bwd_tiles(desc->dtype, desc->d, &bc, &br);
+  const int n = desc->N / bc;
+  const bool causal = desc->causal != 0;
+  const Sched s = (Sched)schedule;
+  const bool ordered = s != Sched::Atomic;
+  if (dbg && (dbg->poison_q < 0 || dbg->poison_q > desc->N / br)) return DASH_ERR_INVALID_ARG;
+
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return DASH_ERR_HIP;
+  const DevTables* tb = nullptr;
+  st = get_tables(dev, n, causal, s, &tb);
+  if (st != DASH_OK) return st;
+  int maxco = 0;
+  st = get_coresident(dev, desc->dtype, desc->d, causal, ordered, &maxco);
+  if (st != DASH_OK) return st;
+
+  const int U = tb->host.units();
+  const long heads = (long)desc->B * desc->H;
+  const long total_units = heads * U;
+  int grid = 0, p_eff = 0, dynamic = 0;
+  if (tb->host.needs_static()) {
+    p_eff = (maxco / U) * U;
+    if (p_eff < 1) return DASH_ERR_UNSUPPORTED;  // a whole head must be resident
+    if (p_eff > total_units) p_eff = (int)total_units;
+    grid = p_eff;
+  } else {
+    dynamic = 1;
+    grid = (int)std::min<long>(maxco, total_units);
+    p_eff = grid;
+  }
+
+  hipStream_t strm = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+  if (dash::launch_zero_u32((uint32_t*)ws, w.total / 4, strm) != hipSuccess) return DASH_ERR_HIP;
+
+  dash::BwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.dout = dout;
+  a.lse = lse;
+  a.delta = delta;
+  a.dk = dk;
+  a.dv = dv;
+  a.dq_accum = (float*)(ws + w.acc_off);
+  a.counters = (uint32_t*)(ws + w.counters_off);
+  a.header = (uint32_t*)ws;
+  a.unit_off = tb->d_unit_off;
+  a.items = tb->d_items;
+  a.N = desc->N;
+  a.n_tiles = n;
+  a.units_per_head = U;
+  a.total_units = (int)total_units;
+  a.p_eff = p_eff;
+  a.dynamic = dynamic;
+  a.scale = scale_of(desc);
+  a.scale_log2 = a.scale * 1.4426950408889634f;
+  a.spin_limit = (dbg && dbg->spin_limit) ? dbg->spin_limit : kDefaultSpin;
+  a.jitter_seed = dbg ? dbg->jitter_seed : 0u;
+  a.poison_q = dbg ? dbg->poison_q - 1 : -1;
+  a.partials = dbg ? dbg->partials : nullptr;
+  if (dash::launch_bwd(desc->dtype, desc->d, causal, ordered, a, grid, strm) != hipSuccess)
+    return DASH_ERR_HIP;
+  const size_t elems = (size_t)heads * desc->N * desc->d;
+  if (dash::launch_dq_convert(desc->dtype, a.dq_accum, dq, a.scale, elems, strm) != hipSuccess)
+    return DASH_ERR_HIP;
+  return DASH_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* dash_status_string(dash_status s) {
+  switch (s) {
+    case DASH_OK: return "ok";
+    case DASH_ERR_INVALID_ARG: return "invalid argument";
+    case DASH_ERR_UNSUPPORTED: return "unsupported shape, dtype or schedule";
+    case DASH_ERR_WORKSPACE: return "workspace too small or misaligned";
+    case DASH_ERR_HIP: return "HIP runtime error";
+    case DASH_ERR_SCHEDULE_INVALID: return "schedule tables failed validation";
+    case DASH_ERR_ORDER_TIMEOUT: return "ordered dQ add timed out";
+  }
+  return "unknown status";
+}
+
+int32_t dash_attn_tile(const dash_attn_desc* desc) {
+  if (!desc) return 0;
+  return desc->dtype == DASH_BF16 ? 128 : 64;
+}
+
+int32_t dash_attn_bwd_subtile(const dash_attn_desc* desc) {
+  if (!desc) return 0;
+  int bc = 0, br = 0;
+  dash::bwd_tiles(desc->dtype, desc->d, &bc, &br);
+  return br;
+}
+
+dash_status dash_attn_fwd(const dash_attn_desc* desc, const void* q, const void* k, const void* v,
+                          void* o, float* lse, void* stream) {
+  dash_status st = check_desc(desc);
+  if (st != DASH_OK) return st;
+  if (!q || !k || !v || !o || !lse) return DASH_ERR_INVALID_ARG;
+  dash::FwdArgs a;
+  a.q = q;
+  a.k = k;
+  a.v = v;
+  a.o = o;
+  a.lse = lse;
+  a.N = desc->N;
+  a.BH = desc->B * desc->H;
+  a.scale_log2 = scale_of(desc) * 1.4426950408889634f;
+  if (dash::launch_fwd(desc->dtype, desc->d, desc->causal != 0, a, (hipStream_t)stream) !=
+      hipSuccess)
+    return DASH_ERR_HIP;
+  return DASH_OK;
+}
+
+dash_status dash_attn_bwd_preprocess(const dash_attn_desc* desc, const void* o, const void* dout,
+                                     float* delta, void* stream) {
+  dash_status st = check_desc(desc);
+  if (st != DASH_OK) return st;
+  if (!o || !dout || !delta) return DASH_ERR_INVALID_ARG;
+  const long rows = (long)desc->B * desc->H * desc->N;
+  if (dash::launch_preprocess(desc->dtype, desc->d, o, dout, delta, rows, (hipStream_t)stream) !=
+      hipSuccess)
+    return DASH_ERR_HIP;
+  return DASH_OK;
+}
+
+dash_status dash_attn_bwd_workspace_size(const dash_attn_desc* desc, dash_schedule schedule,
+                                         size_t* bytes) {
+  dash_status st = check_desc(desc);
+  if (st != DASH_OK) return st;
+  if (!sched_ok(schedule) || !bytes) return DASH_ERR_INVALID_ARG;
+  *bytes = layout(desc).total;
+  return DASH_OK;
+}
+
+dash_status dash_attn_bwd(const dash_attn_desc* desc, dash_schedule schedule, const void* q,
+                          const void* k, const void* v, const void* dout, const float* lse,
+                          const float* delta, void* dq, void* dk, void* dv, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  return run_bwd(desc, schedule, q, k, v, dout, lse, delta, dq, dk, dv, workspace,
+                 workspace_bytes, nullptr, stream);
+}
+
+dash_status dash_attn_bwd_debug(const dash_attn_desc* desc, dash_schedule schedule, const void* q,
+                                const void* k, const void* v, const void* dout, const float* lse,
+                                const float* delta, void* dq, void* dk, void* dv, void* workspace,
+                                size_t workspace_bytes, const dash_bwd_debug* dbg, void* stream) {
+  if (!dbg) return DASH_ERR_INVALID_ARG;
+  return run_bwd(desc, schedule, q, k, v, dout, lse, delta, dq, dk, dv, workspace,
+                 workspace_bytes, dbg, stream);
+}
+
+dash_status dash_attn_bwd_status(const void* workspace, void* stream) {
+  if (!workspace) return DASH_ERR_INVALID_ARG;
+  if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return DASH_ERR_HIP;
+  uint32_t word = 0;
+  if (hipMemcpy(&word, workspace, sizeof(word), hipMemcpyDeviceToHost) != hipSuccess)
+    return DASH_ERR_HIP;
+  return word ? DASH_ERR_ORDER_TIMEOUT : DASH_OK;
+}
+
+dash_status dash_schedule_tables(int32_t n, int32_t causal, dash_schedule schedule,
+                                 int32_t* n_units, int32_t* unit_offsets, int32_t* item_kv,
+                                 int32_t* item_q, int32_t* rank) {
+  if (n < 1 || n > 32767 || (causal != 0 && causal != 1) || !sched_ok(schedule) || !n_units ||
+      !unit_offsets || !item_kv || !item_q || !rank)
+    return DASH_ERR_INVALID_ARG;
+  Tables t;
+  if (!dash::build_tables(n, causal != 0, (Sched)schedule, t)) return DASH_ERR_UNSUPPORTED;
+  if (dash::validate_tables(t)[0] != '\0') return DASH_ERR_SCHEDULE_INVALID;
+  *n_units = t.units();
+  std::memcpy(unit_offsets, t.unit_off.data(), sizeof(int) * t.unit_off.size());
+  std::memcpy(item_kv, t.kv.data(), sizeof(int) * t.kv.size());
+  std::memcpy(item_q, t.q.data(), sizeof(int) * t.q.size());
+  std::memcpy(rank, t.rank.data(), sizeof(int) * t.rank.size());
+  return DASH_OK;
+}
+
+dash_status dash_schedule_predict(int32_t n, int32_t causal, dash_schedule schedule, int32_t heads,
+                                  int32_t slots, const double cost[4], double out[4]) {
+  if (n < 1 || n > 32767 || (causal != 0 && causal != 1) || !sched_ok(schedule) || heads < 1 ||
+      slots < 1 || !cost || !out)
+    return DASH_ERR_INVALID_ARG;
+  for (int i = 0; i < 4; ++i)
+    if (!(cost[i] >= 0.0) || !std::isfinite(cost[i])) return DASH_ERR_INVALID_ARG;
+  Tables t;
+  if (!dash::build_tables(n, causal != 0, (Sched)schedule, t)) return DASH_ERR_UNSUPPORTED;
+  if (dash::validate_tables(t)[0] != '\0') return DASH_ERR_SCHEDULE_INVALID;
+  if (t.needs_static() && t.units() > slots) return DASH_ERR_UNSUPPORTED;
+  dash::DagResult r;
+  if (!dash::dag_predict(t, heads, slots, cost, r)) return DASH_ERR_SCHEDULE_INVALID;
+  out[0] = r.makespan;
+  out[1] = r.total_wait;
+  out[2] = r.max_slot_idle;
+  out[3] = r.lower_bound;
+  return DASH_OK;
+}
+
+dash_status dash_dag_longest_path(int32_t n_nodes, const double* weights, int32_t n_edges,
+                                  const int32_t* src, const int32_t* dst, const double* latency,
+                                  double* start, double* finish) {
+  if (n_nodes < 0 || n_edges < 0 || (n_nodes && (!weights || !start || !finish)) ||
+      (n_edges && (!src || !dst || !latency)))
+    return DASH_ERR_INVALID_ARG;
+  for (int e = 0; e < n_edges; ++e)
+    if (src[e] < 0 || src[e] >= n_nodes || dst[e] < 0 || dst[e] >= n_nodes)
+      return DASH_ERR_INVALID_ARG;
+  if (!dash::dag_longest_path(n_nodes, weights, n_edges, src, dst, latency, start, finish))
+    return DASH_ERR_SCHEDULE_INVALID;
+  return DASH_OK;
+}
+
+dash_status dash_litmus_ordered_add(int32_t workgroups, int32_t len, const int32_t* turn,
+                                    const float* values, float* acc, uint32_t* counters,
+                                    uint32_t spin_limit, void* stream) {
+  if (workgroups < 1 || len < 1 || !turn || !values || !acc || !counters)
+    return DASH_ERR_INVALID_ARG;
+  hipStream_t strm = (hipStream_t)stream;
+  if (dash::launch_zero_u32(counters, 2, strm) != hipSuccess) return DASH_ERR_HIP;
+  if (dash::launch_litmus(workgroups, len, turn, values, acc, counters, counters + 1,
+                          spin_limit ? spin_limit : kDefaultSpin, strm) != hipSuccess)
+    return DASH_ERR_HIP;
+  if (hipStreamSynchronize(strm) != hipSuccess) return DASH_ERR_HIP;
+  uint32_t word = 0;
+  if (hipMemcpy(&word, counters + 1, sizeof(word), hipMemcpyDeviceToHost) != hipSuccess)
+    return DASH_ERR_HIP;
+  return word ? DASH_ERR_ORDER_TIMEOUT : DASH_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,143 @@
+// Device-side building blocks shared by the attention kernels (gfx950).
+//
+// MFMA fragments.  All contractions use the 32x32 output MFMA:
+//   bf16: v_mfma_f32_32x32x16_bf16, 8 bf16 of A and of B per lane per step
+//   fp32: v_mfma_f32_32x32x2_f32,   1 float of A and of B per lane per step
+// Operand A (M x K): lane l holds row l%32; operand B (K x N): lane l holds
+// column l%32.  Both take their K values from the lane half h = l/32 and the
+// slot s; the hardware pairs A's (h, s) with B's (h, s), so any consistent
+// assignment of K indices to (h, s) is a valid contraction.
+// Accumulator C (M x N): lane l holds column l%32; its register r holds row
+//   crow(r, h) = 8*(r/4) + 4*h + (r%4).
+// Reusing an accumulator as a K operand: the rows of a 32-row accumulator
+// tile are cut into chunks of KSTEP rows; chunk c of a lane is registers
+// r = KPL*c + s (s < KPL), i.e. rows crow(KPL*c + s, h).  The other operand
+// is then read with exactly those row indices in its K slots.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dash {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
+typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+
+constexpr float kLog2e = 1.4426950408889634f;
+
+__device__ __forceinline__ int crow(int r, int h) { return ((r >> 2) << 3) + (h << 2) + (r & 3); }
+
+// bf16 <-> fp32, round to nearest even (inputs are finite).
+__device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+__device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
+
+// Element traits: storage type, MFMA fragment type and the K step.
+template <typename T> struct Elt;
+
+template <> struct Elt<float> {
+  typedef float frag;
+  static constexpr int KPL = 1;     // K values per lane per MFMA
+  static constexpr int KSTEP = 2;   // K per MFMA
+  static constexpr int VEC = 4;     // elements per 16-byte global access
+  __device__ static __forceinline__ f32x16 mma(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x2f32(a, b, c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ float to_f32(float x) { return x; }
+  __device__ static __forceinline__ float from_f32(float x) { return x; }
+};
+
+struct bf16_t { uint16_t bits; };
+
+template <> struct Elt<bf16_t> {
+  typedef bf16x8 frag;
+  static constexpr int KPL = 8;
+  static constexpr int KSTEP = 16;
+  static constexpr int VEC = 8;
+  __device__ static __forceinline__ f32x16 mma(frag a, frag b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+  }
+  __device__ static __forceinline__ float to_f32(bf16_t x) { return bf16_bits_to_f32(x.bits); }
+  __device__ static __forceinline__ bf16_t from_f32(float x) { return bf16_t{f32_to_bf16_bits(x)}; }
+};
+
+__device__ __forceinline__ f32x16 zero16() {
+  f32x16 z;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) z[i] = 0.f;
+  return z;
+}
+
+// Build a bf16 fragment from 8 floats (RNE).
+__device__ __forceinline__ bf16x8 pack_bf16x8(const float* v) {
+  u16x8 u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) u[i] = f32_to_bf16_bits(v[i]);
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+// Load a K-contiguous fragment (KPL elements) from memory (LDS or global).
+__device__ __forceinline__ bf16x8 load_frag(const bf16_t* p) {
+  return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u16x8*>(p));
+}
+__device__ __forceinline__ float load_frag(const float* p) { return *p; }
+
+// Device-scope ordering helpers.
+__device__ __forceinline__ uint32_t load_acquire_agent(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ uint32_t load_relaxed_agent(const uint32_t* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void store_release_agent(uint32_t* p, uint32_t v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void fence_release_agent() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
+__device__ __forceinline__ void fence_acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
+
+// fp32 add performed at the device coherence point (no return value).
+__device__ __forceinline__ void atomic_add_f32(float* p, float v) {
+  __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Status word bits (workspace header).
+constexpr uint32_t kStatusTimeout = 1u;
+
+// Bounded wait until *cnt == target.  Called by one lane.  Polls with
+// relaxed device-scope loads and issues one acquire fence after success, so
+// the caches are invalidated once per hand-off rather than once per poll.
+// Gives up after `limit` polls (or soon after another wait gave up),
+// records the time-out in *status and returns false.
+__device__ __forceinline__ bool wait_counter(const uint32_t* cnt, uint32_t target, uint32_t* status,
+                                             uint32_t limit) {
+  uint32_t polls = 0;
+  while (true) {
+    if (load_relaxed_agent(cnt) == target) {
+      fence_acquire_agent();
+      return true;
+    }
+    if ((polls & 255u) == 255u && load_relaxed_agent(status) != 0u) return false;
+    if (++polls > limit) {
+      __hip_atomic_fetch_or(status, kStatusTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      return false;
+    }
+    __builtin_amdgcn_s_sleep(2);
+  }
+}
+
+__device__ __forceinline__ uint32_t hash32(uint32_t x) {
+  x ^= x >> 16;
+  x *= 0x7feb352du;
+  x ^= x >> 15;
+  x *= 0x846ca68bu;
+  x ^= x >> 16;
+  return x;
+}
+
+}  // namespace dash

@@ -1,0 +1,69 @@
+// Host-side launch interface of the HIP kernels (private to the library).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace dash {
+
+// Arguments of the persistent backward kernel.  All pointers are device
+// pointers.  Per-head tensors are indexed by head = b*H + h.
+struct BwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  const void* dout;
+  const float* lse;
+  const float* delta;
+  void* dk;
+  void* dv;
+  float* dq_accum;        // [BH, N, d] fp32, zeroed before the launch
+  uint32_t* counters;     // [BH, N / BR] order counters, zeroed
+  uint32_t* header;       // [0] status word, [1] work counter; zeroed
+  const int* unit_off;    // [units_per_head + 1]
+  const int2* items;      // {kv | q << 16, rank} per item, one head's list
+  int N;
+  int n_tiles;            // N / BC
+  int units_per_head;
+  int total_units;        // units_per_head * BH
+  int p_eff;              // static policy: workgroups that take units
+  int dynamic;            // 1: take units from the work counter
+  float scale;            // softmax scale s
+  float scale_log2;       // s * log2(e)
+  uint32_t spin_limit;
+  uint32_t jitter_seed;
+  int poison_q;
+  float* partials;        // debug: [BH, n_tiles, N, d] or null
+};
+
+struct FwdArgs {
+  const void* q;
+  const void* k;
+  const void* v;
+  void* o;
+  float* lse;
+  int N;
+  int BH;
+  float scale_log2;
+};
+
+// dtype: 0 = fp32, 1 = bf16.  Returns hipSuccess or the launch error.
+hipError_t launch_bwd(int dtype, int d, bool causal, bool ordered, const BwdArgs& a, int grid,
+                      hipStream_t stream);
+// Largest grid of the backward kernel whose workgroups are all resident.
+hipError_t bwd_max_coresident(int dtype, int d, bool causal, bool ordered, int* blocks);
+// Tile sizes of the backward kernel: KV tile (BC) and Q sub-tile (BR).
+void bwd_tiles(int dtype, int d, int* bc, int* br);
+
+hipError_t launch_fwd(int dtype, int d, bool causal, const FwdArgs& a, hipStream_t stream);
+
+hipError_t launch_preprocess(int dtype, int d, const void* o, const void* dout, float* delta,
+                             long rows, hipStream_t stream);
+hipError_t launch_zero_u32(uint32_t* p, size_t n_words, hipStream_t stream);
+hipError_t launch_dq_convert(int dtype, const float* acc, void* dq, float scale, size_t n,
+                             hipStream_t stream);
+hipError_t launch_litmus(int workgroups, int len, const int* turn, const float* values,
+                         float* acc, uint32_t* counter, uint32_t* status, uint32_t spin_limit,
+                         hipStream_t stream);
+
+}  // namespace dash

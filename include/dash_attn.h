@@ -1,0 +1,242 @@
+/*
+ * dash_attn.h - C ABI of the deterministic attention backward for MI355X
+ * (CDNA4, gfx950).
+ *
+ * What the library computes.  For each (batch b, head h), softmax attention
+ * O = softmax(s * Q K^T) V with an optional causal mask (query i sees keys
+ * j <= i), its log-sum-exp LSE, and the backward pass: given Q, K, V, O,
+ * dO and LSE it returns dQ, dK, dV.  The inputs and outputs of the backward
+ * are those of the problem statement of the DASH explainer (gist.science,
+ * "Technisches Resuemee" 1) and of the method outline of the euno.news
+ * summary ("Methodology" 1: the backward's matrix products, score
+ * computation and gradient reduction).
+ *
+ * Determinism.  Per the same explainer section, floating-point addition is
+ * not associative, so a reproducible backward must add the per-KV-tile dQ
+ * partials in a fixed order.  Every schedule except DASH_SCHED_ATOMIC adds
+ * them in the order of a rank table, enforced by device-scope counters, so
+ * dQ, dK and dV are bit-identical from run to run.  DASH_SCHED_ATOMIC is the
+ * non-deterministic reference (unordered atomic adds).
+ *
+ * Schedules (explainer "Technisches Resuemee" 2.2; authors' abstract):
+ *   NAIVE       Q blocks ascending; dQ order = KV tiles ascending.
+ *   DESCENDING  Q blocks descending (descending Q-tile iteration); same
+ *               dQ order as NAIVE.
+ *   SHIFT       full mask: KV tile i visits Q blocks i, i+1, ..., 0, ..., i-1
+ *               (shift scheduling); causal mask: symmetric shift, pairing
+ *               KV tiles w and n-1-w in one workgroup, two phases.  dQ order
+ *               = the step at which each tile reaches the block.
+ *   ATOMIC      NAIVE's traversal, unordered fp32 atomic adds.
+ *
+ * Conventions for every call below.
+ *   Layout      Q, K, V, O, dO, dQ, dK, dV: contiguous [B, H, N, d], d
+ *               innermost.  LSE and delta: contiguous [B, H, N] float.
+ *   dtype       One dtype for all of Q, K, V, O, dO, dQ, dK, dV (fp32 or
+ *               bf16); LSE, delta and all accumulation are fp32.  bf16
+ *               outputs are rounded to nearest even.
+ *   LSE         Natural log of sum_j exp(s * <Q_i, K_j>) over visible j.
+ *   Shapes      N_q = N_k = N; d in {64, 128}; N a multiple of the tile
+ *               (64 for fp32, 128 for bf16); B, H >= 1.  Anything else
+ *               returns DASH_ERR_UNSUPPORTED before any launch.
+ *   Pointers    Device pointers unless stated otherwise; owned by the
+ *               caller; never freed or retained by the library.  Inputs
+ *               are read-only; outputs may not alias inputs.
+ *   Streams     `stream` is a hipStream_t (0 = the null stream).  Calls are
+ *               asynchronous on it unless stated otherwise.
+ *   Errors      Argument errors are returned synchronously, before any
+ *               launch.  HIP launch errors return DASH_ERR_HIP.  A device
+ *               ordering time-out is reported by dash_attn_bwd_status.
+ *   Memory      dash_attn_bwd keeps a per-device cache of schedule tables
+ *               (allocated on first use of a shape/schedule, a few hundred
+ *               KB at most, held until the process ends).  Everything else
+ *               lives in caller buffers.
+ *   Threads     Calls may come from several host threads; the table cache
+ *               is locked.  Calls that share a workspace must be ordered
+ *               on one stream.
+ */
+#ifndef DASH_ATTN_H
+#define DASH_ATTN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  DASH_OK = 0,
+  DASH_ERR_INVALID_ARG = 1,      /* null pointer, bad enum, negative size */
+  DASH_ERR_UNSUPPORTED = 2,      /* valid but unsupported shape/dtype/schedule */
+  DASH_ERR_WORKSPACE = 3,        /* workspace too small or misaligned */
+  DASH_ERR_HIP = 4,              /* a HIP runtime call failed */
+  DASH_ERR_SCHEDULE_INVALID = 5, /* schedule tables failed validation (cycle, coverage) */
+  DASH_ERR_ORDER_TIMEOUT = 6     /* an ordered dQ add waited past its spin limit */
+} dash_status;
+
+typedef enum { DASH_F32 = 0, DASH_BF16 = 1 } dash_dtype;
+
+typedef enum {
+  DASH_SCHED_ATOMIC = 0,
+  DASH_SCHED_NAIVE = 1,
+  DASH_SCHED_DESCENDING = 2,
+  DASH_SCHED_SHIFT = 3
+} dash_schedule;
+
+/* Problem descriptor.  softmax_scale <= 0 selects 1/sqrt(d). */
+typedef struct {
+  int32_t B, H, N, d;
+  int32_t dtype;   /* dash_dtype */
+  int32_t causal;  /* 0 = full mask, 1 = causal */
+  float softmax_scale;
+} dash_attn_desc;
+
+/* Human-readable name of a status code (static string, never NULL). */
+const char* dash_status_string(dash_status s);
+
+/* KV tile (rows) used for a descriptor: 64 for fp32, 128 for bf16; 0 if
+ * desc is NULL. */
+int32_t dash_attn_tile(const dash_attn_desc* desc);
+
+/* Q sub-tile (rows) of the backward: each Q block of dash_attn_tile rows
+ * is processed, counted and ordered in sub-tiles of this many rows (64 for
+ * bf16 and for fp32 with d = 64, 32 for fp32 with d = 128); 0 if desc is
+ * NULL. */
+int32_t dash_attn_bwd_subtile(const dash_attn_desc* desc);
+
+/*
+ * Forward: O = softmax(s Q K^T) V and LSE.  q, k, v: inputs; o: output
+ * [B,H,N,d]; lse: output [B,H,N] float.  Needed to produce the O and LSE
+ * the backward consumes (the backward's inputs, explainer section 1).
+ */
+dash_status dash_attn_fwd(const dash_attn_desc* desc, const void* q, const void* k,
+                          const void* v, void* o, float* lse, void* stream);
+
+/*
+ * Backward preprocess: delta_i = sum_k dO_ik * O_ik in fp32 ([B,H,N]).
+ * This row term is implied by the backward (it equals sum_j P_ij dP_ij) and
+ * needs only O and dO; the pages do not name it separately.
+ */
+dash_status dash_attn_bwd_preprocess(const dash_attn_desc* desc, const void* o,
+                                     const void* dout, float* delta, void* stream);
+
+/*
+ * Workspace bytes dash_attn_bwd needs for this descriptor and schedule
+ * (written to *bytes).  The size is the same for every schedule: the
+ * schedules only reorder work (euno.news summary, "Results": memory
+ * overhead unchanged).  Holds the fp32 dQ accumulator [B,H,N,d], the
+ * per-Q-tile order counters, a work counter and a status word.
+ */
+dash_status dash_attn_bwd_workspace_size(const dash_attn_desc* desc, dash_schedule schedule,
+                                         size_t* bytes);
+
+/*
+ * Backward: dQ, dK, dV from Q, K, V, dO, LSE and delta (from
+ * dash_attn_bwd_preprocess).  workspace: device buffer of at least
+ * dash_attn_bwd_workspace_size bytes, 256-byte aligned; its contents on
+ * entry do not matter and on return are scratch (except the status word).
+ * The call zeroes the accumulator and counters, runs the persistent
+ * backward kernel with the chosen schedule, then scales and converts dQ.
+ */
+dash_status dash_attn_bwd(const dash_attn_desc* desc, dash_schedule schedule, const void* q,
+                          const void* k, const void* v, const void* dout, const float* lse,
+                          const float* delta, void* dq, void* dk, void* dv, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/*
+ * Device status of the last dash_attn_bwd on this workspace.  Synchronizes
+ * `stream`, then reads the status word: DASH_OK, or DASH_ERR_ORDER_TIMEOUT
+ * if some ordered add gave up waiting (its results are then not valid).
+ */
+dash_status dash_attn_bwd_status(const void* workspace, void* stream);
+
+/*
+ * Test and diagnostic controls for dash_attn_bwd_debug.  An all-zero
+ * struct gives the behaviour of dash_attn_bwd.
+ *   spin_limit      0 = default; else the number of polls (each ~1 us
+ *                   apart) after which an ordered add gives up and sets
+ *                   DASH_ERR_ORDER_TIMEOUT.
+ *   jitter_seed     non-zero: each workgroup sleeps a pseudo-random few
+ *                   microseconds before each ordered add (perturbs timing
+ *                   only; results of ordered schedules must not change).
+ *   poison_q        0 = off; k > 0: in head 0, the first contributor to Q
+ *                   sub-tile k-1 (sub-tiles of dash_attn_bwd_subtile rows)
+ *                   waits for a counter value that never comes, which
+ *                   forces the time-out path.
+ *   partials        non-NULL: device float buffer [B,H,n_kv,N,d] (n_kv =
+ *                   N / dash_attn_tile); each KV tile's unscaled dQ partial
+ *                   for every Q row it meets is stored there, in addition
+ *                   to the normal accumulation.
+ */
+typedef struct {
+  uint32_t spin_limit;
+  uint32_t jitter_seed;
+  int32_t poison_q;
+  float* partials;
+} dash_bwd_debug;
+
+dash_status dash_attn_bwd_debug(const dash_attn_desc* desc, dash_schedule schedule,
+                                const void* q, const void* k, const void* v, const void* dout,
+                                const float* lse, const float* delta, void* dq, void* dk,
+                                void* dv, void* workspace, size_t workspace_bytes,
+                                const dash_bwd_debug* dbg, void* stream);
+
+/* ------------------------------------------------------------------ host only */
+
+/*
+ * Schedule tables for one head with n tiles (host memory, no GPU needed).
+ * Outputs (caller-allocated host arrays):
+ *   *n_units        number of units (workgroup work lists)
+ *   unit_offsets    [n + 1]: unit u's items are [unit_offsets[u], unit_offsets[u+1])
+ *   item_kv, item_q [n * n]: the items (KV tile, Q block) in processing order
+ *   rank            [n * n], row-major [q][kv]: position of kv in q's dQ
+ *                   order, -1 where the pair is masked or for ATOMIC
+ * Returns DASH_ERR_UNSUPPORTED for SHIFT with a causal mask and odd n > 1.
+ */
+dash_status dash_schedule_tables(int32_t n, int32_t causal, dash_schedule schedule,
+                                 int32_t* n_units, int32_t* unit_offsets, int32_t* item_kv,
+                                 int32_t* item_q, int32_t* rank);
+
+/*
+ * DAG critical-path prediction for `heads` heads of n tiles run on `slots`
+ * persistent workgroups (explainer 2.1's DAG: compute and reduction nodes,
+ * data and accumulation-order edges, one KV tile per processor chain).
+ * cost[4] = {c_full, c_diag, r, h}: compute time of an unmasked item, of a
+ * causal diagonal item, the dQ add, and the hand-off latency between
+ * consecutive contributors.  out[4] = {makespan, total_wait,
+ * max_slot_idle, lower_bound}.  Host only.
+ * SHIFT needs slots >= units per head (else DASH_ERR_UNSUPPORTED).
+ */
+dash_status dash_schedule_predict(int32_t n, int32_t causal, dash_schedule schedule,
+                                  int32_t heads, int32_t slots, const double cost[4],
+                                  double out[4]);
+
+/*
+ * Longest path (critical path) of a general DAG, host only.  Node weights
+ * [n_nodes]; edges src/dst/latency [n_edges].  Writes earliest start and
+ * finish per node.  DASH_ERR_SCHEDULE_INVALID if the graph has a cycle.
+ */
+dash_status dash_dag_longest_path(int32_t n_nodes, const double* weights, int32_t n_edges,
+                                  const int32_t* src, const int32_t* dst, const double* latency,
+                                  double* start, double* finish);
+
+/*
+ * Ordering litmus (diagnostic): `workgroups` workgroups (spread over all
+ * XCDs by the dispatcher, all resident at once) take turns adding their row
+ * of `values` [workgroups, len] into `acc` [len], workgroup w going when
+ * the counter reaches turn[w] (a permutation of 0..workgroups-1), through
+ * the same counter hand-off and fp32 atomic adds that the ordered dQ adds
+ * use.  turn, values, acc: device arrays; counters: device uint32[2]
+ * (counter, status; cleared by the call).  spin_limit 0 = default.
+ * Synchronizes the stream; returns DASH_ERR_ORDER_TIMEOUT if a hand-off
+ * timed out.
+ */
+dash_status dash_litmus_ordered_add(int32_t workgroups, int32_t len, const int32_t* turn,
+                                    const float* values, float* acc, uint32_t* counters,
+                                    uint32_t spin_limit, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DASH_ATTN_H */

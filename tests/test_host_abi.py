@@ -1,0 +1,139 @@
+"""C-ABI tests that need no GPU: the library loads and exports every symbol
+the header declares; host-only calls (schedule tables, DAG prediction,
+longest path) match the oracle exactly; argument errors come back as status
+codes before any launch."""
+import ctypes
+import random
+
+import numpy as np
+import pytest
+
+import deterministic_attention_backward_attn_amd as D
+from deterministic_attention_backward_attn_amd import _lib
+from oracle import dag as OD
+from oracle import schedules as OS
+
+
+def test_library_exports_every_header_symbol():
+    lib = D.load()
+    syms = D.header_symbols()
+    assert len(syms) >= 12
+    for s in syms:
+        assert hasattr(lib, s), s
+    assert lib.dash_status_string(6) == b"ordered dQ add timed out"
+    assert lib.dash_status_string(99) == b"unknown status"
+
+
+@pytest.mark.parametrize("schedule", OS.SCHEDULES)
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("n", [1, 2, 3, 4, 6, 8, 16, 32, 64, 128])
+def test_schedule_tables_match_oracle(schedule, causal, n):
+    if schedule == OS.SHIFT and causal and n % 2 and n > 1:
+        with pytest.raises(D.DashError) as e:
+            D.schedule_tables(n, causal, schedule)
+        assert e.value.code == 2
+        return
+    units, rank = D.schedule_tables(n, causal, schedule)
+    assert units == OS.units(schedule, n, causal)
+    ref = OS.rank_table(schedule, n, causal)
+    if ref is None:
+        assert np.all(rank == -1)
+    else:
+        want = np.array([[-1 if x is None else x for x in row] for row in ref], dtype=np.int32)
+        assert np.array_equal(rank, want)
+
+
+@pytest.mark.parametrize("schedule", OS.SCHEDULES)
+@pytest.mark.parametrize("causal", [False, True])
+def test_predict_matches_oracle(schedule, causal):
+    rnd = random.Random(3)
+    for n, heads, slots in ((4, 3, 4), (8, 2, 8), (8, 5, 13), (16, 3, 40)):
+        if schedule == OS.SHIFT:
+            slots = max(slots, len(OS.units(schedule, n, causal)))
+        cost = (rnd.uniform(1, 3), rnd.uniform(0.5, 2), rnd.uniform(0.1, 1), rnd.uniform(0, 0.5))
+        got = D.schedule_predict(n, causal, schedule, heads, slots, cost)
+        want = OD.predict(schedule, n, causal, heads, slots, cost)
+        for g, w in zip(got, want):
+            assert abs(g - w) <= 1e-9 * max(1.0, abs(w)), (got, want)
+
+
+def test_predict_closed_forms():
+    c, r = 3.0, 1.0
+    for n in (2, 8, 32):
+        mk = D.schedule_predict(n, False, "naive", 1, n, (c, c, r, 0.0))[0]
+        assert mk == n * (c + r) + (n - 1) * r
+        mk = D.schedule_predict(n, False, "shift", 1, n, (c, c, r, 0.0))[0]
+        assert mk == n * (c + r)
+        mk = D.schedule_predict(n, True, "shift", 1, n // 2, (c, c, r, 0.0))[0]
+        assert mk == (n + 1) * (c + r)
+
+
+def test_predict_rejects_shift_without_resident_head():
+    with pytest.raises(D.DashError) as e:
+        D.schedule_predict(8, False, "shift", 2, 7, (1, 1, 1, 0))
+    assert e.value.code == 2
+
+
+def test_longest_path_and_cycle():
+    rnd = random.Random(9)
+    for _ in range(50):
+        n = rnd.randint(1, 20)
+        w = [float(rnd.randint(0, 7)) for _ in range(n)]
+        edges = [(u, v, float(rnd.randint(0, 3))) for u in range(n) for v in range(u + 1, n)
+                 if rnd.random() < 0.25]
+        s, f = D.dag_longest_path(w, edges)
+        s2, f2 = OD.longest_path(w, edges)
+        assert np.array_equal(s, np.array(s2)) and np.array_equal(f, np.array(f2))
+    with pytest.raises(D.DashError) as e:
+        D.dag_longest_path([1.0, 1.0], [(0, 1, 0.0), (1, 0, 0.0)])
+    assert e.value.code == 5
+
+
+def _desc(B=1, H=2, N=256, d=64, dtype=0, causal=0):
+    return _lib.Desc(B, H, N, d, dtype, causal, 0.0)
+
+
+FAKE = ctypes.c_void_p(0x100000)
+
+
+def test_argument_errors_without_launch():
+    lib = D.load()
+    size = ctypes.c_size_t(0)
+    assert lib.dash_attn_bwd_workspace_size(ctypes.byref(_desc()), 1, ctypes.byref(size)) == 0
+    assert size.value > 4 * 2 * 256 * 64
+    # same size for every schedule (schedules only reorder work)
+    for s in range(4):
+        sz = ctypes.c_size_t(0)
+        assert lib.dash_attn_bwd_workspace_size(ctypes.byref(_desc()), s, ctypes.byref(sz)) == 0
+        assert sz.value == size.value
+    bad = [
+        (_desc(d=96), 2), (_desc(N=200), 2), (_desc(dtype=1, N=192), 2), (_desc(B=0), 1),
+        (_desc(dtype=7), 1), (_desc(causal=2), 1),
+    ]
+    for desc, code in bad:
+        assert lib.dash_attn_bwd_workspace_size(ctypes.byref(desc), 1, ctypes.byref(size)) == code
+        assert lib.dash_attn_fwd(ctypes.byref(desc), FAKE, FAKE, FAKE, FAKE, FAKE, None) == code
+    assert lib.dash_attn_bwd_workspace_size(ctypes.byref(_desc()), 9, ctypes.byref(size)) == 1
+    assert lib.dash_attn_bwd_workspace_size(None, 1, ctypes.byref(size)) == 1
+    desc = _desc()
+    args = [FAKE] * 10
+    ws_ok = ctypes.c_size_t(size.value)
+    # null pointer
+    assert lib.dash_attn_bwd(ctypes.byref(desc), 1, None, *args[1:], ws_ok, None) == 1
+    # workspace too small, or misaligned
+    assert lib.dash_attn_bwd(ctypes.byref(desc), 1, *args, ctypes.c_size_t(size.value - 4), None) == 3
+    mis = args[:9] + [ctypes.c_void_p(0x100010)]
+    assert lib.dash_attn_bwd(ctypes.byref(desc), 1, *mis, ws_ok, None) == 3
+    # bad schedule enum
+    assert lib.dash_attn_bwd(ctypes.byref(desc), 4, *args, ws_ok, None) == 1
+    # debug struct required for the debug entry point; poison out of range
+    assert lib.dash_attn_bwd_debug(ctypes.byref(desc), 1, *args, ws_ok, None, None) == 1
+    dbg = _lib.Debug(0, 0, 10_000, None)
+    assert lib.dash_attn_bwd_debug(ctypes.byref(desc), 1, *args, ws_ok, ctypes.byref(dbg), None) == 1
+    # host-only argument checks
+    assert lib.dash_schedule_predict(0, 0, 1, 1, 1, None, None) == 1
+    assert lib.dash_litmus_ordered_add(0, 1, FAKE, FAKE, FAKE, FAKE, 0, None) == 1
+    assert lib.dash_attn_bwd_status(None, None) == 1
+    assert lib.dash_attn_tile(None) == 0 and lib.dash_attn_bwd_subtile(None) == 0
+    assert lib.dash_attn_tile(ctypes.byref(_desc(dtype=1, N=256))) == 128
+    assert lib.dash_attn_bwd_subtile(ctypes.byref(_desc(d=128))) == 32
