@@ -1,0 +1,223 @@
+#!/usr/bin/env python3
+"""Throughput of the deterministic attention backward on one MI355X.
+
+A step is one pass of the whole backward path over one batch of synthetic
+input already resident in HBM: the row term delta (preprocess), the
+workspace clear, the persistent backward kernel with the chosen schedule,
+and the dQ conversion.  O and LSE come from the library's forward before
+timing.  Default workload: B=1, H=32, N=16384, d=128, bf16, causal mask.
+
+Every schedule (atomic, naive, descending, shift) is timed the same way;
+`value` is the backward TFLOP/s of the primary deterministic schedule
+(descending for a causal mask, shift for a full mask), FLOPs counted as
+2.5x the forward's 4*B*H*N^2*d, halved for a causal mask.  Also reported:
+% of the dense bf16 MFMA peak, the deterministic / atomic throughput ratio
+per schedule, the backward kernel's own roofline figures (HIP events around
+its launch), and the fp64 CPU oracle timed on a bounded sample of heads.
+
+Prints one JSON line.  --gpus above 1 is refused: this path runs on one GPU.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "deterministic attn-bwd TFLOP/s + % bf16 MFMA peak; det/non-det throughput ratio"
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense MFMA (bf16), fp32 MFMA
+KERNEL_SOURCES = ["deterministic_attention_backward_attn_amd/csrc/kernels/attn_bwd.hip",
+                  "deterministic_attention_backward_attn_amd/csrc/kernels/common.hpp"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str):
+    """HBM bytes per launch from the committed rocprofv3 counter summary, or
+    None if absent or taken on a different kernel source."""
+    path = os.path.join(ROOT, "profiles", f"attn_bwd_{workload}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    m_sha = re.search(r"kernel_source_sha256:\s*([0-9a-f]+)", text)
+    m_b = re.search(r"traffic_bytes_per_launch:\s*([0-9.eE+]+)", text)
+    if not m_sha or not m_b or m_sha.group(1) != kernel_source_hash():
+        return None
+    return float(m_b.group(1))
+
+
+# ------------------------------------------------------------ CPU baseline
+
+def _oracle_head(args):
+    """Worker: fp64 oracle backward of one head (forward untimed first)."""
+    q, k, v, do, causal, scale = args
+    from threadpoolctl import threadpool_limits
+    from oracle import attention as A
+    with threadpool_limits(1):
+        o, lse = A._head_forward(q, k, v, causal, scale)
+        t0 = time.perf_counter()
+        A._head_backward(q, k, v, o, do, lse, causal, scale)
+        t1 = time.perf_counter()
+    return t1 - t0
+
+
+def cpu_baseline(exact, w, causal, max_workers):
+    import multiprocessing as mp
+    from concurrent.futures import ProcessPoolExecutor
+    import numpy as np
+    cores = max(1, min(len(os.sched_getaffinity(0)), max_workers, w.B * w.H))
+    scale = 1.0 / np.sqrt(w.d)
+    jobs = []
+    for i in range(cores):
+        b, h = divmod(i, w.H)
+        jobs.append((exact["q"][b, h], exact["k"][b, h], exact["v"][b, h], exact["do"][b, h],
+                     causal, scale))
+    with ProcessPoolExecutor(max_workers=cores, mp_context=mp.get_context("spawn")) as ex:
+        times = list(ex.map(_oracle_head, jobs))
+    per_head = w.flops_bwd(causal) / (w.B * w.H)
+    tflops = cores * per_head / max(times) / 1e12
+    return {"value": tflops, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
+            "sample": f"{cores} of {w.B * w.H} heads, one per process (1 BLAS thread each), "
+                      f"fp64 backward given the oracle's own O/LSE; time = slowest head "
+                      f"({max(times):.1f} s)"}
+
+
+# ------------------------------------------------------------------ main
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="b1h32_n16k_d128_causal")
+    ap.add_argument("--mask", choices=["causal", "full"], default=None,
+                    help="mask (default: the workload's first)")
+    ap.add_argument("--schedules", default="atomic,naive,descending,shift")
+    ap.add_argument("--primary", default=None, help="schedule reported as value")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-workers", type=int, default=16)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py: this backward runs on one GPU; --gpus {args.gpus} is not supported "
+              "(heads shard across GPUs with no exchange; see the design notes)",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    import deterministic_attention_backward_attn_amd as D
+    from synth import WORKLOADS, make_workload_inputs
+
+    D.load()  # fails loudly if the library is missing
+    if not torch.cuda.is_available():
+        print("bench.py: no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    w = WORKLOADS[args.workload]
+    mask = args.mask or w.masks[0]
+    causal = mask == "causal"
+    scheds = [s for s in args.schedules.split(",") if s]
+    primary = args.primary or ("descending" if causal else "shift")
+    if primary not in scheds:
+        scheds.append(primary)
+
+    t_gen = time.perf_counter()
+    raw = make_workload_inputs(w)
+    if w.dtype == "bf16":
+        dev = {k: torch.from_numpy(v[0].view(np.int16)).view(torch.bfloat16).cuda()
+               for k, v in raw.items()}
+    else:
+        dev = {k: torch.from_numpy(v[0]).cuda() for k, v in raw.items()}
+    exact = {k: v[1] for k, v in raw.items()} if not args.no_cpu_baseline else None
+    del raw
+    t_gen = time.perf_counter() - t_gen
+    print(f"[bench] {w.name} {mask}: inputs ready in {t_gen:.1f}s", file=sys.stderr, flush=True)
+
+    o, lse = D.attn_fwd(dev["q"], dev["k"], dev["v"], causal=causal)
+    delta = torch.empty_like(lse)
+    dq, dk, dv = (torch.empty_like(dev["q"]) for _ in range(3))
+    ws = D.alloc_workspace(dev["q"], causal, primary)
+    flops = w.flops_bwd(causal)
+
+    def step(sched, events=None):
+        D.attn_bwd_preprocess(o, dev["do"], out=delta)
+        D.attn_bwd(dev["q"], dev["k"], dev["v"], dev["do"], lse, delta, schedule=sched,
+                   causal=causal, workspace=ws, out=(dq, dk, dv),
+                   debug=None if events is None else {"kernel_events": events})
+
+    results = {}
+    for sched in scheds:
+        for _ in range(args.warmup):
+            step(sched)
+        torch.cuda.synchronize()
+        kev = []
+        for _ in range(args.steps):
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            a.record()
+            b.record()
+            kev.append((a, b))
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for i in range(args.steps):
+            step(sched, (kev[i][0].cuda_event, kev[i][1].cuda_event))
+        t1.record()
+        torch.cuda.synchronize()
+        D.attn_bwd_status(ws)
+        ms = t0.elapsed_time(t1) / args.steps
+        kms = sum(a.elapsed_time(b) for a, b in kev) / args.steps
+        results[sched] = {"ms_per_step": ms, "tflops": flops / ms / 1e9,
+                          "kernel_ms": kms, "kernel_tflops": flops / kms / 1e9}
+        print(f"[bench] {sched:10s} step {ms:8.3f} ms  {flops / ms / 1e9:7.1f} TFLOP/s   "
+              f"kernel {kms:8.3f} ms  {flops / kms / 1e9:7.1f} TFLOP/s", file=sys.stderr,
+              flush=True)
+
+    peak = PEAK_TFLOPS[w.dtype]
+    prim = results[primary]
+    out = {
+        "metric": METRIC,
+        "value": round(prim["tflops"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(prim["ms_per_step"], 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic: i.i.d. N(0,1) Q/K/V/dO from PCG64 seeds, O/LSE from the library's forward",
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "mask": mask,
+                   "schedule": primary, "parallelism": "single GPU"},
+        "pct_peak": round(100.0 * prim["tflops"] / peak, 2),
+        "det_nondet_ratio": ({s: round(r["tflops"] / results["atomic"]["tflops"], 4)
+                              for s, r in results.items() if s != "atomic"}
+                             if "atomic" in results else None),
+        "schedules": {s: {k: round(v, 4) for k, v in r.items()} for s, r in results.items()},
+    }
+    achieved = flops / (prim["kernel_ms"] * 1e-3) / 1e12
+    out["roofline"] = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
+                       "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
+                       "traffic": read_traffic(w.name),
+                       "kernel": f"bwd_kernel ({primary})"}
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a sample of heads", file=sys.stderr, flush=True)
+        out["cpu_baseline"] = cpu_baseline(exact, w, causal, args.cpu_workers)
+    else:
+        out["cpu_baseline"] = None
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

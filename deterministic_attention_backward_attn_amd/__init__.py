@@ -111,13 +111,18 @@ def attn_fwd(q, k, v, causal: bool = False, scale=None, stream=None):
     return o, lse
 
 
-def attn_bwd_preprocess(o, do, stream=None):
-    """delta = rowsum(dO * O) in float32 [B, H, N]."""
+def attn_bwd_preprocess(o, do, out=None, stream=None):
+    """delta = rowsum(dO * O) in float32 [B, H, N] (written to `out` if given)."""
     torch = _torch()
     lib = load()
     _same_shape(o, do)
     desc = _desc_from(o, False, None)
-    delta = torch.empty(o.shape[:3], dtype=torch.float32, device=o.device)
+    if out is None:
+        delta = torch.empty(o.shape[:3], dtype=torch.float32, device=o.device)
+    else:
+        delta = out
+        if delta.dtype != torch.float32 or tuple(delta.shape) != tuple(o.shape[:3]):
+            raise ValueError("out must be float32 [B, H, N]")
     check(lib.dash_attn_bwd_preprocess(ctypes.byref(desc), _ptr(o), _ptr(do), _ptr(delta),
                                        _stream(stream)), "dash_attn_bwd_preprocess")
     return delta
@@ -145,7 +150,8 @@ def attn_bwd(q, k, v, do, lse, delta, *, schedule="naive", causal=False, scale=N
     """Returns (dq, dk, dv).  `workspace`: uint8 GPU tensor of at least
     attn_bwd_workspace_size bytes (allocated if None).  `out`: optional
     preallocated (dq, dk, dv).  `debug`: optional dict with keys spin_limit,
-    jitter_seed, poison_q (1-based, 0 = off), partials (float32 tensor)."""
+    jitter_seed, poison_q (1-based, 0 = off), partials (float32 tensor),
+    kernel_events (two raw hipEvent_t handles)."""
     torch = _torch()
     lib = load()
     _same_shape(q, k, v, do)
@@ -169,6 +175,10 @@ def attn_bwd(q, k, v, do, lse, delta, *, schedule="naive", causal=False, scale=N
         dbg = Debug(int(debug.get("spin_limit", 0)), int(debug.get("jitter_seed", 0)),
                     int(debug.get("poison_q", 0)),
                     _ptr(debug["partials"]) if debug.get("partials") is not None else None)
+        ev = debug.get("kernel_events")
+        if ev is not None:
+            dbg.kernel_events[0] = ctypes.c_void_p(int(ev[0]))
+            dbg.kernel_events[1] = ctypes.c_void_p(int(ev[1]))
         check(lib.dash_attn_bwd_debug(*args, ctypes.byref(dbg), _stream(stream)),
               "dash_attn_bwd_debug")
     return dq, dk, dv

@@ -9,7 +9,7 @@
 #include <tuple>
 #include <vector>
 
-#include "../../../include/dash_attn.h"
+#include "dash_attn.h"
 #include "../kernels/launch.hpp"
 #include "dag.hpp"
 #include "schedule.hpp"
@@ -37,7 +37,9 @@ dash_status check_desc(const dash_attn_desc* d) {
   if (d->N % tile) return DASH_ERR_UNSUPPORTED;
   // row indices (head * N + row) and unit counts are 32-bit on the device
   const long long heads = (long long)d->B * d->H;
-  if (heads * d->N >= (1LL << 31) || d->N / tile > 32767) return DASH_ERR_UNSUPPORTED;
+  // and offsets within one head (row * d + col) are 32-bit
+  if (heads * d->N >= (1LL << 31) || d->N / tile > 32767 || (long long)d->N * d->d >= (1LL << 31))
+    return DASH_ERR_UNSUPPORTED;
   return DASH_OK;
 }
 
@@ -49,13 +51,15 @@ struct WsLayout {
   size_t counters_off, counters_words, acc_off, total;
 };
 
+// [0, 256): header (status word, work counter); then the order counters
+// [BH, N/BR, waves]; then the fp32 dQ accumulator [BH, N, d].
 WsLayout layout(const dash_attn_desc* d) {
   int bc = 0, br = 0;
   dash::bwd_tiles(d->dtype, d->d, &bc, &br);
   WsLayout w;
   const size_t heads = (size_t)d->B * d->H;
   w.counters_off = kHeaderBytes;
-  w.counters_words = heads * (size_t)(d->N / br);
+  w.counters_words = heads * (size_t)(d->N / br) * dash::bwd_waves(d->dtype, d->d);
   w.acc_off = align256(w.counters_off + 4 * w.counters_words);
   w.total = w.acc_off + 4 * heads * (size_t)d->N * d->d;
   return w;
@@ -86,9 +90,16 @@ dash_status get_tables(int dev, int n, bool causal, Sched s, const DevTables** o
   if (dash::validate_tables(dt.host)[0] != '\0') return DASH_ERR_SCHEDULE_INVALID;
   const Tables& t = dt.host;
   std::vector<int2> items(t.items());
+  std::vector<int> contributors(n, 0);
+  for (int i = 0; i < t.items(); ++i) ++contributors[t.q[i]];
   for (int i = 0; i < t.items(); ++i) {
     items[i].x = t.kv[i] | (t.q[i] << 16);
-    items[i].y = t.ordered() ? t.rank[(size_t)t.q[i] * n + t.kv[i]] : 0;
+    if (t.ordered()) {
+      const int r = t.rank[(size_t)t.q[i] * n + t.kv[i]];
+      items[i].y = r | ((r == contributors[t.q[i]] - 1) ? (1 << 30) : 0);
+    } else {
+      items[i].y = 0;
+    }
   }
   if (hipMalloc(&dt.d_unit_off, sizeof(int) * t.unit_off.size()) != hipSuccess) return DASH_ERR_HIP;
   if (hipMalloc(&dt.d_items, sizeof(int2) * (items.empty() ? 1 : items.size())) != hipSuccess) {
@@ -169,7 +180,10 @@ dash_status run_bwd(const dash_attn_desc* desc, dash_schedule schedule, const vo
 
   hipStream_t strm = (hipStream_t)stream;
   char* ws = (char*)workspace;
-  if (dash::launch_zero_u32((uint32_t*)ws, w.total / 4, strm) != hipSuccess) return DASH_ERR_HIP;
+  // ordered schedules never read an accumulator element before its first
+  // contributor wrote it, so only the header and counters need clearing
+  const size_t clear_bytes = ordered ? w.acc_off : w.total;
+  if (dash::launch_zero_u32((uint32_t*)ws, clear_bytes / 4, strm) != hipSuccess) return DASH_ERR_HIP;
 
   dash::BwdArgs a;
   a.q = q;
@@ -178,6 +192,7 @@ dash_status run_bwd(const dash_attn_desc* desc, dash_schedule schedule, const vo
   a.dout = dout;
   a.lse = lse;
   a.delta = delta;
+  a.dq = dq;
   a.dk = dk;
   a.dv = dv;
   a.dq_accum = (float*)(ws + w.acc_off);
@@ -197,11 +212,18 @@ dash_status run_bwd(const dash_attn_desc* desc, dash_schedule schedule, const vo
   a.jitter_seed = dbg ? dbg->jitter_seed : 0u;
   a.poison_q = dbg ? dbg->poison_q - 1 : -1;
   a.partials = dbg ? dbg->partials : nullptr;
+  hipEvent_t ev0 = dbg ? (hipEvent_t)dbg->kernel_events[0] : nullptr;
+  hipEvent_t ev1 = dbg ? (hipEvent_t)dbg->kernel_events[1] : nullptr;
+  if (ev0 && hipEventRecord(ev0, strm) != hipSuccess) return DASH_ERR_HIP;
   if (dash::launch_bwd(desc->dtype, desc->d, causal, ordered, a, grid, strm) != hipSuccess)
     return DASH_ERR_HIP;
-  const size_t elems = (size_t)heads * desc->N * desc->d;
-  if (dash::launch_dq_convert(desc->dtype, a.dq_accum, dq, a.scale, elems, strm) != hipSuccess)
-    return DASH_ERR_HIP;
+  if (ev1 && hipEventRecord(ev1, strm) != hipSuccess) return DASH_ERR_HIP;
+  if (!ordered) {
+    // the atomic schedule accumulates everything first, then scales/converts
+    const size_t elems = (size_t)heads * desc->N * desc->d;
+    if (dash::launch_dq_convert(desc->dtype, a.dq_accum, dq, a.scale, elems, strm) != hipSuccess)
+      return DASH_ERR_HIP;
+  }
   return DASH_OK;
 }
 

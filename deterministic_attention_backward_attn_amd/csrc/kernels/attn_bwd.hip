@@ -12,11 +12,21 @@
 //   dS  = P (dP - delta)
 //   dV += P^T dO ; dK += dS^T Q  (MFMA, accumulators in registers)
 //   dQ_part = dS K             (MFMA, dS staged through LDS)
-// and adds dQ_part into the fp32 accumulator of that Q sub-tile.  With an
-// ordered schedule the add waits until the sub-tile's counter equals this
-// tile's rank in the dQ order and then advances the counter, so the adds
-// happen in one fixed order (explainer section 1: fixed accumulation order
-// for dQ); with the atomic schedule the adds are unordered.
+// and adds dQ_part into the fp32 accumulator of that Q sub-tile.
+//
+// Ordered schedules add in a fixed order (explainer section 1: a fixed
+// accumulation order for dQ): each wave owns the same dQ output columns in
+// every workgroup, so wave w of the contributor ranked r waits until the
+// sub-tile's counter for wave w reads r, reads the accumulator, adds its
+// partial, writes it back and sets the counter to r + 1.  The first
+// contributor writes without reading; the last one writes the final,
+// scaled dQ in the output dtype instead of the accumulator.  The accumulator
+// and counters are accessed with device-coherent loads and stores (the
+// cache policy of device-scope atomics), and a wave's stores complete before
+// it advances the counter, so no cache-wide write-back or invalidation is
+// needed.  The add for sub-tile g runs during sub-tile g+1's products, so its
+// memory latency hides behind MFMA work.  The atomic schedule adds with
+// unordered fp32 atomics instead (non-deterministic reference).
 //
 // The workgroups form a persistent grid: each takes units (work lists from
 // the schedule tables) either from a device work counter in increasing
@@ -25,16 +35,50 @@
 // head, all of which are then resident).
 //
 // Operand placement (see common.hpp for the MFMA layouts):
-//   S and dP are computed as (Q-rows x KV-cols), so the accumulators hold
-//   KV on lanes and Q rows in registers; reused directly as the A operand
-//   of dV += P^T dO and dK += dS^T Q, whose B operands (dO, Q with Q rows
-//   in the K slots) come from transposed LDS copies sdOt and sQt.
-//   dQ = dS K needs dS with Q rows on lanes: dS goes through LDS (sdS),
-//   K through a transposed LDS copy sKt written once per KV tile.
+//   S and dP are computed as (Q-rows x KV-cols): the accumulators hold KV on
+//   lanes and Q rows in registers and serve directly as the A operand of
+//   dV += P^T dO and dK += dS^T Q.  Those products need dO and Q with Q rows
+//   in the K slots; bf16 reads them from the row-major LDS tiles with the
+//   transposing LDS read (ds_read_b64_tr_b16), fp32 with element reads.
+//   dQ = dS K needs dS with Q rows on lanes: dS goes to LDS as dS^T
+//   ([kv][q], 8-byte writes) and comes back through the transposing read;
+//   K^T fragments (d on lanes) are built once per KV tile the same way.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace dash {
+
+// Transposing LDS read of 4 bf16: within each 16-lane group, lane j supplies
+// the address of 4 consecutive elements of row (base_row + j/4), columns
+// (base_col + 4*(j%4) .. +3); lane i receives column base_col + i of rows
+// base_row .. base_row + 3.
+__device__ __forceinline__ u16x4 lds_tr16(const bf16_t* p) {
+  typedef short v4s __attribute__((ext_vector_type(4)));
+  const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      (__attribute__((address_space(3))) v4s*)(p));
+  return __builtin_bit_cast(u16x4, r);
+}
+
+// Fragment whose 8 K slots are rows r0+{0..3} and r1+{0..3} of column
+// c0 + (lane's index in its 16-lane half-column group) of a row-major LDS
+// array with row stride `ld`; c0 already includes 16*(group%2).
+__device__ __forceinline__ bf16x8 tr_frag(const bf16_t* base, int ld, int r0, int r1, int c0,
+                                          int j) {
+  const u16x4 a = lds_tr16(base + (r0 + (j >> 2)) * ld + c0 + 4 * (j & 3));
+  const u16x4 b = lds_tr16(base + (r1 + (j >> 2)) * ld + c0 + 4 * (j & 3));
+  u16x8 u;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    u[s] = a[s];
+    u[s + 4] = b[s];
+  }
+  return __builtin_bit_cast(bf16x8, u);
+}
+
+__device__ __forceinline__ void wait_vm_stores() {
+  // s_waitcnt vmcnt(0): this wave's vector memory operations have completed
+  __builtin_amdgcn_s_waitcnt(0x0F70);
+}
 
 template <typename T, int D, int BC, int BR, bool CAUSAL, bool ORDERED>
 __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
@@ -47,26 +91,28 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
   constexpr int KSTEP = E::KSTEP;
   constexpr int VEC = E::VEC;          // elements per 16-byte access
   constexpr int DK = D / KSTEP;        // MFMA steps over d
+  constexpr int KK = BC / KSTEP;       // MFMA steps over a KV tile
   constexpr int MT = BR / 32;          // 32-row tiles of a Q sub-tile
   constexpr int NTD = D / 32;          // 32-column tiles over d
   constexpr int PAD = 16 / (int)sizeof(T);
-  constexpr int LQ = D + PAD;          // row stride of sQ, sdO  ([q][d])
-  constexpr int LQT = BR + PAD;        // row stride of sQt, sdOt ([d][q])
-  constexpr int LS = BC + PAD;         // row stride of sdS ([q][kv]) and sKt ([d][kv])
+  constexpr int LQ = D + PAD;          // row stride of sQ, sdO, sK ([row][d])
+  constexpr int LS = BR + PAD;         // row stride of sdSt ([kv][q])
   constexpr int CPT = BR * D / VEC / NT;  // 16-byte chunks per thread per tensor
-  constexpr int QTILES = MT * NTD;     // dQ output tiles per sub-tile
-  constexpr int TPW = QTILES / NW;     // dQ tiles per wave
+  // dQ output tiles of a wave: CPW column tiles x RPW row tiles
+  constexpr int CPW = NTD >= NW ? NTD / NW : 1;
+  constexpr int WPC = NW > NTD ? NW / NTD : 1;  // waves sharing a column tile
+  constexpr int RPW = MT / WPC;
+  constexpr int QT = CPW * RPW;
   static_assert(BC % BR == 0 && BR % 32 == 0 && D % 32 == 0, "tile shape");
-  static_assert(QTILES % NW == 0, "dQ tiles must split evenly over waves");
+  static_assert(NTD % NW == 0 || NW % NTD == 0, "dQ columns must split over waves");
+  static_assert(MT % WPC == 0, "dQ rows must split over waves");
   static_assert(CPT * VEC * NT == BR * D, "sub-tile load must split evenly");
   static_assert(NT >= 2 * BR, "LSE/delta staging needs 2*BR threads");
 
   __shared__ __align__(16) T sQ[BR * LQ];
   __shared__ __align__(16) T sdO[BR * LQ];
-  __shared__ __align__(16) T sQt[D * LQT];
-  __shared__ __align__(16) T sdOt[D * LQT];
-  __shared__ __align__(16) T sdS[BR * LS];
-  __shared__ __align__(16) T sKt[D * LS];
+  __shared__ __align__(16) T sdSt[BC * LS];
+  __shared__ __align__(16) T sK[BC * LQ];
   __shared__ float sLSE[BR];
   __shared__ float sDel[BR];
   __shared__ int sUnit;
@@ -76,10 +122,15 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
   const int w = tid >> 6;
   const int l32 = lane & 31;
   const int hh = lane >> 5;
+  const int grp = lane >> 4;           // 16-lane group
+  const int j16 = lane & 15;
+  const int gcol = 16 * (grp & 1);     // column offset of this lane's group
   const int N = a.N;
   const int n_sub = N / BR;
   uint32_t* status = a.header;
   const uint32_t spin_limit = a.spin_limit;
+  const int col0 = w % NTD;            // first dQ column tile of this wave
+  const int row0 = NW > NTD ? w / NTD : 0;
 
   if (a.dynamic == 0 && (int)blockIdx.x >= a.p_eff) return;
   int unit = blockIdx.x;
@@ -94,15 +145,24 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
     const T* dOg = reinterpret_cast<const T*>(a.dout) + hoff;
     const float* lse_g = a.lse + (size_t)head * N;
     const float* del_g = a.delta + (size_t)head * N;
+    float* dqa = a.dq_accum + hoff;
+    T* dqo = reinterpret_cast<T*>(a.dq) + hoff;
+    uint32_t* cnt_h = a.counters + (size_t)head * n_sub * NW;
     const int it0 = a.unit_off[lu];
     const int it1 = a.unit_off[lu + 1];
     const int n_steps = (it1 - it0) * RHO;
 
     frag Kreg[DK], Vreg[DK];
+    frag KT[CPW][KK];
     f32x16 accdK[NTD], accdV[NTD];
     int cur_kv = -1;
 
-    // prefetch registers for the next Q sub-tile
+    // deferred ordered add: partial of the previous sub-tile
+    f32x16 accQp[QT];
+    int p_qtile = -1, p_rank = 0, p_flags = 0;  // flags: bit0 last
+    bool rel_pending = false;                    // stores issued, counter not yet advanced
+    int rel_qtile = 0, rel_rank = 0;
+
     uint4 pq[CPT], pdo[CPT];
     float pstat = 0.f;
     auto fetch = [&](int g) {
@@ -114,8 +174,9 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
         const int c = tid + i * NT;
         const int row = c / (D / VEC);
         const int col = (c % (D / VEC)) * VEC;
-        pq[i] = *reinterpret_cast<const uint4*>(Qg + (size_t)(q0 + row) * D + col);
-        pdo[i] = *reinterpret_cast<const uint4*>(dOg + (size_t)(q0 + row) * D + col);
+        const uint32_t off = (uint32_t)((q0 + row) * D + col);
+        pq[i] = *reinterpret_cast<const uint4*>(Qg + off);
+        pdo[i] = *reinterpret_cast<const uint4*>(dOg + off);
       }
       if (tid < BR) pstat = lse_g[q0 + tid] * kLog2e;
       else if (tid < 2 * BR) pstat = del_g[q0 + tid - BR];
@@ -128,11 +189,73 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
       for (int nt = 0; nt < NTD; ++nt) {
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
-          const int row = cur_kv * BC + 32 * w + crow(r, hh);
-          const int col = nt * 32 + l32;
-          dKg[(size_t)row * D + col] = E::from_f32(accdK[nt][r] * a.scale);
-          dVg[(size_t)row * D + col] = E::from_f32(accdV[nt][r]);
+          const uint32_t off = (uint32_t)((cur_kv * BC + 32 * w + crow(r, hh)) * D + nt * 32 + l32);
+          dKg[off] = E::from_f32(accdK[nt][r] * a.scale);
+          dVg[off] = E::from_f32(accdV[nt][r]);
         }
+      }
+    };
+
+    // this wave's counter for a Q sub-tile
+    auto counter = [&](int qtile) { return cnt_h + (size_t)qtile * NW + w; };
+
+    // Ordered add of the deferred partial: wait for this wave's turn, read
+    // the accumulator (unless first), add, write back or write final dQ.
+    auto ordered_add = [&]() {
+      const int rank = p_rank;
+      const bool last = (p_flags & 1) != 0;
+      const int q0 = p_qtile * BR;
+      if (lane == 0) {
+        if (a.jitter_seed != 0u) {
+          const uint32_t nap =
+              hash32(a.jitter_seed ^ (uint32_t)(head * 7919 + p_qtile * 131 + cur_kv * 17 + w)) & 31u;
+          for (uint32_t i = 0; i < nap; ++i) __builtin_amdgcn_s_sleep(8);
+        }
+        const bool poisoned = a.poison_q >= 0 && head == 0 && p_qtile == a.poison_q && rank == 0;
+        if (poisoned) wait_counter(counter(p_qtile), 0xFFFFFFFFu, status, spin_limit);
+        else if (rank > 0) wait_counter(counter(p_qtile), (uint32_t)rank, status, spin_limit);
+      }
+      __builtin_amdgcn_wave_barrier();
+#pragma unroll
+      for (int i = 0; i < QT; ++i) {
+        const int nt = col0 + (i / RPW) * NW;
+        const int mt = row0 + (i % RPW) * WPC;
+        const int col = nt * 32 + l32;
+        if (rank > 0) {
+          float prev[16];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const uint32_t off = (uint32_t)((q0 + mt * 32 + crow(r, hh)) * D + col);
+            prev[r] = __hip_atomic_load(&dqa[off], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+          }
+#pragma unroll
+          for (int r = 0; r < 16; ++r) accQp[i][r] = prev[r] + accQp[i][r];
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const uint32_t off = (uint32_t)((q0 + mt * 32 + crow(r, hh)) * D + col);
+          if (last)
+            dqo[off] = E::from_f32(accQp[i][r] * a.scale);
+          else
+            __hip_atomic_store(&dqa[off], accQp[i][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+      }
+      if (!last) {
+        rel_pending = true;
+        rel_qtile = p_qtile;
+        rel_rank = rank;
+      }
+      p_qtile = -1;
+    };
+
+    // Advance the counter of the last ordered add once its stores completed.
+    auto release = [&]() {
+      if (rel_pending) {
+        wait_vm_stores();
+        if (lane == 0)
+          __hip_atomic_store(counter(rel_qtile), (uint32_t)rel_rank + 1u, __ATOMIC_RELAXED,
+                             __HIP_MEMORY_SCOPE_AGENT);
+        rel_pending = false;
       }
     };
 
@@ -142,7 +265,8 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
       const int2 itm = a.items[it0 + g / RHO];
       const int kv = itm.x & 0xFFFF;
       const int qblk = itm.x >> 16;
-      const int rank = itm.y;
+      const int rank = itm.y & 0xFFFF;
+      const int flags = (itm.y >> 30) & 1;
       const int rsub = g % RHO;
       const int qtile = qblk * RHO + rsub;
       const int q0 = qtile * BR;
@@ -151,22 +275,32 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
         if (cur_kv >= 0) flush_dkdv();
         cur_kv = kv;
         const int kv0 = kv * BC;
-        // K, V as B operands (KV rows on lanes, d in the K slots)
 #pragma unroll
         for (int ks = 0; ks < DK; ++ks) {
-          const size_t off = (size_t)(kv0 + 32 * w + l32) * D + ks * KSTEP + hh * KPL;
+          const uint32_t off = (uint32_t)((kv0 + 32 * w + l32) * D + ks * KSTEP + hh * KPL);
           Kreg[ks] = load_frag(Kg + off);
           Vreg[ks] = load_frag(Vg + off);
         }
-        // K^T into LDS for the dQ product (previous readers passed the
-        // barrier that ended the last sub-tile)
+        // K tile row-major into LDS, then K^T fragments (d on lanes) for dQ.
+        // sK's previous readers finished before several barriers since.
         for (int c = tid; c < BC * D / VEC; c += NT) {
           const int row = c / (D / VEC);
           const int col = (c % (D / VEC)) * VEC;
-          const uint4 raw = *reinterpret_cast<const uint4*>(Kg + (size_t)(kv0 + row) * D + col);
-          const T* e = reinterpret_cast<const T*>(&raw);
+          *reinterpret_cast<uint4*>(&sK[row * LQ + col]) =
+              *reinterpret_cast<const uint4*>(Kg + (uint32_t)((kv0 + row) * D + col));
+        }
+        __syncthreads();
 #pragma unroll
-          for (int j = 0; j < VEC; ++j) sKt[(col + j) * LS + row] = e[j];
+        for (int cc = 0; cc < CPW; ++cc) {
+          const int nt = col0 + cc * NW;
+#pragma unroll
+          for (int ks = 0; ks < KK; ++ks) {
+            if constexpr (KPL == 8) {
+              KT[cc][ks] = tr_frag(sK, LQ, ks * 16 + 8 * hh, ks * 16 + 8 * hh + 4, nt * 32 + gcol, j16);
+            } else {
+              KT[cc][ks] = load_frag(&sK[(ks * 2 + hh) * LQ + nt * 32 + l32]);
+            }
+          }
         }
 #pragma unroll
         for (int nt = 0; nt < NTD; ++nt) {
@@ -175,7 +309,11 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
         }
       }
 
-      // stage the prefetched Q / dO sub-tile (row-major and transposed)
+      // previous ordered add's stores are complete -> advance its counter;
+      // the prefetched loads are complete too
+      if constexpr (ORDERED) release();
+
+      // stage the prefetched Q / dO sub-tile, row-major
 #pragma unroll
       for (int i = 0; i < CPT; ++i) {
         const int c = tid + i * NT;
@@ -183,13 +321,6 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
         const int col = (c % (D / VEC)) * VEC;
         *reinterpret_cast<uint4*>(&sQ[row * LQ + col]) = pq[i];
         *reinterpret_cast<uint4*>(&sdO[row * LQ + col]) = pdo[i];
-        const T* eq = reinterpret_cast<const T*>(&pq[i]);
-        const T* ed = reinterpret_cast<const T*>(&pdo[i]);
-#pragma unroll
-        for (int j = 0; j < VEC; ++j) {
-          sQt[(col + j) * LQT + row] = eq[j];
-          sdOt[(col + j) * LQT + row] = ed[j];
-        }
       }
       if (tid < BR) sLSE[tid] = pstat;
       else if (tid < 2 * BR) sDel[tid - BR] = pstat;
@@ -214,20 +345,45 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
         }
       }
 
-      // P and dS, in place (accS <- P, accP <- dS)
-      const bool diag = CAUSAL && (qblk == kv);
+      // P and dS; dS^T to LDS.  bf16: P and dS are packed once (hardware
+      // RNE conversion) and the packed words serve both the LDS write and the
+      // MFMA A operands.  fp32: P and dS stay in place (accS <- P, accP <- dS).
+      const bool diag = CAUSAL && (qblk == kv);   // uniform across the workgroup
       const int kvl = 32 * w + l32;
+      uint32_t pw[MT][8], dw[MT][8];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int ql = mt * 32 + crow(r, hh);
-          float p = __builtin_amdgcn_exp2f(accS[mt][r] * a.scale_log2 - sLSE[ql]);
-          if (diag && kvl > rsub * BR + ql) p = 0.f;
-          const float ds = p * (accP[mt][r] - sDel[ql]);
-          accS[mt][r] = p;
-          accP[mt][r] = ds;
-          sdS[ql * LS + kvl] = E::from_f32(ds);
+        for (int gq = 0; gq < 4; ++gq) {
+          const int qb = mt * 32 + 8 * gq + 4 * hh;  // 4 consecutive Q rows
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sLSE[qb]);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sDel[qb]);
+          float p[4], ds[4];
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            p[e] = __builtin_amdgcn_exp2f(accS[mt][4 * gq + e] * a.scale_log2 - l4[e]);
+          if (diag) {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)
+              if (kvl > rsub * BR + qb + e) p[e] = 0.f;
+          }
+#pragma unroll
+          for (int e = 0; e < 4; ++e) ds[e] = p[e] * (accP[mt][4 * gq + e] - d4[e]);
+          if constexpr (KPL == 8) {
+            pw[mt][2 * gq] = pack2_bf16(p[0], p[1]);
+            pw[mt][2 * gq + 1] = pack2_bf16(p[2], p[3]);
+            dw[mt][2 * gq] = pack2_bf16(ds[0], ds[1]);
+            dw[mt][2 * gq + 1] = pack2_bf16(ds[2], ds[3]);
+            *reinterpret_cast<uint2*>(&sdSt[kvl * LS + qb]) =
+                make_uint2(dw[mt][2 * gq], dw[mt][2 * gq + 1]);
+          } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              accS[mt][4 * gq + e] = p[e];
+              accP[mt][4 * gq + e] = ds[e];
+            }
+            *reinterpret_cast<f32x4*>(&sdSt[kvl * LS + qb]) = f32x4{ds[0], ds[1], ds[2], ds[3]};
+          }
         }
       }
 
@@ -239,117 +395,98 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
         const int cc = c % CPM;
         frag pa, da;
         if constexpr (KPL == 8) {
-          float tp[8], td[8];
-#pragma unroll
-          for (int s = 0; s < 8; ++s) {
-            tp[s] = accS[mt][8 * cc + s];
-            td[s] = accP[mt][8 * cc + s];
-          }
-          pa = pack_bf16x8(tp);
-          da = pack_bf16x8(td);
+          pa = __builtin_bit_cast(bf16x8, make_uint4(pw[mt][4 * cc], pw[mt][4 * cc + 1],
+                                                     pw[mt][4 * cc + 2], pw[mt][4 * cc + 3]));
+          da = __builtin_bit_cast(bf16x8, make_uint4(dw[mt][4 * cc], dw[mt][4 * cc + 1],
+                                                     dw[mt][4 * cc + 2], dw[mt][4 * cc + 3]));
         } else {
           pa = accS[mt][cc];
           da = accP[mt][cc];
         }
 #pragma unroll
         for (int nt = 0; nt < NTD; ++nt) {
-          const int dcol = nt * 32 + l32;
           frag bo, bq;
           if constexpr (KPL == 8) {
-            // rows crow(8cc+s, hh): 16cc + 4hh + {0..3} and 16cc + 8 + 4hh + {0..3}
-            const int base = dcol * LQT + mt * 32 + 16 * cc + 4 * hh;
-            u16x8 uo, uq;
-            const u16x4 o0 = *reinterpret_cast<const u16x4*>(&sdOt[base]);
-            const u16x4 o1 = *reinterpret_cast<const u16x4*>(&sdOt[base + 8]);
-            const u16x4 q0v = *reinterpret_cast<const u16x4*>(&sQt[base]);
-            const u16x4 q1v = *reinterpret_cast<const u16x4*>(&sQt[base + 8]);
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-              uo[s] = o0[s];
-              uo[s + 4] = o1[s];
-              uq[s] = q0v[s];
-              uq[s + 4] = q1v[s];
-            }
-            bo = __builtin_bit_cast(bf16x8, uo);
-            bq = __builtin_bit_cast(bf16x8, uq);
+            // K slots: Q rows r0+{0..3}, r0+8+{0..3}, r0 = mt*32 + 16cc + 4h
+            const int r0 = mt * 32 + 16 * cc + 4 * hh;
+            bo = tr_frag(sdO, LQ, r0, r0 + 8, nt * 32 + gcol, j16);
+            bq = tr_frag(sQ, LQ, r0, r0 + 8, nt * 32 + gcol, j16);
           } else {
             const int qrow = mt * 32 + crow(cc, hh);
-            bo = load_frag(&sdOt[dcol * LQT + qrow]);
-            bq = load_frag(&sQt[dcol * LQT + qrow]);
+            bo = load_frag(&sdO[qrow * LQ + nt * 32 + l32]);
+            bq = load_frag(&sQ[qrow * LQ + nt * 32 + l32]);
           }
           accdV[nt] = E::mma(pa, bo, accdV[nt]);
           accdK[nt] = E::mma(da, bq, accdK[nt]);
         }
       }
-      __syncthreads();  // sdS complete
+
+      // the previous sub-tile's ordered add, behind this sub-tile's products
+      if constexpr (ORDERED) {
+        if (p_qtile >= 0) ordered_add();
+      }
+      __syncthreads();  // sdSt complete
 
       // dQ_part = dS K for this wave's output tiles
-      f32x16 accQ[TPW];
+      f32x16 accQ[QT];
 #pragma unroll
-      for (int i = 0; i < TPW; ++i) {
-        const int t = w + i * NW;
-        const int mt = t / NTD;
-        const int nt = t % NTD;
+      for (int i = 0; i < QT; ++i) {
+        const int cc = i / RPW;
+        const int mt = row0 + (i % RPW) * WPC;
         f32x16 acc = zero16();
 #pragma unroll
-        for (int ks = 0; ks < BC / KSTEP; ++ks) {
-          const frag fa = load_frag(&sdS[(mt * 32 + l32) * LS + ks * KSTEP + hh * KPL]);
-          const frag fb = load_frag(&sKt[(nt * 32 + l32) * LS + ks * KSTEP + hh * KPL]);
-          acc = E::mma(fa, fb, acc);
+        for (int ks = 0; ks < KK; ++ks) {
+          frag fa;
+          if constexpr (KPL == 8) {
+            fa = tr_frag(sdSt, LS, ks * 16 + 8 * hh, ks * 16 + 8 * hh + 4, mt * 32 + gcol, j16);
+          } else {
+            fa = load_frag(&sdSt[(ks * 2 + hh) * LS + mt * 32 + l32]);
+          }
+          acc = E::mma(fa, KT[cc][ks], acc);
         }
         accQ[i] = acc;
       }
 
-      // add into the dQ accumulator, in rank order when ORDERED
-      uint32_t* cnt = a.counters + (size_t)head * n_sub + qtile;
-      if constexpr (ORDERED) {
-        if (tid == 0) {
-          if (a.jitter_seed != 0u) {
-            uint32_t nap = hash32(a.jitter_seed ^ (uint32_t)(head * 7919 + qtile * 131 + kv)) & 31u;
-            for (uint32_t i = 0; i < nap; ++i) __builtin_amdgcn_s_sleep(8);
-          }
-          uint32_t target = (uint32_t)rank;
-          if (a.poison_q >= 0 && head == 0 && qtile == a.poison_q && rank == 0) target = 0xFFFFFFFFu;
-          wait_counter(cnt, target, status, spin_limit);
-        }
-        __syncthreads();
-      }
-      float* dqa = a.dq_accum + (size_t)head * N * D;
-#pragma unroll
-      for (int i = 0; i < TPW; ++i) {
-        const int t = w + i * NW;
-        const int mt = t / NTD;
-        const int nt = t % NTD;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int row = q0 + mt * 32 + crow(r, hh);
-          const int col = nt * 32 + l32;
-          atomic_add_f32(&dqa[(size_t)row * D + col], accQ[i][r]);
-        }
-      }
       if (a.partials != nullptr) {
         float* pp = a.partials + (((size_t)head * a.n_tiles + kv) * N) * D;
 #pragma unroll
-        for (int i = 0; i < TPW; ++i) {
-          const int t = w + i * NW;
-          const int mt = t / NTD;
-          const int nt = t % NTD;
+        for (int i = 0; i < QT; ++i) {
+          const int nt = col0 + (i / RPW) * NW;
+          const int mt = row0 + (i % RPW) * WPC;
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int row = q0 + mt * 32 + crow(r, hh);
-            pp[(size_t)row * D + nt * 32 + l32] = accQ[i][r];
-          }
+          for (int r = 0; r < 16; ++r)
+            pp[(size_t)(q0 + mt * 32 + crow(r, hh)) * D + nt * 32 + l32] = accQ[i][r];
         }
       }
+
       if constexpr (ORDERED) {
-        fence_release_agent();
-        __syncthreads();
-        if (tid == 0) store_release_agent(cnt, (uint32_t)rank + 1u);
+#pragma unroll
+        for (int i = 0; i < QT; ++i) accQp[i] = accQ[i];
+        p_qtile = qtile;
+        p_rank = rank;
+        p_flags = flags;
       } else {
-        __syncthreads();
+#pragma unroll
+        for (int i = 0; i < QT; ++i) {
+          const int nt = col0 + (i / RPW) * NW;
+          const int mt = row0 + (i % RPW) * WPC;
+#pragma unroll
+          for (int r = 0; r < 16; ++r)
+            atomic_add_f32(&dqa[(uint32_t)((q0 + mt * 32 + crow(r, hh)) * D + nt * 32 + l32)],
+                           accQ[i][r]);
+        }
       }
+      // No barrier here: every reader of sQ/sdO/sLSE/sDel finished before
+      // the barrier above, and sdSt is rewritten only after the next
+      // sub-tile's staging barrier, which every wave reaches after its dQ
+      // reads.
     }
     if (cur_kv >= 0) flush_dkdv();
+    if constexpr (ORDERED) {
+      release();
+      if (p_qtile >= 0) ordered_add();
+      release();
+    }
 
     // next unit
     if (a.dynamic) {
@@ -377,7 +514,7 @@ static void* pick(bool causal, bool ordered) {
 }
 
 static void* select_bwd(int dtype, int d, bool causal, bool ordered, int* threads) {
-  if (dtype == 1 && d == 128) { *threads = 256; return pick<bf16_t, 128, 128, 64>(causal, ordered); }
+  if (dtype == 1 && d == 128) { *threads = 256; return pick<bf16_t, 128, 128, 32>(causal, ordered); }
   if (dtype == 1 && d == 64) { *threads = 256; return pick<bf16_t, 64, 128, 64>(causal, ordered); }
   if (dtype == 0 && d == 64) { *threads = 128; return pick<float, 64, 64, 64>(causal, ordered); }
   if (dtype == 0 && d == 128) { *threads = 128; return pick<float, 128, 64, 32>(causal, ordered); }
@@ -385,8 +522,14 @@ static void* select_bwd(int dtype, int d, bool causal, bool ordered, int* thread
 }
 
 void bwd_tiles(int dtype, int d, int* bc, int* br) {
-  if (dtype == 1) { *bc = 128; *br = 64; }
+  if (dtype == 1) { *bc = 128; *br = (d == 128) ? 32 : 64; }
   else { *bc = 64; *br = (d == 128) ? 32 : 64; }
+}
+
+int bwd_waves(int dtype, int d) {
+  int bc = 0, br = 0;
+  bwd_tiles(dtype, d, &bc, &br);
+  return bc / 32;
 }
 
 hipError_t bwd_max_coresident(int dtype, int d, bool causal, bool ordered, int* blocks) {

@@ -30,11 +30,17 @@ constexpr float kLog2e = 1.4426950408889634f;
 
 __device__ __forceinline__ int crow(int r, int h) { return ((r >> 2) << 3) + (h << 2) + (r & 3); }
 
-// bf16 <-> fp32, round to nearest even (inputs are finite).
+// fp32 -> bf16 with the hardware conversion (v_cvt_pk_bf16_f32, round to
+// nearest even); bf16 -> fp32 is exact.
 __device__ __forceinline__ uint16_t f32_to_bf16_bits(float f) {
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
+}
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t pack2_bf16(float lo, float hi) {
+  bf16x2_t v;
+  v[0] = (__bf16)lo;
+  v[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
 }
 __device__ __forceinline__ float bf16_bits_to_f32(uint16_t b) { return __uint_as_float(((uint32_t)b) << 16); }
 
@@ -76,9 +82,11 @@ __device__ __forceinline__ f32x16 zero16() {
 
 // Build a bf16 fragment from 8 floats (RNE).
 __device__ __forceinline__ bf16x8 pack_bf16x8(const float* v) {
-  u16x8 u;
-#pragma unroll
-  for (int i = 0; i < 8; ++i) u[i] = f32_to_bf16_bits(v[i]);
+  uint4 u;
+  u.x = pack2_bf16(v[0], v[1]);
+  u.y = pack2_bf16(v[2], v[3]);
+  u.z = pack2_bf16(v[4], v[5]);
+  u.w = pack2_bf16(v[6], v[7]);
   return __builtin_bit_cast(bf16x8, u);
 }
 

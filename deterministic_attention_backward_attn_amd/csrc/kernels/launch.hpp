@@ -15,13 +15,14 @@ struct BwdArgs {
   const void* dout;
   const float* lse;
   const float* delta;
+  void* dq;               // final dQ (ordered schedules write it directly)
   void* dk;
   void* dv;
-  float* dq_accum;        // [BH, N, d] fp32, zeroed before the launch
-  uint32_t* counters;     // [BH, N / BR] order counters, zeroed
+  float* dq_accum;        // [BH, N, d] fp32 (zeroed before the launch only for atomic)
+  uint32_t* counters;     // [BH, N / BR, waves] order counters, zeroed
   uint32_t* header;       // [0] status word, [1] work counter; zeroed
   const int* unit_off;    // [units_per_head + 1]
-  const int2* items;      // {kv | q << 16, rank} per item, one head's list
+  const int2* items;      // {kv | q << 16, rank | last << 30} per item, one head's list
   int N;
   int n_tiles;            // N / BC
   int units_per_head;
@@ -54,6 +55,8 @@ hipError_t launch_bwd(int dtype, int d, bool causal, bool ordered, const BwdArgs
 hipError_t bwd_max_coresident(int dtype, int d, bool causal, bool ordered, int* blocks);
 // Tile sizes of the backward kernel: KV tile (BC) and Q sub-tile (BR).
 void bwd_tiles(int dtype, int d, int* bc, int* br);
+// Waves per workgroup of the backward kernel (one order counter each).
+int bwd_waves(int dtype, int d);
 
 hipError_t launch_fwd(int dtype, int d, bool causal, const FwdArgs& a, hipStream_t stream);
 

@@ -167,12 +167,17 @@ dash_status dash_attn_bwd_status(const void* workspace, void* stream);
  *                   N / dash_attn_tile); each KV tile's unscaled dQ partial
  *                   for every Q row it meets is stored there, in addition
  *                   to the normal accumulation.
+ *   kernel_events   non-NULL pair of hipEvent_t: recorded on `stream`
+ *                   immediately before and after the backward kernel's
+ *                   launch (excluding the workspace clear and the dQ
+ *                   conversion), for timing that kernel alone.
  */
 typedef struct {
   uint32_t spin_limit;
   uint32_t jitter_seed;
   int32_t poison_q;
   float* partials;
+  void* kernel_events[2];
 } dash_bwd_debug;
 
 dash_status dash_attn_bwd_debug(const dash_attn_desc* desc, dash_schedule schedule,
