@@ -151,7 +151,8 @@ def attn_bwd(q, k, v, do, lse, delta, *, schedule="naive", causal=False, scale=N
     attn_bwd_workspace_size bytes (allocated if None).  `out`: optional
     preallocated (dq, dk, dv).  `debug`: optional dict with keys spin_limit,
     jitter_seed, poison_q (1-based, 0 = off), partials (float32 tensor),
-    kernel_events (two raw hipEvent_t handles)."""
+    kernel_events (two raw hipEvent_t handles), wait_stats (int64 tensor of
+    at least 4*4096*4 entries)."""
     torch = _torch()
     lib = load()
     _same_shape(q, k, v, do)
@@ -175,6 +176,8 @@ def attn_bwd(q, k, v, do, lse, delta, *, schedule="naive", causal=False, scale=N
         dbg = Debug(int(debug.get("spin_limit", 0)), int(debug.get("jitter_seed", 0)),
                     int(debug.get("poison_q", 0)),
                     _ptr(debug["partials"]) if debug.get("partials") is not None else None)
+        if debug.get("wait_stats") is not None:
+            dbg.wait_stats = _ptr(debug["wait_stats"])
         ev = debug.get("kernel_events")
         if ev is not None:
             dbg.kernel_events[0] = ctypes.c_void_p(int(ev[0]))

@@ -212,6 +212,8 @@ dash_status run_bwd(const dash_attn_desc* desc, dash_schedule schedule, const vo
   a.jitter_seed = dbg ? dbg->jitter_seed : 0u;
   a.poison_q = dbg ? dbg->poison_q - 1 : -1;
   a.partials = dbg ? dbg->partials : nullptr;
+  a.wait_stats = dbg ? dbg->wait_stats : nullptr;
+  if (a.wait_stats && grid > 4096) return DASH_ERR_UNSUPPORTED;
   hipEvent_t ev0 = dbg ? (hipEvent_t)dbg->kernel_events[0] : nullptr;
   hipEvent_t ev1 = dbg ? (hipEvent_t)dbg->kernel_events[1] : nullptr;
   if (ev0 && hipEventRecord(ev0, strm) != hipSuccess) return DASH_ERR_HIP;

@@ -75,11 +75,6 @@ __device__ __forceinline__ bf16x8 tr_frag(const bf16_t* base, int ld, int r0, in
   return __builtin_bit_cast(bf16x8, u);
 }
 
-__device__ __forceinline__ void wait_vm_stores() {
-  // s_waitcnt vmcnt(0): this wave's vector memory operations have completed
-  __builtin_amdgcn_s_waitcnt(0x0F70);
-}
-
 template <typename T, int D, int BC, int BR, bool CAUSAL, bool ORDERED>
 __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
   using E = Elt<T>;
@@ -134,6 +129,10 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
 
   if (a.dynamic == 0 && (int)blockIdx.x >= a.p_eff) return;
   int unit = blockIdx.x;
+  // diagnostics (lane 0 of each wave): cycles in ordered waits, waits, waits
+  // that had to poll more than once, cycles of the whole unit loop
+  uint64_t st_wait = 0, st_waits = 0, st_spun = 0;
+  const uint64_t st_t0 = a.wait_stats ? (uint64_t)clock64() : 0;
 
   while (unit < a.total_units) {
     const int head = unit / a.units_per_head;
@@ -206,14 +205,21 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
       const bool last = (p_flags & 1) != 0;
       const int q0 = p_qtile * BR;
       if (lane == 0) {
+        const uint64_t t0 = a.wait_stats ? (uint64_t)clock64() : 0;
         if (a.jitter_seed != 0u) {
           const uint32_t nap =
               hash32(a.jitter_seed ^ (uint32_t)(head * 7919 + p_qtile * 131 + cur_kv * 17 + w)) & 31u;
           for (uint32_t i = 0; i < nap; ++i) __builtin_amdgcn_s_sleep(8);
         }
         const bool poisoned = a.poison_q >= 0 && head == 0 && p_qtile == a.poison_q && rank == 0;
-        if (poisoned) wait_counter(counter(p_qtile), 0xFFFFFFFFu, status, spin_limit);
-        else if (rank > 0) wait_counter(counter(p_qtile), (uint32_t)rank, status, spin_limit);
+        uint32_t polls = 0;
+        if (poisoned) polls = wait_counter(counter(p_qtile), 0xFFFFFFFFu, status, spin_limit);
+        else if (rank > 0) polls = wait_counter(counter(p_qtile), (uint32_t)rank, status, spin_limit);
+        if (a.wait_stats) {
+          st_wait += (uint64_t)clock64() - t0;
+          st_waits += rank > 0 ? 1u : 0u;
+          st_spun += polls > 0 ? 1u : 0u;
+        }
       }
       __builtin_amdgcn_wave_barrier();
 #pragma unroll
@@ -226,7 +232,7 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) {
             const uint32_t off = (uint32_t)((q0 + mt * 32 + crow(r, hh)) * D + col);
-            prev[r] = __hip_atomic_load(&dqa[off], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            prev[r] = coherent_load(&dqa[off]);
           }
 #pragma unroll
           for (int r = 0; r < 16; ++r) accQp[i][r] = prev[r] + accQp[i][r];
@@ -237,7 +243,7 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
           if (last)
             dqo[off] = E::from_f32(accQp[i][r] * a.scale);
           else
-            __hip_atomic_store(&dqa[off], accQp[i][r], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            coherent_store(&dqa[off], accQp[i][r]);
         }
       }
       if (!last) {
@@ -252,9 +258,7 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
     auto release = [&]() {
       if (rel_pending) {
         wait_vm_stores();
-        if (lane == 0)
-          __hip_atomic_store(counter(rel_qtile), (uint32_t)rel_rank + 1u, __ATOMIC_RELAXED,
-                             __HIP_MEMORY_SCOPE_AGENT);
+        if (lane == 0) advance_counter(counter(rel_qtile), (uint32_t)rel_rank + 1u);
         rel_pending = false;
       }
     };
@@ -499,6 +503,13 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
     } else {
       unit += a.p_eff;
     }
+  }
+  if (a.wait_stats != nullptr && lane == 0) {
+    uint64_t* st = a.wait_stats + ((size_t)blockIdx.x * NW + w) * 4;
+    st[0] = st_wait;
+    st[1] = st_waits;
+    st[2] = st_spun;
+    st[3] = (uint64_t)clock64() - st_t0;
   }
 }
 

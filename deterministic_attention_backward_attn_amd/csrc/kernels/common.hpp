@@ -96,18 +96,10 @@ __device__ __forceinline__ bf16x8 load_frag(const bf16_t* p) {
 }
 __device__ __forceinline__ float load_frag(const float* p) { return *p; }
 
-// Device-scope ordering helpers.
-__device__ __forceinline__ uint32_t load_acquire_agent(const uint32_t* p) {
-  return __hip_atomic_load(p, __ATOMIC_ACQUIRE, __HIP_MEMORY_SCOPE_AGENT);
-}
+// Device-scope counter load.
 __device__ __forceinline__ uint32_t load_relaxed_agent(const uint32_t* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
-__device__ __forceinline__ void store_release_agent(uint32_t* p, uint32_t v) {
-  __hip_atomic_store(p, v, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
-}
-__device__ __forceinline__ void fence_release_agent() { __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent"); }
-__device__ __forceinline__ void fence_acquire_agent() { __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent"); }
 
 // fp32 add performed at the device coherence point (no return value).
 __device__ __forceinline__ void atomic_add_f32(float* p, float v) {
@@ -117,23 +109,37 @@ __device__ __forceinline__ void atomic_add_f32(float* p, float v) {
 // Status word bits (workspace header).
 constexpr uint32_t kStatusTimeout = 1u;
 
-// Bounded wait until *cnt == target.  Called by one lane.  Polls with
-// relaxed device-scope loads and issues one acquire fence after success, so
-// the caches are invalidated once per hand-off rather than once per poll.
-// Gives up after `limit` polls (or soon after another wait gave up),
-// records the time-out in *status and returns false.
-__device__ __forceinline__ bool wait_counter(const uint32_t* cnt, uint32_t target, uint32_t* status,
-                                             uint32_t limit) {
+// Hand-off primitives of the ordered adds.  The shared data (the fp32 dQ
+// accumulator) and the counters are only ever accessed with device-coherent
+// loads and stores (the cache policy of device-scope atomics), so ordering
+// needs no cache-wide write-back or invalidation: the writer waits until its
+// own stores have completed before it advances the counter, and the reader
+// issues its loads only after it has seen the counter value.
+__device__ __forceinline__ float coherent_load(const float* p) {
+  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+__device__ __forceinline__ void coherent_store(float* p, float v) {
+  __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+// s_waitcnt vmcnt(0): this wave's vector memory operations have completed.
+__device__ __forceinline__ void wait_vm_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+__device__ __forceinline__ void advance_counter(uint32_t* cnt, uint32_t v) {
+  __hip_atomic_store(cnt, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Bounded wait until *cnt == target.  Called by one lane; polls with
+// device-coherent loads.  Gives up after `limit` polls (or soon after another
+// wait gave up) and records the time-out in *status.  Returns the number of
+// failed polls.
+__device__ __forceinline__ uint32_t wait_counter(const uint32_t* cnt, uint32_t target,
+                                                 uint32_t* status, uint32_t limit) {
   uint32_t polls = 0;
   while (true) {
-    if (load_relaxed_agent(cnt) == target) {
-      fence_acquire_agent();
-      return true;
-    }
-    if ((polls & 255u) == 255u && load_relaxed_agent(status) != 0u) return false;
+    if (load_relaxed_agent(cnt) == target) return polls;
+    if ((polls & 255u) == 255u && load_relaxed_agent(status) != 0u) return polls;
     if (++polls > limit) {
       __hip_atomic_fetch_or(status, kStatusTimeout, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      return false;
+      return polls;
     }
     __builtin_amdgcn_s_sleep(2);
   }

@@ -112,29 +112,32 @@ hipError_t launch_dq_convert(int dtype, const float* acc, void* dq, float scale,
   return hipGetLastError();
 }
 
-// Ordering litmus: workgroup w waits until *counter == turn[w], adds its row
-// of `values` into acc with the same fp32 atomic adds the ordered dQ path
-// uses, then releases counter = turn[w] + 1.  With exact-cancellation values
-// any misordering or lost update changes the bits of acc.
-__global__ void __launch_bounds__(256) litmus_kernel(int len, const int* __restrict__ turn,
-                                                     const float* __restrict__ values,
-                                                     float* __restrict__ acc, uint32_t* counter,
-                                                     uint32_t* status, uint32_t spin_limit) {
+// Ordering litmus: contributor w (one wave) waits until *counter == turn[w],
+// adds its row of `values` into acc with the same device-coherent
+// read-modify-write, store completion wait and counter advance that the
+// ordered dQ adds use, then sets the counter to turn[w] + 1.  With
+// order-sensitive values any misordering or lost update changes the bits.
+__global__ void __launch_bounds__(64) litmus_kernel(int len, const int* __restrict__ turn,
+                                                    const float* __restrict__ values,
+                                                    float* __restrict__ acc, uint32_t* counter,
+                                                    uint32_t* status, uint32_t spin_limit) {
   const int w = blockIdx.x;
   const uint32_t my = (uint32_t)turn[w];
-  if (threadIdx.x == 0) wait_counter(counter, my, status, spin_limit);
-  __syncthreads();
-  for (int i = threadIdx.x; i < len; i += blockDim.x) atomic_add_f32(&acc[i], values[(size_t)w * len + i]);
-  fence_release_agent();
-  __syncthreads();
-  if (threadIdx.x == 0) store_release_agent(counter, my + 1u);
+  if (threadIdx.x == 0 && my > 0) wait_counter(counter, my, status, spin_limit);
+  __builtin_amdgcn_wave_barrier();
+  for (int i = threadIdx.x; i < len; i += 64) {
+    const float v = values[(size_t)w * len + i];
+    coherent_store(&acc[i], my == 0 ? v : coherent_load(&acc[i]) + v);
+  }
+  wait_vm_stores();
+  if (threadIdx.x == 0) advance_counter(counter, my + 1u);
 }
 
-hipError_t launch_litmus(int workgroups, int len, const int* turn, const float* values,
+hipError_t launch_litmus(int contributors, int len, const int* turn, const float* values,
                          float* acc, uint32_t* counter, uint32_t* status, uint32_t spin_limit,
                          hipStream_t stream) {
   void* args[] = {&len, &turn, &values, &acc, &counter, &status, &spin_limit};
-  return hipLaunchCooperativeKernel((void*)litmus_kernel, dim3(workgroups), dim3(256), args, 0,
+  return hipLaunchCooperativeKernel((void*)litmus_kernel, dim3(contributors), dim3(64), args, 0,
                                     stream);
 }
 

@@ -35,6 +35,7 @@ struct BwdArgs {
   uint32_t jitter_seed;
   int poison_q;
   float* partials;        // debug: [BH, n_tiles, N, d] or null
+  uint64_t* wait_stats;   // debug: [grid, waves, 4] or null
 };
 
 struct FwdArgs {
@@ -65,7 +66,7 @@ hipError_t launch_preprocess(int dtype, int d, const void* o, const void* dout, 
 hipError_t launch_zero_u32(uint32_t* p, size_t n_words, hipStream_t stream);
 hipError_t launch_dq_convert(int dtype, const float* acc, void* dq, float scale, size_t n,
                              hipStream_t stream);
-hipError_t launch_litmus(int workgroups, int len, const int* turn, const float* values,
+hipError_t launch_litmus(int contributors, int len, const int* turn, const float* values,
                          float* acc, uint32_t* counter, uint32_t* status, uint32_t spin_limit,
                          hipStream_t stream);
 

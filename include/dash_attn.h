@@ -171,6 +171,12 @@ dash_status dash_attn_bwd_status(const void* workspace, void* stream);
  *                   immediately before and after the backward kernel's
  *                   launch (excluding the workspace clear and the dQ
  *                   conversion), for timing that kernel alone.
+ *   wait_stats      non-NULL: device uint64 buffer of at least
+ *                   4 * 4096 * 4 entries; for each workgroup g and wave w,
+ *                   entries [(g*waves + w)*4 + k] receive: k=0 shader-clock
+ *                   cycles spent waiting for ordered adds, k=1 ordered waits,
+ *                   k=2 waits that polled more than once, k=3 cycles of the
+ *                   workgroup's whole run (waves = dash_attn_tile/32).
  */
 typedef struct {
   uint32_t spin_limit;
@@ -178,6 +184,7 @@ typedef struct {
   int32_t poison_q;
   float* partials;
   void* kernel_events[2];
+  uint64_t* wait_stats;
 } dash_bwd_debug;
 
 dash_status dash_attn_bwd_debug(const dash_attn_desc* desc, dash_schedule schedule,
@@ -226,12 +233,12 @@ dash_status dash_dag_longest_path(int32_t n_nodes, const double* weights, int32_
                                   double* start, double* finish);
 
 /*
- * Ordering litmus (diagnostic): `workgroups` workgroups (spread over all
- * XCDs by the dispatcher, all resident at once) take turns adding their row
- * of `values` [workgroups, len] into `acc` [len], workgroup w going when
- * the counter reaches turn[w] (a permutation of 0..workgroups-1), through
- * the same counter hand-off and fp32 atomic adds that the ordered dQ adds
- * use.  turn, values, acc: device arrays; counters: device uint32[2]
+ * Ordering litmus (diagnostic): `workgroups` one-wave workgroups (spread
+ * over all XCDs by the dispatcher, all resident at once) take turns adding
+ * their row of `values` [workgroups, len] into `acc` [len], workgroup w
+ * going when the counter reaches turn[w] (a permutation of
+ * 0..workgroups-1), through the same counter hand-off and coherent
+ * read-modify-write that the ordered dQ adds use.  turn, values, acc: device arrays; counters: device uint32[2]
  * (counter, status; cleared by the call).  spin_limit 0 = default.
  * Synchronizes the stream; returns DASH_ERR_ORDER_TIMEOUT if a hand-off
  * timed out.
