@@ -108,6 +108,9 @@ def main():
     ap.add_argument("--primary", default=None, help="schedule reported as value")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-workers", type=int, default=16)
+    ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
+                    help="run one plain device copy of BYTES before timing (a reference "
+                         "dispatch of known traffic for hardware-counter runs)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py: this backward runs on one GPU; --gpus {args.gpus} is not supported "
@@ -144,6 +147,12 @@ def main():
     t_gen = time.perf_counter() - t_gen
     print(f"[bench] {w.name} {mask}: inputs ready in {t_gen:.1f}s", file=sys.stderr, flush=True)
 
+    if args.copy_calibration > 0:
+        src = torch.ones(args.copy_calibration // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
     o, lse = D.attn_fwd(dev["q"], dev["k"], dev["v"], causal=causal)
     delta = torch.empty_like(lse)
     dq, dk, dv = (torch.empty_like(dev["q"]) for _ in range(3))

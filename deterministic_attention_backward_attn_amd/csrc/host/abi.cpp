@@ -164,6 +164,9 @@ dash_status run_bwd(const dash_attn_desc* desc, dash_schedule schedule, const vo
   if (st != DASH_OK) return st;
 
   const int U = tb->host.units();
+  for (int u = 0; u < U; ++u)
+    if (tb->host.unit_off[u + 1] - tb->host.unit_off[u] > dash::kMaxUnitItems)
+      return DASH_ERR_UNSUPPORTED;
   const long heads = (long)desc->B * desc->H;
   const long total_units = heads * U;
   int grid = 0, p_eff = 0, dynamic = 0;

@@ -104,12 +104,20 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
   static_assert(CPT * VEC * NT == BR * D, "sub-tile load must split evenly");
   static_assert(NT >= 2 * BR, "LSE/delta staging needs 2*BR threads");
 
-  __shared__ __align__(16) T sQ[BR * LQ];
-  __shared__ __align__(16) T sdO[BR * LQ];
-  __shared__ __align__(16) T sdSt[BC * LS];
+  // Double-buffered Q / dO / LSE / delta sub-tiles and dS^T: sub-tile g reads
+  // buffer g%2 while the next one is staged into the other, so a sub-tile
+  // needs one workgroup barrier.
+  __shared__ __align__(16) T sQ[2][BR * LQ];
+  __shared__ __align__(16) T sdO[2][BR * LQ];
+  __shared__ __align__(16) T sdSt[2][BC * LS];
   __shared__ __align__(16) T sK[BC * LQ];
-  __shared__ float sLSE[BR];
-  __shared__ float sDel[BR];
+  __shared__ __align__(16) float sLSE[2][BR];
+  __shared__ __align__(16) float sDel[2][BR];
+  __shared__ int2 sItems[kMaxUnitItems];
+  // per-wave staging of a dQ partial, row-major [32 rows][32 + 4 floats], so
+  // that each 16-byte accumulator access of a lane group covers whole rows
+  constexpr int LR = 36;
+  __shared__ __align__(16) float sRow[ORDERED ? NW : 1][ORDERED ? QT * 32 * LR : 4];
   __shared__ int sUnit;
 
   const int tid = threadIdx.x;
@@ -148,8 +156,13 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
     T* dqo = reinterpret_cast<T*>(a.dq) + hoff;
     uint32_t* cnt_h = a.counters + (size_t)head * n_sub * NW;
     const int it0 = a.unit_off[lu];
-    const int it1 = a.unit_off[lu + 1];
-    const int n_steps = (it1 - it0) * RHO;
+    const int n_items = a.unit_off[lu + 1] - it0;  // <= kMaxUnitItems (checked by the host)
+    const int n_steps = n_items * RHO;
+
+    // The unit's work list into LDS.  Every wave has finished the previous
+    // unit (including all LDS reads) once it passes this barrier.
+    for (int i = tid; i < n_items; i += NT) sItems[i] = a.items[it0 + i];
+    __syncthreads();
 
     frag Kreg[DK], Vreg[DK];
     frag KT[CPW][KK];
@@ -158,6 +171,7 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
 
     // deferred ordered add: partial of the previous sub-tile
     f32x16 accQp[QT];
+    f32x4 lv[QT][4];                             // accumulator values read back
     int p_qtile = -1, p_rank = 0, p_flags = 0;  // flags: bit0 last
     bool rel_pending = false;                    // stores issued, counter not yet advanced
     int rel_qtile = 0, rel_rank = 0;
@@ -165,8 +179,7 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
     uint4 pq[CPT], pdo[CPT];
     float pstat = 0.f;
     auto fetch = [&](int g) {
-      const int2 itm = a.items[it0 + g / RHO];
-      const int qtile = (itm.x >> 16) * RHO + (g % RHO);
+      const int qtile = (sItems[g / RHO].x >> 16) * RHO + (g % RHO);
       const int q0 = qtile * BR;
 #pragma unroll
       for (int i = 0; i < CPT; ++i) {
@@ -179,6 +192,18 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
       }
       if (tid < BR) pstat = lse_g[q0 + tid] * kLog2e;
       else if (tid < 2 * BR) pstat = del_g[q0 + tid - BR];
+    };
+    auto stage = [&](int buf) {
+#pragma unroll
+      for (int i = 0; i < CPT; ++i) {
+        const int c = tid + i * NT;
+        const int row = c / (D / VEC);
+        const int col = (c % (D / VEC)) * VEC;
+        *reinterpret_cast<uint4*>(&sQ[buf][row * LQ + col]) = pq[i];
+        *reinterpret_cast<uint4*>(&sdO[buf][row * LQ + col]) = pdo[i];
+      }
+      if (tid < BR) sLSE[buf][tid] = pstat;
+      else if (tid < 2 * BR) sDel[buf][tid - BR] = pstat;
     };
 
     auto flush_dkdv = [&]() {
@@ -197,13 +222,34 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
 
     // this wave's counter for a Q sub-tile
     auto counter = [&](int qtile) { return cnt_h + (size_t)qtile * NW + w; };
+    // dQ partials are computed transposed (dQ^T = K^T dS^T): lane <-> Q row,
+    // register r <-> column nt*32 + crow(r, h), so registers 4g..4g+3 hold 4
+    // consecutive columns and the accumulator moves in 16-byte pieces.
+    const __amdgpu_buffer_rsrc_t dq_rs = make_rsrc(dqa, (uint32_t)(N * D * 4));
+    // (The atomic schedule keeps dQ untransposed, lane <-> column, so each
+    // atomic instruction covers whole rows.)
+    // row-major chunk k (0..3) of output tile i for this lane: 4 consecutive
+    // columns of one row; 8 lanes cover a 32-column (128-byte) row
+    auto chunk_off = [&](int q0, int i, int k) {
+      const int nt = col0 + (i / RPW) * NW;
+      const int mt = row0 + (i % RPW) * WPC;
+      return (uint32_t)((q0 + mt * 32 + (lane >> 3) + 8 * k) * D + nt * 32 + 4 * (lane & 7));
+    };
+    auto dq_off = [&](int q0, int i, int r) {
+      const int nt = col0 + (i / RPW) * NW;
+      const int mt = row0 + (i % RPW) * WPC;
+      if constexpr (ORDERED) return (uint32_t)((q0 + mt * 32 + l32) * D + nt * 32 + crow(r, hh));
+      else return (uint32_t)((q0 + mt * 32 + crow(r, hh)) * D + nt * 32 + l32);
+    };
 
-    // Ordered add of the deferred partial: wait for this wave's turn, read
-    // the accumulator (unless first), add, write back or write final dQ.
-    auto ordered_add = [&]() {
+    // Ordered add of the deferred partial.  begin_add (top of the next
+    // sub-tile) checks once, without waiting, whether it is this wave's turn
+    // and if so starts reading the accumulator; finish_add (after the next
+    // sub-tile's products) waits for the turn if it had not come yet, reads,
+    // adds and writes back (or writes the final dQ if last).
+    bool p_loaded = false;
+    auto wait_turn = [&]() {
       const int rank = p_rank;
-      const bool last = (p_flags & 1) != 0;
-      const int q0 = p_qtile * BR;
       if (lane == 0) {
         const uint64_t t0 = a.wait_stats ? (uint64_t)clock64() : 0;
         if (a.jitter_seed != 0u) {
@@ -217,43 +263,79 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
         else if (rank > 0) polls = wait_counter(counter(p_qtile), (uint32_t)rank, status, spin_limit);
         if (a.wait_stats) {
           st_wait += (uint64_t)clock64() - t0;
-          st_waits += rank > 0 ? 1u : 0u;
           st_spun += polls > 0 ? 1u : 0u;
         }
       }
       __builtin_amdgcn_wave_barrier();
+    };
+    auto load_acc = [&]() {
+      const int q0 = p_qtile * BR;
+#pragma unroll
+      for (int i = 0; i < QT; ++i)
+#pragma unroll
+        for (int k = 0; k < 4; ++k) lv[i][k] = coherent_load4(dq_rs, 4 * chunk_off(q0, i, k));
+      p_loaded = true;
+    };
+    // p_seen: the counter value lane 0 read (without waiting) right after the
+    // partial was computed; if it already shows this wave's turn, the
+    // accumulator loads start at the top of the next sub-tile.
+    uint32_t p_seen = 0;
+    auto peek_turn = [&]() {
+      if (lane == 0 && p_rank > 0) p_seen = load_relaxed_agent(counter(p_qtile));
+    };
+    auto begin_add = [&]() {
+      p_loaded = false;
+      if (p_rank == 0 || a.jitter_seed != 0u || a.poison_q >= 0) return;
+      const int ready = lane == 0 && p_seen == (uint32_t)p_rank;
+      if (__builtin_amdgcn_readfirstlane(ready)) load_acc();
+    };
+    auto finish_add = [&]() {
+      if (a.wait_stats && lane == 0) st_waits += p_rank > 0 ? 1u : 0u;
+      if (!p_loaded) {
+        wait_turn();
+        if (p_rank > 0) load_acc();
+      }
+      const bool last = (p_flags & 1) != 0;
+      const int q0 = p_qtile * BR;
+      // transpose the partial to row-major through this wave's LDS area
+      float* row = sRow[w];
+#pragma unroll
+      for (int i = 0; i < QT; ++i)
+#pragma unroll
+        for (int gq = 0; gq < 4; ++gq)
+          *reinterpret_cast<f32x4*>(&row[(i * 32 + l32) * LR + 8 * gq + 4 * hh]) =
+              f32x4{accQp[i][4 * gq], accQp[i][4 * gq + 1], accQp[i][4 * gq + 2],
+                    accQp[i][4 * gq + 3]};
+      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes done
+      __builtin_amdgcn_wave_barrier();
 #pragma unroll
       for (int i = 0; i < QT; ++i) {
-        const int nt = col0 + (i / RPW) * NW;
-        const int mt = row0 + (i % RPW) * WPC;
-        const int col = nt * 32 + l32;
-        if (rank > 0) {
-          float prev[16];
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const uint32_t off = (uint32_t)((q0 + mt * 32 + crow(r, hh)) * D + col);
-            prev[r] = coherent_load(&dqa[off]);
+        for (int gq = 0; gq < 4; ++gq) {
+          f32x4 v = *reinterpret_cast<const f32x4*>(
+              &row[(i * 32 + (lane >> 3) + 8 * gq) * LR + 4 * (lane & 7)]);
+          if (p_rank > 0) v = lv[i][gq] + v;
+          const uint32_t off = chunk_off(q0, i, gq);
+          if (last) {
+            v *= a.scale;
+            if constexpr (KPL == 8) {
+              *reinterpret_cast<uint2*>(&dqo[off]) =
+                  make_uint2(pack2_bf16(v[0], v[1]), pack2_bf16(v[2], v[3]));
+            } else {
+              *reinterpret_cast<f32x4*>(&dqo[off]) = v;
+            }
+          } else {
+            coherent_store4(dq_rs, 4 * off, v);
           }
-#pragma unroll
-          for (int r = 0; r < 16; ++r) accQp[i][r] = prev[r] + accQp[i][r];
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const uint32_t off = (uint32_t)((q0 + mt * 32 + crow(r, hh)) * D + col);
-          if (last)
-            dqo[off] = E::from_f32(accQp[i][r] * a.scale);
-          else
-            coherent_store(&dqa[off], accQp[i][r]);
         }
       }
       if (!last) {
         rel_pending = true;
         rel_qtile = p_qtile;
-        rel_rank = rank;
+        rel_rank = p_rank;
       }
       p_qtile = -1;
     };
-
     // Advance the counter of the last ordered add once its stores completed.
     auto release = [&]() {
       if (rel_pending) {
@@ -263,10 +345,15 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
       }
     };
 
-    if (n_steps > 0) fetch(0);
+    if (n_steps > 0) {
+      fetch(0);
+      stage(0);  // made visible by the barrier of the first KV tile below
+    }
+    if (n_steps > 1) fetch(1);
 
     for (int g = 0; g < n_steps; ++g) {
-      const int2 itm = a.items[it0 + g / RHO];
+      const int b = g & 1;
+      const int2 itm = sItems[g / RHO];
       const int kv = itm.x & 0xFFFF;
       const int qblk = itm.x >> 16;
       const int rank = itm.y & 0xFFFF;
@@ -313,25 +400,14 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
         }
       }
 
-      // previous ordered add's stores are complete -> advance its counter;
-      // the prefetched loads are complete too
-      if constexpr (ORDERED) release();
-
-      // stage the prefetched Q / dO sub-tile, row-major
-#pragma unroll
-      for (int i = 0; i < CPT; ++i) {
-        const int c = tid + i * NT;
-        const int row = c / (D / VEC);
-        const int col = (c % (D / VEC)) * VEC;
-        *reinterpret_cast<uint4*>(&sQ[row * LQ + col]) = pq[i];
-        *reinterpret_cast<uint4*>(&sdO[row * LQ + col]) = pdo[i];
+      if constexpr (ORDERED) {
+        // start reading the accumulator for the previous sub-tile's partial
+        // if its turn had already come
+        if (p_qtile >= 0) begin_add();
       }
-      if (tid < BR) sLSE[tid] = pstat;
-      else if (tid < 2 * BR) sDel[tid - BR] = pstat;
-      __syncthreads();
 
-      if (g + 1 < n_steps) fetch(g + 1);
-
+      const T* cQ = sQ[b];
+      const T* cdO = sdO[b];
       // S = Q K^T and dP = dO V^T for this wave's 32 KV columns
       f32x16 accS[MT], accP[MT];
 #pragma unroll
@@ -344,8 +420,8 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt) {
           const int off = (mt * 32 + l32) * LQ + ks * KSTEP + hh * KPL;
-          accS[mt] = E::mma(load_frag(&sQ[off]), Kreg[ks], accS[mt]);
-          accP[mt] = E::mma(load_frag(&sdO[off]), Vreg[ks], accP[mt]);
+          accS[mt] = E::mma(load_frag(&cQ[off]), Kreg[ks], accS[mt]);
+          accP[mt] = E::mma(load_frag(&cdO[off]), Vreg[ks], accP[mt]);
         }
       }
 
@@ -354,14 +430,15 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
       // MFMA A operands.  fp32: P and dS stay in place (accS <- P, accP <- dS).
       const bool diag = CAUSAL && (qblk == kv);   // uniform across the workgroup
       const int kvl = 32 * w + l32;
+      T* cdSt = sdSt[b];
       uint32_t pw[MT][8], dw[MT][8];
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
           const int qb = mt * 32 + 8 * gq + 4 * hh;  // 4 consecutive Q rows
-          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sLSE[qb]);
-          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sDel[qb]);
+          const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sLSE[b][qb]);
+          const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sDel[b][qb]);
           float p[4], ds[4];
 #pragma unroll
           for (int e = 0; e < 4; ++e)
@@ -378,7 +455,7 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
             pw[mt][2 * gq + 1] = pack2_bf16(p[2], p[3]);
             dw[mt][2 * gq] = pack2_bf16(ds[0], ds[1]);
             dw[mt][2 * gq + 1] = pack2_bf16(ds[2], ds[3]);
-            *reinterpret_cast<uint2*>(&sdSt[kvl * LS + qb]) =
+            *reinterpret_cast<uint2*>(&cdSt[kvl * LS + qb]) =
                 make_uint2(dw[mt][2 * gq], dw[mt][2 * gq + 1]);
           } else {
 #pragma unroll
@@ -386,7 +463,7 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
               accS[mt][4 * gq + e] = p[e];
               accP[mt][4 * gq + e] = ds[e];
             }
-            *reinterpret_cast<f32x4*>(&sdSt[kvl * LS + qb]) = f32x4{ds[0], ds[1], ds[2], ds[3]};
+            *reinterpret_cast<f32x4*>(&cdSt[kvl * LS + qb]) = f32x4{ds[0], ds[1], ds[2], ds[3]};
           }
         }
       }
@@ -413,23 +490,26 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
           if constexpr (KPL == 8) {
             // K slots: Q rows r0+{0..3}, r0+8+{0..3}, r0 = mt*32 + 16cc + 4h
             const int r0 = mt * 32 + 16 * cc + 4 * hh;
-            bo = tr_frag(sdO, LQ, r0, r0 + 8, nt * 32 + gcol, j16);
-            bq = tr_frag(sQ, LQ, r0, r0 + 8, nt * 32 + gcol, j16);
+            bo = tr_frag(cdO, LQ, r0, r0 + 8, nt * 32 + gcol, j16);
+            bq = tr_frag(cQ, LQ, r0, r0 + 8, nt * 32 + gcol, j16);
           } else {
             const int qrow = mt * 32 + crow(cc, hh);
-            bo = load_frag(&sdO[qrow * LQ + nt * 32 + l32]);
-            bq = load_frag(&sQ[qrow * LQ + nt * 32 + l32]);
+            bo = load_frag(&cdO[qrow * LQ + nt * 32 + l32]);
+            bq = load_frag(&cQ[qrow * LQ + nt * 32 + l32]);
           }
           accdV[nt] = E::mma(pa, bo, accdV[nt]);
           accdK[nt] = E::mma(da, bq, accdK[nt]);
         }
       }
 
-      // the previous sub-tile's ordered add, behind this sub-tile's products
+      // stage the next sub-tile into the other buffer (its previous readers,
+      // sub-tile g-1, finished before the last barrier)
+      if (g + 1 < n_steps) stage(b ^ 1);
+      // finish the previous sub-tile's ordered add behind this one's products
       if constexpr (ORDERED) {
-        if (p_qtile >= 0) ordered_add();
+        if (p_qtile >= 0) finish_add();
       }
-      __syncthreads();  // sdSt complete
+      __syncthreads();  // dS^T of this sub-tile and the next staged sub-tile are complete
 
       // dQ_part = dS K for this wave's output tiles
       f32x16 accQ[QT];
@@ -442,25 +522,27 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
         for (int ks = 0; ks < KK; ++ks) {
           frag fa;
           if constexpr (KPL == 8) {
-            fa = tr_frag(sdSt, LS, ks * 16 + 8 * hh, ks * 16 + 8 * hh + 4, mt * 32 + gcol, j16);
+            fa = tr_frag(cdSt, LS, ks * 16 + 8 * hh, ks * 16 + 8 * hh + 4, mt * 32 + gcol, j16);
           } else {
-            fa = load_frag(&sdSt[(ks * 2 + hh) * LS + mt * 32 + l32]);
+            fa = load_frag(&cdSt[(ks * 2 + hh) * LS + mt * 32 + l32]);
           }
-          acc = E::mma(fa, KT[cc][ks], acc);
+          if constexpr (ORDERED) acc = E::mma(KT[cc][ks], fa, acc);  // dQ^T tile
+          else acc = E::mma(fa, KT[cc][ks], acc);                    // dQ tile
         }
         accQ[i] = acc;
       }
+      // the previous partial's stores (issued before the barrier) complete
+      // here; advance its counter before issuing the next prefetch, so the
+      // wait does not include loads that were just issued
+      if constexpr (ORDERED) release();
+      if (g + 2 < n_steps) fetch(g + 2);
 
       if (a.partials != nullptr) {
         float* pp = a.partials + (((size_t)head * a.n_tiles + kv) * N) * D;
 #pragma unroll
-        for (int i = 0; i < QT; ++i) {
-          const int nt = col0 + (i / RPW) * NW;
-          const int mt = row0 + (i % RPW) * WPC;
+        for (int i = 0; i < QT; ++i)
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            pp[(size_t)(q0 + mt * 32 + crow(r, hh)) * D + nt * 32 + l32] = accQ[i][r];
-        }
+          for (int r = 0; r < 16; ++r) pp[dq_off(q0, i, r)] = accQ[i][r];
       }
 
       if constexpr (ORDERED) {
@@ -469,26 +551,21 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
         p_qtile = qtile;
         p_rank = rank;
         p_flags = flags;
+        peek_turn();
       } else {
 #pragma unroll
-        for (int i = 0; i < QT; ++i) {
-          const int nt = col0 + (i / RPW) * NW;
-          const int mt = row0 + (i % RPW) * WPC;
+        for (int i = 0; i < QT; ++i)
 #pragma unroll
-          for (int r = 0; r < 16; ++r)
-            atomic_add_f32(&dqa[(uint32_t)((q0 + mt * 32 + crow(r, hh)) * D + nt * 32 + l32)],
-                           accQ[i][r]);
-        }
+          for (int r = 0; r < 16; ++r) atomic_add_f32(&dqa[dq_off(q0, i, r)], accQ[i][r]);
       }
-      // No barrier here: every reader of sQ/sdO/sLSE/sDel finished before
-      // the barrier above, and sdSt is rewritten only after the next
-      // sub-tile's staging barrier, which every wave reaches after its dQ
-      // reads.
     }
     if (cur_kv >= 0) flush_dkdv();
     if constexpr (ORDERED) {
       release();
-      if (p_qtile >= 0) ordered_add();
+      if (p_qtile >= 0) {
+        begin_add();
+        finish_add();
+      }
       release();
     }
 

@@ -121,6 +121,22 @@ __device__ __forceinline__ float coherent_load(const float* p) {
 __device__ __forceinline__ void coherent_store(float* p, float v) {
   __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
+// 16-byte device-coherent accesses through a buffer resource (bounds-checked
+// against num_bytes: out-of-range loads return 0, stores are dropped).  The
+// cache policy is the one device-scope atomics use (sc1); 16-byte requests
+// carry four times the data of per-lane dword requests.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t num_bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)num_bytes,
+                                           0x00020000);
+}
+constexpr int kCoherent = 16;  // cache-policy operand: sc1
+__device__ __forceinline__ f32x4 coherent_load4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kCoherent));
+}
+__device__ __forceinline__ void coherent_store4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off,
+                                                f32x4 v) {
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(f32x4, v), r, byte_off, 0, kCoherent);
+}
 // s_waitcnt vmcnt(0): this wave's vector memory operations have completed.
 __device__ __forceinline__ void wait_vm_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 __device__ __forceinline__ void advance_counter(uint32_t* cnt, uint32_t v) {

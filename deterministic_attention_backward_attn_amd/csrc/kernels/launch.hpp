@@ -6,6 +6,10 @@
 
 namespace dash {
 
+// Largest number of items (KV tile x Q block pairs) in one unit's work list;
+// the backward stages a unit's list in LDS.
+constexpr int kMaxUnitItems = 1024;
+
 // Arguments of the persistent backward kernel.  All pointers are device
 // pointers.  Per-head tensors are indexed by head = b*H + h.
 struct BwdArgs {
