@@ -8,9 +8,9 @@ and the dQ conversion.  O and LSE come from the library's forward before
 timing.  Default workload: B=1, H=32, N=16384, d=128, bf16, causal mask.
 
 Every schedule (atomic, naive, descending, shift) is timed the same way;
-`value` is the backward TFLOP/s of the primary deterministic schedule
-(descending for a causal mask, shift for a full mask), FLOPs counted as
-2.5x the forward's 4*B*H*N^2*d, halved for a causal mask.  Also reported:
+`value` is the backward TFLOP/s of the fastest deterministic schedule in
+the run (or of --primary), FLOPs counted as 2.5x the forward's
+4*B*H*N^2*d, halved for a causal mask.  Also reported:
 % of the dense bf16 MFMA peak, the deterministic / atomic throughput ratio
 per schedule, the backward kernel's own roofline figures (HIP events around
 its launch), and the fp64 CPU oracle timed on a bounded sample of heads.
@@ -44,10 +44,12 @@ def kernel_source_hash() -> str:
     return h.hexdigest()[:16]
 
 
-def read_traffic(workload: str):
-    """HBM bytes per launch from the committed rocprofv3 counter summary, or
-    None if absent or taken on a different kernel source."""
-    path = os.path.join(ROOT, "profiles", f"attn_bwd_{workload}_traffic.md")
+def read_traffic(workload: str, schedule: str):
+    """Bytes per launch moved past L2 by the backward kernel, from the
+    committed rocprofv3 counter summary (FETCH_SIZE + WRITE_SIZE, calibrated
+    against a plain copy), or None if absent or taken on other kernel
+    sources."""
+    path = os.path.join(ROOT, "profiles", f"attn_bwd_{workload}_{schedule}_traffic.md")
     if not os.path.exists(path):
         return None
     text = open(path).read()
@@ -105,7 +107,8 @@ def main():
     ap.add_argument("--mask", choices=["causal", "full"], default=None,
                     help="mask (default: the workload's first)")
     ap.add_argument("--schedules", default="atomic,naive,descending,shift")
-    ap.add_argument("--primary", default=None, help="schedule reported as value")
+    ap.add_argument("--primary", default=None,
+                    help="schedule reported as value (default: fastest deterministic one)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-workers", type=int, default=16)
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -131,9 +134,10 @@ def main():
     mask = args.mask or w.masks[0]
     causal = mask == "causal"
     scheds = [s for s in args.schedules.split(",") if s]
-    primary = args.primary or ("descending" if causal else "shift")
-    if primary not in scheds:
-        scheds.append(primary)
+    if args.primary and args.primary not in scheds:
+        scheds.append(args.primary)
+    if not any(s != "atomic" for s in scheds):
+        scheds.append("shift")
 
     t_gen = time.perf_counter()
     raw = make_workload_inputs(w)
@@ -156,7 +160,7 @@ def main():
     o, lse = D.attn_fwd(dev["q"], dev["k"], dev["v"], causal=causal)
     delta = torch.empty_like(lse)
     dq, dk, dv = (torch.empty_like(dev["q"]) for _ in range(3))
-    ws = D.alloc_workspace(dev["q"], causal, primary)
+    ws = D.alloc_workspace(dev["q"], causal, "naive")
     flops = w.flops_bwd(causal)
 
     def step(sched, events=None):
@@ -193,6 +197,8 @@ def main():
               flush=True)
 
     peak = PEAK_TFLOPS[w.dtype]
+    primary = args.primary or min((s for s in results if s != "atomic"),
+                                  key=lambda s: results[s]["ms_per_step"])
     prim = results[primary]
     out = {
         "metric": METRIC,
@@ -218,7 +224,7 @@ def main():
     achieved = flops / (prim["kernel_ms"] * 1e-3) / 1e12
     out["roofline"] = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                        "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                       "traffic": read_traffic(w.name),
+                       "traffic": read_traffic(w.name, primary),
                        "kernel": f"bwd_kernel ({primary})"}
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample of heads", file=sys.stderr, flush=True)

@@ -1,0 +1,139 @@
+"""Turn rocprofv3 CSV output into the short text summaries kept under profiles/.
+
+  python -m deterministic_attention_backward_attn_amd.rocprof_summary stats \\
+      --csv <dir>/<prefix>_kernel_stats.csv --cmd "<command>" --out profiles/<name>.md
+
+  python -m deterministic_attention_backward_attn_amd.rocprof_summary traffic \\
+      --fetch-csv <dir>/<prefix>_counter_collection.csv \\
+      --write-csv <dir>/<prefix>_counter_collection.csv \\
+      --copy-bytes N --kernel bwd_kernel --flops F \\
+      --cmd-fetch "<command>" --cmd-write "<command>" --out profiles/<name>.md
+
+The traffic summary scales each kernel's FETCH_SIZE / WRITE_SIZE (KiB per
+dispatch) by the factor that makes the same counter read the known size of a
+plain device copy run in the same process, and records the hash of the
+backward kernel's sources so that a reader can tell whether the figure still
+describes the current kernel.
+"""
+from __future__ import annotations
+
+import argparse
+import csv
+import hashlib
+import os
+import statistics
+import sys
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+KERNEL_SOURCES = ["deterministic_attention_backward_attn_amd/csrc/kernels/attn_bwd.hip",
+                  "deterministic_attention_backward_attn_amd/csrc/kernels/common.hpp"]
+
+
+def kernel_source_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def _short(name: str, n: int = 110) -> str:
+    name = name.replace("dash::", "")
+    return name if len(name) <= n else name[: n - 3] + "..."
+
+
+def stats(args):
+    rows = list(csv.DictReader(open(args.csv)))
+    lines = ["# rocprofv3 kernel statistics", "", f"Command: `{args.cmd}`", "",
+             "| kernel | calls | avg us | min us | max us | total ms | % |",
+             "|---|---|---|---|---|---|---|"]
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        lines.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
+                     f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
+                     f"{float(r['TotalDurationNs']) / 1e6:.3f} | {float(r['Percentage']):.1f} |")
+    lines += ["", f"kernel_source_sha256: {kernel_source_hash()}", ""]
+    _write(args.out, lines)
+
+
+def _per_dispatch(path, counter):
+    out = {}
+    for r in csv.DictReader(open(path)):
+        if r["Counter_Name"] != counter:
+            continue
+        key = int(r["Dispatch_Id"])
+        out.setdefault(key, [r["Kernel_Name"], 0.0, int(r["End_Timestamp"]) - int(r["Start_Timestamp"])])
+        out[key][1] += float(r["Counter_Value"])
+    return out
+
+
+def traffic(args):
+    fetch = _per_dispatch(args.fetch_csv, "FETCH_SIZE")
+    write = _per_dispatch(args.write_csv, "WRITE_SIZE")
+
+    def copy_kib(d):
+        # the largest elementwise copy dispatch is the calibration copy
+        cands = [v for v in d.values() if "copy" in v[0].lower() or "elementwise" in v[0].lower()]
+        if not cands:
+            raise SystemExit("no copy dispatch found for calibration")
+        return max(cands, key=lambda v: v[1])[1]
+
+    known_kib = args.copy_bytes / 1024.0
+    f_fac = known_kib / copy_kib(fetch)
+    w_fac = known_kib / copy_kib(write)
+    fk = [v[1] for v in fetch.values() if args.kernel in v[0]]
+    wk = [v[1] for v in write.values() if args.kernel in v[0]]
+    dur = [v[2] for v in fetch.values() if args.kernel in v[0]]
+    if not fk or not wk:
+        raise SystemExit(f"no dispatch of {args.kernel}")
+    fetch_b = statistics.mean(fk) * f_fac * 1024
+    write_b = statistics.mean(wk) * w_fac * 1024
+    lines = ["# HBM traffic of the backward kernel (rocprofv3 counters)", "",
+             f"FETCH_SIZE pass: `{args.cmd_fetch}`", "",
+             f"WRITE_SIZE pass: `{args.cmd_write}`", "",
+             f"Calibration: a plain device copy of {args.copy_bytes} bytes in the same process; "
+             f"FETCH_SIZE factor {f_fac:.4f}, WRITE_SIZE factor {w_fac:.4f} "
+             f"(known bytes / counter reading).", "",
+             f"Dispatches of `{args.kernel}`: {len(fk)}; raw FETCH_SIZE {statistics.mean(fk):.0f} KiB, "
+             f"raw WRITE_SIZE {statistics.mean(wk):.0f} KiB per dispatch.", "",
+             f"fetch_bytes_per_launch: {fetch_b:.6g}",
+             f"write_bytes_per_launch: {write_b:.6g}",
+             f"traffic_bytes_per_launch: {fetch_b + write_b:.6g}"]
+    if args.flops:
+        lines.append(f"arithmetic_intensity_flop_per_byte: {args.flops / (fetch_b + write_b):.1f}")
+    if dur:
+        lines.append(f"counter_pass_avg_duration_us: {statistics.mean(dur) / 1e3:.1f} "
+                     "(counter passes serialise dispatches; not a timing figure)")
+    lines += [f"kernel_source_sha256: {kernel_source_hash()}", ""]
+    _write(args.out, lines)
+
+
+def _write(path, lines):
+    text = "\n".join(lines)
+    if path:
+        with open(path, "w") as f:
+            f.write(text)
+    print(text)
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    sub = ap.add_subparsers(dest="mode", required=True)
+    s = sub.add_parser("stats")
+    s.add_argument("--csv", required=True)
+    s.add_argument("--cmd", required=True)
+    s.add_argument("--out")
+    t = sub.add_parser("traffic")
+    t.add_argument("--fetch-csv", required=True)
+    t.add_argument("--write-csv", required=True)
+    t.add_argument("--copy-bytes", type=int, required=True)
+    t.add_argument("--kernel", default="bwd_kernel")
+    t.add_argument("--flops", type=float, default=0.0)
+    t.add_argument("--cmd-fetch", required=True)
+    t.add_argument("--cmd-write", required=True)
+    t.add_argument("--out")
+    args = ap.parse_args(argv)
+    (stats if args.mode == "stats" else traffic)(args)
+
+
+if __name__ == "__main__":
+    main(sys.argv[1:])
