@@ -152,7 +152,8 @@ def attn_bwd(q, k, v, do, lse, delta, *, schedule="naive", causal=False, scale=N
     preallocated (dq, dk, dv).  `debug`: optional dict with keys spin_limit,
     jitter_seed, poison_q (1-based, 0 = off), partials (float32 tensor),
     kernel_events (two raw hipEvent_t handles), wait_stats (int64 tensor of
-    at least 4*4096*4 entries)."""
+    at least 4*4096*4 entries), placement (0 automatic, 1 device-wide, 2 XCD
+    groups with L2-coherent accumulator, 3 XCD groups device-coherent)."""
     torch = _torch()
     lib = load()
     _same_shape(q, k, v, do)
@@ -176,6 +177,7 @@ def attn_bwd(q, k, v, do, lse, delta, *, schedule="naive", causal=False, scale=N
         dbg = Debug(int(debug.get("spin_limit", 0)), int(debug.get("jitter_seed", 0)),
                     int(debug.get("poison_q", 0)),
                     _ptr(debug["partials"]) if debug.get("partials") is not None else None)
+        dbg.placement = int(debug.get("placement", 0))
         if debug.get("wait_stats") is not None:
             dbg.wait_stats = _ptr(debug["wait_stats"])
         ev = debug.get("kernel_events")

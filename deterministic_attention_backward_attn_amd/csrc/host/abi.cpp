@@ -19,7 +19,7 @@ namespace {
 using dash::Sched;
 using dash::Tables;
 
-constexpr size_t kHeaderBytes = 256;   // [0] status, [1] work counter
+constexpr size_t kHeaderBytes = 256;   // status, work counters, XCD census (64 words)
 constexpr uint32_t kDefaultSpin = 1u << 21;  // polls before giving up (seconds)
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
@@ -153,6 +153,7 @@ dash_status run_bwd(const dash_attn_desc* desc, dash_schedule schedule, const vo
   const Sched s = (Sched)schedule;
   const bool ordered = s != Sched::Atomic;
   if (dbg && (dbg->poison_q < 0 || dbg->poison_q > desc->N / br)) return DASH_ERR_INVALID_ARG;
+  if (dbg && (dbg->placement < 0 || dbg->placement > 3)) return DASH_ERR_INVALID_ARG;
 
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return DASH_ERR_HIP;
@@ -209,6 +210,11 @@ dash_status run_bwd(const dash_attn_desc* desc, dash_schedule schedule, const vo
   a.total_units = (int)total_units;
   a.p_eff = p_eff;
   a.dynamic = dynamic;
+  // placement: XCD-local groups measured faster only for the naive order
+  // under a causal mask (its long hand-off chains gain from the shorter
+  // L2-local hand-off); device-wide is as fast or faster everywhere else
+  a.xcd_mode = (s == Sched::Naive && causal) ? 1 : 0;
+  if (dbg && dbg->placement) a.xcd_mode = dbg->placement - 1;
   a.scale = scale_of(desc);
   a.scale_log2 = a.scale * 1.4426950408889634f;
   a.spin_limit = (dbg && dbg->spin_limit) ? dbg->spin_limit : kDefaultSpin;

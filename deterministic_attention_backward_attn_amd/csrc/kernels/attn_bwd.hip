@@ -119,15 +119,15 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
   constexpr int LR = 36;
   __shared__ __align__(16) float sRow[ORDERED ? NW : 1][ORDERED ? QT * 32 * LR : 4];
   __shared__ int sUnit;
+  __shared__ int sPlace[5];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
   const int w = tid >> 6;
   const int l32 = lane & 31;
   const int hh = lane >> 5;
-  const int grp = lane >> 4;           // 16-lane group
   const int j16 = lane & 15;
-  const int gcol = 16 * (grp & 1);     // column offset of this lane's group
+  const int gcol = 16 * ((lane >> 4) & 1);  // column offset of this lane's 16-lane group
   const int N = a.N;
   const int n_sub = N / BR;
   uint32_t* status = a.header;
@@ -135,16 +135,66 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
   const int col0 = w % NTD;            // first dQ column tile of this wave
   const int row0 = NW > NTD ? w / NTD : 0;
 
-  if (a.dynamic == 0 && (int)blockIdx.x >= a.p_eff) return;
-  int unit = blockIdx.x;
   // diagnostics (lane 0 of each wave): cycles in ordered waits, waits, waits
   // that had to poll more than once, cycles of the whole unit loop
   uint64_t st_wait = 0, st_waits = 0, st_spun = 0;
   const uint64_t st_t0 = a.wait_stats ? (uint64_t)clock64() : 0;
 
-  while (unit < a.total_units) {
-    const int head = unit / a.units_per_head;
-    const int lu = unit - head * a.units_per_head;
+  // ---- placement -------------------------------------------------------
+  // XCD-local mode: every workgroup reads the XCD it runs on, a census
+  // (all workgroups are resident: cooperative launch) counts workgroups per
+  // XCD, and the heads are dealt round-robin to the XCDs present.  All units
+  // of a head then run on one XCD, so its ordered dQ hand-offs stay inside
+  // that XCD's L2 (L2-coherent accumulator accesses) and its Q/dO tiles are
+  // reused from that L2.  The shift schedule needs a whole head resident, so
+  // if some XCD has fewer workgroups than a head has units, every workgroup
+  // falls back to one device-wide group with device-coherent accesses.
+  // Header words: [0] status, [1] device work counter, [2] census arrivals,
+  // [4..19] workgroups per XCD, [20..35] work counter per XCD group.
+  const int U = a.units_per_head;
+  int grp = 0, n_grp = 1, li = blockIdx.x, W = gridDim.x;  // XCD group of this workgroup
+  bool grouped = false;  // units taken from this XCD's own list
+  bool xl = false;       // ... and accumulator accesses coherent in its L2 only
+  if (a.xcd_mode) {
+    if (tid == 0) {
+      const uint32_t x = xcc_id();
+      const uint32_t mine = __hip_atomic_fetch_add(&a.header[4 + x], 1u, __ATOMIC_RELAXED,
+                                                   __HIP_MEMORY_SCOPE_AGENT);
+      __hip_atomic_fetch_add(&a.header[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      wait_counter(&a.header[2], gridDim.x, status, spin_limit);
+      int active = 0, my_grp = 0, fits = 1;
+      for (uint32_t k = 0; k < 16; ++k) {
+        const uint32_t c = load_relaxed_agent(&a.header[4 + k]);
+        if (c == 0) continue;
+        if (k == x) my_grp = active;
+        if (!a.dynamic && (int)c < U) fits = 0;
+        ++active;
+      }
+      sPlace[0] = my_grp;
+      sPlace[1] = active;
+      sPlace[2] = (int)mine;
+      sPlace[3] = (int)load_relaxed_agent(&a.header[4 + x]);
+      sPlace[4] = fits && load_relaxed_agent(status) == 0u;
+    }
+    __syncthreads();
+    if (sPlace[4]) {
+      grouped = true;
+      xl = a.xcd_mode == 1;
+      grp = sPlace[0];
+      n_grp = sPlace[1];
+      li = sPlace[2];
+      W = sPlace[3];
+    }
+  }
+  const int BH = a.total_units / U;
+  const int n_units = ((BH - grp + n_grp - 1) / n_grp) * U;  // units of this group
+  const int stride_static = grouped ? (W / U) * U : a.p_eff;
+  uint32_t* work_counter = grouped ? &a.header[20 + grp] : &a.header[1];
+  int unit = (a.dynamic == 0 && li >= stride_static) ? n_units : li;
+
+  while (unit < n_units) {
+    const int head = grp + n_grp * (unit / U);
+    const int lu = unit - (unit / U) * U;
     const size_t hoff = (size_t)head * N * D;
     const T* Qg = reinterpret_cast<const T*>(a.q) + hoff;
     const T* Kg = reinterpret_cast<const T*>(a.k) + hoff;
@@ -176,7 +226,7 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
     bool rel_pending = false;                    // stores issued, counter not yet advanced
     int rel_qtile = 0, rel_rank = 0;
 
-    uint4 pq[CPT], pdo[CPT];
+    u32x4 pq[CPT], pdo[CPT];
     float pstat = 0.f;
     auto fetch = [&](int g) {
       const int qtile = (sItems[g / RHO].x >> 16) * RHO + (g % RHO);
@@ -187,11 +237,13 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
         const int row = c / (D / VEC);
         const int col = (c % (D / VEC)) * VEC;
         const uint32_t off = (uint32_t)((q0 + row) * D + col);
-        pq[i] = *reinterpret_cast<const uint4*>(Qg + off);
-        pdo[i] = *reinterpret_cast<const uint4*>(dOg + off);
+        pq[i] = *reinterpret_cast<const u32x4*>(Qg + off);
+        pdo[i] = *reinterpret_cast<const u32x4*>(dOg + off);
       }
-      if (tid < BR) pstat = lse_g[q0 + tid] * kLog2e;
-      else if (tid < 2 * BR) pstat = del_g[q0 + tid - BR];
+      // one load into one register (a branch per source would make the
+      // merge wait for every load in flight)
+      const float* src = tid < BR ? lse_g + (q0 + tid) : del_g + (q0 + tid - BR);
+      if (tid < 2 * BR) pstat = *src;
     };
     auto stage = [&](int buf) {
 #pragma unroll
@@ -199,10 +251,10 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
         const int c = tid + i * NT;
         const int row = c / (D / VEC);
         const int col = (c % (D / VEC)) * VEC;
-        *reinterpret_cast<uint4*>(&sQ[buf][row * LQ + col]) = pq[i];
-        *reinterpret_cast<uint4*>(&sdO[buf][row * LQ + col]) = pdo[i];
+        *reinterpret_cast<u32x4*>(&sQ[buf][row * LQ + col]) = pq[i];
+        *reinterpret_cast<u32x4*>(&sdO[buf][row * LQ + col]) = pdo[i];
       }
-      if (tid < BR) sLSE[buf][tid] = pstat;
+      if (tid < BR) sLSE[buf][tid] = pstat * kLog2e;
       else if (tid < 2 * BR) sDel[buf][tid - BR] = pstat;
     };
 
@@ -273,7 +325,9 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
 #pragma unroll
       for (int i = 0; i < QT; ++i)
 #pragma unroll
-        for (int k = 0; k < 4; ++k) lv[i][k] = coherent_load4(dq_rs, 4 * chunk_off(q0, i, k));
+        for (int k = 0; k < 4; ++k)
+          lv[i][k] = xl ? coherent_load4<kXcdCoherent>(dq_rs, 4 * chunk_off(q0, i, k))
+                        : coherent_load4<kCoherent>(dq_rs, 4 * chunk_off(q0, i, k));
       p_loaded = true;
     };
     // p_seen: the counter value lane 0 read (without waiting) right after the
@@ -325,7 +379,8 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
               *reinterpret_cast<f32x4*>(&dqo[off]) = v;
             }
           } else {
-            coherent_store4(dq_rs, 4 * off, v);
+            if (xl) coherent_store4<kXcdCoherent>(dq_rs, 4 * off, v);
+            else coherent_store4<kCoherent>(dq_rs, 4 * off, v);
           }
         }
       }
@@ -572,13 +627,13 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
     // next unit
     if (a.dynamic) {
       if (tid == 0)
-        sUnit = (int)__hip_atomic_fetch_add(&a.header[1], 1u, __ATOMIC_RELAXED,
-                                            __HIP_MEMORY_SCOPE_AGENT) + (int)gridDim.x;
+        sUnit = (int)__hip_atomic_fetch_add(work_counter, 1u, __ATOMIC_RELAXED,
+                                            __HIP_MEMORY_SCOPE_AGENT) + W;
       __syncthreads();
       unit = sUnit;
       __syncthreads();
     } else {
-      unit += a.p_eff;
+      unit += stride_static;
     }
   }
   if (a.wait_stats != nullptr && lane == 0) {

@@ -25,6 +25,7 @@ typedef float f32x16 __attribute__((ext_vector_type(16)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x4 __attribute__((ext_vector_type(4)));
 typedef uint16_t u16x8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr float kLog2e = 1.4426950408889634f;
 
@@ -129,14 +130,27 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)num_bytes,
                                            0x00020000);
 }
-constexpr int kCoherent = 16;  // cache-policy operand: sc1
+// Cache-policy operands: sc1 = coherent across the device (every XCD);
+// sc0 = bypasses the CU's L1 and is served by the XCD's L2, so it is
+// coherent among the workgroups of one XCD.
+constexpr int kCoherent = 16;
+constexpr int kXcdCoherent = 1;
+template <int POLICY = kCoherent>
 __device__ __forceinline__ f32x4 coherent_load4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off) {
-  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, kCoherent));
+  return __builtin_bit_cast(f32x4, __builtin_amdgcn_raw_buffer_load_b128(r, byte_off, 0, POLICY));
 }
+template <int POLICY = kCoherent>
 __device__ __forceinline__ void coherent_store4(__amdgpu_buffer_rsrc_t r, uint32_t byte_off,
                                                 f32x4 v) {
-  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(f32x4, v), r, byte_off, 0, kCoherent);
+  __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(f32x4, v), r, byte_off, 0, POLICY);
 }
+// Index of the XCD (accelerator complex die) this wave runs on.
+__device__ __forceinline__ uint32_t xcc_id() {
+  uint32_t x;
+  asm volatile("s_getreg_b32 %0, hwreg(HW_REG_XCC_ID)" : "=s"(x));
+  return x & 0xFu;
+}
+
 // s_waitcnt vmcnt(0): this wave's vector memory operations have completed.
 __device__ __forceinline__ void wait_vm_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 __device__ __forceinline__ void advance_counter(uint32_t* cnt, uint32_t v) {

@@ -33,6 +33,8 @@ struct BwdArgs {
   int total_units;        // units_per_head * BH
   int p_eff;              // static policy: workgroups that take units
   int dynamic;            // 1: take units from the work counter
+  int xcd_mode;           // 0 device-wide; XCD-local groups when they fit with
+                          // 1: L2-coherent, 2: device-coherent accumulator
   float scale;            // softmax scale s
   float scale_log2;       // s * log2(e)
   uint32_t spin_limit;

@@ -171,6 +171,17 @@ dash_status dash_attn_bwd_status(const void* workspace, void* stream);
  *                   immediately before and after the backward kernel's
  *                   launch (excluding the workspace clear and the dQ
  *                   conversion), for timing that kernel alone.
+ *   placement       where units run; results are bit-identical for every
+ *                   value, only speed differs.  0 = automatic (XCD groups
+ *                   for the naive schedule with a causal mask, device-wide
+ *                   otherwise); 1 = device-wide (every workgroup takes units
+ *                   from one list); 2 = XCD groups: the heads are dealt to the
+ *                   XCDs, each head's units run on the workgroups of one XCD
+ *                   and its accumulator is kept coherent in that XCD's L2;
+ *                   3 = XCD groups with device-coherent accumulator accesses.
+ *                   XCD groups fall back to device-wide when a head's units
+ *                   cannot all be resident on one XCD (static schedules).
+ *                   Other values: DASH_ERR_INVALID_ARG.
  *   wait_stats      non-NULL: device uint64 buffer of at least
  *                   4 * 4096 * 4 entries; for each workgroup g and wave w,
  *                   entries [(g*waves + w)*4 + k] receive: k=0 shader-clock
@@ -185,6 +196,7 @@ typedef struct {
   float* partials;
   void* kernel_events[2];
   uint64_t* wait_stats;
+  int32_t placement;
 } dash_bwd_debug;
 
 dash_status dash_attn_bwd_debug(const dash_attn_desc* desc, dash_schedule schedule,

@@ -12,6 +12,8 @@
   ends the kernel normally and is reported as DASH_ERR_ORDER_TIMEOUT.
 * Causal: KV tiles never read earlier Q blocks, so perturbing those leaves
   their dK, dV bit-identical.
+* Placement (device-wide or XCD groups, L2- or device-coherent accumulator)
+  changes no bit.
 """
 import numpy as np
 import pytest
@@ -185,3 +187,18 @@ def test_causal_tiles_ignore_earlier_q_blocks():
     for a, b in zip(ref[1:], out[1:]):
         assert torch.equal(a[:, :, J * tile:].view(torch.int16), b[:, :, J * tile:].view(torch.int16))
         assert not torch.equal(a[:, :, :J * tile], b[:, :, :J * tile])
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_placement_changes_no_bit(causal):
+    """Units of a head on one XCD (automatic) or spread over the device:
+    same dQ order, so bit-identical results."""
+    require_gpu()
+    log(f"placement causal={causal}")
+    dev, lse, delta = _prep(2, 16, 2048, 128, "bf16", causal, 8100)
+    for sched in ORDERED:
+        ref = [t.clone() for t in _bwd(dev, lse, delta, sched, causal, debug={"placement": 1})]
+        for place in (0, 2, 3):
+            out = _bwd(dev, lse, delta, sched, causal, debug={"placement": place})
+            for x, y in zip(ref, out):
+                assert torch.equal(x.view(torch.int16), y.view(torch.int16)), (sched, place)

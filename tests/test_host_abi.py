@@ -130,6 +130,11 @@ def test_argument_errors_without_launch():
     assert lib.dash_attn_bwd_debug(ctypes.byref(desc), 1, *args, ws_ok, None, None) == 1
     dbg = _lib.Debug(0, 0, 10_000, None)
     assert lib.dash_attn_bwd_debug(ctypes.byref(desc), 1, *args, ws_ok, ctypes.byref(dbg), None) == 1
+    for bad in (-1, 4):  # placement out of range
+        dbg = _lib.Debug()
+        dbg.placement = bad
+        assert lib.dash_attn_bwd_debug(ctypes.byref(desc), 1, *args, ws_ok, ctypes.byref(dbg),
+                                       None) == 1
     # host-only argument checks
     assert lib.dash_schedule_predict(0, 0, 1, 1, 1, None, None) == 1
     assert lib.dash_litmus_ordered_add(0, 1, FAKE, FAKE, FAKE, FAKE, 0, None) == 1
