@@ -210,10 +210,10 @@ dash_status run_bwd(const dash_attn_desc* desc, dash_schedule schedule, const vo
   a.total_units = (int)total_units;
   a.p_eff = p_eff;
   a.dynamic = dynamic;
-  // placement: XCD-local groups measured faster only for the naive order
-  // under a causal mask (its long hand-off chains gain from the shorter
-  // L2-local hand-off); device-wide is as fast or faster everywhere else
-  a.xcd_mode = (s == Sched::Naive && causal) ? 1 : 0;
+  // placement: the ordered schedules run each head on one XCD with its
+  // accumulator coherent in that XCD's L2 (measured as fast or faster on
+  // every workload); the atomic reference gains nothing from it
+  a.xcd_mode = ordered ? 1 : 0;
   if (dbg && dbg->placement) a.xcd_mode = dbg->placement - 1;
   a.scale = scale_of(desc);
   a.scale_log2 = a.scale * 1.4426950408889634f;

@@ -219,8 +219,8 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
     f32x16 accdK[NTD], accdV[NTD];
     int cur_kv = -1;
 
-    // deferred ordered add: partial of the previous sub-tile
-    f32x16 accQp[QT];
+    // deferred ordered add: partial of the previous sub-tile, held row-major
+    // in this wave's LDS area (sRow) from the end of its sub-tile
     f32x4 lv[QT][4];                             // accumulator values read back
     int p_qtile = -1, p_rank = 0, p_flags = 0;  // flags: bit0 last
     bool rel_pending = false;                    // stores issued, counter not yet advanced
@@ -351,17 +351,9 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
       }
       const bool last = (p_flags & 1) != 0;
       const int q0 = p_qtile * BR;
-      // transpose the partial to row-major through this wave's LDS area
-      float* row = sRow[w];
-#pragma unroll
-      for (int i = 0; i < QT; ++i)
-#pragma unroll
-        for (int gq = 0; gq < 4; ++gq)
-          *reinterpret_cast<f32x4*>(&row[(i * 32 + l32) * LR + 8 * gq + 4 * hh]) =
-              f32x4{accQp[i][4 * gq], accQp[i][4 * gq + 1], accQp[i][4 * gq + 2],
-                    accQp[i][4 * gq + 3]};
-      __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): this wave's LDS writes done
-      __builtin_amdgcn_wave_barrier();
+      // the partial was written by this wave at the end of the previous
+      // sub-tile (one wave's LDS accesses complete in issue order)
+      const float* row = sRow[w];
 #pragma unroll
       for (int i = 0; i < QT; ++i) {
 #pragma unroll
@@ -470,14 +462,30 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
         accS[mt] = zero16();
         accP[mt] = zero16();
       }
+      // in two halves over d: all A fragments of a half are read first, then
+      // its MFMAs, so the LDS reads overlap each other and the MFMAs instead
+      // of each MFMA waiting on its own operand (the scheduling barriers keep
+      // the compiler from interleaving them back)
 #pragma unroll
-      for (int ks = 0; ks < DK; ++ks) {
+      for (int h2 = 0; h2 < 2; ++h2) {
+        frag qa[DK / 2][MT], oa[DK / 2][MT];
 #pragma unroll
-        for (int mt = 0; mt < MT; ++mt) {
-          const int off = (mt * 32 + l32) * LQ + ks * KSTEP + hh * KPL;
-          accS[mt] = E::mma(load_frag(&cQ[off]), Kreg[ks], accS[mt]);
-          accP[mt] = E::mma(load_frag(&cdO[off]), Vreg[ks], accP[mt]);
-        }
+        for (int k2 = 0; k2 < DK / 2; ++k2)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            const int off = (mt * 32 + l32) * LQ + (h2 * DK / 2 + k2) * KSTEP + hh * KPL;
+            qa[k2][mt] = load_frag(&cQ[off]);
+            oa[k2][mt] = load_frag(&cdO[off]);
+          }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k2 = 0; k2 < DK / 2; ++k2)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt) {
+            accS[mt] = E::mma(qa[k2][mt], Kreg[h2 * DK / 2 + k2], accS[mt]);
+            accP[mt] = E::mma(oa[k2][mt], Vreg[h2 * DK / 2 + k2], accP[mt]);
+          }
+        __builtin_amdgcn_sched_barrier(0);
       }
 
       // P and dS; dS^T to LDS.  bf16: P and dS are packed once (hardware
@@ -601,8 +609,16 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
       }
 
       if constexpr (ORDERED) {
+        // transpose the partial to row-major through this wave's LDS area
+        // now; its ordered add is finished during the next sub-tile
+        float* row = sRow[w];
 #pragma unroll
-        for (int i = 0; i < QT; ++i) accQp[i] = accQ[i];
+        for (int i = 0; i < QT; ++i)
+#pragma unroll
+          for (int gq = 0; gq < 4; ++gq)
+            *reinterpret_cast<f32x4*>(&row[(i * 32 + l32) * LR + 8 * gq + 4 * hh]) =
+                f32x4{accQ[i][4 * gq], accQ[i][4 * gq + 1], accQ[i][4 * gq + 2],
+                      accQ[i][4 * gq + 3]};
         p_qtile = qtile;
         p_rank = rank;
         p_flags = flags;

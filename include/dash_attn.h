@@ -173,8 +173,8 @@ dash_status dash_attn_bwd_status(const void* workspace, void* stream);
  *                   conversion), for timing that kernel alone.
  *   placement       where units run; results are bit-identical for every
  *                   value, only speed differs.  0 = automatic (XCD groups
- *                   for the naive schedule with a causal mask, device-wide
- *                   otherwise); 1 = device-wide (every workgroup takes units
+ *                   with the L2-coherent accumulator for the ordered
+ *                   schedules, device-wide for ATOMIC); 1 = device-wide (every workgroup takes units
  *                   from one list); 2 = XCD groups: the heads are dealt to the
  *                   XCDs, each head's units run on the workgroups of one XCD
  *                   and its accumulator is kept coherent in that XCD's L2;
