@@ -1,13 +1,21 @@
 """Turn rocprofv3 CSV output into the short text summaries kept under profiles/.
 
   python -m deterministic_attention_backward_attn_amd.rocprof_summary stats \\
-      --csv <dir>/<prefix>_kernel_stats.csv --cmd "<command>" --out profiles/<name>.md
+      --csv <dir>/<prefix>_kernel_stats.csv --cmd "<command>" --out profiles/<name>.md \\
+      [--trace <dir>/<prefix>_kernel_trace.csv --blocks atomic,naive,descending,shift \\
+       --block-size W+K]
 
   python -m deterministic_attention_backward_attn_amd.rocprof_summary traffic \\
       --fetch-csv <dir>/<prefix>_counter_collection.csv \\
       --write-csv <dir>/<prefix>_counter_collection.csv \\
       --copy-bytes N --kernel bwd_kernel --flops F \\
       --cmd-fetch "<command>" --cmd-write "<command>" --out profiles/<name>.md
+
+With --trace, the backward kernel's dispatches (in dispatch order) are cut
+into consecutive blocks of --block-size, one per name in --blocks (bench.py
+times its schedules one after another, W warm-up plus K timed launches
+each), and per-schedule durations are listed: the ordered schedules share
+one kernel instantiation, so the statistics table alone mixes them.
 
 The traffic summary scales each kernel's FETCH_SIZE / WRITE_SIZE (KiB per
 dispatch) by the factor that makes the same counter read the known size of a
@@ -51,6 +59,21 @@ def stats(args):
         lines.append(f"| `{_short(r['Name'])}` | {r['Calls']} | {float(r['AverageNs']) / 1e3:.1f} | "
                      f"{float(r['MinNs']) / 1e3:.1f} | {float(r['MaxNs']) / 1e3:.1f} | "
                      f"{float(r['TotalDurationNs']) / 1e6:.3f} | {float(r['Percentage']):.1f} |")
+    if args.trace:
+        rows = sorted(csv.DictReader(open(args.trace)), key=lambda r: int(r["Dispatch_Id"]))
+        bwd = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
+               for r in rows if "bwd_kernel" in r["Kernel_Name"]]
+        names = [b for b in args.blocks.split(",") if b]
+        if len(bwd) != len(names) * args.block_size:
+            raise SystemExit(f"{len(bwd)} backward dispatches, expected "
+                             f"{len(names)} x {args.block_size}")
+        lines += ["", "Backward kernel per schedule (dispatches in order, "
+                  f"{args.block_size} per schedule):", "",
+                  "| schedule | dispatches | avg us | min us | max us |", "|---|---|---|---|---|"]
+        for i, name in enumerate(names):
+            d = bwd[i * args.block_size:(i + 1) * args.block_size]
+            lines.append(f"| {name} | {len(d)} | {statistics.mean(d):.1f} | {min(d):.1f} | "
+                         f"{max(d):.1f} |")
     lines += ["", f"kernel_source_sha256: {kernel_source_hash()}", ""]
     _write(args.out, lines)
 
@@ -122,6 +145,9 @@ def main(argv=None):
     s.add_argument("--csv", required=True)
     s.add_argument("--cmd", required=True)
     s.add_argument("--out")
+    s.add_argument("--trace")
+    s.add_argument("--blocks", default="atomic,naive,descending,shift")
+    s.add_argument("--block-size", type=int, default=0)
     t = sub.add_parser("traffic")
     t.add_argument("--fetch-csv", required=True)
     t.add_argument("--write-csv", required=True)
