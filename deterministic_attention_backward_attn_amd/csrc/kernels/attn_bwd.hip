@@ -75,7 +75,7 @@ __device__ __forceinline__ bf16x8 tr_frag(const bf16_t* base, int ld, int r0, in
   return __builtin_bit_cast(bf16x8, u);
 }
 
-template <typename T, int D, int BC, int BR, bool CAUSAL, bool ORDERED>
+template <typename T, int D, int BC, int BR, bool CAUSAL, bool ORDERED, bool DEBUG>
 __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
   using E = Elt<T>;
   using frag = typename E::frag;
@@ -138,7 +138,7 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
   // diagnostics (lane 0 of each wave): cycles in ordered waits, waits, waits
   // that had to poll more than once, cycles of the whole unit loop
   uint64_t st_wait = 0, st_waits = 0, st_spun = 0;
-  const uint64_t st_t0 = a.wait_stats ? (uint64_t)clock64() : 0;
+  const uint64_t st_t0 = (DEBUG && a.wait_stats) ? (uint64_t)clock64() : 0;
 
   // ---- placement -------------------------------------------------------
   // XCD-local mode: every workgroup reads the XCD it runs on, a census
@@ -303,17 +303,17 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
     auto wait_turn = [&]() {
       const int rank = p_rank;
       if (lane == 0) {
-        const uint64_t t0 = a.wait_stats ? (uint64_t)clock64() : 0;
-        if (a.jitter_seed != 0u) {
+        const uint64_t t0 = (DEBUG && a.wait_stats) ? (uint64_t)clock64() : 0;
+        if (DEBUG && a.jitter_seed != 0u) {
           const uint32_t nap =
               hash32(a.jitter_seed ^ (uint32_t)(head * 7919 + p_qtile * 131 + cur_kv * 17 + w)) & 31u;
           for (uint32_t i = 0; i < nap; ++i) __builtin_amdgcn_s_sleep(8);
         }
-        const bool poisoned = a.poison_q >= 0 && head == 0 && p_qtile == a.poison_q && rank == 0;
+        const bool poisoned = DEBUG && a.poison_q >= 0 && head == 0 && p_qtile == a.poison_q && rank == 0;
         uint32_t polls = 0;
         if (poisoned) polls = wait_counter(counter(p_qtile), 0xFFFFFFFFu, status, spin_limit);
         else if (rank > 0) polls = wait_counter(counter(p_qtile), (uint32_t)rank, status, spin_limit);
-        if (a.wait_stats) {
+        if (DEBUG && a.wait_stats) {
           st_wait += (uint64_t)clock64() - t0;
           st_spun += polls > 0 ? 1u : 0u;
         }
@@ -339,12 +339,12 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
     };
     auto begin_add = [&]() {
       p_loaded = false;
-      if (p_rank == 0 || a.jitter_seed != 0u || a.poison_q >= 0) return;
+      if (p_rank == 0 || (DEBUG && (a.jitter_seed != 0u || a.poison_q >= 0))) return;
       const int ready = lane == 0 && p_seen == (uint32_t)p_rank;
       if (__builtin_amdgcn_readfirstlane(ready)) load_acc();
     };
     auto finish_add = [&]() {
-      if (a.wait_stats && lane == 0) st_waits += p_rank > 0 ? 1u : 0u;
+      if (DEBUG && a.wait_stats && lane == 0) st_waits += p_rank > 0 ? 1u : 0u;
       if (!p_loaded) {
         wait_turn();
         if (p_rank > 0) load_acc();
@@ -600,7 +600,7 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
       if constexpr (ORDERED) release();
       if (g + 2 < n_steps) fetch(g + 2);
 
-      if (a.partials != nullptr) {
+      if (DEBUG && a.partials != nullptr) {
         float* pp = a.partials + (((size_t)head * a.n_tiles + kv) * N) * D;
 #pragma unroll
         for (int i = 0; i < QT; ++i)
@@ -652,7 +652,7 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
       unit += stride_static;
     }
   }
-  if (a.wait_stats != nullptr && lane == 0) {
+  if (DEBUG && a.wait_stats != nullptr && lane == 0) {
     uint64_t* st = a.wait_stats + ((size_t)blockIdx.x * NW + w) * 4;
     st[0] = st_wait;
     st[1] = st_waits;
@@ -663,20 +663,28 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
 
 // ------------------------------------------------------------ dispatch
 
-template <typename T, int D, int BC, int BR>
-static void* pick(bool causal, bool ordered) {
+// DEBUG instantiations carry the test hooks (jitter, poison, partials dump,
+// wait statistics); the production kernels have none of their code.
+template <typename T, int D, int BC, int BR, bool DEBUG>
+static void* pick2(bool causal, bool ordered) {
   if (causal)
-    return ordered ? (void*)bwd_kernel<T, D, BC, BR, true, true>
-                   : (void*)bwd_kernel<T, D, BC, BR, true, false>;
-  return ordered ? (void*)bwd_kernel<T, D, BC, BR, false, true>
-                 : (void*)bwd_kernel<T, D, BC, BR, false, false>;
+    return ordered ? (void*)bwd_kernel<T, D, BC, BR, true, true, DEBUG>
+                   : (void*)bwd_kernel<T, D, BC, BR, true, false, DEBUG>;
+  return ordered ? (void*)bwd_kernel<T, D, BC, BR, false, true, DEBUG>
+                 : (void*)bwd_kernel<T, D, BC, BR, false, false, DEBUG>;
 }
 
-static void* select_bwd(int dtype, int d, bool causal, bool ordered, int* threads) {
-  if (dtype == 1 && d == 128) { *threads = 256; return pick<bf16_t, 128, 128, 32>(causal, ordered); }
-  if (dtype == 1 && d == 64) { *threads = 256; return pick<bf16_t, 64, 128, 64>(causal, ordered); }
-  if (dtype == 0 && d == 64) { *threads = 128; return pick<float, 64, 64, 64>(causal, ordered); }
-  if (dtype == 0 && d == 128) { *threads = 128; return pick<float, 128, 64, 32>(causal, ordered); }
+template <typename T, int D, int BC, int BR>
+static void* pick(bool causal, bool ordered, bool debug) {
+  return debug ? pick2<T, D, BC, BR, true>(causal, ordered)
+               : pick2<T, D, BC, BR, false>(causal, ordered);
+}
+
+static void* select_bwd(int dtype, int d, bool causal, bool ordered, bool debug, int* threads) {
+  if (dtype == 1 && d == 128) { *threads = 256; return pick<bf16_t, 128, 128, 32>(causal, ordered, debug); }
+  if (dtype == 1 && d == 64) { *threads = 256; return pick<bf16_t, 64, 128, 64>(causal, ordered, debug); }
+  if (dtype == 0 && d == 64) { *threads = 128; return pick<float, 64, 64, 64>(causal, ordered, debug); }
+  if (dtype == 0 && d == 128) { *threads = 128; return pick<float, 128, 64, 32>(causal, ordered, debug); }
   return nullptr;
 }
 
@@ -693,11 +701,17 @@ int bwd_waves(int dtype, int d) {
 
 hipError_t bwd_max_coresident(int dtype, int d, bool causal, bool ordered, int* blocks) {
   int threads = 0;
-  void* f = select_bwd(dtype, d, causal, ordered, &threads);
-  if (!f) return hipErrorInvalidValue;
   int per_cu = 0;
-  hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, f, threads, 0);
-  if (e != hipSuccess) return e;
+  // the test-hook instantiations must fit as many workgroups as production
+  for (int dbg = 0; dbg < 2; ++dbg) {
+    void* f = select_bwd(dtype, d, causal, ordered, dbg != 0, &threads);
+    if (!f) return hipErrorInvalidValue;
+    int n = 0;
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, threads, 0);
+    if (e != hipSuccess) return e;
+    per_cu = dbg == 0 ? n : (n < per_cu ? n : per_cu);
+  }
+  hipError_t e = hipSuccess;
   int dev = 0;
   e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
@@ -711,7 +725,9 @@ hipError_t bwd_max_coresident(int dtype, int d, bool causal, bool ordered, int* 
 hipError_t launch_bwd(int dtype, int d, bool causal, bool ordered, const BwdArgs& a, int grid,
                       hipStream_t stream) {
   int threads = 0;
-  void* f = select_bwd(dtype, d, causal, ordered, &threads);
+  const bool debug = a.jitter_seed != 0u || a.poison_q >= 0 || a.partials != nullptr ||
+                     a.wait_stats != nullptr;
+  void* f = select_bwd(dtype, d, causal, ordered, debug, &threads);
   if (!f) return hipErrorInvalidValue;
   BwdArgs copy = a;
   void* args[] = {&copy};
