@@ -61,11 +61,14 @@ __device__ __forceinline__ u16x4 lds_tr16(const bf16_t* p) {
 
 // Fragment whose 8 K slots are rows r0+{0..3} and r1+{0..3} of column
 // c0 + (lane's index in its 16-lane half-column group) of a row-major LDS
-// array with row stride `ld`; c0 already includes 16*(group%2).
-__device__ __forceinline__ bf16x8 tr_frag(const bf16_t* base, int ld, int r0, int r1, int c0,
+// array; c0 already includes 16*(group%2).  `ix(row, col)` gives the element
+// offset of (row, col) (padded or swizzled layouts); the 4 elements a lane
+// addresses never straddle a 16-byte chunk.
+template <typename IX>
+__device__ __forceinline__ bf16x8 tr_frag(const bf16_t* base, IX ix, int r0, int r1, int c0,
                                           int j) {
-  const u16x4 a = lds_tr16(base + (r0 + (j >> 2)) * ld + c0 + 4 * (j & 3));
-  const u16x4 b = lds_tr16(base + (r1 + (j >> 2)) * ld + c0 + 4 * (j & 3));
+  const u16x4 a = lds_tr16(base + ix(r0 + (j >> 2), c0 + 4 * (j & 3)));
+  const u16x4 b = lds_tr16(base + ix(r1 + (j >> 2), c0 + 4 * (j & 3)));
   u16x8 u;
 #pragma unroll
   for (int s = 0; s < 4; ++s) {
@@ -73,6 +76,22 @@ __device__ __forceinline__ bf16x8 tr_frag(const bf16_t* base, int ld, int r0, in
     u[s + 4] = b[s];
   }
   return __builtin_bit_cast(bf16x8, u);
+}
+
+// Bank-conflict-free layout of the bf16 row-major tiles sQ, sdO, sK (row
+// stride D, no padding): the 16-byte chunk c of row r is stored at chunk
+// c ^ swz(r).  The permutation keeps 16 consecutive rows of one chunk (the
+// S/dP operand reads) and 4 consecutive rows of 4 consecutive chunks (the
+// transposing reads) in distinct LDS banks, and every 16-lane run of the
+// row-major staging writes covers whole rows.
+template <int D>
+__device__ __forceinline__ int swz(int r) {
+  if constexpr (D == 128) {
+    return 4 * (r & 3) + ((r >> 2) & 3);
+  } else {
+    const int m = (r >> 1) & 7;
+    return ((m & 1) << 2) | (m >> 1);
+  }
 }
 
 template <typename T, int D, int BC, int BR, bool CAUSAL, bool ORDERED, bool DEBUG>
@@ -90,7 +109,8 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
   constexpr int MT = BR / 32;          // 32-row tiles of a Q sub-tile
   constexpr int NTD = D / 32;          // 32-column tiles over d
   constexpr int PAD = 16 / (int)sizeof(T);
-  constexpr int LQ = D + PAD;          // row stride of sQ, sdO, sK ([row][d])
+  constexpr bool SWZ = sizeof(T) == 2;  // bf16: swizzled sQ, sdO, sK
+  constexpr int LQ = SWZ ? D : D + PAD;  // row stride of sQ, sdO, sK ([row][d])
   constexpr int LS = BR + PAD;         // row stride of sdSt ([kv][q])
   constexpr int CPT = BR * D / VEC / NT;  // 16-byte chunks per thread per tensor
   // dQ output tiles of a wave: CPW column tiles x RPW row tiles
@@ -120,6 +140,12 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
   __shared__ __align__(16) float sRow[ORDERED ? NW : 1][ORDERED ? QT * 32 * LR : 4];
   __shared__ int sUnit;
   __shared__ int sPlace[5];
+  // element offset of (row, col) in sQ, sdO, sK
+  const auto qix = [](int r, int c) {
+    if constexpr (SWZ) return r * LQ + (((c >> 3) ^ swz<D>(r)) << 3) + (c & 7);
+    else return r * LQ + c;
+  };
+  const auto six = [](int r, int c) { return r * LS + c; };  // sdSt
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -251,8 +277,8 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
         const int c = tid + i * NT;
         const int row = c / (D / VEC);
         const int col = (c % (D / VEC)) * VEC;
-        *reinterpret_cast<u32x4*>(&sQ[buf][row * LQ + col]) = pq[i];
-        *reinterpret_cast<u32x4*>(&sdO[buf][row * LQ + col]) = pdo[i];
+        *reinterpret_cast<u32x4*>(&sQ[buf][qix(row, col)]) = pq[i];
+        *reinterpret_cast<u32x4*>(&sdO[buf][qix(row, col)]) = pdo[i];
       }
       if (tid < BR) sLSE[buf][tid] = pstat * kLog2e;
       else if (tid < 2 * BR) sDel[buf][tid - BR] = pstat;
@@ -424,7 +450,7 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
         for (int c = tid; c < BC * D / VEC; c += NT) {
           const int row = c / (D / VEC);
           const int col = (c % (D / VEC)) * VEC;
-          *reinterpret_cast<uint4*>(&sK[row * LQ + col]) =
+          *reinterpret_cast<uint4*>(&sK[qix(row, col)]) =
               *reinterpret_cast<const uint4*>(Kg + (uint32_t)((kv0 + row) * D + col));
         }
         __syncthreads();
@@ -434,7 +460,7 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
 #pragma unroll
           for (int ks = 0; ks < KK; ++ks) {
             if constexpr (KPL == 8) {
-              KT[cc][ks] = tr_frag(sK, LQ, ks * 16 + 8 * hh, ks * 16 + 8 * hh + 4, nt * 32 + gcol, j16);
+              KT[cc][ks] = tr_frag(sK, qix, ks * 16 + 8 * hh, ks * 16 + 8 * hh + 4, nt * 32 + gcol, j16);
             } else {
               KT[cc][ks] = load_frag(&sK[(ks * 2 + hh) * LQ + nt * 32 + l32]);
             }
@@ -473,7 +499,7 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
         for (int k2 = 0; k2 < DK / 2; ++k2)
 #pragma unroll
           for (int mt = 0; mt < MT; ++mt) {
-            const int off = (mt * 32 + l32) * LQ + (h2 * DK / 2 + k2) * KSTEP + hh * KPL;
+            const int off = qix(mt * 32 + l32, (h2 * DK / 2 + k2) * KSTEP + hh * KPL);
             qa[k2][mt] = load_frag(&cQ[off]);
             oa[k2][mt] = load_frag(&cdO[off]);
           }
@@ -553,8 +579,8 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
           if constexpr (KPL == 8) {
             // K slots: Q rows r0+{0..3}, r0+8+{0..3}, r0 = mt*32 + 16cc + 4h
             const int r0 = mt * 32 + 16 * cc + 4 * hh;
-            bo = tr_frag(cdO, LQ, r0, r0 + 8, nt * 32 + gcol, j16);
-            bq = tr_frag(cQ, LQ, r0, r0 + 8, nt * 32 + gcol, j16);
+            bo = tr_frag(cdO, qix, r0, r0 + 8, nt * 32 + gcol, j16);
+            bq = tr_frag(cQ, qix, r0, r0 + 8, nt * 32 + gcol, j16);
           } else {
             const int qrow = mt * 32 + crow(cc, hh);
             bo = load_frag(&cdO[qrow * LQ + nt * 32 + l32]);
@@ -585,7 +611,7 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
         for (int ks = 0; ks < KK; ++ks) {
           frag fa;
           if constexpr (KPL == 8) {
-            fa = tr_frag(cdSt, LS, ks * 16 + 8 * hh, ks * 16 + 8 * hh + 4, mt * 32 + gcol, j16);
+            fa = tr_frag(cdSt, six, ks * 16 + 8 * hh, ks * 16 + 8 * hh + 4, mt * 32 + gcol, j16);
           } else {
             fa = load_frag(&cdSt[(ks * 2 + hh) * LS + mt * 32 + l32]);
           }
