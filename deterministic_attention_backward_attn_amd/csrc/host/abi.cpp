@@ -37,8 +37,9 @@ dash_status check_desc(const dash_attn_desc* d) {
   if (d->N % tile) return DASH_ERR_UNSUPPORTED;
   // row indices (head * N + row) and unit counts are 32-bit on the device
   const long long heads = (long long)d->B * d->H;
-  // and offsets within one head (row * d + col) are 32-bit
-  if (heads * d->N >= (1LL << 31) || d->N / tile > 32767 || (long long)d->N * d->d >= (1LL << 31))
+  // and byte offsets within one head's fp32 accumulator (4 * (row * d + col))
+  // stay below 2^31, the out-of-range offset the kernel uses for idle loads
+  if (heads * d->N >= (1LL << 31) || d->N / tile > 32767 || (long long)d->N * d->d >= (1LL << 29))
     return DASH_ERR_UNSUPPORTED;
   return DASH_OK;
 }

@@ -254,7 +254,13 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
 
     u32x4 pq[CPT], pdo[CPT];
     float pstat = 0.f;
+    // Every sub-tile issues the same vector-memory sequence (accumulator
+    // loads, stores, counter peek, prefetch), with unneeded loads sent out of
+    // range (they read nothing) or to a valid duplicate: completions are
+    // counted in issue order, and a fixed sequence lets each wait cover only
+    // the loads it needs instead of everything in flight.
     auto fetch = [&](int g) {
+      g = g < n_steps ? g : n_steps - 1;  // past the end: a harmless re-read
       const int qtile = (sItems[g / RHO].x >> 16) * RHO + (g % RHO);
       const int q0 = qtile * BR;
 #pragma unroll
@@ -266,10 +272,11 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
         pq[i] = *reinterpret_cast<const u32x4*>(Qg + off);
         pdo[i] = *reinterpret_cast<const u32x4*>(dOg + off);
       }
-      // one load into one register (a branch per source would make the
-      // merge wait for every load in flight)
-      const float* src = tid < BR ? lse_g + (q0 + tid) : del_g + (q0 + tid - BR);
-      if (tid < 2 * BR) pstat = *src;
+      // one load into one register for every lane (lanes past 2*BR re-read a
+      // valid element and discard it)
+      const float* src = tid < BR ? lse_g + (q0 + tid)
+                                  : del_g + (q0 + (tid < 2 * BR ? tid - BR : 0));
+      pstat = *src;
     };
     auto stage = [&](int buf) {
 #pragma unroll
@@ -346,34 +353,36 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
       }
       __builtin_amdgcn_wave_barrier();
     };
-    auto load_acc = [&]() {
+    // loads of the accumulator values this wave adds to; `live` false sends
+    // them out of the buffer's range (they return 0 and touch no memory)
+    auto load_acc = [&](bool live) {
       const int q0 = p_qtile * BR;
 #pragma unroll
       for (int i = 0; i < QT; ++i)
 #pragma unroll
-        for (int k = 0; k < 4; ++k)
-          lv[i][k] = xl ? coherent_load4<kXcdCoherent>(dq_rs, 4 * chunk_off(q0, i, k))
-                        : coherent_load4<kCoherent>(dq_rs, 4 * chunk_off(q0, i, k));
-      p_loaded = true;
+        for (int k = 0; k < 4; ++k) {
+          const uint32_t off = live ? 4 * chunk_off(q0, i, k) : kOutOfRange;
+          lv[i][k] = xl ? coherent_load4<kXcdCoherent>(dq_rs, off)
+                        : coherent_load4<kCoherent>(dq_rs, off);
+        }
+      p_loaded = live;
     };
     // p_seen: the counter value lane 0 read (without waiting) right after the
     // partial was computed; if it already shows this wave's turn, the
     // accumulator loads start at the top of the next sub-tile.
     uint32_t p_seen = 0;
-    auto peek_turn = [&]() {
-      if (lane == 0 && p_rank > 0) p_seen = load_relaxed_agent(counter(p_qtile));
-    };
+    auto peek_turn = [&]() { p_seen = load_relaxed_agent(counter(p_qtile)); };
     auto begin_add = [&]() {
-      p_loaded = false;
-      if (p_rank == 0 || (DEBUG && (a.jitter_seed != 0u || a.poison_q >= 0))) return;
-      const int ready = lane == 0 && p_seen == (uint32_t)p_rank;
-      if (__builtin_amdgcn_readfirstlane(ready)) load_acc();
+      bool ready = p_qtile >= 0 && p_rank > 0 &&
+                   __builtin_amdgcn_readfirstlane(p_seen) == (uint32_t)p_rank;
+      if (DEBUG && (a.jitter_seed != 0u || a.poison_q >= 0)) ready = false;
+      load_acc(ready);
     };
     auto finish_add = [&]() {
       if (DEBUG && a.wait_stats && lane == 0) st_waits += p_rank > 0 ? 1u : 0u;
       if (!p_loaded) {
         wait_turn();
-        if (p_rank > 0) load_acc();
+        if (p_rank > 0) load_acc(true);
       }
       const bool last = (p_flags & 1) != 0;
       const int q0 = p_qtile * BR;
@@ -473,11 +482,6 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
         }
       }
 
-      if constexpr (ORDERED) {
-        // start reading the accumulator for the previous sub-tile's partial
-        // if its turn had already come
-        if (p_qtile >= 0) begin_add();
-      }
 
       const T* cQ = sQ[b];
       const T* cdO = sdO[b];
@@ -513,6 +517,12 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
           }
         __builtin_amdgcn_sched_barrier(0);
       }
+
+      // Start reading the accumulator for the previous sub-tile's partial if
+      // its turn had already come.  Reading the counter peek waits for every
+      // load issued before it (the prefetch too), so it sits behind the S/dP
+      // products rather than at the top of the sub-tile.
+      if constexpr (ORDERED) begin_add();
 
       // P and dS; dS^T to LDS.  bf16: P and dS are packed once (hardware
       // RNE conversion) and the packed words serve both the LDS write and the
@@ -624,7 +634,7 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
       // here; advance its counter before issuing the next prefetch, so the
       // wait does not include loads that were just issued
       if constexpr (ORDERED) release();
-      if (g + 2 < n_steps) fetch(g + 2);
+      fetch(g + 2);
 
       if (DEBUG && a.partials != nullptr) {
         float* pp = a.partials + (((size_t)head * a.n_tiles + kv) * N) * D;

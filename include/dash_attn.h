@@ -36,7 +36,8 @@
  *               outputs are rounded to nearest even.
  *   LSE         Natural log of sum_j exp(s * <Q_i, K_j>) over visible j.
  *   Shapes      N_q = N_k = N; d in {64, 128}; N a multiple of the tile
- *               (64 for fp32, 128 for bf16); B, H >= 1.  Anything else
+ *               (64 for fp32, 128 for bf16); B, H >= 1; B*H*N < 2^31 and
+ *               N*d < 2^29 (32-bit device offsets).  Anything else
  *               returns DASH_ERR_UNSUPPORTED before any launch.
  *   Pointers    Device pointers unless stated otherwise; owned by the
  *               caller; never freed or retained by the library.  Inputs

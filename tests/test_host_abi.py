@@ -101,6 +101,9 @@ def test_argument_errors_without_launch():
     size = ctypes.c_size_t(0)
     assert lib.dash_attn_bwd_workspace_size(ctypes.byref(_desc()), 1, ctypes.byref(size)) == 0
     assert size.value > 4 * 2 * 256 * 64
+    largest = _desc(B=1, H=1, N=(1 << 22) - 128, d=128, dtype=1)
+    assert lib.dash_attn_bwd_workspace_size(ctypes.byref(largest), 1, ctypes.byref(size)) == 0
+    assert lib.dash_attn_bwd_workspace_size(ctypes.byref(_desc()), 1, ctypes.byref(size)) == 0
     # same size for every schedule (schedules only reorder work)
     for s in range(4):
         sz = ctypes.c_size_t(0)
@@ -109,6 +112,8 @@ def test_argument_errors_without_launch():
     bad = [
         (_desc(d=96), 2), (_desc(N=200), 2), (_desc(dtype=1, N=192), 2), (_desc(B=0), 1),
         (_desc(dtype=7), 1), (_desc(causal=2), 1),
+        # one head's fp32 accumulator must stay below 2^31 bytes
+        (_desc(B=1, H=1, N=1 << 22, d=128, dtype=1), 2),
     ]
     for desc, code in bad:
         assert lib.dash_attn_bwd_workspace_size(ctypes.byref(desc), 1, ctypes.byref(size)) == code
