@@ -35,13 +35,15 @@ any sum (each row's sums run over the full key range in one matmul).
 
 Pins (tests/test_oracle_attention.py): central finite differences of
 L = <dO, O>; sum_j dS_ij = 0; sum_j dK_j = 0; causal zero patterns; the
-closed forms for Q = 0 and for constant V rows; torch float64 autograd.
+closed forms for Q = 0 and for constant V rows; torch float64 autograd;
+the sampled rows of ``sampled_backward`` against the whole backward.
 """
 from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["forward", "backward", "backward_intermediates", "default_scale"]
+__all__ = ["forward", "backward", "backward_intermediates", "default_scale",
+           "sampled_backward"]
 
 _ROW_CHUNK = 1024
 
@@ -182,3 +184,38 @@ def backward_intermediates(q, k, v, do, causal: bool, scale: float | None = None
         "S": s, "LSE": lse, "P": p, "O": o, "D": d_row, "dP": dp, "dS": ds,
         "dV": p.T @ do, "dQ": scale * (ds @ k), "dK": scale * (ds.T @ q),
     }
+
+
+def sampled_backward(q, k, v, do, causal: bool, scale: float, rows_q, rows_kv):
+    """One head ([N, d] inputs): the forward statistics for every row, then
+    only the requested rows of the gradients, each from the same steps 1-9
+    applied to one row of P (dQ_i) or one column of P (dK_j, dV_j).  Cost is
+    one forward plus O(N d) per requested row, so full-length sequences can
+    be checked row by row.  Returns (dq[rows_q], dk[rows_kv], dv[rows_kv])."""
+    q, k, v, do = _as64(q), _as64(k), _as64(v), _as64(do)
+    o, lse = _head_forward(q, k, v, causal, scale)        # steps 1-4
+    d_row = np.sum(do * o, axis=1)                        # step 5
+    n = q.shape[0]
+    rows_q = np.asarray(rows_q, dtype=np.int64)
+    rows_kv = np.asarray(rows_kv, dtype=np.int64)
+    dq = np.empty((len(rows_q), k.shape[1]))
+    for t, i in enumerate(rows_q):
+        s_i = _scores(q[i:i + 1], k, scale, int(i), causal)   # row i of S
+        p_i = _probs(s_i, lse[i:i + 1])[0]
+        dp_i = v @ do[i]                                     # row i of dP
+        ds_i = p_i * (dp_i - d_row[i])
+        dq[t] = scale * (ds_i @ k)
+    dk = np.empty((len(rows_kv), q.shape[1]))
+    dv = np.empty((len(rows_kv), v.shape[1]))
+    for t, j in enumerate(rows_kv):
+        s_j = scale * (q @ k[j])                             # column j of S
+        if causal:
+            s_j = np.where(np.arange(n) >= j, s_j, -np.inf)
+        finite = np.isfinite(lse)
+        with np.errstate(under="ignore"):
+            p_j = np.where(finite, np.exp(s_j - np.where(finite, lse, 0.0)), 0.0)
+        dv[t] = p_j @ do                                     # step 6
+        dp_j = do @ v[j]                                     # column j of dP
+        ds_j = p_j * (dp_j - d_row)
+        dk[t] = scale * (ds_j @ q)                           # step 9
+    return dq, dk, dv

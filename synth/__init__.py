@@ -21,6 +21,8 @@ __all__ = [
     "round_to_bf16_bits",
     "bf16_bits_to_f32",
     "make_inputs",
+    "make_storage",
+    "exact_of",
 ]
 
 
@@ -111,6 +113,28 @@ def make_inputs(B: int, H: int, N: int, d: int, dtype: str, seed_base: int,
             s = round_to_bf16_bits(x)
             out[name] = (s, bf16_bits_to_f32(s).astype(np.float64))
     return out
+
+
+def make_storage(B: int, H: int, N: int, d: int, dtype: str, seed_base: int,
+                 names=("q", "k", "v", "do")) -> dict:
+    """The same tensors as ``make_inputs`` (same seeds, same values), storage
+    only: for full-size workloads whose fp64 copies would not fit; the exact
+    values of any slice come from ``exact_of``."""
+    if dtype not in ("f32", "bf16"):
+        raise ValueError(f"unknown dtype {dtype!r}")
+    out = {}
+    for i, name in enumerate(names):
+        x = gaussian((B, H, N, d), seed_base + i)
+        out[name] = x.astype(np.float32) if dtype == "f32" else round_to_bf16_bits(x)
+        del x
+    return out
+
+
+def exact_of(storage: np.ndarray, dtype: str) -> np.ndarray:
+    """fp64 value of exactly what is stored (fp32 values or bf16 bits)."""
+    if dtype == "f32":
+        return np.asarray(storage, dtype=np.float64)
+    return bf16_bits_to_f32(storage).astype(np.float64)
 
 
 def make_workload_inputs(w: Workload, names=("q", "k", "v", "do")) -> dict:

@@ -185,6 +185,24 @@ def test_against_torch_autograd_float64(causal):
         assert np.max(np.abs(mine - ref)) <= 1e-12 * np.max(np.abs(ref))
 
 
+@pytest.mark.parametrize("causal", [False, True])
+def test_sampled_rows_against_torch_autograd(causal):
+    """The row-by-row backward used for full-length checks equals torch's
+    float64 autograd at the requested rows (first, last, tile edges)."""
+    n, d, scale = 150, 16, 0.21
+    q, k, v, do = (x[0, 0] for x in _small(n=n, d=d, seed=57))
+    rows = [0, 1, 63, 64, 127, 128, 149]
+    dq, dk, dv = A.sampled_backward(q, k, v, do, causal, scale, rows, rows[::-1])
+    tq, tk, tv = (torch.tensor(x, dtype=torch.float64, requires_grad=True) for x in (q, k, v))
+    sc = scale * (tq @ tk.T.contiguous())
+    if causal:
+        sc = sc.masked_fill(~torch.ones(n, n, dtype=torch.bool).tril(), float("-inf"))
+    (torch.softmax(sc, dim=-1) @ tv).backward(torch.tensor(do, dtype=torch.float64))
+    for mine, ref in ((dq, tq.grad.numpy()[rows]), (dk, tk.grad.numpy()[rows[::-1]]),
+                      (dv, tv.grad.numpy()[rows[::-1]])):
+        assert np.max(np.abs(mine - ref)) <= 1e-12 * np.max(np.abs(ref))
+
+
 def test_row_chunking_matches_whole(monkeypatch):
     """Chunked rows equal whole-matrix rows (the chunk is a plain slice)."""
     q, k, v, do = _small(n=100, d=8, seed=41)
