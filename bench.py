@@ -13,7 +13,9 @@ the run (or of --primary), FLOPs counted as 2.5x the forward's
 4*B*H*N^2*d, halved for a causal mask.  Also reported:
 % of the dense bf16 MFMA peak, the deterministic / atomic throughput ratio
 per schedule, the backward kernel's own roofline figures (HIP events around
-its launch), and the fp64 CPU oracle timed on a bounded sample of heads.
+its launch), the share of cycles the ordered schedules spend waiting for
+their turn (one extra untimed, instrumented launch each), and the fp64 CPU
+oracle timed on a bounded sample of heads.
 
 Prints one JSON line.  --gpus above 1 is refused: this path runs on one GPU.
 """
@@ -96,6 +98,25 @@ def cpu_baseline(exact, w, causal, max_workers):
                       f"({max(times):.1f} s)"}
 
 
+# ------------------------------------------------------- ordering waits
+
+def order_wait(D, dev, lse, delta, sched, causal, ws, out):
+    """One extra, untimed launch of the instrumented kernel (wait statistics
+    on): the share of the waves' cycles spent waiting for ordered-add turns,
+    and the share of ordered adds whose turn had not come at the first poll."""
+    import torch
+    st = torch.zeros(4 * 4096 * 4, dtype=torch.int64, device="cuda")
+    D.attn_bwd(dev["q"], dev["k"], dev["v"], dev["do"], lse, delta, schedule=sched,
+               causal=causal, workspace=ws, out=out, debug={"wait_stats": st})
+    torch.cuda.synchronize()
+    D.attn_bwd_status(ws)
+    a = st.view(-1, 4).cpu().numpy()
+    a = a[a[:, 3] > 0]
+    wait, waits, spun, busy = (float(a[:, i].sum()) for i in range(4))
+    return {"order_wait_frac": wait / max(busy, 1.0), "order_adds": int(waits),
+            "order_polled_frac": spun / max(waits, 1.0)}
+
+
 # ------------------------------------------------------------------ main
 
 def main():
@@ -111,6 +132,8 @@ def main():
                     help="schedule reported as value (default: fastest deterministic one)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-workers", type=int, default=16)
+    ap.add_argument("--no-wait-stats", action="store_true",
+                    help="skip the untimed instrumented launch per ordered schedule")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="run one plain device copy of BYTES before timing (a reference "
                          "dispatch of known traffic for hardware-counter runs)")
@@ -192,6 +215,8 @@ def main():
         kms = sum(a.elapsed_time(b) for a, b in kev) / args.steps
         results[sched] = {"ms_per_step": ms, "tflops": flops / ms / 1e9,
                           "kernel_ms": kms, "kernel_tflops": flops / kms / 1e9}
+        if sched != "atomic" and not args.no_wait_stats:
+            results[sched].update(order_wait(D, dev, lse, delta, sched, causal, ws, (dq, dk, dv)))
         print(f"[bench] {sched:10s} step {ms:8.3f} ms  {flops / ms / 1e9:7.1f} TFLOP/s   "
               f"kernel {kms:8.3f} ms  {flops / kms / 1e9:7.1f} TFLOP/s", file=sys.stderr,
               flush=True)
@@ -222,9 +247,12 @@ def main():
         "schedules": {s: {k: round(v, 4) for k, v in r.items()} for s, r in results.items()},
     }
     achieved = flops / (prim["kernel_ms"] * 1e-3) / 1e12
+    traffic = read_traffic(w.name, primary)
     out["roofline"] = {"bound": "mfma", "achieved": round(achieved, 2), "peak": peak,
                        "unit": "TFLOP/s", "frac": round(achieved / peak, 4),
-                       "traffic": read_traffic(w.name, primary),
+                       "traffic": traffic,
+                       "hbm_GBps": (round(traffic / (prim["kernel_ms"] * 1e-3) / 1e9, 1)
+                                    if traffic else None),
                        "kernel": f"bwd_kernel ({primary})"}
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample of heads", file=sys.stderr, flush=True)

@@ -17,6 +17,16 @@ times its schedules one after another, W warm-up plus K timed launches
 each), and per-schedule durations are listed: the ordered schedules share
 one kernel instantiation, so the statistics table alone mixes them.
 
+  python -m deterministic_attention_backward_attn_amd.rocprof_summary counters \\
+      --csv <dir>/<prefix>_counter_collection.csv --cmd "<command>" \\
+      --blocks atomic,descending --block-size K --out profiles/<name>.md
+
+The counters summary lists the SQ counters of one rocprofv3 --pmc pass per
+schedule (backward dispatches cut into blocks as above) with derived
+figures: MFMA busy share (MFMA-busy cycles over 1024 SIMDs / busy cycles
+over 32 shader engines), LDS bank-conflict share of LDS-active cycles, and
+the share of wave cycles spent in s_waitcnt.
+
 The traffic summary scales each kernel's FETCH_SIZE / WRITE_SIZE (KiB per
 dispatch) by the factor that makes the same counter read the known size of a
 plain device copy run in the same process, and records the hash of the
@@ -130,6 +140,42 @@ def traffic(args):
     _write(args.out, lines)
 
 
+def counters(args):
+    per = {}
+    for r in csv.DictReader(open(args.csv)):
+        if args.kernel not in r["Kernel_Name"]:
+            continue
+        d = per.setdefault(int(r["Dispatch_Id"]), {})
+        d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])
+    ids = sorted(per)
+    names = [b for b in args.blocks.split(",") if b]
+    if len(ids) != len(names) * args.block_size:
+        raise SystemExit(f"{len(ids)} dispatches, expected {len(names)} x {args.block_size}")
+    ctrs = sorted({c for d in per.values() for c in d})
+    lines = ["# rocprofv3 SQ counters of the backward kernel", "",
+             f"Command: `{args.cmd}`", "",
+             f"Per schedule: mean over its {args.block_size} dispatches (dispatch order).", "",
+             "| counter | " + " | ".join(names) + " |", "|---|" + "---|" * len(names)]
+    means = []
+    for i, _ in enumerate(names):
+        blk = ids[i * args.block_size:(i + 1) * args.block_size]
+        means.append({c: statistics.mean(per[d].get(c, 0.0) for d in blk) for c in ctrs})
+    for c in ctrs:
+        lines.append(f"| {c} | " + " | ".join(f"{m[c]:.4g}" for m in means) + " |")
+
+    def ratio(m, a, b, k=1.0):
+        return f"{m[a] / (k * m[b]):.3f}" if a in m and b in m and m[b] else "n/a"
+    lines += ["", "| derived | " + " | ".join(names) + " |", "|---|" + "---|" * len(names),
+              "| MFMA busy share | " + " | ".join(
+                  ratio(m, "SQ_VALU_MFMA_BUSY_CYCLES", "SQ_BUSY_CYCLES", 32.0) for m in means) + " |",
+              "| LDS bank-conflict share of LDS-active cycles | " + " | ".join(
+                  ratio(m, "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE") for m in means) + " |",
+              "| wave cycles in s_waitcnt | " + " | ".join(
+                  ratio(m, "SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES") for m in means) + " |",
+              "", f"kernel_source_sha256: {kernel_source_hash()}", ""]
+    _write(args.out, lines)
+
+
 def _write(path, lines):
     text = "\n".join(lines)
     if path:
@@ -148,6 +194,13 @@ def main(argv=None):
     s.add_argument("--trace")
     s.add_argument("--blocks", default="atomic,naive,descending,shift")
     s.add_argument("--block-size", type=int, default=0)
+    c = sub.add_parser("counters")
+    c.add_argument("--csv", required=True)
+    c.add_argument("--cmd", required=True)
+    c.add_argument("--out")
+    c.add_argument("--kernel", default="bwd_kernel")
+    c.add_argument("--blocks", default="atomic,descending")
+    c.add_argument("--block-size", type=int, default=3)
     t = sub.add_parser("traffic")
     t.add_argument("--fetch-csv", required=True)
     t.add_argument("--write-csv", required=True)
@@ -158,7 +211,7 @@ def main(argv=None):
     t.add_argument("--cmd-write", required=True)
     t.add_argument("--out")
     args = ap.parse_args(argv)
-    (stats if args.mode == "stats" else traffic)(args)
+    {"stats": stats, "traffic": traffic, "counters": counters}[args.mode](args)
 
 
 if __name__ == "__main__":
