@@ -223,7 +223,8 @@ dash_status run_bwd(const dash_attn_desc* desc, dash_schedule schedule, const vo
   a.poison_q = dbg ? dbg->poison_q - 1 : -1;
   a.partials = dbg ? dbg->partials : nullptr;
   a.wait_stats = dbg ? dbg->wait_stats : nullptr;
-  if (a.wait_stats && grid > 4096) return DASH_ERR_UNSUPPORTED;
+  if (a.wait_stats && (long)grid * dash::bwd_waves(desc->dtype, desc->d) > 4096L * 4)
+    return DASH_ERR_UNSUPPORTED;
   hipEvent_t ev0 = dbg ? (hipEvent_t)dbg->kernel_events[0] : nullptr;
   hipEvent_t ev1 = dbg ? (hipEvent_t)dbg->kernel_events[1] : nullptr;
   if (ev0 && hipEventRecord(ev0, strm) != hipSuccess) return DASH_ERR_HIP;
@@ -258,7 +259,9 @@ const char* dash_status_string(dash_status s) {
 
 int32_t dash_attn_tile(const dash_attn_desc* desc) {
   if (!desc) return 0;
-  return desc->dtype == DASH_BF16 ? 128 : 64;
+  int bc = 0, br = 0;
+  dash::bwd_tiles(desc->dtype, desc->d, &bc, &br);
+  return bc;
 }
 
 int32_t dash_attn_bwd_subtile(const dash_attn_desc* desc) {

@@ -45,6 +45,7 @@
 //   K^T fragments (d on lanes) are built once per KV tile the same way.
 #include "common.hpp"
 #include "launch.hpp"
+#include "placement.hpp"
 
 namespace dash {
 
@@ -166,52 +167,10 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
   uint64_t st_wait = 0, st_waits = 0, st_spun = 0;
   const uint64_t st_t0 = (DEBUG && a.wait_stats) ? (uint64_t)clock64() : 0;
 
-  // ---- placement -------------------------------------------------------
-  // XCD-local mode: every workgroup reads the XCD it runs on, a census
-  // (all workgroups are resident: cooperative launch) counts workgroups per
-  // XCD, and the heads are dealt round-robin to the XCDs present.  All units
-  // of a head then run on one XCD, so its ordered dQ hand-offs stay inside
-  // that XCD's L2 (L2-coherent accumulator accesses) and its Q/dO tiles are
-  // reused from that L2.  The shift schedule needs a whole head resident, so
-  // if some XCD has fewer workgroups than a head has units, every workgroup
-  // falls back to one device-wide group with device-coherent accesses.
-  // Header words: [0] status, [1] device work counter, [2] census arrivals,
-  // [4..19] workgroups per XCD, [20..35] work counter per XCD group.
+  const Placement pl = place_units(a, tid, sPlace);
   const int U = a.units_per_head;
-  int grp = 0, n_grp = 1, li = blockIdx.x, W = gridDim.x;  // XCD group of this workgroup
-  bool grouped = false;  // units taken from this XCD's own list
-  bool xl = false;       // ... and accumulator accesses coherent in its L2 only
-  if (a.xcd_mode) {
-    if (tid == 0) {
-      const uint32_t x = xcc_id();
-      const uint32_t mine = __hip_atomic_fetch_add(&a.header[4 + x], 1u, __ATOMIC_RELAXED,
-                                                   __HIP_MEMORY_SCOPE_AGENT);
-      __hip_atomic_fetch_add(&a.header[2], 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      wait_counter(&a.header[2], gridDim.x, status, spin_limit);
-      int active = 0, my_grp = 0, fits = 1;
-      for (uint32_t k = 0; k < 16; ++k) {
-        const uint32_t c = load_relaxed_agent(&a.header[4 + k]);
-        if (c == 0) continue;
-        if (k == x) my_grp = active;
-        if (!a.dynamic && (int)c < U) fits = 0;
-        ++active;
-      }
-      sPlace[0] = my_grp;
-      sPlace[1] = active;
-      sPlace[2] = (int)mine;
-      sPlace[3] = (int)load_relaxed_agent(&a.header[4 + x]);
-      sPlace[4] = fits && load_relaxed_agent(status) == 0u;
-    }
-    __syncthreads();
-    if (sPlace[4]) {
-      grouped = true;
-      xl = a.xcd_mode == 1;
-      grp = sPlace[0];
-      n_grp = sPlace[1];
-      li = sPlace[2];
-      W = sPlace[3];
-    }
-  }
+  const int grp = pl.grp, n_grp = pl.n_grp, li = pl.li, W = pl.W;
+  const bool grouped = pl.grouped, xl = pl.xl;
   const int BH = a.total_units / U;
   const int n_units = ((BH - grp + n_grp - 1) / n_grp) * U;  // units of this group
   const int stride_static = grouped ? (W / U) * U : a.p_eff;
@@ -237,6 +196,9 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
 
     // The unit's work list into LDS.  Every wave has finished the previous
     // unit (including all LDS reads) once it passes this barrier.
+    // every wave has finished the previous unit (its last reads of the work
+    // list included) before the list is overwritten
+    __syncthreads();
     for (int i = tid; i < n_items; i += NT) sItems[i] = a.items[it0 + i];
     __syncthreads();
 
@@ -447,6 +409,10 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
       if (kv != cur_kv) {
         if (cur_kv >= 0) flush_dkdv();
         cur_kv = kv;
+        // L2-coherent accumulator accesses may hit this CU's L1: drop lines
+        // it read for earlier KV tiles, which other CUs have updated since
+        // (within one KV tile every Q sub-tile is visited once)
+        if (xl) l1_invalidate();
         const int kv0 = kv * BC;
 #pragma unroll
         for (int ks = 0; ks < DK; ++ks) {

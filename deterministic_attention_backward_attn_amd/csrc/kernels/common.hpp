@@ -134,6 +134,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
 // sc0 = bypasses the CU's L1 and is served by the XCD's L2, so it is
 // coherent among the workgroups of one XCD.
 constexpr int kCoherent = 16;
+// Invalidate this CU's vector L1 cache (L2 untouched).
+__device__ __forceinline__ void l1_invalidate() { asm volatile("buffer_inv sc0" ::: "memory"); }
+
 // A buffer offset past every accumulator's range (the host keeps ranges
 // below 2^31 bytes): loads there return 0 without a memory access.
 constexpr uint32_t kOutOfRange = 0x80000000u;

@@ -143,7 +143,7 @@ def traffic(args):
 def counters(args):
     per = {}
     for r in csv.DictReader(open(args.csv)):
-        if args.kernel not in r["Kernel_Name"]:
+        if not any(k in r["Kernel_Name"] for k in args.kernel.split("|")):
             continue
         d = per.setdefault(int(r["Dispatch_Id"]), {})
         d[r["Counter_Name"]] = d.get(r["Counter_Name"], 0.0) + float(r["Counter_Value"])

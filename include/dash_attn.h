@@ -95,14 +95,13 @@ typedef struct {
 /* Human-readable name of a status code (static string, never NULL). */
 const char* dash_status_string(dash_status s);
 
-/* KV tile (rows) used for a descriptor: 64 for fp32, 128 for bf16; 0 if
- * desc is NULL. */
+/* KV tile (rows) of the backward for a descriptor: 64 for fp32, 128 for
+ * bf16; 0 if desc is NULL. */
 int32_t dash_attn_tile(const dash_attn_desc* desc);
 
 /* Q sub-tile (rows) of the backward: each Q block of dash_attn_tile rows
- * is processed, counted and ordered in sub-tiles of this many rows (64 for
- * bf16 and for fp32 with d = 64, 32 for fp32 with d = 128); 0 if desc is
- * NULL. */
+ * is processed, counted and ordered in sub-tiles of this many rows (32 for
+ * d = 128, 64 for d = 64); 0 if desc is NULL. */
 int32_t dash_attn_bwd_subtile(const dash_attn_desc* desc);
 
 /*
@@ -188,7 +187,9 @@ dash_status dash_attn_bwd_status(const void* workspace, void* stream);
  *                   entries [(g*waves + w)*4 + k] receive: k=0 shader-clock
  *                   cycles spent waiting for ordered adds, k=1 ordered waits,
  *                   k=2 waits that polled more than once, k=3 cycles of the
- *                   workgroup's whole run (waves = dash_attn_tile/32).
+ *                   workgroup's whole run (waves = dash_attn_tile/32;
+ *                   workgroups x waves must not exceed 4096 * 4, else
+ *                   DASH_ERR_UNSUPPORTED).
  */
 typedef struct {
   uint32_t spin_limit;
