@@ -112,7 +112,9 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
   constexpr int PAD = 16 / (int)sizeof(T);
   constexpr bool SWZ = sizeof(T) == 2;  // bf16: swizzled sQ, sdO, sK
   constexpr int LQ = SWZ ? D : D + PAD;  // row stride of sQ, sdO, sK ([row][d])
-  constexpr int LS = BR + PAD;         // row stride of sdSt ([kv][q])
+  // row stride of sdSt ([kv][q]); bf16 with 32-column rows pads by 4
+  // elements, which keeps the 8-byte writes of 32 rows on distinct banks
+  constexpr int LS = (SWZ && BR == 32) ? BR + 4 : BR + PAD;
   constexpr int CPT = BR * D / VEC / NT;  // 16-byte chunks per thread per tensor
   // dQ output tiles of a wave: CPW column tiles x RPW row tiles
   constexpr int CPW = NTD >= NW ? NTD / NW : 1;
@@ -137,7 +139,9 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
   __shared__ int2 sItems[kMaxUnitItems];
   // per-wave staging of a dQ partial, row-major [32 rows][32 + 4 floats], so
   // that each 16-byte accumulator access of a lane group covers whole rows
-  constexpr int LR = 36;
+  // (rows of 32 floats, 16-byte chunk c of row r at chunk c ^ ((r/2)%8), so
+  // that 32 rows of one chunk and 8 whole rows each spread over all banks)
+  constexpr int LR = 32;
   __shared__ __align__(16) float sRow[ORDERED ? NW : 1][ORDERED ? QT * 32 * LR : 4];
   __shared__ int sUnit;
   __shared__ int sPlace[5];
@@ -147,6 +151,7 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
     else return r * LQ + c;
   };
   const auto six = [](int r, int c) { return r * LS + c; };  // sdSt
+  const auto rix = [](int r, int c) { return r * LR + (((c >> 2) ^ ((r >> 1) & 7)) << 2) + (c & 3); };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -356,7 +361,7 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
 #pragma unroll
         for (int gq = 0; gq < 4; ++gq) {
           f32x4 v = *reinterpret_cast<const f32x4*>(
-              &row[(i * 32 + (lane >> 3) + 8 * gq) * LR + 4 * (lane & 7)]);
+              &row[rix(i * 32 + (lane >> 3) + 8 * gq, 4 * (lane & 7))]);
           if (p_rank > 0) v = lv[i][gq] + v;
           const uint32_t off = chunk_off(q0, i, gq);
           if (last) {
@@ -618,7 +623,7 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
         for (int i = 0; i < QT; ++i)
 #pragma unroll
           for (int gq = 0; gq < 4; ++gq)
-            *reinterpret_cast<f32x4*>(&row[(i * 32 + l32) * LR + 8 * gq + 4 * hh]) =
+            *reinterpret_cast<f32x4*>(&row[rix(i * 32 + l32, 8 * gq + 4 * hh)]) =
                 f32x4{accQ[i][4 * gq], accQ[i][4 * gq + 1], accQ[i][4 * gq + 2],
                       accQ[i][4 * gq + 3]};
         p_qtile = qtile;
