@@ -21,7 +21,8 @@ from ._lib import DTYPES, SCHEDULES, DashError, Debug, Desc, check, header_symbo
 
 __all__ = [
     "DashError", "SCHEDULES", "attn_fwd", "attn_bwd_preprocess", "attn_bwd_workspace_size",
-    "attn_bwd", "attn_bwd_status", "backward", "schedule_tables", "schedule_predict",
+    "attn_bwd", "attn_bwd_status", "backward", "schedule_tables", "schedule_predict", "schedule_choose",
+    "resolve_schedule",
     "dag_longest_path", "litmus_ordered_add", "tile", "subtile", "header_symbols", "load",
 ]
 
@@ -137,6 +138,17 @@ def attn_bwd_workspace_size(B, H, N, d, dtype="bf16", causal=False, schedule="na
     return int(out.value)
 
 
+def resolve_schedule(B, H, N, d, dtype="bf16", causal=False, schedule="auto") -> str:
+    """The schedule attn_bwd runs for `schedule` on the current device
+    ("auto" -> the predicted best ordered schedule; others unchanged)."""
+    lib = load()
+    out = ctypes.c_int(-1)
+    check(lib.dash_attn_bwd_resolve_schedule(ctypes.byref(_desc(B, H, N, d, dtype, causal)),
+                                             _sched(schedule), ctypes.byref(out)),
+          "dash_attn_bwd_resolve_schedule")
+    return {v: k for k, v in SCHEDULES.items()}[out.value]
+
+
 def alloc_workspace(q, causal=False, schedule="naive"):
     torch = _torch()
     B, H, N, d = (int(x) for x in q.shape)
@@ -240,6 +252,20 @@ def schedule_predict(n: int, causal: bool, schedule, heads: int, slots: int, cos
     check(lib.dash_schedule_predict(n, 1 if causal else 0, _sched(schedule), heads, slots, c, out),
           "dash_schedule_predict")
     return tuple(out)
+
+
+def schedule_choose(n: int, causal: bool, heads: int, slots: int, cost=None):
+    """The ordered schedule DASH_SCHED_AUTO resolves to: returns (name,
+    {name: predicted makespan}) over naive, descending and shift (NaN where
+    a schedule cannot run).  cost None = the library's default model."""
+    lib = load()
+    c = None if cost is None else (ctypes.c_double * 4)(*[float(x) for x in cost])
+    choice = ctypes.c_int(0)
+    pred = (ctypes.c_double * 3)()
+    check(lib.dash_schedule_choose(n, 1 if causal else 0, heads, slots, c, ctypes.byref(choice),
+                                   pred), "dash_schedule_choose")
+    names = {v: k for k, v in SCHEDULES.items()}
+    return names[choice.value], {"naive": pred[0], "descending": pred[1], "shift": pred[2]}
 
 
 def dag_longest_path(weights, edges):

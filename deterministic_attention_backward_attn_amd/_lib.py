@@ -23,7 +23,7 @@ STATUS = {
     5: "DASH_ERR_SCHEDULE_INVALID",
     6: "DASH_ERR_ORDER_TIMEOUT",
 }
-SCHEDULES = {"atomic": 0, "naive": 1, "descending": 2, "shift": 3}
+SCHEDULES = {"atomic": 0, "naive": 1, "descending": 2, "shift": 3, "auto": 4}
 DTYPES = {"f32": 0, "bf16": 1}
 
 
@@ -67,6 +67,10 @@ _SIGS = {
     "dash_attn_bwd_status": (ctypes.c_int, [_vp, _vp]),
     "dash_schedule_tables": (ctypes.c_int, [_i32, _i32, ctypes.c_int, _ip, _ip, _ip, _ip, _ip]),
     "dash_schedule_predict": (ctypes.c_int, [_i32, _i32, ctypes.c_int, _i32, _i32, _dp, _dp]),
+    "dash_attn_bwd_resolve_schedule": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int,
+                                                      ctypes.POINTER(ctypes.c_int)]),
+    "dash_schedule_choose": (ctypes.c_int, [_i32, _i32, _i32, _i32, _dp,
+                                            ctypes.POINTER(ctypes.c_int), _dp]),
     "dash_dag_longest_path": (ctypes.c_int, [_i32, _dp, _i32, _ip, _ip, _dp, _dp, _dp]),
     "dash_litmus_ordered_add": (ctypes.c_int, [_i32, _i32, _vp, _vp, _vp, _vp, ctypes.c_uint32,
                                                _vp]),

@@ -2,6 +2,7 @@
 // schedule-table cache, and the launch sequence of the backward.
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cmath>
 #include <cstring>
 #include <map>
@@ -25,6 +26,43 @@ constexpr uint32_t kDefaultSpin = 1u << 21;  // polls before giving up (seconds)
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
 bool sched_ok(int s) { return s >= DASH_SCHED_ATOMIC && s <= DASH_SCHED_SHIFT; }
+bool sched_ok_run(int s) { return sched_ok(s) || s == DASH_SCHED_AUTO; }
+
+// Default cost model of the adaptive choice, in units of one unmasked item
+// (KV tile x Q block): causal diagonal items cost half, the ordered add and
+// the hand-off latency each about 5 % of an item (measured on MI355X at
+// d = 128: ~24k cycles per item, ~1.2k per hand-off).
+constexpr double kDefaultCost[4] = {1.0, 0.5, 0.05, 0.05};
+
+// The ordered schedule with the smallest predicted makespan; see
+// dash_schedule_choose.
+dash_status choose_schedule(int n, bool causal, int heads, int slots, const double cost[4],
+                            Sched* choice, double pred[3]) {
+  const Sched cand[3] = {Sched::Naive, Sched::Descending, Sched::Shift};
+  double best = 0.0;
+  int best_i = -1;
+  for (int i = 0; i < 3; ++i) {
+    pred[i] = NAN;
+    Tables t;
+    if (!dash::build_tables(n, causal, cand[i], t)) continue;
+    if (dash::validate_tables(t)[0] != '\0') return DASH_ERR_SCHEDULE_INVALID;
+    if (t.needs_static() && t.units() > slots) continue;
+    // a subset of the heads keeps the prediction to about 2e5 items
+    const long per_head = (long)t.kv.size();
+    const int h = (int)std::max<long>(1, std::min<long>(heads, 200000 / std::max<long>(per_head, 1)));
+    dash::DagResult r;
+    if (!dash::dag_predict(t, h, slots, cost, r)) return DASH_ERR_SCHEDULE_INVALID;
+    pred[i] = r.makespan;
+    // ties go to the later candidate (SHIFT, then DESCENDING)
+    if (best_i < 0 || r.makespan <= best) {
+      best = r.makespan;
+      best_i = i;
+    }
+  }
+  if (best_i < 0) return DASH_ERR_UNSUPPORTED;
+  *choice = cand[best_i];
+  return DASH_OK;
+}
 
 dash_status check_desc(const dash_attn_desc* d) {
   if (!d) return DASH_ERR_INVALID_ARG;
@@ -77,6 +115,7 @@ struct DevTables {
 std::mutex g_mu;
 std::map<std::tuple<int, int, int, int>, DevTables> g_tables;  // (device, n, causal, sched)
 std::map<std::tuple<int, int, int, int, int>, int> g_coresident;  // (device, dtype, d, causal, ordered)
+std::map<std::tuple<int, int, int, int>, Sched> g_auto;  // (n, causal, heads, slots) -> choice
 
 dash_status get_tables(int dev, int n, bool causal, Sched s, const DevTables** out) {
   std::lock_guard<std::mutex> lock(g_mu);
@@ -136,13 +175,34 @@ dash_status get_coresident(int dev, int dtype, int d, bool causal, bool ordered,
   return DASH_OK;
 }
 
+// DASH_SCHED_AUTO -> the predicted best ordered schedule for this problem
+// on `maxco` co-resident workgroups (cached per shape); others unchanged.
+dash_status resolve_schedule(dash_schedule schedule, int n, bool causal, long heads, int maxco,
+                             Sched* s) {
+  *s = (Sched)schedule;
+  if (schedule != DASH_SCHED_AUTO) return DASH_OK;
+  const int h = (int)std::min<long>(heads, 1L << 30);
+  const auto key = std::make_tuple(n, (int)causal, h, maxco);
+  std::lock_guard<std::mutex> lock(g_mu);
+  auto it = g_auto.find(key);
+  if (it != g_auto.end()) {
+    *s = it->second;
+    return DASH_OK;
+  }
+  double pred[3];
+  const dash_status st = choose_schedule(n, causal, h, maxco, kDefaultCost, s, pred);
+  if (st != DASH_OK) return st;
+  g_auto[key] = *s;
+  return DASH_OK;
+}
+
 dash_status run_bwd(const dash_attn_desc* desc, dash_schedule schedule, const void* q,
                     const void* k, const void* v, const void* dout, const float* lse,
                     const float* delta, void* dq, void* dk, void* dv, void* workspace,
                     size_t workspace_bytes, const dash_bwd_debug* dbg, void* stream) {
   dash_status st = check_desc(desc);
   if (st != DASH_OK) return st;
-  if (!sched_ok(schedule)) return DASH_ERR_INVALID_ARG;
+  if (!sched_ok_run(schedule)) return DASH_ERR_INVALID_ARG;
   if (!q || !k || !v || !dout || !lse || !delta || !dq || !dk || !dv || !workspace)
     return DASH_ERR_INVALID_ARG;
   const WsLayout w = layout(desc);
@@ -151,25 +211,27 @@ dash_status run_bwd(const dash_attn_desc* desc, dash_schedule schedule, const vo
   dash::bwd_tiles(desc->dtype, desc->d, &bc, &br);
   const int n = desc->N / bc;
   const bool causal = desc->causal != 0;
-  const Sched s = (Sched)schedule;
-  const bool ordered = s != Sched::Atomic;
+  const bool ordered = schedule != DASH_SCHED_ATOMIC;
   if (dbg && (dbg->poison_q < 0 || dbg->poison_q > desc->N / br)) return DASH_ERR_INVALID_ARG;
   if (dbg && (dbg->placement < 0 || dbg->placement > 3)) return DASH_ERR_INVALID_ARG;
 
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return DASH_ERR_HIP;
-  const DevTables* tb = nullptr;
-  st = get_tables(dev, n, causal, s, &tb);
-  if (st != DASH_OK) return st;
   int maxco = 0;
   st = get_coresident(dev, desc->dtype, desc->d, causal, ordered, &maxco);
+  if (st != DASH_OK) return st;
+  const long heads = (long)desc->B * desc->H;
+  Sched s = Sched::Naive;
+  st = resolve_schedule(schedule, n, causal, heads, maxco, &s);
+  if (st != DASH_OK) return st;
+  const DevTables* tb = nullptr;
+  st = get_tables(dev, n, causal, s, &tb);
   if (st != DASH_OK) return st;
 
   const int U = tb->host.units();
   for (int u = 0; u < U; ++u)
     if (tb->host.unit_off[u + 1] - tb->host.unit_off[u] > dash::kMaxUnitItems)
       return DASH_ERR_UNSUPPORTED;
-  const long heads = (long)desc->B * desc->H;
   const long total_units = heads * U;
   int grid = 0, p_eff = 0, dynamic = 0;
   if (tb->host.needs_static()) {
@@ -307,7 +369,7 @@ dash_status dash_attn_bwd_workspace_size(const dash_attn_desc* desc, dash_schedu
                                          size_t* bytes) {
   dash_status st = check_desc(desc);
   if (st != DASH_OK) return st;
-  if (!sched_ok(schedule) || !bytes) return DASH_ERR_INVALID_ARG;
+  if (!sched_ok_run(schedule) || !bytes) return DASH_ERR_INVALID_ARG;
   *bytes = layout(desc).total;
   return DASH_OK;
 }
@@ -372,6 +434,43 @@ dash_status dash_schedule_predict(int32_t n, int32_t causal, dash_schedule sched
   out[1] = r.total_wait;
   out[2] = r.max_slot_idle;
   out[3] = r.lower_bound;
+  return DASH_OK;
+}
+
+dash_status dash_attn_bwd_resolve_schedule(const dash_attn_desc* desc, dash_schedule schedule,
+                                           dash_schedule* resolved) {
+  dash_status st = check_desc(desc);
+  if (st != DASH_OK) return st;
+  if (!sched_ok_run(schedule) || !resolved) return DASH_ERR_INVALID_ARG;
+  int bc = 0, br = 0;
+  dash::bwd_tiles(desc->dtype, desc->d, &bc, &br);
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return DASH_ERR_HIP;
+  int maxco = 0;
+  st = get_coresident(dev, desc->dtype, desc->d, desc->causal != 0,
+                      schedule != DASH_SCHED_ATOMIC, &maxco);
+  if (st != DASH_OK) return st;
+  Sched s = Sched::Naive;
+  st = resolve_schedule(schedule, desc->N / bc, desc->causal != 0, (long)desc->B * desc->H, maxco,
+                        &s);
+  if (st != DASH_OK) return st;
+  *resolved = (dash_schedule)s;
+  return DASH_OK;
+}
+
+dash_status dash_schedule_choose(int32_t n, int32_t causal, int32_t heads, int32_t slots,
+                                 const double* cost, dash_schedule* choice, double* predicted) {
+  if (n < 1 || n > 32767 || (causal != 0 && causal != 1) || heads < 1 || slots < 1 || !choice)
+    return DASH_ERR_INVALID_ARG;
+  const double* c = cost ? cost : kDefaultCost;
+  for (int i = 0; i < 4; ++i)
+    if (!(c[i] >= 0.0) || !std::isfinite(c[i])) return DASH_ERR_INVALID_ARG;
+  Sched s = Sched::Naive;
+  double pred[3];
+  const dash_status st = choose_schedule(n, causal != 0, heads, slots, c, &s, pred);
+  if (st != DASH_OK) return st;
+  *choice = (dash_schedule)s;
+  if (predicted) std::memcpy(predicted, pred, sizeof(pred));
   return DASH_OK;
 }
 

@@ -81,7 +81,9 @@ typedef enum {
   DASH_SCHED_ATOMIC = 0,
   DASH_SCHED_NAIVE = 1,
   DASH_SCHED_DESCENDING = 2,
-  DASH_SCHED_SHIFT = 3
+  DASH_SCHED_SHIFT = 3,
+  DASH_SCHED_AUTO = 4  /* the ordered schedule with the shortest predicted
+                          critical path (dash_schedule_choose) */
 } dash_schedule;
 
 /* Problem descriptor.  softmax_scale <= 0 selects 1/sqrt(d). */
@@ -236,6 +238,37 @@ dash_status dash_schedule_tables(int32_t n, int32_t causal, dash_schedule schedu
 dash_status dash_schedule_predict(int32_t n, int32_t causal, dash_schedule schedule,
                                   int32_t heads, int32_t slots, const double cost[4],
                                   double out[4]);
+
+/*
+ * Schedule choice, host only (the explainer's significance section presents
+ * DASH as a palette of strategies, heuristic and optimal, from which the
+ * user picks by hardware and model configuration; this makes that pick from
+ * the DAG model).  Predicts the makespan of NAIVE, DESCENDING and SHIFT with
+ * dash_schedule_predict for `heads` heads on `slots` workgroups and the
+ * cost model `cost` (NULL: the library's default {1, 0.5, 0.05, 0.05} in
+ * units of one unmasked item: the dQ add and the hand-off are short next to
+ * an item because the kernel overlaps the add with the next item's
+ * compute), and returns the one
+ * with the smallest makespan (ties: SHIFT, then DESCENDING, then NAIVE).
+ * Schedules that cannot run (SHIFT with an odd causal tile count or more
+ * units per head than slots) are skipped.  predicted[3] (may be NULL)
+ * receives the three makespans in enum order NAIVE, DESCENDING, SHIFT, NaN
+ * where skipped.  For large problems the prediction uses a subset of the
+ * heads (at most about 2e5 items).  DASH_SCHED_AUTO in dash_attn_bwd uses
+ * this choice with slots = the co-resident workgroups of the launch.
+ */
+dash_status dash_schedule_choose(int32_t n, int32_t causal, int32_t heads, int32_t slots,
+                                 const double* cost, dash_schedule* choice, double* predicted);
+
+/*
+ * The schedule dash_attn_bwd runs for `schedule` on the current device:
+ * DASH_SCHED_AUTO resolves to dash_schedule_choose's pick for the
+ * problem's tile count, B*H heads and the launch's co-resident workgroups;
+ * other schedules come back unchanged.  Queries the device (occupancy),
+ * launches nothing.  Errors as dash_attn_bwd's argument checks.
+ */
+dash_status dash_attn_bwd_resolve_schedule(const dash_attn_desc* desc, dash_schedule schedule,
+                                           dash_schedule* resolved);
 
 /*
  * Longest path (critical path) of a general DAG, host only.  Node weights

@@ -202,3 +202,28 @@ def test_placement_changes_no_bit(causal):
             out = _bwd(dev, lse, delta, sched, causal, debug={"placement": place})
             for x, y in zip(ref, out):
                 assert torch.equal(x.view(torch.int16), y.view(torch.int16)), (sched, place)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+@pytest.mark.parametrize("shape", [(2, 16, 2048, 128), (1, 4, 1152, 128), (1, 64, 1024, 64)])
+def test_auto_runs_its_resolved_schedule(shape, causal):
+    """"auto" is bit-identical to the ordered schedule it resolves to, and
+    that schedule is the DAG model's pick for the launch's co-resident
+    workgroups."""
+    require_gpu()
+    B, H, N, d = shape
+    picked = D.resolve_schedule(B, H, N, d, "bf16", causal, "auto")
+    log(f"auto {shape} causal={causal} -> {picked}")
+    assert picked in ORDERED
+    for s in ORDERED + ["atomic"]:
+        assert D.resolve_schedule(B, H, N, d, "bf16", causal, s) == s
+    n = N // D.tile(B, H, N, d, "bf16")
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    # one or two workgroups per compute unit, by the kernel's occupancy
+    assert picked in {D.schedule_choose(n, causal, B * H, k * cus)[0] for k in (1, 2)}
+    dev, lse, delta = _prep(B, H, N, d, "bf16", causal, 8200)
+    ref = _bwd(dev, lse, delta, picked, causal)
+    for _ in range(3):
+        out = _bwd(dev, lse, delta, "auto", causal)
+        for x, y in zip(ref, out):
+            assert torch.equal(x.view(torch.int16), y.view(torch.int16))

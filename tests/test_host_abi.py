@@ -74,6 +74,62 @@ def test_predict_rejects_shift_without_resident_head():
     assert e.value.code == 2
 
 
+_CANDIDATES = (OS.NAIVE, OS.DESCENDING, OS.SHIFT)
+
+
+def _oracle_choice(n, causal, heads, slots, cost):
+    """Argmin of the oracle's predicted makespan over the ordered schedules
+    that can run; ties go to the later candidate."""
+    best, best_s, preds = None, None, {}
+    for s in _CANDIDATES:
+        if s == OS.SHIFT and ((causal and n % 2 and n > 1)
+                              or len(OS.units(s, n, causal)) > slots):
+            continue
+        mk = OD.predict(s, n, causal, heads, slots, cost)[0]
+        preds[s] = mk
+        if best is None or mk <= best:
+            best, best_s = mk, s
+    return best_s, preds
+
+
+def test_choose_is_argmin_of_oracle_prediction():
+    rnd = random.Random(17)
+    cases = [(n, c, h, sl) for n in (1, 2, 3, 5, 8, 16) for c in (False, True)
+             for h, sl in ((1, 4), (3, 8), (4, 16), (2, 3))]
+    for n, causal, heads, slots in cases:
+        cost = (rnd.uniform(1, 3), rnd.uniform(0.3, 2), rnd.uniform(0.01, 1.5),
+                rnd.uniform(0, 0.8))
+        want, preds = _oracle_choice(n, causal, heads, slots, cost)
+        got, pred = D.schedule_choose(n, causal, heads, slots, cost)
+        assert got == want, (n, causal, heads, slots, cost, pred, preds)
+        for s in _CANDIDATES:
+            if s in preds:
+                assert abs(pred[s] - preds[s]) <= 1e-9 * max(1.0, preds[s])
+            else:
+                assert np.isnan(pred[s])
+
+
+def test_choose_follows_the_pages_ordering():
+    # with every head's units resident and a costly dQ hand-off the DAG
+    # model ranks shift first for full masks and for causal masks with an
+    # even tile count, descending before naive for causal masks, and ties
+    # naive and descending for full masks
+    cost = (1.0, 0.5, 0.3, 0.3)
+    for n in (8, 16, 32):
+        got, pred = D.schedule_choose(n, False, 4, 4 * n, cost)
+        assert got == OS.SHIFT and pred[OS.SHIFT] < pred[OS.NAIVE] == pred[OS.DESCENDING]
+        got, pred = D.schedule_choose(n, True, 4, 2 * n, cost)
+        assert got == OS.SHIFT and pred[OS.SHIFT] < pred[OS.DESCENDING] < pred[OS.NAIVE]
+    # shift cannot run: odd causal tile count, or a head's units do not fit
+    got, pred = D.schedule_choose(9, True, 4, 64, cost)
+    assert got == OS.DESCENDING and np.isnan(pred[OS.SHIFT])
+    got, pred = D.schedule_choose(16, False, 4, 15, cost)
+    assert got == OS.DESCENDING and np.isnan(pred[OS.SHIFT])
+    # default cost model: the same shape of answer
+    assert D.schedule_choose(128, True, 32, 256)[0] == OS.SHIFT
+    assert D.schedule_choose(129, True, 32, 256)[0] == OS.DESCENDING
+
+
 def test_longest_path_and_cycle():
     rnd = random.Random(9)
     for _ in range(50):
@@ -105,7 +161,7 @@ def test_argument_errors_without_launch():
     assert lib.dash_attn_bwd_workspace_size(ctypes.byref(largest), 1, ctypes.byref(size)) == 0
     assert lib.dash_attn_bwd_workspace_size(ctypes.byref(_desc()), 1, ctypes.byref(size)) == 0
     # same size for every schedule (schedules only reorder work)
-    for s in range(4):
+    for s in range(5):
         sz = ctypes.c_size_t(0)
         assert lib.dash_attn_bwd_workspace_size(ctypes.byref(_desc()), s, ctypes.byref(sz)) == 0
         assert sz.value == size.value
@@ -130,7 +186,8 @@ def test_argument_errors_without_launch():
     mis = args[:9] + [ctypes.c_void_p(0x100010)]
     assert lib.dash_attn_bwd(ctypes.byref(desc), 1, *mis, ws_ok, None) == 3
     # bad schedule enum
-    assert lib.dash_attn_bwd(ctypes.byref(desc), 4, *args, ws_ok, None) == 1
+    assert lib.dash_attn_bwd(ctypes.byref(desc), 5, *args, ws_ok, None) == 1
+    assert lib.dash_attn_bwd(ctypes.byref(desc), -1, *args, ws_ok, None) == 1
     # debug struct required for the debug entry point; poison out of range
     assert lib.dash_attn_bwd_debug(ctypes.byref(desc), 1, *args, ws_ok, None, None) == 1
     dbg = _lib.Debug(0, 0, 10_000, None)
@@ -142,6 +199,16 @@ def test_argument_errors_without_launch():
                                        None) == 1
     # host-only argument checks
     assert lib.dash_schedule_predict(0, 0, 1, 1, 1, None, None) == 1
+    choice = ctypes.c_int(-1)
+    assert lib.dash_schedule_choose(0, 0, 1, 1, None, ctypes.byref(choice), None) == 1
+    assert lib.dash_schedule_choose(8, 2, 1, 1, None, ctypes.byref(choice), None) == 1
+    assert lib.dash_schedule_choose(8, 0, 1, 0, None, ctypes.byref(choice), None) == 1
+    assert lib.dash_schedule_choose(8, 0, 1, 8, None, None, None) == 1
+    assert lib.dash_attn_bwd_resolve_schedule(None, 4, ctypes.byref(choice)) == 1
+    assert lib.dash_attn_bwd_resolve_schedule(ctypes.byref(desc), 5, ctypes.byref(choice)) == 1
+    assert lib.dash_attn_bwd_resolve_schedule(ctypes.byref(desc), 4, None) == 1
+    assert lib.dash_attn_bwd_resolve_schedule(ctypes.byref(_desc(d=96)), 4,
+                                              ctypes.byref(choice)) == 2
     assert lib.dash_litmus_ordered_add(0, 1, FAKE, FAKE, FAKE, FAKE, 0, None) == 1
     assert lib.dash_attn_bwd_status(None, None) == 1
     assert lib.dash_attn_tile(None) == 0 and lib.dash_attn_bwd_subtile(None) == 0
