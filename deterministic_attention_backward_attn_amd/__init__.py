@@ -22,7 +22,7 @@ from ._lib import DTYPES, SCHEDULES, DashError, Debug, Desc, check, header_symbo
 __all__ = [
     "DashError", "SCHEDULES", "attn_fwd", "attn_bwd_preprocess", "attn_bwd_workspace_size",
     "attn_bwd", "attn_bwd_status", "backward", "schedule_tables", "schedule_predict", "schedule_choose",
-    "resolve_schedule",
+    "resolve_schedule", "mask_schedule_tables", "mask_schedule_predict",
     "dag_longest_path", "litmus_ordered_add", "tile", "subtile", "header_symbols", "load",
 ]
 
@@ -43,17 +43,34 @@ def _dtype_code(t):
     raise TypeError(f"unsupported dtype {t.dtype} (float32 or bfloat16)")
 
 
-def _desc_from(q, causal: bool, scale) -> Desc:
+def _set_mask(desc: Desc, window=0, block_mask=None, block_size=0) -> Desc:
+    """Window and block mask fields (see the C header); the descriptor keeps
+    the block mask's host buffer alive."""
+    desc.window = int(window)
+    if block_mask is not None:
+        bm = np.ascontiguousarray(np.asarray(block_mask) != 0, dtype=np.uint8)
+        if bm.ndim != 2 or bm.shape[0] != bm.shape[1]:
+            raise ValueError("block_mask must be a square 2-D array")
+        desc.block_size = int(block_size) if block_size else desc.N // bm.shape[0]
+        desc.block_mask = bm.ctypes.data
+        desc._keep = bm
+    return desc
+
+
+def _desc_from(q, causal: bool, scale, window=0, block_mask=None, block_size=0) -> Desc:
     if q.dim() != 4:
         raise ValueError("expected a [B, H, N, d] tensor")
     B, H, N, d = (int(x) for x in q.shape)
-    return Desc(B, H, N, d, _dtype_code(q), 1 if causal else 0,
-                float(scale) if scale is not None else 0.0)
+    return _set_mask(Desc(B, H, N, d, _dtype_code(q), 1 if causal else 0,
+                          float(scale) if scale is not None else 0.0),
+                     window, block_mask, block_size)
 
 
-def _desc(B, H, N, d, dtype: str, causal: bool, scale=None) -> Desc:
-    return Desc(B, H, N, d, DTYPES[dtype], 1 if causal else 0,
-                float(scale) if scale is not None else 0.0)
+def _desc(B, H, N, d, dtype: str, causal: bool, scale=None, window=0, block_mask=None,
+          block_size=0) -> Desc:
+    return _set_mask(Desc(B, H, N, d, DTYPES[dtype], 1 if causal else 0,
+                          float(scale) if scale is not None else 0.0),
+                     window, block_mask, block_size)
 
 
 def _ptr(t):
@@ -99,12 +116,16 @@ def subtile(B, H, N, d, dtype="bf16") -> int:
     return int(lib.dash_attn_bwd_subtile(ctypes.byref(_desc(B, H, N, d, dtype, False))))
 
 
-def attn_fwd(q, k, v, causal: bool = False, scale=None, stream=None):
-    """Returns (o, lse): o like q, lse float32 [B, H, N]."""
+def attn_fwd(q, k, v, causal: bool = False, scale=None, stream=None, *, window=0,
+             block_mask=None, block_size=0):
+    """Returns (o, lse): o like q, lse float32 [B, H, N].  Mask: causal,
+    window (sliding window of keys, 0 = none) and block_mask (square host
+    array over blocks of block_size rows; default N / its side), as in the
+    C header."""
     torch = _torch()
     lib = load()
     _same_shape(q, k, v)
-    desc = _desc_from(q, causal, scale)
+    desc = _desc_from(q, causal, scale, window, block_mask, block_size)
     o = torch.empty_like(q)
     lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
     check(lib.dash_attn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
@@ -138,12 +159,14 @@ def attn_bwd_workspace_size(B, H, N, d, dtype="bf16", causal=False, schedule="na
     return int(out.value)
 
 
-def resolve_schedule(B, H, N, d, dtype="bf16", causal=False, schedule="auto") -> str:
+def resolve_schedule(B, H, N, d, dtype="bf16", causal=False, schedule="auto", *, window=0,
+                     block_mask=None, block_size=0) -> str:
     """The schedule attn_bwd runs for `schedule` on the current device
     ("auto" -> the predicted best ordered schedule; others unchanged)."""
     lib = load()
     out = ctypes.c_int(-1)
-    check(lib.dash_attn_bwd_resolve_schedule(ctypes.byref(_desc(B, H, N, d, dtype, causal)),
+    desc = _desc(B, H, N, d, dtype, causal, None, window, block_mask, block_size)
+    check(lib.dash_attn_bwd_resolve_schedule(ctypes.byref(desc),
                                              _sched(schedule), ctypes.byref(out)),
           "dash_attn_bwd_resolve_schedule")
     return {v: k for k, v in SCHEDULES.items()}[out.value]
@@ -158,18 +181,20 @@ def alloc_workspace(q, causal=False, schedule="naive"):
 
 
 def attn_bwd(q, k, v, do, lse, delta, *, schedule="naive", causal=False, scale=None,
-             workspace=None, out=None, debug=None, stream=None):
+             workspace=None, out=None, debug=None, stream=None, window=0, block_mask=None,
+             block_size=0):
     """Returns (dq, dk, dv).  `workspace`: uint8 GPU tensor of at least
     attn_bwd_workspace_size bytes (allocated if None).  `out`: optional
     preallocated (dq, dk, dv).  `debug`: optional dict with keys spin_limit,
     jitter_seed, poison_q (1-based, 0 = off), partials (float32 tensor),
     kernel_events (two raw hipEvent_t handles), wait_stats (int64 tensor of
     at least 4*4096*4 entries), placement (0 automatic, 1 device-wide, 2 XCD
-    groups with L2-coherent accumulator, 3 XCD groups device-coherent)."""
+    groups with L2-coherent accumulator, 3 XCD groups device-coherent).
+    Mask arguments as for attn_fwd."""
     torch = _torch()
     lib = load()
     _same_shape(q, k, v, do)
-    desc = _desc_from(q, causal, scale)
+    desc = _desc_from(q, causal, scale, window, block_mask, block_size)
     if workspace is None:
         workspace = alloc_workspace(q, causal, schedule)
     if out is None:
@@ -208,11 +233,12 @@ def attn_bwd_status(workspace, stream=None):
 
 
 def backward(q, k, v, o, do, lse, *, schedule="naive", causal=False, scale=None,
-             workspace=None, stream=None):
+             workspace=None, stream=None, window=0, block_mask=None, block_size=0):
     """preprocess + bwd: returns (dq, dk, dv)."""
     delta = attn_bwd_preprocess(o, do, stream=stream)
     return attn_bwd(q, k, v, do, lse, delta, schedule=schedule, causal=causal, scale=scale,
-                    workspace=workspace, stream=stream)
+                    workspace=workspace, stream=stream, window=window, block_mask=block_mask,
+                    block_size=block_size)
 
 
 def litmus_ordered_add(turn, values, acc, counters, spin_limit=0, stream=None):
@@ -242,6 +268,54 @@ def schedule_tables(n: int, causal: bool, schedule):
     for u in range(n_units.value):
         units.append([(kv[i], qq[i]) for i in range(off[u], off[u + 1])])
     return units, np.frombuffer(rank, dtype=np.int32).reshape(n, n).copy()
+
+
+def mask_schedule_tables(B, H, N, d, dtype="bf16", causal=False, schedule="naive", *, window=0,
+                         block_mask=None, block_size=0):
+    """The backward's tables for a masked problem.  Returns a dict: n
+    (tiles per side), units (per unit [(kv, q), ...]), steps (per unit, the
+    lockstep step of each item; SHIFT only, else None), partial (per unit,
+    per item bool), rank (int32 [n, n], rank[q, kv], -1 where absent)."""
+    lib = load()
+    desc = _desc(B, H, N, d, dtype, causal, None, window, block_mask, block_size)
+    sizes = (ctypes.c_int32 * 3)()
+    check(lib.dash_attn_schedule_tables(ctypes.byref(desc), _sched(schedule), sizes, None, None,
+                                        None, None, None, None), "dash_attn_schedule_tables")
+    n, nu, ni = sizes[0], sizes[1], sizes[2]
+    off = np.zeros(nu + 1, dtype=np.int32)
+    kv = np.zeros(max(ni, 1), dtype=np.int32)
+    qq = np.zeros(max(ni, 1), dtype=np.int32)
+    st = np.zeros(max(ni, 1), dtype=np.int32)
+    pa = np.zeros(max(ni, 1), dtype=np.uint8)
+    rank = np.zeros(n * n, dtype=np.int32)
+    ip = ctypes.POINTER(ctypes.c_int32)
+    check(lib.dash_attn_schedule_tables(ctypes.byref(desc), _sched(schedule), sizes,
+                                        off.ctypes.data_as(ip), kv.ctypes.data_as(ip),
+                                        qq.ctypes.data_as(ip), st.ctypes.data_as(ip),
+                                        pa.ctypes.data, rank.ctypes.data_as(ip)),
+          "dash_attn_schedule_tables")
+    units, steps, partial = [], [], []
+    for u in range(nu):
+        sl = range(off[u], off[u + 1])
+        units.append([(int(kv[i]), int(qq[i])) for i in sl])
+        steps.append([int(st[i]) for i in sl])
+        partial.append([bool(pa[i]) for i in sl])
+    shift = _sched(schedule) == SCHEDULES["shift"]
+    return {"n": n, "units": units, "steps": steps if shift else None, "partial": partial,
+            "rank": rank.reshape(n, n)}
+
+
+def mask_schedule_predict(B, H, N, d, dtype="bf16", causal=False, schedule="naive", *, slots,
+                          cost, window=0, block_mask=None, block_size=0):
+    """DAG prediction for a masked problem with B*H heads: (makespan,
+    total_wait, max_slot_idle, lower_bound)."""
+    lib = load()
+    desc = _desc(B, H, N, d, dtype, causal, None, window, block_mask, block_size)
+    c = (ctypes.c_double * 4)(*[float(x) for x in cost])
+    out = (ctypes.c_double * 4)()
+    check(lib.dash_attn_schedule_predict(ctypes.byref(desc), _sched(schedule), int(slots), c, out),
+          "dash_attn_schedule_predict")
+    return tuple(out)
 
 
 def schedule_predict(n: int, causal: bool, schedule, heads: int, slots: int, cost):

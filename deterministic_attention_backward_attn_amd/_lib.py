@@ -36,7 +36,8 @@ class DashError(RuntimeError):
 class Desc(ctypes.Structure):
     _fields_ = [("B", ctypes.c_int32), ("H", ctypes.c_int32), ("N", ctypes.c_int32),
                 ("d", ctypes.c_int32), ("dtype", ctypes.c_int32), ("causal", ctypes.c_int32),
-                ("softmax_scale", ctypes.c_float)]
+                ("softmax_scale", ctypes.c_float), ("window", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("block_mask", ctypes.c_void_p)]
 
 
 class Debug(ctypes.Structure):
@@ -69,6 +70,9 @@ _SIGS = {
     "dash_schedule_predict": (ctypes.c_int, [_i32, _i32, ctypes.c_int, _i32, _i32, _dp, _dp]),
     "dash_attn_bwd_resolve_schedule": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int,
                                                       ctypes.POINTER(ctypes.c_int)]),
+    "dash_attn_schedule_tables": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, _ip, _ip, _ip,
+                                                 _ip, _ip, ctypes.c_void_p, _ip]),
+    "dash_attn_schedule_predict": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, _i32, _dp, _dp]),
     "dash_schedule_choose": (ctypes.c_int, [_i32, _i32, _i32, _i32, _dp,
                                             ctypes.POINTER(ctypes.c_int), _dp]),
     "dash_dag_longest_path": (ctypes.c_int, [_i32, _dp, _i32, _ip, _ip, _dp, _dp, _dp]),

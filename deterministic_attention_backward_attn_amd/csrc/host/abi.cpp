@@ -22,6 +22,7 @@ using dash::Tables;
 
 constexpr size_t kHeaderBytes = 256;   // status, work counters, XCD census (64 words)
 constexpr uint32_t kDefaultSpin = 1u << 21;  // polls before giving up (seconds)
+constexpr int kMaxMaskedTiles = 2048;        // tiles per side with a window or block mask
 
 size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
 
@@ -36,7 +37,7 @@ constexpr double kDefaultCost[4] = {1.0, 0.5, 0.05, 0.05};
 
 // The ordered schedule with the smallest predicted makespan; see
 // dash_schedule_choose.
-dash_status choose_schedule(int n, bool causal, int heads, int slots, const double cost[4],
+dash_status choose_schedule(const dash::TileMask& m, int heads, int slots, const double cost[4],
                             Sched* choice, double pred[3]) {
   const Sched cand[3] = {Sched::Naive, Sched::Descending, Sched::Shift};
   double best = 0.0;
@@ -44,7 +45,7 @@ dash_status choose_schedule(int n, bool causal, int heads, int slots, const doub
   for (int i = 0; i < 3; ++i) {
     pred[i] = NAN;
     Tables t;
-    if (!dash::build_tables(n, causal, cand[i], t)) continue;
+    if (!dash::build_tables(m, cand[i], t)) continue;
     if (dash::validate_tables(t)[0] != '\0') return DASH_ERR_SCHEDULE_INVALID;
     if (t.needs_static() && t.units() > slots) continue;
     // a subset of the heads keeps the prediction to about 2e5 items
@@ -79,7 +80,50 @@ dash_status check_desc(const dash_attn_desc* d) {
   // stay below 2^31, the out-of-range offset the kernel uses for idle loads
   if (heads * d->N >= (1LL << 31) || d->N / tile > 32767 || (long long)d->N * d->d >= (1LL << 29))
     return DASH_ERR_UNSUPPORTED;
+  // mask fields
+  if (d->window < 0) return DASH_ERR_INVALID_ARG;
+  if (d->block_mask) {
+    if (d->block_size < 1) return DASH_ERR_INVALID_ARG;
+    if (d->block_size % tile || d->N % d->block_size) return DASH_ERR_UNSUPPORTED;
+  }
+  const bool special = d->block_mask || (d->window > 0 && d->window < d->N);
+  if (special && d->N / tile > kMaxMaskedTiles) return DASH_ERR_UNSUPPORTED;
   return DASH_OK;
+}
+
+// The mask as the schedule and the kernels see it: tiles per side, causal,
+// the window (0 when it covers the whole sequence) and the block mask at
+// block granularity (0/1 bytes; empty without one).
+struct MaskKey {
+  int n = 0, tile = 0, causal = 0, window = 0, bt = 0;
+  std::vector<uint8_t> block;
+  bool operator<(const MaskKey& o) const {
+    return std::tie(n, tile, causal, window, bt, block) <
+           std::tie(o.n, o.tile, o.causal, o.window, o.bt, o.block);
+  }
+  bool masked() const { return causal || window > 0 || !block.empty(); }
+};
+
+MaskKey mask_key(const dash_attn_desc* d) {
+  int bc = 0, br = 0;
+  dash::bwd_tiles(d->dtype, d->d, &bc, &br);
+  MaskKey k;
+  k.tile = bc;
+  k.n = d->N / bc;
+  k.causal = d->causal != 0;
+  k.window = (d->window > 0 && d->window < d->N) ? d->window : 0;
+  if (d->block_mask) {
+    k.bt = d->block_size / bc;
+    const int nb = d->N / d->block_size;
+    k.block.resize((size_t)nb * nb);
+    for (size_t i = 0; i < k.block.size(); ++i) k.block[i] = d->block_mask[i] ? 1 : 0;
+  }
+  return k;
+}
+
+dash::TileMask tile_mask(const MaskKey& k) {
+  return dash::make_mask(k.n, k.tile, k.causal != 0, k.window,
+                         k.block.empty() ? nullptr : k.block.data(), k.bt);
 }
 
 float scale_of(const dash_attn_desc* d) {
@@ -112,33 +156,91 @@ struct DevTables {
   int2* d_items = nullptr;
 };
 
-std::mutex g_mu;
-std::map<std::tuple<int, int, int, int>, DevTables> g_tables;  // (device, n, causal, sched)
-std::map<std::tuple<int, int, int, int, int>, int> g_coresident;  // (device, dtype, d, causal, ordered)
-std::map<std::tuple<int, int, int, int>, Sched> g_auto;  // (n, causal, heads, slots) -> choice
+// Per mask: tile liveness for the forward (block masks only) and the tiles
+// no pair touches (their gradient rows are cleared by the host).
+struct DevMask {
+  dash::TileMask host;
+  uint8_t* d_live = nullptr;  // [n * n] by [q * n + kv], block masks only
+  int* d_dead = nullptr;      // dead Q blocks, then dead KV tiles
+  int n_dead_q = 0, n_dead_kv = 0;
+};
 
-dash_status get_tables(int dev, int n, bool causal, Sched s, const DevTables** out) {
+std::mutex g_mu;
+std::map<std::tuple<int, MaskKey, int>, DevTables> g_tables;  // (device, mask, sched)
+std::map<std::pair<int, MaskKey>, DevMask> g_masks;           // (device, mask)
+std::map<std::tuple<int, int, int, int, int>, int> g_coresident;  // (device, dtype, d, masked, ordered)
+std::map<std::tuple<MaskKey, int, int>, Sched> g_auto;  // (mask, heads, slots) -> choice
+
+dash_status get_mask(int dev, const MaskKey& key, const DevMask** out) {
   std::lock_guard<std::mutex> lock(g_mu);
-  auto key = std::make_tuple(dev, n, (int)causal, (int)s);
+  auto mk = std::make_pair(dev, key);
+  auto it = g_masks.find(mk);
+  if (it != g_masks.end()) {
+    *out = &it->second;
+    return DASH_OK;
+  }
+  DevMask dm;
+  dm.host = tile_mask(key);
+  const int n = key.n;
+  std::vector<int> dead;
+  for (int q = 0; q < n; ++q) {
+    bool any = false;
+    for (int kv = 0; kv < n && !any; ++kv) any = dm.host.live[(size_t)q * n + kv] != 0;
+    if (!any) dead.push_back(q);
+  }
+  dm.n_dead_q = (int)dead.size();
+  for (int kv = 0; kv < n; ++kv) {
+    bool any = false;
+    for (int q = 0; q < n && !any; ++q) any = dm.host.live[(size_t)q * n + kv] != 0;
+    if (!any) dead.push_back(kv);
+  }
+  dm.n_dead_kv = (int)dead.size() - dm.n_dead_q;
+  if (!key.block.empty()) {
+    if (hipMalloc(&dm.d_live, dm.host.live.size()) != hipSuccess) return DASH_ERR_HIP;
+    if (hipMemcpy(dm.d_live, dm.host.live.data(), dm.host.live.size(), hipMemcpyHostToDevice) !=
+        hipSuccess) {
+      (void)hipFree(dm.d_live);
+      return DASH_ERR_HIP;
+    }
+  }
+  if (!dead.empty()) {
+    if (hipMalloc(&dm.d_dead, sizeof(int) * dead.size()) != hipSuccess ||
+        hipMemcpy(dm.d_dead, dead.data(), sizeof(int) * dead.size(), hipMemcpyHostToDevice) !=
+            hipSuccess) {
+      if (dm.d_live) (void)hipFree(dm.d_live);
+      if (dm.d_dead) (void)hipFree(dm.d_dead);
+      return DASH_ERR_HIP;
+    }
+  }
+  auto res = g_masks.emplace(mk, std::move(dm));
+  *out = &res.first->second;
+  return DASH_OK;
+}
+
+dash_status get_tables(int dev, const MaskKey& mkey, const dash::TileMask& m, Sched s,
+                       const DevTables** out) {
+  std::lock_guard<std::mutex> lock(g_mu);
+  auto key = std::make_tuple(dev, mkey, (int)s);
   auto it = g_tables.find(key);
   if (it != g_tables.end()) {
     *out = &it->second;
     return DASH_OK;
   }
   DevTables dt;
-  if (!dash::build_tables(n, causal, s, dt.host)) return DASH_ERR_UNSUPPORTED;
+  if (!dash::build_tables(m, s, dt.host)) return DASH_ERR_UNSUPPORTED;
   if (dash::validate_tables(dt.host)[0] != '\0') return DASH_ERR_SCHEDULE_INVALID;
   const Tables& t = dt.host;
+  const int n = t.n;
   std::vector<int2> items(t.items());
   std::vector<int> contributors(n, 0);
   for (int i = 0; i < t.items(); ++i) ++contributors[t.q[i]];
   for (int i = 0; i < t.items(); ++i) {
     items[i].x = t.kv[i] | (t.q[i] << 16);
+    // bit 29: the pair has hidden elements (the kernel masks them)
+    items[i].y = t.partial[(size_t)t.q[i] * n + t.kv[i]] ? (1 << 29) : 0;
     if (t.ordered()) {
       const int r = t.rank[(size_t)t.q[i] * n + t.kv[i]];
-      items[i].y = r | ((r == contributors[t.q[i]] - 1) ? (1 << 30) : 0);
-    } else {
-      items[i].y = 0;
+      items[i].y |= r | ((r == contributors[t.q[i]] - 1) ? (1 << 30) : 0);
     }
   }
   if (hipMalloc(&dt.d_unit_off, sizeof(int) * t.unit_off.size()) != hipSuccess) return DASH_ERR_HIP;
@@ -148,8 +250,9 @@ dash_status get_tables(int dev, int n, bool causal, Sched s, const DevTables** o
   }
   if (hipMemcpy(dt.d_unit_off, t.unit_off.data(), sizeof(int) * t.unit_off.size(),
                 hipMemcpyHostToDevice) != hipSuccess ||
-      hipMemcpy(dt.d_items, items.data(), sizeof(int2) * items.size(), hipMemcpyHostToDevice) !=
-          hipSuccess) {
+      (!items.empty() &&
+       hipMemcpy(dt.d_items, items.data(), sizeof(int2) * items.size(), hipMemcpyHostToDevice) !=
+           hipSuccess)) {
     (void)hipFree(dt.d_unit_off);
     (void)hipFree(dt.d_items);
     return DASH_ERR_HIP;
@@ -159,16 +262,16 @@ dash_status get_tables(int dev, int n, bool causal, Sched s, const DevTables** o
   return DASH_OK;
 }
 
-dash_status get_coresident(int dev, int dtype, int d, bool causal, bool ordered, int* blocks) {
+dash_status get_coresident(int dev, int dtype, int d, bool masked, bool ordered, int* blocks) {
   std::lock_guard<std::mutex> lock(g_mu);
-  auto key = std::make_tuple(dev, dtype, d, (int)causal, (int)ordered);
+  auto key = std::make_tuple(dev, dtype, d, (int)masked, (int)ordered);
   auto it = g_coresident.find(key);
   if (it != g_coresident.end()) {
     *blocks = it->second;
     return DASH_OK;
   }
   int b = 0;
-  if (dash::bwd_max_coresident(dtype, d, causal, ordered, &b) != hipSuccess || b < 1)
+  if (dash::bwd_max_coresident(dtype, d, masked, ordered, &b) != hipSuccess || b < 1)
     return DASH_ERR_HIP;
   g_coresident[key] = b;
   *blocks = b;
@@ -177,12 +280,12 @@ dash_status get_coresident(int dev, int dtype, int d, bool causal, bool ordered,
 
 // DASH_SCHED_AUTO -> the predicted best ordered schedule for this problem
 // on `maxco` co-resident workgroups (cached per shape); others unchanged.
-dash_status resolve_schedule(dash_schedule schedule, int n, bool causal, long heads, int maxco,
-                             Sched* s) {
+dash_status resolve_schedule(dash_schedule schedule, const MaskKey& mkey, const dash::TileMask& m,
+                             long heads, int maxco, Sched* s) {
   *s = (Sched)schedule;
   if (schedule != DASH_SCHED_AUTO) return DASH_OK;
   const int h = (int)std::min<long>(heads, 1L << 30);
-  const auto key = std::make_tuple(n, (int)causal, h, maxco);
+  const auto key = std::make_tuple(mkey, h, maxco);
   std::lock_guard<std::mutex> lock(g_mu);
   auto it = g_auto.find(key);
   if (it != g_auto.end()) {
@@ -190,7 +293,7 @@ dash_status resolve_schedule(dash_schedule schedule, int n, bool causal, long he
     return DASH_OK;
   }
   double pred[3];
-  const dash_status st = choose_schedule(n, causal, h, maxco, kDefaultCost, s, pred);
+  const dash_status st = choose_schedule(m, h, maxco, kDefaultCost, s, pred);
   if (st != DASH_OK) return st;
   g_auto[key] = *s;
   return DASH_OK;
@@ -210,22 +313,27 @@ dash_status run_bwd(const dash_attn_desc* desc, dash_schedule schedule, const vo
   int bc = 0, br = 0;
   dash::bwd_tiles(desc->dtype, desc->d, &bc, &br);
   const int n = desc->N / bc;
-  const bool causal = desc->causal != 0;
   const bool ordered = schedule != DASH_SCHED_ATOMIC;
   if (dbg && (dbg->poison_q < 0 || dbg->poison_q > desc->N / br)) return DASH_ERR_INVALID_ARG;
   if (dbg && (dbg->placement < 0 || dbg->placement > 3)) return DASH_ERR_INVALID_ARG;
 
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return DASH_ERR_HIP;
+  const MaskKey mkey = mask_key(desc);
+  const DevMask* dm = nullptr;
+  st = get_mask(dev, mkey, &dm);
+  if (st != DASH_OK) return st;
+  // elements are masked inside some pairs (causal diagonal, window edges)
+  const bool masked = dm->host.any_partial();
   int maxco = 0;
-  st = get_coresident(dev, desc->dtype, desc->d, causal, ordered, &maxco);
+  st = get_coresident(dev, desc->dtype, desc->d, masked, ordered, &maxco);
   if (st != DASH_OK) return st;
   const long heads = (long)desc->B * desc->H;
   Sched s = Sched::Naive;
-  st = resolve_schedule(schedule, n, causal, heads, maxco, &s);
+  st = resolve_schedule(schedule, mkey, dm->host, heads, maxco, &s);
   if (st != DASH_OK) return st;
   const DevTables* tb = nullptr;
-  st = get_tables(dev, n, causal, s, &tb);
+  st = get_tables(dev, mkey, dm->host, s, &tb);
   if (st != DASH_OK) return st;
 
   const int U = tb->host.units();
@@ -234,7 +342,9 @@ dash_status run_bwd(const dash_attn_desc* desc, dash_schedule schedule, const vo
       return DASH_ERR_UNSUPPORTED;
   const long total_units = heads * U;
   int grid = 0, p_eff = 0, dynamic = 0;
-  if (tb->host.needs_static()) {
+  if (U == 0) {
+    // no live pair at all: only the dead-tile clears below run
+  } else if (tb->host.needs_static()) {
     p_eff = (maxco / U) * U;
     if (p_eff < 1) return DASH_ERR_UNSUPPORTED;  // a whole head must be resident
     if (p_eff > total_units) p_eff = (int)total_units;
@@ -269,6 +379,7 @@ dash_status run_bwd(const dash_attn_desc* desc, dash_schedule schedule, const vo
   a.items = tb->d_items;
   a.N = desc->N;
   a.n_tiles = n;
+  dash::mask_bounds(mkey.causal != 0, mkey.window, &a.mask_lo, &a.mask_hi);
   a.units_per_head = U;
   a.total_units = (int)total_units;
   a.p_eff = p_eff;
@@ -290,9 +401,24 @@ dash_status run_bwd(const dash_attn_desc* desc, dash_schedule schedule, const vo
   hipEvent_t ev0 = dbg ? (hipEvent_t)dbg->kernel_events[0] : nullptr;
   hipEvent_t ev1 = dbg ? (hipEvent_t)dbg->kernel_events[1] : nullptr;
   if (ev0 && hipEventRecord(ev0, strm) != hipSuccess) return DASH_ERR_HIP;
-  if (dash::launch_bwd(desc->dtype, desc->d, causal, ordered, a, grid, strm) != hipSuccess)
+  if (U > 0 && dash::launch_bwd(desc->dtype, desc->d, masked, ordered, a, grid, strm) != hipSuccess)
     return DASH_ERR_HIP;
   if (ev1 && hipEventRecord(ev1, strm) != hipSuccess) return DASH_ERR_HIP;
+  // gradient rows no pair touches: dQ of Q blocks that see no key (the
+  // atomic path's conversion already writes them), dK and dV of KV tiles no
+  // query sees
+  if (ordered && dm->n_dead_q &&
+      dash::launch_zero_tiles(desc->dtype, dq, dm->d_dead, dm->n_dead_q, bc, desc->d, desc->N,
+                              (int)heads, strm) != hipSuccess)
+    return DASH_ERR_HIP;
+  if (dm->n_dead_kv) {
+    const int* kvs = dm->d_dead + dm->n_dead_q;
+    if (dash::launch_zero_tiles(desc->dtype, dk, kvs, dm->n_dead_kv, bc, desc->d, desc->N,
+                                (int)heads, strm) != hipSuccess ||
+        dash::launch_zero_tiles(desc->dtype, dv, kvs, dm->n_dead_kv, bc, desc->d, desc->N,
+                                (int)heads, strm) != hipSuccess)
+      return DASH_ERR_HIP;
+  }
   if (!ordered) {
     // the atomic schedule accumulates everything first, then scales/converts
     const size_t elems = (size_t)heads * desc->N * desc->d;
@@ -347,8 +473,20 @@ dash_status dash_attn_fwd(const dash_attn_desc* desc, const void* q, const void*
   a.N = desc->N;
   a.BH = desc->B * desc->H;
   a.scale_log2 = scale_of(desc) * 1.4426950408889634f;
-  if (dash::launch_fwd(desc->dtype, desc->d, desc->causal != 0, a, (hipStream_t)stream) !=
-      hipSuccess)
+  const MaskKey mkey = mask_key(desc);
+  a.live = nullptr;
+  a.n_tiles = mkey.n;
+  a.tile = mkey.tile;
+  dash::mask_bounds(mkey.causal != 0, mkey.window, &a.mask_lo, &a.mask_hi);
+  if (!mkey.block.empty()) {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return DASH_ERR_HIP;
+    const DevMask* dm = nullptr;
+    st = get_mask(dev, mkey, &dm);
+    if (st != DASH_OK) return st;
+    a.live = dm->d_live;
+  }
+  if (dash::launch_fwd(desc->dtype, desc->d, mkey.masked(), a, (hipStream_t)stream) != hipSuccess)
     return DASH_ERR_HIP;
   return DASH_OK;
 }
@@ -442,17 +580,18 @@ dash_status dash_attn_bwd_resolve_schedule(const dash_attn_desc* desc, dash_sche
   dash_status st = check_desc(desc);
   if (st != DASH_OK) return st;
   if (!sched_ok_run(schedule) || !resolved) return DASH_ERR_INVALID_ARG;
-  int bc = 0, br = 0;
-  dash::bwd_tiles(desc->dtype, desc->d, &bc, &br);
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return DASH_ERR_HIP;
+  const MaskKey mkey = mask_key(desc);
+  const DevMask* dm = nullptr;
+  st = get_mask(dev, mkey, &dm);
+  if (st != DASH_OK) return st;
   int maxco = 0;
-  st = get_coresident(dev, desc->dtype, desc->d, desc->causal != 0,
+  st = get_coresident(dev, desc->dtype, desc->d, dm->host.any_partial(),
                       schedule != DASH_SCHED_ATOMIC, &maxco);
   if (st != DASH_OK) return st;
   Sched s = Sched::Naive;
-  st = resolve_schedule(schedule, desc->N / bc, desc->causal != 0, (long)desc->B * desc->H, maxco,
-                        &s);
+  st = resolve_schedule(schedule, mkey, dm->host, (long)desc->B * desc->H, maxco, &s);
   if (st != DASH_OK) return st;
   *resolved = (dash_schedule)s;
   return DASH_OK;
@@ -467,10 +606,62 @@ dash_status dash_schedule_choose(int32_t n, int32_t causal, int32_t heads, int32
     if (!(c[i] >= 0.0) || !std::isfinite(c[i])) return DASH_ERR_INVALID_ARG;
   Sched s = Sched::Naive;
   double pred[3];
-  const dash_status st = choose_schedule(n, causal != 0, heads, slots, c, &s, pred);
+  const dash_status st = choose_schedule(dash::plain_mask(n, causal != 0), heads, slots, c, &s, pred);
   if (st != DASH_OK) return st;
   *choice = (dash_schedule)s;
   if (predicted) std::memcpy(predicted, pred, sizeof(pred));
+  return DASH_OK;
+}
+
+dash_status dash_attn_schedule_tables(const dash_attn_desc* desc, dash_schedule schedule,
+                                      int32_t sizes[3], int32_t* unit_offsets, int32_t* item_kv,
+                                      int32_t* item_q, int32_t* item_step, uint8_t* item_partial,
+                                      int32_t* rank) {
+  dash_status st = check_desc(desc);
+  if (st != DASH_OK) return st;
+  if (!sched_ok(schedule) || !sizes) return DASH_ERR_INVALID_ARG;
+  const MaskKey mkey = mask_key(desc);
+  const dash::TileMask m = tile_mask(mkey);
+  Tables t;
+  if (!dash::build_tables(m, (Sched)schedule, t)) return DASH_ERR_UNSUPPORTED;
+  if (dash::validate_tables(t)[0] != '\0') return DASH_ERR_SCHEDULE_INVALID;
+  const bool fill = unit_offsets && item_kv && item_q && item_step && item_partial && rank;
+  if (fill && (sizes[0] != t.n || sizes[1] != t.units() || sizes[2] != t.items()))
+    return DASH_ERR_INVALID_ARG;
+  sizes[0] = t.n;
+  sizes[1] = t.units();
+  sizes[2] = t.items();
+  if (!fill) return DASH_OK;
+  std::memcpy(unit_offsets, t.unit_off.data(), sizeof(int) * t.unit_off.size());
+  if (t.items()) {
+    std::memcpy(item_kv, t.kv.data(), sizeof(int) * t.kv.size());
+    std::memcpy(item_q, t.q.data(), sizeof(int) * t.q.size());
+  }
+  for (int i = 0; i < t.items(); ++i) {
+    item_step[i] = t.step.empty() ? -1 : t.step[i];
+    item_partial[i] = t.partial[(size_t)t.q[i] * t.n + t.kv[i]];
+  }
+  std::memcpy(rank, t.rank.data(), sizeof(int) * t.rank.size());
+  return DASH_OK;
+}
+
+dash_status dash_attn_schedule_predict(const dash_attn_desc* desc, dash_schedule schedule,
+                                       int32_t slots, const double cost[4], double out[4]) {
+  dash_status st = check_desc(desc);
+  if (st != DASH_OK) return st;
+  if (!sched_ok(schedule) || slots < 1 || !cost || !out) return DASH_ERR_INVALID_ARG;
+  for (int i = 0; i < 4; ++i)
+    if (!(cost[i] >= 0.0) || !std::isfinite(cost[i])) return DASH_ERR_INVALID_ARG;
+  Tables t;
+  if (!dash::build_tables(tile_mask(mask_key(desc)), (Sched)schedule, t)) return DASH_ERR_UNSUPPORTED;
+  if (dash::validate_tables(t)[0] != '\0') return DASH_ERR_SCHEDULE_INVALID;
+  if (t.needs_static() && t.units() > slots) return DASH_ERR_UNSUPPORTED;
+  dash::DagResult r;
+  if (!dash::dag_predict(t, desc->B * desc->H, slots, cost, r)) return DASH_ERR_SCHEDULE_INVALID;
+  out[0] = r.makespan;
+  out[1] = r.total_wait;
+  out[2] = r.max_slot_idle;
+  out[3] = r.lower_bound;
   return DASH_OK;
 }
 

@@ -37,8 +37,13 @@ bool dag_longest_path(int n_nodes, const double* w, int n_edges, const int* src,
 bool dag_predict(const Tables& t, int heads, int slots, const double cost[4], DagResult& out) {
   const int n = t.n, U = t.units(), I = t.items();
   if (heads < 1 || slots < 1) return false;
+  if (U == 0) {  // nothing to run (every pair masked)
+    out = DagResult();
+    return true;
+  }
   const double c_full = cost[0], c_diag = cost[1], r = cost[2], hlat = cost[3];
-  auto ccost = [&](int i) { return (t.causal && t.kv[i] == t.q[i]) ? c_diag : c_full; };
+  // partial pairs (the causal diagonal; window or block edges) cost c_diag
+  auto ccost = [&](int i) { return t.partial[(size_t)t.q[i] * t.n + t.kv[i]] ? c_diag : c_full; };
 
   // rank predecessor of every item within one head (-1 for the first / atomic)
   std::vector<int> pos((size_t)n * n, -1), pred(I, -1);

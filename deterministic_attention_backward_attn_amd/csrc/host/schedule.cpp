@@ -13,6 +13,10 @@
 //               triangles with a cyclic offset over n/2+1 super-rows; dQ
 //               order by step.
 //   Atomic      Naive's traversal, no order.
+//
+// Masks other than full and causal (windows, block masks) keep the same
+// Naive / Descending / Atomic rules over the live pairs; Shift becomes a
+// proper edge colouring of the live-pair graph (see build_tables).
 #include "schedule.hpp"
 
 #include <algorithm>
@@ -39,7 +43,7 @@ void ranks_by_kv(Tables& t) {
   for (int q = 0; q < n; ++q) {
     int r = 0;
     for (int kv = 0; kv < n; ++kv)
-      if (!t.causal || kv <= q) t.rank[(size_t)q * n + kv] = r++;
+      if (t.live[(size_t)q * n + kv]) t.rank[(size_t)q * n + kv] = r++;
   }
 }
 
@@ -49,14 +53,178 @@ void ranks_by_step(Tables& t) {
   std::vector<std::vector<std::array<int, 3>>> per_q(n);
   for (int u = 0; u < t.units(); ++u)
     for (int i = t.unit_off[u]; i < t.unit_off[u + 1]; ++i)
-      per_q[t.q[i]].push_back({i - t.unit_off[u], u, t.kv[i]});
+      per_q[t.q[i]].push_back({t.step[i], u, t.kv[i]});
   for (int q = 0; q < n; ++q) {
     std::sort(per_q[q].begin(), per_q[q].end());
     for (size_t r = 0; r < per_q[q].size(); ++r) t.rank[(size_t)q * n + per_q[q][r][2]] = (int)r;
   }
 }
 
+// Proper edge colouring of the bipartite live-pair graph (KV tiles x Q
+// blocks) with as many colours as the largest degree (Koenig's theorem):
+// each pair takes a colour free at both ends, after swapping two colours
+// along an alternating path when the ends disagree.  One unit per KV tile
+// with live pairs, its pairs in colour order; step = colour.
+void colour_units(const TileMask& m, Tables& t) {
+  const int n = m.n;
+  int delta = 0;
+  std::vector<int> deg_q(n, 0);
+  for (int kv = 0; kv < n; ++kv) {
+    int dk = 0;
+    for (int q = 0; q < n; ++q)
+      if (m.live[(size_t)q * n + kv]) {
+        ++dk;
+        ++deg_q[q];
+      }
+    delta = std::max(delta, dk);
+  }
+  for (int q = 0; q < n; ++q) delta = std::max(delta, deg_q[q]);
+  // at_kv[kv * delta + c] = Q block of kv's pair with colour c, or -1
+  std::vector<int> at_kv((size_t)n * delta, -1), at_q((size_t)n * delta, -1);
+  auto first_free = [&](const std::vector<int>& tab, int v) {
+    for (int c = 0; c < delta; ++c)
+      if (tab[(size_t)v * delta + c] < 0) return c;
+    return -1;  // unreachable: an uncoloured pair leaves a colour free
+  };
+  struct Edge { int kv, q, c; };
+  std::vector<Edge> path;
+  for (int kv = 0; kv < n; ++kv)
+    for (int q = 0; q < n; ++q) {
+      if (!m.live[(size_t)q * n + kv]) continue;
+      const int a = first_free(at_kv, kv), b = first_free(at_q, q);
+      if (at_q[(size_t)q * delta + a] >= 0) {
+        // a is taken at q (so a != b): swap a and b on the a/b path from q;
+        // it cannot reach kv, where a is free
+        path.clear();
+        int x = q, c = a;
+        bool q_side = true;
+        for (;;) {
+          const int y = q_side ? at_q[(size_t)x * delta + c] : at_kv[(size_t)x * delta + c];
+          if (y < 0) break;
+          path.push_back(q_side ? Edge{y, x, c} : Edge{x, y, c});
+          x = y;
+          q_side = !q_side;
+          c = (c == a) ? b : a;
+        }
+        for (const Edge& e : path) {
+          at_kv[(size_t)e.kv * delta + e.c] = -1;
+          at_q[(size_t)e.q * delta + e.c] = -1;
+        }
+        for (const Edge& e : path) {
+          const int c2 = (e.c == a) ? b : a;
+          at_kv[(size_t)e.kv * delta + c2] = e.q;
+          at_q[(size_t)e.q * delta + c2] = e.kv;
+        }
+      }
+      at_kv[(size_t)kv * delta + a] = q;
+      at_q[(size_t)q * delta + a] = kv;
+    }
+  for (int kv = 0; kv < n; ++kv) {
+    bool opened = false;
+    for (int c = 0; c < delta; ++c) {
+      const int q = at_kv[(size_t)kv * delta + c];
+      if (q < 0) continue;
+      if (!opened) {
+        t.unit_off.push_back((int)t.kv.size());
+        opened = true;
+      }
+      t.kv.push_back(kv);
+      t.q.push_back(q);
+      t.step.push_back(c);
+    }
+  }
+}
+
 }  // namespace
+
+bool TileMask::any_partial() const {
+  for (uint8_t p : partial)
+    if (p) return true;
+  return false;
+}
+
+TileMask plain_mask(int n, bool causal) {
+  TileMask m;
+  m.n = n;
+  m.causal = causal;
+  m.plain = true;
+  m.live.assign((size_t)n * n, 0);
+  m.partial.assign((size_t)n * n, 0);
+  for (int q = 0; q < n; ++q)
+    for (int kv = 0; kv < n; ++kv) {
+      m.live[(size_t)q * n + kv] = (!causal || kv <= q) ? 1 : 0;
+      m.partial[(size_t)q * n + kv] = (causal && kv == q) ? 1 : 0;
+    }
+  return m;
+}
+
+void mask_bounds(bool causal, int window, int* lo, int* hi) {
+  constexpr int kUnbounded = 1 << 30;
+  *lo = causal ? 0 : -kUnbounded;
+  *hi = kUnbounded;
+  if (window > 0) {
+    *hi = window - 1;
+    if (!causal) *lo = -(window - 1);
+  }
+}
+
+TileMask make_mask(int n, int tile, bool causal, int window, const uint8_t* block, int bt) {
+  if (!block && (window <= 0 || (long long)window >= (long long)n * tile))
+    return plain_mask(n, causal);
+  int lo = 0, hi = 0;
+  mask_bounds(causal, window, &lo, &hi);
+  TileMask m;
+  m.n = n;
+  m.causal = causal;
+  m.plain = false;
+  m.live.assign((size_t)n * n, 0);
+  m.partial.assign((size_t)n * n, 0);
+  const int nb = block ? n / bt : 0;
+  for (int q = 0; q < n; ++q)
+    for (int kv = 0; kv < n; ++kv) {
+      // i - j over the pair spans [(q-kv)T - (T-1), (q-kv)T + (T-1)]
+      const long long a = (long long)(q - kv) * tile - (tile - 1);
+      const long long b = (long long)(q - kv) * tile + (tile - 1);
+      const bool any = a <= hi && b >= lo;
+      const bool all = a >= lo && b <= hi;
+      const bool blk = !block || block[(size_t)(q / bt) * nb + kv / bt] != 0;
+      m.live[(size_t)q * n + kv] = (any && blk) ? 1 : 0;
+      m.partial[(size_t)q * n + kv] = (any && blk && !all) ? 1 : 0;
+    }
+  return m;
+}
+
+bool build_tables(const TileMask& m, Sched s, Tables& t) {
+  if (m.plain) return build_tables(m.n, m.causal, s, t);
+  t = Tables();
+  const int n = m.n;
+  t.n = n;
+  t.causal = m.causal;
+  t.sched = s;
+  if (n < 1) return false;
+  t.live = m.live;
+  t.partial = m.partial;
+  t.rank.assign((size_t)n * n, -1);
+  Builder b(t);
+  if (s == Sched::Shift) {
+    colour_units(m, t);
+  } else {
+    for (int kv = 0; kv < n; ++kv) {
+      bool opened = false;
+      for (int k = 0; k < n; ++k) {
+        const int q = (s == Sched::Descending) ? n - 1 - k : k;
+        if (!m.live[(size_t)q * n + kv]) continue;
+        if (!opened) b.open();
+        opened = true;
+        b.add(kv, q);
+      }
+    }
+  }
+  b.finish();
+  if (s == Sched::Naive || s == Sched::Descending) ranks_by_kv(t);
+  else if (s == Sched::Shift) ranks_by_step(t);
+  return true;
+}
 
 bool build_tables(int n, bool causal, Sched s, Tables& t) {
   t = Tables();
@@ -64,6 +232,11 @@ bool build_tables(int n, bool causal, Sched s, Tables& t) {
   t.causal = causal;
   t.sched = s;
   if (n < 1) return false;
+  {
+    TileMask pm = plain_mask(n, causal);
+    t.live = std::move(pm.live);
+    t.partial = std::move(pm.partial);
+  }
   t.rank.assign((size_t)n * n, -1);
   Builder b(t);
   switch (s) {
@@ -108,6 +281,11 @@ bool build_tables(int n, bool causal, Sched s, Tables& t) {
   }
   // close: unit_off holds each unit's start; append the end
   b.finish();
+  if (s == Sched::Shift) {
+    t.step.assign(t.kv.size(), 0);
+    for (int u = 0; u < t.units(); ++u)
+      for (int i = t.unit_off[u]; i < t.unit_off[u + 1]; ++i) t.step[i] = i - t.unit_off[u];
+  }
   if (s == Sched::Naive || s == Sched::Descending) ranks_by_kv(t);
   else if (s == Sched::Shift) ranks_by_step(t);
   return true;
@@ -117,6 +295,8 @@ const char* validate_tables(const Tables& t) {
   const int n = t.n;
   if (n < 1 || t.unit_off.empty() || t.unit_off.front() != 0 || t.unit_off.back() != t.items())
     return "malformed unit offsets";
+  if (t.live.size() != (size_t)n * n || t.partial.size() != (size_t)n * n)
+    return "malformed liveness";
   std::vector<int> seen((size_t)n * n, 0), unit_of((size_t)n * n, -1), pos((size_t)n * n, -1);
   for (int u = 0; u < t.units(); ++u) {
     if (t.unit_off[u] > t.unit_off[u + 1]) return "malformed unit offsets";
@@ -125,7 +305,7 @@ const char* validate_tables(const Tables& t) {
     for (int i = t.unit_off[u]; i < t.unit_off[u + 1]; ++i) {
       const int kv = t.kv[i], q = t.q[i];
       if (kv < 0 || kv >= n || q < 0 || q >= n) return "tile index out of range";
-      if (t.causal && kv > q) return "masked pair scheduled";
+      if (!t.live[(size_t)q * n + kv]) return "dead pair scheduled";
       if (seen[(size_t)q * n + kv]++) return "pair scheduled twice";
       unit_of[(size_t)q * n + kv] = u;
       pos[(size_t)q * n + kv] = i;
@@ -139,7 +319,7 @@ const char* validate_tables(const Tables& t) {
   }
   for (int q = 0; q < n; ++q)
     for (int kv = 0; kv < n; ++kv)
-      if ((!t.causal || kv <= q) && seen[(size_t)q * n + kv] != 1) return "live pair missing";
+      if (t.live[(size_t)q * n + kv] && seen[(size_t)q * n + kv] != 1) return "live pair missing";
   // KV tile must live in one unit only
   for (int kv = 0; kv < n; ++kv) {
     int u0 = -1;
@@ -150,6 +330,19 @@ const char* validate_tables(const Tables& t) {
       else if (u != u0) return "KV tile spread over units";
     }
   }
+  if (!t.step.empty()) {
+    // lockstep steps: increasing within a unit, distinct within a Q block
+    if (t.step.size() != t.kv.size()) return "malformed steps";
+    for (int u = 0; u < t.units(); ++u)
+      for (int i = t.unit_off[u] + 1; i < t.unit_off[u + 1]; ++i)
+        if (t.step[i] <= t.step[i - 1]) return "steps not increasing within a unit";
+    std::vector<std::vector<int>> per_q(n);
+    for (int i = 0; i < t.items(); ++i) per_q[t.q[i]].push_back(t.step[i]);
+    for (auto& v : per_q) {
+      std::sort(v.begin(), v.end());
+      if (std::adjacent_find(v.begin(), v.end()) != v.end()) return "two units on one block at one step";
+    }
+  }
   if (!t.ordered()) return "";
   // rank rows are permutations
   std::vector<int> pred_item((size_t)t.items(), -1);
@@ -158,7 +351,7 @@ const char* validate_tables(const Tables& t) {
     int cnt = 0;
     for (int kv = 0; kv < n; ++kv) {
       const int r = t.rank[(size_t)q * n + kv];
-      const bool live = !t.causal || kv <= q;
+      const bool live = t.live[(size_t)q * n + kv] != 0;
       if (!live) {
         if (r != -1) return "rank for a masked pair";
         continue;

@@ -15,13 +15,44 @@ namespace dash {
 
 enum class Sched : int { Atomic = 0, Naive = 1, Descending = 2, Shift = 3 };
 
+// Which tile pairs exist.  A plain mask is the full square or the causal
+// triangle, where the pages' constructions apply; otherwise the pairs come
+// from a sliding window and/or a block mask (the summary lists block-sparse
+// and other special masks as needing schedule extensions).  A pair is live
+// when some (query, key) in it is visible and partial when it is live but
+// some pair in it is hidden (the kernel then masks elements).
+struct TileMask {
+  int n = 0;
+  bool causal = false;
+  bool plain = true;
+  std::vector<uint8_t> live;     // [q * n + kv]
+  std::vector<uint8_t> partial;  // [q * n + kv]
+  bool any_partial() const;
+};
+
+TileMask plain_mask(int n, bool causal);
+
+// Element rule: key j visible to query i when (not causal or j <= i), the
+// window (if > 0) holds (causal: i - j < window; else |i - j| < window) and
+// the block mask (if any; row = query block, bt tiles per block side) is
+// nonzero.  `tile` is the tile side in rows.  A window that covers the
+// whole sequence and no block mask gives the plain mask.
+TileMask make_mask(int n, int tile, bool causal, int window, const uint8_t* block, int bt);
+
+// Element bounds of the same rule as a range of i - j: lo <= i - j <= hi
+// (+-2^30 where unbounded).
+void mask_bounds(bool causal, int window, int* lo, int* hi);
+
 struct Tables {
   int n = 0;
   bool causal = false;
   Sched sched = Sched::Naive;
+  std::vector<uint8_t> live;     // [n * n] by [q * n + kv]
+  std::vector<uint8_t> partial;  // [n * n]
   std::vector<int> unit_off;  // [units + 1]
   std::vector<int> kv;        // [items]
   std::vector<int> q;         // [items]
+  std::vector<int> step;      // [items] lockstep step of each item (SHIFT), else empty
   std::vector<int> rank;      // [n * n], -1 where absent or unordered
   int units() const { return (int)unit_off.size() - 1; }
   int items() const { return (int)kv.size(); }
@@ -33,6 +64,12 @@ struct Tables {
 // Returns false when the schedule is undefined for (n, causal): symmetric
 // shift with odd n > 1.
 bool build_tables(int n, bool causal, Sched s, Tables& t);
+// Any mask.  SHIFT on a plain mask is the pages' cyclic / symmetric shift;
+// on any other it gives every live pair a step such that no unit and no Q
+// block has two pairs at one step, with as many steps as the busiest tile
+// has pairs (a bipartite edge colouring), units run in step order and dQ
+// orders are by step.
+bool build_tables(const TileMask& m, Sched s, Tables& t);
 
 // Structural checks: every live pair exactly once, each KV tile's items
 // contiguous in one unit, every rank row a permutation, and (for the

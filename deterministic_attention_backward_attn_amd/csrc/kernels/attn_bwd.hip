@@ -7,7 +7,7 @@
 // accumulation).  For every Q block in its schedule it recomputes, per Q
 // sub-tile of BR rows:
 //   S   = Q K^T                (MFMA; K held in registers)
-//   P   = exp(s S - LSE)       (exactly 0 where the causal mask hides a key)
+//   P   = exp(s S - LSE)       (exactly 0 where the mask hides a key)
 //   dP  = dO V^T               (MFMA; V held in registers)
 //   dS  = P (dP - delta)
 //   dV += P^T dO ; dK += dS^T Q  (MFMA, accumulators in registers)
@@ -95,7 +95,7 @@ __device__ __forceinline__ int swz(int r) {
   }
 }
 
-template <typename T, int D, int BC, int BR, bool CAUSAL, bool ORDERED, bool DEBUG>
+template <typename T, int D, int BC, int BR, bool MASKED, bool ORDERED, bool DEBUG>
 __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
   using E = Elt<T>;
   using frag = typename E::frag;
@@ -498,8 +498,11 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
       // P and dS; dS^T to LDS.  bf16: P and dS are packed once (hardware
       // RNE conversion) and the packed words serve both the LDS write and the
       // MFMA A operands.  fp32: P and dS stay in place (accS <- P, accP <- dS).
-      const bool diag = CAUSAL && (qblk == kv);   // uniform across the workgroup
+      // pairs flagged partial hide the elements outside lo <= i - j <= hi
+      // (the causal diagonal, window edges); uniform across the workgroup
+      const bool emask = MASKED && ((itm.y >> 29) & 1);
       const int kvl = 32 * w + l32;
+      const int mbase = (qblk - kv) * BC + rsub * BR - kvl;  // i - j = mbase + row
       T* cdSt = sdSt[b];
       uint32_t pw[MT][8], dw[MT][8];
 #pragma unroll
@@ -513,10 +516,12 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
 #pragma unroll
           for (int e = 0; e < 4; ++e)
             p[e] = __builtin_amdgcn_exp2f(accS[mt][4 * gq + e] * a.scale_log2 - l4[e]);
-          if (diag) {
+          if (emask) {
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-              if (kvl > rsub * BR + qb + e) p[e] = 0.f;
+            for (int e = 0; e < 4; ++e) {
+              const int dd = mbase + qb + e;
+              if (dd < a.mask_lo || dd > a.mask_hi) p[e] = 0.f;
+            }
           }
 #pragma unroll
           for (int e = 0; e < 4; ++e) ds[e] = p[e] * (accP[mt][4 * gq + e] - d4[e]);
@@ -673,8 +678,8 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
 // DEBUG instantiations carry the test hooks (jitter, poison, partials dump,
 // wait statistics); the production kernels have none of their code.
 template <typename T, int D, int BC, int BR, bool DEBUG>
-static void* pick2(bool causal, bool ordered) {
-  if (causal)
+static void* pick2(bool masked, bool ordered) {
+  if (masked)
     return ordered ? (void*)bwd_kernel<T, D, BC, BR, true, true, DEBUG>
                    : (void*)bwd_kernel<T, D, BC, BR, true, false, DEBUG>;
   return ordered ? (void*)bwd_kernel<T, D, BC, BR, false, true, DEBUG>
@@ -682,16 +687,16 @@ static void* pick2(bool causal, bool ordered) {
 }
 
 template <typename T, int D, int BC, int BR>
-static void* pick(bool causal, bool ordered, bool debug) {
-  return debug ? pick2<T, D, BC, BR, true>(causal, ordered)
-               : pick2<T, D, BC, BR, false>(causal, ordered);
+static void* pick(bool masked, bool ordered, bool debug) {
+  return debug ? pick2<T, D, BC, BR, true>(masked, ordered)
+               : pick2<T, D, BC, BR, false>(masked, ordered);
 }
 
-static void* select_bwd(int dtype, int d, bool causal, bool ordered, bool debug, int* threads) {
-  if (dtype == 1 && d == 128) { *threads = 256; return pick<bf16_t, 128, 128, 32>(causal, ordered, debug); }
-  if (dtype == 1 && d == 64) { *threads = 256; return pick<bf16_t, 64, 128, 64>(causal, ordered, debug); }
-  if (dtype == 0 && d == 64) { *threads = 128; return pick<float, 64, 64, 64>(causal, ordered, debug); }
-  if (dtype == 0 && d == 128) { *threads = 128; return pick<float, 128, 64, 32>(causal, ordered, debug); }
+static void* select_bwd(int dtype, int d, bool masked, bool ordered, bool debug, int* threads) {
+  if (dtype == 1 && d == 128) { *threads = 256; return pick<bf16_t, 128, 128, 32>(masked, ordered, debug); }
+  if (dtype == 1 && d == 64) { *threads = 256; return pick<bf16_t, 64, 128, 64>(masked, ordered, debug); }
+  if (dtype == 0 && d == 64) { *threads = 128; return pick<float, 64, 64, 64>(masked, ordered, debug); }
+  if (dtype == 0 && d == 128) { *threads = 128; return pick<float, 128, 64, 32>(masked, ordered, debug); }
   return nullptr;
 }
 
@@ -706,12 +711,12 @@ int bwd_waves(int dtype, int d) {
   return bc / 32;
 }
 
-hipError_t bwd_max_coresident(int dtype, int d, bool causal, bool ordered, int* blocks) {
+hipError_t bwd_max_coresident(int dtype, int d, bool masked, bool ordered, int* blocks) {
   int threads = 0;
   int per_cu = 0;
   // the test-hook instantiations must fit as many workgroups as production
   for (int dbg = 0; dbg < 2; ++dbg) {
-    void* f = select_bwd(dtype, d, causal, ordered, dbg != 0, &threads);
+    void* f = select_bwd(dtype, d, masked, ordered, dbg != 0, &threads);
     if (!f) return hipErrorInvalidValue;
     int n = 0;
     hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, threads, 0);
@@ -729,12 +734,12 @@ hipError_t bwd_max_coresident(int dtype, int d, bool causal, bool ordered, int* 
   return hipSuccess;
 }
 
-hipError_t launch_bwd(int dtype, int d, bool causal, bool ordered, const BwdArgs& a, int grid,
+hipError_t launch_bwd(int dtype, int d, bool masked, bool ordered, const BwdArgs& a, int grid,
                       hipStream_t stream) {
   int threads = 0;
   const bool debug = a.jitter_seed != 0u || a.poison_q >= 0 || a.partials != nullptr ||
                      a.wait_stats != nullptr;
-  void* f = select_bwd(dtype, d, causal, ordered, debug, &threads);
+  void* f = select_bwd(dtype, d, masked, ordered, debug, &threads);
   if (!f) return hipErrorInvalidValue;
   BwdArgs copy = a;
   void* args[] = {&copy};

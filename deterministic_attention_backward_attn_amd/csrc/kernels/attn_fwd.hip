@@ -7,13 +7,16 @@
 // two lane halves.  Keys/values stream through LDS in tiles of BN rows with
 // an online softmax; O^T = V^T P^T accumulates with the query on lanes, so
 // the per-row rescale is a per-lane scalar.  LSE is the natural log of the
-// row's sum of exp(s * score).
+// row's sum of exp(s * score).  Masked kernels visit only key tiles that
+// can hold a visible key (element bounds lo <= i - j <= hi, and the tile
+// liveness of a block mask) and hide the rest per element; a row that sees
+// no key gets O = 0 and LSE = -inf.
 #include "common.hpp"
 #include "launch.hpp"
 
 namespace dash {
 
-template <typename T, int D, int NW, int BN, bool CAUSAL>
+template <typename T, int D, int NW, int BN, bool MASKED>
 __global__ void __launch_bounds__(NW * 64, 1) fwd_kernel(FwdArgs a) {
   using E = Elt<T>;
   using frag = typename E::frag;
@@ -38,8 +41,9 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_kernel(FwdArgs a) {
   const int l32 = lane & 31;
   const int hh = lane >> 5;
   const int N = a.N;
-  const int head = blockIdx.y;
-  const int q0 = blockIdx.x * BM;
+  const int n_qb = N / BM;
+  const int head = blockIdx.x / n_qb;
+  const int q0 = (blockIdx.x - head * n_qb) * BM;
   const size_t hoff = (size_t)head * N * D;
   const T* Qg = reinterpret_cast<const T*>(a.q) + hoff;
   const T* Kg = reinterpret_cast<const T*>(a.k) + hoff;
@@ -56,9 +60,18 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_kernel(FwdArgs a) {
   float m = -INFINITY;  // running max of s*score*log2(e)
   float l = 0.f;        // running sum of exp2(. - m)
 
-  const int n_kv = CAUSAL ? (q0 + BM + BN - 1) / BN : N / BN;
-  for (int j = 0; j < n_kv; ++j) {
+  // key tiles that can hold a visible key for rows q0 .. q0 + BM - 1
+  int j_lo = 0, j_hi = N / BN;
+  if (MASKED) {
+    const int k_min = q0 - a.mask_hi;             // i - j <= hi
+    const int k_max = q0 + BM - 1 - a.mask_lo;    // i - j >= lo
+    j_lo = k_min > 0 ? k_min / BN : 0;
+    j_hi = k_max < N - 1 ? k_max / BN + 1 : N / BN;
+  }
+  for (int j = j_lo; j < j_hi; ++j) {
     const int k0 = j * BN;
+    // block mask: skip tiles of dead pairs (uniform: BM rows are one tile)
+    if (MASKED && a.live && !a.live[(size_t)(q0 / a.tile) * a.n_tiles + k0 / a.tile]) continue;
     __syncthreads();
     for (int c = tid; c < BN * D / VEC; c += NT) {
       const int row = c / (D / VEC);
@@ -89,20 +102,25 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_kernel(FwdArgs a) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
         float s2 = accS[mt][r] * a.scale_log2;
-        if (CAUSAL && k0 + mt * 32 + crow(r, hh) > qi) s2 = -INFINITY;
+        if (MASKED) {
+          const int dd = qi - (k0 + mt * 32 + crow(r, hh));
+          if (dd < a.mask_lo || dd > a.mask_hi) s2 = -INFINITY;
+        }
         accS[mt][r] = s2;
         mx = fmaxf(mx, s2);
       }
     }
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float m_new = fmaxf(m, mx);  // finite: key 0 is visible to every query
-    const float alpha = __builtin_amdgcn_exp2f(m - m_new);
+    const float m_new = fmaxf(m, mx);
+    // while a row has seen no key its max stays -inf: subtract 0 instead
+    const float m_use = m_new == -INFINITY ? 0.f : m_new;
+    const float alpha = __builtin_amdgcn_exp2f(m - m_use);
     float ps = 0.f;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt) {
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
-        const float p = __builtin_amdgcn_exp2f(accS[mt][r] - m_new);
+        const float p = __builtin_amdgcn_exp2f(accS[mt][r] - m_use);
         accS[mt][r] = p;
         ps += p;
       }
@@ -151,7 +169,7 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_kernel(FwdArgs a) {
     }
   }
 
-  const float inv_l = 1.f / l;
+  const float inv_l = l > 0.f ? 1.f / l : 0.f;
   T* Og = reinterpret_cast<T*>(a.o) + hoff;
 #pragma unroll
   for (int md = 0; md < MD; ++md) {
@@ -161,22 +179,27 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_kernel(FwdArgs a) {
       Og[(size_t)qi * D + dcol] = E::from_f32(accO[md][r] * inv_l);
     }
   }
-  if (hh == 0) a.lse[(size_t)head * N + qi] = (m + log2f(l)) * (1.0f / kLog2e);
+  if (hh == 0)
+    a.lse[(size_t)head * N + qi] = l > 0.f ? (m + log2f(l)) * (1.0f / kLog2e) : -INFINITY;
 }
 
 template <typename T, int D, int NW, int BN>
-static hipError_t go_fwd(bool causal, const FwdArgs& a, hipStream_t s) {
-  dim3 grid(a.N / (32 * NW), a.BH);
-  if (causal) hipLaunchKernelGGL((fwd_kernel<T, D, NW, BN, true>), grid, dim3(NW * 64), 0, s, a);
+static hipError_t go_fwd(bool masked, const FwdArgs& a, hipStream_t s) {
+  // one workgroup per (head, query block); the block is one tile
+  if (32 * NW != a.tile) return hipErrorInvalidValue;
+  const long blocks = (long)(a.N / (32 * NW)) * a.BH;
+  if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
+  dim3 grid((unsigned)blocks);
+  if (masked) hipLaunchKernelGGL((fwd_kernel<T, D, NW, BN, true>), grid, dim3(NW * 64), 0, s, a);
   else hipLaunchKernelGGL((fwd_kernel<T, D, NW, BN, false>), grid, dim3(NW * 64), 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_fwd(int dtype, int d, bool causal, const FwdArgs& a, hipStream_t stream) {
-  if (dtype == 1 && d == 128) return go_fwd<bf16_t, 128, 4, 64>(causal, a, stream);
-  if (dtype == 1 && d == 64) return go_fwd<bf16_t, 64, 4, 64>(causal, a, stream);
-  if (dtype == 0 && d == 64) return go_fwd<float, 64, 2, 64>(causal, a, stream);
-  if (dtype == 0 && d == 128) return go_fwd<float, 128, 2, 64>(causal, a, stream);
+hipError_t launch_fwd(int dtype, int d, bool masked, const FwdArgs& a, hipStream_t stream) {
+  if (dtype == 1 && d == 128) return go_fwd<bf16_t, 128, 4, 64>(masked, a, stream);
+  if (dtype == 1 && d == 64) return go_fwd<bf16_t, 64, 4, 64>(masked, a, stream);
+  if (dtype == 0 && d == 64) return go_fwd<float, 64, 2, 64>(masked, a, stream);
+  if (dtype == 0 && d == 128) return go_fwd<float, 128, 2, 64>(masked, a, stream);
   return hipErrorInvalidValue;
 }
 

@@ -79,6 +79,33 @@ hipError_t launch_zero_u32(uint32_t* p, size_t n_words, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// Clear whole row tiles of every head: block (t, head) zeroes the
+// contiguous span of tile tiles[t] in that head, 16 bytes per store.
+__global__ void __launch_bounds__(256) zero_tiles_kernel(uint4* __restrict__ base,
+                                                         const int* __restrict__ tiles,
+                                                         size_t tile_vec, size_t head_vec) {
+  uint4* p = base + (size_t)blockIdx.y * head_vec + (size_t)tiles[blockIdx.x] * tile_vec;
+  for (size_t i = threadIdx.x; i < tile_vec; i += blockDim.x) p[i] = make_uint4(0u, 0u, 0u, 0u);
+}
+
+hipError_t launch_zero_tiles(int dtype, void* base, const int* tiles, int count, int rows, int d,
+                             int N, int BH, hipStream_t stream) {
+  if (count <= 0 || BH <= 0) return hipSuccess;
+  const size_t esize = dtype == 1 ? 2 : 4;
+  const size_t tile_bytes = (size_t)rows * d * esize;
+  if (tile_bytes % 16) return hipErrorInvalidValue;
+  const size_t head_vec = (size_t)N * d * esize / 16;
+  for (int h0 = 0; h0 < BH; h0 += 65535) {  // grid y is at most 65535
+    const int hn = BH - h0 < 65535 ? BH - h0 : 65535;
+    hipLaunchKernelGGL(zero_tiles_kernel, dim3((unsigned)count, (unsigned)hn), dim3(256), 0, stream,
+                       reinterpret_cast<uint4*>(base) + (size_t)h0 * head_vec, tiles,
+                       tile_bytes / 16, head_vec);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  return hipSuccess;
+}
+
 // dQ = scale * dQ_accum, converted to the output dtype (RNE for bf16).
 template <typename T>
 __global__ void __launch_bounds__(256) dq_convert_kernel(const float4* __restrict__ acc,

@@ -26,9 +26,10 @@ struct BwdArgs {
   uint32_t* counters;     // [BH, N / BR, waves] order counters, zeroed
   uint32_t* header;       // [0] status word, [1] work counter; zeroed
   const int* unit_off;    // [units_per_head + 1]
-  const int2* items;      // {kv | q << 16, rank | last << 30} per item, one head's list
+  const int2* items;      // {kv | q << 16, rank | partial << 29 | last << 30} per item
   int N;
   int n_tiles;            // N / BC
+  int mask_lo, mask_hi;   // pairs flagged partial: key j visible to query i iff lo <= i - j <= hi
   int units_per_head;
   int total_units;        // units_per_head * BH
   int p_eff;              // static policy: workgroups that take units
@@ -53,23 +54,32 @@ struct FwdArgs {
   int N;
   int BH;
   float scale_log2;
+  int mask_lo, mask_hi;   // masked kernels: key j visible to query i iff lo <= i - j <= hi
+  const uint8_t* live;    // or null; else tile pair (i / tile, j / tile) must be live too
+  int n_tiles;            // N / tile
+  int tile;
 };
 
 // dtype: 0 = fp32, 1 = bf16.  Returns hipSuccess or the launch error.
-hipError_t launch_bwd(int dtype, int d, bool causal, bool ordered, const BwdArgs& a, int grid,
+// masked: some pairs carry the partial flag (elements hidden by mask_lo/hi).
+hipError_t launch_bwd(int dtype, int d, bool masked, bool ordered, const BwdArgs& a, int grid,
                       hipStream_t stream);
 // Largest grid of the backward kernel whose workgroups are all resident.
-hipError_t bwd_max_coresident(int dtype, int d, bool causal, bool ordered, int* blocks);
+hipError_t bwd_max_coresident(int dtype, int d, bool masked, bool ordered, int* blocks);
 // Tile sizes of the backward kernel: KV tile (BC) and Q sub-tile (BR).
 void bwd_tiles(int dtype, int d, int* bc, int* br);
 // Waves per workgroup of the backward kernel (one order counter each).
 int bwd_waves(int dtype, int d);
 
-hipError_t launch_fwd(int dtype, int d, bool causal, const FwdArgs& a, hipStream_t stream);
+hipError_t launch_fwd(int dtype, int d, bool masked, const FwdArgs& a, hipStream_t stream);
 
 hipError_t launch_preprocess(int dtype, int d, const void* o, const void* dout, float* delta,
                              long rows, hipStream_t stream);
 hipError_t launch_zero_u32(uint32_t* p, size_t n_words, hipStream_t stream);
+// Zero rows [t * rows, t * rows + rows) of every head of a [BH, N, d] tensor
+// for each tile t in tiles[0..count) (a device array).
+hipError_t launch_zero_tiles(int dtype, void* base, const int* tiles, int count, int rows, int d,
+                             int N, int BH, hipStream_t stream);
 hipError_t launch_dq_convert(int dtype, const float* acc, void* dq, float scale, size_t n,
                              hipStream_t stream);
 hipError_t launch_litmus(int contributors, int len, const int* turn, const float* values,

@@ -86,12 +86,30 @@ typedef enum {
                           critical path (dash_schedule_choose) */
 } dash_schedule;
 
-/* Problem descriptor.  softmax_scale <= 0 selects 1/sqrt(d). */
+/* Problem descriptor.  softmax_scale <= 0 selects 1/sqrt(d).
+ *
+ * Mask: key j is visible to query i when every given constraint holds:
+ *   causal      j <= i;
+ *   window > 0  a sliding window: i - j < window if causal, else
+ *               |i - j| < window (0 = no window);
+ *   block_mask  (host pointer, may be NULL) the entry [i / block_size]
+ *               [j / block_size] of a row-major (N / block_size)^2 byte
+ *               array is nonzero.  block_size must be a multiple of
+ *               dash_attn_tile(desc) and divide N.  Read during the call
+ *               only (the library keeps its own copy).
+ * Full and causal are the pages' masks; windows and block masks are the
+ * special masks the summary's limitations list names as needing schedule
+ * extensions.  A query row that sees no key gets O = 0, LSE = -inf and
+ * zero gradients.  With a window or block mask, N / tile must be at most
+ * 2048.  Zero-initialised trailing fields give the full or causal mask. */
 typedef struct {
   int32_t B, H, N, d;
   int32_t dtype;   /* dash_dtype */
-  int32_t causal;  /* 0 = full mask, 1 = causal */
+  int32_t causal;  /* 0 = no causal constraint, 1 = causal */
   float softmax_scale;
+  int32_t window;
+  int32_t block_size;
+  const uint8_t* block_mask;
 } dash_attn_desc;
 
 /* Human-readable name of a status code (static string, never NULL). */
@@ -269,6 +287,32 @@ dash_status dash_schedule_choose(int32_t n, int32_t causal, int32_t heads, int32
  */
 dash_status dash_attn_bwd_resolve_schedule(const dash_attn_desc* desc, dash_schedule schedule,
                                            dash_schedule* resolved);
+
+/*
+ * The backward's schedule tables for any descriptor (any mask), host only:
+ * the same tables dash_attn_bwd runs (after DASH_SCHED_AUTO resolution).
+ * Two calls: with any array NULL, fills sizes = {n tiles per side, units,
+ * items} and returns; then with arrays of those sizes (sizes unchanged):
+ * unit_offsets[units + 1], item_kv/item_q/item_step/item_partial[items]
+ * (step: lockstep step for SHIFT, else -1; partial: the pair has hidden
+ * elements) and rank[n * n] (rank[q * n + kv], -1 where absent).  SHIFT on
+ * a window or block mask is a proper colouring of the live pairs: no unit
+ * and no Q block holds two pairs at one step (the shift's defining
+ * property, explainer 2.2 B), with as many steps as the busiest tile has
+ * pairs.  Tile pairs that hold no visible key are left out; KV tiles with
+ * none get no unit.
+ */
+dash_status dash_attn_schedule_tables(const dash_attn_desc* desc, dash_schedule schedule,
+                                      int32_t sizes[3], int32_t* unit_offsets, int32_t* item_kv,
+                                      int32_t* item_q, int32_t* item_step, uint8_t* item_partial,
+                                      int32_t* rank);
+
+/*
+ * dash_schedule_predict for any descriptor: B*H heads, its mask's tables
+ * (partial pairs cost c_diag).  Host only.
+ */
+dash_status dash_attn_schedule_predict(const dash_attn_desc* desc, dash_schedule schedule,
+                                       int32_t slots, const double cost[4], double out[4]);
 
 /*
  * Longest path (critical path) of a general DAG, host only.  Node weights

@@ -33,6 +33,16 @@ Rows are processed in chunks so that P is never formed whole for long
 sequences; a chunk is a plain slice of the definition, not a reordering of
 any sum (each row's sums run over the full key range in one matmul).
 
+Masks.  ``causal`` may be a bool or a ``Mask``.  A Mask states which keys
+each query sees: causal (key j only if j <= i), a sliding window of W keys
+(causal: i - j < W; otherwise |i - j| < W) and a block mask (query block
+i // bs and key block j // bs visible only where the block entry is
+nonzero); all given constraints hold together.  The summary page
+("Limitations and future work") names block-sparse and other special
+masks as the coverage gap of full and causal; these definitions are this
+project's reading of that item.  A row that sees no key has LSE = -inf,
+P = 0 and O = 0, so its gradients are zero.
+
 Pins (tests/test_oracle_attention.py): central finite differences of
 L = <dO, O>; sum_j dS_ij = 0; sum_j dK_j = 0; causal zero patterns; the
 closed forms for Q = 0 and for constant V rows; torch float64 autograd;
@@ -42,7 +52,7 @@ from __future__ import annotations
 
 import numpy as np
 
-__all__ = ["forward", "backward", "backward_intermediates", "default_scale",
+__all__ = ["Mask", "forward", "backward", "backward_intermediates", "default_scale",
            "sampled_backward"]
 
 _ROW_CHUNK = 1024
@@ -52,14 +62,48 @@ def default_scale(d: int) -> float:
     return 1.0 / np.sqrt(d)
 
 
+class Mask:
+    """Which keys each query sees (see the module notes)."""
+
+    def __init__(self, causal: bool = False, window: int = 0, block=None,
+                 block_size: int = 0):
+        self.causal = bool(causal)
+        self.window = int(window)
+        self.block = None if block is None else np.asarray(block, dtype=bool)
+        self.block_size = int(block_size)
+        if self.window < 0:
+            raise ValueError("window must be >= 0")
+        if self.block is not None and self.block_size < 1:
+            raise ValueError("a block mask needs block_size >= 1")
+
+    def visible(self, rows, cols):
+        """Boolean [len(rows), len(cols)]: query rows[a] sees key cols[b]."""
+        i = np.asarray(rows, dtype=np.int64)[:, None]
+        j = np.asarray(cols, dtype=np.int64)[None, :]
+        vis = np.ones((i.shape[0], j.shape[1]), dtype=bool)
+        if self.causal:
+            vis &= j <= i
+        if self.window:
+            vis &= (i - j < self.window) if self.causal else (np.abs(i - j) < self.window)
+        if self.block is not None:
+            vis &= self.block[i // self.block_size, j // self.block_size]
+        return vis
+
+    def is_plain(self):
+        return self.window == 0 and self.block is None
+
+
+def _mask_of(causal) -> Mask:
+    return causal if isinstance(causal, Mask) else Mask(causal=bool(causal))
+
+
 def _scores(q_rows, k, scale, row0, causal):
     """Step 1 for a block of query rows starting at global row ``row0``."""
     s = scale * (q_rows @ k.T)
-    if causal:
-        n_rows, n_keys = s.shape
-        qi = np.arange(row0, row0 + n_rows)[:, None]
-        kj = np.arange(n_keys)[None, :]
-        s = np.where(kj <= qi, s, -np.inf)
+    mask = _mask_of(causal)
+    if mask.causal or not mask.is_plain():
+        vis = mask.visible(np.arange(row0, row0 + s.shape[0]), np.arange(s.shape[1]))
+        s = np.where(vis, s, -np.inf)
     return s
 
 
@@ -120,7 +164,7 @@ def _as64(x):
     return np.ascontiguousarray(x, dtype=np.float64)
 
 
-def forward(q, k, v, causal: bool, scale: float | None = None):
+def forward(q, k, v, causal, scale: float | None = None):
     """O [B,H,N,d] and LSE [B,H,N] (natural log of the scaled scores), fp64."""
     q, k, v = _as64(q), _as64(k), _as64(v)
     B, H, N, d = q.shape
@@ -134,7 +178,7 @@ def forward(q, k, v, causal: bool, scale: float | None = None):
     return o, lse
 
 
-def backward(q, k, v, do, causal: bool, scale: float | None = None, o=None, lse=None):
+def backward(q, k, v, do, causal, scale: float | None = None, o=None, lse=None):
     """dQ, dK, dV [B,H,N,d] in fp64.
 
     ``o`` and ``lse`` default to this module's own forward; callers that
@@ -157,7 +201,7 @@ def backward(q, k, v, do, causal: bool, scale: float | None = None, o=None, lse=
     return dq, dk, dv
 
 
-def head_forward_backward(q, k, v, do, causal: bool, scale: float):
+def head_forward_backward(q, k, v, do, causal, scale: float):
     """One (b, h) head end to end: returns (o, lse, dq, dk, dv).  Used by the
     CPU-baseline timing, which runs heads in a process pool."""
     q, k, v, do = _as64(q), _as64(k), _as64(v), _as64(do)
@@ -166,7 +210,7 @@ def head_forward_backward(q, k, v, do, causal: bool, scale: float):
     return o, lse, dq, dk, dv
 
 
-def backward_intermediates(q, k, v, do, causal: bool, scale: float | None = None):
+def backward_intermediates(q, k, v, do, causal, scale: float | None = None):
     """Single head [N,d] inputs: returns dict with S, P, LSE, O, D, dP, dS, dQ,
     dK, dV formed whole (small N only; used by the pins)."""
     q, k, v, do = _as64(q), _as64(k), _as64(v), _as64(do)
@@ -186,7 +230,7 @@ def backward_intermediates(q, k, v, do, causal: bool, scale: float | None = None
     }
 
 
-def sampled_backward(q, k, v, do, causal: bool, scale: float, rows_q, rows_kv):
+def sampled_backward(q, k, v, do, causal, scale: float, rows_q, rows_kv):
     """One head ([N, d] inputs): the forward statistics for every row, then
     only the requested rows of the gradients, each from the same steps 1-9
     applied to one row of P (dQ_i) or one column of P (dK_j, dV_j).  Cost is
@@ -209,8 +253,7 @@ def sampled_backward(q, k, v, do, causal: bool, scale: float, rows_q, rows_kv):
     dv = np.empty((len(rows_kv), v.shape[1]))
     for t, j in enumerate(rows_kv):
         s_j = scale * (q @ k[j])                             # column j of S
-        if causal:
-            s_j = np.where(np.arange(n) >= j, s_j, -np.inf)
+        s_j = np.where(_mask_of(causal).visible(np.arange(n), [int(j)])[:, 0], s_j, -np.inf)
         finite = np.isfinite(lse)
         with np.errstate(under="ignore"):
             p_j = np.where(finite, np.exp(s_j - np.where(finite, lse, 0.0)), 0.0)

@@ -82,17 +82,38 @@ def _policy(schedule):
     return "static" if schedule == S.SHIFT else "dynamic"
 
 
-def realize(schedule, n, causal, heads, slots, cost):
+def _item_costs(causal, cost, partial):
+    """Compute weight of an item: c_diag on a partial item (explicit set of
+    (kv, q) pairs for masked tables; the causal diagonal otherwise)."""
+    if partial is None:
+        return lambda kv, q: item_cost(kv, q, causal, cost)
+    return lambda kv, q: cost[1] if (kv, q) in partial else cost[0]
+
+
+def realize(schedule, n, causal, heads, slots, cost, tables=None):
     """Assign units to slots and build the graph.
+
+    ``tables`` (optional) gives one head's tables explicitly, for masks the
+    oracle does not construct itself: {"units": [[(kv, q), ...], ...],
+    "rank": rank[q][kv] (None or negative where absent; None for ATOMIC),
+    "partial": set of (kv, q) pairs costed c_diag}.
 
     Returns dict with 'weights', 'edges', 'assign' (unit -> slot),
     'units' (global unit list of item lists, each item (head, kv, q)) and
     for the dynamic policy the times of the event simulation used to decide
     the assignment ('sim_finish').
     """
-    per_head = S.units(schedule, n, causal)
+    if tables is None:
+        per_head = S.units(schedule, n, causal)
+        ranks = S.rank_table(schedule, n, causal)
+        icost = _item_costs(causal, cost, None)
+    else:
+        per_head = tables["units"]
+        ranks = tables["rank"]
+        if ranks is not None:
+            ranks = [[None if (r is None or r < 0) else int(r) for r in row] for row in ranks]
+        icost = _item_costs(causal, cost, tables["partial"])
     U = len(per_head)
-    ranks = S.rank_table(schedule, n, causal)
     glob = []
     for hd in range(heads):
         for items in per_head:
@@ -103,7 +124,7 @@ def realize(schedule, n, causal, heads, slots, cost):
     for u, items in enumerate(glob):
         for k, (hd, kv, q) in enumerate(items):
             idx_of[(u, k)] = len(weights) // 2
-            weights.append(item_cost(kv, q, causal, cost))
+            weights.append(icost(kv, q))
             weights.append(cost[2])
     r_node = {}
     for u, items in enumerate(glob):
@@ -123,7 +144,7 @@ def realize(schedule, n, causal, heads, slots, cost):
     if policy == "static":
         if U > slots:
             raise ValueError("static policy needs a whole head of units resident")
-        p_eff = (slots // U) * U
+        p_eff = (slots // U) * U if U else 1
         for u in range(len(glob)):
             assign[u] = u % p_eff
     else:
@@ -136,7 +157,7 @@ def realize(schedule, n, causal, heads, slots, cost):
             assign[u] = s
             t = free[s]
             for k, (hd, kv, q) in enumerate(items):
-                c = item_cost(kv, q, causal, cost)
+                c = icost(kv, q)
                 t_c = t + c
                 t_r = t_c
                 if ranks is not None and ranks[q][kv] > 0:
@@ -161,16 +182,18 @@ def realize(schedule, n, causal, heads, slots, cost):
         if items:
             last_on_slot[s] = 2 * idx_of[(u, len(items) - 1)] + 1
     return {"weights": weights, "edges": edges, "assign": assign, "units": glob,
-            "sim_finish": sim_finish, "policy": policy, "n_order": len(order_edges)}
+            "sim_finish": sim_finish, "policy": policy, "n_order": len(order_edges),
+            "icost": icost}
 
 
-def predict(schedule, n, causal, heads, slots, cost):
+def predict(schedule, n, causal, heads, slots, cost, tables=None):
     """Returns (makespan, total_wait, max_slot_idle, lower_bound).
 
     total_wait: summed time R nodes spend held by their order edge beyond
     what their own chain allows; max_slot_idle: largest (makespan - busy)
     over slots; lower_bound: max(total work / slots, longest single unit)."""
-    g = realize(schedule, n, causal, heads, slots, cost)
+    g = realize(schedule, n, causal, heads, slots, cost, tables)
+    icost = g["icost"]
     start, finish = longest_path(g["weights"], g["edges"])
     makespan = max(finish) if finish else 0.0
     # time each R node could start from its own chain alone (order edges
@@ -185,9 +208,9 @@ def predict(schedule, n, causal, heads, slots, cost):
     busy = [0.0] * slots
     for u, items in enumerate(g["units"]):
         for hd, kv, q in items:
-            busy[g["assign"][u]] += item_cost(kv, q, causal, cost) + cost[2]
+            busy[g["assign"][u]] += icost(kv, q) + cost[2]
     max_idle = max(makespan - b for b in busy) if slots else 0.0
-    longest_unit = max((sum(item_cost(kv, q, causal, cost) + cost[2] for _, kv, q in items)
+    longest_unit = max((sum(icost(kv, q) + cost[2] for _, kv, q in items)
                         for items in g["units"]), default=0.0)
     lower = max(sum(busy) / slots, longest_unit)
     return makespan, total_wait, max_idle, lower

@@ -139,3 +139,97 @@ def rank_table(schedule: str, n: int, causal: bool):
 
 def contributors(n: int, causal: bool, q: int) -> int:
     return sum(1 for kv in range(n) if live(kv, q, causal))
+
+
+# ------------------------------------------------------------ masked tiles
+#
+# Windows and block masks (the summary's limitations list names special
+# masks such as block-sparse ones as needing schedule extensions).  Readings:
+# a tile pair (kv, q) is live when at least one of its (query, key) pairs is
+# visible, and partial when it is live but some pair is hidden (the kernel
+# then masks elements).  NAIVE / DESCENDING / ATOMIC visit each KV tile's
+# live Q blocks ascending / descending, dQ order ascending kv.  SHIFT for a
+# general tile graph keeps the pages' defining property - at every step the
+# units touch distinct Q blocks - by giving each live pair a step (colour)
+# such that no unit and no Q block has two pairs at one step, with as many
+# steps as the busiest tile has pairs; a unit runs its pairs in step order
+# and a block's dQ order is by step.  Such colourings are not unique, so the
+# oracle checks a product table against these rules (``check_step_schedule``)
+# instead of building its own.
+
+
+def tile_liveness(mask, n_tiles: int, tile: int):
+    """(live, partial): n_tiles x n_tiles lists of bools indexed [q][kv],
+    from the element mask (``oracle.attention.Mask``) by brute force."""
+    import numpy as np
+    n = n_tiles * tile
+    vis = mask.visible(np.arange(n), np.arange(n)).reshape(n_tiles, tile, n_tiles, tile)
+    any_vis = vis.any(axis=(1, 3))
+    all_vis = vis.all(axis=(1, 3))
+    live_t = [[bool(any_vis[q, kv]) for kv in range(n_tiles)] for q in range(n_tiles)]
+    part_t = [[bool(any_vis[q, kv] and not all_vis[q, kv]) for kv in range(n_tiles)]
+              for q in range(n_tiles)]
+    return live_t, part_t
+
+
+def masked_units(schedule: str, live_t):
+    """Per-KV-tile item lists for NAIVE, DESCENDING and ATOMIC."""
+    n = len(live_t)
+    if schedule in (NAIVE, ATOMIC):
+        return [[(kv, q) for q in range(n) if live_t[q][kv]] for kv in range(n)]
+    if schedule == DESCENDING:
+        return [[(kv, q) for q in reversed(range(n)) if live_t[q][kv]] for kv in range(n)]
+    raise ValueError(f"no fixed masked construction for {schedule!r}")
+
+
+def masked_rank_table(live_t):
+    """NAIVE / DESCENDING dQ order: ascending kv among the block's live tiles."""
+    n = len(live_t)
+    rank = [[None] * n for _ in range(n)]
+    for q in range(n):
+        r = 0
+        for kv in range(n):
+            if live_t[q][kv]:
+                rank[q][kv] = r
+                r += 1
+    return rank
+
+
+def check_step_schedule(live_t, unit_items, steps, rank):
+    """Validate a SHIFT table for a general tile graph.  unit_items: per unit
+    [(kv, q), ...] in run order; steps: per unit the step of each item;
+    rank[q][kv].  Returns '' or the first rule broken."""
+    n = len(live_t)
+    deg_kv = [sum(1 for q in range(n) if live_t[q][kv]) for kv in range(n)]
+    deg_q = [sum(1 for kv in range(n) if live_t[q][kv]) for q in range(n)]
+    delta = max(deg_kv + deg_q + [0])
+    seen = {}
+    owner = {}
+    for u, (items, st) in enumerate(zip(unit_items, steps)):
+        if len(items) != len(st):
+            return "steps do not match items"
+        if any(b <= a for a, b in zip(st, st[1:])):
+            return "steps not increasing within a unit"
+        for (kv, q), s in zip(items, st):
+            if not (0 <= kv < n and 0 <= q < n) or not live_t[q][kv]:
+                return "dead or out-of-range pair"
+            if (kv, q) in seen:
+                return "pair twice"
+            if not 0 <= s < delta:
+                return "step out of range"
+            if owner.setdefault(kv, u) != u:
+                return "KV tile in two units"
+            seen[(kv, q)] = s
+    if len(seen) != sum(deg_q):
+        return "live pair missing"
+    for q in range(n):
+        contrib = sorted((seen[(kv, q)], kv) for kv in range(n) if live_t[q][kv])
+        if len({s for s, _ in contrib}) != len(contrib):
+            return "two units on one block at one step"
+        for r, (_, kv) in enumerate(contrib):
+            if rank[q][kv] != r:
+                return "dQ order is not by step"
+        for kv in range(n):
+            if not live_t[q][kv] and rank[q][kv] is not None:
+                return "rank for a dead pair"
+    return ""

@@ -28,10 +28,11 @@ def device_inputs(B, H, N, d, dtype, seed):
     return dev, exact
 
 
-def rel_err(gpu, ref):
+def rel_err(gpu, ref, floor=0.0):
+    """max|gpu - ref| / max|ref| (the denominator at least `floor`)."""
     g = gpu.detach().float().cpu().numpy().astype(np.float64)
     ref = np.asarray(ref, dtype=np.float64)
-    return float(np.max(np.abs(g - ref)) / max(np.max(np.abs(ref)), 1e-30))
+    return float(np.max(np.abs(g - ref)) / max(np.max(np.abs(ref)), floor, 1e-30))
 
 
 def log(msg):

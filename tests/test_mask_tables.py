@@ -1,0 +1,186 @@
+"""Masked schedule tables and DAG prediction (CPU only, host calls).
+
+The library's tables for sliding windows and block masks are checked
+against the oracle: tile liveness and partial flags from the element mask
+by brute force; NAIVE / DESCENDING / ATOMIC item lists and dQ orders
+exactly; SHIFT (a colouring, not unique) against the rules it must obey;
+the DAG prediction on the library's own tables against the oracle's DAG.
+"""
+import numpy as np
+import pytest
+
+import deterministic_attention_backward_attn_amd as D
+from oracle import attention as A
+from oracle import dag as OD
+from oracle import schedules as OS
+
+T = 64  # fp32 tile
+rng = np.random.default_rng(23)
+BLOCKS = {
+    "rand8": rng.random((8, 8)) < 0.55,
+    "rand4": rng.random((4, 4)) < 0.7,
+}
+DEAD = np.ones((8, 8), dtype=bool)
+DEAD[3, :] = False   # a query block that sees nothing
+DEAD[:, 5] = False   # a key block no query sees
+BLOCKS["dead"] = DEAD
+
+# (N, causal, window, block name, block_size)
+CASES = [
+    (512, True, 100, None, 0),
+    (512, True, 64, None, 0),
+    (512, True, 1, None, 0),
+    (512, False, 130, None, 0),
+    (512, False, 0, "rand8", 64),
+    (512, True, 0, "rand8", 64),
+    (512, False, 0, "rand4", 128),
+    (512, True, 200, "rand4", 128),
+    (512, False, 0, "dead", 64),
+    (512, True, 0, "dead", 64),
+    (1024, True, 300, None, 0),
+]
+
+
+def _ids(c):
+    return f"N{c[0]}_{'c' if c[1] else 'f'}_w{c[2]}_{c[3]}"
+
+
+def _oracle_mask(N, causal, window, block, bs):
+    return A.Mask(causal=causal, window=window,
+                  block=None if block is None else BLOCKS[block], block_size=bs)
+
+
+def _kw(window, block, bs):
+    return dict(window=window, block_mask=None if block is None else BLOCKS[block].astype(np.uint8),
+                block_size=bs)
+
+
+@pytest.mark.parametrize("case", CASES, ids=_ids)
+@pytest.mark.parametrize("schedule", ["naive", "descending", "atomic", "shift"])
+def test_masked_tables_against_oracle(case, schedule):
+    N, causal, window, block, bs = case
+    n = N // T
+    live, part = OS.tile_liveness(_oracle_mask(N, causal, window, block, bs), n, T)
+    t = D.mask_schedule_tables(1, 1, N, 64, "f32", causal, schedule, **_kw(window, block, bs))
+    assert t["n"] == n
+    # partial flags
+    for items, flags in zip(t["units"], t["partial"]):
+        for (kv, q), f in zip(items, flags):
+            assert f == part[q][kv], (kv, q)
+    plain = window == 0 and block is None
+    if schedule == "shift":
+        assert OS.check_step_schedule(live, t["units"], t["steps"],
+                                      [[None if r < 0 else int(r) for r in row]
+                                       for row in t["rank"]]) == ""
+        return
+    want_units = [u for u in OS.masked_units(schedule, live) if u]
+    assert t["units"] == want_units
+    if schedule == "atomic":
+        assert np.all(t["rank"] == -1)
+    else:
+        want = OS.masked_rank_table(live)
+        assert np.array_equal(t["rank"], np.array([[-1 if x is None else x for x in row]
+                                                   for row in want]))
+    assert not plain
+
+
+@pytest.mark.parametrize("causal", [False, True])
+@pytest.mark.parametrize("schedule", ["naive", "descending", "shift"])
+def test_covering_window_gives_the_plain_tables(causal, schedule):
+    N = 512
+    units, rank = D.schedule_tables(N // T, causal, schedule)
+    for w in (0, N, 4 * N):
+        t = D.mask_schedule_tables(1, 1, N, 64, "f32", causal, schedule, window=w)
+        assert t["units"] == units and np.array_equal(t["rank"], rank)
+        if schedule == "shift":
+            assert all(s == list(range(len(s))) for s in t["steps"])
+
+
+def test_causal_band_shift_runs_each_tile_in_query_order():
+    """A causal window of whole tiles: the colouring puts every KV tile's
+    pairs at consecutive steps in ascending Q order and gives each Q block
+    its contributors nearest-first, so in lockstep every hand-off is one
+    step (no stall)."""
+    N, w = 1024, 3 * T
+    t = D.mask_schedule_tables(1, 1, N, 64, "f32", True, "shift", window=w)
+    for items, steps in zip(t["units"], t["steps"]):
+        qs = [q for _, q in items]
+        assert qs == sorted(qs)
+    live, _ = OS.tile_liveness(A.Mask(causal=True, window=w), N // T, T)
+    assert OS.check_step_schedule(live, t["units"], t["steps"],
+                                  [[None if r < 0 else int(r) for r in row]
+                                   for row in t["rank"]]) == ""
+
+
+def test_step_checker_catches_broken_tables():
+    """The oracle's checker (CPU) rejects tables with planted mistakes."""
+    n = 8
+    live, _ = OS.tile_liveness(A.Mask(causal=True, window=3 * T), n, T)
+    t = D.mask_schedule_tables(1, 1, n * T, 64, "f32", True, "shift", window=3 * T)
+    rank = [[None if r < 0 else int(r) for r in row] for row in t["rank"]]
+    assert OS.check_step_schedule(live, t["units"], t["steps"], rank) == ""
+    bad_steps = [list(s) for s in t["steps"]]
+    bad_steps[1][0] = bad_steps[0][0] if t["units"][1][0][1] == t["units"][0][0][1] else -1
+    assert OS.check_step_schedule(live, t["units"], bad_steps, rank) != ""
+    bad_rank = [list(r) for r in rank]
+    q = t["units"][2][0][1]
+    kvs = [kv for kv in range(n) if bad_rank[q][kv] is not None]
+    bad_rank[q][kvs[0]], bad_rank[q][kvs[-1]] = bad_rank[q][kvs[-1]], bad_rank[q][kvs[0]]
+    assert OS.check_step_schedule(live, t["units"], t["steps"], bad_rank) != ""
+    assert OS.check_step_schedule(live, t["units"][:-1], t["steps"][:-1], rank) != ""
+
+
+def test_oracle_tile_liveness_closed_forms():
+    n = 6
+    live, part = OS.tile_liveness(A.Mask(causal=True), n, T)
+    for q in range(n):
+        for kv in range(n):
+            assert live[q][kv] == OS.live(kv, q, True)
+            assert part[q][kv] == (kv == q)
+    live, part = OS.tile_liveness(A.Mask(), n, T)
+    assert all(all(r) for r in live) and not any(any(r) for r in part)
+    # a causal window of exactly one tile: the diagonal and the tile below
+    # it are live, both partial
+    live, part = OS.tile_liveness(A.Mask(causal=True, window=T), n, T)
+    for q in range(n):
+        for kv in range(n):
+            assert live[q][kv] == (q - kv in (0, 1))
+            assert part[q][kv] == live[q][kv]
+
+
+@pytest.mark.parametrize("case", CASES[:8], ids=_ids)
+@pytest.mark.parametrize("schedule", ["naive", "descending", "shift", "atomic"])
+def test_masked_predict_matches_oracle_dag(case, schedule):
+    N, causal, window, block, bs = case
+    n = N // T
+    kw = _kw(window, block, bs)
+    t = D.mask_schedule_tables(1, 1, N, 64, "f32", causal, schedule, **kw)
+    tables = {"units": t["units"],
+              "rank": None if schedule == "atomic" else t["rank"].tolist(),
+              "partial": {it for items, fl in zip(t["units"], t["partial"])
+                          for it, f in zip(items, fl) if f}}
+    cost = (1.0, 0.6, 0.2, 0.1)
+    heads = 3
+    slots = max(len(t["units"]), 5) if schedule == "shift" else 5
+    got = D.mask_schedule_predict(1, heads, N, 64, "f32", causal, schedule, slots=slots, cost=cost,
+                                  **kw)
+    want = OD.predict(schedule, n, causal, heads, slots, cost, tables)
+    for g, w in zip(got, want):
+        assert abs(g - w) <= 1e-9 * max(1.0, abs(w)), (got, want)
+
+
+def test_mask_argument_errors():
+    with pytest.raises(D.DashError) as e:   # block size not a multiple of the tile
+        D.mask_schedule_tables(1, 1, 512, 64, "f32", False, "naive",
+                               block_mask=np.ones((16, 16)), block_size=32)
+    assert e.value.code == 2
+    with pytest.raises(D.DashError) as e:   # block size does not divide N
+        D.mask_schedule_tables(1, 1, 512, 64, "f32", False, "naive",
+                               block_mask=np.ones((2, 2)), block_size=192)
+    assert e.value.code == 2
+    with pytest.raises(D.DashError) as e:   # negative window
+        D.mask_schedule_tables(1, 1, 512, 64, "f32", False, "naive", window=-1)
+    assert e.value.code == 1
+    with pytest.raises(D.DashError) as e:   # too many tiles with a special mask
+        D.mask_schedule_tables(1, 1, 64 * 4096, 64, "f32", True, "naive", window=100)
+    assert e.value.code == 2
