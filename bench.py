@@ -10,7 +10,9 @@ timing.  Default workload: B=1, H=32, N=16384, d=128, bf16, causal mask.
 Every schedule (atomic, naive, descending, shift, and auto, the library's
 own pick from its DAG model) is timed the same way; `value` is the backward
 TFLOP/s of auto (or of --primary), FLOPs counted as 2.5x the forward's
-4*B*H*N^2*d, halved for a causal mask.  Also reported:
+4*B*H*N^2*d, halved for a causal mask (with a window or block mask:
+2.5x 4*B*H*d times the exact number of visible query-key pairs; the
+workloads ..._swa4k and ..._blocksparse).  Also reported:
 % of the dense bf16 MFMA peak, the deterministic / atomic throughput ratio
 per schedule, the backward kernel's own roofline figures (HIP events around
 its launch), the share of cycles the ordered schedules spend waiting for
@@ -83,11 +85,17 @@ def cpu_baseline(exact, w, causal, max_workers):
     import numpy as np
     cores = max(1, min(len(os.sched_getaffinity(0)), max_workers, w.B * w.H))
     scale = 1.0 / np.sqrt(w.d)
+    mask = causal
+    if w.window or w.block_spec:
+        from oracle import attention as A
+        mk = w.mask_args()
+        mask = A.Mask(causal=causal, window=mk["window"], block=mk["block_mask"],
+                      block_size=mk["block_size"])
     jobs = []
     for i in range(cores):
         b, h = divmod(i, w.H)
         jobs.append((exact["q"][b, h], exact["k"][b, h], exact["v"][b, h], exact["do"][b, h],
-                     causal, scale))
+                     mask, scale))
     with ProcessPoolExecutor(max_workers=cores, mp_context=mp.get_context("spawn")) as ex:
         times = list(ex.map(_oracle_head, jobs))
     per_head = w.flops_bwd(causal) / (w.B * w.H)
@@ -100,14 +108,14 @@ def cpu_baseline(exact, w, causal, max_workers):
 
 # ------------------------------------------------------- ordering waits
 
-def order_wait(D, dev, lse, delta, sched, causal, ws, out):
+def order_wait(D, dev, lse, delta, sched, causal, ws, out, mkw):
     """One extra, untimed launch of the instrumented kernel (wait statistics
     on): the share of the waves' cycles spent waiting for ordered-add turns,
     and the share of ordered adds whose turn had not come at the first poll."""
     import torch
     st = torch.zeros(4 * 4096 * 4, dtype=torch.int64, device="cuda")
     D.attn_bwd(dev["q"], dev["k"], dev["v"], dev["do"], lse, delta, schedule=sched,
-               causal=causal, workspace=ws, out=out, debug={"wait_stats": st})
+               causal=causal, workspace=ws, out=out, debug={"wait_stats": st}, **mkw)
     torch.cuda.synchronize()
     D.attn_bwd_status(ws)
     a = st.view(-1, 4).cpu().numpy()
@@ -180,7 +188,8 @@ def main():
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-    o, lse = D.attn_fwd(dev["q"], dev["k"], dev["v"], causal=causal)
+    mkw = w.mask_args()
+    o, lse = D.attn_fwd(dev["q"], dev["k"], dev["v"], causal=causal, **mkw)
     delta = torch.empty_like(lse)
     dq, dk, dv = (torch.empty_like(dev["q"]) for _ in range(3))
     ws = D.alloc_workspace(dev["q"], causal, "naive")
@@ -190,7 +199,7 @@ def main():
         D.attn_bwd_preprocess(o, dev["do"], out=delta)
         D.attn_bwd(dev["q"], dev["k"], dev["v"], dev["do"], lse, delta, schedule=sched,
                    causal=causal, workspace=ws, out=(dq, dk, dv),
-                   debug=None if events is None else {"kernel_events": events})
+                   debug=None if events is None else {"kernel_events": events}, **mkw)
 
     results = {}
     for sched in scheds:
@@ -216,7 +225,8 @@ def main():
         results[sched] = {"ms_per_step": ms, "tflops": flops / ms / 1e9,
                           "kernel_ms": kms, "kernel_tflops": flops / kms / 1e9}
         if sched not in ("atomic", "auto") and not args.no_wait_stats:
-            results[sched].update(order_wait(D, dev, lse, delta, sched, causal, ws, (dq, dk, dv)))
+            results[sched].update(order_wait(D, dev, lse, delta, sched, causal, ws, (dq, dk, dv),
+                                             mkw))
         print(f"[bench] {sched:10s} step {ms:8.3f} ms  {flops / ms / 1e9:7.1f} TFLOP/s   "
               f"kernel {kms:8.3f} ms  {flops / kms / 1e9:7.1f} TFLOP/s", file=sys.stderr,
               flush=True)
@@ -226,7 +236,7 @@ def main():
                                   key=lambda s: results[s]["ms_per_step"])
     prim = results[primary]
     # the schedule the launches ran (auto resolves to an ordered one)
-    ran = D.resolve_schedule(w.B, w.H, w.N, w.d, w.dtype, causal, primary)
+    ran = D.resolve_schedule(w.B, w.H, w.N, w.d, w.dtype, causal, primary, **mkw)
     out = {
         "metric": METRIC,
         "value": round(prim["tflops"], 2),
@@ -240,7 +250,9 @@ def main():
         "vs_baseline": None,
         "dtype": w.dtype,
         "data": "synthetic: i.i.d. N(0,1) Q/K/V/dO from PCG64 seeds, O/LSE from the library's forward",
-        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d, "mask": mask,
+        "config": {"workload": w.name, "B": w.B, "H": w.H, "N": w.N, "d": w.d,
+                   "mask": mask + (f" window {w.window}" if w.window else "")
+                   + (" block " + json.dumps(w.block_spec) if w.block_spec else ""),
                    "schedule": primary if ran == primary else f"{primary} ({ran})",
                    "parallelism": "single GPU"},
         "pct_peak": round(100.0 * prim["tflops"] / peak, 2),

@@ -47,9 +47,68 @@ class Workload:
         return self.B * self.H * self.N * self.d
 
     def flops_bwd(self, causal: bool) -> float:
-        """Backward FLOP convention: 2.5x the forward's 4*B*H*N^2*d, halved when causal."""
+        """Backward FLOP convention: 2.5x the forward's 4*B*H*N^2*d, halved
+        when causal.  With a window or block mask: 2.5x 4*B*H*d times the
+        exact number of visible (query, key) pairs."""
+        if self.window or self.block_spec:
+            return 2.5 * 4.0 * self.B * self.H * self.d * self.visible_pairs(causal)
         f = 2.5 * 4.0 * self.B * self.H * self.N * self.N * self.d
         return f / 2.0 if causal else f
+
+    @property
+    def window(self) -> int:
+        return int(self.extra.get("window", 0))
+
+    @property
+    def block_spec(self):
+        return self.extra.get("block")
+
+    def block_mask(self):
+        """The seeded block mask (bool [N/bs, N/bs]) or None.
+
+        "local_global": each query block sees the key blocks within
+        `band` blocks of it, the first `globals` key blocks, and a random
+        `density` share of the others (seed = seed_base + 9)."""
+        spec = self.block_spec
+        if spec is None:
+            return None
+        nb = self.N // spec["size"]
+        qb = np.arange(nb)[:, None]
+        kb = np.arange(nb)[None, :]
+        rng = np.random.Generator(np.random.PCG64(self.seed_base + 9))
+        m = (np.abs(qb - kb) <= spec["band"]) | (kb < spec["globals"])
+        m |= rng.random((nb, nb)) < spec["density"]
+        return m
+
+    def mask_args(self) -> dict:
+        """Keyword arguments of the library's mask (window, block mask)."""
+        bm = self.block_mask()
+        return {"window": self.window, "block_mask": bm,
+                "block_size": 0 if bm is None else self.block_spec["size"]}
+
+    def visible_pairs(self, causal: bool) -> int:
+        """Exact count of visible (query, key) pairs under the mask, counted
+        per tile pair: a pair of tiles at offset D = q - kv holds T - |e|
+        element pairs with i - j = D*T + e for each e in (-T, T)."""
+        T = self.tile
+        n = self.N // T
+        lo = 0 if causal else -(1 << 40)
+        hi = (self.window - 1) if self.window else (1 << 40)
+        if self.window and not causal:
+            lo = -(self.window - 1)
+        e = np.arange(-(T - 1), T)
+        mult = T - np.abs(e)
+        offs = np.arange(-(n - 1), n)
+        diff = offs[:, None] * T + e[None, :]
+        per_off = ((diff >= lo) & (diff <= hi)).astype(np.int64) @ mult   # by offset D
+        q = np.arange(n)[:, None]
+        kv = np.arange(n)[None, :]
+        cnt = per_off[(q - kv) + (n - 1)]
+        bm = self.block_mask()
+        if bm is not None:
+            bt = self.block_spec["size"] // T
+            cnt = cnt * bm[q // bt, kv // bt]
+        return int(cnt.sum())
 
 
 # The five workloads: a tiny fp32 case the oracle finishes in seconds, and four
@@ -66,6 +125,14 @@ WORKLOADS = {
                                        ("causal",), 4000),
     "b8h64_n8k_d64": Workload("b8h64_n8k_d64", 8, 64, 8192, 64, "bf16",
                               ("causal", "full"), 5000),
+    # special masks (measurement of the window / block-mask extension): a
+    # causal sliding window of 4096 keys, and a causal local + global +
+    # random block mask over 128-row blocks
+    "b1h32_n16k_d128_swa4k": Workload("b1h32_n16k_d128_swa4k", 1, 32, 16384, 128, "bf16",
+                                      ("causal",), 6000, extra={"window": 4096}),
+    "b1h32_n16k_d128_blocksparse": Workload(
+        "b1h32_n16k_d128_blocksparse", 1, 32, 16384, 128, "bf16", ("causal",), 7000,
+        extra={"block": {"size": 128, "band": 4, "globals": 2, "density": 0.1}}),
 }
 
 

@@ -184,3 +184,21 @@ def test_mask_argument_errors():
     with pytest.raises(D.DashError) as e:   # too many tiles with a special mask
         D.mask_schedule_tables(1, 1, 64 * 4096, 64, "f32", True, "naive", window=100)
     assert e.value.code == 2
+
+
+def test_workload_visible_pairs_match_the_oracle_mask():
+    """The bench's FLOP count for masked workloads (exact visible pairs,
+    counted per tile pair) equals a brute-force count of the oracle's mask."""
+    from dataclasses import replace
+    from synth import WORKLOADS
+    base = WORKLOADS["b1h32_n16k_d128_swa4k"]
+    for extra, causal in [({"window": 300}, True), ({"window": 200}, False),
+                          ({"block": {"size": 128, "band": 1, "globals": 1, "density": 0.2}}, True),
+                          ({"block": {"size": 256, "band": 0, "globals": 1, "density": 0.3}}, False),
+                          ({"window": 150, "block": {"size": 128, "band": 2, "globals": 0,
+                                                     "density": 0.1}}, True)]:
+        w = replace(base, N=1024, extra=extra)
+        mk = w.mask_args()
+        m = A.Mask(causal=causal, window=mk["window"], block=mk["block_mask"],
+                   block_size=mk["block_size"])
+        assert w.visible_pairs(causal) == int(m.visible(np.arange(1024), np.arange(1024)).sum())
