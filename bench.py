@@ -16,8 +16,10 @@ workloads ..._swa4k and ..._blocksparse).  Also reported:
 % of the dense bf16 MFMA peak, the deterministic / atomic throughput ratio
 per schedule, the backward kernel's own roofline figures (HIP events around
 its launch), the share of cycles the ordered schedules spend waiting for
-their turn (one extra untimed, instrumented launch each), and the fp64 CPU
-oracle timed on a bounded sample of heads.
+their turn (one extra untimed, instrumented launch each), the forward alone
+and a synthetic attention block (forward, then preprocess and backward with
+the reported schedule; forward FLOPs 4*B*H*N^2*d, halved when causal), and
+the fp64 CPU oracle timed on a bounded sample of heads.
 
 Prints one JSON line.  --gpus above 1 is refused: this path runs on one GPU.
 """
@@ -142,6 +144,8 @@ def main():
     ap.add_argument("--cpu-workers", type=int, default=16)
     ap.add_argument("--no-wait-stats", action="store_true",
                     help="skip the untimed instrumented launch per ordered schedule")
+    ap.add_argument("--no-fwd", action="store_true",
+                    help="skip the forward and forward+backward timings")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="run one plain device copy of BYTES before timing (a reference "
                          "dispatch of known traffic for hardware-counter runs)")
@@ -234,6 +238,42 @@ def main():
     peak = PEAK_TFLOPS[w.dtype]
     primary = args.primary or min((s for s in results if s != "atomic"),
                                   key=lambda s: results[s]["ms_per_step"])
+
+    def timed(fn):
+        for _ in range(args.warmup):
+            fn()
+        torch.cuda.synchronize()
+        t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        t0.record()
+        for _ in range(args.steps):
+            fn()
+        t1.record()
+        torch.cuda.synchronize()
+        return t0.elapsed_time(t1) / args.steps
+
+    fwd_stats = None
+    if not args.no_fwd:
+        # the forward alone, and a synthetic attention block: forward, then
+        # the backward pass (preprocess + kernel) with the primary schedule
+        def fwd():
+            D.attn_fwd(dev["q"], dev["k"], dev["v"], causal=causal, out=(o, lse), **mkw)
+
+        def block():
+            fwd()
+            step(primary)
+
+        f_fwd = flops / 2.5
+        ms_f = timed(fwd)
+        ms_b = timed(block)
+        D.attn_bwd_status(ws)
+        fwd_stats = {"forward": {"ms": round(ms_f, 4), "tflops": round(f_fwd / ms_f / 1e9, 2),
+                                 "pct_peak": round(100.0 * f_fwd / ms_f / 1e9 / peak, 2)},
+                     "fwd_bwd_block": {"ms": round(ms_b, 4),
+                                       "tflops": round((f_fwd + flops) / ms_b / 1e9, 2),
+                                       "schedule": primary}}
+        print(f"[bench] forward    {ms_f:8.3f} ms  {f_fwd / ms_f / 1e9:7.1f} TFLOP/s   "
+              f"fwd+bwd {ms_b:8.3f} ms  {(f_fwd + flops) / ms_b / 1e9:7.1f} TFLOP/s",
+              file=sys.stderr, flush=True)
     prim = results[primary]
     # the schedule the launches ran (auto resolves to an ordered one)
     ran = D.resolve_schedule(w.B, w.H, w.N, w.d, w.dtype, causal, primary, **mkw)
@@ -269,6 +309,8 @@ def main():
                        "hbm_GBps": (round(traffic / (prim["kernel_ms"] * 1e-3) / 1e9, 1)
                                     if traffic else None),
                        "kernel": f"bwd_kernel ({ran})"}
+    if fwd_stats:
+        out.update(fwd_stats)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample of heads", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(exact, w, causal, args.cpu_workers)

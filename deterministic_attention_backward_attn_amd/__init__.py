@@ -117,17 +117,23 @@ def subtile(B, H, N, d, dtype="bf16") -> int:
 
 
 def attn_fwd(q, k, v, causal: bool = False, scale=None, stream=None, *, window=0,
-             block_mask=None, block_size=0):
-    """Returns (o, lse): o like q, lse float32 [B, H, N].  Mask: causal,
-    window (sliding window of keys, 0 = none) and block_mask (square host
-    array over blocks of block_size rows; default N / its side), as in the
-    C header."""
+             block_mask=None, block_size=0, out=None):
+    """Returns (o, lse): o like q, lse float32 [B, H, N] (written to `out`
+    = (o, lse) if given).  Mask: causal, window (sliding window of keys,
+    0 = none) and block_mask (square host array over blocks of block_size
+    rows; default N / its side), as in the C header."""
     torch = _torch()
     lib = load()
     _same_shape(q, k, v)
     desc = _desc_from(q, causal, scale, window, block_mask, block_size)
-    o = torch.empty_like(q)
-    lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    if out is None:
+        o = torch.empty_like(q)
+        lse = torch.empty(q.shape[:3], dtype=torch.float32, device=q.device)
+    else:
+        o, lse = out
+        _same_shape(q, o)
+        if lse.dtype != torch.float32 or tuple(lse.shape) != tuple(q.shape[:3]):
+            raise ValueError("lse must be float32 [B, H, N]")
     check(lib.dash_attn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
                             _stream(stream)), "dash_attn_fwd")
     return o, lse

@@ -49,52 +49,6 @@
 
 namespace dash {
 
-// Transposing LDS read of 4 bf16: within each 16-lane group, lane j supplies
-// the address of 4 consecutive elements of row (base_row + j/4), columns
-// (base_col + 4*(j%4) .. +3); lane i receives column base_col + i of rows
-// base_row .. base_row + 3.
-__device__ __forceinline__ u16x4 lds_tr16(const bf16_t* p) {
-  typedef short v4s __attribute__((ext_vector_type(4)));
-  const v4s r = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-      (__attribute__((address_space(3))) v4s*)(p));
-  return __builtin_bit_cast(u16x4, r);
-}
-
-// Fragment whose 8 K slots are rows r0+{0..3} and r1+{0..3} of column
-// c0 + (lane's index in its 16-lane half-column group) of a row-major LDS
-// array; c0 already includes 16*(group%2).  `ix(row, col)` gives the element
-// offset of (row, col) (padded or swizzled layouts); the 4 elements a lane
-// addresses never straddle a 16-byte chunk.
-template <typename IX>
-__device__ __forceinline__ bf16x8 tr_frag(const bf16_t* base, IX ix, int r0, int r1, int c0,
-                                          int j) {
-  const u16x4 a = lds_tr16(base + ix(r0 + (j >> 2), c0 + 4 * (j & 3)));
-  const u16x4 b = lds_tr16(base + ix(r1 + (j >> 2), c0 + 4 * (j & 3)));
-  u16x8 u;
-#pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    u[s] = a[s];
-    u[s + 4] = b[s];
-  }
-  return __builtin_bit_cast(bf16x8, u);
-}
-
-// Bank-conflict-free layout of the bf16 row-major tiles sQ, sdO, sK (row
-// stride D, no padding): the 16-byte chunk c of row r is stored at chunk
-// c ^ swz(r).  The permutation keeps 16 consecutive rows of one chunk (the
-// S/dP operand reads) and 4 consecutive rows of 4 consecutive chunks (the
-// transposing reads) in distinct LDS banks, and every 16-lane run of the
-// row-major staging writes covers whole rows.
-template <int D>
-__device__ __forceinline__ int swz(int r) {
-  if constexpr (D == 128) {
-    return 4 * (r & 3) + ((r >> 2) & 3);
-  } else {
-    const int m = (r >> 1) & 7;
-    return ((m & 1) << 2) | (m >> 1);
-  }
-}
-
 template <typename T, int D, int BC, int BR, bool MASKED, bool ORDERED, bool DEBUG>
 __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
   using E = Elt<T>;

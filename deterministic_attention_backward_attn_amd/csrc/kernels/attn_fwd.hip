@@ -183,6 +183,304 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_kernel(FwdArgs a) {
     a.lse[(size_t)head * N + qi] = l > 0.f ? (m + log2f(l)) * (1.0f / kLog2e) : -INFINITY;
 }
 
+// bf16 forward.  A workgroup owns 256 query rows: 4 waves x 64 rows (two
+// 32-query column tiles each), so every K / V fragment read from LDS feeds
+// two MFMAs.  Key and value tiles of 64 rows stay row-major in LDS (XOR
+// swizzled, double buffered) and are prefetched into registers one tile
+// ahead, so a tile costs one workgroup barrier.  S^T = K Q^T with K from LDS
+// (A operand) and Q^T in registers (B); O^T = V^T P^T with V^T from the
+// transposing LDS read (A) and P^T taken straight from the S^T accumulators
+// (B), their key order matching the accumulator's row order.  The query is
+// on lanes: row statistics need one exchange between the lane halves and
+// the rescale of O^T is a per-lane scalar.  Waves skip key tiles their rows
+// cannot see and mask elements only on tiles that cross a mask bound.
+template <int D, bool MASKED>
+__global__ void __launch_bounds__(256, 1) fwd_bf16_kernel(FwdArgs a) {
+  constexpr int NW = 4;
+  constexpr int QN = 2;                    // 32-query tiles per wave
+  constexpr int WR = 32 * QN;              // query rows per wave
+  constexpr int BM = NW * WR;              // query rows per workgroup
+  constexpr int BN = 64;                   // keys per tile
+  constexpr int DK = D / 16;               // MFMA steps over d
+  constexpr int MT = BN / 32;              // 32-key tiles
+  constexpr int MD = D / 32;               // 32-row tiles of O^T
+  constexpr int CPT = BN * D / 8 / 256;    // 16-byte chunks per thread per tensor
+  static_assert(CPT >= 1 && CPT * 8 * 256 == BN * D, "tile staging");
+  __shared__ __align__(16) bf16_t sK[2][BN * D];
+  __shared__ __align__(16) bf16_t sV[2][BN * D];
+  // block-mask liveness of the (at most 2) query tiles this workgroup covers
+  constexpr int kMaxLive = 2048;
+  __shared__ uint8_t sLive[MASKED ? 2 * kMaxLive : 1];
+  const auto kix = [](int r, int c) { return r * D + (((c >> 3) ^ swz<D>(r)) << 3) + (c & 7); };
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int w = tid >> 6;
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+  const int j16 = lane & 15;
+  const int gcol = 16 * ((lane >> 4) & 1);
+  const int N = a.N;
+  const int n_qb = (N + BM - 1) / BM;
+  // the heaviest query blocks first (under a causal mask work grows with
+  // the block index); heads vary fastest
+  const int qb = n_qb - 1 - (int)(blockIdx.x / (unsigned)a.BH);
+  const int head = (int)(blockIdx.x % (unsigned)a.BH);
+  const int q0 = qb * BM;
+  const int q_end = q0 + BM < N ? q0 + BM : N;
+  const size_t hoff = (size_t)head * N * D;
+  const bf16_t* Qg = reinterpret_cast<const bf16_t*>(a.q) + hoff;
+  const bf16_t* Kg = reinterpret_cast<const bf16_t*>(a.k) + hoff;
+  const bf16_t* Vg = reinterpret_cast<const bf16_t*>(a.v) + hoff;
+  // the tile liveness rows of this workgroup's query tiles (tile = 128 rows)
+  const int qt0 = q0 / (MASKED ? a.tile : 1);
+  if (MASKED && a.live) {
+    for (int i = tid; i < 2 * a.n_tiles; i += 256) {
+      const int r = qt0 + i / a.n_tiles;
+      sLive[i] = r < a.n_tiles ? a.live[(size_t)r * a.n_tiles + i % a.n_tiles] : 0;
+    }
+    __syncthreads();
+  }
+
+  // Does wave v (rows q0 + v*WR ...) need key tile j, and must it mask
+  // elements there?  i - j over the pair spans [qv - k0 - 63, qv + WR-1 - k0].
+  const auto need = [&](int v, int j, bool* emask) {
+    const int qv = q0 + v * WR;
+    if (qv >= N) return false;
+    const int k0 = j * BN;
+    if (!MASKED) {
+      *emask = false;
+      return true;
+    }
+    const int dmin = qv - (k0 + BN - 1), dmax = qv + WR - 1 - k0;
+    if (dmax < a.mask_lo || dmin > a.mask_hi) return false;
+    if (a.live && !sLive[(qv / a.tile - qt0) * a.n_tiles + k0 / a.tile]) return false;
+    *emask = dmin < a.mask_lo || dmax > a.mask_hi;
+    return true;
+  };
+  const auto need_any = [&](int j) {
+    bool e;
+    return need(0, j, &e) || need(1, j, &e) || need(2, j, &e) || need(3, j, &e);
+  };
+  int j_lo = 0, j_hi = N / BN;
+  if (MASKED) {
+    const int k_min = q0 - a.mask_hi;
+    const int k_max = q_end - 1 - a.mask_lo;
+    j_lo = k_min > 0 ? k_min / BN : 0;
+    j_hi = k_max < N - 1 ? k_max / BN + 1 : N / BN;
+  }
+  const auto next_tile = [&](int j) {
+    for (++j; j < j_hi; ++j)
+      if (need_any(j)) return j;
+    return j_hi;
+  };
+
+  const int qw = q0 + w * WR;
+  bf16x8 Qreg[QN][DK];
+#pragma unroll
+  for (int nt = 0; nt < QN; ++nt) {
+    const int row = qw + nt * 32 + l32 < N ? qw + nt * 32 + l32 : N - 1;
+#pragma unroll
+    for (int ks = 0; ks < DK; ++ks) Qreg[nt][ks] = load_frag(Qg + (size_t)row * D + ks * 16 + hh * 8);
+  }
+  // Settle the query loads here: the fragments pass through an empty asm,
+  // so inside the loop they no longer count as outstanding loads (vector
+  // memory completions are counted in order, and a wait for them there
+  // would also wait for the key/value prefetch issued after them).
+#pragma unroll
+  for (int nt = 0; nt < QN; ++nt)
+#pragma unroll
+    for (int ks = 0; ks < DK; ++ks) asm volatile("" : "+v"(Qreg[nt][ks]));
+  f32x16 accO[MD][QN];
+#pragma unroll
+  for (int md = 0; md < MD; ++md)
+#pragma unroll
+    for (int nt = 0; nt < QN; ++nt) accO[md][nt] = zero16();
+  float m_run[QN], l_run[QN];
+#pragma unroll
+  for (int nt = 0; nt < QN; ++nt) {
+    m_run[nt] = -INFINITY;
+    l_run[nt] = 0.f;
+  }
+
+  u32x4 pk[CPT], pv[CPT];
+  const auto fetch = [&](int j) {
+    const int k0 = j * BN;
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + i * 256;
+      const size_t off = (size_t)(k0 + c / (D / 8)) * D + (c % (D / 8)) * 8;
+      pk[i] = *reinterpret_cast<const u32x4*>(Kg + off);
+      pv[i] = *reinterpret_cast<const u32x4*>(Vg + off);
+    }
+  };
+  const auto stage = [&](int buf) {
+#pragma unroll
+    for (int i = 0; i < CPT; ++i) {
+      const int c = tid + i * 256;
+      const int o = kix(c / (D / 8), (c % (D / 8)) * 8);
+      *reinterpret_cast<u32x4*>(&sK[buf][o]) = pk[i];
+      *reinterpret_cast<u32x4*>(&sV[buf][o]) = pv[i];
+    }
+  };
+
+  int j = next_tile(j_lo - 1);
+  int jn = j_hi;
+  if (j < j_hi) {
+    fetch(j);
+    stage(0);
+    jn = next_tile(j);
+    if (jn < j_hi) fetch(jn);
+  }
+  __syncthreads();
+  int buf = 0;
+  while (j < j_hi) {
+    bool emask = false;
+    if (need(w, j, &emask)) {
+      const bf16_t* cK = sK[buf];
+      const bf16_t* cV = sV[buf];
+      const int k0 = j * BN;
+      f32x16 accS[MT][QN];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int nt = 0; nt < QN; ++nt) accS[mt][nt] = zero16();
+      // K fragments in groups of KG steps: a group's LDS reads are issued
+      // together, then its MFMAs (the barriers keep the compiler from
+      // placing each read right before its consumer)
+      constexpr int KG = DK / 2;
+#pragma unroll
+      for (int g = 0; g < DK / KG; ++g) {
+        bf16x8 kf[KG][MT];
+#pragma unroll
+        for (int k2 = 0; k2 < KG; ++k2)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+            kf[k2][mt] = load_frag(&cK[kix(mt * 32 + l32, (g * KG + k2) * 16 + hh * 8)]);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int k2 = 0; k2 < KG; ++k2)
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int nt = 0; nt < QN; ++nt)
+              accS[mt][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                  kf[k2][mt], Qreg[nt][g * KG + k2], accS[mt][nt], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // online softmax per query (lane) column
+#pragma unroll
+      for (int nt = 0; nt < QN; ++nt) {
+        if (MASKED && emask) {
+          // i - j of register r: qi - k0 - mt*32 - crow(r, h)
+          const int base = qw + nt * 32 + l32 - k0 - 4 * hh;
+#pragma unroll
+          for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+              const int dd = base - mt * 32 - ((r >> 2) << 3) - (r & 3);
+              accS[mt][nt][r] = (dd < a.mask_lo || dd > a.mask_hi) ? -INFINITY : accS[mt][nt][r];
+            }
+        }
+        float mx = -INFINITY;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) mx = fmaxf(mx, accS[mt][nt][r]);
+        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        // running max in the exp2 domain (scale > 0 keeps the order)
+        const float m_new = fmaxf(m_run[nt], mx * a.scale_log2);
+        // a row that has seen no key yet keeps max -inf: subtract 0 instead
+        const float m_use = m_new == -INFINITY ? 0.f : m_new;
+        const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - m_use);
+        float ps = 0.f;
+#pragma unroll
+        for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float p = __builtin_amdgcn_exp2f(fmaf(accS[mt][nt][r], a.scale_log2, -m_use));
+            accS[mt][nt][r] = p;
+            ps += p;
+          }
+        ps += __shfl_xor(ps, 32);
+        l_run[nt] = l_run[nt] * alpha + ps;
+        m_run[nt] = m_new;
+#pragma unroll
+        for (int md = 0; md < MD; ++md) accO[md][nt] *= alpha;
+      }
+      // O^T += V^T P^T over this tile's keys, 16 keys per step: keys
+      // mt*32 + 16cc + 4h + {0..3} and + 8 + {0..3} (the accumulator's rows)
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int cc = 0; cc < 2; ++cc) {
+          bf16x8 pb[QN];
+#pragma unroll
+          for (int nt = 0; nt < QN; ++nt) {
+            float t8[8];
+#pragma unroll
+            for (int s8 = 0; s8 < 8; ++s8) t8[s8] = accS[mt][nt][8 * cc + s8];
+            pb[nt] = pack_bf16x8(t8);
+          }
+          const int r0 = mt * 32 + 16 * cc + 4 * hh;
+          bf16x8 va[MD];
+#pragma unroll
+          for (int md = 0; md < MD; ++md) va[md] = tr_frag(cV, kix, r0, r0 + 8, md * 32 + gcol, j16);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int md = 0; md < MD; ++md)
+#pragma unroll
+            for (int nt = 0; nt < QN; ++nt)
+              accO[md][nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(va[md], pb[nt], accO[md][nt],
+                                                                     0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    // the prefetched tile into the other buffer (last read before the
+    // previous barrier), then the next prefetch
+    int jnn = j_hi;
+    if (jn < j_hi) {
+      stage(buf ^ 1);
+      jnn = next_tile(jn);
+      if (jnn < j_hi) fetch(jnn);
+    }
+    __syncthreads();
+    j = jn;
+    jn = jnn;
+    buf ^= 1;
+  }
+
+  if (qw >= N) return;
+  bf16_t* Og = reinterpret_cast<bf16_t*>(a.o) + hoff;
+#pragma unroll
+  for (int nt = 0; nt < QN; ++nt) {
+    const int qi = qw + nt * 32 + l32;
+    const float inv_l = l_run[nt] > 0.f ? 1.f / l_run[nt] : 0.f;
+#pragma unroll
+    for (int md = 0; md < MD; ++md)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        uint2 u;
+        u.x = pack2_bf16(accO[md][nt][4 * g] * inv_l, accO[md][nt][4 * g + 1] * inv_l);
+        u.y = pack2_bf16(accO[md][nt][4 * g + 2] * inv_l, accO[md][nt][4 * g + 3] * inv_l);
+        *reinterpret_cast<uint2*>(Og + (size_t)qi * D + md * 32 + 8 * g + 4 * hh) = u;
+      }
+    if (hh == 0)
+      a.lse[(size_t)head * N + qi] =
+          l_run[nt] > 0.f ? (m_run[nt] + log2f(l_run[nt])) * (1.0f / kLog2e) : -INFINITY;
+  }
+}
+
+template <int D>
+static hipError_t go_fwd_bf16(bool masked, const FwdArgs& a, hipStream_t s) {
+  const long blocks = (long)((a.N + 255) / 256) * a.BH;
+  if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
+  dim3 grid((unsigned)blocks);
+  if (masked) hipLaunchKernelGGL((fwd_bf16_kernel<D, true>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((fwd_bf16_kernel<D, false>), grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
 template <typename T, int D, int NW, int BN>
 static hipError_t go_fwd(bool masked, const FwdArgs& a, hipStream_t s) {
   // one workgroup per (head, query block); the block is one tile
@@ -196,8 +494,8 @@ static hipError_t go_fwd(bool masked, const FwdArgs& a, hipStream_t s) {
 }
 
 hipError_t launch_fwd(int dtype, int d, bool masked, const FwdArgs& a, hipStream_t stream) {
-  if (dtype == 1 && d == 128) return go_fwd<bf16_t, 128, 4, 64>(masked, a, stream);
-  if (dtype == 1 && d == 64) return go_fwd<bf16_t, 64, 4, 64>(masked, a, stream);
+  if (dtype == 1 && d == 128) return go_fwd_bf16<128>(masked, a, stream);
+  if (dtype == 1 && d == 64) return go_fwd_bf16<64>(masked, a, stream);
   if (dtype == 0 && d == 64) return go_fwd<float, 64, 2, 64>(masked, a, stream);
   if (dtype == 0 && d == 128) return go_fwd<float, 128, 2, 64>(masked, a, stream);
   return hipErrorInvalidValue;
