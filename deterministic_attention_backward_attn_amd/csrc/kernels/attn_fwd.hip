@@ -368,7 +368,8 @@ __global__ void __launch_bounds__(256, 1) fwd_bf16_kernel(FwdArgs a) {
                   kf[k2][mt], Qreg[nt][g * KG + k2], accS[mt][nt], 0, 0, 0);
         __builtin_amdgcn_sched_barrier(0);
       }
-      // online softmax per query (lane) column
+      // online softmax per query (lane) column; P packed to bf16 pairs
+      uint32_t pP[MT][QN][8];
 #pragma unroll
       for (int nt = 0; nt < QN; ++nt) {
         if (MASKED && emask) {
@@ -388,25 +389,34 @@ __global__ void __launch_bounds__(256, 1) fwd_bf16_kernel(FwdArgs a) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) mx = fmaxf(mx, accS[mt][nt][r]);
         mx = fmaxf(mx, __shfl_xor(mx, 32));
-        // running max in the exp2 domain (scale > 0 keeps the order)
-        const float m_new = fmaxf(m_run[nt], mx * a.scale_log2);
+        // Lazy rescaling: the running max (exp2 domain; scale > 0 keeps the
+        // order) moves, and O^T and the sum are rescaled, only when some
+        // query of the wave gained more than 2^8 over it; otherwise P is
+        // taken against the stale max (at most 2^8, exact in the final
+        // normalisation by the sum).
+        const float cand = fmaxf(m_run[nt], mx * a.scale_log2);
+        if (__builtin_amdgcn_ballot_w64(cand > m_run[nt] + 8.0f) != 0) {
+          const float c_use = cand == -INFINITY ? 0.f : cand;
+          const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - c_use);
+          m_run[nt] = cand;
+          l_run[nt] *= alpha;
+#pragma unroll
+          for (int md = 0; md < MD; ++md) accO[md][nt] *= alpha;
+        }
         // a row that has seen no key yet keeps max -inf: subtract 0 instead
-        const float m_use = m_new == -INFINITY ? 0.f : m_new;
-        const float alpha = __builtin_amdgcn_exp2f(m_run[nt] - m_use);
+        const float m_use = m_run[nt] == -INFINITY ? 0.f : m_run[nt];
         float ps = 0.f;
 #pragma unroll
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const float p = __builtin_amdgcn_exp2f(fmaf(accS[mt][nt][r], a.scale_log2, -m_use));
-            accS[mt][nt][r] = p;
-            ps += p;
+          for (int r = 0; r < 16; r += 2) {
+            const float p0 = __builtin_amdgcn_exp2f(fmaf(accS[mt][nt][r], a.scale_log2, -m_use));
+            const float p1 = __builtin_amdgcn_exp2f(fmaf(accS[mt][nt][r + 1], a.scale_log2, -m_use));
+            pP[mt][nt][r / 2] = pack2_bf16(p0, p1);
+            ps += p0 + p1;
           }
         ps += __shfl_xor(ps, 32);
-        l_run[nt] = l_run[nt] * alpha + ps;
-        m_run[nt] = m_new;
-#pragma unroll
-        for (int md = 0; md < MD; ++md) accO[md][nt] *= alpha;
+        l_run[nt] += ps;
       }
       // O^T += V^T P^T over this tile's keys, 16 keys per step: keys
       // mt*32 + 16cc + 4h + {0..3} and + 8 + {0..3} (the accumulator's rows)
@@ -416,12 +426,10 @@ __global__ void __launch_bounds__(256, 1) fwd_bf16_kernel(FwdArgs a) {
         for (int cc = 0; cc < 2; ++cc) {
           bf16x8 pb[QN];
 #pragma unroll
-          for (int nt = 0; nt < QN; ++nt) {
-            float t8[8];
-#pragma unroll
-            for (int s8 = 0; s8 < 8; ++s8) t8[s8] = accS[mt][nt][8 * cc + s8];
-            pb[nt] = pack_bf16x8(t8);
-          }
+          for (int nt = 0; nt < QN; ++nt)
+            pb[nt] = __builtin_bit_cast(bf16x8, make_uint4(pP[mt][nt][4 * cc], pP[mt][nt][4 * cc + 1],
+                                                           pP[mt][nt][4 * cc + 2],
+                                                           pP[mt][nt][4 * cc + 3]));
           const int r0 = mt * 32 + 16 * cc + 4 * hh;
           bf16x8 va[MD];
 #pragma unroll
