@@ -195,7 +195,8 @@ def attn_bwd(q, k, v, do, lse, delta, *, schedule="naive", causal=False, scale=N
     jitter_seed, poison_q (1-based, 0 = off), partials (float32 tensor),
     kernel_events (two raw hipEvent_t handles), wait_stats (int64 tensor of
     at least 4*4096*4 entries), placement (0 automatic, 1 device-wide, 2 XCD
-    groups with L2-coherent accumulator, 3 XCD groups device-coherent).
+    groups with L2-coherent accumulator, 3 XCD groups device-coherent),
+    unit_order (0 automatic, 1 head by head, 2 unit-major).
     Mask arguments as for attn_fwd."""
     torch = _torch()
     lib = load()
@@ -221,6 +222,7 @@ def attn_bwd(q, k, v, do, lse, delta, *, schedule="naive", causal=False, scale=N
                     int(debug.get("poison_q", 0)),
                     _ptr(debug["partials"]) if debug.get("partials") is not None else None)
         dbg.placement = int(debug.get("placement", 0))
+        dbg.unit_order = int(debug.get("unit_order", 0))
         if debug.get("wait_stats") is not None:
             dbg.wait_stats = _ptr(debug["wait_stats"])
         ev = debug.get("kernel_events")
@@ -312,14 +314,16 @@ def mask_schedule_tables(B, H, N, d, dtype="bf16", causal=False, schedule="naive
 
 
 def mask_schedule_predict(B, H, N, d, dtype="bf16", causal=False, schedule="naive", *, slots,
-                          cost, window=0, block_mask=None, block_size=0):
+                          cost, window=0, block_mask=None, block_size=0, unit_major=False):
     """DAG prediction for a masked problem with B*H heads: (makespan,
-    total_wait, max_slot_idle, lower_bound)."""
+    total_wait, max_slot_idle, lower_bound); unit_major: dynamic schedules
+    take unit 0 of every head, then unit 1, ..."""
     lib = load()
     desc = _desc(B, H, N, d, dtype, causal, None, window, block_mask, block_size)
     c = (ctypes.c_double * 4)(*[float(x) for x in cost])
     out = (ctypes.c_double * 4)()
-    check(lib.dash_attn_schedule_predict(ctypes.byref(desc), _sched(schedule), int(slots), c, out),
+    check(lib.dash_attn_schedule_predict(ctypes.byref(desc), _sched(schedule), int(slots),
+                                         1 if unit_major else 0, c, out),
           "dash_attn_schedule_predict")
     return tuple(out)
 

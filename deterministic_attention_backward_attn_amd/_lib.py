@@ -44,7 +44,7 @@ class Debug(ctypes.Structure):
     _fields_ = [("spin_limit", ctypes.c_uint32), ("jitter_seed", ctypes.c_uint32),
                 ("poison_q", ctypes.c_int32), ("partials", ctypes.c_void_p),
                 ("kernel_events", ctypes.c_void_p * 2), ("wait_stats", ctypes.c_void_p),
-                ("placement", ctypes.c_int32)]
+                ("placement", ctypes.c_int32), ("unit_order", ctypes.c_int32)]
 
 
 _vp = ctypes.c_void_p
@@ -72,7 +72,8 @@ _SIGS = {
                                                       ctypes.POINTER(ctypes.c_int)]),
     "dash_attn_schedule_tables": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, _ip, _ip, _ip,
                                                  _ip, _ip, ctypes.c_void_p, _ip]),
-    "dash_attn_schedule_predict": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, _i32, _dp, _dp]),
+    "dash_attn_schedule_predict": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, _i32, _i32, _dp,
+                                                  _dp]),
     "dash_schedule_choose": (ctypes.c_int, [_i32, _i32, _i32, _i32, _dp,
                                             ctypes.POINTER(ctypes.c_int), _dp]),
     "dash_dag_longest_path": (ctypes.c_int, [_i32, _dp, _i32, _ip, _ip, _dp, _dp, _dp]),

@@ -170,6 +170,40 @@ std::map<std::tuple<int, MaskKey, int>, DevTables> g_tables;  // (device, mask, 
 std::map<std::pair<int, MaskKey>, DevMask> g_masks;           // (device, mask)
 std::map<std::tuple<int, int, int, int, int>, int> g_coresident;  // (device, dtype, d, masked, ordered)
 std::map<std::tuple<MaskKey, int, int>, Sched> g_auto;  // (mask, heads, slots) -> choice
+// (mask, sched, heads, slots, grouped) -> unit-major
+std::map<std::tuple<MaskKey, int, long, int, int>, bool> g_order;
+
+constexpr int kXcds = 8;  // XCDs of an MI355X: the group share the order choice predicts for
+
+// Unit order of a dynamic ordered schedule: unit-major (unit 0 of every
+// head, then unit 1, ...) when the DAG model predicts a makespan at least
+// 5 % shorter than head by head for one group's share (the heads and
+// workgroups of one XCD when units run in XCD groups).  A head's own units
+// keep their relative order either way, so results are bit-identical; the
+// order only changes which heads run side by side (masks whose units
+// differ much in length gain most).
+bool unit_major_for(const MaskKey& mkey, const Tables& t, Sched s, long heads, int maxco,
+                    bool grouped) {
+  if (t.needs_static() || !t.ordered() || t.units() == 0) return false;
+  const auto key = std::make_tuple(mkey, (int)s, heads, maxco, (int)grouped);
+  {
+    std::lock_guard<std::mutex> lock(g_mu);
+    auto it = g_order.find(key);
+    if (it != g_order.end()) return it->second;
+  }
+  const int g = grouped ? kXcds : 1;
+  const int slots = std::max(1, maxco / g);
+  long hg = (heads + g - 1) / g;
+  hg = std::max<long>(1, std::min<long>(hg, 200000 / std::max(1, t.items())));
+  dash::DagResult hm, um;
+  bool pick = false;
+  if (dash::dag_predict(t, (int)hg, slots, kDefaultCost, hm, false) &&
+      dash::dag_predict(t, (int)hg, slots, kDefaultCost, um, true))
+    pick = um.makespan < 0.95 * hm.makespan;
+  std::lock_guard<std::mutex> lock(g_mu);
+  g_order[key] = pick;
+  return pick;
+}
 
 dash_status get_mask(int dev, const MaskKey& key, const DevMask** out) {
   std::lock_guard<std::mutex> lock(g_mu);
@@ -316,6 +350,7 @@ dash_status run_bwd(const dash_attn_desc* desc, dash_schedule schedule, const vo
   const bool ordered = schedule != DASH_SCHED_ATOMIC;
   if (dbg && (dbg->poison_q < 0 || dbg->poison_q > desc->N / br)) return DASH_ERR_INVALID_ARG;
   if (dbg && (dbg->placement < 0 || dbg->placement > 3)) return DASH_ERR_INVALID_ARG;
+  if (dbg && (dbg->unit_order < 0 || dbg->unit_order > 2)) return DASH_ERR_INVALID_ARG;
 
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return DASH_ERR_HIP;
@@ -389,6 +424,9 @@ dash_status run_bwd(const dash_attn_desc* desc, dash_schedule schedule, const vo
   // every workload); the atomic reference gains nothing from it
   a.xcd_mode = ordered ? 1 : 0;
   if (dbg && dbg->placement) a.xcd_mode = dbg->placement - 1;
+  a.unit_major = dynamic ? (unit_major_for(mkey, tb->host, s, heads, maxco, a.xcd_mode != 0) ? 1 : 0)
+                         : 0;
+  if (dbg && dbg->unit_order && dynamic) a.unit_major = dbg->unit_order - 1;
   a.scale = scale_of(desc);
   a.scale_log2 = a.scale * 1.4426950408889634f;
   a.spin_limit = (dbg && dbg->spin_limit) ? dbg->spin_limit : kDefaultSpin;
@@ -646,10 +684,12 @@ dash_status dash_attn_schedule_tables(const dash_attn_desc* desc, dash_schedule 
 }
 
 dash_status dash_attn_schedule_predict(const dash_attn_desc* desc, dash_schedule schedule,
-                                       int32_t slots, const double cost[4], double out[4]) {
+                                       int32_t slots, int32_t unit_major, const double cost[4],
+                                       double out[4]) {
   dash_status st = check_desc(desc);
   if (st != DASH_OK) return st;
-  if (!sched_ok(schedule) || slots < 1 || !cost || !out) return DASH_ERR_INVALID_ARG;
+  if (!sched_ok(schedule) || slots < 1 || !cost || !out || (unit_major != 0 && unit_major != 1))
+    return DASH_ERR_INVALID_ARG;
   for (int i = 0; i < 4; ++i)
     if (!(cost[i] >= 0.0) || !std::isfinite(cost[i])) return DASH_ERR_INVALID_ARG;
   Tables t;
@@ -657,7 +697,8 @@ dash_status dash_attn_schedule_predict(const dash_attn_desc* desc, dash_schedule
   if (dash::validate_tables(t)[0] != '\0') return DASH_ERR_SCHEDULE_INVALID;
   if (t.needs_static() && t.units() > slots) return DASH_ERR_UNSUPPORTED;
   dash::DagResult r;
-  if (!dash::dag_predict(t, desc->B * desc->H, slots, cost, r)) return DASH_ERR_SCHEDULE_INVALID;
+  if (!dash::dag_predict(t, desc->B * desc->H, slots, cost, r, unit_major != 0))
+    return DASH_ERR_SCHEDULE_INVALID;
   out[0] = r.makespan;
   out[1] = r.total_wait;
   out[2] = r.max_slot_idle;

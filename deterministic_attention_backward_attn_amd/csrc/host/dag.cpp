@@ -34,7 +34,8 @@ bool dag_longest_path(int n_nodes, const double* w, int n_edges, const int* src,
   return (int)order.size() == n_nodes;
 }
 
-bool dag_predict(const Tables& t, int heads, int slots, const double cost[4], DagResult& out) {
+bool dag_predict(const Tables& t, int heads, int slots, const double cost[4], DagResult& out,
+                 bool unit_major) {
   const int n = t.n, U = t.units(), I = t.items();
   if (heads < 1 || slots < 1) return false;
   if (U == 0) {  // nothing to run (every pair masked)
@@ -60,6 +61,11 @@ bool dag_predict(const Tables& t, int heads, int slots, const double cost[4], Da
   }
 
   const long total_units = (long)U * heads;
+  // global unit order: head-major (g = head * U + unit) or, for the dynamic
+  // policy on request, unit-major (g = unit * heads + head)
+  const bool um = unit_major && !t.needs_static();
+  auto head_of = [&](long g) { return (int)(um ? g % heads : g / U); };
+  auto unit_of = [&](long g) { return (int)(um ? g / heads : g % U); };
   std::vector<int> slot_of(total_units);
   if (t.needs_static()) {
     if (U > slots) return false;
@@ -75,7 +81,7 @@ bool dag_predict(const Tables& t, int heads, int slots, const double cost[4], Da
       const Ev ev = freeq.top();
       freeq.pop();
       slot_of[g] = ev.second;
-      const int hd = (int)(g / U), u = (int)(g % U);
+      const int hd = head_of(g), u = unit_of(g);
       double tnow = ev.first;
       for (int i = t.unit_off[u]; i < t.unit_off[u + 1]; ++i) {
         double tr = tnow + ccost(i);
@@ -108,7 +114,7 @@ bool dag_predict(const Tables& t, int heads, int slots, const double cost[4], Da
     }
   std::vector<long> last_r(slots, -1);
   for (long g = 0; g < total_units; ++g) {
-    const int hd = (int)(g / U), u = (int)(g % U);
+    const int hd = head_of(g), u = unit_of(g);
     const int a = t.unit_off[u], b = t.unit_off[u + 1];
     if (a == b) continue;
     for (int i = a + 1; i < b; ++i) {
@@ -135,7 +141,7 @@ bool dag_predict(const Tables& t, int heads, int slots, const double cost[4], Da
   for (long v = 0; v < nodes; ++v) res.makespan = std::max(res.makespan, fin[v]);
   for (long gi = 0; gi < (long)I * heads; ++gi) res.total_wait += st[2 * gi + 1] - fin[2 * gi];
   for (long g = 0; g < total_units; ++g) {
-    const int u = (int)(g % U);
+    const int u = unit_of(g);
     double len = 0.0;
     for (int i = t.unit_off[u]; i < t.unit_off[u + 1]; ++i) len += ccost(i) + r;
     busy[slot_of[g]] += len;

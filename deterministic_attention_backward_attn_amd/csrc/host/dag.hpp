@@ -28,6 +28,9 @@ bool dag_longest_path(int n_nodes, const double* w, int n_edges, const int* src,
 
 // Returns false if the policy cannot run these tables on `slots` slots
 // (static policy with fewer slots than units per head) or on a cycle.
-bool dag_predict(const Tables& t, int heads, int slots, const double cost[4], DagResult& out);
+// unit_major: the dynamic policy takes unit 0 of every head, then unit 1 of
+// every head, ... (default: head after head).
+bool dag_predict(const Tables& t, int heads, int slots, const double cost[4], DagResult& out,
+                 bool unit_major = false);
 
 }  // namespace dash

@@ -131,14 +131,18 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
   const int grp = pl.grp, n_grp = pl.n_grp, li = pl.li, W = pl.W;
   const bool grouped = pl.grouped, xl = pl.xl;
   const int BH = a.total_units / U;
-  const int n_units = ((BH - grp + n_grp - 1) / n_grp) * U;  // units of this group
+  const int hg = (BH - grp + n_grp - 1) / n_grp;  // heads of this group
+  const int n_units = hg * U;                      // units of this group
   const int stride_static = grouped ? (W / U) * U : a.p_eff;
   uint32_t* work_counter = grouped ? &a.header[20 + grp] : &a.header[1];
   int unit = (a.dynamic == 0 && li >= stride_static) ? n_units : li;
 
   while (unit < n_units) {
-    const int head = grp + n_grp * (unit / U);
-    const int lu = unit - (unit / U) * U;
+    // head-major: a head's units in a row; unit-major (dynamic schedules
+    // only): unit lu of every head of the group in turn
+    const int hq = a.unit_major ? unit % hg : unit / U;
+    const int lu = a.unit_major ? unit / hg : unit - hq * U;
+    const int head = grp + n_grp * hq;
     const size_t hoff = (size_t)head * N * D;
     const T* Qg = reinterpret_cast<const T*>(a.q) + hoff;
     const T* Kg = reinterpret_cast<const T*>(a.k) + hoff;

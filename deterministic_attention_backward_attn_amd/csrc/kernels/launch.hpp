@@ -34,6 +34,7 @@ struct BwdArgs {
   int total_units;        // units_per_head * BH
   int p_eff;              // static policy: workgroups that take units
   int dynamic;            // 1: take units from the work counter
+  int unit_major;         // dynamic only: 1 = unit lu of every head in turn, 0 = head by head
   int xcd_mode;           // 0 device-wide; XCD-local groups when they fit with
                           // 1: L2-coherent, 2: device-coherent accumulator
   float scale;            // softmax scale s

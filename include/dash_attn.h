@@ -202,6 +202,13 @@ dash_status dash_attn_bwd_status(const void* workspace, void* stream);
  *                   XCD groups fall back to device-wide when a head's units
  *                   cannot all be resident on one XCD (static schedules).
  *                   Other values: DASH_ERR_INVALID_ARG.
+ *   unit_order      order in which workgroups take the units of a dynamic
+ *                   schedule (NAIVE, DESCENDING); results are bit-identical
+ *                   for every value.  0 = automatic (unit-major when the DAG
+ *                   model predicts a makespan at least 5 % shorter, else
+ *                   head by head); 1 = head by head; 2 = unit-major (unit 0
+ *                   of every head, then unit 1, ...).  Ignored by static
+ *                   schedules.  Other values: DASH_ERR_INVALID_ARG.
  *   wait_stats      non-NULL: device uint64 buffer of at least
  *                   4 * 4096 * 4 entries; for each workgroup g and wave w,
  *                   entries [(g*waves + w)*4 + k] receive: k=0 shader-clock
@@ -219,6 +226,7 @@ typedef struct {
   void* kernel_events[2];
   uint64_t* wait_stats;
   int32_t placement;
+  int32_t unit_order;
 } dash_bwd_debug;
 
 dash_status dash_attn_bwd_debug(const dash_attn_desc* desc, dash_schedule schedule,
@@ -309,10 +317,13 @@ dash_status dash_attn_schedule_tables(const dash_attn_desc* desc, dash_schedule 
 
 /*
  * dash_schedule_predict for any descriptor: B*H heads, its mask's tables
- * (partial pairs cost c_diag).  Host only.
+ * (partial pairs cost c_diag).  unit_major = 1: the dynamic policy takes
+ * unit 0 of every head, then unit 1, ... (0: head by head; ignored by
+ * SHIFT).  Host only.
  */
 dash_status dash_attn_schedule_predict(const dash_attn_desc* desc, dash_schedule schedule,
-                                       int32_t slots, const double cost[4], double out[4]);
+                                       int32_t slots, int32_t unit_major, const double cost[4],
+                                       double out[4]);
 
 /*
  * Longest path (critical path) of a general DAG, host only.  Node weights

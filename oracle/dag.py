@@ -90,8 +90,12 @@ def _item_costs(causal, cost, partial):
     return lambda kv, q: cost[1] if (kv, q) in partial else cost[0]
 
 
-def realize(schedule, n, causal, heads, slots, cost, tables=None):
+def realize(schedule, n, causal, heads, slots, cost, tables=None, unit_major=False):
     """Assign units to slots and build the graph.
+
+    ``unit_major`` (dynamic policy only): slots take units in the order
+    unit 0 of every head, unit 1 of every head, ... instead of head after
+    head (a head's own units keep their order either way).
 
     ``tables`` (optional) gives one head's tables explicitly, for masks the
     oracle does not construct itself: {"units": [[(kv, q), ...], ...],
@@ -115,9 +119,15 @@ def realize(schedule, n, causal, heads, slots, cost, tables=None):
         icost = _item_costs(causal, cost, tables["partial"])
     U = len(per_head)
     glob = []
-    for hd in range(heads):
+    if unit_major and _policy(schedule) == "dynamic":
+        # all heads' first units, then all heads' second units, ...
         for items in per_head:
-            glob.append([(hd, kv, q) for kv, q in items])
+            for hd in range(heads):
+                glob.append([(hd, kv, q) for kv, q in items])
+    else:
+        for hd in range(heads):
+            for items in per_head:
+                glob.append([(hd, kv, q) for kv, q in items])
     # node ids: for unit u item k -> C = 2*idx, R = 2*idx + 1
     idx_of = {}
     weights = []
@@ -186,13 +196,13 @@ def realize(schedule, n, causal, heads, slots, cost, tables=None):
             "icost": icost}
 
 
-def predict(schedule, n, causal, heads, slots, cost, tables=None):
+def predict(schedule, n, causal, heads, slots, cost, tables=None, unit_major=False):
     """Returns (makespan, total_wait, max_slot_idle, lower_bound).
 
     total_wait: summed time R nodes spend held by their order edge beyond
     what their own chain allows; max_slot_idle: largest (makespan - busy)
     over slots; lower_bound: max(total work / slots, longest single unit)."""
-    g = realize(schedule, n, causal, heads, slots, cost, tables)
+    g = realize(schedule, n, causal, heads, slots, cost, tables, unit_major)
     icost = g["icost"]
     start, finish = longest_path(g["weights"], g["edges"])
     makespan = max(finish) if finish else 0.0

@@ -135,3 +135,19 @@ def test_masked_determinism_and_bit_relations(causal, window, block):
                 assert torch.equal(iv(a), iv(b)), (sched, run)
         D.attn_bwd_status(ws)
         log(f"  {sched}: 10 further runs identical")
+
+
+def test_block_mask_unit_order_changes_no_bit():
+    """The block-sparse case the unit-major order is for: same bits either way."""
+    dev, lse, delta, kw, outs = _run(1, 8, 1024, 128, "bf16", True, 0, BLOCK8, 5900,
+                                     schedules=["descending"])
+    for sched in ("naive", "descending"):
+        ref = None
+        for order in (1, 2, 0):
+            out = D.attn_bwd(dev["q"], dev["k"], dev["v"], dev["do"], lse, delta, schedule=sched,
+                             causal=True, debug={"unit_order": order}, **kw)
+            if ref is None:
+                ref = [t.clone() for t in out]
+                continue
+            for x, y in zip(ref, out):
+                assert torch.equal(x.view(torch.int16), y.view(torch.int16)), (sched, order)

@@ -227,3 +227,18 @@ def test_auto_runs_its_resolved_schedule(shape, causal):
         out = _bwd(dev, lse, delta, "auto", causal)
         for x, y in zip(ref, out):
             assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_unit_order_changes_no_bit(causal):
+    """Units taken head by head or unit-major: a head's units keep their
+    order, so results are bit-identical."""
+    require_gpu()
+    log(f"unit order causal={causal}")
+    dev, lse, delta = _prep(2, 16, 2048, 128, "bf16", causal, 8300)
+    for sched in ("naive", "descending"):
+        ref = [t.clone() for t in _bwd(dev, lse, delta, sched, causal, debug={"unit_order": 1})]
+        for order in (0, 2):
+            out = _bwd(dev, lse, delta, sched, causal, debug={"unit_order": order})
+            for x, y in zip(ref, out):
+                assert torch.equal(x.view(torch.int16), y.view(torch.int16)), (sched, order)

@@ -197,6 +197,11 @@ def test_argument_errors_without_launch():
         dbg.placement = bad
         assert lib.dash_attn_bwd_debug(ctypes.byref(desc), 1, *args, ws_ok, ctypes.byref(dbg),
                                        None) == 1
+    for bad in (-1, 3):  # unit order out of range
+        dbg = _lib.Debug()
+        dbg.unit_order = bad
+        assert lib.dash_attn_bwd_debug(ctypes.byref(desc), 1, *args, ws_ok, ctypes.byref(dbg),
+                                       None) == 1
     # host-only argument checks
     assert lib.dash_schedule_predict(0, 0, 1, 1, 1, None, None) == 1
     choice = ctypes.c_int(-1)
