@@ -26,7 +26,6 @@ Prints one JSON line.  --gpus above 1 is refused: this path runs on one GPU.
 from __future__ import annotations
 
 import argparse
-import hashlib
 import json
 import os
 import re
@@ -38,16 +37,11 @@ sys.path.insert(0, ROOT)
 
 METRIC = "deterministic attn-bwd TFLOP/s + % bf16 MFMA peak; det/non-det throughput ratio"
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense MFMA (bf16), fp32 MFMA
-KERNEL_SOURCES = ["deterministic_attention_backward_attn_amd/csrc/kernels/attn_bwd.hip",
-                  "deterministic_attention_backward_attn_amd/csrc/kernels/common.hpp"]
-
-
 def kernel_source_hash() -> str:
-    h = hashlib.sha256()
-    for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
-    return h.hexdigest()[:16]
+    """Hash of the backward kernel's sources and build flags, as recorded in
+    the committed traffic summaries."""
+    from deterministic_attention_backward_attn_amd.rocprof_summary import kernel_source_hash as h
+    return h()
 
 
 def read_traffic(workload: str, schedule: str):

@@ -8,7 +8,7 @@
   python -m deterministic_attention_backward_attn_amd.rocprof_summary traffic \\
       --fetch-csv <dir>/<prefix>_counter_collection.csv \\
       --write-csv <dir>/<prefix>_counter_collection.csv \\
-      --copy-bytes N --kernel bwd_kernel --flops F \\
+      --copy-bytes N --kernel bwd_kernel --flops F [--dispatches A:B] \\
       --cmd-fetch "<command>" --cmd-write "<command>" --out profiles/<name>.md
 
 With --trace, the backward kernel's dispatches (in dispatch order) are cut
@@ -44,7 +44,8 @@ import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 KERNEL_SOURCES = ["deterministic_attention_backward_attn_amd/csrc/kernels/attn_bwd.hip",
-                  "deterministic_attention_backward_attn_amd/csrc/kernels/common.hpp"]
+                  "deterministic_attention_backward_attn_amd/csrc/kernels/common.hpp",
+                  "deterministic_attention_backward_attn_amd/build.py"]   # compile flags
 
 
 def kernel_source_hash() -> str:
@@ -113,9 +114,14 @@ def traffic(args):
     known_kib = args.copy_bytes / 1024.0
     f_fac = known_kib / copy_kib(fetch)
     w_fac = known_kib / copy_kib(write)
-    fk = [v[1] for v in fetch.values() if args.kernel in v[0]]
-    wk = [v[1] for v in write.values() if args.kernel in v[0]]
-    dur = [v[2] for v in fetch.values() if args.kernel in v[0]]
+    def pick(d, i):
+        vals = [d[k][i] for k in sorted(d) if args.kernel in d[k][0]]
+        if args.dispatches:
+            a, b = (int(x) for x in args.dispatches.split(":"))
+            vals = vals[a:b]
+        return vals
+
+    fk, wk, dur = pick(fetch, 1), pick(write, 1), pick(fetch, 2)
     if not fk or not wk:
         raise SystemExit(f"no dispatch of {args.kernel}")
     fetch_b = statistics.mean(fk) * f_fac * 1024
@@ -126,7 +132,9 @@ def traffic(args):
              f"Calibration: a plain device copy of {args.copy_bytes} bytes in the same process; "
              f"FETCH_SIZE factor {f_fac:.4f}, WRITE_SIZE factor {w_fac:.4f} "
              f"(known bytes / counter reading).", "",
-             f"Dispatches of `{args.kernel}`: {len(fk)}; raw FETCH_SIZE {statistics.mean(fk):.0f} KiB, "
+             f"Dispatches of `{args.kernel}`: {len(fk)}"
+             + (f" (numbers {args.dispatches} of the run, in dispatch order)" if args.dispatches else "")
+             + f"; raw FETCH_SIZE {statistics.mean(fk):.0f} KiB, "
              f"raw WRITE_SIZE {statistics.mean(wk):.0f} KiB per dispatch.", "",
              f"fetch_bytes_per_launch: {fetch_b:.6g}",
              f"write_bytes_per_launch: {write_b:.6g}",
@@ -207,6 +215,9 @@ def main(argv=None):
     t.add_argument("--copy-bytes", type=int, required=True)
     t.add_argument("--kernel", default="bwd_kernel")
     t.add_argument("--flops", type=float, default=0.0)
+    t.add_argument("--dispatches", default="",
+                   help="a:b = only the backward dispatches a..b-1 (dispatch order), e.g. one "
+                        "schedule's block when the run timed several")
     t.add_argument("--cmd-fetch", required=True)
     t.add_argument("--cmd-write", required=True)
     t.add_argument("--out")
