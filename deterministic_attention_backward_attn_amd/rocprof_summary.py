@@ -44,15 +44,17 @@ import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 KERNEL_SOURCES = ["deterministic_attention_backward_attn_amd/csrc/kernels/attn_bwd.hip",
-                  "deterministic_attention_backward_attn_amd/csrc/kernels/common.hpp",
-                  "deterministic_attention_backward_attn_amd/build.py"]   # compile flags
+                  "deterministic_attention_backward_attn_amd/csrc/kernels/common.hpp"]
 
 
 def kernel_source_hash() -> str:
+    """Hash of the backward kernel's sources and its device compile flags."""
+    from deterministic_attention_backward_attn_amd import build as B
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
+    h.update(" ".join(B.DEVICE + B.PER_FILE.get("kernels/attn_bwd.hip", [])).encode())
     return h.hexdigest()[:16]
 
 
