@@ -194,6 +194,16 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_kernel(FwdArgs a) {
 // on lanes: row statistics need one exchange between the lane halves and
 // the rescale of O^T is a per-lane scalar.  Waves skip key tiles their rows
 // cannot see and mask elements only on tiles that cross a mask bound.
+// max(x of this lane, x of lane l ^ 32): v_permlane32_swap exchanges the
+// upper half of its first operand with the lower half of its second, so
+// with x in both the two results hold, per lane, x and the other half's x.
+// A VALU operation (no LDS traffic, unlike a shuffle).
+__device__ __forceinline__ float max_halves(float x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false,
+                                                  false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
 template <int D, bool MASKED>
 __global__ void __launch_bounds__(256, 1) fwd_bf16_kernel(FwdArgs a) {
   constexpr int NW = 4;
@@ -388,7 +398,7 @@ __global__ void __launch_bounds__(256, 1) fwd_bf16_kernel(FwdArgs a) {
         for (int mt = 0; mt < MT; ++mt)
 #pragma unroll
           for (int r = 0; r < 16; ++r) mx = fmaxf(mx, accS[mt][nt][r]);
-        mx = fmaxf(mx, __shfl_xor(mx, 32));
+        mx = max_halves(mx);
         // Lazy rescaling: the running max (exp2 domain; scale > 0 keeps the
         // order) moves, and O^T and the sum are rescaled, only when some
         // query of the wave gained more than 2^8 over it; otherwise P is
@@ -415,7 +425,8 @@ __global__ void __launch_bounds__(256, 1) fwd_bf16_kernel(FwdArgs a) {
             pP[mt][nt][r / 2] = pack2_bf16(p0, p1);
             ps += p0 + p1;
           }
-        ps += __shfl_xor(ps, 32);
+        // each lane half keeps the sum over its own keys (the halves share
+        // the running max); they are added once at the end
         l_run[nt] += ps;
       }
       // O^T += V^T P^T over this tile's keys, 16 keys per step: keys
@@ -460,6 +471,8 @@ __global__ void __launch_bounds__(256, 1) fwd_bf16_kernel(FwdArgs a) {
 
   if (qw >= N) return;
   bf16_t* Og = reinterpret_cast<bf16_t*>(a.o) + hoff;
+#pragma unroll
+  for (int nt = 0; nt < QN; ++nt) l_run[nt] += __shfl_xor(l_run[nt], 32);
 #pragma unroll
   for (int nt = 0; nt < QN; ++nt) {
     const int qi = qw + nt * 32 + l32;
