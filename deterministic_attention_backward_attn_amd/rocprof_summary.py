@@ -81,12 +81,15 @@ def stats(args):
             raise SystemExit(f"{len(bwd)} backward dispatches, expected "
                              f"{len(names)} x {args.block_size}")
         lines += ["", "Backward kernel per schedule (dispatches in order, "
-                  f"{args.block_size} per schedule):", "",
-                  "| schedule | dispatches | avg us | min us | max us |", "|---|---|---|---|---|"]
+                  f"{args.block_size} per schedule; 'timed avg' leaves out the first "
+                  f"{args.warmup}, the warm-up launches):", "",
+                  "| schedule | dispatches | avg us | timed avg us | min us | max us |",
+                  "|---|---|---|---|---|---|"]
         for i, name in enumerate(names):
             d = bwd[i * args.block_size:(i + 1) * args.block_size]
-            lines.append(f"| {name} | {len(d)} | {statistics.mean(d):.1f} | {min(d):.1f} | "
-                         f"{max(d):.1f} |")
+            timed = d[args.warmup:] or d
+            lines.append(f"| {name} | {len(d)} | {statistics.mean(d):.1f} | "
+                         f"{statistics.mean(timed):.1f} | {min(d):.1f} | {max(d):.1f} |")
     lines += ["", f"kernel_source_sha256: {kernel_source_hash()}", ""]
     _write(args.out, lines)
 
@@ -204,6 +207,8 @@ def main(argv=None):
     s.add_argument("--trace")
     s.add_argument("--blocks", default="atomic,naive,descending,shift")
     s.add_argument("--block-size", type=int, default=0)
+    s.add_argument("--warmup", type=int, default=0,
+                   help="leading dispatches of each block that were warm-up launches")
     c = sub.add_parser("counters")
     c.add_argument("--csv", required=True)
     c.add_argument("--cmd", required=True)
