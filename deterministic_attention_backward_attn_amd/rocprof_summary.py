@@ -165,7 +165,7 @@ def counters(args):
     if len(ids) != len(names) * args.block_size:
         raise SystemExit(f"{len(ids)} dispatches, expected {len(names)} x {args.block_size}")
     ctrs = sorted({c for d in per.values() for c in d})
-    lines = ["# rocprofv3 SQ counters of the backward kernel", "",
+    lines = [f"# rocprofv3 SQ counters of `{args.kernel}`", "",
              f"Command: `{args.cmd}`", "",
              f"Per schedule: mean over its {args.block_size} dispatches (dispatch order).", "",
              "| counter | " + " | ".join(names) + " |", "|---|" + "---|" * len(names)]
@@ -185,7 +185,9 @@ def counters(args):
                   ratio(m, "SQ_LDS_BANK_CONFLICT", "SQ_LDS_IDX_ACTIVE") for m in means) + " |",
               "| wave cycles in s_waitcnt | " + " | ".join(
                   ratio(m, "SQ_WAIT_INST_ANY", "SQ_WAVE_CYCLES") for m in means) + " |",
-              "", f"kernel_source_sha256: {kernel_source_hash()}", ""]
+              ""]
+    if "bwd" in args.kernel:
+        lines += [f"kernel_source_sha256: {kernel_source_hash()}", ""]
     _write(args.out, lines)
 
 
