@@ -230,12 +230,13 @@ def backward_intermediates(q, k, v, do, causal, scale: float | None = None):
     }
 
 
-def sampled_backward(q, k, v, do, causal, scale: float, rows_q, rows_kv):
+def sampled_backward(q, k, v, do, causal, scale: float, rows_q, rows_kv, with_forward=False):
     """One head ([N, d] inputs): the forward statistics for every row, then
     only the requested rows of the gradients, each from the same steps 1-9
     applied to one row of P (dQ_i) or one column of P (dK_j, dV_j).  Cost is
     one forward plus O(N d) per requested row, so full-length sequences can
-    be checked row by row.  Returns (dq[rows_q], dk[rows_kv], dv[rows_kv])."""
+    be checked row by row.  Returns (dq[rows_q], dk[rows_kv], dv[rows_kv]),
+    followed by (o[rows_q], lse[rows_q]) if with_forward."""
     q, k, v, do = _as64(q), _as64(k), _as64(v), _as64(do)
     o, lse = _head_forward(q, k, v, causal, scale)        # steps 1-4
     d_row = np.sum(do * o, axis=1)                        # step 5
@@ -261,4 +262,6 @@ def sampled_backward(q, k, v, do, causal, scale: float, rows_q, rows_kv):
         dp_j = do @ v[j]                                     # column j of dP
         ds_j = p_j * (dp_j - d_row)
         dk[t] = scale * (ds_j @ q)                           # step 9
+    if with_forward:
+        return dq, dk, dv, o[rows_q], lse[rows_q]
     return dq, dk, dv

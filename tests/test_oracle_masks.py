@@ -210,7 +210,10 @@ def test_masked_sampled_rows_match_whole_backward(case):
     q, k, v, do = (x[0, 0] for x in _inputs(n, 8, 171 + case))
     dq, dk, dv = A.backward(q[None, None], k[None, None], v[None, None], do[None, None], m, 0.3)
     rows = [0, 3, 4, 11, 12, 23]
-    sq, sk, sv = A.sampled_backward(q, k, v, do, m, 0.3, rows, rows[::-1])
+    sq, sk, sv, so, sl = A.sampled_backward(q, k, v, do, m, 0.3, rows, rows[::-1],
+                                            with_forward=True)
+    fo, fl = A.forward(q[None, None], k[None, None], v[None, None], m, 0.3)
+    assert np.array_equal(so, fo[0, 0, rows]) and np.array_equal(sl, fl[0, 0, rows])
     assert np.allclose(sq, dq[0, 0, rows], rtol=0, atol=1e-13)
     assert np.allclose(sk, dk[0, 0, rows[::-1]], rtol=0, atol=1e-13)
     assert np.allclose(sv, dv[0, 0, rows[::-1]], rtol=0, atol=1e-13)
