@@ -385,11 +385,21 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
         }
         // K tile row-major into LDS, then K^T fragments (d on lanes) for dQ.
         // sK's previous readers finished before several barriers since.
-        for (int c = tid; c < BC * D / VEC; c += NT) {
-          const int row = c / (D / VEC);
-          const int col = (c % (D / VEC)) * VEC;
-          *reinterpret_cast<uint4*>(&sK[qix(row, col)]) =
-              *reinterpret_cast<const uint4*>(Kg + (uint32_t)((kv0 + row) * D + col));
+        if constexpr (KPL == 8 && D == 64) {
+          // bf16: each lane's K fragments are 16-byte row chunks already
+          // (row 32w + l32, columns 16ks + 8h ..): write them out, no second
+          // read of K
+#pragma unroll
+          for (int ks = 0; ks < DK; ++ks)
+            *reinterpret_cast<uint4*>(&sK[qix(32 * w + l32, ks * KSTEP + hh * KPL)]) =
+                __builtin_bit_cast(uint4, Kreg[ks]);
+        } else {
+          for (int c = tid; c < BC * D / VEC; c += NT) {
+            const int row = c / (D / VEC);
+            const int col = (c % (D / VEC)) * VEC;
+            *reinterpret_cast<uint4*>(&sK[qix(row, col)]) =
+                *reinterpret_cast<const uint4*>(Kg + (uint32_t)((kv0 + row) * D + col));
+          }
         }
         __syncthreads();
 #pragma unroll
