@@ -183,17 +183,6 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_kernel(FwdArgs a) {
     a.lse[(size_t)head * N + qi] = l > 0.f ? (m + log2f(l)) * (1.0f / kLog2e) : -INFINITY;
 }
 
-// bf16 forward.  A workgroup owns 256 query rows: 4 waves x 64 rows (two
-// 32-query column tiles each), so every K / V fragment read from LDS feeds
-// two MFMAs.  Key and value tiles of 64 rows stay row-major in LDS (XOR
-// swizzled, double buffered) and are prefetched into registers one tile
-// ahead, so a tile costs one workgroup barrier.  S^T = K Q^T with K from LDS
-// (A operand) and Q^T in registers (B); O^T = V^T P^T with V^T from the
-// transposing LDS read (A) and P^T taken straight from the S^T accumulators
-// (B), their key order matching the accumulator's row order.  The query is
-// on lanes: row statistics need one exchange between the lane halves and
-// the rescale of O^T is a per-lane scalar.  Waves skip key tiles their rows
-// cannot see and mask elements only on tiles that cross a mask bound.
 // max(x of this lane, x of lane l ^ 32): v_permlane32_swap exchanges the
 // upper half of its first operand with the lower half of its second, so
 // with x in both the two results hold, per lane, x and the other half's x.
@@ -204,9 +193,20 @@ __device__ __forceinline__ float max_halves(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-template <int D, bool MASKED>
-__global__ void __launch_bounds__(256, 1) fwd_bf16_kernel(FwdArgs a) {
-  constexpr int NW = 4;
+// bf16 forward.  A workgroup owns NW x 64 query rows: NW waves x 64 rows
+// (two 32-query column tiles each), so every K / V fragment read from LDS
+// feeds two MFMAs.  Key and value tiles of 64 rows stay row-major in LDS (XOR
+// swizzled, double buffered) and are prefetched into registers one tile
+// ahead, so a tile costs one workgroup barrier.  S^T = K Q^T with K from LDS
+// (A operand) and Q^T in registers (B); O^T = V^T P^T with V^T from the
+// transposing LDS read (A) and P^T taken straight from the S^T accumulators
+// (B), their key order matching the accumulator's row order.  The query is
+// on lanes: row statistics need one exchange between the lane halves and
+// the rescale of O^T is a per-lane scalar.  Waves skip key tiles their rows
+// cannot see and mask elements only on tiles that cross a mask bound.
+template <int D, bool MASKED, int NW>
+__global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdArgs a) {
+  constexpr int NT = NW * 64;
   constexpr int QN = 2;                    // 32-query tiles per wave
   constexpr int WR = 32 * QN;              // query rows per wave
   constexpr int BM = NW * WR;              // query rows per workgroup
@@ -214,8 +214,8 @@ __global__ void __launch_bounds__(256, 1) fwd_bf16_kernel(FwdArgs a) {
   constexpr int DK = D / 16;               // MFMA steps over d
   constexpr int MT = BN / 32;              // 32-key tiles
   constexpr int MD = D / 32;               // 32-row tiles of O^T
-  constexpr int CPT = BN * D / 8 / 256;    // 16-byte chunks per thread per tensor
-  static_assert(CPT >= 1 && CPT * 8 * 256 == BN * D, "tile staging");
+  constexpr int CPT = BN * D / 8 / NT;     // 16-byte chunks per thread per tensor
+  static_assert(CPT >= 1 && CPT * 8 * NT == BN * D, "tile staging");
   __shared__ __align__(16) bf16_t sK[2][BN * D];
   __shared__ __align__(16) bf16_t sV[2][BN * D];
   // block-mask liveness of the (at most 2) query tiles this workgroup covers
@@ -245,7 +245,7 @@ __global__ void __launch_bounds__(256, 1) fwd_bf16_kernel(FwdArgs a) {
   // the tile liveness rows of this workgroup's query tiles (tile = 128 rows)
   const int qt0 = q0 / (MASKED ? a.tile : 1);
   if (MASKED && a.live) {
-    for (int i = tid; i < 2 * a.n_tiles; i += 256) {
+    for (int i = tid; i < 2 * a.n_tiles; i += NT) {
       const int r = qt0 + i / a.n_tiles;
       sLive[i] = r < a.n_tiles ? a.live[(size_t)r * a.n_tiles + i % a.n_tiles] : 0;
     }
@@ -269,8 +269,10 @@ __global__ void __launch_bounds__(256, 1) fwd_bf16_kernel(FwdArgs a) {
     return true;
   };
   const auto need_any = [&](int j) {
-    bool e;
-    return need(0, j, &e) || need(1, j, &e) || need(2, j, &e) || need(3, j, &e);
+    bool e, any = false;
+#pragma unroll
+    for (int v = 0; v < NW; ++v) any = any || need(v, j, &e);
+    return any;
   };
   int j_lo = 0, j_hi = N / BN;
   if (MASKED) {
@@ -318,7 +320,7 @@ __global__ void __launch_bounds__(256, 1) fwd_bf16_kernel(FwdArgs a) {
     const int k0 = j * BN;
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      const int c = tid + i * 256;
+      const int c = tid + i * NT;
       const size_t off = (size_t)(k0 + c / (D / 8)) * D + (c % (D / 8)) * 8;
       pk[i] = *reinterpret_cast<const u32x4*>(Kg + off);
       pv[i] = *reinterpret_cast<const u32x4*>(Vg + off);
@@ -327,7 +329,7 @@ __global__ void __launch_bounds__(256, 1) fwd_bf16_kernel(FwdArgs a) {
   const auto stage = [&](int buf) {
 #pragma unroll
     for (int i = 0; i < CPT; ++i) {
-      const int c = tid + i * 256;
+      const int c = tid + i * NT;
       const int o = kix(c / (D / 8), (c % (D / 8)) * 8);
       *reinterpret_cast<u32x4*>(&sK[buf][o]) = pk[i];
       *reinterpret_cast<u32x4*>(&sV[buf][o]) = pv[i];
@@ -492,13 +494,19 @@ __global__ void __launch_bounds__(256, 1) fwd_bf16_kernel(FwdArgs a) {
   }
 }
 
+// Block masks: workgroups of one query tile (2 waves, 128 rows), so the
+// waves of a workgroup see the same live key tiles; two such workgroups
+// share a compute unit.  Otherwise 4 waves, 256 rows.
 template <int D>
 static hipError_t go_fwd_bf16(bool masked, const FwdArgs& a, hipStream_t s) {
-  const long blocks = (long)((a.N + 255) / 256) * a.BH;
+  const int nw = a.live ? 2 : 4;
+  if (a.live && 64 * nw != a.tile) return hipErrorInvalidValue;
+  const long blocks = (long)((a.N + 64 * nw - 1) / (64 * nw)) * a.BH;
   if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
   dim3 grid((unsigned)blocks);
-  if (masked) hipLaunchKernelGGL((fwd_bf16_kernel<D, true>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((fwd_bf16_kernel<D, false>), grid, dim3(256), 0, s, a);
+  if (a.live) hipLaunchKernelGGL((fwd_bf16_kernel<D, true, 2>), grid, dim3(128), 0, s, a);
+  else if (masked) hipLaunchKernelGGL((fwd_bf16_kernel<D, true, 4>), grid, dim3(256), 0, s, a);
+  else hipLaunchKernelGGL((fwd_bf16_kernel<D, false, 4>), grid, dim3(256), 0, s, a);
   return hipGetLastError();
 }
 
