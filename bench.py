@@ -138,6 +138,9 @@ def main():
     ap.add_argument("--cpu-workers", type=int, default=16)
     ap.add_argument("--no-wait-stats", action="store_true",
                     help="skip the untimed instrumented launch per ordered schedule")
+    ap.add_argument("--tune", action="store_true",
+                    help="time naive/descending/shift first (dash_attn_bwd_tune) so that auto "
+                         "runs the measured fastest instead of the DAG model's pick")
     ap.add_argument("--no-fwd", action="store_true",
                     help="skip the forward and forward+backward timings")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
@@ -198,6 +201,14 @@ def main():
         D.attn_bwd(dev["q"], dev["k"], dev["v"], dev["do"], lse, delta, schedule=sched,
                    causal=causal, workspace=ws, out=(dq, dk, dv),
                    debug=None if events is None else {"kernel_events": events}, **mkw)
+
+    tuned = None
+    if args.tune:
+        D.attn_bwd_preprocess(o, dev["do"], out=delta)
+        pick, times = D.attn_bwd_tune(dev["q"], dev["k"], dev["v"], dev["do"], lse, delta,
+                                      causal=causal, reps=3, workspace=ws, out=(dq, dk, dv), **mkw)
+        tuned = {"choice": pick, "ms": {k: round(v, 4) for k, v in times.items()}}
+        print(f"[bench] tuned: {tuned}", file=sys.stderr, flush=True)
 
     results = {}
     for sched in scheds:
@@ -305,6 +316,8 @@ def main():
                        "kernel": f"bwd_kernel ({ran})"}
     if fwd_stats:
         out.update(fwd_stats)
+    if tuned:
+        out["tuned"] = tuned
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a sample of heads", file=sys.stderr, flush=True)
         out["cpu_baseline"] = cpu_baseline(exact, w, causal, args.cpu_workers)

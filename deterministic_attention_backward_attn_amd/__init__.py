@@ -21,7 +21,7 @@ from ._lib import DTYPES, SCHEDULES, DashError, Debug, Desc, check, header_symbo
 
 __all__ = [
     "DashError", "SCHEDULES", "attn_fwd", "attn_bwd_preprocess", "attn_bwd_workspace_size",
-    "attn_bwd", "attn_bwd_status", "backward", "schedule_tables", "schedule_predict", "schedule_choose",
+    "attn_bwd", "attn_bwd_status", "attn_bwd_tune", "backward", "schedule_tables", "schedule_predict", "schedule_choose",
     "resolve_schedule", "mask_schedule_tables", "mask_schedule_predict",
     "dag_longest_path", "litmus_ordered_add", "tile", "subtile", "header_symbols", "load",
 ]
@@ -232,6 +232,34 @@ def attn_bwd(q, k, v, do, lse, delta, *, schedule="naive", causal=False, scale=N
         check(lib.dash_attn_bwd_debug(*args, ctypes.byref(dbg), _stream(stream)),
               "dash_attn_bwd_debug")
     return dq, dk, dv
+
+
+def attn_bwd_tune(q, k, v, do, lse, delta, *, causal=False, scale=None, reps=3, workspace=None,
+                  out=None, stream=None, window=0, block_mask=None, block_size=0):
+    """Time naive, descending and shift on these inputs and record the
+    fastest for "auto" launches of this shape (see dash_attn_bwd_tune).
+    Returns (name, {name: ms per launch}); overwrites `out` (or scratch
+    outputs) and the workspace."""
+    torch = _torch()
+    lib = load()
+    _same_shape(q, k, v, do)
+    desc = _desc_from(q, causal, scale, window, block_mask, block_size)
+    if workspace is None:
+        workspace = alloc_workspace(q, causal, "auto")
+    if out is None:
+        out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    dq, dk, dv = out
+    _same_shape(q, dq, dk, dv)
+    choice = ctypes.c_int(-1)
+    t = (ctypes.c_float * 3)()
+    check(lib.dash_attn_bwd_tune(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(do),
+                                 _ptr(lse), _ptr(delta), _ptr(dq), _ptr(dk), _ptr(dv),
+                                 _ptr(workspace),
+                                 ctypes.c_size_t(workspace.numel() * workspace.element_size()),
+                                 int(reps), ctypes.byref(choice), t, _stream(stream)),
+          "dash_attn_bwd_tune")
+    names = {v: k for k, v in SCHEDULES.items()}
+    return names[choice.value], {"naive": t[0], "descending": t[1], "shift": t[2]}
 
 
 def attn_bwd_status(workspace, stream=None):

@@ -567,6 +567,82 @@ dash_status dash_attn_bwd_debug(const dash_attn_desc* desc, dash_schedule schedu
                  workspace_bytes, dbg, stream);
 }
 
+dash_status dash_attn_bwd_tune(const dash_attn_desc* desc, const void* q, const void* k,
+                              const void* v, const void* dout, const float* lse,
+                              const float* delta, void* dq, void* dk, void* dv, void* workspace,
+                              size_t workspace_bytes, int32_t reps, dash_schedule* choice,
+                              float* times_ms, void* stream) {
+  dash_status st = check_desc(desc);
+  if (st != DASH_OK) return st;
+  if (reps < 1 || reps > 1000 || !choice) return DASH_ERR_INVALID_ARG;
+  if (!q || !k || !v || !dout || !lse || !delta || !dq || !dk || !dv || !workspace)
+    return DASH_ERR_INVALID_ARG;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return DASH_ERR_HIP;
+  const MaskKey mkey = mask_key(desc);
+  const DevMask* dm = nullptr;
+  st = get_mask(dev, mkey, &dm);
+  if (st != DASH_OK) return st;
+  int maxco = 0;
+  st = get_coresident(dev, desc->dtype, desc->d, dm->host.any_partial(), true, &maxco);
+  if (st != DASH_OK) return st;
+  hipStream_t strm = (hipStream_t)stream;
+  hipEvent_t ev[2];
+  if (hipEventCreate(&ev[0]) != hipSuccess) return DASH_ERR_HIP;
+  if (hipEventCreate(&ev[1]) != hipSuccess) {
+    (void)hipEventDestroy(ev[0]);
+    return DASH_ERR_HIP;
+  }
+  const dash_schedule cand[3] = {DASH_SCHED_NAIVE, DASH_SCHED_DESCENDING, DASH_SCHED_SHIFT};
+  float t[3];
+  int best = -1;
+  for (int i = 0; i < 3 && st == DASH_OK; ++i) {
+    t[i] = NAN;
+    Tables tb;
+    if (!dash::build_tables(dm->host, (Sched)cand[i], tb)) continue;
+    if (tb.needs_static() && tb.units() > maxco) continue;
+    // one untimed launch, then `reps` timed ones
+    st = run_bwd(desc, cand[i], q, k, v, dout, lse, delta, dq, dk, dv, workspace, workspace_bytes,
+                 nullptr, stream);
+    if (st == DASH_ERR_UNSUPPORTED) {  // e.g. a unit longer than the kernel's work list
+      st = DASH_OK;
+      continue;
+    }
+    if (st != DASH_OK) break;
+    if (hipEventRecord(ev[0], strm) != hipSuccess) st = DASH_ERR_HIP;
+    for (int r = 0; r < reps && st == DASH_OK; ++r)
+      st = run_bwd(desc, cand[i], q, k, v, dout, lse, delta, dq, dk, dv, workspace,
+                   workspace_bytes, nullptr, stream);
+    if (st != DASH_OK) break;
+    if (hipEventRecord(ev[1], strm) != hipSuccess || hipEventSynchronize(ev[1]) != hipSuccess) {
+      st = DASH_ERR_HIP;
+      break;
+    }
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, ev[0], ev[1]) != hipSuccess) {
+      st = DASH_ERR_HIP;
+      break;
+    }
+    t[i] = ms / reps;
+    if (best < 0 || t[i] < t[best]) best = i;
+  }
+  (void)hipEventDestroy(ev[0]);
+  (void)hipEventDestroy(ev[1]);
+  if (st != DASH_OK) return st;
+  // a time-out of an ordered add would make the times meaningless
+  st = dash_attn_bwd_status(workspace, stream);
+  if (st != DASH_OK) return st;
+  if (best < 0) return DASH_ERR_UNSUPPORTED;
+  {
+    const int h = (int)std::min<long>((long)desc->B * desc->H, 1L << 30);
+    std::lock_guard<std::mutex> lock(g_mu);
+    g_auto[std::make_tuple(mkey, h, maxco)] = (Sched)cand[best];
+  }
+  *choice = cand[best];
+  if (times_ms) std::memcpy(times_ms, t, sizeof(t));
+  return DASH_OK;
+}
+
 dash_status dash_attn_bwd_status(const void* workspace, void* stream) {
   if (!workspace) return DASH_ERR_INVALID_ARG;
   if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return DASH_ERR_HIP;

@@ -287,6 +287,26 @@ dash_status dash_schedule_choose(int32_t n, int32_t causal, int32_t heads, int32
                                  const double* cost, dash_schedule* choice, double* predicted);
 
 /*
+ * Profiling-driven schedule choice (the summary's limitations list runtime
+ * profiling-based adaptive selection as future work; the DAG model's pick
+ * is the default).  Runs NAIVE, DESCENDING and SHIFT (those that can run)
+ * once untimed and `reps` times timed (1..1000) on the given buffers,
+ * exactly as dash_attn_bwd would (dq, dk, dv and the workspace are
+ * overwritten; their final contents are those of the last schedule run),
+ * times each with HIP events on `stream`, and records the fastest for this
+ * shape and mask on the current device: later DASH_SCHED_AUTO launches of
+ * the same shape run it.  Blocking: waits for `stream`.  *choice receives
+ * the pick; times_ms[3] (may be NULL) the mean time per launch of NAIVE,
+ * DESCENDING, SHIFT (NaN where a schedule cannot run).  Errors as
+ * dash_attn_bwd, DASH_ERR_ORDER_TIMEOUT if an ordered add timed out.
+ */
+dash_status dash_attn_bwd_tune(const dash_attn_desc* desc, const void* q, const void* k,
+                              const void* v, const void* dout, const float* lse,
+                              const float* delta, void* dq, void* dk, void* dv, void* workspace,
+                              size_t workspace_bytes, int32_t reps, dash_schedule* choice,
+                              float* times_ms, void* stream);
+
+/*
  * The schedule dash_attn_bwd runs for `schedule` on the current device:
  * DASH_SCHED_AUTO resolves to dash_schedule_choose's pick for the
  * problem's tile count, B*H heads and the launch's co-resident workgroups;

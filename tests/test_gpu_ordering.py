@@ -242,3 +242,23 @@ def test_unit_order_changes_no_bit(causal):
             out = _bwd(dev, lse, delta, sched, causal, debug={"unit_order": order})
             for x, y in zip(ref, out):
                 assert torch.equal(x.view(torch.int16), y.view(torch.int16)), (sched, order)
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_tune_records_the_fastest_for_auto(causal):
+    """Profiling-driven choice: the timed pick is the fastest candidate, and
+    later "auto" launches of the shape run it (bit-identical)."""
+    require_gpu()
+    B, H, N, d = 1, 16, 2048, 128
+    log(f"tune causal={causal}")
+    dev, lse, delta = _prep(B, H, N, d, "bf16", causal, 8400)
+    picked, times = D.attn_bwd_tune(dev["q"], dev["k"], dev["v"], dev["do"], lse, delta,
+                                    causal=causal, reps=3)
+    log(f"  times {times} -> {picked}")
+    finite = {k: v for k, v in times.items() if v == v}
+    assert picked == min(finite, key=finite.get)
+    assert D.resolve_schedule(B, H, N, d, "bf16", causal, "auto") == picked
+    ref = _bwd(dev, lse, delta, picked, causal)
+    out = _bwd(dev, lse, delta, "auto", causal)
+    for x, y in zip(ref, out):
+        assert torch.equal(x.view(torch.int16), y.view(torch.int16))

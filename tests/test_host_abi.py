@@ -209,6 +209,11 @@ def test_argument_errors_without_launch():
     assert lib.dash_schedule_choose(8, 2, 1, 1, None, ctypes.byref(choice), None) == 1
     assert lib.dash_schedule_choose(8, 0, 1, 0, None, ctypes.byref(choice), None) == 1
     assert lib.dash_schedule_choose(8, 0, 1, 8, None, None, None) == 1
+    tune_args = [FAKE] * 10 + [ws_ok]
+    assert lib.dash_attn_bwd_tune(None, *tune_args, 3, ctypes.byref(choice), None, None) == 1
+    assert lib.dash_attn_bwd_tune(ctypes.byref(desc), *tune_args, 0, ctypes.byref(choice), None,
+                                  None) == 1
+    assert lib.dash_attn_bwd_tune(ctypes.byref(desc), *tune_args, 3, None, None, None) == 1
     assert lib.dash_attn_bwd_resolve_schedule(None, 4, ctypes.byref(choice)) == 1
     assert lib.dash_attn_bwd_resolve_schedule(ctypes.byref(desc), 5, ctypes.byref(choice)) == 1
     assert lib.dash_attn_bwd_resolve_schedule(ctypes.byref(desc), 4, None) == 1
