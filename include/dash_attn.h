@@ -3,9 +3,10 @@
  * (CDNA4, gfx950).
  *
  * What the library computes.  For each (batch b, head h), softmax attention
- * O = softmax(s * Q K^T) V with an optional causal mask (query i sees keys
- * j <= i), its log-sum-exp LSE, and the backward pass: given Q, K, V, O,
- * dO and LSE it returns dQ, dK, dV.  The inputs and outputs of the backward
+ * O = softmax(s * Q K^T) V with an optional mask (causal: query i sees keys
+ * j <= i; also sliding windows and block masks, see dash_attn_desc), its
+ * log-sum-exp LSE, and the backward pass: given Q, K, V, O, dO and LSE it
+ * returns dQ, dK, dV.  The inputs and outputs of the backward
  * are those of the problem statement of the DASH explainer (gist.science,
  * "Technisches Resuemee" 1) and of the method outline of the euno.news
  * summary ("Methodology" 1: the backward's matrix products, score
@@ -27,6 +28,10 @@
  *               KV tiles w and n-1-w in one workgroup, two phases.  dQ order
  *               = the step at which each tile reaches the block.
  *   ATOMIC      NAIVE's traversal, unordered fp32 atomic adds.
+ *   AUTO        the ordered schedule the DAG model predicts fastest (or the
+ *               one dash_attn_bwd_tune measured fastest for the shape).
+ * With a window or block mask the same rules run over the tile pairs that
+ * hold a visible key; SHIFT becomes a proper colouring of those pairs.
  *
  * Conventions for every call below.
  *   Layout      Q, K, V, O, dO, dQ, dK, dV: contiguous [B, H, N, d], d
@@ -48,9 +53,11 @@
  *               launch.  HIP launch errors return DASH_ERR_HIP.  A device
  *               ordering time-out is reported by dash_attn_bwd_status.
  *   Memory      dash_attn_bwd keeps a per-device cache of schedule tables
- *               (allocated on first use of a shape/schedule, a few hundred
- *               KB at most, held until the process ends).  Everything else
- *               lives in caller buffers.
+ *               (allocated on first use of a shape/schedule/mask, a few
+ *               hundred KB at most for full and causal masks, up to tens
+ *               of MB for windows and block masks at 2048 tiles per side,
+ *               held until the process ends).  Everything else lives in
+ *               caller buffers.
  *   Threads     Calls may come from several host threads; the table cache
  *               is locked.  Calls that share a workspace must be ordered
  *               on one stream.
