@@ -151,3 +151,22 @@ def test_block_mask_unit_order_changes_no_bit():
                 continue
             for x, y in zip(ref, out):
                 assert torch.equal(x.view(torch.int16), y.view(torch.int16)), (sched, order)
+
+
+@pytest.mark.parametrize("sched", ["atomic", "naive", "descending", "shift", "auto"])
+def test_mask_that_hides_everything(sched):
+    """No visible pair at all: O = 0, LSE = -inf, and every gradient is
+    exactly zero (no unit runs; the cleared tiles are all of them)."""
+    require_gpu()
+    B, H, N, d = 1, 2, 512, 128
+    blk = np.zeros((4, 4), dtype=bool)
+    dev, _ = device_inputs(B, H, N, d, "bf16", 6100)
+    o, lse = D.attn_fwd(dev["q"], dev["k"], dev["v"], causal=True, block_mask=blk)
+    assert torch.all(o.float() == 0) and torch.all(torch.isneginf(lse))
+    delta = D.attn_bwd_preprocess(o, dev["do"])
+    outs = tuple(torch.full_like(dev["q"], 3.0) for _ in range(3))
+    D.attn_bwd(dev["q"], dev["k"], dev["v"], dev["do"], lse, delta, schedule=sched, causal=True,
+               block_mask=blk, out=outs)
+    torch.cuda.synchronize()
+    for t in outs:
+        assert torch.all(t.float() == 0)

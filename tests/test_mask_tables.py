@@ -224,3 +224,23 @@ def test_unit_major_order_on_a_block_sparse_mask():
     um = D.mask_schedule_predict(1, 4, 4096, 128, "bf16", True, "descending", slots=32, cost=cost,
                                  unit_major=True)[0]
     assert um <= hm * 1.0001
+
+
+def test_table_export_protocol():
+    """Two-call export: sizes first; arrays of other sizes are refused."""
+    import ctypes
+    lib = D.load()
+    desc = D._desc(1, 1, 512, 64, "f32", True, None, 100)
+    sizes = (ctypes.c_int32 * 3)()
+    assert lib.dash_attn_schedule_tables(ctypes.byref(desc), 2, sizes, None, None, None, None,
+                                         None, None) == 0
+    n, nu, ni = sizes[0], sizes[1], sizes[2]
+    assert n == 8 and nu == 8 and ni > 0
+    arr = lambda m: (ctypes.c_int32 * max(m, 1))()
+    bad = (ctypes.c_int32 * 3)(n, nu, ni + 1)
+    assert lib.dash_attn_schedule_tables(ctypes.byref(desc), 2, bad, arr(nu + 1), arr(ni),
+                                         arr(ni), arr(ni), (ctypes.c_uint8 * ni)(),
+                                         arr(n * n)) == 1
+    assert lib.dash_attn_schedule_tables(ctypes.byref(desc), 9, sizes, None, None, None, None,
+                                         None, None) == 1
+    assert lib.dash_attn_schedule_tables(None, 2, sizes, None, None, None, None, None, None) == 1
