@@ -311,10 +311,11 @@ def mask_schedule_tables(B, H, N, d, dtype="bf16", causal=False, schedule="naive
     """The backward's tables for a masked problem.  Returns a dict: n
     (tiles per side), units (per unit [(kv, q), ...]), steps (per unit, the
     lockstep step of each item; SHIFT only, else None), partial (per unit,
-    per item bool), rank (int32 [n, n], rank[q, kv], -1 where absent)."""
+    per item bool), rank (int32 [n, n], rank[q, kv], -1 where absent),
+    static (units run in head-aligned rounds)."""
     lib = load()
     desc = _desc(B, H, N, d, dtype, causal, None, window, block_mask, block_size)
-    sizes = (ctypes.c_int32 * 3)()
+    sizes = (ctypes.c_int32 * 4)()
     check(lib.dash_attn_schedule_tables(ctypes.byref(desc), _sched(schedule), sizes, None, None,
                                         None, None, None, None), "dash_attn_schedule_tables")
     n, nu, ni = sizes[0], sizes[1], sizes[2]
@@ -338,7 +339,7 @@ def mask_schedule_tables(B, H, N, d, dtype="bf16", causal=False, schedule="naive
         partial.append([bool(pa[i]) for i in sl])
     shift = _sched(schedule) == SCHEDULES["shift"]
     return {"n": n, "units": units, "steps": steps if shift else None, "partial": partial,
-            "rank": rank.reshape(n, n)}
+            "rank": rank.reshape(n, n), "static": bool(sizes[3])}
 
 
 def mask_schedule_predict(B, H, N, d, dtype="bf16", causal=False, schedule="naive", *, slots,

@@ -728,7 +728,7 @@ dash_status dash_schedule_choose(int32_t n, int32_t causal, int32_t heads, int32
 }
 
 dash_status dash_attn_schedule_tables(const dash_attn_desc* desc, dash_schedule schedule,
-                                      int32_t sizes[3], int32_t* unit_offsets, int32_t* item_kv,
+                                      int32_t sizes[4], int32_t* unit_offsets, int32_t* item_kv,
                                       int32_t* item_q, int32_t* item_step, uint8_t* item_partial,
                                       int32_t* rank) {
   dash_status st = check_desc(desc);
@@ -745,6 +745,7 @@ dash_status dash_attn_schedule_tables(const dash_attn_desc* desc, dash_schedule 
   sizes[0] = t.n;
   sizes[1] = t.units();
   sizes[2] = t.items();
+  sizes[3] = t.needs_static() ? 1 : 0;
   if (!fill) return DASH_OK;
   std::memcpy(unit_offsets, t.unit_off.data(), sizeof(int) * t.unit_off.size());
   if (t.items()) {

@@ -20,6 +20,7 @@
 #include "schedule.hpp"
 
 #include <algorithm>
+#include <queue>
 #include <array>
 #include <tuple>
 
@@ -135,6 +136,64 @@ void colour_units(const TileMask& m, Tables& t) {
   }
 }
 
+// If the units' waits (a unit waits for the unit ranked just before it at
+// each of its Q blocks) form no cycle, order the units so that every wait
+// points to an earlier unit (a topological order, earliest first step
+// first): a work counter can then hand them out with no deadlock and no
+// need for a whole head to be resident.  Otherwise the tables stay static.
+void order_for_dynamic(Tables& t) {
+  const int n = t.n, U = t.units();
+  std::vector<int> unit_of_item(t.items());
+  for (int u = 0; u < U; ++u)
+    for (int i = t.unit_off[u]; i < t.unit_off[u + 1]; ++i) unit_of_item[i] = u;
+  std::vector<int> pos((size_t)n * n, -1);
+  for (int i = 0; i < t.items(); ++i) pos[(size_t)t.q[i] * n + t.kv[i]] = i;
+  std::vector<std::vector<int>> succ(U);
+  std::vector<int> indeg(U, 0);
+  for (int q = 0; q < n; ++q) {
+    std::vector<int> by_rank(n, -1);
+    for (int kv = 0; kv < n; ++kv) {
+      const int r = t.rank[(size_t)q * n + kv];
+      if (r >= 0) by_rank[r] = pos[(size_t)q * n + kv];
+    }
+    for (int r = 1; r < n && by_rank[r] >= 0; ++r) {
+      const int a = unit_of_item[by_rank[r - 1]], b = unit_of_item[by_rank[r]];
+      if (a != b) {
+        succ[a].push_back(b);
+        ++indeg[b];
+      }
+    }
+  }
+  typedef std::pair<int, int> Key;  // (first step, unit)
+  std::priority_queue<Key, std::vector<Key>, std::greater<Key>> ready;
+  for (int u = 0; u < U; ++u)
+    if (!indeg[u]) ready.push(Key(t.step[t.unit_off[u]], u));
+  std::vector<int> order;
+  while (!ready.empty()) {
+    const int u = ready.top().second;
+    ready.pop();
+    order.push_back(u);
+    for (int v : succ[u])
+      if (--indeg[v] == 0) ready.push(Key(t.step[t.unit_off[v]], v));
+  }
+  if ((int)order.size() != U) return;  // cyclic: keep head-aligned rounds
+  Tables r = t;
+  r.unit_off.assign(1, 0);
+  r.kv.clear();
+  r.q.clear();
+  r.step.clear();
+  for (int u : order) {
+    for (int i = t.unit_off[u]; i < t.unit_off[u + 1]; ++i) {
+      r.kv.push_back(t.kv[i]);
+      r.q.push_back(t.q[i]);
+      r.step.push_back(t.step[i]);
+    }
+    r.unit_off.push_back((int)r.kv.size());
+  }
+  r.static_policy = false;
+  t = std::move(r);
+}
+
 }  // namespace
 
 bool TileMask::any_partial() const {
@@ -201,6 +260,7 @@ bool build_tables(const TileMask& m, Sched s, Tables& t) {
   t.n = n;
   t.causal = m.causal;
   t.sched = s;
+  t.static_policy = s == Sched::Shift;
   if (n < 1) return false;
   t.live = m.live;
   t.partial = m.partial;
@@ -222,7 +282,10 @@ bool build_tables(const TileMask& m, Sched s, Tables& t) {
   }
   b.finish();
   if (s == Sched::Naive || s == Sched::Descending) ranks_by_kv(t);
-  else if (s == Sched::Shift) ranks_by_step(t);
+  else if (s == Sched::Shift) {
+    ranks_by_step(t);
+    order_for_dynamic(t);
+  }
   return true;
 }
 
@@ -231,6 +294,7 @@ bool build_tables(int n, bool causal, Sched s, Tables& t) {
   t.n = n;
   t.causal = causal;
   t.sched = s;
+  t.static_policy = s == Sched::Shift;
   if (n < 1) return false;
   {
     TileMask pm = plain_mask(n, causal);

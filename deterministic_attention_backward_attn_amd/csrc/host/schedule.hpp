@@ -54,11 +54,14 @@ struct Tables {
   std::vector<int> q;         // [items]
   std::vector<int> step;      // [items] lockstep step of each item (SHIFT), else empty
   std::vector<int> rank;      // [n * n], -1 where absent or unordered
+  // Units must be taken in head-aligned rounds (some wait points to a later
+  // unit).  SHIFT on a window or block mask clears it when its units could
+  // be ordered so that every wait points to an earlier one.
+  bool static_policy = false;
   int units() const { return (int)unit_off.size() - 1; }
   int items() const { return (int)kv.size(); }
   bool ordered() const { return sched != Sched::Atomic; }
-  // Units must be taken in head-aligned rounds (waits point to later units).
-  bool needs_static() const { return sched == Sched::Shift; }
+  bool needs_static() const { return static_policy; }
 };
 
 // Returns false when the schedule is undefined for (n, causal): symmetric

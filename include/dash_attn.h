@@ -327,18 +327,22 @@ dash_status dash_attn_bwd_resolve_schedule(const dash_attn_desc* desc, dash_sche
  * The backward's schedule tables for any descriptor (any mask), host only:
  * the same tables dash_attn_bwd runs (after DASH_SCHED_AUTO resolution).
  * Two calls: with any array NULL, fills sizes = {n tiles per side, units,
- * items} and returns; then with arrays of those sizes (sizes unchanged):
+ * items, static} and returns (static = 1: units run in head-aligned rounds,
+ * a whole head resident; 0: from a work counter in unit order); then with
+ * arrays of those sizes (sizes unchanged):
  * unit_offsets[units + 1], item_kv/item_q/item_step/item_partial[items]
  * (step: lockstep step for SHIFT, else -1; partial: the pair has hidden
  * elements) and rank[n * n] (rank[q * n + kv], -1 where absent).  SHIFT on
  * a window or block mask is a proper colouring of the live pairs: no unit
  * and no Q block holds two pairs at one step (the shift's defining
  * property, explainer 2.2 B), with as many steps as the busiest tile has
- * pairs.  Tile pairs that hold no visible key are left out; KV tiles with
- * none get no unit.
+ * pairs; when the units can be ordered so that every wait points to an
+ * earlier unit, they are, and run from a work counter (static = 0).  Tile
+ * pairs that hold no visible key are left out; KV tiles with none get no
+ * unit.
  */
 dash_status dash_attn_schedule_tables(const dash_attn_desc* desc, dash_schedule schedule,
-                                      int32_t sizes[3], int32_t* unit_offsets, int32_t* item_kv,
+                                      int32_t sizes[4], int32_t* unit_offsets, int32_t* item_kv,
                                       int32_t* item_q, int32_t* item_step, uint8_t* item_partial,
                                       int32_t* rank);
 

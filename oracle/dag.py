@@ -100,7 +100,8 @@ def realize(schedule, n, causal, heads, slots, cost, tables=None, unit_major=Fal
     ``tables`` (optional) gives one head's tables explicitly, for masks the
     oracle does not construct itself: {"units": [[(kv, q), ...], ...],
     "rank": rank[q][kv] (None or negative where absent; None for ATOMIC),
-    "partial": set of (kv, q) pairs costed c_diag}.
+    "partial": set of (kv, q) pairs costed c_diag, optional "static": whether
+    the units run in head-aligned rounds (default: SHIFT only)}.
 
     Returns dict with 'weights', 'edges', 'assign' (unit -> slot),
     'units' (global unit list of item lists, each item (head, kv, q)) and
@@ -119,7 +120,9 @@ def realize(schedule, n, causal, heads, slots, cost, tables=None, unit_major=Fal
         icost = _item_costs(causal, cost, tables["partial"])
     U = len(per_head)
     glob = []
-    if unit_major and _policy(schedule) == "dynamic":
+    dynamic = (_policy(schedule) == "dynamic" if tables is None or "static" not in tables
+               else not tables["static"])
+    if unit_major and dynamic:
         # all heads' first units, then all heads' second units, ...
         for items in per_head:
             for hd in range(heads):
@@ -149,6 +152,8 @@ def realize(schedule, n, causal, heads, slots, cost, tables=None, unit_major=Fal
                     order_edges.append((r_node[(hd, kv0, q)], r_node[(hd, kv1, q)], cost[3]))
 
     policy = _policy(schedule)
+    if tables is not None and "static" in tables:
+        policy = "static" if tables["static"] else "dynamic"
     assign = [None] * len(glob)
     sim_finish = None
     if policy == "static":

@@ -195,10 +195,13 @@ def masked_rank_table(live_t):
     return rank
 
 
-def check_step_schedule(live_t, unit_items, steps, rank):
+def check_step_schedule(live_t, unit_items, steps, rank, dynamic=False):
     """Validate a SHIFT table for a general tile graph.  unit_items: per unit
     [(kv, q), ...] in run order; steps: per unit the step of each item;
-    rank[q][kv].  Returns '' or the first rule broken."""
+    rank[q][kv].  dynamic: the units are handed out in list order by a work
+    counter, so every wait (an item waits for the item ranked just before
+    it at its Q block) must point to an earlier unit.  Returns '' or the
+    first rule broken."""
     n = len(live_t)
     deg_kv = [sum(1 for q in range(n) if live_t[q][kv]) for kv in range(n)]
     deg_q = [sum(1 for kv in range(n) if live_t[q][kv]) for q in range(n)]
@@ -232,4 +235,8 @@ def check_step_schedule(live_t, unit_items, steps, rank):
         for kv in range(n):
             if not live_t[q][kv] and rank[q][kv] is not None:
                 return "rank for a dead pair"
+        if dynamic:
+            for (_, kv0), (_, kv1) in zip(contrib, contrib[1:]):
+                if owner[kv0] > owner[kv1]:
+                    return "a wait points to a later unit under a work counter"
     return ""

@@ -71,7 +71,7 @@ def test_masked_tables_against_oracle(case, schedule):
     if schedule == "shift":
         assert OS.check_step_schedule(live, t["units"], t["steps"],
                                       [[None if r < 0 else int(r) for r in row]
-                                       for row in t["rank"]]) == ""
+                                       for row in t["rank"]], dynamic=not t["static"]) == ""
         return
     want_units = [u for u in OS.masked_units(schedule, live) if u]
     assert t["units"] == want_units
@@ -107,9 +107,13 @@ def test_causal_band_shift_runs_each_tile_in_query_order():
         qs = [q for _, q in items]
         assert qs == sorted(qs)
     live, _ = OS.tile_liveness(A.Mask(causal=True, window=w), N // T, T)
+    # a KV tile waits only for the next one at each block: the units order
+    # (last tile first) so that a work counter can hand them out
+    assert not t["static"]
+    assert [items[0][0] for items in t["units"]] == list(range(N // T - 1, -1, -1))
     assert OS.check_step_schedule(live, t["units"], t["steps"],
                                   [[None if r < 0 else int(r) for r in row]
-                                   for row in t["rank"]]) == ""
+                                   for row in t["rank"]], dynamic=True) == ""
 
 
 def test_step_checker_catches_broken_tables():
@@ -122,6 +126,9 @@ def test_step_checker_catches_broken_tables():
     bad_steps = [list(s) for s in t["steps"]]
     bad_steps[1][0] = bad_steps[0][0] if t["units"][1][0][1] == t["units"][0][0][1] else -1
     assert OS.check_step_schedule(live, t["units"], bad_steps, rank) != ""
+    # the same units handed out in the opposite order break the counter rule
+    assert OS.check_step_schedule(live, t["units"][::-1], t["steps"][::-1], rank,
+                                  dynamic=True) != ""
     bad_rank = [list(r) for r in rank]
     q = t["units"][2][0][1]
     kvs = [kv for kv in range(n) if bad_rank[q][kv] is not None]
@@ -158,10 +165,11 @@ def test_masked_predict_matches_oracle_dag(case, schedule):
     tables = {"units": t["units"],
               "rank": None if schedule == "atomic" else t["rank"].tolist(),
               "partial": {it for items, fl in zip(t["units"], t["partial"])
-                          for it, f in zip(items, fl) if f}}
+                          for it, f in zip(items, fl) if f},
+              "static": t["static"]}
     cost = (1.0, 0.6, 0.2, 0.1)
     heads = 3
-    slots = max(len(t["units"]), 5) if schedule == "shift" else 5
+    slots = max(len(t["units"]), 5) if t["static"] else 5
     for um in (False, True):
         got = D.mask_schedule_predict(1, heads, N, 64, "f32", causal, schedule, slots=slots,
                                       cost=cost, unit_major=um, **kw)
@@ -231,13 +239,13 @@ def test_table_export_protocol():
     import ctypes
     lib = D.load()
     desc = D._desc(1, 1, 512, 64, "f32", True, None, 100)
-    sizes = (ctypes.c_int32 * 3)()
+    sizes = (ctypes.c_int32 * 4)()
     assert lib.dash_attn_schedule_tables(ctypes.byref(desc), 2, sizes, None, None, None, None,
                                          None, None) == 0
     n, nu, ni = sizes[0], sizes[1], sizes[2]
     assert n == 8 and nu == 8 and ni > 0
     arr = lambda m: (ctypes.c_int32 * max(m, 1))()
-    bad = (ctypes.c_int32 * 3)(n, nu, ni + 1)
+    bad = (ctypes.c_int32 * 4)(n, nu, ni + 1, 0)
     assert lib.dash_attn_schedule_tables(ctypes.byref(desc), 2, bad, arr(nu + 1), arr(ni),
                                          arr(ni), arr(ni), (ctypes.c_uint8 * ni)(),
                                          arr(n * n)) == 1
