@@ -282,6 +282,11 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
     // them out of the buffer's range (they return 0 and touch no memory)
     auto load_acc = [&](bool live) {
       const int q0 = p_qtile * BR;
+      // L2-coherent loads may hit this CU's L1: drop every line read before
+      // other workgroups updated it, right before the reads (an add can run
+      // after the next KV tile has started, and a unit may visit a Q
+      // sub-tile again under a later KV tile)
+      if (xl && live) l1_invalidate();
 #pragma unroll
       for (int i = 0; i < QT; ++i)
 #pragma unroll
@@ -372,10 +377,6 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
       if (kv != cur_kv) {
         if (cur_kv >= 0) flush_dkdv();
         cur_kv = kv;
-        // L2-coherent accumulator accesses may hit this CU's L1: drop lines
-        // it read for earlier KV tiles, which other CUs have updated since
-        // (within one KV tile every Q sub-tile is visited once)
-        if (xl) l1_invalidate();
         const int kv0 = kv * BC;
 #pragma unroll
         for (int ks = 0; ks < DK; ++ks) {
