@@ -37,6 +37,8 @@ sys.path.insert(0, ROOT)
 
 METRIC = "deterministic attn-bwd TFLOP/s + % bf16 MFMA peak; det/non-det throughput ratio"
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense MFMA (bf16), fp32 MFMA
+# the library's default DAG costs: full item, partial item, dQ add, hand-off
+DAG_COST = (1.0, 0.5, 0.05, 0.05)
 def kernel_source_hash() -> str:
     """Hash of the backward kernel's sources and build flags, as recorded in
     the committed traffic summaries."""
@@ -119,6 +121,32 @@ def order_wait(D, dev, lse, delta, sched, causal, ws, out, mkw):
     wait, waits, spun, busy = (float(a[:, i].sum()) for i in range(4))
     return {"order_wait_frac": wait / max(busy, 1.0), "order_adds": int(waits),
             "order_polled_frac": spun / max(waits, 1.0)}
+
+
+def dag_prediction(D, w, causal, sched, mkw, coresident):
+    """The host DAG model's view of one ordered schedule on this workload:
+    predicted makespan and its lower bound (in units of one full item) and
+    the predicted share of slot time spent waiting for ordered-add turns,
+    with the library's default costs (full item 1, partial item 0.5, dQ add
+    0.05, hand-off 0.05).  Heads and co-resident workgroups are divided by
+    the same power of two until the graph holds at most 1e6 items, which
+    keeps the heads per round of the static schedules as in the launch
+    (None if the sample cannot hold one head's static round)."""
+    n = w.N // D.tile(w.B, w.H, w.N, w.d, w.dtype)
+    items = n * (n + 1) // 2 if causal else n * n
+    heads = w.B * w.H
+    m = 1
+    while (heads // m) * items > 1000000 and heads % (2 * m) == 0 and coresident % (2 * m) == 0:
+        m *= 2
+    hp, slots = heads // m, coresident // m
+    try:
+        mk, wait, _, lb = D.mask_schedule_predict(1, hp, w.N, w.d, w.dtype, causal, sched,
+                                                  slots=slots, cost=DAG_COST, **mkw)
+    except D.DashError:
+        return None
+    return {"makespan_items": round(mk, 1), "lower_bound_items": round(lb, 1),
+            "wait_frac": round(wait / (slots * mk), 4) if mk > 0 else 0.0,
+            "heads": hp, "slots": slots}
 
 
 # ------------------------------------------------------------------ main
@@ -236,6 +264,10 @@ def main():
         if sched not in ("atomic", "auto") and not args.no_wait_stats:
             results[sched].update(order_wait(D, dev, lse, delta, sched, causal, ws, (dq, dk, dv),
                                              mkw))
+        if sched not in ("atomic", "auto"):
+            results[sched]["dag"] = dag_prediction(D, w, causal, sched, mkw,
+                                                   torch.cuda.get_device_properties(0)
+                                                   .multi_processor_count)
         print(f"[bench] {sched:10s} step {ms:8.3f} ms  {flops / ms / 1e9:7.1f} TFLOP/s   "
               f"kernel {kms:8.3f} ms  {flops / kms / 1e9:7.1f} TFLOP/s", file=sys.stderr,
               flush=True)
@@ -304,7 +336,8 @@ def main():
         "det_nondet_ratio": ({s: round(r["tflops"] / results["atomic"]["tflops"], 4)
                               for s, r in results.items() if s != "atomic"}
                              if "atomic" in results else None),
-        "schedules": {s: {k: round(v, 4) for k, v in r.items()} for s, r in results.items()},
+        "schedules": {s: {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
+                      for s, r in results.items()},
     }
     achieved = flops / (prim["kernel_ms"] * 1e-3) / 1e12
     traffic = read_traffic(w.name, ran)
