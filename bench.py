@@ -123,6 +123,26 @@ def order_wait(D, dev, lse, delta, sched, causal, ws, out, mkw):
             "order_polled_frac": spun / max(waits, 1.0)}
 
 
+PHASES = ("item/KV change", "S,dP products", "counter check", "softmax,dS", "dV,dK products",
+          "staging", "ordered add", "barrier", "dQ product", "hand-off", "prefetch,partial")
+
+
+def phase_shares(D, dev, lse, delta, sched, causal, ws, out, mkw):
+    """One extra, untimed launch with the phase timer on: the share of the
+    waves' cycles spent in each phase of their Q sub-tiles (the timer's own
+    clock reads slow the launch down; the shares are the result)."""
+    import torch
+    st = torch.zeros(16 * 4096 * 4, dtype=torch.int64, device="cuda")
+    D.attn_bwd(dev["q"], dev["k"], dev["v"], dev["do"], lse, delta, schedule=sched,
+               causal=causal, workspace=ws, out=out, debug={"phase_stats": st}, **mkw)
+    torch.cuda.synchronize()
+    D.attn_bwd_status(ws)
+    a = st.view(-1, 16).cpu().numpy().astype("float64")
+    a = a[a[:, 15] > 0]
+    total = a[:, 15].sum()
+    return {name: round(float(a[:, k].sum() / total), 4) for k, name in enumerate(PHASES)}
+
+
 def dag_prediction(D, w, causal, sched, mkw, coresident):
     """The host DAG model's view of one ordered schedule on this workload:
     predicted makespan and its lower bound (in units of one full item) and
@@ -171,6 +191,9 @@ def main():
                          "runs the measured fastest instead of the DAG model's pick")
     ap.add_argument("--no-fwd", action="store_true",
                     help="skip the forward and forward+backward timings")
+    ap.add_argument("--phases", action="store_true",
+                    help="one extra launch per schedule with the phase timer: share of wave "
+                         "cycles per phase of a Q sub-tile")
     ap.add_argument("--copy-calibration", type=int, default=0, metavar="BYTES",
                     help="run one plain device copy of BYTES before timing (a reference "
                          "dispatch of known traffic for hardware-counter runs)")
@@ -264,6 +287,12 @@ def main():
         if sched not in ("atomic", "auto") and not args.no_wait_stats:
             results[sched].update(order_wait(D, dev, lse, delta, sched, causal, ws, (dq, dk, dv),
                                              mkw))
+        if args.phases:
+            results[sched]["phases"] = phase_shares(D, dev, lse, delta, sched, causal, ws,
+                                                    (dq, dk, dv), mkw)
+            print(f"[bench] {sched:10s} phases " + "  ".join(
+                f"{k} {v:.3f}" for k, v in results[sched]["phases"].items()), file=sys.stderr,
+                flush=True)
         if sched not in ("atomic", "auto"):
             results[sched]["dag"] = dag_prediction(D, w, causal, sched, mkw,
                                                    torch.cuda.get_device_properties(0)

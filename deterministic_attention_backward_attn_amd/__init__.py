@@ -194,7 +194,9 @@ def attn_bwd(q, k, v, do, lse, delta, *, schedule="naive", causal=False, scale=N
     preallocated (dq, dk, dv).  `debug`: optional dict with keys spin_limit,
     jitter_seed, poison_q (1-based, 0 = off), partials (float32 tensor),
     kernel_events (two raw hipEvent_t handles), wait_stats (int64 tensor of
-    at least 4*4096*4 entries), placement (0 automatic, 1 device-wide, 2 XCD
+    at least 4*4096*4 entries), phase_stats (int64 tensor of at least
+    16*4096*4 entries: cycles per phase of each wave's sub-tiles, see the
+    header), placement (0 automatic, 1 device-wide, 2 XCD
     groups with L2-coherent accumulator, 3 XCD groups device-coherent),
     unit_order (0 automatic, 1 head by head, 2 unit-major).
     Mask arguments as for attn_fwd."""
@@ -225,6 +227,8 @@ def attn_bwd(q, k, v, do, lse, delta, *, schedule="naive", causal=False, scale=N
         dbg.unit_order = int(debug.get("unit_order", 0))
         if debug.get("wait_stats") is not None:
             dbg.wait_stats = _ptr(debug["wait_stats"])
+        if debug.get("phase_stats") is not None:
+            dbg.phase_stats = _ptr(debug["phase_stats"])
         ev = debug.get("kernel_events")
         if ev is not None:
             dbg.kernel_events[0] = ctypes.c_void_p(int(ev[0]))

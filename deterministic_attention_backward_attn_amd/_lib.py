@@ -44,7 +44,8 @@ class Debug(ctypes.Structure):
     _fields_ = [("spin_limit", ctypes.c_uint32), ("jitter_seed", ctypes.c_uint32),
                 ("poison_q", ctypes.c_int32), ("partials", ctypes.c_void_p),
                 ("kernel_events", ctypes.c_void_p * 2), ("wait_stats", ctypes.c_void_p),
-                ("placement", ctypes.c_int32), ("unit_order", ctypes.c_int32)]
+                ("placement", ctypes.c_int32), ("unit_order", ctypes.c_int32),
+                ("phase_stats", ctypes.c_void_p)]
 
 
 _vp = ctypes.c_void_p

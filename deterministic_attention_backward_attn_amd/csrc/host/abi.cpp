@@ -434,7 +434,9 @@ dash_status run_bwd(const dash_attn_desc* desc, dash_schedule schedule, const vo
   a.poison_q = dbg ? dbg->poison_q - 1 : -1;
   a.partials = dbg ? dbg->partials : nullptr;
   a.wait_stats = dbg ? dbg->wait_stats : nullptr;
-  if (a.wait_stats && (long)grid * dash::bwd_waves(desc->dtype, desc->d) > 4096L * 4)
+  a.phase_stats = dbg ? dbg->phase_stats : nullptr;
+  if ((a.wait_stats || a.phase_stats) &&
+      (long)grid * dash::bwd_waves(desc->dtype, desc->d) > 4096L * 4)
     return DASH_ERR_UNSUPPORTED;
   hipEvent_t ev0 = dbg ? (hipEvent_t)dbg->kernel_events[0] : nullptr;
   hipEvent_t ev1 = dbg ? (hipEvent_t)dbg->kernel_events[1] : nullptr;

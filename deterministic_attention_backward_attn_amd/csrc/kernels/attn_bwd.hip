@@ -49,6 +49,9 @@
 
 namespace dash {
 
+// phases of a sub-tile timed by the phase-timer test hook
+constexpr int kPhases = 11;
+
 template <typename T, int D, int BC, int BR, bool MASKED, bool ORDERED, bool DEBUG>
 __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
   using E = Elt<T>;
@@ -125,6 +128,17 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
   // that had to poll more than once, cycles of the whole unit loop
   uint64_t st_wait = 0, st_waits = 0, st_spun = 0;
   const uint64_t st_t0 = (DEBUG && a.wait_stats) ? (uint64_t)clock64() : 0;
+  // phase timer (test hook): lane 0 of each wave adds the shader-clock
+  // cycles since the previous mark to the phase that just ended
+  uint64_t ph[kPhases] = {};
+  uint64_t ph_t = (DEBUG && a.phase_stats) ? (uint64_t)clock64() : 0;
+  const uint64_t ph_t0 = ph_t;
+#define PHASE(k)                                                   \
+  if (DEBUG && a.phase_stats && lane == 0) {                       \
+    const uint64_t t_ = (uint64_t)clock64();                       \
+    ph[k] += t_ - ph_t;                                            \
+    ph_t = t_;                                                     \
+  }
 
   const Placement pl = place_units(a, tid, sPlace);
   const int U = a.units_per_head;
@@ -423,6 +437,7 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
       }
 
 
+      PHASE(0);  // item decode, KV tile change
       const T* cQ = sQ[b];
       const T* cdO = sdO[b];
       // S = Q K^T and dP = dO V^T for this wave's 32 KV columns
@@ -462,7 +477,9 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
       // its turn had already come.  Reading the counter peek waits for every
       // load issued before it (the prefetch too), so it sits behind the S/dP
       // products rather than at the top of the sub-tile.
+      PHASE(1);  // S and dP products
       if constexpr (ORDERED) begin_add();
+      PHASE(2);  // counter check, accumulator reads issued
 
       // P and dS; dS^T to LDS.  bf16: P and dS are packed once (hardware
       // RNE conversion) and the packed words serve both the LDS write and the
@@ -512,6 +529,7 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
         }
       }
 
+      PHASE(3);  // softmax, dS
       // dV += P^T dO ; dK += dS^T Q   (contraction over this sub-tile's Q rows)
 #pragma unroll
       for (int c = 0; c < BR / KSTEP; ++c) {
@@ -548,12 +566,16 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
 
       // stage the next sub-tile into the other buffer (its previous readers,
       // sub-tile g-1, finished before the last barrier)
+      PHASE(4);  // dV and dK products
       if (g + 1 < n_steps) stage(b ^ 1);
+      PHASE(5);  // staging the next sub-tile
       // finish the previous sub-tile's ordered add behind this one's products
       if constexpr (ORDERED) {
         if (p_qtile >= 0) finish_add();
       }
+      PHASE(6);  // previous partial's add
       __syncthreads();  // dS^T of this sub-tile and the next staged sub-tile are complete
+      PHASE(7);  // barrier
 
       // dQ_part = dS K for this wave's output tiles
       f32x16 accQ[QT];
@@ -578,7 +600,9 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
       // the previous partial's stores (issued before the barrier) complete
       // here; advance its counter before issuing the next prefetch, so the
       // wait does not include loads that were just issued
+      PHASE(8);  // dQ product
       if constexpr (ORDERED) release();
+      PHASE(9);  // hand-off
       fetch(g + 2);
 
       if (DEBUG && a.partials != nullptr) {
@@ -610,6 +634,7 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
 #pragma unroll
           for (int r = 0; r < 16; ++r) atomic_add_f32(&dqa[dq_off(q0, i, r)], accQ[i][r]);
       }
+      PHASE(10);  // prefetch, partial staging, counter read (or atomic adds)
     }
     if (cur_kv >= 0) flush_dkdv();
     if constexpr (ORDERED) {
@@ -640,6 +665,12 @@ __global__ void __launch_bounds__(BC * 2, 1) bwd_kernel(BwdArgs a) {
     st[2] = st_spun;
     st[3] = (uint64_t)clock64() - st_t0;
   }
+  if (DEBUG && a.phase_stats != nullptr && lane == 0) {
+    uint64_t* st = a.phase_stats + ((size_t)blockIdx.x * NW + w) * 16;
+    for (int k = 0; k < kPhases; ++k) st[k] = ph[k];
+    st[15] = (uint64_t)clock64() - ph_t0;
+  }
+#undef PHASE
 }
 
 // ------------------------------------------------------------ dispatch
@@ -707,7 +738,7 @@ hipError_t launch_bwd(int dtype, int d, bool masked, bool ordered, const BwdArgs
                       hipStream_t stream) {
   int threads = 0;
   const bool debug = a.jitter_seed != 0u || a.poison_q >= 0 || a.partials != nullptr ||
-                     a.wait_stats != nullptr;
+                     a.wait_stats != nullptr || a.phase_stats != nullptr;
   void* f = select_bwd(dtype, d, masked, ordered, debug, &threads);
   if (!f) return hipErrorInvalidValue;
   BwdArgs copy = a;

@@ -44,6 +44,7 @@ struct BwdArgs {
   int poison_q;
   float* partials;        // debug: [BH, n_tiles, N, d] or null
   uint64_t* wait_stats;   // debug: [grid, waves, 4] or null
+  uint64_t* phase_stats;  // debug: [grid, waves, 16] or null
 };
 
 struct FwdArgs {

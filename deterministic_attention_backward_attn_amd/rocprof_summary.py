@@ -27,6 +27,14 @@ figures: MFMA busy share (MFMA-busy cycles over 1024 SIMDs / busy cycles
 over 32 shader engines), LDS bank-conflict share of LDS-active cycles, and
 the share of wave cycles spent in s_waitcnt.
 
+  python -m deterministic_attention_backward_attn_amd.rocprof_summary phases \\
+      --log <bench output with --phases> --cmd "<command>" --out profiles/<name>.md
+
+The phases summary tabulates the per-phase shares of wave cycles that
+bench.py --phases reads from the backward's phase timer (a test hook; its
+clock reads slow the launch, so shares, not times, are the result), one
+column per schedule, with the kernel times of the same run.
+
 The traffic summary scales each kernel's FETCH_SIZE / WRITE_SIZE (KiB per
 dispatch) by the factor that makes the same counter read the known size of a
 plain device copy run in the same process, and records the hash of the
@@ -199,6 +207,34 @@ def _write(path, lines):
     print(text)
 
 
+def phases(args):
+    import json
+    line = [ln for ln in open(args.log) if ln.startswith('{"metric"')][-1]
+    run = json.loads(line)
+    scheds = [s for s, r in run["schedules"].items() if "phases" in r]
+    names = list(run["schedules"][scheds[0]]["phases"])
+    lines = ["# Phase shares of the backward kernel's wave cycles", "",
+             f"Command: `{args.cmd}`", "",
+             f"Workload: {run['config']['workload']}.  Shares of each wave's cycles per phase "
+             "of its Q sub-tiles, from one extra launch per schedule with the phase timer "
+             "(its clock reads slow that launch; shares, not times).", "",
+             "| phase | " + " | ".join(scheds) + " |",
+             "|---|" + "---|" * len(scheds)]
+    for n in names:
+        lines.append(f"| {n} | " + " | ".join(f"{run['schedules'][s]['phases'][n]:.3f}"
+                                              for s in scheds) + " |")
+    lines.append("| sum | " + " | ".join(f"{sum(run['schedules'][s]['phases'].values()):.3f}"
+                                        for s in scheds) + " |")
+    lines.append("| kernel ms (timed launches, no timer) | " + " | ".join(
+        f"{run['schedules'][s]['kernel_ms']:.3f}" for s in scheds) + " |")
+    lines += ["", f"kernel_source_sha256: {kernel_source_hash()}", ""]
+    text = "\n".join(lines)
+    if args.out:
+        with open(args.out, "w") as f:
+            f.write(text)
+    print(text)
+
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
     sub = ap.add_subparsers(dest="mode", required=True)
@@ -230,8 +266,12 @@ def main(argv=None):
     t.add_argument("--cmd-fetch", required=True)
     t.add_argument("--cmd-write", required=True)
     t.add_argument("--out")
+    ph = sub.add_parser("phases")
+    ph.add_argument("--log", required=True)
+    ph.add_argument("--cmd", required=True)
+    ph.add_argument("--out")
     args = ap.parse_args(argv)
-    {"stats": stats, "traffic": traffic, "counters": counters}[args.mode](args)
+    {"stats": stats, "traffic": traffic, "counters": counters, "phases": phases}[args.mode](args)
 
 
 if __name__ == "__main__":

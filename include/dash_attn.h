@@ -224,6 +224,21 @@ dash_status dash_attn_bwd_status(const void* workspace, void* stream);
  *                   workgroup's whole run (waves = dash_attn_tile/32;
  *                   workgroups x waves must not exceed 4096 * 4, else
  *                   DASH_ERR_UNSUPPORTED).
+ *   phase_stats     non-NULL: device uint64 buffer of at least
+ *                   16 * 4096 * 4 entries; for each workgroup g and wave w,
+ *                   entries [(g*waves + w)*16 + k] receive the shader-clock
+ *                   cycles the wave spent in phase k of its Q sub-tiles:
+ *                   0 item decode and KV tile changes, 1 S and dP products,
+ *                   2 counter check and accumulator reads issued, 3 softmax
+ *                   and dS, 4 dV and dK products, 5 staging the next
+ *                   sub-tile, 6 the previous partial's ordered add, 7 the
+ *                   sub-tile barrier, 8 the dQ product, 9 the hand-off,
+ *                   10 prefetch, partial staging and counter read (atomic
+ *                   adds for ATOMIC); k=15 the cycles of the whole run.  The
+ *                   timer reads the clock between phases, which itself waits
+ *                   for outstanding LDS accesses, so the launch runs slower
+ *                   than without it; shares, not times, are the result.
+ *                   Same size limit as wait_stats.
  */
 typedef struct {
   uint32_t spin_limit;
@@ -234,6 +249,7 @@ typedef struct {
   uint64_t* wait_stats;
   int32_t placement;
   int32_t unit_order;
+  uint64_t* phase_stats;
 } dash_bwd_debug;
 
 dash_status dash_attn_bwd_debug(const dash_attn_desc* desc, dash_schedule schedule,

@@ -14,6 +14,8 @@
   their dK, dV bit-identical.
 * Placement (device-wide or XCD groups, L2- or device-coherent accumulator)
   changes no bit.
+* The phase timer (a test hook) changes no bit and its phases fit inside
+  each wave's run.
 """
 import numpy as np
 import pytest
@@ -262,3 +264,31 @@ def test_tune_records_the_fastest_for_auto(causal):
     out = _bwd(dev, lse, delta, "auto", causal)
     for x, y in zip(ref, out):
         assert torch.equal(x.view(torch.int16), y.view(torch.int16))
+
+
+@pytest.mark.parametrize("causal", [True, False])
+def test_phase_timer_changes_no_bit(causal):
+    """The phase timer (a test hook) changes no result bit, and its phase
+    cycles of every wave add up to no more than that wave's whole run."""
+    require_gpu()
+    B, H, N, d = 2, 16, 2048, 128
+    log(f"phase timer B={B} H={H} N={N} d={d} causal={causal}")
+    dev, lse, delta = _prep(B, H, N, d, "bf16", causal, 2400)
+    for sched in ORDERED + ["atomic"]:
+        ws = D.alloc_workspace(dev["q"], causal, sched)
+        st = torch.zeros(16 * 4096 * 4, dtype=torch.int64, device="cuda")
+        timed = _bwd(dev, lse, delta, sched, causal, ws, debug={"phase_stats": st})
+        D.attn_bwd_status(ws)
+        a = st.view(-1, 16).cpu().numpy()
+        a = a[a[:, 15] > 0]
+        assert len(a) > 0 and (a >= 0).all()
+        assert (a[:, :11].sum(axis=1) <= a[:, 15]).all()
+        # every wave that ran a sub-tile spent cycles in its products
+        ran = a[:, :11].sum(axis=1) > 0
+        assert ran.any() and (a[ran, 1] > 0).all() and (a[ran, 4] > 0).all()
+        if sched != "atomic":
+            plain = _bwd(dev, lse, delta, sched, causal, ws)
+            for x, y in zip(timed, plain):
+                assert torch.equal(x.view(torch.int16), y.view(torch.int16)), sched
+        log(f"  {sched}: {len(a)} waves, ordered-add share "
+            f"{a[:, 6].sum() / a[:, 15].sum():.3f}")
