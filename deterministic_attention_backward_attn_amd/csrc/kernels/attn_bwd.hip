@@ -20,11 +20,12 @@
 // sub-tile's counter for wave w reads r, reads the accumulator, adds its
 // partial, writes it back and sets the counter to r + 1.  The first
 // contributor writes without reading; the last one writes the final,
-// scaled dQ in the output dtype instead of the accumulator.  The accumulator
-// and counters are accessed with device-coherent loads and stores (the
-// cache policy of device-scope atomics), and a wave's stores complete before
-// it advances the counter, so no cache-wide write-back or invalidation is
-// needed.  The add for sub-tile g runs during sub-tile g+1's products, so its
+// scaled dQ in the output dtype instead of the accumulator.  The counters
+// are accessed with device-coherent loads and stores (the cache policy of
+// device-scope atomics); the accumulator too, or with L2-coherent ones when
+// every contributor of a head runs on one XCD (then this CU's L1 is
+// invalidated right before each accumulator read).  A wave's stores complete
+// before it advances the counter, so no cache-wide write-back is needed.  The add for sub-tile g runs during sub-tile g+1's products, so its
 // memory latency hides behind MFMA work.  The atomic schedule adds with
 // unordered fp32 atomics instead (non-deterministic reference).
 //

@@ -177,8 +177,9 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, ui
                                            0x00020000);
 }
 // Cache-policy operands: sc1 = coherent across the device (every XCD);
-// sc0 = bypasses the CU's L1 and is served by the XCD's L2, so it is
-// coherent among the workgroups of one XCD.
+// sc0 = workgroup scope: a load may still be served by a line in this CU's
+// L1, otherwise by the XCD's L2, so a reader of data that other CUs of the
+// XCD wrote invalidates its L1 first (l1_invalidate), then reads with sc0.
 constexpr int kCoherent = 16;
 // Invalidate this CU's vector L1 cache (L2 untouched).
 __device__ __forceinline__ void l1_invalidate() { asm volatile("buffer_inv sc0" ::: "memory"); }
