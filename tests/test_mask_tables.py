@@ -252,3 +252,25 @@ def test_table_export_protocol():
     assert lib.dash_attn_schedule_tables(ctypes.byref(desc), 9, sizes, None, None, None, None,
                                          None, None) == 1
     assert lib.dash_attn_schedule_tables(None, 2, sizes, None, None, None, None, None, None) == 1
+
+
+def test_bench_dag_prediction_on_the_plain_workloads():
+    """The bench's DAG view of each ordered schedule: on the full and causal
+    masks shift meets its lower bound with no waits (the pages' conflict-free
+    construction), descending needs no longer than naive, and the head sample
+    keeps the launch's heads per co-resident workgroup."""
+    import bench
+    from synth import WORKLOADS
+    for name in ("b1h32_n16k_d128_causal", "b4h32_n4k_d128_full", "b2h16_n2k_d128_causal"):
+        w = WORKLOADS[name]
+        causal = w.masks[0] == "causal"
+        pred = {s: bench.dag_prediction(D, w, causal, s, w.mask_args(), 256)
+                for s in ("naive", "descending", "shift")}
+        for p in pred.values():
+            assert p is not None
+            assert p["heads"] * 256 == p["slots"] * w.B * w.H
+            assert p["makespan_items"] >= p["lower_bound_items"] - 1e-6
+            assert 0.0 <= p["wait_frac"] < 1.0
+        assert pred["shift"]["makespan_items"] == pytest.approx(pred["shift"]["lower_bound_items"])
+        assert pred["shift"]["wait_frac"] == 0.0
+        assert pred["descending"]["makespan_items"] <= pred["naive"]["makespan_items"] + 1e-6
