@@ -106,14 +106,14 @@ def cpu_baseline(exact, w, causal, max_workers):
 
 # ------------------------------------------------------- ordering waits
 
-def order_wait(D, dev, lse, delta, sched, causal, ws, out, mkw):
+def order_wait(D, dev, lse, delta, sched, causal, ws, out, mkw, lay=None):
     """One extra, untimed launch of the instrumented kernel (wait statistics
     on): the share of the waves' cycles spent waiting for ordered-add turns,
     and the share of ordered adds whose turn had not come at the first poll."""
     import torch
     st = torch.zeros(4 * 4096 * 4, dtype=torch.int64, device="cuda")
     D.attn_bwd(dev["q"], dev["k"], dev["v"], dev["do"], lse, delta, schedule=sched,
-               causal=causal, workspace=ws, out=out, debug={"wait_stats": st}, **mkw)
+               causal=causal, workspace=ws, out=out, debug=dict(lay or {}, wait_stats=st), **mkw)
     torch.cuda.synchronize()
     D.attn_bwd_status(ws)
     a = st.view(-1, 4).cpu().numpy()
@@ -191,6 +191,9 @@ def main():
                          "runs the measured fastest instead of the DAG model's pick")
     ap.add_argument("--no-fwd", action="store_true",
                     help="skip the forward and forward+backward timings")
+    ap.add_argument("--layout", choices=["default", "pairs"], default="default",
+                    help="backward kernel layout: default, or wave pairs (bf16 d=128; "
+                         "bit-identical results)")
     ap.add_argument("--phases", action="store_true",
                     help="one extra launch per schedule with the phase timer: share of wave "
                          "cycles per phase of a Q sub-tile")
@@ -247,11 +250,13 @@ def main():
     ws = D.alloc_workspace(dev["q"], causal, "naive")
     flops = w.flops_bwd(causal)
 
+    lay = {"layout": 1} if args.layout == "pairs" else {}
+
     def step(sched, events=None):
         D.attn_bwd_preprocess(o, dev["do"], out=delta)
+        dbg = dict(lay, **({} if events is None else {"kernel_events": events}))
         D.attn_bwd(dev["q"], dev["k"], dev["v"], dev["do"], lse, delta, schedule=sched,
-                   causal=causal, workspace=ws, out=(dq, dk, dv),
-                   debug=None if events is None else {"kernel_events": events}, **mkw)
+                   causal=causal, workspace=ws, out=(dq, dk, dv), debug=dbg or None, **mkw)
 
     tuned = None
     if args.tune:
@@ -286,8 +291,8 @@ def main():
                           "kernel_ms": kms, "kernel_tflops": flops / kms / 1e9}
         if sched not in ("atomic", "auto") and not args.no_wait_stats:
             results[sched].update(order_wait(D, dev, lse, delta, sched, causal, ws, (dq, dk, dv),
-                                             mkw))
-        if args.phases:
+                                             mkw, lay))
+        if args.phases and not lay:
             results[sched]["phases"] = phase_shares(D, dev, lse, delta, sched, causal, ws,
                                                     (dq, dk, dv), mkw)
             print(f"[bench] {sched:10s} phases " + "  ".join(
@@ -360,7 +365,8 @@ def main():
                    "mask": mask + (f" window {w.window}" if w.window else "")
                    + (" block " + json.dumps(w.block_spec) if w.block_spec else ""),
                    "schedule": primary if ran == primary else f"{primary} ({ran})",
-                   "parallelism": "single GPU"},
+                   "parallelism": "single GPU",
+                   **({"layout": "wave pairs"} if lay else {})},
         "pct_peak": round(100.0 * prim["tflops"] / peak, 2),
         "det_nondet_ratio": ({s: round(r["tflops"] / results["atomic"]["tflops"], 4)
                               for s, r in results.items() if s != "atomic"}

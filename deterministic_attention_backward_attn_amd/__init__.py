@@ -196,7 +196,8 @@ def attn_bwd(q, k, v, do, lse, delta, *, schedule="naive", causal=False, scale=N
     kernel_events (two raw hipEvent_t handles), wait_stats (int64 tensor of
     at least 4*4096*4 entries), phase_stats (int64 tensor of at least
     16*4096*4 entries: cycles per phase of each wave's sub-tiles, see the
-    header), placement (0 automatic, 1 device-wide, 2 XCD
+    header), layout (0 default kernel, 1 wave pairs: bf16 d=128 only,
+    bit-identical results), placement (0 automatic, 1 device-wide, 2 XCD
     groups with L2-coherent accumulator, 3 XCD groups device-coherent),
     unit_order (0 automatic, 1 head by head, 2 unit-major).
     Mask arguments as for attn_fwd."""
@@ -229,6 +230,7 @@ def attn_bwd(q, k, v, do, lse, delta, *, schedule="naive", causal=False, scale=N
             dbg.wait_stats = _ptr(debug["wait_stats"])
         if debug.get("phase_stats") is not None:
             dbg.phase_stats = _ptr(debug["phase_stats"])
+        dbg.layout = int(debug.get("layout", 0))
         ev = debug.get("kernel_events")
         if ev is not None:
             dbg.kernel_events[0] = ctypes.c_void_p(int(ev[0]))

@@ -45,7 +45,7 @@ class Debug(ctypes.Structure):
                 ("poison_q", ctypes.c_int32), ("partials", ctypes.c_void_p),
                 ("kernel_events", ctypes.c_void_p * 2), ("wait_stats", ctypes.c_void_p),
                 ("placement", ctypes.c_int32), ("unit_order", ctypes.c_int32),
-                ("phase_stats", ctypes.c_void_p)]
+                ("phase_stats", ctypes.c_void_p), ("layout", ctypes.c_int32)]
 
 
 _vp = ctypes.c_void_p

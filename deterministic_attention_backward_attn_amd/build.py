@@ -25,6 +25,7 @@ SOURCES = [
     "host/schedule.cpp",
     "host/dag.cpp",
     "kernels/attn_bwd.hip",
+    "kernels/attn_bwd_pair.hip",
     "kernels/attn_fwd.hip",
     "kernels/elementwise.hip",
 ]

@@ -351,6 +351,10 @@ dash_status run_bwd(const dash_attn_desc* desc, dash_schedule schedule, const vo
   if (dbg && (dbg->poison_q < 0 || dbg->poison_q > desc->N / br)) return DASH_ERR_INVALID_ARG;
   if (dbg && (dbg->placement < 0 || dbg->placement > 3)) return DASH_ERR_INVALID_ARG;
   if (dbg && (dbg->unit_order < 0 || dbg->unit_order > 2)) return DASH_ERR_INVALID_ARG;
+  const bool pairs = dbg && dbg->layout == 1;
+  if (dbg && (dbg->layout < 0 || dbg->layout > 1)) return DASH_ERR_INVALID_ARG;
+  if (pairs && (desc->dtype != 1 || desc->d != 128 || dbg->phase_stats))
+    return DASH_ERR_UNSUPPORTED;
 
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return DASH_ERR_HIP;
@@ -363,6 +367,12 @@ dash_status run_bwd(const dash_attn_desc* desc, dash_schedule schedule, const vo
   int maxco = 0;
   st = get_coresident(dev, desc->dtype, desc->d, masked, ordered, &maxco);
   if (st != DASH_OK) return st;
+  if (pairs) {
+    // the wave-pair kernel must fit as many workgroups (the same schedule)
+    int pb = 0;
+    if (dash::bwd_pair_max_coresident(masked, ordered, &pb) != hipSuccess) return DASH_ERR_HIP;
+    if (pb < maxco) return DASH_ERR_UNSUPPORTED;
+  }
   const long heads = (long)desc->B * desc->H;
   Sched s = Sched::Naive;
   st = resolve_schedule(schedule, mkey, dm->host, heads, maxco, &s);
@@ -441,7 +451,9 @@ dash_status run_bwd(const dash_attn_desc* desc, dash_schedule schedule, const vo
   hipEvent_t ev0 = dbg ? (hipEvent_t)dbg->kernel_events[0] : nullptr;
   hipEvent_t ev1 = dbg ? (hipEvent_t)dbg->kernel_events[1] : nullptr;
   if (ev0 && hipEventRecord(ev0, strm) != hipSuccess) return DASH_ERR_HIP;
-  if (U > 0 && dash::launch_bwd(desc->dtype, desc->d, masked, ordered, a, grid, strm) != hipSuccess)
+  if (U > 0 && (pairs ? dash::launch_bwd_pair(masked, ordered, a, grid, strm)
+                       : dash::launch_bwd(desc->dtype, desc->d, masked, ordered, a, grid, strm)) !=
+                   hipSuccess)
     return DASH_ERR_HIP;
   if (ev1 && hipEventRecord(ev1, strm) != hipSuccess) return DASH_ERR_HIP;
   // gradient rows no pair touches: dQ of Q blocks that see no key (the

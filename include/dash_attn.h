@@ -239,6 +239,13 @@ dash_status dash_attn_bwd_status(const void* workspace, void* stream);
  *                   for outstanding LDS accesses, so the launch runs slower
  *                   than without it; shares, not times, are the result.
  *                   Same size limit as wait_stats.
+ *   layout          0 = the default backward kernel; 1 = the wave-pair
+ *                   layout (bf16, d = 128 only; two waves per SIMD, each KV
+ *                   slice split between a wave for S, P, dV and the dQ
+ *                   product and a wave for dP, dS, dK and the ordered add).
+ *                   Results are bit-identical for both.  1 with another
+ *                   dtype or head dim, or with phase_stats:
+ *                   DASH_ERR_UNSUPPORTED; other values: DASH_ERR_INVALID_ARG.
  */
 typedef struct {
   uint32_t spin_limit;
@@ -250,6 +257,7 @@ typedef struct {
   int32_t placement;
   int32_t unit_order;
   uint64_t* phase_stats;
+  int32_t layout;
 } dash_bwd_debug;
 
 dash_status dash_attn_bwd_debug(const dash_attn_desc* desc, dash_schedule schedule,

@@ -16,6 +16,7 @@
   changes no bit.
 * The phase timer (a test hook) changes no bit and its phases fit inside
   each wave's run.
+* The wave-pair layout gives the same bits as the default kernel.
 """
 import numpy as np
 import pytest
@@ -292,3 +293,48 @@ def test_phase_timer_changes_no_bit(causal):
                 assert torch.equal(x.view(torch.int16), y.view(torch.int16)), sched
         log(f"  {sched}: {len(a)} waves, ordered-add share "
             f"{a[:, 6].sum() / a[:, 15].sum():.3f}")
+
+
+@pytest.mark.parametrize("causal,window", [(True, 0), (False, 0), (True, 300)])
+def test_wave_pair_layout_is_bit_identical(causal, window):
+    """The wave-pair layout of the backward (two waves per KV slice) computes
+    every product, exponential and add in the same order as the default
+    kernel: bit-identical dQ, dK, dV for every ordered schedule, the same
+    bits again on a second run; the atomic schedule runs and matches within
+    the bf16 tolerance."""
+    require_gpu()
+    B, H, N, d = 2, 16, 2048, 128
+    log(f"wave pairs B={B} H={H} N={N} d={d} causal={causal} window={window}")
+    dev, _ = device_inputs(B, H, N, d, "bf16", 2500)
+    o, lse = D.attn_fwd(dev["q"], dev["k"], dev["v"], causal=causal, window=window)
+    delta = D.attn_bwd_preprocess(o, dev["do"])
+
+    def run(sched, layout, ws):
+        return D.attn_bwd(dev["q"], dev["k"], dev["v"], dev["do"], lse, delta, schedule=sched,
+                          causal=causal, workspace=ws, window=window,
+                          debug={"layout": layout} if layout else None)
+
+    for sched in ORDERED + ["atomic"]:
+        ws = D.alloc_workspace(dev["q"], causal, sched)
+        ref = [t.clone() for t in run(sched, 0, ws)]
+        for rep in range(2):
+            out = run(sched, 1, ws)
+            D.attn_bwd_status(ws)
+            for x, y in zip(ref, out):
+                if sched == "atomic":
+                    err = (x.float() - y.float()).abs().max() / x.float().abs().max()
+                    assert float(err) <= 2e-2, (sched, float(err))
+                else:
+                    assert torch.equal(x.view(torch.int16), y.view(torch.int16)), (sched, rep)
+        log(f"  {sched}: wave pairs match")
+
+
+def test_wave_pair_layout_rejects_other_shapes():
+    require_gpu()
+    dev, _ = device_inputs(1, 2, 512, 64, "bf16", 2600)
+    o, lse = D.attn_fwd(dev["q"], dev["k"], dev["v"], causal=True)
+    delta = D.attn_bwd_preprocess(o, dev["do"])
+    with pytest.raises(D.DashError) as e:
+        D.attn_bwd(dev["q"], dev["k"], dev["v"], dev["do"], lse, delta, schedule="shift",
+                   causal=True, debug={"layout": 1})
+    assert e.value.code == 2  # DASH_ERR_UNSUPPORTED
