@@ -224,3 +224,28 @@ def test_argument_errors_without_launch():
     assert lib.dash_attn_tile(None) == 0 and lib.dash_attn_bwd_subtile(None) == 0
     assert lib.dash_attn_tile(ctypes.byref(_desc(dtype=1, N=256))) == 128
     assert lib.dash_attn_bwd_subtile(ctypes.byref(_desc(d=128))) == 32
+
+
+def _header_struct_fields(name):
+    """Field names of a typedef'd struct in include/dash_attn.h, in order."""
+    import re
+    text = open(_lib.HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    m = re.search(r"typedef struct \{(.*?)\}\s*" + name + r";", text, flags=re.S)
+    assert m, name
+    fields = []
+    for decl in m.group(1).split(";"):
+        decl = decl.strip()
+        if not decl:
+            continue
+        # "type a, b" declares several fields; arrays keep their name
+        for part in decl.split(","):
+            fields.append(re.match(r".*?(\w+)\s*(\[\d+\])?$", part.strip()).group(1))
+    return fields
+
+
+def test_ctypes_structs_mirror_the_header():
+    """The binding's ctypes structures list the header's fields in the same
+    order (the binding passes them by pointer to the library)."""
+    assert [f[0] for f in _lib.Desc._fields_] == _header_struct_fields("dash_attn_desc")
+    assert [f[0] for f in _lib.Debug._fields_] == _header_struct_fields("dash_bwd_debug")
