@@ -231,7 +231,7 @@ def _header_struct_fields(name):
     import re
     text = open(_lib.HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    m = re.search(r"typedef struct \{(.*?)\}\s*" + name + r";", text, flags=re.S)
+    m = re.search(r"typedef struct \{([^{}]*)\}\s*" + name + r";", text)
     assert m, name
     fields = []
     for decl in m.group(1).split(";"):
