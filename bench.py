@@ -125,22 +125,36 @@ def order_wait(D, dev, lse, delta, sched, causal, ws, out, mkw, lay=None):
 
 PHASES = ("item/KV change", "S,dP products", "counter check", "softmax,dS", "dV,dK products",
           "staging", "ordered add", "barrier", "dQ product", "hand-off", "prefetch,partial")
+# wave-pair layout: phases of the two roles
+PHASES_A = ("item/KV change", "S products", "softmax,P", "P barrier", "dV products", "staging",
+            "barrier", "dQ product,partial", "prefetch")
+PHASES_B = ("item/KV change", "dP products,counter check", "-", "P barrier", "dS,dK products",
+            "staging", "ordered add,barrier", "hand-off", "prefetch,counter read")
 
 
-def phase_shares(D, dev, lse, delta, sched, causal, ws, out, mkw):
+def phase_shares(D, dev, lse, delta, sched, causal, ws, out, mkw, lay=None):
     """One extra, untimed launch with the phase timer on: the share of the
     waves' cycles spent in each phase of their Q sub-tiles (the timer's own
     clock reads slow the launch down; the shares are the result)."""
     import torch
     st = torch.zeros(16 * 4096 * 4, dtype=torch.int64, device="cuda")
     D.attn_bwd(dev["q"], dev["k"], dev["v"], dev["do"], lse, delta, schedule=sched,
-               causal=causal, workspace=ws, out=out, debug={"phase_stats": st}, **mkw)
+               causal=causal, workspace=ws, out=out, debug=dict(lay or {}, phase_stats=st),
+               **mkw)
     torch.cuda.synchronize()
     D.attn_bwd_status(ws)
     a = st.view(-1, 16).cpu().numpy().astype("float64")
     a = a[a[:, 15] > 0]
-    total = a[:, 15].sum()
-    return {name: round(float(a[:, k].sum() / total), 4) for k, name in enumerate(PHASES)}
+    if not lay:
+        total = a[:, 15].sum()
+        return {name: round(float(a[:, k].sum() / total), 4) for k, name in enumerate(PHASES)}
+    res = {}
+    for role, tag, names in ((1, "A", PHASES_A), (2, "B", PHASES_B)):
+        r = a[a[:, 14] == role]
+        total = r[:, 15].sum()
+        res.update({f"{tag}: {n}": round(float(r[:, k].sum() / total), 4)
+                    for k, n in enumerate(names) if n != "-"})
+    return res
 
 
 def dag_prediction(D, w, causal, sched, mkw, coresident):
@@ -292,9 +306,9 @@ def main():
         if sched not in ("atomic", "auto") and not args.no_wait_stats:
             results[sched].update(order_wait(D, dev, lse, delta, sched, causal, ws, (dq, dk, dv),
                                              mkw, lay))
-        if args.phases and not lay:
+        if args.phases:
             results[sched]["phases"] = phase_shares(D, dev, lse, delta, sched, causal, ws,
-                                                    (dq, dk, dv), mkw)
+                                                    (dq, dk, dv), mkw, lay)
             print(f"[bench] {sched:10s} phases " + "  ".join(
                 f"{k} {v:.3f}" for k, v in results[sched]["phases"].items()), file=sys.stderr,
                 flush=True)

@@ -353,8 +353,7 @@ dash_status run_bwd(const dash_attn_desc* desc, dash_schedule schedule, const vo
   if (dbg && (dbg->unit_order < 0 || dbg->unit_order > 2)) return DASH_ERR_INVALID_ARG;
   const bool pairs = dbg && dbg->layout == 1;
   if (dbg && (dbg->layout < 0 || dbg->layout > 1)) return DASH_ERR_INVALID_ARG;
-  if (pairs && (desc->dtype != 1 || desc->d != 128 || dbg->phase_stats))
-    return DASH_ERR_UNSUPPORTED;
+  if (pairs && (desc->dtype != 1 || desc->d != 128)) return DASH_ERR_UNSUPPORTED;
 
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return DASH_ERR_HIP;
@@ -445,8 +444,9 @@ dash_status run_bwd(const dash_attn_desc* desc, dash_schedule schedule, const vo
   a.partials = dbg ? dbg->partials : nullptr;
   a.wait_stats = dbg ? dbg->wait_stats : nullptr;
   a.phase_stats = dbg ? dbg->phase_stats : nullptr;
+  // (the wave-pair layout times 8 waves per workgroup)
   if ((a.wait_stats || a.phase_stats) &&
-      (long)grid * dash::bwd_waves(desc->dtype, desc->d) > 4096L * 4)
+      (long)grid * (pairs ? 8 : dash::bwd_waves(desc->dtype, desc->d)) > 4096L * 4)
     return DASH_ERR_UNSUPPORTED;
   hipEvent_t ev0 = dbg ? (hipEvent_t)dbg->kernel_events[0] : nullptr;
   hipEvent_t ev1 = dbg ? (hipEvent_t)dbg->kernel_events[1] : nullptr;

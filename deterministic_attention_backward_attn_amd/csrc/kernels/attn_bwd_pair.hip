@@ -68,6 +68,23 @@ __global__ void __launch_bounds__(512, 1) bwd_pair_kernel(BwdArgs a) {
 
   uint64_t st_wait = 0, st_waits = 0, st_spun = 0;
   const uint64_t st_t0 = (DEBUG && a.wait_stats) ? (uint64_t)clock64() : 0;
+  // phase timer (test hook): lane 0 of each wave adds the shader-clock
+  // cycles since the previous mark to the phase that just ended; the
+  // phases of A waves: 0 item decode and KV tile changes, 1 S products,
+  // 2 softmax and P to LDS, 3 the P barrier, 4 dV products, 5 staging,
+  // 6 the sub-tile barrier, 7 dQ product and partial to LDS, 8 prefetch;
+  // of B waves: 0, 1 dP products and counter check, 2 -, 3 the P barrier,
+  // 4 dS and dK products, 5 staging, 6 the ordered add and the sub-tile
+  // barrier, 7 the hand-off, 8 prefetch and counter read
+  uint64_t ph[9] = {};
+  uint64_t ph_t = (DEBUG && a.phase_stats) ? (uint64_t)clock64() : 0;
+  const uint64_t ph_t0 = ph_t;
+#define PHASE(k)                                                   \
+  if (DEBUG && a.phase_stats && lane == 0) {                       \
+    const uint64_t t_ = (uint64_t)clock64();                       \
+    ph[k] += t_ - ph_t;                                            \
+    ph_t = t_;                                                     \
+  }
 
   const Placement pl = place_units(a, tid, sPlace);
   const int U = a.units_per_head;
@@ -290,6 +307,7 @@ __global__ void __launch_bounds__(512, 1) bwd_pair_kernel(BwdArgs a) {
           for (int nt = 0; nt < NTD; ++nt) acc[nt] = zero16();
         }
 
+        PHASE(0);
         const T* cQ = sQ[b];
         const T* cdO = sdO[b];
         // A: S = Q K^T; B: dP = dO V^T (this slice's 32 KV columns)
@@ -311,6 +329,7 @@ __global__ void __launch_bounds__(512, 1) bwd_pair_kernel(BwdArgs a) {
         const int kvl = 32 * w + l32;
         uint32_t pw[8];
         if constexpr (!IS_A && ORDERED) begin_add();
+        PHASE(1);
         if constexpr (IS_A) {
 
           const bool emask = MASKED && ((itm.y >> 29) & 1);
@@ -334,7 +353,9 @@ __global__ void __launch_bounds__(512, 1) bwd_pair_kernel(BwdArgs a) {
             *reinterpret_cast<f32x4*>(&sP[w][lane * 16 + 4 * gq]) = f32x4{p[0], p[1], p[2], p[3]};
           }
         }
+        PHASE(2);
         __syncthreads();  // P of every slice visible to its B wave
+        PHASE(3);
         if constexpr (IS_A) {
           // dV += P^T dO
   #pragma unroll
@@ -377,11 +398,14 @@ __global__ void __launch_bounds__(512, 1) bwd_pair_kernel(BwdArgs a) {
           }
         }
 
+        PHASE(4);
         if (g + 1 < n_steps) stage(b ^ 1);
+        PHASE(5);
         if constexpr (ORDERED) {
           if (!IS_A && p_qtile >= 0) finish_add();
         }
         __syncthreads();  // dS^T of this sub-tile and the next staged sub-tile are complete
+        PHASE(6);
 
         if constexpr (IS_A) {
           // dQ_part = dS K (transposed for the ordered add) for column tile w
@@ -399,7 +423,7 @@ __global__ void __launch_bounds__(512, 1) bwd_pair_kernel(BwdArgs a) {
             for (int r = 0; r < 16; ++r) pp[dq_off(q0, r)] = accQ[r];
           }
           if constexpr (ORDERED) {
-            // row-major into this slice's LDS area; its A wave adds it during
+            // row-major into this slice's LDS area; its B wave adds it during
             // the next sub-tile (after the next barrier)
             float* row = sRow[w];
   #pragma unroll
@@ -419,14 +443,16 @@ __global__ void __launch_bounds__(512, 1) bwd_pair_kernel(BwdArgs a) {
             p_flags = flags;
           }
         }
+        PHASE(7);
         fetch(g + 2);
         if constexpr (ORDERED) {
           if constexpr (!IS_A) p_seen = load_relaxed_agent(counter(p_qtile));
         }
+        PHASE(8);
       }
       if (cur_kv >= 0) flush();
-      // the last partial, written by the B waves after the last barrier, is
-      // complete before the A waves add it
+      // the last partial, written by the A waves after the last barrier, is
+      // complete before the B waves add it
       __syncthreads();
       if constexpr (ORDERED) {
         if constexpr (!IS_A) {
@@ -453,6 +479,13 @@ __global__ void __launch_bounds__(512, 1) bwd_pair_kernel(BwdArgs a) {
   };
   if (isA) run(std::true_type{});
   else run(std::false_type{});
+  if (DEBUG && a.phase_stats != nullptr && lane == 0) {
+    uint64_t* st = a.phase_stats + ((size_t)blockIdx.x * 8 + (isA ? w : 4 + w)) * 16;
+    for (int k = 0; k < 9; ++k) st[k] = ph[k];
+    st[14] = isA ? 1u : 2u;
+    st[15] = (uint64_t)clock64() - ph_t0;
+  }
+#undef PHASE
   if (DEBUG && a.wait_stats != nullptr && lane == 0 && !isA) {
     uint64_t* st = a.wait_stats + ((size_t)blockIdx.x * NW + w) * 4;
     st[0] = st_wait;
@@ -490,7 +523,7 @@ hipError_t bwd_pair_max_coresident(bool masked, bool ordered, int* blocks) {
 hipError_t launch_bwd_pair(bool masked, bool ordered, const BwdArgs& a, int grid,
                            hipStream_t stream) {
   const bool debug = a.jitter_seed != 0u || a.poison_q >= 0 || a.partials != nullptr ||
-                     a.wait_stats != nullptr;
+                     a.wait_stats != nullptr || a.phase_stats != nullptr;
   void* f = debug ? pick_pair<true>(masked, ordered) : pick_pair<false>(masked, ordered);
   BwdArgs copy = a;
   void* args[] = {&copy};

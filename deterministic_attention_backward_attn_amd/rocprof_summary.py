@@ -215,7 +215,9 @@ def phases(args):
     names = list(run["schedules"][scheds[0]]["phases"])
     lines = ["# Phase shares of the backward kernel's wave cycles", "",
              f"Command: `{args.cmd}`", "",
-             f"Workload: {run['config']['workload']}.  Shares of each wave's cycles per phase "
+             f"Workload: {run['config']['workload']}"
+             + (f", backward layout: {run['config']['layout']}" if "layout" in run["config"] else "")
+             + ".  Shares of each wave's cycles per phase "
              "of its Q sub-tiles, from one extra launch per schedule with the phase timer "
              "(its clock reads slow that launch; shares, not times).", "",
              "| phase | " + " | ".join(scheds) + " |",

@@ -238,14 +238,18 @@ dash_status dash_attn_bwd_status(const void* workspace, void* stream);
  *                   timer reads the clock between phases, which itself waits
  *                   for outstanding LDS accesses, so the launch runs slower
  *                   than without it; shares, not times, are the result.
- *                   Same size limit as wait_stats.
+ *                   Same size limit as wait_stats.  With layout 1 every one
+ *                   of the 8 waves of a workgroup g writes entries
+ *                   [(g*8 + v)*16 + k]: k = 0..8 its phases (the kernel
+ *                   source lists them per role), k = 14 its role (1 or 2),
+ *                   k = 15 its whole run.
  *   layout          0 = the default backward kernel; 1 = the wave-pair
  *                   layout (bf16, d = 128 only; two waves per SIMD, each KV
  *                   slice split between a wave for S, P, dV and the dQ
  *                   product and a wave for dP, dS, dK and the ordered add).
  *                   Results are bit-identical for both.  1 with another
- *                   dtype or head dim, or with phase_stats:
- *                   DASH_ERR_UNSUPPORTED; other values: DASH_ERR_INVALID_ARG.
+ *                   dtype or head dim: DASH_ERR_UNSUPPORTED; other values:
+ *                   DASH_ERR_INVALID_ARG.
  */
 typedef struct {
   uint32_t spin_limit;

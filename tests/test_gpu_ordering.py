@@ -338,3 +338,24 @@ def test_wave_pair_layout_rejects_other_shapes():
         D.attn_bwd(dev["q"], dev["k"], dev["v"], dev["do"], lse, delta, schedule="shift",
                    causal=True, debug={"layout": 1})
     assert e.value.code == 2  # DASH_ERR_UNSUPPORTED
+
+
+def test_wave_pair_phase_timer_changes_no_bit():
+    """The phase timer of the wave-pair layout changes no result bit and
+    records both roles' phases inside each wave's run."""
+    require_gpu()
+    B, H, N, d = 2, 16, 2048, 128
+    dev, lse, delta = _prep(B, H, N, d, "bf16", True, 2700)
+    for sched in ORDERED:
+        ws = D.alloc_workspace(dev["q"], True, sched)
+        st = torch.zeros(16 * 4096 * 4, dtype=torch.int64, device="cuda")
+        timed = _bwd(dev, lse, delta, sched, True, ws, debug={"layout": 1, "phase_stats": st})
+        plain = _bwd(dev, lse, delta, sched, True, ws, debug={"layout": 1})
+        D.attn_bwd_status(ws)
+        for x, y in zip(timed, plain):
+            assert torch.equal(x.view(torch.int16), y.view(torch.int16)), sched
+        a = st.view(-1, 16).cpu().numpy()
+        a = a[a[:, 15] > 0]
+        assert set(a[:, 14].tolist()) == {1, 2}
+        assert (a[:, :9].sum(axis=1) <= a[:, 15]).all()
+        log(f"  {sched}: {len(a)} waves timed")
