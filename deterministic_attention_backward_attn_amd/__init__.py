@@ -8,8 +8,8 @@ longest path) take and return plain Python / numpy values.
 
 Public calls (same names as the C entry points, without the prefix):
   attn_fwd, attn_bwd_preprocess, attn_bwd_workspace_size, attn_bwd,
-  attn_bwd_status, backward (preprocess + bwd), schedule_tables,
-  schedule_predict, dag_longest_path, litmus_ordered_add.
+  status_query, attn_bwd_status, backward (preprocess + bwd),
+  schedule_tables, schedule_predict, dag_longest_path, litmus_ordered_add.
 """
 from __future__ import annotations
 
@@ -21,7 +21,7 @@ from ._lib import DTYPES, SCHEDULES, DashError, Debug, Desc, check, header_symbo
 
 __all__ = [
     "DashError", "SCHEDULES", "attn_fwd", "attn_bwd_preprocess", "attn_bwd_workspace_size",
-    "attn_bwd", "attn_bwd_status", "attn_bwd_tune", "backward", "schedule_tables", "schedule_predict", "schedule_choose",
+    "attn_bwd", "attn_bwd_status", "status_query", "attn_bwd_tune", "backward", "schedule_tables", "schedule_predict", "schedule_choose",
     "resolve_schedule", "mask_schedule_tables", "mask_schedule_predict",
     "dag_longest_path", "litmus_ordered_add", "tile", "subtile", "header_symbols", "load",
 ]
@@ -134,8 +134,11 @@ def attn_fwd(q, k, v, causal: bool = False, scale=None, stream=None, *, window=0
         _same_shape(q, o)
         if lse.dtype != torch.float32 or tuple(lse.shape) != tuple(q.shape[:3]):
             raise ValueError("lse must be float32 [B, H, N]")
-    check(lib.dash_attn_fwd(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
-                            _stream(stream)), "dash_attn_fwd")
+    nws = int(lib.dash_attn_fwd_workspace_size(ctypes.byref(desc)))
+    ws = torch.empty(nws, dtype=torch.uint8, device=q.device) if nws else None
+    check(lib.dash_attn_fwd_ws(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(o), _ptr(lse),
+                               _ptr(ws), ctypes.c_size_t(nws), _stream(stream)),
+          "dash_attn_fwd_ws")
     return o, lse
 
 
@@ -156,13 +159,15 @@ def attn_bwd_preprocess(o, do, out=None, stream=None):
     return delta
 
 
-def attn_bwd_workspace_size(B, H, N, d, dtype="bf16", causal=False, schedule="naive") -> int:
+def attn_bwd_workspace_size(B, H, N, d, dtype="bf16", causal=False, schedule="naive", *,
+                            window=0, block_mask=None, block_size=0) -> int:
+    """Workspace bytes of the backward (the same for every schedule)."""
     lib = load()
-    out = ctypes.c_size_t(0)
-    check(lib.dash_attn_bwd_workspace_size(ctypes.byref(_desc(B, H, N, d, dtype, causal)),
-                                           _sched(schedule), ctypes.byref(out)),
-          "dash_attn_bwd_workspace_size")
-    return int(out.value)
+    desc = _desc(B, H, N, d, dtype, causal, None, window, block_mask, block_size)
+    n = int(lib.dash_attn_bwd_workspace_size(ctypes.byref(desc), _sched(schedule)))
+    if n == 0:
+        raise DashError(2, "dash_attn_bwd_workspace_size")
+    return n
 
 
 def resolve_schedule(B, H, N, d, dtype="bf16", causal=False, schedule="auto", *, window=0,
@@ -178,11 +183,13 @@ def resolve_schedule(B, H, N, d, dtype="bf16", causal=False, schedule="auto", *,
     return {v: k for k, v in SCHEDULES.items()}[out.value]
 
 
-def alloc_workspace(q, causal=False, schedule="naive"):
+def alloc_workspace(q, causal=False, schedule="naive", *, window=0, block_mask=None,
+                    block_size=0):
     torch = _torch()
     B, H, N, d = (int(x) for x in q.shape)
     dt = "f32" if q.dtype == torch.float32 else "bf16"
-    n = attn_bwd_workspace_size(B, H, N, d, dt, causal, schedule)
+    n = attn_bwd_workspace_size(B, H, N, d, dt, causal, schedule, window=window,
+                                block_mask=block_mask, block_size=block_size)
     return torch.empty(n, dtype=torch.uint8, device=q.device)
 
 
@@ -206,7 +213,8 @@ def attn_bwd(q, k, v, do, lse, delta, *, schedule="naive", causal=False, scale=N
     _same_shape(q, k, v, do)
     desc = _desc_from(q, causal, scale, window, block_mask, block_size)
     if workspace is None:
-        workspace = alloc_workspace(q, causal, schedule)
+        workspace = alloc_workspace(q, causal, schedule, window=window, block_mask=block_mask,
+                                    block_size=block_size)
     if out is None:
         dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
     else:
@@ -251,7 +259,8 @@ def attn_bwd_tune(q, k, v, do, lse, delta, *, causal=False, scale=None, reps=3, 
     _same_shape(q, k, v, do)
     desc = _desc_from(q, causal, scale, window, block_mask, block_size)
     if workspace is None:
-        workspace = alloc_workspace(q, causal, "auto")
+        workspace = alloc_workspace(q, causal, "auto", window=window, block_mask=block_mask,
+                                    block_size=block_size)
     if out is None:
         out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
     dq, dk, dv = out
@@ -272,6 +281,13 @@ def attn_bwd_status(workspace, stream=None):
     """Synchronizes the stream and raises DashError if an ordered add timed out."""
     lib = load()
     check(lib.dash_attn_bwd_status(_ptr(workspace), _stream(stream)), "dash_attn_bwd_status")
+
+
+def status_query(workspace):
+    """Status word of the last backward on `workspace` (call after the
+    stream was synchronized); raises DashError on a time-out."""
+    lib = load()
+    check(lib.dash_status_query(_ptr(workspace)), "dash_status_query")
 
 
 def backward(q, k, v, o, do, lse, *, schedule="naive", causal=False, scale=None,
@@ -364,11 +380,14 @@ def mask_schedule_predict(B, H, N, d, dtype="bf16", causal=False, schedule="naiv
 
 
 def schedule_predict(n: int, causal: bool, schedule, heads: int, slots: int, cost):
-    """Returns (makespan, total_wait, max_slot_idle, lower_bound)."""
+    """DAG prediction for `heads` heads of n tiles under the full or causal
+    mask (a descriptor with B = 1, H = heads, fp32 64-row tiles, N = 64 n).
+    Returns (makespan, total_wait, max_slot_idle, lower_bound)."""
     lib = load()
+    desc = _desc(1, int(heads), 64 * int(n), 64, "f32", causal)
     c = (ctypes.c_double * 4)(*[float(x) for x in cost])
     out = (ctypes.c_double * 4)()
-    check(lib.dash_schedule_predict(n, 1 if causal else 0, _sched(schedule), heads, slots, c, out),
+    check(lib.dash_schedule_predict(ctypes.byref(desc), _sched(schedule), int(slots), c, out),
           "dash_schedule_predict")
     return tuple(out)
 

@@ -22,6 +22,7 @@ STATUS = {
     4: "DASH_ERR_HIP",
     5: "DASH_ERR_SCHEDULE_INVALID",
     6: "DASH_ERR_ORDER_TIMEOUT",
+    7: "DASH_ERR_HOST_MEMORY",
 }
 SCHEDULES = {"atomic": 0, "naive": 1, "descending": 2, "shift": 3, "auto": 4}
 DTYPES = {"f32": 0, "bf16": 1}
@@ -59,16 +60,20 @@ _SIGS = {
     "dash_attn_bwd_subtile": (_i32, [ctypes.POINTER(Desc)]),
     "dash_attn_fwd": (ctypes.c_int, [ctypes.POINTER(Desc), _vp, _vp, _vp, _vp, _vp, _vp]),
     "dash_attn_bwd_preprocess": (ctypes.c_int, [ctypes.POINTER(Desc), _vp, _vp, _vp, _vp]),
-    "dash_attn_bwd_workspace_size": (ctypes.c_int, [ctypes.POINTER(Desc), ctypes.c_int,
-                                                    ctypes.POINTER(ctypes.c_size_t)]),
+    "dash_attn_fwd_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(Desc)]),
+    "dash_attn_fwd_ws": (ctypes.c_int, [ctypes.POINTER(Desc), _vp, _vp, _vp, _vp, _vp, _vp,
+                                        ctypes.c_size_t, _vp]),
+    "dash_attn_bwd_workspace_size": (ctypes.c_size_t, [ctypes.POINTER(Desc), ctypes.c_int]),
     "dash_attn_bwd": (ctypes.c_int, [ctypes.POINTER(Desc), ctypes.c_int, _vp, _vp, _vp, _vp, _vp,
                                      _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _vp]),
     "dash_attn_bwd_debug": (ctypes.c_int, [ctypes.POINTER(Desc), ctypes.c_int, _vp, _vp, _vp, _vp,
                                            _vp, _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t,
                                            ctypes.POINTER(Debug), _vp]),
     "dash_attn_bwd_status": (ctypes.c_int, [_vp, _vp]),
+    "dash_status_query": (ctypes.c_int, [_vp]),
     "dash_schedule_tables": (ctypes.c_int, [_i32, _i32, ctypes.c_int, _ip, _ip, _ip, _ip, _ip]),
-    "dash_schedule_predict": (ctypes.c_int, [_i32, _i32, ctypes.c_int, _i32, _i32, _dp, _dp]),
+    "dash_schedule_predict": (ctypes.c_int, [ctypes.POINTER(Desc), ctypes.c_int, _i32, _dp,
+                                             _dp]),
     "dash_attn_bwd_resolve_schedule": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int,
                                                       ctypes.POINTER(ctypes.c_int)]),
     "dash_attn_schedule_tables": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, _ip, _ip, _ip,

@@ -1,4 +1,4 @@
-// C ABI of the library: argument checks, workspace layout, the per-device
+// C ABI of the library: argument checks, workspace layout, the host-side
 // schedule-table cache, and the launch sequence of the backward.
 #include <hip/hip_runtime.h>
 
@@ -7,11 +7,13 @@
 #include <cstring>
 #include <map>
 #include <mutex>
+#include <new>
 #include <tuple>
 #include <vector>
 
 #include "dash_attn.h"
 #include "../kernels/launch.hpp"
+#include "../kernels/plain_tables.hpp"
 #include "dag.hpp"
 #include "schedule.hpp"
 
@@ -130,140 +132,140 @@ float scale_of(const dash_attn_desc* d) {
   return d->softmax_scale > 0.f ? d->softmax_scale : 1.0f / std::sqrt((float)d->d);
 }
 
+// ----------------------------------------------------------- workspace
+
+// [0, 256): header (status word, work counters, XCD census); the order
+// counters [BH, N/BR, waves] u32; one head's schedule tables (unit offsets
+// [n + 1], items [live pairs] int2, and the Q blocks / KV tiles no pair
+// touches [<= 2n]); the fp32 dQ accumulator [BH, N, d].  The table region
+// holds the largest table any schedule builds for the mask (at most n + 1
+// units, one item per live pair), so the size is the same for every
+// schedule.
 struct WsLayout {
-  size_t counters_off, counters_words, acc_off, total;
+  size_t counters_off, counters_words, unit_off_off, items_off, dead_off, acc_off, total;
 };
 
-// [0, 256): header (status word, work counter); then the order counters
-// [BH, N/BR, waves]; then the fp32 dQ accumulator [BH, N, d].
-WsLayout layout(const dash_attn_desc* d) {
+WsLayout layout(const dash_attn_desc* d, long live_pairs) {
   int bc = 0, br = 0;
   dash::bwd_tiles(d->dtype, d->d, &bc, &br);
+  const int n = d->N / bc;
   WsLayout w;
   const size_t heads = (size_t)d->B * d->H;
   w.counters_off = kHeaderBytes;
   w.counters_words = heads * (size_t)(d->N / br) * dash::bwd_waves(d->dtype, d->d);
-  w.acc_off = align256(w.counters_off + 4 * w.counters_words);
+  w.unit_off_off = align256(w.counters_off + 4 * w.counters_words);
+  w.items_off = align256(w.unit_off_off + 4 * (size_t)(n + 1));
+  w.dead_off = align256(w.items_off + 8 * (size_t)std::max<long>(live_pairs, 1));
+  w.acc_off = align256(w.dead_off + 4 * (size_t)(2 * n));
   w.total = w.acc_off + 4 * heads * (size_t)d->N * d->d;
   return w;
 }
 
-// ----------------------------------------------------------- table cache
+bool plain_key(const MaskKey& k) { return k.window == 0 && k.block.empty(); }
 
-struct DevTables {
-  Tables host;
-  int* d_unit_off = nullptr;
-  int2* d_items = nullptr;
+// ------------------------------------------------------ host table caches
+//
+// Host memory only.  Plain masks: the host builds and validates the tables
+// once and checks them against the closed forms the device writes into the
+// workspace at every launch.  Windows and block masks: the host builds the
+// tables and keeps them in pinned host memory, laid out as the workspace's
+// table region, and every launch copies them into the caller's workspace on
+// the caller's stream.  Entries are evicted least recently used beyond
+// kMaxEntries; an evicted pinned buffer is freed only after the last copy
+// from it has completed (an event recorded behind each copy).
+
+constexpr size_t kMaxEntries = 32;
+
+struct MaskEntry {
+  dash::TileMask host;
+  long live_pairs = 0;
+  std::vector<int> dead;  // Q blocks no pair touches, then KV tiles
+  int n_dead_q = 0, n_dead_kv = 0;
+  uint8_t* pinned_live = nullptr;  // block masks: tile liveness for the forward
+  hipEvent_t used = nullptr;
+  uint64_t stamp = 0;
 };
 
-// Per mask: tile liveness for the forward (block masks only) and the tiles
-// no pair touches (their gradient rows are cleared by the host).
-struct DevMask {
-  dash::TileMask host;
-  uint8_t* d_live = nullptr;  // [n * n] by [q * n + kv], block masks only
-  int* d_dead = nullptr;      // dead Q blocks, then dead KV tiles
-  int n_dead_q = 0, n_dead_kv = 0;
+struct TabEntry {
+  Tables host;
+  int max_unit_items = 0;
+  char* pinned = nullptr;  // special masks: unit offsets | items | dead list
+  size_t bytes = 0;
+  hipEvent_t used = nullptr;
+  uint64_t stamp = 0;
 };
 
 std::mutex g_mu;
-std::map<std::tuple<int, MaskKey, int>, DevTables> g_tables;  // (device, mask, sched)
-std::map<std::pair<int, MaskKey>, DevMask> g_masks;           // (device, mask)
+uint64_t g_clock = 0;
+std::map<MaskKey, MaskEntry> g_masks;                     // special masks only
+std::map<std::pair<MaskKey, int>, TabEntry> g_tables;     // (mask, sched)
 std::map<std::tuple<int, int, int, int, int>, int> g_coresident;  // (device, dtype, d, masked, ordered)
 std::map<std::tuple<MaskKey, int, int>, Sched> g_auto;  // (mask, heads, slots) -> choice
 // (mask, sched, heads, slots, grouped) -> unit-major
 std::map<std::tuple<MaskKey, int, long, int, int>, bool> g_order;
 
-constexpr int kXcds = 8;  // XCDs of an MI355X: the group share the order choice predicts for
-
-// Unit order of a dynamic ordered schedule: unit-major (unit 0 of every
-// head, then unit 1, ...) when the DAG model predicts a makespan at least
-// 5 % shorter than head by head for one group's share (the heads and
-// workgroups of one XCD when units run in XCD groups).  A head's own units
-// keep their relative order either way, so results are bit-identical; the
-// order only changes which heads run side by side (masks whose units
-// differ much in length gain most).
-bool unit_major_for(const MaskKey& mkey, const Tables& t, Sched s, long heads, int maxco,
-                    bool grouped) {
-  if (t.needs_static() || !t.ordered() || t.units() == 0) return false;
-  const auto key = std::make_tuple(mkey, (int)s, heads, maxco, (int)grouped);
-  {
-    std::lock_guard<std::mutex> lock(g_mu);
-    auto it = g_order.find(key);
-    if (it != g_order.end()) return it->second;
+template <typename E>
+void release_entry(E& e, void* buf) {
+  if (e.used) {
+    (void)hipEventSynchronize(e.used);
+    (void)hipEventDestroy(e.used);
+    e.used = nullptr;
   }
-  const int g = grouped ? kXcds : 1;
-  const int slots = std::max(1, maxco / g);
-  long hg = (heads + g - 1) / g;
-  hg = std::max<long>(1, std::min<long>(hg, 200000 / std::max(1, t.items())));
-  dash::DagResult hm, um;
-  bool pick = false;
-  if (dash::dag_predict(t, (int)hg, slots, kDefaultCost, hm, false) &&
-      dash::dag_predict(t, (int)hg, slots, kDefaultCost, um, true))
-    pick = um.makespan < 0.95 * hm.makespan;
-  std::lock_guard<std::mutex> lock(g_mu);
-  g_order[key] = pick;
-  return pick;
+  if (buf) (void)hipHostFree(buf);
 }
 
-dash_status get_mask(int dev, const MaskKey& key, const DevMask** out) {
-  std::lock_guard<std::mutex> lock(g_mu);
-  auto mk = std::make_pair(dev, key);
-  auto it = g_masks.find(mk);
-  if (it != g_masks.end()) {
-    *out = &it->second;
-    return DASH_OK;
+void free_entry(MaskEntry& e) { release_entry(e, e.pinned_live); e.pinned_live = nullptr; }
+void free_entry(TabEntry& e) { release_entry(e, e.pinned); e.pinned = nullptr; }
+
+template <typename M>
+void evict(M& m) {
+  while (m.size() >= kMaxEntries) {
+    auto victim = m.begin();
+    for (auto it = m.begin(); it != m.end(); ++it)
+      if (it->second.stamp < victim->second.stamp) victim = it;
+    free_entry(victim->second);
+    m.erase(victim);
   }
-  DevMask dm;
-  dm.host = tile_mask(key);
+}
+
+// The mask entry of a window or block mask (caller holds g_mu).
+MaskEntry* mask_entry(const MaskKey& key) {
+  auto it = g_masks.find(key);
+  if (it != g_masks.end()) {
+    it->second.stamp = ++g_clock;
+    return &it->second;
+  }
+  evict(g_masks);
+  MaskEntry e;
+  e.host = tile_mask(key);
   const int n = key.n;
-  std::vector<int> dead;
   for (int q = 0; q < n; ++q) {
     bool any = false;
-    for (int kv = 0; kv < n && !any; ++kv) any = dm.host.live[(size_t)q * n + kv] != 0;
-    if (!any) dead.push_back(q);
+    for (int kv = 0; kv < n; ++kv) {
+      const bool l = e.host.live[(size_t)q * n + kv] != 0;
+      any = any || l;
+      e.live_pairs += l ? 1 : 0;
+    }
+    if (!any) e.dead.push_back(q);
   }
-  dm.n_dead_q = (int)dead.size();
+  e.n_dead_q = (int)e.dead.size();
   for (int kv = 0; kv < n; ++kv) {
     bool any = false;
-    for (int q = 0; q < n && !any; ++q) any = dm.host.live[(size_t)q * n + kv] != 0;
-    if (!any) dead.push_back(kv);
+    for (int q = 0; q < n && !any; ++q) any = e.host.live[(size_t)q * n + kv] != 0;
+    if (!any) e.dead.push_back(kv);
   }
-  dm.n_dead_kv = (int)dead.size() - dm.n_dead_q;
-  if (!key.block.empty()) {
-    if (hipMalloc(&dm.d_live, dm.host.live.size()) != hipSuccess) return DASH_ERR_HIP;
-    if (hipMemcpy(dm.d_live, dm.host.live.data(), dm.host.live.size(), hipMemcpyHostToDevice) !=
-        hipSuccess) {
-      (void)hipFree(dm.d_live);
-      return DASH_ERR_HIP;
-    }
-  }
-  if (!dead.empty()) {
-    if (hipMalloc(&dm.d_dead, sizeof(int) * dead.size()) != hipSuccess ||
-        hipMemcpy(dm.d_dead, dead.data(), sizeof(int) * dead.size(), hipMemcpyHostToDevice) !=
-            hipSuccess) {
-      if (dm.d_live) (void)hipFree(dm.d_live);
-      if (dm.d_dead) (void)hipFree(dm.d_dead);
-      return DASH_ERR_HIP;
-    }
-  }
-  auto res = g_masks.emplace(mk, std::move(dm));
-  *out = &res.first->second;
-  return DASH_OK;
+  e.n_dead_kv = (int)e.dead.size() - e.n_dead_q;
+  e.stamp = ++g_clock;
+  return &g_masks.emplace(key, std::move(e)).first->second;
 }
 
-dash_status get_tables(int dev, const MaskKey& mkey, const dash::TileMask& m, Sched s,
-                       const DevTables** out) {
-  std::lock_guard<std::mutex> lock(g_mu);
-  auto key = std::make_tuple(dev, mkey, (int)s);
-  auto it = g_tables.find(key);
-  if (it != g_tables.end()) {
-    *out = &it->second;
-    return DASH_OK;
-  }
-  DevTables dt;
-  if (!dash::build_tables(m, s, dt.host)) return DASH_ERR_UNSUPPORTED;
-  if (dash::validate_tables(dt.host)[0] != '\0') return DASH_ERR_SCHEDULE_INVALID;
-  const Tables& t = dt.host;
+// Live tile pairs of a descriptor's mask (caller holds g_mu for special masks).
+long live_pairs_of(const MaskKey& key) {
+  if (plain_key(key)) return dash::plain::items(key.n, key.causal != 0);
+  return mask_entry(key)->live_pairs;
+}
+
+std::vector<int2> encode_items(const Tables& t) {
   const int n = t.n;
   std::vector<int2> items(t.items());
   std::vector<int> contributors(n, 0);
@@ -277,23 +279,115 @@ dash_status get_tables(int dev, const MaskKey& mkey, const dash::TileMask& m, Sc
       items[i].y |= r | ((r == contributors[t.q[i]] - 1) ? (1 << 30) : 0);
     }
   }
-  if (hipMalloc(&dt.d_unit_off, sizeof(int) * t.unit_off.size()) != hipSuccess) return DASH_ERR_HIP;
-  if (hipMalloc(&dt.d_items, sizeof(int2) * (items.empty() ? 1 : items.size())) != hipSuccess) {
-    (void)hipFree(dt.d_unit_off);
-    return DASH_ERR_HIP;
+  return items;
+}
+
+// Most items of one unit of a plain schedule (without building it).
+int plain_max_unit_items(int n, bool causal, Sched s) {
+  return (s == Sched::Shift && causal && n > 1) ? n + 1 : n;
+}
+
+// Tables of (mask, schedule), built, validated and (plain masks) checked
+// against the closed forms the device writes.  Host memory only.  Caller
+// holds g_mu.
+dash_status tab_entry(const MaskKey& key, Sched s, TabEntry** out) {
+  const auto k = std::make_pair(key, (int)s);
+  auto it = g_tables.find(k);
+  if (it != g_tables.end()) {
+    it->second.stamp = ++g_clock;
+    *out = &it->second;
+    return DASH_OK;
   }
-  if (hipMemcpy(dt.d_unit_off, t.unit_off.data(), sizeof(int) * t.unit_off.size(),
-                hipMemcpyHostToDevice) != hipSuccess ||
-      (!items.empty() &&
-       hipMemcpy(dt.d_items, items.data(), sizeof(int2) * items.size(), hipMemcpyHostToDevice) !=
-           hipSuccess)) {
-    (void)hipFree(dt.d_unit_off);
-    (void)hipFree(dt.d_items);
-    return DASH_ERR_HIP;
+  const bool plain = plain_key(key);
+  const int n = key.n;
+  if (plain && plain_max_unit_items(n, key.causal != 0, s) > dash::kMaxUnitItems)
+    return DASH_ERR_UNSUPPORTED;
+  TabEntry e;
+  if (plain) {
+    if (!dash::build_tables(n, key.causal != 0, s, e.host)) return DASH_ERR_UNSUPPORTED;
+  } else {
+    if (!dash::build_tables(mask_entry(key)->host, s, e.host)) return DASH_ERR_UNSUPPORTED;
   }
-  auto res = g_tables.emplace(key, std::move(dt));
-  *out = &res.first->second;
+  const Tables& t = e.host;
+  if (dash::validate_tables(t)[0] != '\0') return DASH_ERR_SCHEDULE_INVALID;
+  for (int u = 0; u < t.units(); ++u)
+    e.max_unit_items = std::max(e.max_unit_items, t.unit_off[u + 1] - t.unit_off[u]);
+  if (e.max_unit_items > dash::kMaxUnitItems) return DASH_ERR_UNSUPPORTED;
+  if (plain) {
+    // the device writes the closed forms: they must be these tables
+    const std::vector<int2> items = encode_items(t);
+    const bool c = key.causal != 0;
+    const int ps = (int)s;
+    bool same = dash::plain::defined(n, c, ps) && dash::plain::units(n, c, ps) == t.units() &&
+                dash::plain::items(n, c) == (long)t.items();
+    for (int u = 0; same && u <= t.units(); ++u)
+      same = dash::plain::unit_off(n, c, ps, u) == (long)t.unit_off[u];
+    for (int i = 0; same && i < t.items(); ++i) {
+      const int2 g = dash::plain::encode(n, c, ps, i);
+      same = g.x == items[i].x && g.y == items[i].y;
+    }
+    if (!same) return DASH_ERR_SCHEDULE_INVALID;
+  }
+  evict(g_tables);
+  e.stamp = ++g_clock;
+  *out = &g_tables.emplace(k, std::move(e)).first->second;
   return DASH_OK;
+}
+
+// A special mask's tables packed into pinned host memory as the
+// workspace's table region from its unit offsets on (unit offsets | items |
+// dead list), made on the first launch that needs them.  Caller holds g_mu.
+dash_status pinned_blob(const MaskKey& key, TabEntry* e) {
+  if (e->pinned) return DASH_OK;
+  const MaskEntry* me = mask_entry(key);
+  const Tables& t = e->host;
+  const int n = key.n;
+  const std::vector<int2> items = encode_items(t);
+  const size_t items_at = align256(4 * (size_t)(n + 1));
+  const size_t dead_at = align256(items_at + 8 * (size_t)std::max<long>(me->live_pairs, 1));
+  const size_t bytes = dead_at + 4 * me->dead.size();
+  char* p = nullptr;
+  if (hipHostMalloc((void**)&p, bytes, hipHostMallocDefault) != hipSuccess) return DASH_ERR_HIP;
+  std::memset(p, 0, bytes);
+  std::memcpy(p, t.unit_off.data(), sizeof(int) * t.unit_off.size());
+  if (!items.empty()) std::memcpy(p + items_at, items.data(), sizeof(int2) * items.size());
+  if (!me->dead.empty()) std::memcpy(p + dead_at, me->dead.data(), 4 * me->dead.size());
+  if (hipEventCreateWithFlags(&e->used, hipEventDisableTiming) != hipSuccess) {
+    e->used = nullptr;
+    (void)hipHostFree(p);
+    return DASH_ERR_HIP;
+  }
+  e->pinned = p;
+  e->bytes = bytes;
+  return DASH_OK;
+}
+
+constexpr int kXcds = 8;  // XCDs of an MI355X: the group share the order choice predicts for
+
+// Unit order of a dynamic ordered schedule: unit-major (unit 0 of every
+// head, then unit 1, ...) when the DAG model predicts a makespan at least
+// 5 % shorter than head by head for one group's share (the heads and
+// workgroups of one XCD when units run in XCD groups).  A head's own units
+// keep their relative order either way, so results are bit-identical; the
+// order only changes which heads run side by side (masks whose units
+// differ much in length gain most).  Caller holds g_mu.
+bool unit_major_for(const MaskKey& mkey, const Tables& t, Sched s, long heads, int maxco,
+                    bool grouped) {
+  if (t.needs_static() || !t.ordered() || t.units() == 0) return false;
+  const auto key = std::make_tuple(mkey, (int)s, heads, maxco, (int)grouped);
+  auto it = g_order.find(key);
+  if (it != g_order.end()) return it->second;
+  const int g = grouped ? kXcds : 1;
+  const int slots = std::max(1, maxco / g);
+  long hg = (heads + g - 1) / g;
+  hg = std::max<long>(1, std::min<long>(hg, 200000 / std::max(1, t.items())));
+  dash::DagResult hm, um;
+  bool pick = false;
+  if (dash::dag_predict(t, (int)hg, slots, kDefaultCost, hm, false) &&
+      dash::dag_predict(t, (int)hg, slots, kDefaultCost, um, true))
+    pick = um.makespan < 0.95 * hm.makespan;
+  g_order[key] = pick;
+  return pick;
 }
 
 dash_status get_coresident(int dev, int dtype, int d, bool masked, bool ordered, int* blocks) {
@@ -312,25 +406,44 @@ dash_status get_coresident(int dev, int dtype, int d, bool masked, bool ordered,
   return DASH_OK;
 }
 
+// Whether some live pair hides elements (the kernel then masks them).
+// Caller holds g_mu.
+bool any_partial(const MaskKey& key) {
+  if (plain_key(key)) return key.causal != 0;
+  return mask_entry(key)->host.any_partial();
+}
+
 // DASH_SCHED_AUTO -> the predicted best ordered schedule for this problem
 // on `maxco` co-resident workgroups (cached per shape); others unchanged.
-dash_status resolve_schedule(dash_schedule schedule, const MaskKey& mkey, const dash::TileMask& m,
-                             long heads, int maxco, Sched* s) {
+// Caller holds g_mu.
+dash_status resolve_schedule(dash_schedule schedule, const MaskKey& mkey, long heads, int maxco,
+                             Sched* s) {
   *s = (Sched)schedule;
   if (schedule != DASH_SCHED_AUTO) return DASH_OK;
   const int h = (int)std::min<long>(heads, 1L << 30);
   const auto key = std::make_tuple(mkey, h, maxco);
-  std::lock_guard<std::mutex> lock(g_mu);
   auto it = g_auto.find(key);
   if (it != g_auto.end()) {
     *s = it->second;
     return DASH_OK;
   }
   double pred[3];
+  if (plain_key(mkey) && mkey.n + 1 > dash::kMaxUnitItems) return DASH_ERR_UNSUPPORTED;
+  const dash::TileMask m = plain_key(mkey) ? dash::plain_mask(mkey.n, mkey.causal != 0)
+                                           : mask_entry(mkey)->host;
   const dash_status st = choose_schedule(m, h, maxco, kDefaultCost, s, pred);
   if (st != DASH_OK) return st;
   g_auto[key] = *s;
   return DASH_OK;
+}
+
+// Reads the workspace's status word (synchronous copy; the caller has
+// synchronized the stream the backward ran on).
+dash_status read_status(const void* workspace) {
+  uint32_t word = 0;
+  if (hipMemcpy(&word, workspace, sizeof(word), hipMemcpyDeviceToHost) != hipSuccess)
+    return DASH_ERR_HIP;
+  return word ? DASH_ERR_ORDER_TIMEOUT : DASH_OK;
 }
 
 dash_status run_bwd(const dash_attn_desc* desc, dash_schedule schedule, const void* q,
@@ -342,8 +455,6 @@ dash_status run_bwd(const dash_attn_desc* desc, dash_schedule schedule, const vo
   if (!sched_ok_run(schedule)) return DASH_ERR_INVALID_ARG;
   if (!q || !k || !v || !dout || !lse || !delta || !dq || !dk || !dv || !workspace)
     return DASH_ERR_INVALID_ARG;
-  const WsLayout w = layout(desc);
-  if (workspace_bytes < w.total || ((uintptr_t)workspace & 255u)) return DASH_ERR_WORKSPACE;
   int bc = 0, br = 0;
   dash::bwd_tiles(desc->dtype, desc->d, &bc, &br);
   const int n = desc->N / bc;
@@ -355,14 +466,21 @@ dash_status run_bwd(const dash_attn_desc* desc, dash_schedule schedule, const vo
   if (dbg && (dbg->layout < 0 || dbg->layout > 1)) return DASH_ERR_INVALID_ARG;
   if (pairs && (desc->dtype != 1 || desc->d != 128)) return DASH_ERR_UNSUPPORTED;
 
+  const MaskKey mkey = mask_key(desc);
+  const bool plain = plain_key(mkey);
+  if (plain && n > dash::kMaxUnitItems) return DASH_ERR_UNSUPPORTED;
+  const long heads = (long)desc->B * desc->H;
+  hipStream_t strm = (hipStream_t)stream;
+  char* ws = (char*)workspace;
+
+  std::unique_lock<std::mutex> lock(g_mu);
+  const WsLayout w = layout(desc, live_pairs_of(mkey));
+  if (workspace_bytes < w.total || ((uintptr_t)workspace & 255u)) return DASH_ERR_WORKSPACE;
+  // elements are masked inside some pairs (causal diagonal, window edges)
+  const bool masked = any_partial(mkey);
+  lock.unlock();
   int dev = 0;
   if (hipGetDevice(&dev) != hipSuccess) return DASH_ERR_HIP;
-  const MaskKey mkey = mask_key(desc);
-  const DevMask* dm = nullptr;
-  st = get_mask(dev, mkey, &dm);
-  if (st != DASH_OK) return st;
-  // elements are masked inside some pairs (causal diagonal, window edges)
-  const bool masked = dm->host.any_partial();
   int maxco = 0;
   st = get_coresident(dev, desc->dtype, desc->d, masked, ordered, &maxco);
   if (st != DASH_OK) return st;
@@ -372,23 +490,20 @@ dash_status run_bwd(const dash_attn_desc* desc, dash_schedule schedule, const vo
     if (dash::bwd_pair_max_coresident(masked, ordered, &pb) != hipSuccess) return DASH_ERR_HIP;
     if (pb < maxco) return DASH_ERR_UNSUPPORTED;
   }
-  const long heads = (long)desc->B * desc->H;
+  lock.lock();
   Sched s = Sched::Naive;
-  st = resolve_schedule(schedule, mkey, dm->host, heads, maxco, &s);
+  st = resolve_schedule(schedule, mkey, heads, maxco, &s);
   if (st != DASH_OK) return st;
-  const DevTables* tb = nullptr;
-  st = get_tables(dev, mkey, dm->host, s, &tb);
+  TabEntry* tb = nullptr;
+  st = tab_entry(mkey, s, &tb);
   if (st != DASH_OK) return st;
-
-  const int U = tb->host.units();
-  for (int u = 0; u < U; ++u)
-    if (tb->host.unit_off[u + 1] - tb->host.unit_off[u] > dash::kMaxUnitItems)
-      return DASH_ERR_UNSUPPORTED;
+  const Tables& host = tb->host;
+  const int U = host.units();
   const long total_units = heads * U;
   int grid = 0, p_eff = 0, dynamic = 0;
   if (U == 0) {
     // no live pair at all: only the dead-tile clears below run
-  } else if (tb->host.needs_static()) {
+  } else if (host.needs_static()) {
     p_eff = (maxco / U) * U;
     if (p_eff < 1) return DASH_ERR_UNSUPPORTED;  // a whole head must be resident
     if (p_eff > total_units) p_eff = (int)total_units;
@@ -398,13 +513,45 @@ dash_status run_bwd(const dash_attn_desc* desc, dash_schedule schedule, const vo
     grid = (int)std::min<long>(maxco, total_units);
     p_eff = grid;
   }
+  int xcd_mode = ordered ? 1 : 0;
+  if (dbg && dbg->placement) xcd_mode = dbg->placement - 1;
+  int unit_major = dynamic ? (unit_major_for(mkey, host, s, heads, maxco, xcd_mode != 0) ? 1 : 0)
+                           : 0;
+  if (dbg && dbg->unit_order && dynamic) unit_major = dbg->unit_order - 1;
+  int n_dead_q = 0, n_dead_kv = 0;
+  if (!plain) {
+    const MaskEntry* me = mask_entry(mkey);
+    n_dead_q = me->n_dead_q;
+    n_dead_kv = me->n_dead_kv;
+    st = pinned_blob(mkey, tb);
+    if (st != DASH_OK) return st;
+  }
 
-  hipStream_t strm = (hipStream_t)stream;
-  char* ws = (char*)workspace;
-  // ordered schedules never read an accumulator element before its first
-  // contributor wrote it, so only the header and counters need clearing
-  const size_t clear_bytes = ordered ? w.acc_off : w.total;
-  if (dash::launch_zero_u32((uint32_t*)ws, clear_bytes / 4, strm) != hipSuccess) return DASH_ERR_HIP;
+  // workspace prologue: clear the header and counters (and, for the atomic
+  // schedule, the accumulator); write a plain mask's tables.  Ordered
+  // schedules never read an accumulator element before its first
+  // contributor wrote it.
+  dash::PrologueArgs pa;
+  pa.clear = (uint32_t*)ws;
+  pa.clear_words = w.unit_off_off / 4;
+  pa.clear2 = ordered ? nullptr : (uint32_t*)(ws + w.acc_off);
+  pa.clear2_words = ordered ? 0 : (w.total - w.acc_off) / 4;
+  pa.n = plain ? n : 0;
+  pa.causal = mkey.causal;
+  pa.sched = (int)s;
+  pa.units = U;
+  pa.items = plain ? dash::plain::items(n, mkey.causal != 0) : 0;
+  pa.unit_off = (int*)(ws + w.unit_off_off);
+  pa.item = (int2*)(ws + w.items_off);
+  if (dash::launch_bwd_prologue(pa, strm) != hipSuccess) return DASH_ERR_HIP;
+  if (!plain) {
+    // special masks: the host-built tables, copied on the caller's stream
+    if (hipMemcpyAsync(ws + w.unit_off_off, tb->pinned, tb->bytes, hipMemcpyHostToDevice, strm) !=
+            hipSuccess ||
+        hipEventRecord(tb->used, strm) != hipSuccess)
+      return DASH_ERR_HIP;
+  }
+  lock.unlock();
 
   dash::BwdArgs a;
   a.q = q;
@@ -419,8 +566,8 @@ dash_status run_bwd(const dash_attn_desc* desc, dash_schedule schedule, const vo
   a.dq_accum = (float*)(ws + w.acc_off);
   a.counters = (uint32_t*)(ws + w.counters_off);
   a.header = (uint32_t*)ws;
-  a.unit_off = tb->d_unit_off;
-  a.items = tb->d_items;
+  a.unit_off = (const int*)(ws + w.unit_off_off);
+  a.items = (const int2*)(ws + w.items_off);
   a.N = desc->N;
   a.n_tiles = n;
   dash::mask_bounds(mkey.causal != 0, mkey.window, &a.mask_lo, &a.mask_hi);
@@ -431,11 +578,8 @@ dash_status run_bwd(const dash_attn_desc* desc, dash_schedule schedule, const vo
   // placement: the ordered schedules run each head on one XCD with its
   // accumulator coherent in that XCD's L2 (measured as fast or faster on
   // every workload); the atomic reference gains nothing from it
-  a.xcd_mode = ordered ? 1 : 0;
-  if (dbg && dbg->placement) a.xcd_mode = dbg->placement - 1;
-  a.unit_major = dynamic ? (unit_major_for(mkey, tb->host, s, heads, maxco, a.xcd_mode != 0) ? 1 : 0)
-                         : 0;
-  if (dbg && dbg->unit_order && dynamic) a.unit_major = dbg->unit_order - 1;
+  a.xcd_mode = xcd_mode;
+  a.unit_major = unit_major;
   a.scale = scale_of(desc);
   a.scale_log2 = a.scale * 1.4426950408889634f;
   a.spin_limit = (dbg && dbg->spin_limit) ? dbg->spin_limit : kDefaultSpin;
@@ -459,15 +603,15 @@ dash_status run_bwd(const dash_attn_desc* desc, dash_schedule schedule, const vo
   // gradient rows no pair touches: dQ of Q blocks that see no key (the
   // atomic path's conversion already writes them), dK and dV of KV tiles no
   // query sees
-  if (ordered && dm->n_dead_q &&
-      dash::launch_zero_tiles(desc->dtype, dq, dm->d_dead, dm->n_dead_q, bc, desc->d, desc->N,
-                              (int)heads, strm) != hipSuccess)
+  const int* dead = (const int*)(ws + w.dead_off);
+  if (ordered && n_dead_q &&
+      dash::launch_zero_tiles(desc->dtype, dq, dead, n_dead_q, bc, desc->d, desc->N, (int)heads,
+                              strm) != hipSuccess)
     return DASH_ERR_HIP;
-  if (dm->n_dead_kv) {
-    const int* kvs = dm->d_dead + dm->n_dead_q;
-    if (dash::launch_zero_tiles(desc->dtype, dk, kvs, dm->n_dead_kv, bc, desc->d, desc->N,
+  if (n_dead_kv) {
+    if (dash::launch_zero_tiles(desc->dtype, dk, dead + n_dead_q, n_dead_kv, bc, desc->d, desc->N,
                                 (int)heads, strm) != hipSuccess ||
-        dash::launch_zero_tiles(desc->dtype, dv, kvs, dm->n_dead_kv, bc, desc->d, desc->N,
+        dash::launch_zero_tiles(desc->dtype, dv, dead + n_dead_q, n_dead_kv, bc, desc->d, desc->N,
                                 (int)heads, strm) != hipSuccess)
       return DASH_ERR_HIP;
   }
@@ -478,6 +622,24 @@ dash_status run_bwd(const dash_attn_desc* desc, dash_schedule schedule, const vo
       return DASH_ERR_HIP;
   }
   return DASH_OK;
+}
+
+// Host entry points that build tables can run out of host memory; nothing
+// may throw across the C boundary.
+template <typename F>
+dash_status guarded(F&& f) {
+  try {
+    return f();
+  } catch (const std::bad_alloc&) {
+    return DASH_ERR_HOST_MEMORY;
+  } catch (...) {
+    return DASH_ERR_INVALID_ARG;
+  }
+}
+
+// The DAG calculator numbers 2 nodes per item with 32-bit indices.
+bool predict_fits(const Tables& t, long heads) {
+  return 2.0 * (double)t.items() * (double)heads < 2147483647.0;
 }
 
 }  // namespace
@@ -493,6 +655,7 @@ const char* dash_status_string(dash_status s) {
     case DASH_ERR_HIP: return "HIP runtime error";
     case DASH_ERR_SCHEDULE_INVALID: return "schedule tables failed validation";
     case DASH_ERR_ORDER_TIMEOUT: return "ordered dQ add timed out";
+    case DASH_ERR_HOST_MEMORY: return "out of host memory";
   }
   return "unknown status";
 }
@@ -511,36 +674,70 @@ int32_t dash_attn_bwd_subtile(const dash_attn_desc* desc) {
   return br;
 }
 
+size_t dash_attn_fwd_workspace_size(const dash_attn_desc* desc) {
+  if (check_desc(desc) != DASH_OK) return 0;
+  const MaskKey mkey = mask_key(desc);
+  if (mkey.block.empty()) return 0;
+  return align256((size_t)mkey.n * mkey.n);
+}
+
+dash_status dash_attn_fwd_ws(const dash_attn_desc* desc, const void* q, const void* k,
+                             const void* v, void* o, float* lse, void* workspace,
+                             size_t workspace_bytes, void* stream) {
+  return guarded([&]() -> dash_status {
+    dash_status st = check_desc(desc);
+    if (st != DASH_OK) return st;
+    if (!q || !k || !v || !o || !lse) return DASH_ERR_INVALID_ARG;
+    dash::FwdArgs a;
+    a.q = q;
+    a.k = k;
+    a.v = v;
+    a.o = o;
+    a.lse = lse;
+    a.N = desc->N;
+    a.BH = desc->B * desc->H;
+    a.scale_log2 = scale_of(desc) * 1.4426950408889634f;
+    const MaskKey mkey = mask_key(desc);
+    a.live = nullptr;
+    a.n_tiles = mkey.n;
+    a.tile = mkey.tile;
+    dash::mask_bounds(mkey.causal != 0, mkey.window, &a.mask_lo, &a.mask_hi);
+    hipStream_t strm = (hipStream_t)stream;
+    std::unique_lock<std::mutex> lock(g_mu, std::defer_lock);
+    if (!mkey.block.empty()) {
+      // block masks: the tile liveness, copied into the caller's workspace
+      const size_t bytes = (size_t)mkey.n * mkey.n;
+      if (!workspace || workspace_bytes < align256(bytes) || ((uintptr_t)workspace & 255u))
+        return DASH_ERR_WORKSPACE;
+      lock.lock();
+      MaskEntry* me = mask_entry(mkey);
+      if (!me->pinned_live) {
+        if (hipHostMalloc((void**)&me->pinned_live, bytes, hipHostMallocDefault) != hipSuccess) {
+          me->pinned_live = nullptr;
+          return DASH_ERR_HIP;
+        }
+        std::memcpy(me->pinned_live, me->host.live.data(), bytes);
+      }
+      if (!me->used && hipEventCreateWithFlags(&me->used, hipEventDisableTiming) != hipSuccess) {
+        me->used = nullptr;
+        return DASH_ERR_HIP;
+      }
+      if (hipMemcpyAsync(workspace, me->pinned_live, bytes, hipMemcpyHostToDevice, strm) !=
+              hipSuccess ||
+          hipEventRecord(me->used, strm) != hipSuccess)
+        return DASH_ERR_HIP;
+      lock.unlock();
+      a.live = (const uint8_t*)workspace;
+    }
+    if (dash::launch_fwd(desc->dtype, desc->d, mkey.masked(), a, strm) != hipSuccess)
+      return DASH_ERR_HIP;
+    return DASH_OK;
+  });
+}
+
 dash_status dash_attn_fwd(const dash_attn_desc* desc, const void* q, const void* k, const void* v,
                           void* o, float* lse, void* stream) {
-  dash_status st = check_desc(desc);
-  if (st != DASH_OK) return st;
-  if (!q || !k || !v || !o || !lse) return DASH_ERR_INVALID_ARG;
-  dash::FwdArgs a;
-  a.q = q;
-  a.k = k;
-  a.v = v;
-  a.o = o;
-  a.lse = lse;
-  a.N = desc->N;
-  a.BH = desc->B * desc->H;
-  a.scale_log2 = scale_of(desc) * 1.4426950408889634f;
-  const MaskKey mkey = mask_key(desc);
-  a.live = nullptr;
-  a.n_tiles = mkey.n;
-  a.tile = mkey.tile;
-  dash::mask_bounds(mkey.causal != 0, mkey.window, &a.mask_lo, &a.mask_hi);
-  if (!mkey.block.empty()) {
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return DASH_ERR_HIP;
-    const DevMask* dm = nullptr;
-    st = get_mask(dev, mkey, &dm);
-    if (st != DASH_OK) return st;
-    a.live = dm->d_live;
-  }
-  if (dash::launch_fwd(desc->dtype, desc->d, mkey.masked(), a, (hipStream_t)stream) != hipSuccess)
-    return DASH_ERR_HIP;
-  return DASH_OK;
+  return dash_attn_fwd_ws(desc, q, k, v, o, lse, nullptr, 0, stream);
 }
 
 dash_status dash_attn_bwd_preprocess(const dash_attn_desc* desc, const void* o, const void* dout,
@@ -555,21 +752,27 @@ dash_status dash_attn_bwd_preprocess(const dash_attn_desc* desc, const void* o, 
   return DASH_OK;
 }
 
-dash_status dash_attn_bwd_workspace_size(const dash_attn_desc* desc, dash_schedule schedule,
-                                         size_t* bytes) {
-  dash_status st = check_desc(desc);
-  if (st != DASH_OK) return st;
-  if (!sched_ok_run(schedule) || !bytes) return DASH_ERR_INVALID_ARG;
-  *bytes = layout(desc).total;
-  return DASH_OK;
+size_t dash_attn_bwd_workspace_size(const dash_attn_desc* desc, dash_schedule schedule) {
+  if (check_desc(desc) != DASH_OK || !sched_ok_run(schedule)) return 0;
+  try {
+    const MaskKey mkey = mask_key(desc);
+    // longer units than the kernel stages cannot run
+    if (plain_key(mkey) && mkey.n > dash::kMaxUnitItems) return 0;
+    std::lock_guard<std::mutex> lock(g_mu);
+    return layout(desc, live_pairs_of(mkey)).total;
+  } catch (...) {
+    return 0;
+  }
 }
 
 dash_status dash_attn_bwd(const dash_attn_desc* desc, dash_schedule schedule, const void* q,
                           const void* k, const void* v, const void* dout, const float* lse,
                           const float* delta, void* dq, void* dk, void* dv, void* workspace,
                           size_t workspace_bytes, void* stream) {
-  return run_bwd(desc, schedule, q, k, v, dout, lse, delta, dq, dk, dv, workspace,
-                 workspace_bytes, nullptr, stream);
+  return guarded([&] {
+    return run_bwd(desc, schedule, q, k, v, dout, lse, delta, dq, dk, dv, workspace,
+                   workspace_bytes, nullptr, stream);
+  });
 }
 
 dash_status dash_attn_bwd_debug(const dash_attn_desc* desc, dash_schedule schedule, const void* q,
@@ -577,8 +780,10 @@ dash_status dash_attn_bwd_debug(const dash_attn_desc* desc, dash_schedule schedu
                                 const float* delta, void* dq, void* dk, void* dv, void* workspace,
                                 size_t workspace_bytes, const dash_bwd_debug* dbg, void* stream) {
   if (!dbg) return DASH_ERR_INVALID_ARG;
-  return run_bwd(desc, schedule, q, k, v, dout, lse, delta, dq, dk, dv, workspace,
-                 workspace_bytes, dbg, stream);
+  return guarded([&] {
+    return run_bwd(desc, schedule, q, k, v, dout, lse, delta, dq, dk, dv, workspace,
+                   workspace_bytes, dbg, stream);
+  });
 }
 
 dash_status dash_attn_bwd_tune(const dash_attn_desc* desc, const void* q, const void* k,
@@ -586,84 +791,94 @@ dash_status dash_attn_bwd_tune(const dash_attn_desc* desc, const void* q, const 
                               const float* delta, void* dq, void* dk, void* dv, void* workspace,
                               size_t workspace_bytes, int32_t reps, dash_schedule* choice,
                               float* times_ms, void* stream) {
-  dash_status st = check_desc(desc);
-  if (st != DASH_OK) return st;
-  if (reps < 1 || reps > 1000 || !choice) return DASH_ERR_INVALID_ARG;
-  if (!q || !k || !v || !dout || !lse || !delta || !dq || !dk || !dv || !workspace)
-    return DASH_ERR_INVALID_ARG;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return DASH_ERR_HIP;
-  const MaskKey mkey = mask_key(desc);
-  const DevMask* dm = nullptr;
-  st = get_mask(dev, mkey, &dm);
-  if (st != DASH_OK) return st;
-  int maxco = 0;
-  st = get_coresident(dev, desc->dtype, desc->d, dm->host.any_partial(), true, &maxco);
-  if (st != DASH_OK) return st;
-  hipStream_t strm = (hipStream_t)stream;
-  hipEvent_t ev[2];
-  if (hipEventCreate(&ev[0]) != hipSuccess) return DASH_ERR_HIP;
-  if (hipEventCreate(&ev[1]) != hipSuccess) {
-    (void)hipEventDestroy(ev[0]);
-    return DASH_ERR_HIP;
-  }
-  const dash_schedule cand[3] = {DASH_SCHED_NAIVE, DASH_SCHED_DESCENDING, DASH_SCHED_SHIFT};
-  float t[3];
-  int best = -1;
-  for (int i = 0; i < 3 && st == DASH_OK; ++i) {
-    t[i] = NAN;
-    Tables tb;
-    if (!dash::build_tables(dm->host, (Sched)cand[i], tb)) continue;
-    if (tb.needs_static() && tb.units() > maxco) continue;
-    // one untimed launch, then `reps` timed ones
-    st = run_bwd(desc, cand[i], q, k, v, dout, lse, delta, dq, dk, dv, workspace, workspace_bytes,
-                 nullptr, stream);
-    if (st == DASH_ERR_UNSUPPORTED) {  // e.g. a unit longer than the kernel's work list
-      st = DASH_OK;
-      continue;
+  return guarded([&]() -> dash_status {
+    dash_status st = check_desc(desc);
+    if (st != DASH_OK) return st;
+    if (reps < 1 || reps > 1000 || !choice) return DASH_ERR_INVALID_ARG;
+    if (!q || !k || !v || !dout || !lse || !delta || !dq || !dk || !dv || !workspace)
+      return DASH_ERR_INVALID_ARG;
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return DASH_ERR_HIP;
+    const MaskKey mkey = mask_key(desc);
+    bool masked = false;
+    {
+      std::lock_guard<std::mutex> lock(g_mu);
+      masked = any_partial(mkey);
     }
-    if (st != DASH_OK) break;
-    if (hipEventRecord(ev[0], strm) != hipSuccess) st = DASH_ERR_HIP;
-    for (int r = 0; r < reps && st == DASH_OK; ++r)
+    int maxco = 0;
+    st = get_coresident(dev, desc->dtype, desc->d, masked, true, &maxco);
+    if (st != DASH_OK) return st;
+    hipStream_t strm = (hipStream_t)stream;
+    hipEvent_t ev[2];
+    if (hipEventCreate(&ev[0]) != hipSuccess) return DASH_ERR_HIP;
+    if (hipEventCreate(&ev[1]) != hipSuccess) {
+      (void)hipEventDestroy(ev[0]);
+      return DASH_ERR_HIP;
+    }
+    const dash_schedule cand[3] = {DASH_SCHED_NAIVE, DASH_SCHED_DESCENDING, DASH_SCHED_SHIFT};
+    float t[3];
+    int best = -1;
+    for (int i = 0; i < 3 && st == DASH_OK; ++i) {
+      t[i] = NAN;
+      {
+        std::lock_guard<std::mutex> lock(g_mu);
+        TabEntry* tb = nullptr;
+        if (tab_entry(mkey, (Sched)cand[i], &tb) != DASH_OK) continue;
+        if (tb->host.needs_static() && tb->host.units() > maxco) continue;
+      }
+      // one untimed launch, then `reps` timed ones
       st = run_bwd(desc, cand[i], q, k, v, dout, lse, delta, dq, dk, dv, workspace,
                    workspace_bytes, nullptr, stream);
-    if (st != DASH_OK) break;
-    if (hipEventRecord(ev[1], strm) != hipSuccess || hipEventSynchronize(ev[1]) != hipSuccess) {
-      st = DASH_ERR_HIP;
-      break;
+      if (st == DASH_ERR_UNSUPPORTED) {  // e.g. a unit longer than the kernel's work list
+        st = DASH_OK;
+        continue;
+      }
+      if (st != DASH_OK) break;
+      if (hipEventRecord(ev[0], strm) != hipSuccess) st = DASH_ERR_HIP;
+      for (int r = 0; r < reps && st == DASH_OK; ++r)
+        st = run_bwd(desc, cand[i], q, k, v, dout, lse, delta, dq, dk, dv, workspace,
+                     workspace_bytes, nullptr, stream);
+      if (st != DASH_OK) break;
+      if (hipEventRecord(ev[1], strm) != hipSuccess || hipEventSynchronize(ev[1]) != hipSuccess) {
+        st = DASH_ERR_HIP;
+        break;
+      }
+      // every launch clears the status word, so a time-out of this
+      // candidate is visible only now, before the next one runs
+      st = read_status(workspace);
+      if (st != DASH_OK) break;
+      float ms = 0.f;
+      if (hipEventElapsedTime(&ms, ev[0], ev[1]) != hipSuccess) {
+        st = DASH_ERR_HIP;
+        break;
+      }
+      t[i] = ms / reps;
+      if (best < 0 || t[i] < t[best]) best = i;
     }
-    float ms = 0.f;
-    if (hipEventElapsedTime(&ms, ev[0], ev[1]) != hipSuccess) {
-      st = DASH_ERR_HIP;
-      break;
+    (void)hipEventDestroy(ev[0]);
+    (void)hipEventDestroy(ev[1]);
+    if (st != DASH_OK) return st;
+    if (best < 0) return DASH_ERR_UNSUPPORTED;
+    {
+      const int h = (int)std::min<long>((long)desc->B * desc->H, 1L << 30);
+      std::lock_guard<std::mutex> lock(g_mu);
+      g_auto[std::make_tuple(mkey, h, maxco)] = (Sched)cand[best];
     }
-    t[i] = ms / reps;
-    if (best < 0 || t[i] < t[best]) best = i;
-  }
-  (void)hipEventDestroy(ev[0]);
-  (void)hipEventDestroy(ev[1]);
-  if (st != DASH_OK) return st;
-  // a time-out of an ordered add would make the times meaningless
-  st = dash_attn_bwd_status(workspace, stream);
-  if (st != DASH_OK) return st;
-  if (best < 0) return DASH_ERR_UNSUPPORTED;
-  {
-    const int h = (int)std::min<long>((long)desc->B * desc->H, 1L << 30);
-    std::lock_guard<std::mutex> lock(g_mu);
-    g_auto[std::make_tuple(mkey, h, maxco)] = (Sched)cand[best];
-  }
-  *choice = cand[best];
-  if (times_ms) std::memcpy(times_ms, t, sizeof(t));
-  return DASH_OK;
+    *choice = cand[best];
+    if (times_ms) std::memcpy(times_ms, t, sizeof(t));
+    return DASH_OK;
+  });
+}
+
+dash_status dash_status_query(const void* workspace) {
+  if (!workspace) return DASH_ERR_INVALID_ARG;
+  return read_status(workspace);
 }
 
 dash_status dash_attn_bwd_status(const void* workspace, void* stream) {
   if (!workspace) return DASH_ERR_INVALID_ARG;
   if (hipStreamSynchronize((hipStream_t)stream) != hipSuccess) return DASH_ERR_HIP;
-  uint32_t word = 0;
-  if (hipMemcpy(&word, workspace, sizeof(word), hipMemcpyDeviceToHost) != hipSuccess)
-    return DASH_ERR_HIP;
-  return word ? DASH_ERR_ORDER_TIMEOUT : DASH_OK;
+  return read_status(workspace);
 }
 
 dash_status dash_schedule_tables(int32_t n, int32_t causal, dash_schedule schedule,
@@ -672,106 +887,17 @@ dash_status dash_schedule_tables(int32_t n, int32_t causal, dash_schedule schedu
   if (n < 1 || n > 32767 || (causal != 0 && causal != 1) || !sched_ok(schedule) || !n_units ||
       !unit_offsets || !item_kv || !item_q || !rank)
     return DASH_ERR_INVALID_ARG;
-  Tables t;
-  if (!dash::build_tables(n, causal != 0, (Sched)schedule, t)) return DASH_ERR_UNSUPPORTED;
-  if (dash::validate_tables(t)[0] != '\0') return DASH_ERR_SCHEDULE_INVALID;
-  *n_units = t.units();
-  std::memcpy(unit_offsets, t.unit_off.data(), sizeof(int) * t.unit_off.size());
-  std::memcpy(item_kv, t.kv.data(), sizeof(int) * t.kv.size());
-  std::memcpy(item_q, t.q.data(), sizeof(int) * t.q.size());
-  std::memcpy(rank, t.rank.data(), sizeof(int) * t.rank.size());
-  return DASH_OK;
-}
-
-dash_status dash_schedule_predict(int32_t n, int32_t causal, dash_schedule schedule, int32_t heads,
-                                  int32_t slots, const double cost[4], double out[4]) {
-  if (n < 1 || n > 32767 || (causal != 0 && causal != 1) || !sched_ok(schedule) || heads < 1 ||
-      slots < 1 || !cost || !out)
-    return DASH_ERR_INVALID_ARG;
-  for (int i = 0; i < 4; ++i)
-    if (!(cost[i] >= 0.0) || !std::isfinite(cost[i])) return DASH_ERR_INVALID_ARG;
-  Tables t;
-  if (!dash::build_tables(n, causal != 0, (Sched)schedule, t)) return DASH_ERR_UNSUPPORTED;
-  if (dash::validate_tables(t)[0] != '\0') return DASH_ERR_SCHEDULE_INVALID;
-  if (t.needs_static() && t.units() > slots) return DASH_ERR_UNSUPPORTED;
-  dash::DagResult r;
-  if (!dash::dag_predict(t, heads, slots, cost, r)) return DASH_ERR_SCHEDULE_INVALID;
-  out[0] = r.makespan;
-  out[1] = r.total_wait;
-  out[2] = r.max_slot_idle;
-  out[3] = r.lower_bound;
-  return DASH_OK;
-}
-
-dash_status dash_attn_bwd_resolve_schedule(const dash_attn_desc* desc, dash_schedule schedule,
-                                           dash_schedule* resolved) {
-  dash_status st = check_desc(desc);
-  if (st != DASH_OK) return st;
-  if (!sched_ok_run(schedule) || !resolved) return DASH_ERR_INVALID_ARG;
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess) return DASH_ERR_HIP;
-  const MaskKey mkey = mask_key(desc);
-  const DevMask* dm = nullptr;
-  st = get_mask(dev, mkey, &dm);
-  if (st != DASH_OK) return st;
-  int maxco = 0;
-  st = get_coresident(dev, desc->dtype, desc->d, dm->host.any_partial(),
-                      schedule != DASH_SCHED_ATOMIC, &maxco);
-  if (st != DASH_OK) return st;
-  Sched s = Sched::Naive;
-  st = resolve_schedule(schedule, mkey, dm->host, (long)desc->B * desc->H, maxco, &s);
-  if (st != DASH_OK) return st;
-  *resolved = (dash_schedule)s;
-  return DASH_OK;
-}
-
-dash_status dash_schedule_choose(int32_t n, int32_t causal, int32_t heads, int32_t slots,
-                                 const double* cost, dash_schedule* choice, double* predicted) {
-  if (n < 1 || n > 32767 || (causal != 0 && causal != 1) || heads < 1 || slots < 1 || !choice)
-    return DASH_ERR_INVALID_ARG;
-  const double* c = cost ? cost : kDefaultCost;
-  for (int i = 0; i < 4; ++i)
-    if (!(c[i] >= 0.0) || !std::isfinite(c[i])) return DASH_ERR_INVALID_ARG;
-  Sched s = Sched::Naive;
-  double pred[3];
-  const dash_status st = choose_schedule(dash::plain_mask(n, causal != 0), heads, slots, c, &s, pred);
-  if (st != DASH_OK) return st;
-  *choice = (dash_schedule)s;
-  if (predicted) std::memcpy(predicted, pred, sizeof(pred));
-  return DASH_OK;
-}
-
-dash_status dash_attn_schedule_tables(const dash_attn_desc* desc, dash_schedule schedule,
-                                      int32_t sizes[4], int32_t* unit_offsets, int32_t* item_kv,
-                                      int32_t* item_q, int32_t* item_step, uint8_t* item_partial,
-                                      int32_t* rank) {
-  dash_status st = check_desc(desc);
-  if (st != DASH_OK) return st;
-  if (!sched_ok(schedule) || !sizes) return DASH_ERR_INVALID_ARG;
-  const MaskKey mkey = mask_key(desc);
-  const dash::TileMask m = tile_mask(mkey);
-  Tables t;
-  if (!dash::build_tables(m, (Sched)schedule, t)) return DASH_ERR_UNSUPPORTED;
-  if (dash::validate_tables(t)[0] != '\0') return DASH_ERR_SCHEDULE_INVALID;
-  const bool fill = unit_offsets && item_kv && item_q && item_step && item_partial && rank;
-  if (fill && (sizes[0] != t.n || sizes[1] != t.units() || sizes[2] != t.items()))
-    return DASH_ERR_INVALID_ARG;
-  sizes[0] = t.n;
-  sizes[1] = t.units();
-  sizes[2] = t.items();
-  sizes[3] = t.needs_static() ? 1 : 0;
-  if (!fill) return DASH_OK;
-  std::memcpy(unit_offsets, t.unit_off.data(), sizeof(int) * t.unit_off.size());
-  if (t.items()) {
+  return guarded([&]() -> dash_status {
+    Tables t;
+    if (!dash::build_tables(n, causal != 0, (Sched)schedule, t)) return DASH_ERR_UNSUPPORTED;
+    if (dash::validate_tables(t)[0] != '\0') return DASH_ERR_SCHEDULE_INVALID;
+    *n_units = t.units();
+    std::memcpy(unit_offsets, t.unit_off.data(), sizeof(int) * t.unit_off.size());
     std::memcpy(item_kv, t.kv.data(), sizeof(int) * t.kv.size());
     std::memcpy(item_q, t.q.data(), sizeof(int) * t.q.size());
-  }
-  for (int i = 0; i < t.items(); ++i) {
-    item_step[i] = t.step.empty() ? -1 : t.step[i];
-    item_partial[i] = t.partial[(size_t)t.q[i] * t.n + t.kv[i]];
-  }
-  std::memcpy(rank, t.rank.data(), sizeof(int) * t.rank.size());
-  return DASH_OK;
+    std::memcpy(rank, t.rank.data(), sizeof(int) * t.rank.size());
+    return DASH_OK;
+  });
 }
 
 dash_status dash_attn_schedule_predict(const dash_attn_desc* desc, dash_schedule schedule,
@@ -783,18 +909,116 @@ dash_status dash_attn_schedule_predict(const dash_attn_desc* desc, dash_schedule
     return DASH_ERR_INVALID_ARG;
   for (int i = 0; i < 4; ++i)
     if (!(cost[i] >= 0.0) || !std::isfinite(cost[i])) return DASH_ERR_INVALID_ARG;
-  Tables t;
-  if (!dash::build_tables(tile_mask(mask_key(desc)), (Sched)schedule, t)) return DASH_ERR_UNSUPPORTED;
-  if (dash::validate_tables(t)[0] != '\0') return DASH_ERR_SCHEDULE_INVALID;
-  if (t.needs_static() && t.units() > slots) return DASH_ERR_UNSUPPORTED;
-  dash::DagResult r;
-  if (!dash::dag_predict(t, desc->B * desc->H, slots, cost, r, unit_major != 0))
-    return DASH_ERR_SCHEDULE_INVALID;
-  out[0] = r.makespan;
-  out[1] = r.total_wait;
-  out[2] = r.max_slot_idle;
-  out[3] = r.lower_bound;
-  return DASH_OK;
+  return guarded([&]() -> dash_status {
+    const MaskKey mkey = mask_key(desc);
+    if (plain_key(mkey) && mkey.n + 1 > dash::kMaxUnitItems) return DASH_ERR_UNSUPPORTED;
+    Tables t;
+    if (!dash::build_tables(tile_mask(mkey), (Sched)schedule, t)) return DASH_ERR_UNSUPPORTED;
+    if (dash::validate_tables(t)[0] != '\0') return DASH_ERR_SCHEDULE_INVALID;
+    if (t.needs_static() && t.units() > slots) return DASH_ERR_UNSUPPORTED;
+    const long heads = (long)desc->B * desc->H;
+    if (!predict_fits(t, heads)) return DASH_ERR_UNSUPPORTED;
+    dash::DagResult r;
+    if (!dash::dag_predict(t, (int)heads, slots, cost, r, unit_major != 0))
+      return DASH_ERR_SCHEDULE_INVALID;
+    out[0] = r.makespan;
+    out[1] = r.total_wait;
+    out[2] = r.max_slot_idle;
+    out[3] = r.lower_bound;
+    return DASH_OK;
+  });
+}
+
+dash_status dash_schedule_predict(const dash_attn_desc* desc, dash_schedule schedule,
+                                  int32_t slots, const double cost[4], double out[4]) {
+  return dash_attn_schedule_predict(desc, schedule, slots, 0, cost, out);
+}
+
+dash_status dash_attn_bwd_resolve_schedule(const dash_attn_desc* desc, dash_schedule schedule,
+                                           dash_schedule* resolved) {
+  dash_status st = check_desc(desc);
+  if (st != DASH_OK) return st;
+  if (!sched_ok_run(schedule) || !resolved) return DASH_ERR_INVALID_ARG;
+  return guarded([&]() -> dash_status {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return DASH_ERR_HIP;
+    const MaskKey mkey = mask_key(desc);
+    bool masked = false;
+    {
+      std::lock_guard<std::mutex> lock(g_mu);
+      masked = any_partial(mkey);
+    }
+    int maxco = 0;
+    dash_status st2 = get_coresident(dev, desc->dtype, desc->d, masked,
+                                     schedule != DASH_SCHED_ATOMIC, &maxco);
+    if (st2 != DASH_OK) return st2;
+    Sched s = Sched::Naive;
+    std::lock_guard<std::mutex> lock(g_mu);
+    st2 = resolve_schedule(schedule, mkey, (long)desc->B * desc->H, maxco, &s);
+    if (st2 != DASH_OK) return st2;
+    *resolved = (dash_schedule)s;
+    return DASH_OK;
+  });
+}
+
+dash_status dash_schedule_choose(int32_t n, int32_t causal, int32_t heads, int32_t slots,
+                                 const double* cost, dash_schedule* choice, double* predicted) {
+  if (n < 1 || n > 32767 || (causal != 0 && causal != 1) || heads < 1 || slots < 1 || !choice)
+    return DASH_ERR_INVALID_ARG;
+  const double* c = cost ? cost : kDefaultCost;
+  for (int i = 0; i < 4; ++i)
+    if (!(c[i] >= 0.0) || !std::isfinite(c[i])) return DASH_ERR_INVALID_ARG;
+  return guarded([&]() -> dash_status {
+    Sched s = Sched::Naive;
+    double pred[3];
+    const dash_status st =
+        choose_schedule(dash::plain_mask(n, causal != 0), heads, slots, c, &s, pred);
+    if (st != DASH_OK) return st;
+    *choice = (dash_schedule)s;
+    if (predicted) std::memcpy(predicted, pred, sizeof(pred));
+    return DASH_OK;
+  });
+}
+
+dash_status dash_attn_schedule_tables(const dash_attn_desc* desc, dash_schedule schedule,
+                                      int32_t sizes[4], int32_t* unit_offsets, int32_t* item_kv,
+                                      int32_t* item_q, int32_t* item_step, uint8_t* item_partial,
+                                      int32_t* rank) {
+  dash_status st = check_desc(desc);
+  if (st != DASH_OK) return st;
+  if (!sched_ok(schedule) || !sizes) return DASH_ERR_INVALID_ARG;
+  return guarded([&]() -> dash_status {
+    const MaskKey mkey = mask_key(desc);
+    Tables t;
+    {
+      // the tables a launch runs: for a plain mask this also checks them
+      // against the closed forms the device writes
+      std::lock_guard<std::mutex> lock(g_mu);
+      TabEntry* tb = nullptr;
+      const dash_status st2 = tab_entry(mkey, (Sched)schedule, &tb);
+      if (st2 != DASH_OK) return st2;
+      t = tb->host;
+    }
+    const bool fill = unit_offsets && item_kv && item_q && item_step && item_partial && rank;
+    if (fill && (sizes[0] != t.n || sizes[1] != t.units() || sizes[2] != t.items()))
+      return DASH_ERR_INVALID_ARG;
+    sizes[0] = t.n;
+    sizes[1] = t.units();
+    sizes[2] = t.items();
+    sizes[3] = t.needs_static() ? 1 : 0;
+    if (!fill) return DASH_OK;
+    std::memcpy(unit_offsets, t.unit_off.data(), sizeof(int) * t.unit_off.size());
+    if (t.items()) {
+      std::memcpy(item_kv, t.kv.data(), sizeof(int) * t.kv.size());
+      std::memcpy(item_q, t.q.data(), sizeof(int) * t.q.size());
+    }
+    for (int i = 0; i < t.items(); ++i) {
+      item_step[i] = t.step.empty() ? -1 : t.step[i];
+      item_partial[i] = t.partial[(size_t)t.q[i] * t.n + t.kv[i]];
+    }
+    std::memcpy(rank, t.rank.data(), sizeof(int) * t.rank.size());
+    return DASH_OK;
+  });
 }
 
 dash_status dash_dag_longest_path(int32_t n_nodes, const double* weights, int32_t n_edges,
@@ -806,9 +1030,11 @@ dash_status dash_dag_longest_path(int32_t n_nodes, const double* weights, int32_
   for (int e = 0; e < n_edges; ++e)
     if (src[e] < 0 || src[e] >= n_nodes || dst[e] < 0 || dst[e] >= n_nodes)
       return DASH_ERR_INVALID_ARG;
-  if (!dash::dag_longest_path(n_nodes, weights, n_edges, src, dst, latency, start, finish))
-    return DASH_ERR_SCHEDULE_INVALID;
-  return DASH_OK;
+  return guarded([&]() -> dash_status {
+    if (!dash::dag_longest_path(n_nodes, weights, n_edges, src, dst, latency, start, finish))
+      return DASH_ERR_SCHEDULE_INVALID;
+    return DASH_OK;
+  });
 }
 
 dash_status dash_litmus_ordered_add(int32_t workgroups, int32_t len, const int32_t* turn,

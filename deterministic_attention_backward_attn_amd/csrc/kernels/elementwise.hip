@@ -3,6 +3,7 @@
 // litmus.
 #include "common.hpp"
 #include "launch.hpp"
+#include "plain_tables.hpp"
 
 namespace dash {
 
@@ -76,6 +77,37 @@ hipError_t launch_zero_u32(uint32_t* p, size_t n_words, hipStream_t stream) {
   if (blocks == 0) blocks = 1;
   hipLaunchKernelGGL(zero_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
                      reinterpret_cast<uint4*>(p), n16, p + n16 * 4, n_tail);
+  return hipGetLastError();
+}
+
+// Backward workspace prologue: the clears and, for a plain mask, the
+// schedule tables written from their closed forms (one thread per item),
+// in one launch.
+__global__ void __launch_bounds__(256) bwd_prologue_kernel(PrologueArgs a) {
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  const size_t t0 = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+  uint4* c1 = reinterpret_cast<uint4*>(a.clear);
+  for (size_t i = t0; i < a.clear_words / 4; i += stride) c1[i] = make_uint4(0u, 0u, 0u, 0u);
+  uint4* c2 = reinterpret_cast<uint4*>(a.clear2);
+  for (size_t i = t0; i < a.clear2_words / 4; i += stride) c2[i] = make_uint4(0u, 0u, 0u, 0u);
+  if (a.n <= 0) return;
+  const bool causal = a.causal != 0;
+  for (size_t u = t0; u <= (size_t)a.units; u += stride)
+    a.unit_off[u] = (int)plain::unit_off(a.n, causal, a.sched, (int)u);
+  for (size_t i = t0; i < (size_t)a.items; i += stride)
+    a.item[i] = plain::encode(a.n, causal, a.sched, (long)i);
+}
+
+hipError_t launch_bwd_prologue(const PrologueArgs& a, hipStream_t stream) {
+  if ((a.clear_words | a.clear2_words) & 3u) return hipErrorInvalidValue;
+  size_t work = a.clear_words / 4;
+  if (a.clear2_words / 4 > work) work = a.clear2_words / 4;
+  if ((size_t)a.items > work) work = (size_t)a.items;
+  if ((size_t)a.units + 1 > work) work = (size_t)a.units + 1;
+  size_t blocks = (work + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  if (blocks == 0) blocks = 1;
+  hipLaunchKernelGGL(bwd_prologue_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

@@ -84,6 +84,23 @@ hipError_t launch_fwd(int dtype, int d, bool masked, const FwdArgs& a, hipStream
 hipError_t launch_preprocess(int dtype, int d, const void* o, const void* dout, float* delta,
                              long rows, hipStream_t stream);
 hipError_t launch_zero_u32(uint32_t* p, size_t n_words, hipStream_t stream);
+
+// Workspace prologue of the backward: clear [clear, clear + clear_words)
+// and [clear2, clear2 + clear2_words), and, when n > 0, write the plain
+// mask's schedule tables (closed forms, plain_tables.hpp) for `sched`:
+// unit_off[0 .. units] and item[0 .. items).  Both clears are 16-byte
+// aligned multiples of 4 words.
+struct PrologueArgs {
+  uint32_t* clear = nullptr;
+  size_t clear_words = 0;
+  uint32_t* clear2 = nullptr;
+  size_t clear2_words = 0;
+  int n = 0, causal = 0, sched = 0, units = 0;
+  long items = 0;
+  int* unit_off = nullptr;
+  int2* item = nullptr;
+};
+hipError_t launch_bwd_prologue(const PrologueArgs& a, hipStream_t stream);
 // Zero rows [t * rows, t * rows + rows) of every head of a [BH, N, d] tensor
 // for each tile t in tiles[0..count) (a device array).
 hipError_t launch_zero_tiles(int dtype, void* base, const int* tiles, int count, int rows, int d,

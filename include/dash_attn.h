@@ -51,15 +51,22 @@
  *               asynchronous on it unless stated otherwise.
  *   Errors      Argument errors are returned synchronously, before any
  *               launch.  HIP launch errors return DASH_ERR_HIP.  A device
- *               ordering time-out is reported by dash_attn_bwd_status.
- *   Memory      dash_attn_bwd keeps a per-device cache of schedule tables
- *               (allocated on first use of a shape/schedule/mask, a few
- *               hundred KB at most for full and causal masks, up to tens
- *               of MB for windows and block masks at 2048 tiles per side,
- *               held until the process ends).  Everything else lives in
- *               caller buffers.
- *   Threads     Calls may come from several host threads; the table cache
- *               is locked.  Calls that share a workspace must be ordered
+ *               ordering time-out is read after the stream has been
+ *               synchronized, with dash_status_query.
+ *   Memory      The library allocates no device memory: every device
+ *               buffer, the backward's workspace included, is the
+ *               caller's.  The schedule tables of the full and causal
+ *               masks are written into the workspace by the backward's
+ *               first kernel (closed forms, no host-to-device copy).  For
+ *               windows and block masks the host builds the tables once
+ *               per mask and schedule and keeps them in pinned host memory
+ *               (a least-recently-used cache of 32 entries per kind, each
+ *               freed only after the last copy from it has completed); each
+ *               launch copies them into the workspace with hipMemcpyAsync
+ *               on the caller's stream.  The host also caches validated
+ *               tables and DAG predictions (host memory).
+ *   Threads     Calls may come from several host threads; the host caches
+ *               are locked.  Calls that share a workspace must be ordered
  *               on one stream.
  */
 #ifndef DASH_ATTN_H
@@ -79,7 +86,8 @@ typedef enum {
   DASH_ERR_WORKSPACE = 3,        /* workspace too small or misaligned */
   DASH_ERR_HIP = 4,              /* a HIP runtime call failed */
   DASH_ERR_SCHEDULE_INVALID = 5, /* schedule tables failed validation (cycle, coverage) */
-  DASH_ERR_ORDER_TIMEOUT = 6     /* an ordered dQ add waited past its spin limit */
+  DASH_ERR_ORDER_TIMEOUT = 6,    /* an ordered dQ add waited past its spin limit */
+  DASH_ERR_HOST_MEMORY = 7       /* a host-side table or cache allocation failed */
 } dash_status;
 
 typedef enum { DASH_F32 = 0, DASH_BF16 = 1 } dash_dtype;
@@ -135,9 +143,28 @@ int32_t dash_attn_bwd_subtile(const dash_attn_desc* desc);
  * Forward: O = softmax(s Q K^T) V and LSE.  q, k, v: inputs; o: output
  * [B,H,N,d]; lse: output [B,H,N] float.  Needed to produce the O and LSE
  * the backward consumes (the backward's inputs, explainer section 1).
+ * A block mask needs dash_attn_fwd_ws (DASH_ERR_WORKSPACE here).
  */
 dash_status dash_attn_fwd(const dash_attn_desc* desc, const void* q, const void* k,
                           const void* v, void* o, float* lse, void* stream);
+
+/*
+ * Device bytes the forward needs for this descriptor: 0 for the full,
+ * causal and window masks; with a block mask, room for the tile liveness
+ * (n tiles per side, n * n bytes rounded up to 256).  0 on invalid input.
+ */
+size_t dash_attn_fwd_workspace_size(const dash_attn_desc* desc);
+
+/*
+ * dash_attn_fwd with a caller-provided workspace (device, 256-byte aligned,
+ * at least dash_attn_fwd_workspace_size bytes; may be NULL when that is 0).
+ * With a block mask the call copies the tile liveness into it on `stream`
+ * (asynchronously, from pinned host memory); its contents on entry do not
+ * matter.  DASH_ERR_WORKSPACE if it is missing, too small or misaligned.
+ */
+dash_status dash_attn_fwd_ws(const dash_attn_desc* desc, const void* q, const void* k,
+                             const void* v, void* o, float* lse, void* workspace,
+                             size_t workspace_bytes, void* stream);
 
 /*
  * Backward preprocess: delta_i = sum_k dO_ik * O_ik in fp32 ([B,H,N]).
@@ -148,14 +175,16 @@ dash_status dash_attn_bwd_preprocess(const dash_attn_desc* desc, const void* o,
                                      const void* dout, float* delta, void* stream);
 
 /*
- * Workspace bytes dash_attn_bwd needs for this descriptor and schedule
- * (written to *bytes).  The size is the same for every schedule: the
- * schedules only reorder work (euno.news summary, "Results": memory
- * overhead unchanged).  Holds the fp32 dQ accumulator [B,H,N,d], the
- * per-Q-tile order counters, a work counter and a status word.
+ * Workspace bytes dash_attn_bwd needs for this descriptor and schedule;
+ * 0 for an invalid or unsupported descriptor or schedule.  The size is the
+ * same for every schedule: the schedules only reorder work (euno.news
+ * summary, "Results": memory overhead unchanged).  Layout, 256-byte
+ * aligned parts: a header (status word, work counters), the per-Q-sub-tile
+ * order counters, one head's schedule tables (unit offsets, items, tiles
+ * no pair touches; sized for the largest table of any schedule), and the
+ * fp32 dQ accumulator [B,H,N,d].
  */
-dash_status dash_attn_bwd_workspace_size(const dash_attn_desc* desc, dash_schedule schedule,
-                                         size_t* bytes);
+size_t dash_attn_bwd_workspace_size(const dash_attn_desc* desc, dash_schedule schedule);
 
 /*
  * Backward: dQ, dK, dV from Q, K, V, dO, LSE and delta (from
@@ -171,9 +200,17 @@ dash_status dash_attn_bwd(const dash_attn_desc* desc, dash_schedule schedule, co
                           size_t workspace_bytes, void* stream);
 
 /*
- * Device status of the last dash_attn_bwd on this workspace.  Synchronizes
- * `stream`, then reads the status word: DASH_OK, or DASH_ERR_ORDER_TIMEOUT
- * if some ordered add gave up waiting (its results are then not valid).
+ * Device status of the last dash_attn_bwd on this workspace: reads the
+ * status word with a synchronous copy; call it after the stream the
+ * backward ran on has been synchronized.  DASH_OK, or
+ * DASH_ERR_ORDER_TIMEOUT if some ordered add gave up waiting (that
+ * launch's results are then not valid); DASH_ERR_INVALID_ARG for NULL.
+ * Each dash_attn_bwd clears the word, so it reports the last launch only.
+ */
+dash_status dash_status_query(const void* workspace);
+
+/*
+ * Convenience: synchronizes `stream`, then dash_status_query(workspace).
  */
 dash_status dash_attn_bwd_status(const void* workspace, void* stream);
 
@@ -287,25 +324,26 @@ dash_status dash_schedule_tables(int32_t n, int32_t causal, dash_schedule schedu
                                  int32_t* item_q, int32_t* rank);
 
 /*
- * DAG critical-path prediction for `heads` heads of n tiles run on `slots`
- * persistent workgroups (explainer 2.1's DAG: compute and reduction nodes,
- * data and accumulation-order edges, one KV tile per processor chain).
+ * DAG critical-path prediction for the descriptor's B*H heads (its mask's
+ * tiles) run on `slots` persistent workgroups, heads taken one after the
+ * other (explainer 2.1's DAG: compute and reduction nodes, data and
+ * accumulation-order edges, one KV tile per processor chain).
  * cost[4] = {c_full, c_diag, r, h}: compute time of an unmasked item, of a
- * causal diagonal item, the dQ add, and the hand-off latency between
- * consecutive contributors.  out[4] = {makespan, total_wait,
- * max_slot_idle, lower_bound}.  Host only.
- * SHIFT needs slots >= units per head (else DASH_ERR_UNSUPPORTED).
+ * partial item (causal diagonal, window or block edge), the dQ add, and
+ * the hand-off latency between consecutive contributors.
+ * out[4] = {makespan, total_wait, max_slot_idle, lower_bound}.  Host only.
+ * SHIFT needs slots >= units per head (else DASH_ERR_UNSUPPORTED), and so
+ * does a graph of 2^31 nodes or more (2 per item and head).
  */
-dash_status dash_schedule_predict(int32_t n, int32_t causal, dash_schedule schedule,
-                                  int32_t heads, int32_t slots, const double cost[4],
-                                  double out[4]);
+dash_status dash_schedule_predict(const dash_attn_desc* desc, dash_schedule schedule,
+                                  int32_t slots, const double cost[4], double out[4]);
 
 /*
  * Schedule choice, host only (the explainer's significance section presents
  * DASH as a palette of strategies, heuristic and optimal, from which the
  * user picks by hardware and model configuration; this makes that pick from
- * the DAG model).  Predicts the makespan of NAIVE, DESCENDING and SHIFT with
- * dash_schedule_predict for `heads` heads on `slots` workgroups and the
+ * the DAG model).  Predicts the makespan of NAIVE, DESCENDING and SHIFT
+ * (the full or causal mask of n tiles) for `heads` heads on `slots` workgroups and the
  * cost model `cost` (NULL: the library's default {1, 0.5, 0.05, 0.05} in
  * units of one unmasked item: the dQ add and the hand-off are short next to
  * an item because the kernel overlaps the add with the next item's
@@ -375,10 +413,9 @@ dash_status dash_attn_schedule_tables(const dash_attn_desc* desc, dash_schedule 
                                       int32_t* rank);
 
 /*
- * dash_schedule_predict for any descriptor: B*H heads, its mask's tables
- * (partial pairs cost c_diag).  unit_major = 1: the dynamic policy takes
- * unit 0 of every head, then unit 1, ... (0: head by head; ignored by
- * SHIFT).  Host only.
+ * dash_schedule_predict with a choice of unit order: unit_major = 1: the
+ * dynamic policy takes unit 0 of every head, then unit 1, ... (0: head by
+ * head, as dash_schedule_predict; ignored by static schedules).  Host only.
  */
 dash_status dash_attn_schedule_predict(const dash_attn_desc* desc, dash_schedule schedule,
                                        int32_t slots, int32_t unit_major, const double cost[4],

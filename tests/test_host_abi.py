@@ -154,17 +154,17 @@ FAKE = ctypes.c_void_p(0x100000)
 
 def test_argument_errors_without_launch():
     lib = D.load()
-    size = ctypes.c_size_t(0)
-    assert lib.dash_attn_bwd_workspace_size(ctypes.byref(_desc()), 1, ctypes.byref(size)) == 0
-    assert size.value > 4 * 2 * 256 * 64
-    largest = _desc(B=1, H=1, N=(1 << 22) - 128, d=128, dtype=1)
-    assert lib.dash_attn_bwd_workspace_size(ctypes.byref(largest), 1, ctypes.byref(size)) == 0
-    assert lib.dash_attn_bwd_workspace_size(ctypes.byref(_desc()), 1, ctypes.byref(size)) == 0
+    ws_size = lib.dash_attn_bwd_workspace_size
+    n0 = ws_size(ctypes.byref(_desc()), 1)
+    assert n0 > 4 * 2 * 256 * 64
+    # the longest plain sequence whose units fit the kernel's work list
+    # (1024 tiles); beyond that the size query reports 0 (unsupported)
+    largest = _desc(B=1, H=1, N=1024 * 128, d=128, dtype=1)
+    assert ws_size(ctypes.byref(largest), 1) > 4 * 1024 * 128 * 128
+    assert ws_size(ctypes.byref(_desc(B=1, H=1, N=1025 * 128, d=128, dtype=1)), 1) == 0
     # same size for every schedule (schedules only reorder work)
     for s in range(5):
-        sz = ctypes.c_size_t(0)
-        assert lib.dash_attn_bwd_workspace_size(ctypes.byref(_desc()), s, ctypes.byref(sz)) == 0
-        assert sz.value == size.value
+        assert ws_size(ctypes.byref(_desc()), s) == n0
     bad = [
         (_desc(d=96), 2), (_desc(N=200), 2), (_desc(dtype=1, N=192), 2), (_desc(B=0), 1),
         (_desc(dtype=7), 1), (_desc(causal=2), 1),
@@ -172,10 +172,12 @@ def test_argument_errors_without_launch():
         (_desc(B=1, H=1, N=1 << 22, d=128, dtype=1), 2),
     ]
     for desc, code in bad:
-        assert lib.dash_attn_bwd_workspace_size(ctypes.byref(desc), 1, ctypes.byref(size)) == code
+        assert ws_size(ctypes.byref(desc), 1) == 0
         assert lib.dash_attn_fwd(ctypes.byref(desc), FAKE, FAKE, FAKE, FAKE, FAKE, None) == code
-    assert lib.dash_attn_bwd_workspace_size(ctypes.byref(_desc()), 9, ctypes.byref(size)) == 1
-    assert lib.dash_attn_bwd_workspace_size(None, 1, ctypes.byref(size)) == 1
+        assert lib.dash_attn_fwd_workspace_size(ctypes.byref(desc)) == 0
+    assert ws_size(ctypes.byref(_desc()), 9) == 0
+    assert ws_size(None, 1) == 0
+    size = ctypes.c_size_t(n0)
     desc = _desc()
     args = [FAKE] * 10
     ws_ok = ctypes.c_size_t(size.value)
@@ -203,7 +205,12 @@ def test_argument_errors_without_launch():
         assert lib.dash_attn_bwd_debug(ctypes.byref(desc), 1, *args, ws_ok, ctypes.byref(dbg),
                                        None) == 1
     # host-only argument checks
-    assert lib.dash_schedule_predict(0, 0, 1, 1, 1, None, None) == 1
+    cost = (ctypes.c_double * 4)(1, 1, 1, 0)
+    out = (ctypes.c_double * 4)()
+    assert lib.dash_schedule_predict(None, 1, 1, cost, out) == 1
+    assert lib.dash_schedule_predict(ctypes.byref(desc), 1, 0, cost, out) == 1
+    assert lib.dash_schedule_predict(ctypes.byref(desc), 1, 1, None, out) == 1
+    assert lib.dash_schedule_predict(ctypes.byref(_desc(d=96)), 1, 1, cost, out) == 2
     choice = ctypes.c_int(-1)
     assert lib.dash_schedule_choose(0, 0, 1, 1, None, ctypes.byref(choice), None) == 1
     assert lib.dash_schedule_choose(8, 2, 1, 1, None, ctypes.byref(choice), None) == 1
@@ -221,6 +228,7 @@ def test_argument_errors_without_launch():
                                               ctypes.byref(choice)) == 2
     assert lib.dash_litmus_ordered_add(0, 1, FAKE, FAKE, FAKE, FAKE, 0, None) == 1
     assert lib.dash_attn_bwd_status(None, None) == 1
+    assert lib.dash_status_query(None) == 1
     assert lib.dash_attn_tile(None) == 0 and lib.dash_attn_bwd_subtile(None) == 0
     assert lib.dash_attn_tile(ctypes.byref(_desc(dtype=1, N=256))) == 128
     assert lib.dash_attn_bwd_subtile(ctypes.byref(_desc(d=128))) == 32
@@ -249,3 +257,41 @@ def test_ctypes_structs_mirror_the_header():
     order (the binding passes them by pointer to the library)."""
     assert [f[0] for f in _lib.Desc._fields_] == _header_struct_fields("dash_attn_desc")
     assert [f[0] for f in _lib.Debug._fields_] == _header_struct_fields("dash_bwd_debug")
+
+
+@pytest.mark.parametrize("causal", [False, True])
+def test_device_closed_form_tables_equal_the_host_tables(causal):
+    """The backward writes the full and causal masks' tables on the device
+    from closed forms; the library compares them item for item with its
+    general builder (whose tables the oracle pins) before they are used,
+    here through the table export, which fails on any difference."""
+    for n in list(range(1, 41)) + [64, 127, 128]:
+        for sched in ("atomic", "naive", "descending", "shift"):
+            B, H, N, d = 1, 1, 64 * n, 64
+            if sched == "shift" and causal and n > 1 and n % 2:
+                with pytest.raises(D.DashError) as e:
+                    D.mask_schedule_tables(B, H, N, d, "f32", causal, sched)
+                assert e.value.code == 2
+                continue
+            t = D.mask_schedule_tables(B, H, N, d, "f32", causal, sched)
+            units = OS.units(sched, n, causal)
+            assert t["units"] == units, (n, sched)
+            want = OS.rank_table(sched, n, causal)
+            if want is not None:
+                got = [[None if r < 0 else int(r) for r in row] for row in t["rank"]]
+                assert got == want, (n, sched)
+
+
+def test_library_imports_no_device_allocator():
+    """The library allocates no device memory: its dynamic symbol table
+    imports none of HIP's device allocators (pinned host memory for the
+    tables of special masks is host memory)."""
+    import subprocess
+    out = subprocess.run(["nm", "-D", "--undefined-only", _lib.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    names = {line.split()[-1].split("@")[0] for line in out.splitlines() if line.strip()}
+    device_alloc = {n for n in names if n.startswith(("hipMalloc", "hipFree", "hipExtMalloc",
+                                                      "hipMallocAsync", "hipMemPool"))
+                    and n not in ("hipFreeHost",)}
+    assert not device_alloc, sorted(device_alloc)
+    assert "hipMemcpyAsync" in names
