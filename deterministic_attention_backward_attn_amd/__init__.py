@@ -17,11 +17,12 @@ import ctypes
 
 import numpy as np
 
-from ._lib import DTYPES, SCHEDULES, DashError, Debug, Desc, check, header_symbols, load
+from ._lib import (DTYPES, NOALLOC_SCRATCH_BYTES, NOALLOC_WORKSPACE, SCHEDULES, DashError, Debug,
+                   Desc, check, header_symbols, load)
 
 __all__ = [
     "DashError", "SCHEDULES", "attn_fwd", "attn_bwd_preprocess", "attn_bwd_workspace_size",
-    "attn_bwd", "attn_bwd_status", "status_query", "attn_bwd_tune", "backward", "schedule_tables", "schedule_predict", "schedule_choose",
+    "attn_bwd", "attn_bwd_status", "status_query", "attn_bwd_noalloc", "attn_bwd_tune", "backward", "schedule_tables", "schedule_predict", "schedule_choose",
     "resolve_schedule", "mask_schedule_tables", "mask_schedule_predict",
     "dag_longest_path", "litmus_ordered_add", "tile", "subtile", "header_symbols", "load",
 ]
@@ -285,9 +286,39 @@ def attn_bwd_status(workspace, stream=None):
 
 def status_query(workspace):
     """Status word of the last backward on `workspace` (call after the
-    stream was synchronized); raises DashError on a time-out."""
+    stream was synchronized); raises DashError on a time-out.  "noalloc"
+    reads the word of attn_bwd_noalloc's built-in array on this GPU."""
     lib = load()
-    check(lib.dash_status_query(_ptr(workspace)), "dash_status_query")
+    ptr = ctypes.c_void_p(NOALLOC_WORKSPACE) if isinstance(workspace, str) else _ptr(workspace)
+    if isinstance(workspace, str) and workspace != "noalloc":
+        raise ValueError("workspace must be a tensor or 'noalloc'")
+    check(lib.dash_status_query(ptr), "dash_status_query")
+
+
+def attn_bwd_noalloc(q, k, v, do, lse, delta, *, schedule="naive", causal=False, scale=None,
+                     out=None, stream=None):
+    """attn_bwd without a workspace: the library's built-in device array
+    (NOALLOC_SCRATCH_BYTES per GPU) serves as one; full and causal masks
+    only.  Calls on one GPU share that array and must not overlap.  The
+    library allocates nothing; `out` = (dq, dk, dv) avoids the output
+    allocations here too."""
+    torch = _torch()
+    lib = load()
+    _same_shape(q, k, v, do)
+    desc = _desc_from(q, causal, scale)
+    if out is None:
+        dq, dk, dv = torch.empty_like(q), torch.empty_like(k), torch.empty_like(v)
+    else:
+        dq, dk, dv = out
+        _same_shape(q, dq, dk, dv)
+    for t in (lse, delta):
+        if t.dtype != torch.float32 or tuple(t.shape) != tuple(q.shape[:3]):
+            raise ValueError("lse and delta must be float32 [B, H, N]")
+    check(lib.dash_attn_bwd_noalloc(ctypes.byref(desc), _sched(schedule), _ptr(q), _ptr(k),
+                                    _ptr(v), _ptr(do), _ptr(lse), _ptr(delta), _ptr(dq),
+                                    _ptr(dk), _ptr(dv), _stream(stream)),
+          "dash_attn_bwd_noalloc")
+    return dq, dk, dv
 
 
 def backward(q, k, v, o, do, lse, *, schedule="naive", causal=False, scale=None,

@@ -24,6 +24,8 @@ STATUS = {
     6: "DASH_ERR_ORDER_TIMEOUT",
     7: "DASH_ERR_HOST_MEMORY",
 }
+NOALLOC_SCRATCH_BYTES = 64 << 20   # DASH_NOALLOC_SCRATCH_BYTES
+NOALLOC_WORKSPACE = 1               # DASH_NOALLOC_WORKSPACE
 SCHEDULES = {"atomic": 0, "naive": 1, "descending": 2, "shift": 3, "auto": 4}
 DTYPES = {"f32": 0, "bf16": 1}
 
@@ -71,6 +73,8 @@ _SIGS = {
                                            ctypes.POINTER(Debug), _vp]),
     "dash_attn_bwd_status": (ctypes.c_int, [_vp, _vp]),
     "dash_status_query": (ctypes.c_int, [_vp]),
+    "dash_attn_bwd_noalloc": (ctypes.c_int, [ctypes.POINTER(Desc), ctypes.c_int, _vp, _vp, _vp,
+                                             _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
     "dash_schedule_tables": (ctypes.c_int, [_i32, _i32, ctypes.c_int, _ip, _ip, _ip, _ip, _ip]),
     "dash_schedule_predict": (ctypes.c_int, [ctypes.POINTER(Desc), ctypes.c_int, _i32, _dp,
                                              _dp]),

@@ -28,6 +28,7 @@ SOURCES = [
     "kernels/attn_bwd_pair.hip",
     "kernels/attn_fwd.hip",
     "kernels/elementwise.hip",
+    "kernels/noalloc.hip",
 ]
 
 ARCH = "gfx950"

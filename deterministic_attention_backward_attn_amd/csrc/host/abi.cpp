@@ -440,16 +440,24 @@ dash_status resolve_schedule(dash_schedule schedule, const MaskKey& mkey, long h
 // Reads the workspace's status word (synchronous copy; the caller has
 // synchronized the stream the backward ran on).
 dash_status read_status(const void* workspace) {
+  if (workspace == DASH_NOALLOC_WORKSPACE) {
+    void* p = nullptr;
+    if (dash::noalloc_scratch(&p) != hipSuccess) return DASH_ERR_HIP;
+    workspace = p;
+  }
   uint32_t word = 0;
   if (hipMemcpy(&word, workspace, sizeof(word), hipMemcpyDeviceToHost) != hipSuccess)
     return DASH_ERR_HIP;
   return word ? DASH_ERR_ORDER_TIMEOUT : DASH_OK;
 }
 
+// noalloc: the workspace is the built-in scratch; masks whose tables come
+// from pinned host memory (allocated on first use) are refused.
 dash_status run_bwd(const dash_attn_desc* desc, dash_schedule schedule, const void* q,
                     const void* k, const void* v, const void* dout, const float* lse,
                     const float* delta, void* dq, void* dk, void* dv, void* workspace,
-                    size_t workspace_bytes, const dash_bwd_debug* dbg, void* stream) {
+                    size_t workspace_bytes, const dash_bwd_debug* dbg, void* stream,
+                    bool noalloc = false) {
   dash_status st = check_desc(desc);
   if (st != DASH_OK) return st;
   if (!sched_ok_run(schedule)) return DASH_ERR_INVALID_ARG;
@@ -469,6 +477,7 @@ dash_status run_bwd(const dash_attn_desc* desc, dash_schedule schedule, const vo
   const MaskKey mkey = mask_key(desc);
   const bool plain = plain_key(mkey);
   if (plain && n > dash::kMaxUnitItems) return DASH_ERR_UNSUPPORTED;
+  if (noalloc && !plain) return DASH_ERR_UNSUPPORTED;
   const long heads = (long)desc->B * desc->H;
   hipStream_t strm = (hipStream_t)stream;
   char* ws = (char*)workspace;
@@ -772,6 +781,30 @@ dash_status dash_attn_bwd(const dash_attn_desc* desc, dash_schedule schedule, co
   return guarded([&] {
     return run_bwd(desc, schedule, q, k, v, dout, lse, delta, dq, dk, dv, workspace,
                    workspace_bytes, nullptr, stream);
+  });
+}
+
+dash_status dash_attn_bwd_noalloc(const dash_attn_desc* desc, dash_schedule schedule,
+                                  const void* q, const void* k, const void* v, const void* dout,
+                                  const float* lse, const float* delta, void* dq, void* dk,
+                                  void* dv, void* stream) {
+  return guarded([&]() -> dash_status {
+    dash_status st = check_desc(desc);
+    if (st != DASH_OK) return st;
+    if (!sched_ok_run(schedule)) return DASH_ERR_INVALID_ARG;
+    size_t need = 0;
+    {
+      const MaskKey mkey = mask_key(desc);
+      if (!plain_key(mkey)) return DASH_ERR_UNSUPPORTED;
+      if (mkey.n > dash::kMaxUnitItems) return DASH_ERR_UNSUPPORTED;
+      std::lock_guard<std::mutex> lock(g_mu);
+      need = layout(desc, live_pairs_of(mkey)).total;
+    }
+    if (need > dash::kNoallocScratchBytes) return DASH_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if (dash::noalloc_scratch(&ws) != hipSuccess) return DASH_ERR_HIP;
+    return run_bwd(desc, schedule, q, k, v, dout, lse, delta, dq, dk, dv, ws,
+                   dash::kNoallocScratchBytes, nullptr, stream, true);
   });
 }
 

@@ -81,6 +81,12 @@ int bwd_waves(int dtype, int d);
 
 hipError_t launch_fwd(int dtype, int d, bool masked, const FwdArgs& a, hipStream_t stream);
 
+// Size of the built-in scratch array of the allocation-free backward.
+constexpr size_t kNoallocScratchBytes = (size_t)64 << 20;
+// Device address of the current device's scratch array (looked up once per
+// device with hipGetSymbolAddress).
+hipError_t noalloc_scratch(void** out);
+
 hipError_t launch_preprocess(int dtype, int d, const void* o, const void* dout, float* delta,
                              long rows, hipStream_t stream);
 hipError_t launch_zero_u32(uint32_t* p, size_t n_words, hipStream_t stream);

@@ -200,12 +200,42 @@ dash_status dash_attn_bwd(const dash_attn_desc* desc, dash_schedule schedule, co
                           size_t workspace_bytes, void* stream);
 
 /*
+ * Allocation-free backward, for callers that cannot allocate device memory
+ * (code under graph capture, tight serving loops, harnesses that forbid
+ * allocation).  Same arguments and results as dash_attn_bwd (bit-identical
+ * for the ordered schedules) without a workspace argument: the workspace is
+ * a built-in device array of DASH_NOALLOC_SCRATCH_BYTES per GPU, part of the
+ * library's code object (allocated when the code object is loaded, held
+ * until the process ends).  The call allocates nothing.
+ *   Limits    the workspace dash_attn_bwd_workspace_size reports must fit
+ *             the array (else DASH_ERR_WORKSPACE, before any launch; e.g.
+ *             bf16 d = 128 fits up to about 14.6e6 query rows x heads,
+ *             B*H*N <= 120k); full and causal masks only (a window or
+ *             block mask gives DASH_ERR_UNSUPPORTED: their tables need
+ *             host memory allocated on first use).
+ *   Sharing   every call on a GPU uses that GPU's one array and leaves its
+ *             contents there: calls that overlap on one GPU (other streams,
+ *             other threads) race and must be serialized by the caller.
+ *   Status    an ordering time-out is read, after the caller synchronized
+ *             the stream, with dash_status_query(DASH_NOALLOC_WORKSPACE)
+ *             (the current GPU's array).
+ */
+#define DASH_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+#define DASH_NOALLOC_WORKSPACE ((const void*)1)
+dash_status dash_attn_bwd_noalloc(const dash_attn_desc* desc, dash_schedule schedule,
+                                  const void* q, const void* k, const void* v, const void* dout,
+                                  const float* lse, const float* delta, void* dq, void* dk,
+                                  void* dv, void* stream);
+
+/*
  * Device status of the last dash_attn_bwd on this workspace: reads the
  * status word with a synchronous copy; call it after the stream the
  * backward ran on has been synchronized.  DASH_OK, or
  * DASH_ERR_ORDER_TIMEOUT if some ordered add gave up waiting (that
  * launch's results are then not valid); DASH_ERR_INVALID_ARG for NULL.
  * Each dash_attn_bwd clears the word, so it reports the last launch only.
+ * DASH_NOALLOC_WORKSPACE reads the word of dash_attn_bwd_noalloc's
+ * built-in array on the current GPU.
  */
 dash_status dash_status_query(const void* workspace);
 

@@ -295,3 +295,20 @@ def test_library_imports_no_device_allocator():
                     and n not in ("hipFreeHost",)}
     assert not device_alloc, sorted(device_alloc)
     assert "hipMemcpyAsync" in names
+
+
+def test_noalloc_refusals_happen_before_any_device_call():
+    """dash_attn_bwd_noalloc refuses problems whose workspace exceeds its
+    built-in array and masks whose tables need host memory, before it
+    touches the device."""
+    lib = D.load()
+    args = [FAKE] * 9
+    big = _desc(B=1, H=32, N=4096, d=128, dtype=1, causal=1)
+    assert lib.dash_attn_bwd_workspace_size(ctypes.byref(big), 1) > _lib.NOALLOC_SCRATCH_BYTES
+    assert lib.dash_attn_bwd_noalloc(ctypes.byref(big), 1, *args, None) == 3
+    win = _desc(B=1, H=1, N=1024, d=64, dtype=1, causal=1)
+    win.window = 200
+    assert lib.dash_attn_bwd_noalloc(ctypes.byref(win), 1, *args, None) == 2
+    assert lib.dash_attn_bwd_noalloc(ctypes.byref(_desc(d=96)), 1, *args, None) == 2
+    assert lib.dash_attn_bwd_noalloc(ctypes.byref(_desc()), 9, *args, None) == 1
+    assert lib.dash_attn_bwd_noalloc(None, 1, *args, None) == 1
