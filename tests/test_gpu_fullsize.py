@@ -3,9 +3,11 @@ bench times, on sampled rows the oracle computes one by one.
 
 For each full-size workload and mask (the sliding-window and block-sparse
 workloads included), every schedule (auto too) runs the whole backward on
-the GPU; for two heads (the first and the last) the oracle computes the
-forward statistics and then O, LSE, dQ, dK and dV at rows on tile edges,
-at the middle and at the ends of the sequence.  Error metric:
+the GPU; for eight heads the oracle computes the forward statistics and
+then O, LSE, dQ, dK and dV at rows on tile edges, at the middle and at the
+ends of the sequence.  The ordered schedules deal heads round-robin to the
+8 XCD groups (head b*H + h to group (b*H + h) mod 8), so the eight heads are
+one per group, from the first head to the last.  Error metric:
 max|gpu - oracle| / max|oracle| over the sampled rows of each tensor,
 bound 2e-2 (bf16 inputs and outputs, fp32 accumulation).
 """
@@ -46,7 +48,11 @@ def test_full_size_sampled_rows(wl, mask):
     delta = D.attn_bwd_preprocess(o, dev["do"])
     rows = _rows(w.N)
     scale = 1.0 / np.sqrt(w.d)
-    heads = [(0, 0), (w.B - 1, w.H - 1)]
+    bh = w.B * w.H
+    # one head per XCD group: flat index i (mod 8) from 0 up to bh - 1
+    flat = [i + 8 * ((bh // 8 - 1) * i // 7) for i in range(8)]
+    assert flat[0] == 0 and flat[-1] == bh - 1 and len({f % 8 for f in flat}) == 8
+    heads = [divmod(f, w.H) for f in flat]
     refs = {}
     for (b, h) in heads:
         ex = {k: exact_of(host[k][b, h], w.dtype) for k in host}
