@@ -158,29 +158,23 @@ def phase_shares(D, dev, lse, delta, sched, causal, ws, out, mkw, lay=None):
 
 
 def dag_prediction(D, w, causal, sched, mkw, coresident):
-    """The host DAG model's view of one ordered schedule on this workload:
-    predicted makespan and its lower bound (in units of one full item) and
-    the predicted share of slot time spent waiting for ordered-add turns,
-    with the library's default costs (full item 1, partial item 0.5, dQ add
-    0.05, hand-off 0.05).  Heads and co-resident workgroups are divided by
-    the same power of two until the graph holds at most 1e6 items, which
-    keeps the heads per round of the static schedules as in the launch
-    (None if the sample cannot hold one head's static round)."""
-    n = w.N // D.tile(w.B, w.H, w.N, w.d, w.dtype)
-    items = n * (n + 1) // 2 if causal else n * n
-    heads = w.B * w.H
-    m = 1
-    while (heads // m) * items > 1000000 and heads % (2 * m) == 0 and coresident % (2 * m) == 0:
-        m *= 2
-    hp, slots = heads // m, coresident // m
+    """The host DAG model's view of one ordered schedule on this workload, as
+    the launch places it (dash_attn_bwd_predict: XCD groups when the
+    schedule's units fit one, the library's unit order): predicted makespan
+    and its lower bound in units of one full item, for one group's share,
+    and the predicted share of slot time spent waiting for ordered-add
+    turns, with the library's default costs (full item 1, partial item 0.5,
+    dQ add 0.05, hand-off 0.05).  None if the launch cannot run it."""
     try:
-        mk, wait, _, lb = D.mask_schedule_predict(1, hp, w.N, w.d, w.dtype, causal, sched,
-                                                  slots=slots, cost=DAG_COST, **mkw)
+        (mk, wait, _, lb), info = D.bwd_predict(w.B, w.H, w.N, w.d, w.dtype, causal, sched,
+                                                slots=coresident, cost=DAG_COST, **mkw)
     except D.DashError:
         return None
+    slots = info["slots"]
     return {"makespan_items": round(mk, 1), "lower_bound_items": round(lb, 1),
             "wait_frac": round(wait / (slots * mk), 4) if mk > 0 else 0.0,
-            "heads": hp, "slots": slots}
+            "groups": info["groups"], "unit_major": info["unit_major"],
+            "heads_modelled": info["heads"], "slots": slots}
 
 
 # ------------------------------------------------------------------ main
@@ -323,6 +317,15 @@ def main():
     peak = PEAK_TFLOPS[w.dtype]
     primary = args.primary or min((s for s in results if s != "atomic"),
                                   key=lambda s: results[s]["ms_per_step"])
+    ran = D.resolve_schedule(w.B, w.H, w.N, w.d, w.dtype, causal, primary, **mkw)
+    # the ordered add's share of the primary schedule's wave cycles (one
+    # extra untimed launch with the phase timer, unless --phases ran it)
+    add_share = None
+    if ran != "atomic" and not args.no_wait_stats:
+        ph = results[primary].get("phases") or phase_shares(D, dev, lse, delta, ran, causal, ws,
+                                                            (dq, dk, dv), mkw, lay)
+        if not lay:
+            add_share = round(sum(ph[k] for k in ("counter check", "ordered add", "hand-off")), 4)
 
     def timed(fn):
         for _ in range(args.warmup):
@@ -360,8 +363,6 @@ def main():
               f"fwd+bwd {ms_b:8.3f} ms  {(f_fwd + flops) / ms_b / 1e9:7.1f} TFLOP/s",
               file=sys.stderr, flush=True)
     prim = results[primary]
-    # the schedule the launches ran (auto resolves to an ordered one)
-    ran = D.resolve_schedule(w.B, w.H, w.N, w.d, w.dtype, causal, primary, **mkw)
     out = {
         "metric": METRIC,
         "value": round(prim["tflops"], 2),
@@ -385,6 +386,16 @@ def main():
         "det_nondet_ratio": ({s: round(r["tflops"] / results["atomic"]["tflops"], 4)
                               for s, r in results.items() if s != "atomic"}
                              if "atomic" in results else None),
+        # what that ratio measures on this chip, and the cost of ordering itself
+        "ordering_cost": {
+            "det_nondet_ratio_measures": "throughput against the atomic reference, whose "
+                                         "unordered fp32 atomic dQ adds are themselves bound by "
+                                         "the chip's fp32 atomic throughput (not a free baseline)",
+            "ordered_add_share_of_wave_cycles": add_share,
+            "schedule": ran,
+            "source": "phase timer of the backward kernel (one instrumented launch): counter "
+                      "check + ordered add + hand-off phases"},
+        "dag_vs_measured": dag_vs_measured(results),
         "schedules": {s: {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
                       for s, r in results.items()},
     }
@@ -406,6 +417,27 @@ def main():
     else:
         out["cpu_baseline"] = None
     print(json.dumps(out), flush=True)
+    # release device memory while every library (a profiler's included) is
+    # still live, so that nothing is left to free during interpreter exit
+    del dev, o, lse, delta, dq, dk, dv, ws
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+
+
+def dag_vs_measured(results):
+    """For naive and descending: the DAG model's predicted makespan relative
+    to shift's, next to the measured kernel-time ratio."""
+    sh = results.get("shift", {})
+    if not sh.get("dag") or not sh.get("kernel_ms"):
+        return None
+    out = {}
+    for s in ("naive", "descending"):
+        r = results.get(s, {})
+        if r.get("dag") and r.get("kernel_ms"):
+            out[s] = {"predicted_vs_shift": round(r["dag"]["makespan_items"]
+                                                  / sh["dag"]["makespan_items"], 3),
+                      "measured_vs_shift": round(r["kernel_ms"] / sh["kernel_ms"], 3)}
+    return out or None
 
 
 if __name__ == "__main__":

@@ -23,7 +23,7 @@ from ._lib import (DTYPES, NOALLOC_SCRATCH_BYTES, NOALLOC_WORKSPACE, SCHEDULES, 
 __all__ = [
     "DashError", "SCHEDULES", "attn_fwd", "attn_bwd_preprocess", "attn_bwd_workspace_size",
     "attn_bwd", "attn_bwd_status", "status_query", "attn_bwd_noalloc", "attn_bwd_tune", "backward", "schedule_tables", "schedule_predict", "schedule_choose",
-    "resolve_schedule", "mask_schedule_tables", "mask_schedule_predict",
+    "resolve_schedule", "mask_schedule_tables", "mask_schedule_predict", "bwd_predict",
     "dag_longest_path", "litmus_ordered_add", "tile", "subtile", "header_symbols", "load",
 ]
 
@@ -421,6 +421,23 @@ def schedule_predict(n: int, causal: bool, schedule, heads: int, slots: int, cos
     check(lib.dash_schedule_predict(ctypes.byref(desc), _sched(schedule), int(slots), c, out),
           "dash_schedule_predict")
     return tuple(out)
+
+
+def bwd_predict(B, H, N, d, dtype="bf16", causal=False, schedule="naive", *, slots, cost,
+                window=0, block_mask=None, block_size=0):
+    """DAG prediction of a launch on `slots` co-resident workgroups, with the
+    library's placement (XCD groups when the schedule's units fit one) and
+    unit order.  Returns (makespan, total_wait, max_slot_idle, lower_bound)
+    of one group's share and a dict groups, unit_major, heads, slots."""
+    lib = load()
+    desc = _desc(B, H, N, d, dtype, causal, None, window, block_mask, block_size)
+    c = (ctypes.c_double * 4)(*[float(x) for x in cost])
+    out = (ctypes.c_double * 4)()
+    info = (ctypes.c_int32 * 4)()
+    check(lib.dash_attn_bwd_predict(ctypes.byref(desc), _sched(schedule), int(slots), c, out,
+                                    info), "dash_attn_bwd_predict")
+    return tuple(out), {"groups": info[0], "unit_major": bool(info[1]), "heads": info[2],
+                        "slots": info[3]}
 
 
 def schedule_choose(n: int, causal: bool, heads: int, slots: int, cost=None):

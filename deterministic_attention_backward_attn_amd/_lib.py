@@ -78,6 +78,8 @@ _SIGS = {
     "dash_schedule_tables": (ctypes.c_int, [_i32, _i32, ctypes.c_int, _ip, _ip, _ip, _ip, _ip]),
     "dash_schedule_predict": (ctypes.c_int, [ctypes.POINTER(Desc), ctypes.c_int, _i32, _dp,
                                              _dp]),
+    "dash_attn_bwd_predict": (ctypes.c_int, [ctypes.POINTER(Desc), ctypes.c_int, _i32, _dp, _dp,
+                                             _ip]),
     "dash_attn_bwd_resolve_schedule": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int,
                                                       ctypes.POINTER(ctypes.c_int)]),
     "dash_attn_schedule_tables": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, _ip, _ip, _ip,

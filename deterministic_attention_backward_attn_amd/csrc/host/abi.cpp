@@ -37,10 +37,71 @@ bool sched_ok_run(int s) { return sched_ok(s) || s == DASH_SCHED_AUTO; }
 // d = 128: ~24k cycles per item, ~1.2k per hand-off).
 constexpr double kDefaultCost[4] = {1.0, 0.5, 0.05, 0.05};
 
+constexpr int kXcds = 8;  // XCDs of an MI355X: the workgroup groups of the placement
+
+// How a launch runs a schedule's tables, as the kernel places them: the
+// ordered schedules run in XCD groups (each group's workgroups take the units
+// of 1/8 of the heads) unless a static table's units do not fit one group's
+// workgroups (then device-wide); the dynamic tables take units head by head,
+// or unit-major when that is predicted at least 5 % shorter.
+struct LaunchPrediction {
+  dash::DagResult r;   // makespan etc. of one group's share (all groups alike)
+  int groups = 1;      // 8 (XCD groups) or 1 (device-wide)
+  int unit_major = 0;  // the dynamic unit order
+  int heads = 0, slots = 0;  // the share the model ran (sampled when large)
+};
+
+// DAG prediction of a launch on `maxco` co-resident workgroups (grouped:
+// whether the launch places units in XCD groups when they fit).  A group's
+// share larger than about 2e5 items is sampled: fewer heads on the same
+// workgroups (whole rounds for static tables), the times scaled up by the
+// ratio of heads (steady state: each further head adds the same work).
+bool launch_predict(const Tables& t, long heads, int maxco, const double cost[4], bool grouped,
+                    LaunchPrediction& out) {
+  if (t.units() == 0 || heads < 1 || maxco < 1) return false;
+  int g = grouped ? kXcds : 1;
+  if (maxco / g < 1 || (t.needs_static() && t.units() > maxco / g)) g = 1;
+  if (t.needs_static() && t.units() > maxco) return false;
+  const int slots = maxco / g;
+  const long hg = (heads + g - 1) / g;
+  long hs = hg;
+  const long cap = std::max<long>(1, 200000 / std::max(1, t.items()));
+  if (hs > cap) {
+    hs = cap;
+    if (t.needs_static()) {
+      const long per_round = slots / t.units();  // heads of one round
+      hs = std::max(per_round, (hs / per_round) * per_round);
+    }
+  }
+  out.groups = g;
+  out.heads = (int)hs;
+  out.slots = slots;
+  out.unit_major = 0;
+  if (!dash::dag_predict(t, (int)hs, slots, cost, out.r, false)) return false;
+  if (!t.needs_static() && t.ordered()) {
+    dash::DagResult um;
+    if (dash::dag_predict(t, (int)hs, slots, cost, um, true) &&
+        um.makespan < 0.95 * out.r.makespan) {
+      out.r = um;
+      out.unit_major = 1;
+    }
+  }
+  if (hs < hg) {
+    const double f = (double)hg / (double)hs;
+    out.r.makespan *= f;
+    out.r.total_wait *= f;
+    out.r.max_slot_idle *= f;
+    out.r.lower_bound *= f;
+  }
+  return true;
+}
+
 // The ordered schedule with the smallest predicted makespan; see
-// dash_schedule_choose.
+// dash_schedule_choose.  placement: predict each schedule as the launch
+// places it (launch_predict, on `slots` co-resident workgroups); otherwise
+// all `heads` heads head by head on `slots` workgroups.
 dash_status choose_schedule(const dash::TileMask& m, int heads, int slots, const double cost[4],
-                            Sched* choice, double pred[3]) {
+                            Sched* choice, double pred[3], bool placement = false) {
   const Sched cand[3] = {Sched::Naive, Sched::Descending, Sched::Shift};
   double best = 0.0;
   int best_i = -1;
@@ -50,11 +111,18 @@ dash_status choose_schedule(const dash::TileMask& m, int heads, int slots, const
     if (!dash::build_tables(m, cand[i], t)) continue;
     if (dash::validate_tables(t)[0] != '\0') return DASH_ERR_SCHEDULE_INVALID;
     if (t.needs_static() && t.units() > slots) continue;
-    // a subset of the heads keeps the prediction to about 2e5 items
-    const long per_head = (long)t.kv.size();
-    const int h = (int)std::max<long>(1, std::min<long>(heads, 200000 / std::max<long>(per_head, 1)));
     dash::DagResult r;
-    if (!dash::dag_predict(t, h, slots, cost, r)) return DASH_ERR_SCHEDULE_INVALID;
+    if (placement) {
+      LaunchPrediction lp;
+      if (!launch_predict(t, heads, slots, cost, true, lp)) return DASH_ERR_SCHEDULE_INVALID;
+      r = lp.r;
+    } else {
+      // a subset of the heads keeps the prediction to about 2e5 items
+      const long per_head = (long)t.kv.size();
+      const int h =
+          (int)std::max<long>(1, std::min<long>(heads, 200000 / std::max<long>(per_head, 1)));
+      if (!dash::dag_predict(t, h, slots, cost, r)) return DASH_ERR_SCHEDULE_INVALID;
+    }
     pred[i] = r.makespan;
     // ties go to the later candidate (SHIFT, then DESCENDING)
     if (best_i < 0 || r.makespan <= best) {
@@ -362,8 +430,6 @@ dash_status pinned_blob(const MaskKey& key, TabEntry* e) {
   return DASH_OK;
 }
 
-constexpr int kXcds = 8;  // XCDs of an MI355X: the group share the order choice predicts for
-
 // Unit order of a dynamic ordered schedule: unit-major (unit 0 of every
 // head, then unit 1, ...) when the DAG model predicts a makespan at least
 // 5 % shorter than head by head for one group's share (the heads and
@@ -377,15 +443,8 @@ bool unit_major_for(const MaskKey& mkey, const Tables& t, Sched s, long heads, i
   const auto key = std::make_tuple(mkey, (int)s, heads, maxco, (int)grouped);
   auto it = g_order.find(key);
   if (it != g_order.end()) return it->second;
-  const int g = grouped ? kXcds : 1;
-  const int slots = std::max(1, maxco / g);
-  long hg = (heads + g - 1) / g;
-  hg = std::max<long>(1, std::min<long>(hg, 200000 / std::max(1, t.items())));
-  dash::DagResult hm, um;
-  bool pick = false;
-  if (dash::dag_predict(t, (int)hg, slots, kDefaultCost, hm, false) &&
-      dash::dag_predict(t, (int)hg, slots, kDefaultCost, um, true))
-    pick = um.makespan < 0.95 * hm.makespan;
+  LaunchPrediction lp;
+  const bool pick = launch_predict(t, heads, maxco, kDefaultCost, grouped, lp) && lp.unit_major;
   g_order[key] = pick;
   return pick;
 }
@@ -431,7 +490,7 @@ dash_status resolve_schedule(dash_schedule schedule, const MaskKey& mkey, long h
   if (plain_key(mkey) && mkey.n + 1 > dash::kMaxUnitItems) return DASH_ERR_UNSUPPORTED;
   const dash::TileMask m = plain_key(mkey) ? dash::plain_mask(mkey.n, mkey.causal != 0)
                                            : mask_entry(mkey)->host;
-  const dash_status st = choose_schedule(m, h, maxco, kDefaultCost, s, pred);
+  const dash_status st = choose_schedule(m, h, maxco, kDefaultCost, s, pred, true);
   if (st != DASH_OK) return st;
   g_auto[key] = *s;
   return DASH_OK;
@@ -958,6 +1017,39 @@ dash_status dash_attn_schedule_predict(const dash_attn_desc* desc, dash_schedule
     out[1] = r.total_wait;
     out[2] = r.max_slot_idle;
     out[3] = r.lower_bound;
+    return DASH_OK;
+  });
+}
+
+dash_status dash_attn_bwd_predict(const dash_attn_desc* desc, dash_schedule schedule,
+                                  int32_t slots, const double cost[4], double out[4],
+                                  int32_t info[4]) {
+  dash_status st = check_desc(desc);
+  if (st != DASH_OK) return st;
+  if (!sched_ok(schedule) || slots < 1 || !cost || !out) return DASH_ERR_INVALID_ARG;
+  for (int i = 0; i < 4; ++i)
+    if (!(cost[i] >= 0.0) || !std::isfinite(cost[i])) return DASH_ERR_INVALID_ARG;
+  return guarded([&]() -> dash_status {
+    const MaskKey mkey = mask_key(desc);
+    if (plain_key(mkey) && mkey.n + 1 > dash::kMaxUnitItems) return DASH_ERR_UNSUPPORTED;
+    Tables t;
+    if (!dash::build_tables(tile_mask(mkey), (Sched)schedule, t)) return DASH_ERR_UNSUPPORTED;
+    if (dash::validate_tables(t)[0] != '\0') return DASH_ERR_SCHEDULE_INVALID;
+    if (t.needs_static() && t.units() > slots) return DASH_ERR_UNSUPPORTED;
+    LaunchPrediction lp;
+    if (!launch_predict(t, (long)desc->B * desc->H, slots, cost, schedule != DASH_SCHED_ATOMIC,
+                        lp))
+      return DASH_ERR_SCHEDULE_INVALID;
+    out[0] = lp.r.makespan;
+    out[1] = lp.r.total_wait;
+    out[2] = lp.r.max_slot_idle;
+    out[3] = lp.r.lower_bound;
+    if (info) {
+      info[0] = lp.groups;
+      info[1] = lp.unit_major;
+      info[2] = lp.heads;
+      info[3] = lp.slots;
+    }
     return DASH_OK;
   });
 }

@@ -51,8 +51,11 @@ import statistics
 import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+# every source the backward kernel's translation unit includes
 KERNEL_SOURCES = ["deterministic_attention_backward_attn_amd/csrc/kernels/attn_bwd.hip",
-                  "deterministic_attention_backward_attn_amd/csrc/kernels/common.hpp"]
+                  "deterministic_attention_backward_attn_amd/csrc/kernels/common.hpp",
+                  "deterministic_attention_backward_attn_amd/csrc/kernels/launch.hpp",
+                  "deterministic_attention_backward_attn_amd/csrc/kernels/placement.hpp"]
 
 
 def kernel_source_hash() -> str:

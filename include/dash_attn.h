@@ -28,8 +28,9 @@
  *               KV tiles w and n-1-w in one workgroup, two phases.  dQ order
  *               = the step at which each tile reaches the block.
  *   ATOMIC      NAIVE's traversal, unordered fp32 atomic adds.
- *   AUTO        the ordered schedule the DAG model predicts fastest (or the
- *               one dash_attn_bwd_tune measured fastest for the shape).
+ *   AUTO        the ordered schedule the DAG model predicts fastest under
+ *               the launch's placement (dash_attn_bwd_predict), or the one
+ *               dash_attn_bwd_tune measured fastest for the shape.
  * With a window or block mask the same rules run over the tile pairs that
  * hold a visible key; SHIFT becomes a proper colouring of those pairs.
  *
@@ -369,6 +370,23 @@ dash_status dash_schedule_predict(const dash_attn_desc* desc, dash_schedule sche
                                   int32_t slots, const double cost[4], double out[4]);
 
 /*
+ * DAG prediction of a launch, host only: the schedule's tables for the
+ * descriptor's mask run as dash_attn_bwd places them on `slots` co-resident
+ * workgroups.  The ordered schedules run in XCD groups (each of the 8 XCDs'
+ * workgroups takes the units of 1/8 of the heads) unless a static table's
+ * units per head exceed one group's workgroups (then device-wide); dynamic
+ * tables take units head by head, or unit-major when that is predicted at
+ * least 5 % shorter.  out[4] as dash_schedule_predict, for one group's share
+ * (every group carries the same share); info[4] (may be NULL) = {groups
+ * (8 or 1), unit-major (0/1), heads and workgroups the model ran (the share
+ * is sampled to about 2e5 items with proportionally fewer workgroups)}.
+ * DASH_SCHED_AUTO predicts its candidates this way.
+ */
+dash_status dash_attn_bwd_predict(const dash_attn_desc* desc, dash_schedule schedule,
+                                  int32_t slots, const double cost[4], double out[4],
+                                  int32_t info[4]);
+
+/*
  * Schedule choice, host only (the explainer's significance section presents
  * DASH as a palette of strategies, heuristic and optimal, from which the
  * user picks by hardware and model configuration; this makes that pick from
@@ -379,12 +397,13 @@ dash_status dash_schedule_predict(const dash_attn_desc* desc, dash_schedule sche
  * an item because the kernel overlaps the add with the next item's
  * compute), and returns the one
  * with the smallest makespan (ties: SHIFT, then DESCENDING, then NAIVE).
+ * (DASH_SCHED_AUTO in dash_attn_bwd makes the same choice with each
+ * candidate predicted under the launch's placement, dash_attn_bwd_predict.)
  * Schedules that cannot run (SHIFT with an odd causal tile count or more
  * units per head than slots) are skipped.  predicted[3] (may be NULL)
  * receives the three makespans in enum order NAIVE, DESCENDING, SHIFT, NaN
  * where skipped.  For large problems the prediction uses a subset of the
- * heads (at most about 2e5 items).  DASH_SCHED_AUTO in dash_attn_bwd uses
- * this choice with slots = the co-resident workgroups of the launch.
+ * heads (at most about 2e5 items).
  */
 dash_status dash_schedule_choose(int32_t n, int32_t causal, int32_t heads, int32_t slots,
                                  const double* cost, dash_schedule* choice, double* predicted);

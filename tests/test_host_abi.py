@@ -3,6 +3,7 @@ the header declares; host-only calls (schedule tables, DAG prediction,
 longest path) match the oracle exactly; argument errors come back as status
 codes before any launch."""
 import ctypes
+import os
 import random
 
 import numpy as np
@@ -312,3 +313,20 @@ def test_noalloc_refusals_happen_before_any_device_call():
     assert lib.dash_attn_bwd_noalloc(ctypes.byref(_desc(d=96)), 1, *args, None) == 2
     assert lib.dash_attn_bwd_noalloc(ctypes.byref(_desc()), 9, *args, None) == 1
     assert lib.dash_attn_bwd_noalloc(None, 1, *args, None) == 1
+
+
+def test_profile_hash_covers_every_kernel_include():
+    """The freshness hash of the committed traffic summaries covers every
+    file the backward kernel's source includes from this package."""
+    import re
+    from deterministic_attention_backward_attn_amd import rocprof_summary as RS
+    kdir = "deterministic_attention_backward_attn_amd/csrc/kernels/"
+    seen, todo = set(), ["attn_bwd.hip"]
+    while todo:
+        f = todo.pop()
+        if f in seen:
+            continue
+        seen.add(f)
+        text = open(os.path.join(RS.ROOT, kdir + f)).read()
+        todo += re.findall(r'#include\s+"([^"]+)"', text)
+    assert {kdir + f for f in seen} == set(RS.KERNEL_SOURCES)

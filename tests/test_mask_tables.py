@@ -255,10 +255,12 @@ def test_table_export_protocol():
 
 
 def test_bench_dag_prediction_on_the_plain_workloads():
-    """The bench's DAG view of each ordered schedule: on the full and causal
-    masks shift meets its lower bound with no waits (the pages' conflict-free
-    construction), descending needs no longer than naive, and the head sample
-    keeps the launch's heads per co-resident workgroup."""
+    """The bench's DAG view of each ordered schedule, as the launch places
+    it: on the full and causal masks shift meets its lower bound with no
+    waits (the pages' conflict-free construction), descending needs no
+    longer than naive, the dynamic schedules run in 8 XCD groups of 32
+    workgroups, and shift runs grouped exactly when its units per head fit
+    a group (32 at 4K full, 64 at 16K causal: device-wide)."""
     import bench
     from synth import WORKLOADS
     for name in ("b1h32_n16k_d128_causal", "b4h32_n4k_d128_full", "b2h16_n2k_d128_causal"):
@@ -268,9 +270,14 @@ def test_bench_dag_prediction_on_the_plain_workloads():
                 for s in ("naive", "descending", "shift")}
         for p in pred.values():
             assert p is not None
-            assert p["heads"] * 256 == p["slots"] * w.B * w.H
+            assert p["slots"] * p["groups"] == 256
+            assert p["heads_modelled"] <= -(-w.B * w.H // p["groups"])
             assert p["makespan_items"] >= p["lower_bound_items"] - 1e-6
             assert 0.0 <= p["wait_frac"] < 1.0
         assert pred["shift"]["makespan_items"] == pytest.approx(pred["shift"]["lower_bound_items"])
         assert pred["shift"]["wait_frac"] == 0.0
         assert pred["descending"]["makespan_items"] <= pred["naive"]["makespan_items"] + 1e-6
+        assert pred["naive"]["groups"] == pred["descending"]["groups"] == 8
+        n = w.N // 128
+        shift_units = n // 2 if causal else n
+        assert pred["shift"]["groups"] == (8 if shift_units <= 32 else 1)
