@@ -360,17 +360,21 @@ def schedule_tables(n: int, causal: bool, schedule):
 
 
 def mask_schedule_tables(B, H, N, d, dtype="bf16", causal=False, schedule="naive", *, window=0,
-                         block_mask=None, block_size=0):
-    """The backward's tables for a masked problem.  Returns a dict: n
-    (tiles per side), units (per unit [(kv, q), ...]), steps (per unit, the
-    lockstep step of each item; SHIFT only, else None), partial (per unit,
-    per item bool), rank (int32 [n, n], rank[q, kv], -1 where absent),
-    static (units run in head-aligned rounds)."""
+                         block_mask=None, block_size=0, slots=256):
+    """The backward's tables for a masked problem, as a launch on `slots`
+    co-resident workgroups runs them (0: this device's count; 256 is
+    MI355X's for the backward).  Returns a dict: n (tiles per side), units
+    (per unit [(kv, q), ...]), steps (per unit, the lockstep or timed step
+    of each item; SHIFT only, else None), partial (per unit, per item
+    bool), rank (int32 [n, n], rank[q, kv], -1 where absent), static (units
+    run in head-aligned rounds), slots_per_head (timed shift: the slots per
+    head it was timed on; 0 otherwise)."""
     lib = load()
     desc = _desc(B, H, N, d, dtype, causal, None, window, block_mask, block_size)
-    sizes = (ctypes.c_int32 * 4)()
-    check(lib.dash_attn_schedule_tables(ctypes.byref(desc), _sched(schedule), sizes, None, None,
-                                        None, None, None, None), "dash_attn_schedule_tables")
+    sizes = (ctypes.c_int32 * 5)()
+    check(lib.dash_attn_schedule_tables(ctypes.byref(desc), _sched(schedule), int(slots), sizes,
+                                        None, None, None, None, None, None),
+          "dash_attn_schedule_tables")
     n, nu, ni = sizes[0], sizes[1], sizes[2]
     off = np.zeros(nu + 1, dtype=np.int32)
     kv = np.zeros(max(ni, 1), dtype=np.int32)
@@ -379,7 +383,7 @@ def mask_schedule_tables(B, H, N, d, dtype="bf16", causal=False, schedule="naive
     pa = np.zeros(max(ni, 1), dtype=np.uint8)
     rank = np.zeros(n * n, dtype=np.int32)
     ip = ctypes.POINTER(ctypes.c_int32)
-    check(lib.dash_attn_schedule_tables(ctypes.byref(desc), _sched(schedule), sizes,
+    check(lib.dash_attn_schedule_tables(ctypes.byref(desc), _sched(schedule), int(slots), sizes,
                                         off.ctypes.data_as(ip), kv.ctypes.data_as(ip),
                                         qq.ctypes.data_as(ip), st.ctypes.data_as(ip),
                                         pa.ctypes.data, rank.ctypes.data_as(ip)),
@@ -392,7 +396,7 @@ def mask_schedule_tables(B, H, N, d, dtype="bf16", causal=False, schedule="naive
         partial.append([bool(pa[i]) for i in sl])
     shift = _sched(schedule) == SCHEDULES["shift"]
     return {"n": n, "units": units, "steps": steps if shift else None, "partial": partial,
-            "rank": rank.reshape(n, n), "static": bool(sizes[3])}
+            "rank": rank.reshape(n, n), "static": bool(sizes[3]), "slots_per_head": int(sizes[4])}
 
 
 def mask_schedule_predict(B, H, N, d, dtype="bf16", causal=False, schedule="naive", *, slots,

@@ -82,8 +82,8 @@ _SIGS = {
                                              _ip]),
     "dash_attn_bwd_resolve_schedule": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int,
                                                       ctypes.POINTER(ctypes.c_int)]),
-    "dash_attn_schedule_tables": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, _ip, _ip, _ip,
-                                                 _ip, _ip, ctypes.c_void_p, _ip]),
+    "dash_attn_schedule_tables": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, _i32, _ip, _ip,
+                                                 _ip, _ip, _ip, ctypes.c_void_p, _ip]),
     "dash_attn_schedule_predict": (ctypes.c_int, [ctypes.c_void_p, ctypes.c_int, _i32, _i32, _dp,
                                                   _dp]),
     "dash_attn_bwd_tune": (ctypes.c_int, [ctypes.POINTER(Desc), _vp, _vp, _vp, _vp, _vp, _vp,

@@ -58,7 +58,12 @@ struct LaunchPrediction {
 // ratio of heads (steady state: each further head adds the same work).
 bool launch_predict(const Tables& t, long heads, int maxco, const double cost[4], bool grouped,
                     LaunchPrediction& out) {
-  if (t.units() == 0 || heads < 1 || maxco < 1) return false;
+  if (heads < 1 || maxco < 1) return false;
+  if (t.units() == 0) {  // every pair masked: nothing runs
+    out = LaunchPrediction();
+    out.slots = maxco;
+    return true;
+  }
   int g = grouped ? kXcds : 1;
   if (maxco / g < 1 || (t.needs_static() && t.units() > maxco / g)) g = 1;
   if (t.needs_static() && t.units() > maxco) return false;
@@ -105,10 +110,18 @@ dash_status choose_schedule(const dash::TileMask& m, int heads, int slots, const
   const Sched cand[3] = {Sched::Naive, Sched::Descending, Sched::Shift};
   double best = 0.0;
   int best_i = -1;
+  int live_kv = 0;
+  for (int kv = 0; kv < m.n; ++kv)
+    for (int q = 0; q < m.n; ++q)
+      if (m.live[(size_t)q * m.n + kv]) {
+        ++live_kv;
+        break;
+      }
   for (int i = 0; i < 3; ++i) {
     pred[i] = NAN;
     Tables t;
-    if (!dash::build_tables(m, cand[i], t)) continue;
+    const int ws = m.plain ? 1 : dash::timed_slots(slots, heads, live_kv);
+    if (!dash::build_tables(m, cand[i], t, ws)) continue;
     if (dash::validate_tables(t)[0] != '\0') return DASH_ERR_SCHEDULE_INVALID;
     if (t.needs_static() && t.units() > slots) continue;
     dash::DagResult r;
@@ -266,7 +279,7 @@ struct TabEntry {
 std::mutex g_mu;
 uint64_t g_clock = 0;
 std::map<MaskKey, MaskEntry> g_masks;                     // special masks only
-std::map<std::pair<MaskKey, int>, TabEntry> g_tables;     // (mask, sched)
+std::map<std::tuple<MaskKey, int, int>, TabEntry> g_tables;  // (mask, sched, timed slots)
 std::map<std::tuple<int, int, int, int, int>, int> g_coresident;  // (device, dtype, d, masked, ordered)
 std::map<std::tuple<MaskKey, int, int>, Sched> g_auto;  // (mask, heads, slots) -> choice
 // (mask, sched, heads, slots, grouped) -> unit-major
@@ -355,11 +368,19 @@ int plain_max_unit_items(int n, bool causal, Sched s) {
   return (s == Sched::Shift && causal && n > 1) ? n + 1 : n;
 }
 
-// Tables of (mask, schedule), built, validated and (plain masks) checked
-// against the closed forms the device writes.  Host memory only.  Caller
-// holds g_mu.
-dash_status tab_entry(const MaskKey& key, Sched s, TabEntry** out) {
-  const auto k = std::make_pair(key, (int)s);
+// Slots per head of the timed shift that a launch on `maxco` co-resident
+// workgroups runs for a window or block mask (0: other schedules and the
+// plain masks, whose tables do not depend on it).  Caller holds g_mu.
+int plan_slots(const MaskKey& key, Sched s, long heads, int maxco) {
+  if (s != Sched::Shift || plain_key(key)) return 0;
+  return dash::timed_slots(maxco, heads, key.n - mask_entry(key)->n_dead_kv);
+}
+
+// Tables of (mask, schedule, timed slots from plan_slots), built, validated
+// and (plain masks) checked against the closed forms the device writes.
+// Host memory only.  Caller holds g_mu.
+dash_status tab_entry(const MaskKey& key, Sched s, int ws, TabEntry** out) {
+  const auto k = std::make_tuple(key, (int)s, ws);
   auto it = g_tables.find(k);
   if (it != g_tables.end()) {
     it->second.stamp = ++g_clock;
@@ -374,7 +395,8 @@ dash_status tab_entry(const MaskKey& key, Sched s, TabEntry** out) {
   if (plain) {
     if (!dash::build_tables(n, key.causal != 0, s, e.host)) return DASH_ERR_UNSUPPORTED;
   } else {
-    if (!dash::build_tables(mask_entry(key)->host, s, e.host)) return DASH_ERR_UNSUPPORTED;
+    if (!dash::build_tables(mask_entry(key)->host, s, e.host, ws > 0 ? ws : 1))
+      return DASH_ERR_UNSUPPORTED;
   }
   const Tables& t = e.host;
   if (dash::validate_tables(t)[0] != '\0') return DASH_ERR_SCHEDULE_INVALID;
@@ -563,7 +585,7 @@ dash_status run_bwd(const dash_attn_desc* desc, dash_schedule schedule, const vo
   st = resolve_schedule(schedule, mkey, heads, maxco, &s);
   if (st != DASH_OK) return st;
   TabEntry* tb = nullptr;
-  st = tab_entry(mkey, s, &tb);
+  st = tab_entry(mkey, s, plan_slots(mkey, s, heads, maxco), &tb);
   if (st != DASH_OK) return st;
   const Tables& host = tb->host;
   const int U = host.units();
@@ -580,6 +602,10 @@ dash_status run_bwd(const dash_attn_desc* desc, dash_schedule schedule, const vo
     dynamic = 1;
     grid = (int)std::min<long>(maxco, total_units);
     p_eff = grid;
+    // a timed shift needs enough workgroups to be deadlock-free device-wide
+    // (the kernel checks its XCD groups itself)
+    if (host.timed() && grid < dash::timed_need(host.slots_per_head, heads))
+      return DASH_ERR_UNSUPPORTED;
   }
   int xcd_mode = ordered ? 1 : 0;
   if (dbg && dbg->placement) xcd_mode = dbg->placement - 1;
@@ -648,6 +674,7 @@ dash_status run_bwd(const dash_attn_desc* desc, dash_schedule schedule, const vo
   // every workload); the atomic reference gains nothing from it
   a.xcd_mode = xcd_mode;
   a.unit_major = unit_major;
+  a.timed_slots = host.timed() ? host.slots_per_head : 0;
   a.scale = scale_of(desc);
   a.scale_log2 = a.scale * 1.4426950408889634f;
   a.spin_limit = (dbg && dbg->spin_limit) ? dbg->spin_limit : kDefaultSpin;
@@ -915,7 +942,10 @@ dash_status dash_attn_bwd_tune(const dash_attn_desc* desc, const void* q, const 
       {
         std::lock_guard<std::mutex> lock(g_mu);
         TabEntry* tb = nullptr;
-        if (tab_entry(mkey, (Sched)cand[i], &tb) != DASH_OK) continue;
+        const long bh = (long)desc->B * desc->H;
+        if (tab_entry(mkey, (Sched)cand[i], plan_slots(mkey, (Sched)cand[i], bh, maxco), &tb) !=
+            DASH_OK)
+          continue;
         if (tb->host.needs_static() && tb->host.units() > maxco) continue;
       }
       // one untimed launch, then `reps` timed ones
@@ -1004,8 +1034,14 @@ dash_status dash_attn_schedule_predict(const dash_attn_desc* desc, dash_schedule
   return guarded([&]() -> dash_status {
     const MaskKey mkey = mask_key(desc);
     if (plain_key(mkey) && mkey.n + 1 > dash::kMaxUnitItems) return DASH_ERR_UNSUPPORTED;
+    int ws = 0;
+    {
+      std::lock_guard<std::mutex> lock(g_mu);
+      ws = plan_slots(mkey, (Sched)schedule, (long)desc->B * desc->H, slots);
+    }
     Tables t;
-    if (!dash::build_tables(tile_mask(mkey), (Sched)schedule, t)) return DASH_ERR_UNSUPPORTED;
+    if (!dash::build_tables(tile_mask(mkey), (Sched)schedule, t, ws > 0 ? ws : 1))
+      return DASH_ERR_UNSUPPORTED;
     if (dash::validate_tables(t)[0] != '\0') return DASH_ERR_SCHEDULE_INVALID;
     if (t.needs_static() && t.units() > slots) return DASH_ERR_UNSUPPORTED;
     const long heads = (long)desc->B * desc->H;
@@ -1032,8 +1068,14 @@ dash_status dash_attn_bwd_predict(const dash_attn_desc* desc, dash_schedule sche
   return guarded([&]() -> dash_status {
     const MaskKey mkey = mask_key(desc);
     if (plain_key(mkey) && mkey.n + 1 > dash::kMaxUnitItems) return DASH_ERR_UNSUPPORTED;
+    int ws = 0;
+    {
+      std::lock_guard<std::mutex> lock(g_mu);
+      ws = plan_slots(mkey, (Sched)schedule, (long)desc->B * desc->H, slots);
+    }
     Tables t;
-    if (!dash::build_tables(tile_mask(mkey), (Sched)schedule, t)) return DASH_ERR_UNSUPPORTED;
+    if (!dash::build_tables(tile_mask(mkey), (Sched)schedule, t, ws > 0 ? ws : 1))
+      return DASH_ERR_UNSUPPORTED;
     if (dash::validate_tables(t)[0] != '\0') return DASH_ERR_SCHEDULE_INVALID;
     if (t.needs_static() && t.units() > slots) return DASH_ERR_UNSUPPORTED;
     LaunchPrediction lp;
@@ -1106,21 +1148,35 @@ dash_status dash_schedule_choose(int32_t n, int32_t causal, int32_t heads, int32
 }
 
 dash_status dash_attn_schedule_tables(const dash_attn_desc* desc, dash_schedule schedule,
-                                      int32_t sizes[4], int32_t* unit_offsets, int32_t* item_kv,
-                                      int32_t* item_q, int32_t* item_step, uint8_t* item_partial,
-                                      int32_t* rank) {
+                                      int32_t slots, int32_t sizes[5], int32_t* unit_offsets,
+                                      int32_t* item_kv, int32_t* item_q, int32_t* item_step,
+                                      uint8_t* item_partial, int32_t* rank) {
   dash_status st = check_desc(desc);
   if (st != DASH_OK) return st;
-  if (!sched_ok(schedule) || !sizes) return DASH_ERR_INVALID_ARG;
+  if (!sched_ok(schedule) || !sizes || slots < 0) return DASH_ERR_INVALID_ARG;
   return guarded([&]() -> dash_status {
     const MaskKey mkey = mask_key(desc);
+    int maxco = slots;
+    if (maxco == 0) {
+      int dev = 0;
+      if (hipGetDevice(&dev) != hipSuccess) return DASH_ERR_HIP;
+      bool masked = false;
+      {
+        std::lock_guard<std::mutex> lock(g_mu);
+        masked = any_partial(mkey);
+      }
+      const dash_status st2 = get_coresident(dev, desc->dtype, desc->d, masked,
+                                             schedule != DASH_SCHED_ATOMIC, &maxco);
+      if (st2 != DASH_OK) return st2;
+    }
     Tables t;
     {
       // the tables a launch runs: for a plain mask this also checks them
       // against the closed forms the device writes
       std::lock_guard<std::mutex> lock(g_mu);
       TabEntry* tb = nullptr;
-      const dash_status st2 = tab_entry(mkey, (Sched)schedule, &tb);
+      const int ws = plan_slots(mkey, (Sched)schedule, (long)desc->B * desc->H, maxco);
+      const dash_status st2 = tab_entry(mkey, (Sched)schedule, ws, &tb);
       if (st2 != DASH_OK) return st2;
       t = tb->host;
     }
@@ -1131,6 +1187,7 @@ dash_status dash_attn_schedule_tables(const dash_attn_desc* desc, dash_schedule 
     sizes[1] = t.units();
     sizes[2] = t.items();
     sizes[3] = t.needs_static() ? 1 : 0;
+    sizes[4] = t.slots_per_head;
     if (!fill) return DASH_OK;
     std::memcpy(unit_offsets, t.unit_off.data(), sizeof(int) * t.unit_off.size());
     if (t.items()) {

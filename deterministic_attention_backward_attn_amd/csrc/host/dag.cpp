@@ -2,7 +2,6 @@
 #include "dag.hpp"
 
 #include <algorithm>
-#include <functional>
 #include <queue>
 #include <utility>
 
@@ -72,25 +71,72 @@ bool dag_predict(const Tables& t, int heads, int slots, const double cost[4], Da
     const int p_eff = (slots / U) * U;
     for (long g = 0; g < total_units; ++g) slot_of[g] = (int)(g % p_eff);
   } else {
-    // first free slot, ties to the lowest index; times follow the model
-    typedef std::pair<double, int> Ev;
-    std::priority_queue<Ev, std::vector<Ev>, std::greater<Ev>> freeq;
-    for (int s = 0; s < slots; ++s) freeq.push(Ev(0.0, s));
-    std::vector<double> r_fin((size_t)I * heads, 0.0);
-    for (long g = 0; g < total_units; ++g) {
-      const Ev ev = freeq.top();
-      freeq.pop();
-      slot_of[g] = ev.second;
-      const int hd = head_of(g), u = unit_of(g);
-      double tnow = ev.first;
-      for (int i = t.unit_off[u]; i < t.unit_off[u + 1]; ++i) {
-        double tr = tnow + ccost(i);
-        if (pred[i] >= 0) tr = std::max(tr, r_fin[(size_t)hd * I + pred[i]] + hlat);
-        tnow = tr + r;
-        r_fin[(size_t)hd * I + i] = tnow;
+    // Event simulation of the work counter: a slot that becomes free takes
+    // the next unit (free slots in time order, ties to the lowest index);
+    // an item whose rank predecessor has not finished waits for it, also
+    // when that predecessor's unit was handed out later (timed shift).
+    typedef std::pair<double, int> Ev;  // (time the slot's next step starts, slot)
+    std::priority_queue<Ev, std::vector<Ev>, std::greater<Ev>> evq;
+    std::vector<long> cur(slots, -1);   // global unit on the slot, -1 when free
+    std::vector<int> pos_in(slots, 0);  // next item of that unit
+    std::vector<double> r_fin((size_t)I * heads, -1.0);
+    std::vector<int> waiter((size_t)I * heads, -1);  // slot blocked on this item
+    std::vector<double> ready((size_t)I * heads, 0.0);  // start of a blocked item
+    long next_unit = 0, done_units = 0;
+    for (int s = 0; s < slots; ++s) evq.push(Ev(0.0, s));
+    // run slots' items until each blocks or frees; an item that finishes
+    // hands its blocked successor's slot to the same loop (times only grow:
+    // every slot resumed here runs at or after the event being handled)
+    std::vector<std::pair<int, double>> work;
+    auto advance = [&](int s0, double t0) {
+      work.push_back(std::make_pair(s0, t0));
+      while (!work.empty()) {
+        const int s = work.back().first;
+        double tnow = work.back().second;
+        work.pop_back();
+        for (;;) {
+          if (cur[s] < 0) {
+            evq.push(Ev(tnow, s));  // free: takes a unit when its turn comes
+            break;
+          }
+          const long g = cur[s];
+          const int hd = head_of(g), u = unit_of(g);
+          const size_t gi = (size_t)hd * I + t.unit_off[u] + pos_in[s];
+          const int p = pred[t.unit_off[u] + pos_in[s]];
+          if (p >= 0 && r_fin[(size_t)hd * I + p] < 0.0) {
+            waiter[(size_t)hd * I + p] = s;
+            ready[gi] = tnow;
+            break;
+          }
+          double tr = tnow + ccost((int)(gi - (size_t)hd * I));
+          if (p >= 0) tr = std::max(tr, r_fin[(size_t)hd * I + p] + hlat);
+          tnow = tr + r;
+          r_fin[gi] = tnow;
+          if (++pos_in[s] == t.unit_off[u + 1] - t.unit_off[u]) {
+            cur[s] = -1;
+            ++done_units;
+          }
+          const int w = waiter[gi];
+          if (w >= 0) {
+            waiter[gi] = -1;
+            const size_t wi = (size_t)head_of(cur[w]) * I + t.unit_off[unit_of(cur[w])] + pos_in[w];
+            work.push_back(std::make_pair(w, ready[wi]));
+          }
+        }
       }
-      freeq.push(Ev(tnow, ev.second));
+    };
+    while (!evq.empty()) {
+      const Ev ev = evq.top();
+      evq.pop();
+      const int s = ev.second;
+      if (cur[s] >= 0) continue;  // stale
+      if (next_unit >= total_units) continue;
+      cur[s] = next_unit;
+      pos_in[s] = 0;
+      slot_of[next_unit++] = s;
+      advance(s, ev.first);
     }
+    if (done_units != total_units) return false;  // the counter would deadlock
   }
 
   // explicit graph: node 2*gi = C, 2*gi+1 = R, gi = head*I + i

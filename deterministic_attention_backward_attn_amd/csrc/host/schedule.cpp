@@ -16,7 +16,7 @@
 //
 // Masks other than full and causal (windows, block masks) keep the same
 // Naive / Descending / Atomic rules over the live pairs; Shift becomes a
-// proper edge colouring of the live-pair graph (see build_tables).
+// timed shift (see build_tables in schedule.hpp).
 #include "schedule.hpp"
 
 #include <algorithm>
@@ -61,137 +61,65 @@ void ranks_by_step(Tables& t) {
   }
 }
 
-// Proper edge colouring of the bipartite live-pair graph (KV tiles x Q
-// blocks) with as many colours as the largest degree (Koenig's theorem):
-// each pair takes a colour free at both ends, after swapping two colours
-// along an alternating path when the ends disagree.  One unit per KV tile
-// with live pairs, its pairs in colour order; step = colour.
-void colour_units(const TileMask& m, Tables& t) {
+// Timed shift (declared with build_tables): a step-by-step simulation of
+// `slots` workgroups running the units of one head.
+void timed_shift(const TileMask& m, int slots, Tables& t) {
   const int n = m.n;
-  int delta = 0;
-  std::vector<int> deg_q(n, 0);
+  std::vector<int> len(n, 0), order;
   for (int kv = 0; kv < n; ++kv) {
-    int dk = 0;
-    for (int q = 0; q < n; ++q)
-      if (m.live[(size_t)q * n + kv]) {
-        ++dk;
-        ++deg_q[q];
-      }
-    delta = std::max(delta, dk);
+    for (int q = 0; q < n; ++q) len[kv] += m.live[(size_t)q * n + kv] ? 1 : 0;
+    if (len[kv]) order.push_back(kv);
   }
-  for (int q = 0; q < n; ++q) delta = std::max(delta, deg_q[q]);
-  // at_kv[kv * delta + c] = Q block of kv's pair with colour c, or -1
-  std::vector<int> at_kv((size_t)n * delta, -1), at_q((size_t)n * delta, -1);
-  auto first_free = [&](const std::vector<int>& tab, int v) {
-    for (int c = 0; c < delta; ++c)
-      if (tab[(size_t)v * delta + c] < 0) return c;
-    return -1;  // unreachable: an uncoloured pair leaves a colour free
-  };
-  struct Edge { int kv, q, c; };
-  std::vector<Edge> path;
-  for (int kv = 0; kv < n; ++kv)
-    for (int q = 0; q < n; ++q) {
-      if (!m.live[(size_t)q * n + kv]) continue;
-      const int a = first_free(at_kv, kv), b = first_free(at_q, q);
-      if (at_q[(size_t)q * delta + a] >= 0) {
-        // a is taken at q (so a != b): swap a and b on the a/b path from q;
-        // it cannot reach kv, where a is free
-        path.clear();
-        int x = q, c = a;
-        bool q_side = true;
-        for (;;) {
-          const int y = q_side ? at_q[(size_t)x * delta + c] : at_kv[(size_t)x * delta + c];
-          if (y < 0) break;
-          path.push_back(q_side ? Edge{y, x, c} : Edge{x, y, c});
-          x = y;
-          q_side = !q_side;
-          c = (c == a) ? b : a;
-        }
-        for (const Edge& e : path) {
-          at_kv[(size_t)e.kv * delta + e.c] = -1;
-          at_q[(size_t)e.q * delta + e.c] = -1;
-        }
-        for (const Edge& e : path) {
-          const int c2 = (e.c == a) ? b : a;
-          at_kv[(size_t)e.kv * delta + c2] = e.q;
-          at_q[(size_t)e.q * delta + c2] = e.kv;
-        }
-      }
-      at_kv[(size_t)kv * delta + a] = q;
-      at_q[(size_t)q * delta + a] = kv;
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return len[a] > len[b]; });
+  const int U = (int)order.size();
+  // each unit's Q blocks in cyclic order from its diagonal; a unit takes
+  // the first one not yet used by itself and not taken by another unit at
+  // this step (scanned from `head`, the first one it has not used)
+  std::vector<std::vector<int>> cyc(n);
+  std::vector<std::vector<uint8_t>> used(n);
+  std::vector<int> head(n, 0);
+  for (int kv : order) {
+    for (int d = 0; d < n; ++d) {
+      const int q = (kv + d) % n;
+      if (m.live[(size_t)q * n + kv]) cyc[kv].push_back(q);
     }
-  for (int kv = 0; kv < n; ++kv) {
-    bool opened = false;
-    for (int c = 0; c < delta; ++c) {
-      const int q = at_kv[(size_t)kv * delta + c];
-      if (q < 0) continue;
-      if (!opened) {
-        t.unit_off.push_back((int)t.kv.size());
-        opened = true;
+    used[kv].assign(cyc[kv].size(), 0);
+  }
+  std::vector<std::vector<std::pair<int, int>>> got(n);  // per KV tile: (step, q)
+  std::vector<int> taken(n, -1);                         // step at which q was last taken
+  std::vector<int> running, start(n, -1);
+  int next = 0;
+  for (int step = 0; next < U || !running.empty(); ++step) {
+    while ((int)running.size() < slots && next < U) {
+      start[order[next]] = step;
+      running.push_back(order[next++]);
+    }
+    for (int kv : running) {
+      const std::vector<int>& c = cyc[kv];
+      int& h = head[kv];
+      while (h < (int)c.size() && used[kv][h]) ++h;
+      for (int i = h; i < (int)c.size(); ++i) {
+        if (used[kv][i] || taken[c[i]] == step) continue;
+        used[kv][i] = 1;
+        taken[c[i]] = step;
+        got[kv].push_back(std::make_pair(step, c[i]));
+        break;
       }
+    }
+    running.erase(std::remove_if(running.begin(), running.end(),
+                                 [&](int kv) { return got[kv].size() == cyc[kv].size(); }),
+                  running.end());
+  }
+  for (int kv : order) {
+    t.unit_off.push_back((int)t.kv.size());
+    t.unit_start.push_back(start[kv]);
+    for (const auto& e : got[kv]) {
       t.kv.push_back(kv);
-      t.q.push_back(q);
-      t.step.push_back(c);
+      t.q.push_back(e.second);
+      t.step.push_back(e.first);
     }
   }
-}
-
-// If the units' waits (a unit waits for the unit ranked just before it at
-// each of its Q blocks) form no cycle, order the units so that every wait
-// points to an earlier unit (a topological order, earliest first step
-// first): a work counter can then hand them out with no deadlock and no
-// need for a whole head to be resident.  Otherwise the tables stay static.
-void order_for_dynamic(Tables& t) {
-  const int n = t.n, U = t.units();
-  std::vector<int> unit_of_item(t.items());
-  for (int u = 0; u < U; ++u)
-    for (int i = t.unit_off[u]; i < t.unit_off[u + 1]; ++i) unit_of_item[i] = u;
-  std::vector<int> pos((size_t)n * n, -1);
-  for (int i = 0; i < t.items(); ++i) pos[(size_t)t.q[i] * n + t.kv[i]] = i;
-  std::vector<std::vector<int>> succ(U);
-  std::vector<int> indeg(U, 0);
-  for (int q = 0; q < n; ++q) {
-    std::vector<int> by_rank(n, -1);
-    for (int kv = 0; kv < n; ++kv) {
-      const int r = t.rank[(size_t)q * n + kv];
-      if (r >= 0) by_rank[r] = pos[(size_t)q * n + kv];
-    }
-    for (int r = 1; r < n && by_rank[r] >= 0; ++r) {
-      const int a = unit_of_item[by_rank[r - 1]], b = unit_of_item[by_rank[r]];
-      if (a != b) {
-        succ[a].push_back(b);
-        ++indeg[b];
-      }
-    }
-  }
-  typedef std::pair<int, int> Key;  // (first step, unit)
-  std::priority_queue<Key, std::vector<Key>, std::greater<Key>> ready;
-  for (int u = 0; u < U; ++u)
-    if (!indeg[u]) ready.push(Key(t.step[t.unit_off[u]], u));
-  std::vector<int> order;
-  while (!ready.empty()) {
-    const int u = ready.top().second;
-    ready.pop();
-    order.push_back(u);
-    for (int v : succ[u])
-      if (--indeg[v] == 0) ready.push(Key(t.step[t.unit_off[v]], v));
-  }
-  if ((int)order.size() != U) return;  // cyclic: keep head-aligned rounds
-  Tables r = t;
-  r.unit_off.assign(1, 0);
-  r.kv.clear();
-  r.q.clear();
-  r.step.clear();
-  for (int u : order) {
-    for (int i = t.unit_off[u]; i < t.unit_off[u + 1]; ++i) {
-      r.kv.push_back(t.kv[i]);
-      r.q.push_back(t.q[i]);
-      r.step.push_back(t.step[i]);
-    }
-    r.unit_off.push_back((int)r.kv.size());
-  }
-  r.static_policy = false;
-  t = std::move(r);
+  t.slots_per_head = U > 0 ? std::min(slots, U) : 0;  // no unit: nothing to time
 }
 
 }  // namespace
@@ -253,21 +181,21 @@ TileMask make_mask(int n, int tile, bool causal, int window, const uint8_t* bloc
   return m;
 }
 
-bool build_tables(const TileMask& m, Sched s, Tables& t) {
+bool build_tables(const TileMask& m, Sched s, Tables& t, int slots) {
   if (m.plain) return build_tables(m.n, m.causal, s, t);
   t = Tables();
   const int n = m.n;
   t.n = n;
   t.causal = m.causal;
   t.sched = s;
-  t.static_policy = s == Sched::Shift;
-  if (n < 1) return false;
+  t.static_policy = false;
+  if (n < 1 || slots < 1) return false;
   t.live = m.live;
   t.partial = m.partial;
   t.rank.assign((size_t)n * n, -1);
   Builder b(t);
   if (s == Sched::Shift) {
-    colour_units(m, t);
+    timed_shift(m, slots, t);
   } else {
     for (int kv = 0; kv < n; ++kv) {
       bool opened = false;
@@ -282,11 +210,17 @@ bool build_tables(const TileMask& m, Sched s, Tables& t) {
   }
   b.finish();
   if (s == Sched::Naive || s == Sched::Descending) ranks_by_kv(t);
-  else if (s == Sched::Shift) {
-    ranks_by_step(t);
-    order_for_dynamic(t);
-  }
+  else if (s == Sched::Shift) ranks_by_step(t);
   return true;
+}
+
+int timed_slots(int maxco, long heads, int units) {
+  if (maxco < 1 || heads < 1 || units < 1) return 1;
+  const long grid = std::min<long>(maxco, heads * units);
+  long ws = (grid - 1) / heads + 1;  // device-wide
+  const int g = maxco / 8;
+  if (g >= 1) ws = std::min<long>(ws, (g - 1) / ((heads + 7) / 8) + 1);  // XCD groups
+  return (int)std::max<long>(1, std::min<long>(ws, units));
 }
 
 bool build_tables(int n, bool causal, Sched s, Tables& t) {
@@ -407,6 +341,29 @@ const char* validate_tables(const Tables& t) {
       if (std::adjacent_find(v.begin(), v.end()) != v.end()) return "two units on one block at one step";
     }
   }
+  if (t.timed()) {
+    // the timing certificate: units listed in start order, and at most
+    // slots_per_head units between their first and last step at any step
+    if (t.step.empty() || t.needs_static() || (int)t.unit_start.size() != t.units())
+      return "malformed timed tables";
+    std::vector<int> opens, closes;
+    for (int u = 0; u < t.units(); ++u) {
+      if (t.unit_off[u] == t.unit_off[u + 1]) return "empty unit";
+      opens.push_back(t.unit_start[u]);
+      closes.push_back(t.step[t.unit_off[u + 1] - 1]);
+      if (opens[u] < 0 || t.step[t.unit_off[u]] < opens[u]) return "item before its unit's start";
+      if (u > 0 && opens[u] < opens[u - 1]) return "units not in start order";
+    }
+    std::sort(closes.begin(), closes.end());
+    // units running at the step where unit u starts: started at or before
+    // it (listed no later) and not closed before it
+    for (int u = 0; u < t.units(); ++u) {
+      const long closed_before =
+          std::lower_bound(closes.begin(), closes.end(), opens[u]) - closes.begin();
+      const long started = std::upper_bound(opens.begin(), opens.end(), opens[u]) - opens.begin();
+      if (started - closed_before > t.slots_per_head) return "more units running than slots";
+    }
+  }
   if (!t.ordered()) return "";
   // rank rows are permutations
   std::vector<int> pred_item((size_t)t.items(), -1);
@@ -430,8 +387,12 @@ const char* validate_tables(const Tables& t) {
       const int cur = pos[(size_t)q * n + by_rank[r]];
       const int prev = pos[(size_t)q * n + by_rank[r - 1]];
       pred_item[cur] = prev;
-      if (!t.needs_static() && unit_of[(size_t)q * n + by_rank[r - 1]] >= unit_of[(size_t)q * n + by_rank[r]])
+      if (t.timed()) {
+        if (t.step[prev] >= t.step[cur]) return "dQ order is not by step";
+      } else if (!t.needs_static() &&
+                 unit_of[(size_t)q * n + by_rank[r - 1]] >= unit_of[(size_t)q * n + by_rank[r]]) {
         return "wait on a later unit under the dynamic policy";
+      }
     }
   }
   // item-level graph of one head (unit chains + order edges) must be acyclic

@@ -35,6 +35,8 @@ struct BwdArgs {
   int p_eff;              // static policy: workgroups that take units
   int dynamic;            // 1: take units from the work counter
   int unit_major;         // dynamic only: 1 = unit lu of every head in turn, 0 = head by head
+  int timed_slots;        // dynamic timed shift: slots per head it was timed on (0: none);
+                          // a group of W workgroups with h heads needs W >= (slots-1)h + 1
   int xcd_mode;           // 0 device-wide; XCD-local groups when they fit with
                           // 1: L2-coherent, 2: device-coherent accumulator
   float scale;            // softmax scale s

@@ -32,7 +32,9 @@
  *               the launch's placement (dash_attn_bwd_predict), or the one
  *               dash_attn_bwd_tune measured fastest for the shape.
  * With a window or block mask the same rules run over the tile pairs that
- * hold a visible key; SHIFT becomes a proper colouring of those pairs.
+ * hold a visible key; SHIFT becomes a timed shift (see
+ * dash_attn_schedule_tables), the summary's limitations naming
+ * block-sparse masks as needing schedule extensions.
  *
  * Conventions for every call below.
  *   Layout      Q, K, V, O, dO, dQ, dK, dV: contiguous [B, H, N, d], d
@@ -440,26 +442,36 @@ dash_status dash_attn_bwd_resolve_schedule(const dash_attn_desc* desc, dash_sche
 
 /*
  * The backward's schedule tables for any descriptor (any mask), host only:
- * the same tables dash_attn_bwd runs (after DASH_SCHED_AUTO resolution).
- * Two calls: with any array NULL, fills sizes = {n tiles per side, units,
- * items, static} and returns (static = 1: units run in head-aligned rounds,
- * a whole head resident; 0: from a work counter in unit order); then with
- * arrays of those sizes (sizes unchanged):
+ * the same tables dash_attn_bwd runs on `slots` co-resident workgroups (0:
+ * this device's count for the backward; queries the device).  Two calls:
+ * with any array NULL, fills sizes = {n tiles per side, units, items,
+ * static, slots per head} and returns (static = 1: units run in
+ * head-aligned rounds, a whole head resident; 0: from a work counter in
+ * unit order); then with arrays of those sizes (sizes unchanged):
  * unit_offsets[units + 1], item_kv/item_q/item_step/item_partial[items]
- * (step: lockstep step for SHIFT, else -1; partial: the pair has hidden
- * elements) and rank[n * n] (rank[q * n + kv], -1 where absent).  SHIFT on
- * a window or block mask is a proper colouring of the live pairs: no unit
- * and no Q block holds two pairs at one step (the shift's defining
- * property, explainer 2.2 B), with as many steps as the busiest tile has
- * pairs; when the units can be ordered so that every wait points to an
- * earlier unit, they are, and run from a work counter (static = 0).  Tile
- * pairs that hold no visible key are left out; KV tiles with none get no
- * unit.
+ * (step: lockstep or timed step for SHIFT, else -1; partial: the pair has
+ * hidden elements) and rank[n * n] (rank[q * n + kv], -1 where absent).
+ *
+ * SHIFT on a window or block mask is a timed shift: a step-by-step
+ * simulation of s workgroup slots running one head (s = slots per head,
+ * sizes[4]): one unit per KV tile with live pairs, started longest first
+ * (ties: lower KV tile) as slots free up; at each step every running unit,
+ * in start order, takes the remaining Q block of its own that no other
+ * unit took at that step and that comes first cyclically from its own
+ * diagonal (smallest (q - kv) mod n), or idles for the step.  No two units
+ * meet on a block at one step (the shift's defining property, explainer
+ * 2.2 B), a block's dQ order is by step, items run in step order and units
+ * in start order.  Run from a work counter, such tables cannot deadlock
+ * when W >= (s - 1) h + 1 for W workgroups shared by h heads, in any
+ * interleaving of the heads' units; s is the largest count for which that
+ * holds both in the launch's 8 XCD groups (slots / 8 workgroups, ceil(B*H
+ * / 8) heads each) and device-wide.  Tile pairs that hold no visible key
+ * are left out; KV tiles with none get no unit.
  */
 dash_status dash_attn_schedule_tables(const dash_attn_desc* desc, dash_schedule schedule,
-                                      int32_t sizes[4], int32_t* unit_offsets, int32_t* item_kv,
-                                      int32_t* item_q, int32_t* item_step, uint8_t* item_partial,
-                                      int32_t* rank);
+                                      int32_t slots, int32_t sizes[5], int32_t* unit_offsets,
+                                      int32_t* item_kv, int32_t* item_q, int32_t* item_step,
+                                      uint8_t* item_partial, int32_t* rank);
 
 /*
  * dash_schedule_predict with a choice of unit order: unit_major = 1: the

@@ -24,11 +24,13 @@ processor.  Concretely, for a launch with P processor slots:
 Slots take units in one of two ways (this project's reading of how a
 persistent grid runs the explainer's "one KV tile per SM" chains):
 * "dynamic": units in head-major order go to whichever slot frees first
-  (ties to the lowest slot) - used when every order edge points to an
-  earlier unit (NAIVE, DESCENDING, ATOMIC);
+  (ties to the lowest slot), an add waiting for its block's previous
+  contributor even when that one's unit was handed out later - used for
+  NAIVE, DESCENDING, ATOMIC and the timed shift of window and block masks;
 * "static": head-aligned rounds, slot = u mod P' with P' the largest
-  multiple of the units per head not above P - used for SHIFT, whose order
-  edges point to later units of the same head.
+  multiple of the units per head not above P - used for the pages' SHIFT
+  on the full and causal masks, whose order edges point to later units of
+  the same head.
 
 Lemma 1 of the explainer (2.2 B): adding a zero-weight edge u -> v keeps the
 critical path when depth(u) <= depth(v).  Read with depth(u) = earliest
@@ -163,25 +165,64 @@ def realize(schedule, n, causal, heads, slots, cost, tables=None, unit_major=Fal
         for u in range(len(glob)):
             assign[u] = u % p_eff
     else:
-        # Event simulation: every order edge points to an earlier unit, so
-        # units can be timed in grab order.
-        free = [0.0] * slots
+        # Event simulation of the work counter: a slot that becomes free
+        # takes the next unit in `glob` order; an item runs when its slot
+        # reaches it, and its add waits for the block's previous
+        # contributor, also when that contributor's unit was handed out
+        # later (timed shift).  Events are handled in time order: an item at
+        # the time its compute starts (once its predecessor's add is known),
+        # a free slot at the time it frees; ties go to items, then to the
+        # lower slot.
+        state = [None] * slots        # [unit, item index, time] per busy slot
+        free_at = [0.0] * slots       # time a free slot frees (None when busy)
         r_fin = {}
-        for u, items in enumerate(glob):
-            s = min(range(slots), key=lambda i: (free[i], i))
-            assign[u] = s
-            t = free[s]
-            for k, (hd, kv, q) in enumerate(items):
-                c = icost(kv, q)
-                t_c = t + c
-                t_r = t_c
+        nxt = 0
+        while True:
+            best = None
+            for s_ in range(slots):
+                if state[s_] is None:
+                    if free_at[s_] is not None and nxt < len(glob):
+                        key = (free_at[s_], 1, s_)
+                        if best is None or key < best:
+                            best = key
+                    continue
+                u, k, t = state[s_]
+                hd, kv, q = glob[u][k]
                 if ranks is not None and ranks[q][kv] > 0:
                     prev = [kv2 for kv2 in range(n) if ranks[q][kv2] == ranks[q][kv] - 1][0]
-                    t_r = max(t_r, r_fin[(hd, prev, q)] + cost[3])
-                t = t_r + cost[2]
-                r_fin[(hd, kv, q)] = t
-            free[s] = t
-        sim_finish = max(free) if glob else 0.0
+                    if (hd, prev, q) not in r_fin:
+                        continue
+                key = (t, 0, s_)
+                if best is None or key < best:
+                    best = key
+            if best is None:
+                break
+            t, kind, s_ = best
+            if kind == 1:
+                assign[nxt] = s_
+                state[s_] = [nxt, 0, t]
+                free_at[s_] = None
+                nxt += 1
+                if not glob[nxt - 1]:
+                    state[s_] = None
+                    free_at[s_] = t
+                continue
+            u, k, t = state[s_]
+            hd, kv, q = glob[u][k]
+            t_r = t + icost(kv, q)
+            if ranks is not None and ranks[q][kv] > 0:
+                prev = [kv2 for kv2 in range(n) if ranks[q][kv2] == ranks[q][kv] - 1][0]
+                t_r = max(t_r, r_fin[(hd, prev, q)] + cost[3])
+            t = t_r + cost[2]
+            r_fin[(hd, kv, q)] = t
+            if k + 1 < len(glob[u]):
+                state[s_] = [u, k + 1, t]
+            else:
+                state[s_] = None
+                free_at[s_] = t
+        if nxt < len(glob) or any(x is not None for x in state):
+            raise ValueError("the work counter deadlocks on these tables")
+        sim_finish = max(r_fin.values()) if r_fin else 0.0
 
     edges = list(order_edges)
     last_on_slot = {}

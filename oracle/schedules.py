@@ -148,14 +148,195 @@ def contributors(n: int, causal: bool, q: int) -> int:
 # a tile pair (kv, q) is live when at least one of its (query, key) pairs is
 # visible, and partial when it is live but some pair is hidden (the kernel
 # then masks elements).  NAIVE / DESCENDING / ATOMIC visit each KV tile's
-# live Q blocks ascending / descending, dQ order ascending kv.  SHIFT for a
-# general tile graph keeps the pages' defining property - at every step the
-# units touch distinct Q blocks - by giving each live pair a step (colour)
-# such that no unit and no Q block has two pairs at one step, with as many
-# steps as the busiest tile has pairs; a unit runs its pairs in step order
-# and a block's dQ order is by step.  Such colourings are not unique, so the
-# oracle checks a product table against these rules (``check_step_schedule``)
-# instead of building its own.
+# live Q blocks ascending / descending, dQ order ascending kv.
+#
+# SHIFT on such a mask is a *timed shift* (``timed_shift``): the pages'
+# defining property - units running side by side touch distinct Q blocks,
+# and a block's dQ order is the order in which units reach it - kept by
+# simulating, step by step, a number of workgroup slots running one head's
+# units, and taking the dQ orders from that simulated timing.  The pages'
+# full-mask shift is the special case of a full mask with a slot per tile.
+# Tables built that way may make a unit wait for one handed out later, so
+# they carry a slot count; ``timed_slots`` and ``run_counter`` give and
+# check the number of workgroups under which a work counter cannot
+# deadlock on them.
+
+
+def timed_shift(live_t, slots):
+    """Timed shift of one head on `slots` workgroup slots.
+
+    Units: one per KV tile with live pairs, started longest first (ties: the
+    lower KV tile), each as soon as a slot is free (at step 0 the first
+    `slots`; a unit that takes its last block at step t frees its slot for
+    step t + 1).  At every step the running units, in start order, each
+    take the one of their remaining Q blocks that no other unit has taken at
+    this step and that comes first going up cyclically from the unit's own
+    diagonal, i.e. with the smallest (q - kv) mod n; a unit with every
+    remaining block taken idles for the step.
+
+    Returns (units, steps, rank, starts): per unit in start order its items
+    [(kv, q), ...] in step order and their steps, rank[q][kv] = the
+    position of kv's step among the block's steps (None where dead), and
+    the step at which each unit took its slot (a unit whose blocks are all
+    taken when it starts idles, so its first item can come later)."""
+    n = len(live_t)
+    if slots < 1:
+        raise ValueError("slots must be >= 1")
+    blocks = {kv: [q for q in range(n) if live_t[q][kv]] for kv in range(n)}
+    order = sorted((kv for kv in range(n) if blocks[kv]), key=lambda kv: (-len(blocks[kv]), kv))
+    remaining = {kv: set(blocks[kv]) for kv in order}
+    got = {kv: [] for kv in order}
+    start = {}
+    running, started, step = [], 0, 0
+    while started < len(order) or running:
+        while len(running) < slots and started < len(order):
+            start[order[started]] = step
+            running.append(order[started])
+            started += 1
+        taken = set()
+        for kv in running:
+            free = [q for q in remaining[kv] if q not in taken]
+            if free:
+                q = min(free, key=lambda q: (q - kv) % n)
+                taken.add(q)
+                remaining[kv].remove(q)
+                got[kv].append((step, q))
+        running = [kv for kv in running if remaining[kv]]
+        step += 1
+    units_out = [[(kv, q) for _, q in got[kv]] for kv in order]
+    steps_out = [[st for st, _ in got[kv]] for kv in order]
+    rank = [[None] * n for _ in range(n)]
+    for q in range(n):
+        by_step = sorted((st, kv) for kv in order for st, qq in got[kv] if qq == q)
+        for r, (_, kv) in enumerate(by_step):
+            rank[q][kv] = r
+    return units_out, steps_out, rank, [start[kv] for kv in order]
+
+
+def timed_slots(maxco, heads, n_units):
+    """Slots per head of the timed shift for a launch on `maxco` co-resident
+    workgroups and `heads` heads of `n_units` units: the largest s with
+    (s - 1) * h + 1 workgroups available both in 8 XCD groups (maxco // 8
+    workgroups, h = ceil(heads / 8)) and device-wide (min(maxco,
+    heads * n_units) workgroups, h = heads), at most n_units, at least 1."""
+    if maxco < 1 or heads < 1 or n_units < 1:
+        return 1
+    grid = min(maxco, heads * n_units)
+    s = (grid - 1) // heads + 1
+    g = maxco // 8
+    if g >= 1:
+        s = min(s, (g - 1) // -(-heads // 8) + 1)
+    return max(1, min(s, n_units))
+
+
+def run_counter(units, rank, heads, workgroups, durations, order="head"):
+    """Executes tables under a work counter, one event at a time, with no
+    model of time beyond the given durations: `workgroups` workers take
+    units from a counter (head-major: head 0's units in list order, then
+    head 1's ...; "unit": unit 0 of every head, then unit 1, ...; or an
+    explicit list of (head, unit)), run their items in list order, and an
+    item's dQ add waits until the block's previous contributor (by rank)
+    of the same head has added.  durations(head, unit, item) > 0 is each
+    item's compute time.  Returns the finish time, or None when every
+    worker is stuck waiting (a deadlock)."""
+    n = len(rank)
+    if order == "head":
+        seq = [(h, u) for h in range(heads) for u in range(len(units))]
+    elif order == "unit":
+        seq = [(h, u) for u in range(len(units)) for h in range(heads)]
+    else:
+        seq = list(order)
+    prev = {}
+    for q in range(n):
+        chain = sorted((rank[q][kv], kv) for kv in range(n) if rank[q][kv] is not None)
+        for (_, a), (_, b) in zip(chain, chain[1:]):
+            prev[(b, q)] = a
+    added = {}                       # (head, kv, q) -> time its add finished
+    work = [None] * workgroups       # [head, unit, item index, clock] per worker
+    nxt = 0
+    clock = 0.0
+    for w in range(workgroups):
+        if nxt < len(seq):
+            work[w] = [seq[nxt][0], seq[nxt][1], 0, 0.0]
+            nxt += 1
+    while any(x is not None for x in work):
+        # the worker whose next add can happen earliest goes first
+        best = None
+        for w, x in enumerate(work):
+            if x is None:
+                continue
+            h, u, i, t = x
+            kv, q = units[u][i]
+            ready = t + durations(h, u, i)
+            p = prev.get((kv, q))
+            if p is not None:
+                if (h, p, q) not in added:
+                    continue
+                ready = max(ready, added[(h, p, q)])
+            if best is None or (ready, w) < best[:2]:
+                best = (ready, w)
+        if best is None:
+            return None
+        t_add, w = best
+        h, u, i, _ = work[w]
+        kv, q = units[u][i]
+        added[(h, kv, q)] = t_add
+        clock = max(clock, t_add)
+        if i + 1 < len(units[u]):
+            work[w] = [h, u, i + 1, t_add]
+        elif nxt < len(seq):
+            work[w] = [seq[nxt][0], seq[nxt][1], 0, t_add]
+            nxt += 1
+        else:
+            work[w] = None
+    return clock
+
+
+def check_timed_schedule(live_t, unit_items, steps, rank, starts, slots):
+    """The timing certificate of a timed shift: every live pair once, a KV
+    tile in one unit, steps increasing within a unit and distinct within a
+    Q block, dQ orders by step, units listed in the order of their start
+    steps, no item before its unit's start, and at most `slots` units
+    between their start and their last step at any step.  Returns '' or
+    the first rule broken."""
+    n = len(live_t)
+    seen, owner = {}, {}
+    for u, (items, st) in enumerate(zip(unit_items, steps)):
+        if not items or len(items) != len(st):
+            return "empty unit or steps do not match items"
+        if any(b <= a for a, b in zip(st, st[1:])):
+            return "steps not increasing within a unit"
+        for (kv, q), s in zip(items, st):
+            if not (0 <= kv < n and 0 <= q < n) or not live_t[q][kv]:
+                return "dead or out-of-range pair"
+            if (kv, q) in seen:
+                return "pair twice"
+            if owner.setdefault(kv, u) != u:
+                return "KV tile in two units"
+            seen[(kv, q)] = s
+    if len(seen) != sum(sum(1 for x in row if x) for row in live_t):
+        return "live pair missing"
+    if len(starts) != len(steps):
+        return "starts do not match units"
+    if any(st[0] < s0 for st, s0 in zip(steps, starts)):
+        return "item before its unit's start"
+    if any(b < a for a, b in zip(starts, starts[1:])):
+        return "units not in start order"
+    last = max((st[-1] for st in steps), default=-1)
+    for t in range(last + 1):
+        if sum(1 for st, s0 in zip(steps, starts) if s0 <= t <= st[-1]) > slots:
+            return "more units running than slots"
+    for q in range(n):
+        contrib = sorted((seen[(kv, q)], kv) for kv in range(n) if live_t[q][kv])
+        if len({s for s, _ in contrib}) != len(contrib):
+            return "two units on one block at one step"
+        for r, (_, kv) in enumerate(contrib):
+            if rank[q][kv] != r:
+                return "dQ order is not by step"
+        for kv in range(n):
+            if not live_t[q][kv] and rank[q][kv] is not None:
+                return "rank for a dead pair"
+    return ""
 
 
 def tile_liveness(mask, n_tiles: int, tile: int):
@@ -193,50 +374,3 @@ def masked_rank_table(live_t):
                 rank[q][kv] = r
                 r += 1
     return rank
-
-
-def check_step_schedule(live_t, unit_items, steps, rank, dynamic=False):
-    """Validate a SHIFT table for a general tile graph.  unit_items: per unit
-    [(kv, q), ...] in run order; steps: per unit the step of each item;
-    rank[q][kv].  dynamic: the units are handed out in list order by a work
-    counter, so every wait (an item waits for the item ranked just before
-    it at its Q block) must point to an earlier unit.  Returns '' or the
-    first rule broken."""
-    n = len(live_t)
-    deg_kv = [sum(1 for q in range(n) if live_t[q][kv]) for kv in range(n)]
-    deg_q = [sum(1 for kv in range(n) if live_t[q][kv]) for q in range(n)]
-    delta = max(deg_kv + deg_q + [0])
-    seen = {}
-    owner = {}
-    for u, (items, st) in enumerate(zip(unit_items, steps)):
-        if len(items) != len(st):
-            return "steps do not match items"
-        if any(b <= a for a, b in zip(st, st[1:])):
-            return "steps not increasing within a unit"
-        for (kv, q), s in zip(items, st):
-            if not (0 <= kv < n and 0 <= q < n) or not live_t[q][kv]:
-                return "dead or out-of-range pair"
-            if (kv, q) in seen:
-                return "pair twice"
-            if not 0 <= s < delta:
-                return "step out of range"
-            if owner.setdefault(kv, u) != u:
-                return "KV tile in two units"
-            seen[(kv, q)] = s
-    if len(seen) != sum(deg_q):
-        return "live pair missing"
-    for q in range(n):
-        contrib = sorted((seen[(kv, q)], kv) for kv in range(n) if live_t[q][kv])
-        if len({s for s, _ in contrib}) != len(contrib):
-            return "two units on one block at one step"
-        for r, (_, kv) in enumerate(contrib):
-            if rank[q][kv] != r:
-                return "dQ order is not by step"
-        for kv in range(n):
-            if not live_t[q][kv] and rank[q][kv] is not None:
-                return "rank for a dead pair"
-        if dynamic:
-            for (_, kv0), (_, kv1) in zip(contrib, contrib[1:]):
-                if owner[kv0] > owner[kv1]:
-                    return "a wait points to a later unit under a work counter"
-    return ""

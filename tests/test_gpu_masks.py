@@ -170,3 +170,56 @@ def test_mask_that_hides_everything(sched):
     torch.cuda.synchronize()
     for t in outs:
         assert torch.all(t.float() == 0)
+
+
+def _bf16_rne(x32):
+    u = x32.view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+@pytest.mark.parametrize("block,causal", [(BLOCK8, True), (DEAD8, False)])
+def test_timed_shift_order_replay(block, causal):
+    """SHIFT on a block mask (the timed shift): dQ equals a host fp32 sum of
+    the kernel's own partials in the rank order of the tables the launch
+    ran (fetched for this device's co-resident count), bit for bit; head
+    by head, unit-major and jittered timing give the same bits."""
+    require_gpu()
+    B, H, N, d = 1, 16, 1024, 128
+    log(f"timed shift replay causal={causal} block={block.shape}")
+    bs = N // block.shape[0]
+    kw = dict(block_mask=block, block_size=bs)
+    dev, _ = device_inputs(B, H, N, d, "bf16", 6300)
+    o, lse = D.attn_fwd(dev["q"], dev["k"], dev["v"], causal=causal, **kw)
+    delta = D.attn_bwd_preprocess(o, dev["do"])
+    t = D.mask_schedule_tables(B, H, N, d, "bf16", causal, "shift", slots=0, **kw)
+    assert t["slots_per_head"] >= 1 and not t["static"]
+    n = t["n"]
+    tile = N // n
+    partials = torch.zeros((B * H, n, N, d), dtype=torch.float32, device="cuda")
+    ws = D.alloc_workspace(dev["q"], causal, "shift", **kw)
+    dq, _, _ = D.attn_bwd(dev["q"], dev["k"], dev["v"], dev["do"], lse, delta, schedule="shift",
+                          causal=causal, workspace=ws, debug={"partials": partials}, **kw)
+    D.attn_bwd_status(ws)
+    part = partials.cpu().numpy()
+    rank = t["rank"]
+    acc = np.zeros((B * H, N, d), dtype=np.float32)
+    for qb in range(n):
+        rows = slice(qb * tile, (qb + 1) * tile)
+        for _, kv in sorted((rank[qb, kv], kv) for kv in range(n) if rank[qb, kv] >= 0):
+            acc[:, rows] = acc[:, rows] + part[:, kv, rows]
+    want = _bf16_rne((acc * np.float32(1.0 / np.sqrt(d))).astype(np.float32))
+    seen = (rank >= 0).any(axis=1)
+    for qb in range(n):
+        if not seen[qb]:
+            want[:, qb * tile:(qb + 1) * tile] = 0
+    got = dq.reshape(B * H, N, d).view(torch.int16).cpu().numpy().view(np.uint16)
+    assert np.array_equal(got, want)
+    ref = D.attn_bwd(dev["q"], dev["k"], dev["v"], dev["do"], lse, delta, schedule="shift",
+                     causal=causal, workspace=ws, **kw)
+    for dbg in ({"unit_order": 1}, {"unit_order": 2}, {"jitter_seed": 9},
+                {"placement": 1}):
+        out = D.attn_bwd(dev["q"], dev["k"], dev["v"], dev["do"], lse, delta, schedule="shift",
+                         causal=causal, workspace=ws, debug=dbg, **kw)
+        D.attn_bwd_status(ws)
+        for a, b in zip(ref, out):
+            assert torch.equal(a.view(torch.int16), b.view(torch.int16)), dbg

@@ -3,8 +3,9 @@
 The library's tables for sliding windows and block masks are checked
 against the oracle: tile liveness and partial flags from the element mask
 by brute force; NAIVE / DESCENDING / ATOMIC item lists and dQ orders
-exactly; SHIFT (a colouring, not unique) against the rules it must obey;
-the DAG prediction on the library's own tables against the oracle's DAG.
+exactly; SHIFT (the timed shift) exactly against the oracle's own timed
+shift and against the timing certificate; the DAG prediction on the
+library's own tables against the oracle's DAG.
 """
 import numpy as np
 import pytest
@@ -69,9 +70,14 @@ def test_masked_tables_against_oracle(case, schedule):
             assert f == part[q][kv], (kv, q)
     plain = window == 0 and block is None
     if schedule == "shift":
-        assert OS.check_step_schedule(live, t["units"], t["steps"],
-                                      [[None if r < 0 else int(r) for r in row]
-                                       for row in t["rank"]], dynamic=not t["static"]) == ""
+        n_units = sum(1 for kv in range(n) if any(live[q][kv] for q in range(n)))
+        ws = OS.timed_slots(256, 1, n_units)
+        assert t["slots_per_head"] == ws and not t["static"]
+        units, steps, rank, starts = OS.timed_shift(live, ws)
+        assert t["units"] == units and t["steps"] == steps
+        assert np.array_equal(t["rank"], np.array([[-1 if x is None else x for x in row]
+                                                   for row in rank]))
+        assert OS.check_timed_schedule(live, units, steps, rank, starts, ws) == ""
         return
     want_units = [u for u in OS.masked_units(schedule, live) if u]
     assert t["units"] == want_units
@@ -96,45 +102,49 @@ def test_covering_window_gives_the_plain_tables(causal, schedule):
             assert all(s == list(range(len(s))) for s in t["steps"])
 
 
-def test_causal_band_shift_runs_each_tile_in_query_order():
-    """A causal window of whole tiles: the colouring puts every KV tile's
-    pairs at consecutive steps in ascending Q order and gives each Q block
-    its contributors nearest-first, so in lockstep every hand-off is one
-    step (no stall)."""
-    N, w = 1024, 3 * T
-    t = D.mask_schedule_tables(1, 1, N, 64, "f32", True, "shift", window=w)
+def test_causal_band_shift_runs_each_tile_from_its_diagonal():
+    """A causal window of whole tiles: with a slot per unit every KV tile
+    starts on its diagonal block and walks up one block per step, so at
+    block q the contributors come nearest first (rank q - kv) and every
+    hand-off is one step."""
+    n, w = 16, 3 * T
+    t = D.mask_schedule_tables(1, 1, n * T, 64, "f32", True, "shift", window=w, slots=8 * n)
+    assert t["slots_per_head"] == n
     for items, steps in zip(t["units"], t["steps"]):
-        qs = [q for _, q in items]
-        assert qs == sorted(qs)
-    live, _ = OS.tile_liveness(A.Mask(causal=True, window=w), N // T, T)
-    # a KV tile waits only for the next one at each block: the units order
-    # (last tile first) so that a work counter can hand them out
-    assert not t["static"]
-    assert [items[0][0] for items in t["units"]] == list(range(N // T - 1, -1, -1))
-    assert OS.check_step_schedule(live, t["units"], t["steps"],
-                                  [[None if r < 0 else int(r) for r in row]
-                                   for row in t["rank"]], dynamic=True) == ""
+        kv = items[0][0]
+        assert [q for _, q in items] == list(range(kv, min(n, kv + 4)))
+        assert steps == list(range(len(items)))
+    for q in range(n):
+        for kv in range(n):
+            want = q - kv if 0 <= q - kv <= 3 else -1
+            assert t["rank"][q, kv] == want
 
 
-def test_step_checker_catches_broken_tables():
-    """The oracle's checker (CPU) rejects tables with planted mistakes."""
+def test_timed_checker_catches_broken_tables():
+    """The oracle's certificate checker rejects tables with planted
+    mistakes (steps clashing on a block, units out of start order, a dQ
+    order not by step, a missing unit, more units running than slots)."""
     n = 8
     live, _ = OS.tile_liveness(A.Mask(causal=True, window=3 * T), n, T)
-    t = D.mask_schedule_tables(1, 1, n * T, 64, "f32", True, "shift", window=3 * T)
-    rank = [[None if r < 0 else int(r) for r in row] for row in t["rank"]]
-    assert OS.check_step_schedule(live, t["units"], t["steps"], rank) == ""
-    bad_steps = [list(s) for s in t["steps"]]
-    bad_steps[1][0] = bad_steps[0][0] if t["units"][1][0][1] == t["units"][0][0][1] else -1
-    assert OS.check_step_schedule(live, t["units"], bad_steps, rank) != ""
-    # the same units handed out in the opposite order break the counter rule
-    assert OS.check_step_schedule(live, t["units"][::-1], t["steps"][::-1], rank,
-                                  dynamic=True) != ""
+    units, steps, rank, starts = OS.timed_shift(live, 3)
+    ok = lambda u, st, r, s0, k: OS.check_timed_schedule(live, u, st, r, s0, k)  # noqa: E731
+    assert ok(units, steps, rank, starts, 3) == ""
+    assert ok(units, steps, rank, starts, 2) != ""
+    # two units on one block at one step
+    bad = [list(x) for x in steps]
+    i = next(i for i in range(1, len(units)) if units[i][0][1] == units[0][1][1])
+    bad[i] = [steps[0][1] + k for k in range(len(bad[i]))]
+    assert ok(units, bad, rank, starts, 3) != ""
+    assert ok(units[::-1], steps[::-1], rank, starts[::-1], 3) != ""
+    late = list(starts)
+    late[1] = steps[1][0] + 1
+    assert ok(units, steps, rank, late, 3) != ""
     bad_rank = [list(r) for r in rank]
-    q = t["units"][2][0][1]
+    q = units[2][0][1]
     kvs = [kv for kv in range(n) if bad_rank[q][kv] is not None]
     bad_rank[q][kvs[0]], bad_rank[q][kvs[-1]] = bad_rank[q][kvs[-1]], bad_rank[q][kvs[0]]
-    assert OS.check_step_schedule(live, t["units"], t["steps"], bad_rank) != ""
-    assert OS.check_step_schedule(live, t["units"][:-1], t["steps"][:-1], rank) != ""
+    assert ok(units, steps, bad_rank, starts, 3) != ""
+    assert ok(units[:-1], steps[:-1], rank, starts[:-1], 3) != ""
 
 
 def test_oracle_tile_liveness_closed_forms():
@@ -161,15 +171,17 @@ def test_masked_predict_matches_oracle_dag(case, schedule):
     N, causal, window, block, bs = case
     n = N // T
     kw = _kw(window, block, bs)
-    t = D.mask_schedule_tables(1, 1, N, 64, "f32", causal, schedule, **kw)
+    heads, slots = 3, 5
+    # the tables a launch on `slots` workgroups runs for `heads` heads (the
+    # timed shift's slots per head depend on both)
+    t = D.mask_schedule_tables(1, heads, N, 64, "f32", causal, schedule, slots=slots, **kw)
     tables = {"units": t["units"],
               "rank": None if schedule == "atomic" else t["rank"].tolist(),
               "partial": {it for items, fl in zip(t["units"], t["partial"])
                           for it, f in zip(items, fl) if f},
               "static": t["static"]}
     cost = (1.0, 0.6, 0.2, 0.1)
-    heads = 3
-    slots = max(len(t["units"]), 5) if t["static"] else 5
+    assert not t["static"]
     for um in (False, True):
         got = D.mask_schedule_predict(1, heads, N, 64, "f32", causal, schedule, slots=slots,
                                       cost=cost, unit_major=um, **kw)
@@ -235,23 +247,31 @@ def test_unit_major_order_on_a_block_sparse_mask():
 
 
 def test_table_export_protocol():
-    """Two-call export: sizes first; arrays of other sizes are refused."""
+    """Two-call export: sizes first; arrays of other sizes are refused; a
+    negative workgroup count is refused."""
     import ctypes
     lib = D.load()
     desc = D._desc(1, 1, 512, 64, "f32", True, None, 100)
-    sizes = (ctypes.c_int32 * 4)()
-    assert lib.dash_attn_schedule_tables(ctypes.byref(desc), 2, sizes, None, None, None, None,
-                                         None, None) == 0
+    sizes = (ctypes.c_int32 * 5)()
+    assert lib.dash_attn_schedule_tables(ctypes.byref(desc), 2, 256, sizes, None, None, None,
+                                         None, None, None) == 0
     n, nu, ni = sizes[0], sizes[1], sizes[2]
-    assert n == 8 and nu == 8 and ni > 0
+    assert n == 8 and nu == 8 and ni > 0 and sizes[3] == 0 and sizes[4] == 0
     arr = lambda m: (ctypes.c_int32 * max(m, 1))()
-    bad = (ctypes.c_int32 * 4)(n, nu, ni + 1, 0)
-    assert lib.dash_attn_schedule_tables(ctypes.byref(desc), 2, bad, arr(nu + 1), arr(ni),
+    bad = (ctypes.c_int32 * 5)(n, nu, ni + 1, 0, 0)
+    assert lib.dash_attn_schedule_tables(ctypes.byref(desc), 2, 256, bad, arr(nu + 1), arr(ni),
                                          arr(ni), arr(ni), (ctypes.c_uint8 * ni)(),
                                          arr(n * n)) == 1
-    assert lib.dash_attn_schedule_tables(ctypes.byref(desc), 9, sizes, None, None, None, None,
-                                         None, None) == 1
-    assert lib.dash_attn_schedule_tables(None, 2, sizes, None, None, None, None, None, None) == 1
+    assert lib.dash_attn_schedule_tables(ctypes.byref(desc), 9, 256, sizes, None, None, None,
+                                         None, None, None) == 1
+    assert lib.dash_attn_schedule_tables(ctypes.byref(desc), 2, -1, sizes, None, None, None,
+                                         None, None, None) == 1
+    assert lib.dash_attn_schedule_tables(None, 2, 256, sizes, None, None, None, None, None,
+                                         None) == 1
+    # SHIFT on the window: a timed shift for min(256 / 8, 8) slots per head
+    assert lib.dash_attn_schedule_tables(ctypes.byref(desc), 3, 256, sizes, None, None, None,
+                                         None, None, None) == 0
+    assert sizes[3] == 0 and sizes[4] == 8
 
 
 def test_bench_dag_prediction_on_the_plain_workloads():
