@@ -193,9 +193,15 @@ __device__ __forceinline__ float max_halves(float x) {
   return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
 }
 
-// bf16 forward.  A workgroup owns NW x 64 query rows: NW waves x 64 rows
-// (two 32-query column tiles each), so every K / V fragment read from LDS
-// feeds two MFMAs.  Key and value tiles of 64 rows stay row-major in LDS (XOR
+// bf16 forward.  A workgroup owns NW x 32QN query rows: NW waves x QN
+// 32-query column tiles.  With QN = 2 every K / V fragment read from LDS
+// feeds two MFMAs and a wave needs more than half a SIMD's registers (one
+// wave per SIMD: its softmax leaves the matrix core idle); with QN = 1 and
+// 8 waves two waves share each SIMD at 256 registers, and one wave's
+// softmax runs beside the other's MFMAs, for twice the LDS reads per MFMA
+// (16K causal d = 128: 2.80 -> 2.46 ms; d = 64 and the block-mask kernel
+// lose, 6.0 -> 7.1 and 0.85 -> 0.94 ms, and keep QN = 2).  Key and value
+// tiles of 64 rows stay row-major in LDS (XOR
 // swizzled, double buffered) and are prefetched into registers one tile
 // ahead, so a tile costs one workgroup barrier.  S^T = K Q^T with K from LDS
 // (A operand) and Q^T in registers (B); O^T = V^T P^T with V^T from the
@@ -204,10 +210,9 @@ __device__ __forceinline__ float max_halves(float x) {
 // on lanes: row statistics need one exchange between the lane halves and
 // the rescale of O^T is a per-lane scalar.  Waves skip key tiles their rows
 // cannot see and mask elements only on tiles that cross a mask bound.
-template <int D, bool MASKED, int NW>
-__global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdArgs a) {
+template <int D, bool MASKED, int NW, int QN>
+__global__ void __launch_bounds__(NW * 64, QN == 1 ? 8 / NW : 1) fwd_bf16_kernel(FwdArgs a) {
   constexpr int NT = NW * 64;
-  constexpr int QN = 2;                    // 32-query tiles per wave
   constexpr int WR = 32 * QN;              // query rows per wave
   constexpr int BM = NW * WR;              // query rows per workgroup
   constexpr int BN = 64;                   // keys per tile
@@ -496,7 +501,8 @@ __global__ void __launch_bounds__(NW * 64, 1) fwd_bf16_kernel(FwdArgs a) {
 
 // Block masks: workgroups of one query tile (2 waves, 128 rows), so the
 // waves of a workgroup see the same live key tiles; two such workgroups
-// share a compute unit.  Otherwise 4 waves, 256 rows.
+// share a compute unit.  Otherwise 256 rows: d = 128 in 8 waves of 32 rows
+// (two per SIMD), d = 64 in 4 waves of 64.
 template <int D>
 static hipError_t go_fwd_bf16(bool masked, const FwdArgs& a, hipStream_t s) {
   const int nw = a.live ? 2 : 4;
@@ -504,9 +510,10 @@ static hipError_t go_fwd_bf16(bool masked, const FwdArgs& a, hipStream_t s) {
   const long blocks = (long)((a.N + 64 * nw - 1) / (64 * nw)) * a.BH;
   if (blocks > 0x7fffffffL) return hipErrorInvalidValue;
   dim3 grid((unsigned)blocks);
-  if (a.live) hipLaunchKernelGGL((fwd_bf16_kernel<D, true, 2>), grid, dim3(128), 0, s, a);
-  else if (masked) hipLaunchKernelGGL((fwd_bf16_kernel<D, true, 4>), grid, dim3(256), 0, s, a);
-  else hipLaunchKernelGGL((fwd_bf16_kernel<D, false, 4>), grid, dim3(256), 0, s, a);
+  constexpr int NW = D == 128 ? 8 : 4, QN = D == 128 ? 1 : 2;
+  if (a.live) hipLaunchKernelGGL((fwd_bf16_kernel<D, true, 2, 2>), grid, dim3(128), 0, s, a);
+  else if (masked) hipLaunchKernelGGL((fwd_bf16_kernel<D, true, NW, QN>), grid, dim3(NW * 64), 0, s, a);
+  else hipLaunchKernelGGL((fwd_bf16_kernel<D, false, NW, QN>), grid, dim3(NW * 64), 0, s, a);
   return hipGetLastError();
 }
 
