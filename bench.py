@@ -396,6 +396,8 @@ def main():
             "source": "phase timer of the backward kernel (one instrumented launch): counter "
                       "check + ordered add + hand-off phases"},
         "dag_vs_measured": dag_vs_measured(results),
+        "dag_fit": dag_fit(D, w, causal, mkw, results,
+                           torch.cuda.get_device_properties(0).multi_processor_count),
         "schedules": {s: {k: (round(v, 4) if isinstance(v, float) else v) for k, v in r.items()}
                       for s, r in results.items()},
     }
@@ -422,6 +424,29 @@ def main():
     del dev, o, lse, delta, dq, dk, dv, ws
     torch.cuda.synchronize()
     torch.cuda.empty_cache()
+
+
+def dag_fit(D, w, causal, mkw, results, coresident):
+    """The DAG model's costs fitted to this run's measured kernel times of
+    naive, descending and shift (dash_schedule_fit_costs: what
+    dash_attn_bwd_calibrate would record for "auto"), the fit's relative RMS
+    error, the kernel time of one cost unit, and the fitted model's
+    makespans of naive and descending relative to shift's."""
+    ms = [results.get(s, {}).get("kernel_ms") for s in ("naive", "descending", "shift")]
+    if sum(m is not None for m in ms) < 2:
+        return None
+    try:
+        cost, res, unit = D.fit_costs(w.B, w.H, w.N, w.d, w.dtype, causal, slots=coresident,
+                                      ms=ms, **mkw)
+        pred = {s: D.bwd_predict(w.B, w.H, w.N, w.d, w.dtype, causal, s, slots=coresident,
+                                 cost=cost, **mkw)[0][0]
+                for s in ("naive", "descending", "shift")}
+    except D.DashError:
+        return None
+    return {"cost": [round(c, 4) for c in cost], "rel_rms_error": round(res, 4),
+            "ms_per_cost_unit": round(unit, 6),
+            "fitted_vs_shift": {s: round(pred[s] / pred["shift"], 3)
+                                for s in ("naive", "descending")}}
 
 
 def dag_vs_measured(results):

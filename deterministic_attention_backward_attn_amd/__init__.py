@@ -278,6 +278,61 @@ def attn_bwd_tune(q, k, v, do, lse, delta, *, causal=False, scale=None, reps=3, 
     return names[choice.value], {"naive": t[0], "descending": t[1], "shift": t[2]}
 
 
+def attn_bwd_calibrate(q, k, v, do, lse, delta, *, causal=False, scale=None, reps=3,
+                       workspace=None, out=None, stream=None, window=0, block_mask=None,
+                       block_size=0):
+    """Time naive, descending and shift on these inputs, fit the DAG model's
+    costs to the times and record them for "auto" launches of this dtype
+    and head dim on this device (see dash_attn_bwd_calibrate).  Returns
+    (costs (c_full, c_diag, r, h), relative RMS residual, {name: ms})."""
+    torch = _torch()
+    lib = load()
+    _same_shape(q, k, v, do)
+    desc = _desc_from(q, causal, scale, window, block_mask, block_size)
+    if workspace is None:
+        workspace = alloc_workspace(q, causal, "auto", window=window, block_mask=block_mask,
+                                    block_size=block_size)
+    if out is None:
+        out = (torch.empty_like(q), torch.empty_like(k), torch.empty_like(v))
+    dq, dk, dv = out
+    _same_shape(q, dq, dk, dv)
+    c = (ctypes.c_double * 4)()
+    res = ctypes.c_double(0.0)
+    t = (ctypes.c_float * 3)()
+    check(lib.dash_attn_bwd_calibrate(ctypes.byref(desc), _ptr(q), _ptr(k), _ptr(v), _ptr(do),
+                                      _ptr(lse), _ptr(delta), _ptr(dq), _ptr(dk), _ptr(dv),
+                                      _ptr(workspace),
+                                      ctypes.c_size_t(workspace.numel() * workspace.element_size()),
+                                      int(reps), c, ctypes.byref(res), t, _stream(stream)),
+          "dash_attn_bwd_calibrate")
+    return tuple(c), res.value, {"naive": t[0], "descending": t[1], "shift": t[2]}
+
+
+def bwd_costs(B, H, N, d, dtype="bf16", causal=False):
+    """The costs "auto" uses on the current device for this dtype and d."""
+    lib = load()
+    desc = _desc(B, H, N, d, dtype, causal)
+    c = (ctypes.c_double * 4)()
+    check(lib.dash_attn_bwd_costs(ctypes.byref(desc), c), "dash_attn_bwd_costs")
+    return tuple(c)
+
+
+def fit_costs(B, H, N, d, dtype="bf16", causal=False, *, slots, ms, window=0, block_mask=None,
+              block_size=0):
+    """Host-only fit of the DAG model's costs to measured times ms =
+    (naive, descending, shift) (None or <= 0: not measured).  Returns
+    (costs, relative RMS residual, time of one cost unit)."""
+    lib = load()
+    desc = _desc(B, H, N, d, dtype, causal, None, window, block_mask, block_size)
+    m = (ctypes.c_double * 3)(*[float("nan") if x is None else float(x) for x in ms])
+    c = (ctypes.c_double * 4)()
+    res = ctypes.c_double(0.0)
+    unit = ctypes.c_double(0.0)
+    check(lib.dash_schedule_fit_costs(ctypes.byref(desc), int(slots), m, c, ctypes.byref(res),
+                                      ctypes.byref(unit)), "dash_schedule_fit_costs")
+    return tuple(c), res.value, unit.value
+
+
 def attn_bwd_status(workspace, stream=None):
     """Synchronizes the stream and raises DashError if an ordered add timed out."""
     lib = load()

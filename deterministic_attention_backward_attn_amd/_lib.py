@@ -89,6 +89,11 @@ _SIGS = {
     "dash_attn_bwd_tune": (ctypes.c_int, [ctypes.POINTER(Desc), _vp, _vp, _vp, _vp, _vp, _vp,
                                           _vp, _vp, _vp, _vp, ctypes.c_size_t, _i32,
                                           ctypes.POINTER(ctypes.c_int), _vp, _vp]),
+    "dash_attn_bwd_calibrate": (ctypes.c_int, [ctypes.POINTER(Desc), _vp, _vp, _vp, _vp, _vp,
+                                               _vp, _vp, _vp, _vp, _vp, ctypes.c_size_t, _i32,
+                                               _dp, _dp, _vp, _vp]),
+    "dash_attn_bwd_costs": (ctypes.c_int, [ctypes.c_void_p, _dp]),
+    "dash_schedule_fit_costs": (ctypes.c_int, [ctypes.c_void_p, _i32, _dp, _dp, _dp, _dp]),
     "dash_schedule_choose": (ctypes.c_int, [_i32, _i32, _i32, _i32, _dp,
                                             ctypes.POINTER(ctypes.c_int), _dp]),
     "dash_dag_longest_path": (ctypes.c_int, [_i32, _dp, _i32, _ip, _ip, _dp, _dp, _dp]),

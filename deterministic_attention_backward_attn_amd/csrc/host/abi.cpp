@@ -3,6 +3,7 @@
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
+#include <array>
 #include <cmath>
 #include <cstring>
 #include <map>
@@ -36,6 +37,7 @@ bool sched_ok_run(int s) { return sched_ok(s) || s == DASH_SCHED_AUTO; }
 // the hand-off latency each about 5 % of an item (measured on MI355X at
 // d = 128: ~24k cycles per item, ~1.2k per hand-off).
 constexpr double kDefaultCost[4] = {1.0, 0.5, 0.05, 0.05};
+typedef std::array<double, 4> Cost;
 
 constexpr int kXcds = 8;  // XCDs of an MI355X: the workgroup groups of the placement
 
@@ -101,6 +103,24 @@ bool launch_predict(const Tables& t, long heads, int maxco, const double cost[4]
   return true;
 }
 
+// The tables a launch on `slots` co-resident workgroups runs for `heads`
+// heads (the timed shift of a special mask depends on both).  Returns false
+// where the schedule is undefined.
+bool launch_tables(const dash::TileMask& m, Sched s, long heads, int slots, Tables& t) {
+  int ws = 1;
+  if (!m.plain) {
+    int live_kv = 0;
+    for (int kv = 0; kv < m.n; ++kv)
+      for (int q = 0; q < m.n; ++q)
+        if (m.live[(size_t)q * m.n + kv]) {
+          ++live_kv;
+          break;
+        }
+    ws = dash::timed_slots(slots, heads, live_kv);
+  }
+  return dash::build_tables(m, s, t, ws);
+}
+
 // The ordered schedule with the smallest predicted makespan; see
 // dash_schedule_choose.  placement: predict each schedule as the launch
 // places it (launch_predict, on `slots` co-resident workgroups); otherwise
@@ -110,18 +130,10 @@ dash_status choose_schedule(const dash::TileMask& m, int heads, int slots, const
   const Sched cand[3] = {Sched::Naive, Sched::Descending, Sched::Shift};
   double best = 0.0;
   int best_i = -1;
-  int live_kv = 0;
-  for (int kv = 0; kv < m.n; ++kv)
-    for (int q = 0; q < m.n; ++q)
-      if (m.live[(size_t)q * m.n + kv]) {
-        ++live_kv;
-        break;
-      }
   for (int i = 0; i < 3; ++i) {
     pred[i] = NAN;
     Tables t;
-    const int ws = m.plain ? 1 : dash::timed_slots(slots, heads, live_kv);
-    if (!dash::build_tables(m, cand[i], t, ws)) continue;
+    if (!launch_tables(m, cand[i], heads, slots, t)) continue;
     if (dash::validate_tables(t)[0] != '\0') return DASH_ERR_SCHEDULE_INVALID;
     if (t.needs_static() && t.units() > slots) continue;
     dash::DagResult r;
@@ -145,6 +157,66 @@ dash_status choose_schedule(const dash::TileMask& m, int heads, int slots, const
   }
   if (best_i < 0) return DASH_ERR_UNSUPPORTED;
   *choice = cand[best_i];
+  return DASH_OK;
+}
+
+// The DAG model's costs fitted to measured kernel times ms[3] of NAIVE,
+// DESCENDING and SHIFT (NaN or <= 0: not measured; at least two needed), each
+// predicted as a launch on `slots` co-resident workgroups places it: c_full
+// = 1, c_diag, r and h on a grid, and per candidate the time of one item
+// unit that best matches all measured times (least squares on relative
+// error).  The candidate with the smallest relative RMS error wins; ties go
+// to the one nearest the defaults.  Host only.
+dash_status fit_costs(const dash::TileMask& m, long heads, int slots, const double ms[3],
+                      Cost& out, double* residual, double* item_ms) {
+  const Sched cand[3] = {Sched::Naive, Sched::Descending, Sched::Shift};
+  std::vector<Tables> tabs;
+  std::vector<double> meas;
+  for (int i = 0; i < 3; ++i) {
+    if (!(ms[i] > 0.0) || !std::isfinite(ms[i])) continue;
+    Tables t;
+    if (!launch_tables(m, cand[i], heads, slots, t)) return DASH_ERR_UNSUPPORTED;
+    if (dash::validate_tables(t)[0] != '\0') return DASH_ERR_SCHEDULE_INVALID;
+    if (t.needs_static() && t.units() > slots) return DASH_ERR_UNSUPPORTED;
+    if (t.units() == 0) return DASH_ERR_UNSUPPORTED;  // nothing runs: nothing to fit
+    tabs.push_back(std::move(t));
+    meas.push_back(ms[i]);
+  }
+  if (tabs.size() < 2) return DASH_ERR_INVALID_ARG;
+  const double cd_grid[] = {0.5, 0.75, 1.0};
+  const double rh_grid[] = {0.0, 0.025, 0.05, 0.1, 0.2, 0.3};
+  double best = INFINITY, best_dist = INFINITY, best_scale = 0.0;
+  for (double cd : cd_grid)
+    for (double r : rh_grid)
+      for (double h : rh_grid) {
+        const double cost[4] = {1.0, cd, r, h};
+        // a_i = predicted / measured; scale t minimises sum (t a_i - 1)^2
+        double sa = 0.0, saa = 0.0;
+        std::vector<double> a;
+        for (size_t i = 0; i < tabs.size(); ++i) {
+          LaunchPrediction lp;
+          if (!launch_predict(tabs[i], heads, slots, cost, true, lp)) return DASH_ERR_SCHEDULE_INVALID;
+          a.push_back(lp.r.makespan / meas[i]);
+          sa += a.back();
+          saa += a.back() * a.back();
+        }
+        if (!(saa > 0.0)) continue;
+        const double tsc = sa / saa;
+        double err = 0.0;
+        for (double ai : a) err += (tsc * ai - 1.0) * (tsc * ai - 1.0);
+        err = std::sqrt(err / (double)a.size());
+        const double dist = std::fabs(cd - kDefaultCost[1]) + std::fabs(r - kDefaultCost[2]) +
+                            std::fabs(h - kDefaultCost[3]);
+        if (err < best - 1e-12 || (err <= best + 1e-12 && dist < best_dist)) {
+          best = err;
+          best_dist = dist;
+          best_scale = tsc;
+          out = Cost{1.0, cd, r, h};
+        }
+      }
+  if (!std::isfinite(best)) return DASH_ERR_UNSUPPORTED;
+  if (residual) *residual = best;
+  if (item_ms) *item_ms = best_scale;  // measured time per cost unit
   return DASH_OK;
 }
 
@@ -281,9 +353,16 @@ uint64_t g_clock = 0;
 std::map<MaskKey, MaskEntry> g_masks;                     // special masks only
 std::map<std::tuple<MaskKey, int, int>, TabEntry> g_tables;  // (mask, sched, timed slots)
 std::map<std::tuple<int, int, int, int, int>, int> g_coresident;  // (device, dtype, d, masked, ordered)
-std::map<std::tuple<MaskKey, int, int>, Sched> g_auto;  // (mask, heads, slots) -> choice
-// (mask, sched, heads, slots, grouped) -> unit-major
-std::map<std::tuple<MaskKey, int, long, int, int>, bool> g_order;
+// AUTO: the problem on a device (device, dtype, d, mask, heads, co-resident
+// workgroups); its model pick is cached per cost vector, a pick that
+// dash_attn_bwd_tune measured takes precedence
+typedef std::tuple<int, int, int, MaskKey, int, int> AutoKey;
+std::map<std::pair<AutoKey, Cost>, Sched> g_auto;
+std::map<AutoKey, Sched> g_tuned;
+// costs AUTO uses per (device, dtype, d) once dash_attn_bwd_calibrate fitted them
+std::map<std::tuple<int, int, int>, Cost> g_costs;
+// (mask, sched, heads, slots, grouped, costs) -> unit-major
+std::map<std::tuple<MaskKey, int, long, int, int, Cost>, bool> g_order;
 
 template <typename E>
 void release_entry(E& e, void* buf) {
@@ -460,13 +539,13 @@ dash_status pinned_blob(const MaskKey& key, TabEntry* e) {
 // order only changes which heads run side by side (masks whose units
 // differ much in length gain most).  Caller holds g_mu.
 bool unit_major_for(const MaskKey& mkey, const Tables& t, Sched s, long heads, int maxco,
-                    bool grouped) {
+                    bool grouped, const Cost& cost) {
   if (t.needs_static() || !t.ordered() || t.units() == 0) return false;
-  const auto key = std::make_tuple(mkey, (int)s, heads, maxco, (int)grouped);
+  const auto key = std::make_tuple(mkey, (int)s, heads, maxco, (int)grouped, cost);
   auto it = g_order.find(key);
   if (it != g_order.end()) return it->second;
   LaunchPrediction lp;
-  const bool pick = launch_predict(t, heads, maxco, kDefaultCost, grouped, lp) && lp.unit_major;
+  const bool pick = launch_predict(t, heads, maxco, cost.data(), grouped, lp) && lp.unit_major;
   g_order[key] = pick;
   return pick;
 }
@@ -494,15 +573,35 @@ bool any_partial(const MaskKey& key) {
   return mask_entry(key)->host.any_partial();
 }
 
-// DASH_SCHED_AUTO -> the predicted best ordered schedule for this problem
-// on `maxco` co-resident workgroups (cached per shape); others unchanged.
-// Caller holds g_mu.
-dash_status resolve_schedule(dash_schedule schedule, const MaskKey& mkey, long heads, int maxco,
-                             Sched* s) {
+// The costs AUTO uses for (device, dtype, d): fitted by
+// dash_attn_bwd_calibrate, else the defaults.  Caller holds g_mu.
+Cost costs_for(int dev, int dtype, int d) {
+  auto it = g_costs.find(std::make_tuple(dev, dtype, d));
+  return it != g_costs.end() ? it->second
+                             : Cost{kDefaultCost[0], kDefaultCost[1], kDefaultCost[2], kDefaultCost[3]};
+}
+
+AutoKey auto_key(int dev, const dash_attn_desc* d, const MaskKey& mkey, int maxco) {
+  const int h = (int)std::min<long>((long)d->B * d->H, 1L << 30);
+  return AutoKey(dev, (int)d->dtype, d->d, mkey, h, maxco);
+}
+
+// DASH_SCHED_AUTO -> the schedule dash_attn_bwd_tune measured fastest for
+// this problem on this device, else the ordered schedule the model predicts
+// fastest on `maxco` co-resident workgroups with the device's costs
+// (cached); other schedules unchanged.  Caller holds g_mu.
+dash_status resolve_schedule(dash_schedule schedule, int dev, const dash_attn_desc* desc,
+                             const MaskKey& mkey, int maxco, Sched* s) {
   *s = (Sched)schedule;
   if (schedule != DASH_SCHED_AUTO) return DASH_OK;
-  const int h = (int)std::min<long>(heads, 1L << 30);
-  const auto key = std::make_tuple(mkey, h, maxco);
+  const AutoKey akey = auto_key(dev, desc, mkey, maxco);
+  auto tt = g_tuned.find(akey);
+  if (tt != g_tuned.end()) {
+    *s = tt->second;
+    return DASH_OK;
+  }
+  const Cost cost = costs_for(dev, desc->dtype, desc->d);
+  const auto key = std::make_pair(akey, cost);
   auto it = g_auto.find(key);
   if (it != g_auto.end()) {
     *s = it->second;
@@ -512,7 +611,7 @@ dash_status resolve_schedule(dash_schedule schedule, const MaskKey& mkey, long h
   if (plain_key(mkey) && mkey.n + 1 > dash::kMaxUnitItems) return DASH_ERR_UNSUPPORTED;
   const dash::TileMask m = plain_key(mkey) ? dash::plain_mask(mkey.n, mkey.causal != 0)
                                            : mask_entry(mkey)->host;
-  const dash_status st = choose_schedule(m, h, maxco, kDefaultCost, s, pred, true);
+  const dash_status st = choose_schedule(m, std::get<4>(akey), maxco, cost.data(), s, pred, true);
   if (st != DASH_OK) return st;
   g_auto[key] = *s;
   return DASH_OK;
@@ -582,7 +681,7 @@ dash_status run_bwd(const dash_attn_desc* desc, dash_schedule schedule, const vo
   }
   lock.lock();
   Sched s = Sched::Naive;
-  st = resolve_schedule(schedule, mkey, heads, maxco, &s);
+  st = resolve_schedule(schedule, dev, desc, mkey, maxco, &s);
   if (st != DASH_OK) return st;
   TabEntry* tb = nullptr;
   st = tab_entry(mkey, s, plan_slots(mkey, s, heads, maxco), &tb);
@@ -609,8 +708,10 @@ dash_status run_bwd(const dash_attn_desc* desc, dash_schedule schedule, const vo
   }
   int xcd_mode = ordered ? 1 : 0;
   if (dbg && dbg->placement) xcd_mode = dbg->placement - 1;
-  int unit_major = dynamic ? (unit_major_for(mkey, host, s, heads, maxco, xcd_mode != 0) ? 1 : 0)
-                           : 0;
+  int unit_major =
+      dynamic ? (unit_major_for(mkey, host, s, heads, maxco, xcd_mode != 0,
+                                costs_for(dev, desc->dtype, desc->d)) ? 1 : 0)
+              : 0;
   if (dbg && dbg->unit_order && dynamic) unit_major = dbg->unit_order - 1;
   int n_dead_q = 0, n_dead_kv = 0;
   if (!plain) {
@@ -717,6 +818,85 @@ dash_status run_bwd(const dash_attn_desc* desc, dash_schedule schedule, const vo
       return DASH_ERR_HIP;
   }
   return DASH_OK;
+}
+
+// Runs NAIVE, DESCENDING and SHIFT (those that can run) once untimed and
+// `reps` times timed on the caller's buffers, exactly as dash_attn_bwd
+// would, and returns the mean time per launch (NaN where a schedule cannot
+// run), reading the status word after each candidate (every launch clears
+// it).  Blocking.  Reports the device and its co-resident workgroups.
+dash_status time_schedules(const dash_attn_desc* desc, const void* q, const void* k,
+                           const void* v, const void* dout, const float* lse, const float* delta,
+                           void* dq, void* dk, void* dv, void* workspace, size_t workspace_bytes,
+                           int32_t reps, void* stream, float t[3], int* dev_out, int* maxco_out) {
+  dash_status st = check_desc(desc);
+  if (st != DASH_OK) return st;
+  if (reps < 1 || reps > 1000) return DASH_ERR_INVALID_ARG;
+  if (!q || !k || !v || !dout || !lse || !delta || !dq || !dk || !dv || !workspace)
+    return DASH_ERR_INVALID_ARG;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return DASH_ERR_HIP;
+  const MaskKey mkey = mask_key(desc);
+  bool masked = false;
+  {
+    std::lock_guard<std::mutex> lock(g_mu);
+    masked = any_partial(mkey);
+  }
+  int maxco = 0;
+  st = get_coresident(dev, desc->dtype, desc->d, masked, true, &maxco);
+  if (st != DASH_OK) return st;
+  *dev_out = dev;
+  *maxco_out = maxco;
+  hipStream_t strm = (hipStream_t)stream;
+  hipEvent_t ev[2];
+  if (hipEventCreate(&ev[0]) != hipSuccess) return DASH_ERR_HIP;
+  if (hipEventCreate(&ev[1]) != hipSuccess) {
+    (void)hipEventDestroy(ev[0]);
+    return DASH_ERR_HIP;
+  }
+  const dash_schedule cand[3] = {DASH_SCHED_NAIVE, DASH_SCHED_DESCENDING, DASH_SCHED_SHIFT};
+  const long bh = (long)desc->B * desc->H;
+  for (int i = 0; i < 3 && st == DASH_OK; ++i) {
+    t[i] = NAN;
+    {
+      std::lock_guard<std::mutex> lock(g_mu);
+      TabEntry* tb = nullptr;
+      if (tab_entry(mkey, (Sched)cand[i], plan_slots(mkey, (Sched)cand[i], bh, maxco), &tb) !=
+          DASH_OK)
+        continue;
+      if (tb->host.needs_static() && tb->host.units() > maxco) continue;
+    }
+    // one untimed launch, then `reps` timed ones
+    st = run_bwd(desc, cand[i], q, k, v, dout, lse, delta, dq, dk, dv, workspace, workspace_bytes,
+                 nullptr, stream);
+    if (st == DASH_ERR_UNSUPPORTED) {  // e.g. a unit longer than the kernel's work list
+      st = DASH_OK;
+      continue;
+    }
+    if (st != DASH_OK) break;
+    if (hipEventRecord(ev[0], strm) != hipSuccess) st = DASH_ERR_HIP;
+    for (int r = 0; r < reps && st == DASH_OK; ++r)
+      st = run_bwd(desc, cand[i], q, k, v, dout, lse, delta, dq, dk, dv, workspace,
+                   workspace_bytes, nullptr, stream);
+    if (st != DASH_OK) break;
+    if (hipEventRecord(ev[1], strm) != hipSuccess || hipEventSynchronize(ev[1]) != hipSuccess) {
+      st = DASH_ERR_HIP;
+      break;
+    }
+    // every launch clears the status word, so a time-out of this
+    // candidate is visible only now, before the next one runs
+    st = read_status(workspace);
+    if (st != DASH_OK) break;
+    float ms = 0.f;
+    if (hipEventElapsedTime(&ms, ev[0], ev[1]) != hipSuccess) {
+      st = DASH_ERR_HIP;
+      break;
+    }
+    t[i] = ms / reps;
+  }
+  (void)hipEventDestroy(ev[0]);
+  (void)hipEventDestroy(ev[1]);
+  return st;
 }
 
 // Host entry points that build tables can run out of host memory; nothing
@@ -911,83 +1091,88 @@ dash_status dash_attn_bwd_tune(const dash_attn_desc* desc, const void* q, const 
                               size_t workspace_bytes, int32_t reps, dash_schedule* choice,
                               float* times_ms, void* stream) {
   return guarded([&]() -> dash_status {
-    dash_status st = check_desc(desc);
-    if (st != DASH_OK) return st;
-    if (reps < 1 || reps > 1000 || !choice) return DASH_ERR_INVALID_ARG;
-    if (!q || !k || !v || !dout || !lse || !delta || !dq || !dk || !dv || !workspace)
-      return DASH_ERR_INVALID_ARG;
-    int dev = 0;
-    if (hipGetDevice(&dev) != hipSuccess) return DASH_ERR_HIP;
-    const MaskKey mkey = mask_key(desc);
-    bool masked = false;
-    {
-      std::lock_guard<std::mutex> lock(g_mu);
-      masked = any_partial(mkey);
-    }
-    int maxco = 0;
-    st = get_coresident(dev, desc->dtype, desc->d, masked, true, &maxco);
-    if (st != DASH_OK) return st;
-    hipStream_t strm = (hipStream_t)stream;
-    hipEvent_t ev[2];
-    if (hipEventCreate(&ev[0]) != hipSuccess) return DASH_ERR_HIP;
-    if (hipEventCreate(&ev[1]) != hipSuccess) {
-      (void)hipEventDestroy(ev[0]);
-      return DASH_ERR_HIP;
-    }
-    const dash_schedule cand[3] = {DASH_SCHED_NAIVE, DASH_SCHED_DESCENDING, DASH_SCHED_SHIFT};
+    if (!choice) return DASH_ERR_INVALID_ARG;
     float t[3];
-    int best = -1;
-    for (int i = 0; i < 3 && st == DASH_OK; ++i) {
-      t[i] = NAN;
-      {
-        std::lock_guard<std::mutex> lock(g_mu);
-        TabEntry* tb = nullptr;
-        const long bh = (long)desc->B * desc->H;
-        if (tab_entry(mkey, (Sched)cand[i], plan_slots(mkey, (Sched)cand[i], bh, maxco), &tb) !=
-            DASH_OK)
-          continue;
-        if (tb->host.needs_static() && tb->host.units() > maxco) continue;
-      }
-      // one untimed launch, then `reps` timed ones
-      st = run_bwd(desc, cand[i], q, k, v, dout, lse, delta, dq, dk, dv, workspace,
-                   workspace_bytes, nullptr, stream);
-      if (st == DASH_ERR_UNSUPPORTED) {  // e.g. a unit longer than the kernel's work list
-        st = DASH_OK;
-        continue;
-      }
-      if (st != DASH_OK) break;
-      if (hipEventRecord(ev[0], strm) != hipSuccess) st = DASH_ERR_HIP;
-      for (int r = 0; r < reps && st == DASH_OK; ++r)
-        st = run_bwd(desc, cand[i], q, k, v, dout, lse, delta, dq, dk, dv, workspace,
-                     workspace_bytes, nullptr, stream);
-      if (st != DASH_OK) break;
-      if (hipEventRecord(ev[1], strm) != hipSuccess || hipEventSynchronize(ev[1]) != hipSuccess) {
-        st = DASH_ERR_HIP;
-        break;
-      }
-      // every launch clears the status word, so a time-out of this
-      // candidate is visible only now, before the next one runs
-      st = read_status(workspace);
-      if (st != DASH_OK) break;
-      float ms = 0.f;
-      if (hipEventElapsedTime(&ms, ev[0], ev[1]) != hipSuccess) {
-        st = DASH_ERR_HIP;
-        break;
-      }
-      t[i] = ms / reps;
-      if (best < 0 || t[i] < t[best]) best = i;
-    }
-    (void)hipEventDestroy(ev[0]);
-    (void)hipEventDestroy(ev[1]);
+    int dev = 0, maxco = 0;
+    const dash_status st = time_schedules(desc, q, k, v, dout, lse, delta, dq, dk, dv, workspace,
+                                          workspace_bytes, reps, stream, t, &dev, &maxco);
     if (st != DASH_OK) return st;
+    const dash_schedule cand[3] = {DASH_SCHED_NAIVE, DASH_SCHED_DESCENDING, DASH_SCHED_SHIFT};
+    int best = -1;
+    for (int i = 0; i < 3; ++i)
+      if (std::isfinite(t[i]) && (best < 0 || t[i] < t[best])) best = i;
     if (best < 0) return DASH_ERR_UNSUPPORTED;
     {
-      const int h = (int)std::min<long>((long)desc->B * desc->H, 1L << 30);
       std::lock_guard<std::mutex> lock(g_mu);
-      g_auto[std::make_tuple(mkey, h, maxco)] = (Sched)cand[best];
+      g_tuned[auto_key(dev, desc, mask_key(desc), maxco)] = (Sched)cand[best];
     }
     *choice = cand[best];
     if (times_ms) std::memcpy(times_ms, t, sizeof(t));
+    return DASH_OK;
+  });
+}
+
+dash_status dash_attn_bwd_calibrate(const dash_attn_desc* desc, const void* q, const void* k,
+                                    const void* v, const void* dout, const float* lse,
+                                    const float* delta, void* dq, void* dk, void* dv,
+                                    void* workspace, size_t workspace_bytes, int32_t reps,
+                                    double cost_out[4], double* residual, float* times_ms,
+                                    void* stream) {
+  return guarded([&]() -> dash_status {
+    float t[3];
+    int dev = 0, maxco = 0;
+    dash_status st = time_schedules(desc, q, k, v, dout, lse, delta, dq, dk, dv, workspace,
+                                    workspace_bytes, reps, stream, t, &dev, &maxco);
+    if (st != DASH_OK) return st;
+    if (times_ms) std::memcpy(times_ms, t, sizeof(t));
+    const double ms[3] = {t[0], t[1], t[2]};
+    const MaskKey mkey = mask_key(desc);
+    Cost c;
+    double res = 0.0;
+    {
+      std::lock_guard<std::mutex> lock(g_mu);
+      const dash::TileMask m = plain_key(mkey) ? dash::plain_mask(mkey.n, mkey.causal != 0)
+                                               : mask_entry(mkey)->host;
+      st = fit_costs(m, (long)desc->B * desc->H, maxco, ms, c, &res, nullptr);
+      if (st != DASH_OK) return st;
+      g_costs[std::make_tuple(dev, (int)desc->dtype, desc->d)] = c;
+    }
+    if (cost_out) std::memcpy(cost_out, c.data(), sizeof(double) * 4);
+    if (residual) *residual = res;
+    return DASH_OK;
+  });
+}
+
+dash_status dash_attn_bwd_costs(const dash_attn_desc* desc, double cost_out[4]) {
+  dash_status st = check_desc(desc);
+  if (st != DASH_OK) return st;
+  if (!cost_out) return DASH_ERR_INVALID_ARG;
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return DASH_ERR_HIP;
+  std::lock_guard<std::mutex> lock(g_mu);
+  const Cost c = costs_for(dev, desc->dtype, desc->d);
+  std::memcpy(cost_out, c.data(), sizeof(double) * 4);
+  return DASH_OK;
+}
+
+dash_status dash_schedule_fit_costs(const dash_attn_desc* desc, int32_t slots,
+                                    const double ms[3], double cost_out[4], double* residual,
+                                    double* item_ms) {
+  dash_status st = check_desc(desc);
+  if (st != DASH_OK) return st;
+  if (slots < 1 || !ms || !cost_out) return DASH_ERR_INVALID_ARG;
+  for (int i = 0; i < 3; ++i)
+    if (ms[i] < 0.0) return DASH_ERR_INVALID_ARG;
+  return guarded([&]() -> dash_status {
+    const MaskKey mkey = mask_key(desc);
+    if (plain_key(mkey) && mkey.n + 1 > dash::kMaxUnitItems) return DASH_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_mu);
+    const dash::TileMask m = plain_key(mkey) ? dash::plain_mask(mkey.n, mkey.causal != 0)
+                                             : mask_entry(mkey)->host;
+    Cost c;
+    const dash_status st2 = fit_costs(m, (long)desc->B * desc->H, slots, ms, c, residual, item_ms);
+    if (st2 != DASH_OK) return st2;
+    std::memcpy(cost_out, c.data(), sizeof(double) * 4);
     return DASH_OK;
   });
 }
@@ -1121,7 +1306,7 @@ dash_status dash_attn_bwd_resolve_schedule(const dash_attn_desc* desc, dash_sche
     if (st2 != DASH_OK) return st2;
     Sched s = Sched::Naive;
     std::lock_guard<std::mutex> lock(g_mu);
-    st2 = resolve_schedule(schedule, mkey, (long)desc->B * desc->H, maxco, &s);
+    st2 = resolve_schedule(schedule, dev, desc, mkey, maxco, &s);
     if (st2 != DASH_OK) return st2;
     *resolved = (dash_schedule)s;
     return DASH_OK;

@@ -28,9 +28,12 @@
  *               KV tiles w and n-1-w in one workgroup, two phases.  dQ order
  *               = the step at which each tile reaches the block.
  *   ATOMIC      NAIVE's traversal, unordered fp32 atomic adds.
- *   AUTO        the ordered schedule the DAG model predicts fastest under
- *               the launch's placement (dash_attn_bwd_predict), or the one
- *               dash_attn_bwd_tune measured fastest for the shape.
+ *   AUTO        the one dash_attn_bwd_tune measured fastest for the
+ *               problem on this device, else the ordered schedule the DAG
+ *               model predicts fastest under the launch's placement
+ *               (dash_attn_bwd_predict) with the device's costs: the
+ *               defaults, or those dash_attn_bwd_calibrate fitted to
+ *               measured kernel times.
  * With a window or block mask the same rules run over the tile pairs that
  * hold a visible key; SHIFT becomes a timed shift (see
  * dash_attn_schedule_tables), the summary's limitations naming
@@ -429,6 +432,53 @@ dash_status dash_attn_bwd_tune(const dash_attn_desc* desc, const void* q, const 
                               const float* delta, void* dq, void* dk, void* dv, void* workspace,
                               size_t workspace_bytes, int32_t reps, dash_schedule* choice,
                               float* times_ms, void* stream);
+
+/*
+ * Calibration of the DAG model from measured kernel times (the summary's
+ * limitations list runtime-profiling-based adaptive selection as future
+ * work).  Times NAIVE, DESCENDING and SHIFT as dash_attn_bwd_tune does
+ * (blocking, on the caller's buffers, which are overwritten), fits the
+ * model's costs to those times with dash_schedule_fit_costs, and records
+ * them for this device, dtype and head dimension: later DASH_SCHED_AUTO
+ * launches of any shape with that dtype and head dimension predict with
+ * them (a shape dash_attn_bwd_tune measured keeps its measured pick).
+ * cost_out[4] (may be NULL) receives the fitted {c_full, c_diag, r, h},
+ * *residual (may be NULL) the fit's relative RMS error, times_ms[3] (may be
+ * NULL) the measured times as dash_attn_bwd_tune reports them.  Errors as
+ * dash_attn_bwd_tune; DASH_ERR_UNSUPPORTED if fewer than two schedules can
+ * run or nothing runs (every pair masked).
+ */
+dash_status dash_attn_bwd_calibrate(const dash_attn_desc* desc, const void* q, const void* k,
+                                    const void* v, const void* dout, const float* lse,
+                                    const float* delta, void* dq, void* dk, void* dv,
+                                    void* workspace, size_t workspace_bytes, int32_t reps,
+                                    double cost_out[4], double* residual, float* times_ms,
+                                    void* stream);
+
+/*
+ * The costs DASH_SCHED_AUTO uses on the current device for the
+ * descriptor's dtype and head dimension: {1, 0.5, 0.05, 0.05} until
+ * dash_attn_bwd_calibrate fitted others.  Queries the current device only.
+ */
+dash_status dash_attn_bwd_costs(const dash_attn_desc* desc, double cost_out[4]);
+
+/*
+ * The fit itself, host only: the DAG model's costs for which the predicted
+ * makespans of NAIVE, DESCENDING and SHIFT (dash_attn_bwd_predict's, on
+ * `slots` co-resident workgroups) are proportional to measured times
+ * ms[3] (<= 0 or NaN: not measured; at least two).  c_full = 1; c_diag in
+ * {0.5, 0.75, 1}, r and h in {0, 0.025, 0.05, 0.1, 0.2, 0.3}; per
+ * candidate, the time of one cost unit that best matches all measured
+ * times in relative least squares; the candidate with the smallest
+ * relative RMS error wins (ties: nearest the defaults).  cost_out[4]
+ * receives the costs, *residual (may be NULL) the relative RMS error,
+ * *item_ms (may be NULL) the fitted time of one cost unit in the units of
+ * ms.  DASH_ERR_INVALID_ARG with fewer than two measured times or a
+ * negative one; DASH_ERR_UNSUPPORTED if a measured schedule cannot run.
+ */
+dash_status dash_schedule_fit_costs(const dash_attn_desc* desc, int32_t slots,
+                                    const double ms[3], double cost_out[4], double* residual,
+                                    double* item_ms);
 
 /*
  * The schedule dash_attn_bwd runs for `schedule` on the current device:
