@@ -8,7 +8,9 @@
 // length.  Here: P persistent workgroup slots, item nodes C (c_full or
 // c_diag) -> R (r), unit chains, slot chains, and order edges R -> R with
 // hand-off latency h.  Units go to slots by the kernel's own policy:
-// dynamic (first free slot, head-major order) or static head-aligned rounds.
+// dynamic (first free slot, head-major or unit-major order; an add may wait
+// for a unit handed out later, as in the timed shift) or static
+// head-aligned rounds.
 #pragma once
 
 #include <cstdint>

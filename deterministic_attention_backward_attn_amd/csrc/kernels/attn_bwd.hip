@@ -30,10 +30,12 @@
 // unordered fp32 atomics instead (non-deterministic reference).
 //
 // The workgroups form a persistent grid: each takes units (work lists from
-// the schedule tables) either from a device work counter in increasing
-// order (schedules whose waits point only to earlier units) or in
-// head-aligned rounds (shift, whose waits point to other units of the same
-// head, all of which are then resident).
+// the schedule tables) either from a work counter in increasing order
+// (schedules whose waits point only to earlier units, and the timed shift of
+// window and block masks, whose waits point only to units that reached the
+// block earlier in its simulated timing, run on enough workgroups) or in
+// head-aligned rounds (the pages' shift, whose waits point to other units of
+// the same head, all of which are then resident).
 //
 // Operand placement (see common.hpp for the MFMA layouts):
 //   S and dP are computed as (Q-rows x KV-cols): the accumulators hold KV on

@@ -368,8 +368,10 @@ dash_status dash_schedule_tables(int32_t n, int32_t causal, dash_schedule schedu
  * partial item (causal diagonal, window or block edge), the dQ add, and
  * the hand-off latency between consecutive contributors.
  * out[4] = {makespan, total_wait, max_slot_idle, lower_bound}.  Host only.
- * SHIFT needs slots >= units per head (else DASH_ERR_UNSUPPORTED), and so
- * does a graph of 2^31 nodes or more (2 per item and head).
+ * The pages' SHIFT (full and causal masks) needs slots >= units per head
+ * (else DASH_ERR_UNSUPPORTED), and so does a graph of 2^31 nodes or more (2
+ * per item and head); a window or block mask's SHIFT is the timed shift a
+ * launch on `slots` co-resident workgroups runs.
  */
 dash_status dash_schedule_predict(const dash_attn_desc* desc, dash_schedule schedule,
                                   int32_t slots, const double cost[4], double out[4]);
