@@ -199,9 +199,9 @@ def main():
                          "runs the measured fastest instead of the DAG model's pick")
     ap.add_argument("--no-fwd", action="store_true",
                     help="skip the forward and forward+backward timings")
-    ap.add_argument("--layout", choices=["default", "pairs"], default="default",
-                    help="backward kernel layout: default, or wave pairs (bf16 d=128; "
-                         "bit-identical results)")
+    ap.add_argument("--layout", choices=["default", "pairs", "pipe"], default="default",
+                    help="backward kernel layout: default, wave pairs or the two-stage "
+                         "pipeline (bf16 d=128; bit-identical results)")
     ap.add_argument("--phases", action="store_true",
                     help="one extra launch per schedule with the phase timer: share of wave "
                          "cycles per phase of a Q sub-tile")
@@ -258,7 +258,9 @@ def main():
     ws = D.alloc_workspace(dev["q"], causal, "naive")
     flops = w.flops_bwd(causal)
 
-    lay = {"layout": 1} if args.layout == "pairs" else {}
+    lay = {"pairs": {"layout": 1}, "pipe": {"layout": 2}}.get(args.layout, {})
+    # the pipeline layout has no phase timer
+    no_phases = args.layout == "pipe"
 
     def step(sched, events=None):
         D.attn_bwd_preprocess(o, dev["do"], out=delta)
@@ -300,7 +302,7 @@ def main():
         if sched not in ("atomic", "auto") and not args.no_wait_stats:
             results[sched].update(order_wait(D, dev, lse, delta, sched, causal, ws, (dq, dk, dv),
                                              mkw, lay))
-        if args.phases:
+        if args.phases and not no_phases:
             results[sched]["phases"] = phase_shares(D, dev, lse, delta, sched, causal, ws,
                                                     (dq, dk, dv), mkw, lay)
             print(f"[bench] {sched:10s} phases " + "  ".join(
@@ -321,7 +323,7 @@ def main():
     # the ordered add's share of the primary schedule's wave cycles (one
     # extra untimed launch with the phase timer, unless --phases ran it)
     add_share = None
-    if ran != "atomic" and not args.no_wait_stats:
+    if ran != "atomic" and not args.no_wait_stats and not no_phases:
         ph = results[primary].get("phases") or phase_shares(D, dev, lse, delta, ran, causal, ws,
                                                             (dq, dk, dv), mkw, lay)
         if not lay:
@@ -381,7 +383,8 @@ def main():
                    + (" block " + json.dumps(w.block_spec) if w.block_spec else ""),
                    "schedule": primary if ran == primary else f"{primary} ({ran})",
                    "parallelism": "single GPU",
-                   **({"layout": "wave pairs"} if lay else {})},
+                   **({"layout": {"pairs": "wave pairs", "pipe": "two-stage pipeline"}[args.layout]}
+                      if lay else {})},
         "pct_peak": round(100.0 * prim["tflops"] / peak, 2),
         "det_nondet_ratio": ({s: round(r["tflops"] / results["atomic"]["tflops"], 4)
                               for s, r in results.items() if s != "atomic"}

@@ -26,6 +26,7 @@ SOURCES = [
     "host/dag.cpp",
     "kernels/attn_bwd.hip",
     "kernels/attn_bwd_pair.hip",
+    "kernels/attn_bwd_pipe.hip",
     "kernels/attn_fwd.hip",
     "kernels/elementwise.hip",
     "kernels/noalloc.hip",

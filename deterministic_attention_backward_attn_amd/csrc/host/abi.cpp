@@ -651,8 +651,10 @@ dash_status run_bwd(const dash_attn_desc* desc, dash_schedule schedule, const vo
   if (dbg && (dbg->placement < 0 || dbg->placement > 3)) return DASH_ERR_INVALID_ARG;
   if (dbg && (dbg->unit_order < 0 || dbg->unit_order > 2)) return DASH_ERR_INVALID_ARG;
   const bool pairs = dbg && dbg->layout == 1;
-  if (dbg && (dbg->layout < 0 || dbg->layout > 1)) return DASH_ERR_INVALID_ARG;
-  if (pairs && (desc->dtype != 1 || desc->d != 128)) return DASH_ERR_UNSUPPORTED;
+  const bool pipe = dbg && dbg->layout == 2;
+  if (dbg && (dbg->layout < 0 || dbg->layout > 2)) return DASH_ERR_INVALID_ARG;
+  if ((pairs || pipe) && (desc->dtype != 1 || desc->d != 128)) return DASH_ERR_UNSUPPORTED;
+  if (pipe && dbg->phase_stats) return DASH_ERR_UNSUPPORTED;
 
   const MaskKey mkey = mask_key(desc);
   const bool plain = plain_key(mkey);
@@ -673,10 +675,12 @@ dash_status run_bwd(const dash_attn_desc* desc, dash_schedule schedule, const vo
   int maxco = 0;
   st = get_coresident(dev, desc->dtype, desc->d, masked, ordered, &maxco);
   if (st != DASH_OK) return st;
-  if (pairs) {
-    // the wave-pair kernel must fit as many workgroups (the same schedule)
+  if (pairs || pipe) {
+    // the 8-wave kernels must fit as many workgroups (the same schedule)
     int pb = 0;
-    if (dash::bwd_pair_max_coresident(masked, ordered, &pb) != hipSuccess) return DASH_ERR_HIP;
+    if ((pairs ? dash::bwd_pair_max_coresident(masked, ordered, &pb)
+               : dash::bwd_pipe_max_coresident(masked, ordered, &pb)) != hipSuccess)
+      return DASH_ERR_HIP;
     if (pb < maxco) return DASH_ERR_UNSUPPORTED;
   }
   lock.lock();
@@ -791,7 +795,8 @@ dash_status run_bwd(const dash_attn_desc* desc, dash_schedule schedule, const vo
   hipEvent_t ev0 = dbg ? (hipEvent_t)dbg->kernel_events[0] : nullptr;
   hipEvent_t ev1 = dbg ? (hipEvent_t)dbg->kernel_events[1] : nullptr;
   if (ev0 && hipEventRecord(ev0, strm) != hipSuccess) return DASH_ERR_HIP;
-  if (U > 0 && (pairs ? dash::launch_bwd_pair(masked, ordered, a, grid, strm)
+  if (U > 0 && (pairs  ? dash::launch_bwd_pair(masked, ordered, a, grid, strm)
+                : pipe ? dash::launch_bwd_pipe(masked, ordered, a, grid, strm)
                        : dash::launch_bwd(desc->dtype, desc->d, masked, ordered, a, grid, strm)) !=
                    hipSuccess)
     return DASH_ERR_HIP;

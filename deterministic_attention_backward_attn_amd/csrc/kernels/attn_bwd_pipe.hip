@@ -1,0 +1,581 @@
+// Deterministic attention backward, two-stage pipeline (bf16, d = 128).
+//
+// The same method, schedules, tables and ordered dQ hand-off as the
+// one-wave-per-slice kernel (attn_bwd.hip), with the work of each 32-row KV
+// slice split into two stages that run one Q sub-tile apart on the two
+// waves sharing a SIMD (8 waves per workgroup, at most 256 registers each):
+//
+//   stage A (waves 0..3: K and V fragments and the dV accumulator in
+//     registers), sub-tile t: S = Q K^T, dP = dO V^T, P = exp(s S - LSE)
+//     (masked), dS = P (dP - delta), dV += P^T dO; dS^T to LDS; stages the
+//     next Q/dO sub-tile and prefetches the one after;
+//   stage B (waves 4..7: the dK accumulator and K^T fragments), sub-tile
+//     t - 1: dK += dS^T Q, dQ_part^T = K^T dS^T, and the ordered add of
+//     dQ_part into the fp32 accumulator.
+//
+// Every input of stage B was written by stage A one period earlier, so one
+// workgroup barrier per period is the only synchronisation: within a period
+// the two waves of a SIMD never wait for each other, and the matrix core
+// runs B's products while A computes its exponentials.  The ordered add's
+// memory round trips (counter read, accumulator read, store, hand-off) are
+// issued only by the B waves, whose vector-memory queue holds nothing else,
+// so a wait for one of them never waits for a prefetch.  Results are
+// bit-identical to the other layouts: every product, exponential and add is
+// computed with the same operands in the same order.
+//
+// The ordered add (explainer section 1, a fixed accumulation order for dQ)
+// keeps the other kernel's protocol: wave B of slice s owns dQ columns
+// [32s, 32s+32) in every workgroup and hands off to slice s of the next
+// contributor through the sub-tile's counter for s.  Its timing per period
+// (B processing sub-tile g):
+//   1. the counter value read one period earlier shows whether this
+//      contributor's turn has come; if it has not, the previous add is
+//      released first (a wave never waits while holding an unreleased add)
+//      and the counter is polled;
+//   2. the accumulator reads for sub-tile g are issued (out of range, reading
+//      nothing, for the first contributor), then the counter read for g + 1;
+//   3. after the dK product the previous add is released: a wait until its
+//      stores completed (exactly the five operations issued after them may
+//      still be outstanding), then the counter store;
+//   4. after the dQ product the partial is transposed through this wave's LDS
+//      area, added to the accumulator values and stored (the last contributor
+//      writes the scaled dQ instead).
+#include "common.hpp"
+#include "launch.hpp"
+#include "placement.hpp"
+
+namespace dash {
+
+template <bool MASKED, bool ORDERED, bool DEBUG>
+__global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
+  using T = bf16_t;
+  using E = Elt<T>;
+  using frag = typename E::frag;
+  constexpr int D = 128, BC = 128, BR = 32;
+  constexpr int NW = 4;                 // KV slices (counter layout: one per slice)
+  constexpr int NT = 512;
+  constexpr int NA = 256;               // threads of stage A
+  constexpr int RHO = BC / BR;          // Q sub-tiles per Q block
+  constexpr int KPL = 8, KSTEP = 16, VEC = 8;
+  constexpr int DK = D / KSTEP;         // 8 MFMA steps over d
+  constexpr int KK = BC / KSTEP;        // 8 MFMA steps over the KV tile
+  constexpr int NTD = D / 32;           // 4 column tiles over d
+  constexpr int LQ = D;
+  constexpr int LS = BR + 4;            // row stride of sdSt ([kv][q])
+  constexpr int CPT = BR * D / VEC / NA;  // 16-byte chunks per A thread per tensor (2)
+  static_assert(CPT * VEC * NA == BR * D, "sub-tile load must split evenly");
+
+  // Q / dO / LSE / delta sub-tiles: sub-tile g in buffer g % 3 (A reads t,
+  // B reads t - 1, A stages t + 1).  dS^T of sub-tile g in buffer g % 2
+  // (A writes t, B reads t - 1).
+  __shared__ __align__(16) T sQ[3][BR * LQ];
+  __shared__ __align__(16) T sdO[3][BR * LQ];
+  __shared__ __align__(16) T sdSt[2][BC * LS];
+  __shared__ __align__(16) T sK[BC * LQ];
+  __shared__ __align__(16) float sLSE[3][BR];
+  __shared__ __align__(16) float sDel[3][BR];
+  __shared__ int2 sItems[kMaxUnitItems];
+  constexpr int LR = 32;
+  __shared__ __align__(16) float sRow[ORDERED ? NW : 1][ORDERED ? 32 * LR : 4];
+  __shared__ int sUnit;
+  __shared__ int sPlace[5];
+  const auto qix = [](int r, int c) { return r * LQ + (((c >> 3) ^ swz<D>(r)) << 3) + (c & 7); };
+  const auto six = [](int r, int c) { return r * LS + c; };
+  const auto rix = [](int r, int c) { return r * LR + (((c >> 2) ^ ((r >> 1) & 7)) << 2) + (c & 3); };
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wv = tid >> 6;              // 0..7
+  const bool isA = wv < NW;
+  const int w = wv & 3;                 // KV slice
+  const int l32 = lane & 31;
+  const int hh = lane >> 5;
+  const int j16 = lane & 15;
+  const int gcol = 16 * ((lane >> 4) & 1);
+  const int N = a.N;
+  const int n_sub = N / BR;
+  uint32_t* status = a.header;
+  const uint32_t spin_limit = a.spin_limit;
+  const int kvl = 32 * w + l32;         // this lane's KV row within the tile
+
+  uint64_t st_wait = 0, st_waits = 0, st_spun = 0;
+  const uint64_t st_t0 = (DEBUG && a.wait_stats) ? (uint64_t)clock64() : 0;
+
+  const Placement pl = place_units(a, tid, sPlace);
+  const int U = a.units_per_head;
+  const int grp = pl.grp, n_grp = pl.n_grp, li = pl.li, W = pl.W;
+  const bool grouped = pl.grouped;
+  const int BH = a.total_units / U;
+  const int hg = (BH - grp + n_grp - 1) / n_grp;
+  const int n_units = hg * U;
+  const int stride_static = grouped ? (W / U) * U : a.p_eff;
+  uint32_t* work_counter = grouped ? &a.header[20 + grp] : &a.header[1];
+  const int unit0 = (a.dynamic == 0 && li >= stride_static) ? n_units : li;
+
+  // One copy of the unit loop per stage, so that each stage's registers are
+  // allocated for its own values only; both copies pass the same barriers
+  // in the same order.  Stage B has one copy per accumulator cache policy
+  // (XL: the head's contributors share one XCD's L2), so that its memory
+  // operations are not split over branches.
+  auto run = [&](auto stage_tag, auto xl_tag) {
+    constexpr bool IS_A = decltype(stage_tag)::value;
+    constexpr bool XL = decltype(xl_tag)::value;
+    constexpr int POL = XL ? kXcdCoherent : kCoherent;
+    int unit = unit0;
+    while (unit < n_units) {
+      const int hq = a.unit_major ? unit % hg : unit / U;
+      const int lu = a.unit_major ? unit / hg : unit - hq * U;
+      const int head = grp + n_grp * hq;
+      const size_t hoff = (size_t)head * N * D;
+      const T* Qg = reinterpret_cast<const T*>(a.q) + hoff;
+      const T* dOg = reinterpret_cast<const T*>(a.dout) + hoff;
+      const int it0 = a.unit_off[lu];
+      const int n_items = a.unit_off[lu + 1] - it0;  // <= kMaxUnitItems (checked by the host)
+      const int n_steps = n_items * RHO;
+
+      // every wave has finished the previous unit (its last reads of the
+      // work list included) before the list is overwritten
+      __syncthreads();
+      for (int i = tid; i < n_items; i += NT) sItems[i] = a.items[it0 + i];
+      __syncthreads();
+
+      auto qtile_of = [&](int g) { return (sItems[g / RHO].x >> 16) * RHO + (g % RHO); };
+
+      if constexpr (IS_A) {
+        // ---------------------------------------------------------- stage A
+        const T* Kg = reinterpret_cast<const T*>(a.k) + hoff;
+        const T* Vg = reinterpret_cast<const T*>(a.v) + hoff;
+        frag Kreg[DK], Vreg[DK];
+        f32x16 accdV[NTD];
+        int a_kv = -1;
+        auto flush_dv = [&]() {
+          T* dVg = reinterpret_cast<T*>(a.dv) + hoff;
+#pragma unroll
+          for (int nt = 0; nt < NTD; ++nt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              dVg[(uint32_t)((a_kv * BC + 32 * w + crow(r, hh)) * D + nt * 32 + l32)] =
+                  E::from_f32(accdV[nt][r]);
+        };
+        __syncthreads();  // sub-tile 0 staged by stage B
+
+        for (int t = 0; t <= n_steps; ++t) {
+          if (t < n_steps) {
+            const int b3 = t % 3;
+            const int b2 = t & 1;
+            const int2 itm = sItems[t / RHO];
+            const int kv = itm.x & 0xFFFF;
+            const int qblk = itm.x >> 16;
+            const int rsub = t % RHO;
+            if (kv != a_kv) {
+              // new KV tile: dV of the previous one is complete; K and V
+              // fragments (row 32w + l32, columns 16ks + 8h ..), and K
+              // row-major into LDS for stage B's K^T (stage B read the
+              // previous tile's K one period after it was written, at least
+              // three periods ago)
+              if (a_kv >= 0) flush_dv();
+              a_kv = kv;
+#pragma unroll
+              for (int nt = 0; nt < NTD; ++nt) accdV[nt] = zero16();
+              const int kv0 = kv * BC;
+#pragma unroll
+              for (int ks = 0; ks < DK; ++ks) {
+                const uint32_t off = (uint32_t)((kv0 + kvl) * D + ks * KSTEP + hh * KPL);
+                Kreg[ks] = load_frag(Kg + off);
+                Vreg[ks] = load_frag(Vg + off);
+              }
+#pragma unroll
+              for (int ks = 0; ks < DK; ++ks)
+                *reinterpret_cast<uint4*>(&sK[qix(kvl, ks * KSTEP + hh * KPL)]) =
+                    __builtin_bit_cast(uint4, Kreg[ks]);
+            }
+            const T* cQ = sQ[b3];
+            const T* cdO = sdO[b3];
+            f32x16 accS = zero16(), accP = zero16();
+            // in two halves over d: all A fragments of a half are read
+            // first, then its MFMAs (the scheduling barriers keep them apart)
+#pragma unroll
+            for (int h2 = 0; h2 < 2; ++h2) {
+              frag qa[DK / 2], oa[DK / 2];
+#pragma unroll
+              for (int k2 = 0; k2 < DK / 2; ++k2) {
+                const int off = qix(l32, (h2 * DK / 2 + k2) * KSTEP + hh * KPL);
+                qa[k2] = load_frag(&cQ[off]);
+                oa[k2] = load_frag(&cdO[off]);
+              }
+              __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+              for (int k2 = 0; k2 < DK / 2; ++k2) {
+                accS = E::mma(qa[k2], Kreg[h2 * DK / 2 + k2], accS);
+                accP = E::mma(oa[k2], Vreg[h2 * DK / 2 + k2], accP);
+              }
+              __builtin_amdgcn_sched_barrier(0);
+            }
+
+            // P and dS (pairs flagged partial hide the elements outside
+            // lo <= i - j <= hi), packed once to bf16 (hardware RNE
+            // conversion); P stays in registers for dV, dS^T goes to LDS
+            // [kv][q] for stage B
+            const bool emask = MASKED && ((itm.y >> 29) & 1);
+            const int mbase = (qblk - kv) * BC + rsub * BR - kvl;  // i - j = mbase + row
+            T* cdSt = sdSt[b2];
+            uint32_t pw[8];
+#pragma unroll
+            for (int gq = 0; gq < 4; ++gq) {
+              const int qb = 8 * gq + 4 * hh;  // 4 consecutive Q rows
+              const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sLSE[b3][qb]);
+              const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sDel[b3][qb]);
+              float p[4], ds[4];
+#pragma unroll
+              for (int e = 0; e < 4; ++e)
+                p[e] = __builtin_amdgcn_exp2f(accS[4 * gq + e] * a.scale_log2 - l4[e]);
+              if (emask) {
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                  const int dd = mbase + qb + e;
+                  if (dd < a.mask_lo || dd > a.mask_hi) p[e] = 0.f;
+                }
+              }
+#pragma unroll
+              for (int e = 0; e < 4; ++e) ds[e] = p[e] * (accP[4 * gq + e] - d4[e]);
+              pw[2 * gq] = pack2_bf16(p[0], p[1]);
+              pw[2 * gq + 1] = pack2_bf16(p[2], p[3]);
+              *reinterpret_cast<uint2*>(&cdSt[kvl * LS + qb]) =
+                  make_uint2(pack2_bf16(ds[0], ds[1]), pack2_bf16(ds[2], ds[3]));
+            }
+            // dV += P^T dO (contraction over the sub-tile's Q rows; K slots:
+            // Q rows r0 + {0..3}, r0 + 8 + {0..3})
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) {
+              const int r0 = 16 * cc + 4 * hh;
+              const frag pa = __builtin_bit_cast(
+                  bf16x8, make_uint4(pw[4 * cc], pw[4 * cc + 1], pw[4 * cc + 2], pw[4 * cc + 3]));
+#pragma unroll
+              for (int nt = 0; nt < NTD; ++nt) {
+                const frag bo = tr_frag(cdO, qix, r0, r0 + 8, nt * 32 + gcol, j16);
+                accdV[nt] = E::mma(pa, bo, accdV[nt]);
+              }
+            }
+          }
+          __syncthreads();  // end of period t
+        }
+        if (a_kv >= 0) flush_dv();
+      } else {
+        // ---------------------------------------------------------- stage B
+        float* dqa = a.dq_accum + hoff;
+        T* dqo = reinterpret_cast<T*>(a.dq) + hoff;
+        uint32_t* cnt_h = a.counters + (size_t)head * n_sub * NW;
+        const int tb = tid - NA;  // thread index within stage B
+        const float* lse_g = a.lse + (size_t)head * N;
+        const float* del_g = a.delta + (size_t)head * N;
+        u32x4 pq[CPT], pdo[CPT];
+        float pstat = 0.f;
+        auto fetch = [&](int g) {
+          g = g < n_steps ? g : n_steps - 1;  // past the end: a harmless re-read
+          const int q0 = qtile_of(g) * BR;
+#pragma unroll
+          for (int i = 0; i < CPT; ++i) {
+            const int c = tb + i * NA;
+            const int row = c / (D / VEC);
+            const int col = (c % (D / VEC)) * VEC;
+            const uint32_t off = (uint32_t)((q0 + row) * D + col);
+            pq[i] = *reinterpret_cast<const u32x4*>(Qg + off);
+            pdo[i] = *reinterpret_cast<const u32x4*>(dOg + off);
+          }
+          // one load into one register for every lane (lanes past 2*BR
+          // re-read a valid element and discard it)
+          const float* src = tb < BR ? lse_g + (q0 + tb)
+                                     : del_g + (q0 + (tb < 2 * BR ? tb - BR : 0));
+          pstat = *src;
+        };
+        auto stage = [&](int buf) {
+#pragma unroll
+          for (int i = 0; i < CPT; ++i) {
+            const int c = tb + i * NA;
+            const int row = c / (D / VEC);
+            const int col = (c % (D / VEC)) * VEC;
+            *reinterpret_cast<u32x4*>(&sQ[buf][qix(row, col)]) = pq[i];
+            *reinterpret_cast<u32x4*>(&sdO[buf][qix(row, col)]) = pdo[i];
+          }
+          if (tb < BR) sLSE[buf][tb] = pstat * kLog2e;
+          else if (tb < 2 * BR) sDel[buf][tb - BR] = pstat;
+        };
+
+        frag KT[KK];
+        f32x16 accdK[NTD];
+        int b_kv = -1;
+        auto flush_dk = [&]() {
+          T* dKg = reinterpret_cast<T*>(a.dk) + hoff;
+#pragma unroll
+          for (int nt = 0; nt < NTD; ++nt)
+#pragma unroll
+            for (int r = 0; r < 16; ++r)
+              dKg[(uint32_t)((b_kv * BC + 32 * w + crow(r, hh)) * D + nt * 32 + l32)] =
+                  E::from_f32(accdK[nt][r] * a.scale);
+        };
+        auto counter = [&](int qtile) { return cnt_h + (size_t)qtile * NW + w; };
+        const __amdgpu_buffer_rsrc_t dq_rs = make_rsrc(dqa, (uint32_t)(N * D * 4));
+        const __amdgpu_buffer_rsrc_t dqo_rs = make_rsrc(dqo, (uint32_t)(N * D * 2));
+        const __amdgpu_buffer_rsrc_t cnt_rs = make_rsrc(cnt_h, (uint32_t)(n_sub * NW * 4));
+        // row-major chunk k (0..3) of this slice's 32 x 32 output tile:
+        // 4 consecutive columns of one row; 8 lanes cover a 128-byte row
+        auto chunk_off = [&](int q0, int k) {
+          return (uint32_t)((q0 + (lane >> 3) + 8 * k) * D + w * 32 + 4 * (lane & 7));
+        };
+        auto dq_off = [&](int q0, int r) {
+          if constexpr (ORDERED) return (uint32_t)((q0 + l32) * D + w * 32 + crow(r, hh));
+          else return (uint32_t)((q0 + crow(r, hh)) * D + w * 32 + l32);
+        };
+        f32x4 lv[4];
+        auto load_acc = [&](int qtile, bool live) {
+          // L2-coherent loads may hit this CU's L1: drop every line read
+          // before other workgroups updated it, right before the reads
+          if constexpr (XL) l1_invalidate();
+#pragma unroll
+          for (int k = 0; k < 4; ++k) {
+            const uint32_t off = live ? 4 * chunk_off(qtile * BR, k) : kOutOfRange;
+            lv[k] = coherent_load4<POL>(dq_rs, off);
+          }
+        };
+        auto wait_turn = [&](int qtile, int rank) {
+          if (lane == 0) {
+            const uint64_t t0 = (DEBUG && a.wait_stats) ? (uint64_t)clock64() : 0;
+            if (DEBUG && a.jitter_seed != 0u) {
+              const uint32_t nap =
+                  hash32(a.jitter_seed ^ (uint32_t)(head * 7919 + qtile * 131 + b_kv * 17 + w)) & 31u;
+              for (uint32_t i = 0; i < nap; ++i) __builtin_amdgcn_s_sleep(8);
+            }
+            const bool poisoned = DEBUG && a.poison_q >= 0 && head == 0 && qtile == a.poison_q && rank == 0;
+            uint32_t polls = 0;
+            if (poisoned) polls = wait_counter(counter(qtile), 0xFFFFFFFFu, status, spin_limit);
+            else if (rank > 0) polls = wait_counter(counter(qtile), (uint32_t)rank, status, spin_limit);
+            if (DEBUG && a.wait_stats) {
+              st_wait += (uint64_t)clock64() - t0;
+              st_spun += polls > 0 ? 1u : 0u;
+            }
+          }
+          __builtin_amdgcn_wave_barrier();
+        };
+        bool rel_pending = false;
+        int rel_qtile = 0, rel_rank = 0;
+        // Hand-off of the previous add: wait until its stores completed,
+        // then store the next rank into its counter (device-coherent, every
+        // lane the same word).  In the loop it is issued every period (to an
+        // offset out of the counters' range, storing nothing, when no add is
+        // pending) after at least the prefetch (5 operations), the
+        // accumulator reads (4) and the counter read (1) of the period, of
+        // which the last five may stay outstanding.
+        auto release_drain = [&]() {
+          if (rel_pending) {
+            __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+            advance_counter(counter(rel_qtile), (uint32_t)rel_rank + 1u);
+            rel_pending = false;
+          }
+        };
+        auto release_in_loop = [&]() {
+          __builtin_amdgcn_s_waitcnt(0x0F75);  // vmcnt(5)
+          const uint32_t off = rel_pending ? (uint32_t)(rel_qtile * NW + w) * 4u : kOutOfRange;
+          __builtin_amdgcn_raw_buffer_store_b32((uint32_t)rel_rank + 1u, cnt_rs, off, 0, kCoherent);
+          rel_pending = false;
+        };
+        // counter value read one period earlier (none before the first
+        // sub-tile: its turn is polled, so that every wait for this read
+        // inside the loop sees the same operations issued after it)
+        uint32_t p_seen = 0;
+        if (n_steps > 0) {
+          fetch(0);
+          stage(0);
+        }
+        __syncthreads();  // sub-tile 0 staged
+        // period 0: stage A starts sub-tile 0; stage B stages sub-tile 1
+        if (n_steps > 0) {
+          fetch(1);
+          stage(1);
+        }
+        __syncthreads();
+
+        // Periods 1 .. n_steps.  Every period issues the same sequence of
+        // vector-memory operations (a prefetch past the end re-reads the
+        // last sub-tile into a buffer nobody reads any more), so that the
+        // waits the compiler places for each of them count only the
+        // operations issued after it.
+        for (int t = 1; t <= n_steps; ++t) {
+          // prefetch sub-tile t + 1 first: the ordered add's waits below then
+          // never wait for it (vector-memory operations complete in order)
+          fetch(t + 1);
+          {
+            const int g = t - 1;
+            const int b3 = g % 3;
+            const int b2 = g & 1;
+            const int2 itm = sItems[g / RHO];
+            const int kv = itm.x & 0xFFFF;
+            const int rank = itm.y & 0xFFFF;
+            const bool last = ((itm.y >> 30) & 1) != 0;
+            const int qtile = (itm.x >> 16) * RHO + (g % RHO);
+            const int q0 = qtile * BR;
+            if (kv != b_kv) {
+              // stage A wrote this tile's K into sK one period ago
+              if (b_kv >= 0) {
+                flush_dk();
+                __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): a fixed state after this rare path
+              }
+              b_kv = kv;
+#pragma unroll
+              for (int ks = 0; ks < KK; ++ks)
+                KT[ks] = tr_frag(sK, qix, ks * 16 + 8 * hh, ks * 16 + 8 * hh + 4, w * 32 + gcol, j16);
+#pragma unroll
+              for (int nt = 0; nt < NTD; ++nt) accdK[nt] = zero16();
+            }
+
+            if constexpr (ORDERED) {
+              // 1-2: turn check, accumulator reads for g, counter read for g + 1
+              bool ready = rank == 0 || __builtin_amdgcn_readfirstlane(p_seen) == (uint32_t)rank;
+              if (DEBUG && (a.jitter_seed != 0u || a.poison_q >= 0)) ready = false;
+              if (DEBUG && a.wait_stats && lane == 0) st_waits += rank > 0 ? 1u : 0u;
+              if (!ready) {
+                release_drain();
+                wait_turn(qtile, rank);
+              }
+              load_acc(qtile, rank > 0);
+              p_seen = load_relaxed_agent(counter(qtile_of(g + 1 < n_steps ? g + 1 : g)));
+            }
+
+            // dK += dS^T Q (contraction over the sub-tile's Q rows; K slots:
+            // Q rows r0 + {0..3}, r0 + 8 + {0..3}, the packed dS words stage
+            // A wrote, read back from dS^T)
+            const T* cQ = sQ[b3];
+            const T* cdSt = sdSt[b2];
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc) {
+              const int r0 = 16 * cc + 4 * hh;
+              const uint2 d0 = *reinterpret_cast<const uint2*>(&cdSt[kvl * LS + r0]);
+              const uint2 d1 = *reinterpret_cast<const uint2*>(&cdSt[kvl * LS + r0 + 8]);
+              const frag da = __builtin_bit_cast(bf16x8, make_uint4(d0.x, d0.y, d1.x, d1.y));
+#pragma unroll
+              for (int nt = 0; nt < NTD; ++nt) {
+                const frag bq = tr_frag(cQ, qix, r0, r0 + 8, nt * 32 + gcol, j16);
+                accdK[nt] = E::mma(da, bq, accdK[nt]);
+              }
+            }
+
+            // 3: release the previous add (its stores have had the products
+            // above as cover)
+            if constexpr (ORDERED) release_in_loop();
+
+            // dQ_part = dS K for column tile w (transposed when ordered)
+            f32x16 accQ = zero16();
+#pragma unroll
+            for (int ks = 0; ks < KK; ++ks) {
+              const frag fa = tr_frag(cdSt, six, ks * 16 + 8 * hh, ks * 16 + 8 * hh + 4, gcol, j16);
+              if constexpr (ORDERED) accQ = E::mma(KT[ks], fa, accQ);
+              else accQ = E::mma(fa, KT[ks], accQ);
+            }
+            if (DEBUG && a.partials != nullptr) {
+              float* pp = a.partials + (((size_t)head * a.n_tiles + kv) * N) * D;
+#pragma unroll
+              for (int r = 0; r < 16; ++r) pp[dq_off(q0, r)] = accQ[r];
+            }
+
+            if constexpr (ORDERED) {
+              // 4: the partial row-major through this wave's LDS area, added
+              // to the accumulator values read at the top of the period
+              float* row = sRow[w];
+#pragma unroll
+              for (int gq = 0; gq < 4; ++gq)
+                *reinterpret_cast<f32x4*>(&row[rix(l32, 8 * gq + 4 * hh)]) =
+                    f32x4{accQ[4 * gq], accQ[4 * gq + 1], accQ[4 * gq + 2], accQ[4 * gq + 3]};
+#pragma unroll
+              for (int gq = 0; gq < 4; ++gq) {
+                f32x4 v = *reinterpret_cast<const f32x4*>(&row[rix((lane >> 3) + 8 * gq, 4 * (lane & 7))]);
+                if (rank > 0) v = lv[gq] + v;
+                const uint32_t off = chunk_off(q0, gq);
+                // both stores issued, the one not wanted out of range: the
+                // accumulator (not last) or the scaled bf16 dQ (last)
+                const f32x4 vs = v * a.scale;
+                coherent_store4<POL>(dq_rs, last ? kOutOfRange : 4 * off, v);
+                typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+                __builtin_amdgcn_raw_buffer_store_b64(
+                    u32x2{pack2_bf16(vs[0], vs[1]), pack2_bf16(vs[2], vs[3])}, dqo_rs,
+                    last ? 2 * off : kOutOfRange, 0, 0);
+              }
+              if (!last) {
+                rel_pending = true;
+                rel_qtile = qtile;
+                rel_rank = rank;
+              }
+            } else {
+#pragma unroll
+              for (int r = 0; r < 16; ++r) atomic_add_f32(&dqa[dq_off(q0, r)], accQ[r]);
+            }
+          }
+          // sub-tile t + 1 into its buffer (last read by this stage in the
+          // previous period)
+          stage((t + 1) % 3);
+          __syncthreads();  // end of period t
+        }
+        if (b_kv >= 0) flush_dk();
+        if constexpr (ORDERED) release_drain();
+      }
+
+      // next unit
+      if (a.dynamic) {
+        if (tid == 0)
+          sUnit = (int)__hip_atomic_fetch_add(work_counter, 1u, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT) + W;
+        __syncthreads();
+        unit = sUnit;
+        __syncthreads();
+      } else {
+        unit += stride_static;
+      }
+    }
+  };
+  if (isA) run(std::true_type{}, std::false_type{});
+  else if (pl.xl) run(std::false_type{}, std::true_type{});
+  else run(std::false_type{}, std::false_type{});
+  if (DEBUG && a.wait_stats != nullptr && lane == 0 && !isA) {
+    uint64_t* st = a.wait_stats + ((size_t)blockIdx.x * NW + w) * 4;
+    st[0] = st_wait;
+    st[1] = st_waits;
+    st[2] = st_spun;
+    st[3] = (uint64_t)clock64() - st_t0;
+  }
+}
+
+template <bool DEBUG>
+static void* pick_pipe(bool masked, bool ordered) {
+  if (masked)
+    return ordered ? (void*)bwd_pipe_kernel<true, true, DEBUG> : (void*)bwd_pipe_kernel<true, false, DEBUG>;
+  return ordered ? (void*)bwd_pipe_kernel<false, true, DEBUG> : (void*)bwd_pipe_kernel<false, false, DEBUG>;
+}
+
+hipError_t bwd_pipe_max_coresident(bool masked, bool ordered, int* blocks) {
+  int per_cu = 0;
+  for (int dbg = 0; dbg < 2; ++dbg) {
+    void* f = dbg ? pick_pipe<true>(masked, ordered) : pick_pipe<false>(masked, ordered);
+    int n = 0;
+    hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, 512, 0);
+    if (e != hipSuccess) return e;
+    per_cu = dbg == 0 ? n : (n < per_cu ? n : per_cu);
+  }
+  int dev = 0, cus = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  e = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev);
+  if (e != hipSuccess) return e;
+  *blocks = per_cu * cus;
+  return hipSuccess;
+}
+
+hipError_t launch_bwd_pipe(bool masked, bool ordered, const BwdArgs& a, int grid,
+                           hipStream_t stream) {
+  const bool debug = a.jitter_seed != 0u || a.poison_q >= 0 || a.partials != nullptr ||
+                     a.wait_stats != nullptr;
+  void* f = debug ? pick_pipe<true>(masked, ordered) : pick_pipe<false>(masked, ordered);
+  BwdArgs copy = a;
+  void* args[] = {&copy};
+  // cooperative: every workgroup resident, which the ordered waits rely on
+  return hipLaunchCooperativeKernel(f, dim3(grid), dim3(512), args, 0, stream);
+}
+
+}  // namespace dash
