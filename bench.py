@@ -130,6 +130,11 @@ PHASES_A = ("item/KV change", "S products", "softmax,P", "P barrier", "dV produc
             "barrier", "dQ product,partial", "prefetch")
 PHASES_B = ("item/KV change", "dP products,counter check", "-", "P barrier", "dS,dK products",
             "staging", "ordered add,barrier", "hand-off", "prefetch,counter read")
+# two-stage pipeline layout: stage A (S, dP, P, dS, dV of sub-tile t) and
+# stage B (dK, dQ and the ordered add of sub-tile t - 1)
+PIPE_A = ("item/KV change,loads", "S,dP products", "softmax,dS", "dV product", "barrier")
+PIPE_B = ("item/KV change", "turn check,acc reads", "dK product", "hand-off", "dQ product",
+          "ordered add", "barrier")
 
 
 def phase_shares(D, dev, lse, delta, sched, causal, ws, out, mkw, lay=None):
@@ -149,7 +154,9 @@ def phase_shares(D, dev, lse, delta, sched, causal, ws, out, mkw, lay=None):
         total = a[:, 15].sum()
         return {name: round(float(a[:, k].sum() / total), 4) for k, name in enumerate(PHASES)}
     res = {}
-    for role, tag, names in ((1, "A", PHASES_A), (2, "B", PHASES_B)):
+    pipe = (lay or {}).get("layout") == 2
+    for role, tag, names in ((1, "A", PIPE_A if pipe else PHASES_A),
+                             (2, "B", PIPE_B if pipe else PHASES_B)):
         r = a[a[:, 14] == role]
         total = r[:, 15].sum()
         res.update({f"{tag}: {n}": round(float(r[:, k].sum() / total), 4)
@@ -259,8 +266,6 @@ def main():
     flops = w.flops_bwd(causal)
 
     lay = {"pairs": {"layout": 1}, "pipe": {"layout": 2}}.get(args.layout, {})
-    # the pipeline layout has no phase timer
-    no_phases = args.layout == "pipe"
 
     def step(sched, events=None):
         D.attn_bwd_preprocess(o, dev["do"], out=delta)
@@ -302,7 +307,7 @@ def main():
         if sched not in ("atomic", "auto") and not args.no_wait_stats:
             results[sched].update(order_wait(D, dev, lse, delta, sched, causal, ws, (dq, dk, dv),
                                              mkw, lay))
-        if args.phases and not no_phases:
+        if args.phases:
             results[sched]["phases"] = phase_shares(D, dev, lse, delta, sched, causal, ws,
                                                     (dq, dk, dv), mkw, lay)
             print(f"[bench] {sched:10s} phases " + "  ".join(
@@ -323,7 +328,7 @@ def main():
     # the ordered add's share of the primary schedule's wave cycles (one
     # extra untimed launch with the phase timer, unless --phases ran it)
     add_share = None
-    if ran != "atomic" and not args.no_wait_stats and not no_phases:
+    if ran != "atomic" and not args.no_wait_stats:
         ph = results[primary].get("phases") or phase_shares(D, dev, lse, delta, ran, causal, ws,
                                                             (dq, dk, dv), mkw, lay)
         if not lay:

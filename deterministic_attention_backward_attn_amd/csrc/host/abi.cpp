@@ -654,7 +654,6 @@ dash_status run_bwd(const dash_attn_desc* desc, dash_schedule schedule, const vo
   const bool pipe = dbg && dbg->layout == 2;
   if (dbg && (dbg->layout < 0 || dbg->layout > 2)) return DASH_ERR_INVALID_ARG;
   if ((pairs || pipe) && (desc->dtype != 1 || desc->d != 128)) return DASH_ERR_UNSUPPORTED;
-  if (pipe && dbg->phase_stats) return DASH_ERR_UNSUPPORTED;
 
   const MaskKey mkey = mask_key(desc);
   const bool plain = plain_key(mkey);
@@ -788,9 +787,9 @@ dash_status run_bwd(const dash_attn_desc* desc, dash_schedule schedule, const vo
   a.partials = dbg ? dbg->partials : nullptr;
   a.wait_stats = dbg ? dbg->wait_stats : nullptr;
   a.phase_stats = dbg ? dbg->phase_stats : nullptr;
-  // (the wave-pair layout times 8 waves per workgroup)
+  // (the 8-wave layouts time 8 waves per workgroup)
   if ((a.wait_stats || a.phase_stats) &&
-      (long)grid * (pairs ? 8 : dash::bwd_waves(desc->dtype, desc->d)) > 4096L * 4)
+      (long)grid * ((pairs || pipe) ? 8 : dash::bwd_waves(desc->dtype, desc->d)) > 4096L * 4)
     return DASH_ERR_UNSUPPORTED;
   hipEvent_t ev0 = dbg ? (hipEvent_t)dbg->kernel_events[0] : nullptr;
   hipEvent_t ev1 = dbg ? (hipEvent_t)dbg->kernel_events[1] : nullptr;

@@ -7,8 +7,8 @@
 //
 //   stage A (waves 0..3: K and V fragments and the dV accumulator in
 //     registers), sub-tile t: S = Q K^T, dP = dO V^T, P = exp(s S - LSE)
-//     (masked), dS = P (dP - delta), dV += P^T dO; dS^T to LDS; stages the
-//     next Q/dO sub-tile and prefetches the one after;
+//     (masked), dS = P (dP - delta), dV += P^T dO; dS^T to LDS; loads the
+//     next Q/dO sub-tile straight into LDS;
 //   stage B (waves 4..7: the dK accumulator and K^T fragments), sub-tile
 //     t - 1: dK += dS^T Q, dQ_part^T = K^T dS^T, and the ordered add of
 //     dQ_part into the fp32 accumulator.
@@ -19,7 +19,8 @@
 // runs B's products while A computes its exponentials.  The ordered add's
 // memory round trips (counter read, accumulator read, store, hand-off) are
 // issued only by the B waves, whose vector-memory queue holds nothing else,
-// so a wait for one of them never waits for a prefetch.  Results are
+// so a wait for one of them never waits for a prefetch (vector-memory
+// operations of a wave complete in issue order).  Results are
 // bit-identical to the other layouts: every product, exponential and add is
 // computed with the same operands in the same order.
 //
@@ -72,8 +73,8 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
   __shared__ __align__(16) T sdO[3][BR * LQ];
   __shared__ __align__(16) T sdSt[2][BC * LS];
   __shared__ __align__(16) T sK[BC * LQ];
-  __shared__ __align__(16) float sLSE[3][BR];
-  __shared__ __align__(16) float sDel[3][BR];
+  // LSE (unscaled) in [0, BR), delta in [BR, 2 BR) of each buffer
+  __shared__ __align__(16) float sStat[3][2 * BR];
   __shared__ int2 sItems[kMaxUnitItems];
   constexpr int LR = 32;
   __shared__ __align__(16) float sRow[ORDERED ? NW : 1][ORDERED ? 32 * LR : 4];
@@ -100,6 +101,22 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
 
   uint64_t st_wait = 0, st_waits = 0, st_spun = 0;
   const uint64_t st_t0 = (DEBUG && a.wait_stats) ? (uint64_t)clock64() : 0;
+  // phase timer (test hook, debug instantiation only): lane 0 of each wave
+  // adds the shader-clock cycles since the previous mark to the phase that
+  // just ended.  Stage A: 0 item decode, KV tile changes and the next
+  // sub-tile's loads, 1 S and dP products, 2 softmax and dS, 3 dV product,
+  // 4 barrier.  Stage B: 0 item decode and KV tile changes, 1 turn check and
+  // accumulator reads, 2 dK product, 3 hand-off, 4 dQ product, 5 ordered
+  // add, 6 barrier.
+  uint64_t ph[8] = {};
+  uint64_t ph_t = (DEBUG && a.phase_stats) ? (uint64_t)clock64() : 0;
+  const uint64_t ph_t0 = ph_t;
+#define PHASE(k)                                                   \
+  if (DEBUG && a.phase_stats && lane == 0) {                       \
+    const uint64_t t_ = (uint64_t)clock64();                       \
+    ph[k] += t_ - ph_t;                                            \
+    ph_t = t_;                                                     \
+  }
 
   const Placement pl = place_units(a, tid, sPlace);
   const int U = a.units_per_head;
@@ -145,6 +162,39 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
         // ---------------------------------------------------------- stage A
         const T* Kg = reinterpret_cast<const T*>(a.k) + hoff;
         const T* Vg = reinterpret_cast<const T*>(a.v) + hoff;
+        const float* lse_g = a.lse + (size_t)head * N;
+        const float* del_g = a.delta + (size_t)head * N;
+        // Sub-tile g into buffer `buf` by direct loads to LDS (no registers:
+        // lane i of a 16-byte load writes LDS bytes [16 i, 16 i + 16) of the
+        // instruction's 1 KB).  Wave w loads LDS chunks [128 w, 128 w + 128)
+        // of sQ and of sdO, i.e. rows 8w .. 8w + 7: lane i of instruction m
+        // fills row 8w + 4m + i / 16, 16-byte slot i % 16, which holds the
+        // row's global chunk (slot ^ swz(row)).  Wave 0 also loads LSE and
+        // delta (one dword per lane).  The loads complete before the barrier
+        // that ends the period (the compiler waits for them there).
+        const int wu = __builtin_amdgcn_readfirstlane(w);
+        // per-lane element offsets within a sub-tile of the two 16-byte
+        // loads (rows 8w + 4m + lane / 16, m = 0, 1; swz depends on the row
+        // only through lane / 16 and 2w + m)
+        uint32_t doff[2];
+#pragma unroll
+        for (int m = 0; m < 2; ++m) {
+          const int row = 8 * w + 4 * m + (lane >> 4);
+          doff[m] = (uint32_t)(row * D + ((lane & 15) ^ swz<D>(row)) * VEC);
+        }
+        // LSE for lanes < BR, delta for the others
+        const float* stat_src = lane < BR ? lse_g + lane : del_g + (lane - BR);
+        auto dma = [&](int g, int buf) {
+          const int q0 = qtile_of(g) * BR;
+#pragma unroll
+          for (int m = 0; m < 2; ++m) {
+            __builtin_amdgcn_global_load_lds(Qg + (size_t)q0 * D + doff[m],
+                                             &sQ[buf][(8 * wu + 4 * m) * LQ], 16, 0, 0);
+            __builtin_amdgcn_global_load_lds(dOg + (size_t)q0 * D + doff[m],
+                                             &sdO[buf][(8 * wu + 4 * m) * LQ], 16, 0, 0);
+          }
+          if (wu == 0) __builtin_amdgcn_global_load_lds(stat_src + q0, &sStat[buf][0], 4, 0, 0);
+        };
         frag Kreg[DK], Vreg[DK];
         f32x16 accdV[NTD];
         int a_kv = -1;
@@ -157,9 +207,15 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
               dVg[(uint32_t)((a_kv * BC + 32 * w + crow(r, hh)) * D + nt * 32 + l32)] =
                   E::from_f32(accdV[nt][r]);
         };
-        __syncthreads();  // sub-tile 0 staged by stage B
+        if (n_steps > 0) dma(0, 0);
+        __syncthreads();  // sub-tile 0 in LDS
 
         for (int t = 0; t <= n_steps; ++t) {
+          PHASE(4);
+          // Nothing of this stage is in flight here (the barrier waited for
+          // the sub-tile loads); saying so keeps the compiler from waiting
+          // on the next loads for a value it last loaded before the loop.
+          __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
           if (t < n_steps) {
             const int b3 = t % 3;
             const int b2 = t & 1;
@@ -188,7 +244,15 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
               for (int ks = 0; ks < DK; ++ks)
                 *reinterpret_cast<uint4*>(&sK[qix(kvl, ks * KSTEP + hh * KPL)]) =
                     __builtin_bit_cast(uint4, Kreg[ks]);
+              // all of this rare path's loads complete here, so that the
+              // products below never wait for the sub-tile loads issued
+              // after it
+              __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
             }
+            // sub-tile t + 1 into its buffer (its previous contents, sub-tile
+            // t - 2, were last read by stage B in the previous period)
+            if (t + 1 < n_steps) dma(t + 1, (t + 1) % 3);
+            PHASE(0);
             const T* cQ = sQ[b3];
             const T* cdO = sdO[b3];
             f32x16 accS = zero16(), accP = zero16();
@@ -212,6 +276,7 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
               __builtin_amdgcn_sched_barrier(0);
             }
 
+            PHASE(1);
             // P and dS (pairs flagged partial hide the elements outside
             // lo <= i - j <= hi), packed once to bf16 (hardware RNE
             // conversion); P stays in registers for dV, dS^T goes to LDS
@@ -223,12 +288,15 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
               const int qb = 8 * gq + 4 * hh;  // 4 consecutive Q rows
-              const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sLSE[b3][qb]);
-              const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sDel[b3][qb]);
+              const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sStat[b3][qb]);
+              const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sStat[b3][BR + qb]);
               float p[4], ds[4];
+              // exp2(s log2(e) S - log2(e) LSE): both products rounded to
+              // fp32 once, the first fused into the subtraction
 #pragma unroll
               for (int e = 0; e < 4; ++e)
-                p[e] = __builtin_amdgcn_exp2f(accS[4 * gq + e] * a.scale_log2 - l4[e]);
+                p[e] = __builtin_amdgcn_exp2f(
+                    __builtin_fmaf(accS[4 * gq + e], a.scale_log2, -__fmul_rn(l4[e], kLog2e)));
               if (emask) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -243,6 +311,7 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
               *reinterpret_cast<uint2*>(&cdSt[kvl * LS + qb]) =
                   make_uint2(pack2_bf16(ds[0], ds[1]), pack2_bf16(ds[2], ds[3]));
             }
+            PHASE(2);
             // dV += P^T dO (contraction over the sub-tile's Q rows; K slots:
             // Q rows r0 + {0..3}, r0 + 8 + {0..3})
 #pragma unroll
@@ -256,6 +325,7 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
                 accdV[nt] = E::mma(pa, bo, accdV[nt]);
               }
             }
+            PHASE(3);
           }
           __syncthreads();  // end of period t
         }
@@ -265,42 +335,6 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
         float* dqa = a.dq_accum + hoff;
         T* dqo = reinterpret_cast<T*>(a.dq) + hoff;
         uint32_t* cnt_h = a.counters + (size_t)head * n_sub * NW;
-        const int tb = tid - NA;  // thread index within stage B
-        const float* lse_g = a.lse + (size_t)head * N;
-        const float* del_g = a.delta + (size_t)head * N;
-        u32x4 pq[CPT], pdo[CPT];
-        float pstat = 0.f;
-        auto fetch = [&](int g) {
-          g = g < n_steps ? g : n_steps - 1;  // past the end: a harmless re-read
-          const int q0 = qtile_of(g) * BR;
-#pragma unroll
-          for (int i = 0; i < CPT; ++i) {
-            const int c = tb + i * NA;
-            const int row = c / (D / VEC);
-            const int col = (c % (D / VEC)) * VEC;
-            const uint32_t off = (uint32_t)((q0 + row) * D + col);
-            pq[i] = *reinterpret_cast<const u32x4*>(Qg + off);
-            pdo[i] = *reinterpret_cast<const u32x4*>(dOg + off);
-          }
-          // one load into one register for every lane (lanes past 2*BR
-          // re-read a valid element and discard it)
-          const float* src = tb < BR ? lse_g + (q0 + tb)
-                                     : del_g + (q0 + (tb < 2 * BR ? tb - BR : 0));
-          pstat = *src;
-        };
-        auto stage = [&](int buf) {
-#pragma unroll
-          for (int i = 0; i < CPT; ++i) {
-            const int c = tb + i * NA;
-            const int row = c / (D / VEC);
-            const int col = (c % (D / VEC)) * VEC;
-            *reinterpret_cast<u32x4*>(&sQ[buf][qix(row, col)]) = pq[i];
-            *reinterpret_cast<u32x4*>(&sdO[buf][qix(row, col)]) = pdo[i];
-          }
-          if (tb < BR) sLSE[buf][tb] = pstat * kLog2e;
-          else if (tb < 2 * BR) sDel[buf][tb - BR] = pstat;
-        };
-
         frag KT[KK];
         f32x16 accdK[NTD];
         int b_kv = -1;
@@ -362,9 +396,8 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
         // then store the next rank into its counter (device-coherent, every
         // lane the same word).  In the loop it is issued every period (to an
         // offset out of the counters' range, storing nothing, when no add is
-        // pending) after at least the prefetch (5 operations), the
-        // accumulator reads (4) and the counter read (1) of the period, of
-        // which the last five may stay outstanding.
+        // pending) after exactly the accumulator reads (4) and the counter
+        // read (1) of the period, which may stay outstanding.
         auto release_drain = [&]() {
           if (rel_pending) {
             __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
@@ -382,27 +415,14 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
         // sub-tile: its turn is polled, so that every wait for this read
         // inside the loop sees the same operations issued after it)
         uint32_t p_seen = 0;
-        if (n_steps > 0) {
-          fetch(0);
-          stage(0);
-        }
-        __syncthreads();  // sub-tile 0 staged
-        // period 0: stage A starts sub-tile 0; stage B stages sub-tile 1
-        if (n_steps > 0) {
-          fetch(1);
-          stage(1);
-        }
-        __syncthreads();
+        __syncthreads();  // sub-tile 0 in LDS
+        __syncthreads();  // period 0: stage A starts sub-tile 0
 
         // Periods 1 .. n_steps.  Every period issues the same sequence of
-        // vector-memory operations (a prefetch past the end re-reads the
-        // last sub-tile into a buffer nobody reads any more), so that the
-        // waits the compiler places for each of them count only the
-        // operations issued after it.
+        // vector-memory operations, so that the waits the compiler places
+        // for each of them count only the operations issued after it.
         for (int t = 1; t <= n_steps; ++t) {
-          // prefetch sub-tile t + 1 first: the ordered add's waits below then
-          // never wait for it (vector-memory operations complete in order)
-          fetch(t + 1);
+          PHASE(6);
           {
             const int g = t - 1;
             const int b3 = g % 3;
@@ -427,6 +447,7 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
               for (int nt = 0; nt < NTD; ++nt) accdK[nt] = zero16();
             }
 
+            PHASE(0);
             if constexpr (ORDERED) {
               // 1-2: turn check, accumulator reads for g, counter read for g + 1
               bool ready = rank == 0 || __builtin_amdgcn_readfirstlane(p_seen) == (uint32_t)rank;
@@ -440,6 +461,7 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
               p_seen = load_relaxed_agent(counter(qtile_of(g + 1 < n_steps ? g + 1 : g)));
             }
 
+            PHASE(1);
             // dK += dS^T Q (contraction over the sub-tile's Q rows; K slots:
             // Q rows r0 + {0..3}, r0 + 8 + {0..3}, the packed dS words stage
             // A wrote, read back from dS^T)
@@ -460,7 +482,9 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
 
             // 3: release the previous add (its stores have had the products
             // above as cover)
+            PHASE(2);
             if constexpr (ORDERED) release_in_loop();
+            PHASE(3);
 
             // dQ_part = dS K for column tile w (transposed when ordered)
             f32x16 accQ = zero16();
@@ -476,6 +500,7 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
               for (int r = 0; r < 16; ++r) pp[dq_off(q0, r)] = accQ[r];
             }
 
+            PHASE(4);
             if constexpr (ORDERED) {
               // 4: the partial row-major through this wave's LDS area, added
               // to the accumulator values read at the top of the period
@@ -508,9 +533,7 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
               for (int r = 0; r < 16; ++r) atomic_add_f32(&dqa[dq_off(q0, r)], accQ[r]);
             }
           }
-          // sub-tile t + 1 into its buffer (last read by this stage in the
-          // previous period)
-          stage((t + 1) % 3);
+          PHASE(5);
           __syncthreads();  // end of period t
         }
         if (b_kv >= 0) flush_dk();
@@ -540,6 +563,13 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
     st[2] = st_spun;
     st[3] = (uint64_t)clock64() - st_t0;
   }
+  if (DEBUG && a.phase_stats != nullptr && lane == 0) {
+    uint64_t* st = a.phase_stats + ((size_t)blockIdx.x * 8 + wv) * 16;
+    for (int k = 0; k < 8; ++k) st[k] = ph[k];
+    st[14] = isA ? 1u : 2u;
+    st[15] = (uint64_t)clock64() - ph_t0;
+  }
+#undef PHASE
 }
 
 template <bool DEBUG>
@@ -570,7 +600,7 @@ hipError_t bwd_pipe_max_coresident(bool masked, bool ordered, int* blocks) {
 hipError_t launch_bwd_pipe(bool masked, bool ordered, const BwdArgs& a, int grid,
                            hipStream_t stream) {
   const bool debug = a.jitter_seed != 0u || a.poison_q >= 0 || a.partials != nullptr ||
-                     a.wait_stats != nullptr;
+                     a.wait_stats != nullptr || a.phase_stats != nullptr;
   void* f = debug ? pick_pipe<true>(masked, ordered) : pick_pipe<false>(masked, ordered);
   BwdArgs copy = a;
   void* args[] = {&copy};
