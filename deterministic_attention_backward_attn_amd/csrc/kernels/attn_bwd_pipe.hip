@@ -313,18 +313,23 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
             }
             PHASE(2);
             // dV += P^T dO (contraction over the sub-tile's Q rows; K slots:
-            // Q rows r0 + {0..3}, r0 + 8 + {0..3})
+            // Q rows r0 + {0..3}, r0 + 8 + {0..3}); the dO operands are read
+            // before the first product
+            frag bo[2][NTD];
+#pragma unroll
+            for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+              for (int nt = 0; nt < NTD; ++nt)
+                bo[cc][nt] = tr_frag(cdO, qix, 16 * cc + 4 * hh, 16 * cc + 4 * hh + 8, nt * 32 + gcol, j16);
+            __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int cc = 0; cc < 2; ++cc) {
-              const int r0 = 16 * cc + 4 * hh;
               const frag pa = __builtin_bit_cast(
                   bf16x8, make_uint4(pw[4 * cc], pw[4 * cc + 1], pw[4 * cc + 2], pw[4 * cc + 3]));
 #pragma unroll
-              for (int nt = 0; nt < NTD; ++nt) {
-                const frag bo = tr_frag(cdO, qix, r0, r0 + 8, nt * 32 + gcol, j16);
-                accdV[nt] = E::mma(pa, bo, accdV[nt]);
-              }
+              for (int nt = 0; nt < NTD; ++nt) accdV[nt] = E::mma(pa, bo[cc][nt], accdV[nt]);
             }
+            __builtin_amdgcn_sched_barrier(0);
             PHASE(3);
           }
           __syncthreads();  // end of period t
@@ -464,36 +469,44 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
             PHASE(1);
             // dK += dS^T Q (contraction over the sub-tile's Q rows; K slots:
             // Q rows r0 + {0..3}, r0 + 8 + {0..3}, the packed dS words stage
-            // A wrote, read back from dS^T)
+            // A wrote, read back from dS^T), then dQ_part = dS K for column
+            // tile w (transposed when ordered).  The dK operands are all read
+            // from LDS before its first product and the dQ operands while
+            // the dK products run, so that the products wait for the reads'
+            // latency once rather than once each.
             const T* cQ = sQ[b3];
             const T* cdSt = sdSt[b2];
+            frag da[2], bq[2][NTD], fa[KK];
 #pragma unroll
             for (int cc = 0; cc < 2; ++cc) {
               const int r0 = 16 * cc + 4 * hh;
               const uint2 d0 = *reinterpret_cast<const uint2*>(&cdSt[kvl * LS + r0]);
               const uint2 d1 = *reinterpret_cast<const uint2*>(&cdSt[kvl * LS + r0 + 8]);
-              const frag da = __builtin_bit_cast(bf16x8, make_uint4(d0.x, d0.y, d1.x, d1.y));
+              da[cc] = __builtin_bit_cast(bf16x8, make_uint4(d0.x, d0.y, d1.x, d1.y));
 #pragma unroll
-              for (int nt = 0; nt < NTD; ++nt) {
-                const frag bq = tr_frag(cQ, qix, r0, r0 + 8, nt * 32 + gcol, j16);
-                accdK[nt] = E::mma(da, bq, accdK[nt]);
-              }
+              for (int nt = 0; nt < NTD; ++nt)
+                bq[cc][nt] = tr_frag(cQ, qix, r0, r0 + 8, nt * 32 + gcol, j16);
             }
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int i = 0; i < KK; ++i) {
+              accdK[i % NTD] = E::mma(da[i / NTD], bq[i / NTD][i % NTD], accdK[i % NTD]);
+              fa[i] = tr_frag(cdSt, six, i * 16 + 8 * hh, i * 16 + 8 * hh + 4, gcol, j16);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+            f32x16 accQ = zero16();
+#pragma unroll
+            for (int ks = 0; ks < KK; ++ks) {
+              if constexpr (ORDERED) accQ = E::mma(KT[ks], fa[ks], accQ);
+              else accQ = E::mma(fa[ks], KT[ks], accQ);
+            }
+            __builtin_amdgcn_sched_barrier(0);
 
             // 3: release the previous add (its stores have had the products
             // above as cover)
             PHASE(2);
             if constexpr (ORDERED) release_in_loop();
             PHASE(3);
-
-            // dQ_part = dS K for column tile w (transposed when ordered)
-            f32x16 accQ = zero16();
-#pragma unroll
-            for (int ks = 0; ks < KK; ++ks) {
-              const frag fa = tr_frag(cdSt, six, ks * 16 + 8 * hh, ks * 16 + 8 * hh + 4, gcol, j16);
-              if constexpr (ORDERED) accQ = E::mma(KT[ks], fa, accQ);
-              else accQ = E::mma(fa, KT[ks], accQ);
-            }
             if (DEBUG && a.partials != nullptr) {
               float* pp = a.partials + (((size_t)head * a.n_tiles + kv) * N) * D;
 #pragma unroll
