@@ -137,7 +137,7 @@ PIPE_B = ("item/KV change", "turn check,acc reads", "dK product", "hand-off", "d
           "ordered add", "barrier")
 
 
-def phase_shares(D, dev, lse, delta, sched, causal, ws, out, mkw, lay=None):
+def phase_shares(D, dev, lse, delta, sched, causal, ws, out, mkw, lay=None, kind="single"):
     """One extra, untimed launch with the phase timer on: the share of the
     waves' cycles spent in each phase of their Q sub-tiles (the timer's own
     clock reads slow the launch down; the shares are the result)."""
@@ -150,11 +150,11 @@ def phase_shares(D, dev, lse, delta, sched, causal, ws, out, mkw, lay=None):
     D.attn_bwd_status(ws)
     a = st.view(-1, 16).cpu().numpy().astype("float64")
     a = a[a[:, 15] > 0]
-    if not lay:
+    if kind == "single":
         total = a[:, 15].sum()
         return {name: round(float(a[:, k].sum() / total), 4) for k, name in enumerate(PHASES)}
     res = {}
-    pipe = (lay or {}).get("layout") == 2
+    pipe = kind == "pipe"
     for role, tag, names in ((1, "A", PIPE_A if pipe else PHASES_A),
                              (2, "B", PIPE_B if pipe else PHASES_B)):
         r = a[a[:, 14] == role]
@@ -206,7 +206,7 @@ def main():
                          "runs the measured fastest instead of the DAG model's pick")
     ap.add_argument("--no-fwd", action="store_true",
                     help="skip the forward and forward+backward timings")
-    ap.add_argument("--layout", choices=["default", "pairs", "pipe"], default="default",
+    ap.add_argument("--layout", choices=["auto", "single", "pairs", "pipe"], default="auto",
                     help="backward kernel layout: default, wave pairs or the two-stage "
                          "pipeline (bf16 d=128; bit-identical results)")
     ap.add_argument("--phases", action="store_true",
@@ -265,7 +265,12 @@ def main():
     ws = D.alloc_workspace(dev["q"], causal, "naive")
     flops = w.flops_bwd(causal)
 
-    lay = {"pairs": {"layout": 1}, "pipe": {"layout": 2}}.get(args.layout, {})
+    lay = {"auto": {}, "single": {"layout": 3}, "pairs": {"layout": 1},
+           "pipe": {"layout": 2}}[args.layout]
+    # the kernel that runs (the library's automatic choice: the pipeline for
+    # bf16 with d = 128), for the phase names and the report
+    kind = args.layout if args.layout != "auto" else (
+        "pipe" if w.dtype == "bf16" and w.d == 128 else "single")
 
     def step(sched, events=None):
         D.attn_bwd_preprocess(o, dev["do"], out=delta)
@@ -309,7 +314,7 @@ def main():
                                              mkw, lay))
         if args.phases:
             results[sched]["phases"] = phase_shares(D, dev, lse, delta, sched, causal, ws,
-                                                    (dq, dk, dv), mkw, lay)
+                                                    (dq, dk, dv), mkw, lay, kind)
             print(f"[bench] {sched:10s} phases " + "  ".join(
                 f"{k} {v:.3f}" for k, v in results[sched]["phases"].items()), file=sys.stderr,
                 flush=True)
@@ -330,9 +335,13 @@ def main():
     add_share = None
     if ran != "atomic" and not args.no_wait_stats:
         ph = results[primary].get("phases") or phase_shares(D, dev, lse, delta, ran, causal, ws,
-                                                            (dq, dk, dv), mkw, lay)
-        if not lay:
+                                                            (dq, dk, dv), mkw, lay, kind)
+        if kind == "single":
             add_share = round(sum(ph[k] for k in ("counter check", "ordered add", "hand-off")), 4)
+        elif kind == "pipe":
+            # the stage that adds (half of the waves)
+            add_share = round(sum(ph[f"B: {k}"] for k in ("turn check,acc reads", "ordered add",
+                                                          "hand-off")), 4)
 
     def timed(fn):
         for _ in range(args.warmup):
@@ -388,8 +397,8 @@ def main():
                    + (" block " + json.dumps(w.block_spec) if w.block_spec else ""),
                    "schedule": primary if ran == primary else f"{primary} ({ran})",
                    "parallelism": "single GPU",
-                   **({"layout": {"pairs": "wave pairs", "pipe": "two-stage pipeline"}[args.layout]}
-                      if lay else {})},
+                   "layout": {"single": "one-stage", "pairs": "wave pairs",
+                              "pipe": "two-stage pipeline"}[kind]},
         "pct_peak": round(100.0 * prim["tflops"] / peak, 2),
         "det_nondet_ratio": ({s: round(r["tflops"] / results["atomic"]["tflops"], 4)
                               for s, r in results.items() if s != "atomic"}
@@ -402,7 +411,8 @@ def main():
             "ordered_add_share_of_wave_cycles": add_share,
             "schedule": ran,
             "source": "phase timer of the backward kernel (one instrumented launch): counter "
-                      "check + ordered add + hand-off phases"},
+                      "check + ordered add + hand-off phases"
+                      + (" of the adding stage's waves" if kind == "pipe" else "")},
         "dag_vs_measured": dag_vs_measured(results),
         "dag_fit": dag_fit(D, w, causal, mkw, results,
                            torch.cuda.get_device_properties(0).multi_processor_count),

@@ -37,7 +37,22 @@ bool sched_ok_run(int s) { return sched_ok(s) || s == DASH_SCHED_AUTO; }
 // the hand-off latency each about 5 % of an item (measured on MI355X at
 // d = 128: ~24k cycles per item, ~1.2k per hand-off).
 constexpr double kDefaultCost[4] = {1.0, 0.5, 0.05, 0.05};
+// The two-stage pipeline layout overlaps a sub-tile's products with the
+// previous sub-tile's dQ add, so an item costs less and the chain of ordered
+// adds relatively more: fitted to its times on MI355X (the add and the
+// hand-off each about 30 % of an item; this model picks the fastest ordered
+// schedule on the causal, full, sliding-window and block-sparse workloads).
+constexpr double kPipeCost[4] = {1.0, 0.5, 0.3, 0.3};
 typedef std::array<double, 4> Cost;
+
+// Backward kernel layouts (dash_bwd_debug.layout): 0 automatic, 1 wave
+// pairs, 2 two-stage pipeline, 3 one-stage kernel.
+constexpr int kLayoutPairs = 1, kLayoutPipe = 2, kLayoutOneStage = 3;
+// The layout an automatic launch runs: the pipeline where it exists (bf16,
+// d = 128), else the one-stage kernel.
+int auto_layout(int dtype, int d) {
+  return dtype == DASH_BF16 && d == 128 ? kLayoutPipe : kLayoutOneStage;
+}
 
 constexpr int kXcds = 8;  // XCDs of an MI355X: the workgroup groups of the placement
 
@@ -574,11 +589,13 @@ bool any_partial(const MaskKey& key) {
 }
 
 // The costs AUTO uses for (device, dtype, d): fitted by
-// dash_attn_bwd_calibrate, else the defaults.  Caller holds g_mu.
+// dash_attn_bwd_calibrate, else the defaults of the layout an automatic
+// launch runs.  Caller holds g_mu.
 Cost costs_for(int dev, int dtype, int d) {
   auto it = g_costs.find(std::make_tuple(dev, dtype, d));
-  return it != g_costs.end() ? it->second
-                             : Cost{kDefaultCost[0], kDefaultCost[1], kDefaultCost[2], kDefaultCost[3]};
+  if (it != g_costs.end()) return it->second;
+  const double* c = auto_layout(dtype, d) == kLayoutPipe ? kPipeCost : kDefaultCost;
+  return Cost{c[0], c[1], c[2], c[3]};
 }
 
 AutoKey auto_key(int dev, const dash_attn_desc* d, const MaskKey& mkey, int maxco) {
@@ -650,10 +667,12 @@ dash_status run_bwd(const dash_attn_desc* desc, dash_schedule schedule, const vo
   if (dbg && (dbg->poison_q < 0 || dbg->poison_q > desc->N / br)) return DASH_ERR_INVALID_ARG;
   if (dbg && (dbg->placement < 0 || dbg->placement > 3)) return DASH_ERR_INVALID_ARG;
   if (dbg && (dbg->unit_order < 0 || dbg->unit_order > 2)) return DASH_ERR_INVALID_ARG;
-  const bool pairs = dbg && dbg->layout == 1;
-  const bool pipe = dbg && dbg->layout == 2;
-  if (dbg && (dbg->layout < 0 || dbg->layout > 2)) return DASH_ERR_INVALID_ARG;
-  if ((pairs || pipe) && (desc->dtype != 1 || desc->d != 128)) return DASH_ERR_UNSUPPORTED;
+  int lay = dbg ? dbg->layout : 0;
+  if (lay < 0 || lay > kLayoutOneStage) return DASH_ERR_INVALID_ARG;
+  const bool auto_lay = lay == 0;
+  if (auto_lay) lay = auto_layout(desc->dtype, desc->d);
+  if ((lay == kLayoutPairs || lay == kLayoutPipe) && (desc->dtype != DASH_BF16 || desc->d != 128))
+    return DASH_ERR_UNSUPPORTED;
 
   const MaskKey mkey = mask_key(desc);
   const bool plain = plain_key(mkey);
@@ -674,14 +693,20 @@ dash_status run_bwd(const dash_attn_desc* desc, dash_schedule schedule, const vo
   int maxco = 0;
   st = get_coresident(dev, desc->dtype, desc->d, masked, ordered, &maxco);
   if (st != DASH_OK) return st;
-  if (pairs || pipe) {
-    // the 8-wave kernels must fit as many workgroups (the same schedule)
+  if (lay != kLayoutOneStage) {
+    // the 8-wave kernels must fit as many workgroups as the one-stage kernel
+    // (the schedule's tables are planned for that many); an automatic launch
+    // that finds fewer runs the one-stage kernel instead
     int pb = 0;
-    if ((pairs ? dash::bwd_pair_max_coresident(masked, ordered, &pb)
-               : dash::bwd_pipe_max_coresident(masked, ordered, &pb)) != hipSuccess)
+    if ((lay == kLayoutPairs ? dash::bwd_pair_max_coresident(masked, ordered, &pb)
+                             : dash::bwd_pipe_max_coresident(masked, ordered, &pb)) != hipSuccess)
       return DASH_ERR_HIP;
-    if (pb < maxco) return DASH_ERR_UNSUPPORTED;
+    if (pb < maxco) {
+      if (!auto_lay) return DASH_ERR_UNSUPPORTED;
+      lay = kLayoutOneStage;
+    }
   }
+  const bool pairs = lay == kLayoutPairs, pipe = lay == kLayoutPipe;
   lock.lock();
   Sched s = Sched::Naive;
   st = resolve_schedule(schedule, dev, desc, mkey, maxco, &s);

@@ -295,7 +295,8 @@ dash_status dash_attn_bwd_status(const void* workspace, void* stream);
  *                   cycles spent waiting for ordered adds, k=1 ordered waits,
  *                   k=2 waits that polled more than once, k=3 cycles of the
  *                   workgroup's whole run (waves = dash_attn_tile/32;
- *                   workgroups x waves must not exceed 4096 * 4, else
+ *                   workgroups x waves, counting 8 waves per workgroup with
+ *                   layouts 1 and 2, must not exceed 4096 * 4, else
  *                   DASH_ERR_UNSUPPORTED).
  *   phase_stats     non-NULL: device uint64 buffer of at least
  *                   16 * 4096 * 4 entries; for each workgroup g and wave w,
@@ -311,17 +312,26 @@ dash_status dash_attn_bwd_status(const void* workspace, void* stream);
  *                   timer reads the clock between phases, which itself waits
  *                   for outstanding LDS accesses, so the launch runs slower
  *                   than without it; shares, not times, are the result.
- *                   Same size limit as wait_stats.  With layout 1 every one
+ *                   Same size limit as wait_stats.  With layout 1 or 2
+ *                   (also when layout 0 picks the pipeline) every one
  *                   of the 8 waves of a workgroup g writes entries
  *                   [(g*8 + v)*16 + k]: k = 0..8 its phases (the kernel
  *                   source lists them per role), k = 14 its role (1 or 2),
  *                   k = 15 its whole run.
- *   layout          0 = the default backward kernel; 1 = the wave-pair
- *                   layout (bf16, d = 128 only; two waves per SIMD, each KV
+ *   layout          which backward kernel runs; results are bit-identical
+ *                   for every value (the ATOMIC schedule's unordered adds
+ *                   aside).  0 = automatic: the two-stage pipeline for bf16
+ *                   with d = 128, the one-stage kernel otherwise;
+ *                   1 = the wave-pair layout (two waves per SIMD, each KV
  *                   slice split between a wave for S, P, dV and the dQ
- *                   product and a wave for dP, dS, dK and the ordered add).
- *                   Results are bit-identical for both.  1 with another
- *                   dtype or head dim: DASH_ERR_UNSUPPORTED; other values:
+ *                   product and a wave for dP, dS, dK and the ordered add);
+ *                   2 = the two-stage pipeline (per SIMD, one wave computes
+ *                   S, dP, P, dS and dV of a Q sub-tile while another
+ *                   computes dK, dQ and the ordered dQ add of the sub-tile
+ *                   before it); 3 = the one-stage kernel (one wave per KV
+ *                   slice does every product of a sub-tile).  1 and 2 exist
+ *                   for bf16 with d = 128 only: another dtype or head dim
+ *                   gives DASH_ERR_UNSUPPORTED; other values:
  *                   DASH_ERR_INVALID_ARG.
  */
 typedef struct {
@@ -399,10 +409,10 @@ dash_status dash_attn_bwd_predict(const dash_attn_desc* desc, dash_schedule sche
  * user picks by hardware and model configuration; this makes that pick from
  * the DAG model).  Predicts the makespan of NAIVE, DESCENDING and SHIFT
  * (the full or causal mask of n tiles) for `heads` heads on `slots` workgroups and the
- * cost model `cost` (NULL: the library's default {1, 0.5, 0.05, 0.05} in
- * units of one unmasked item: the dQ add and the hand-off are short next to
- * an item because the kernel overlaps the add with the next item's
- * compute), and returns the one
+ * cost model `cost` (NULL: the one-stage kernel's default {1, 0.5, 0.05,
+ * 0.05} in units of one unmasked item: the dQ add and the hand-off are short
+ * next to an item because the kernel overlaps the add with the next item's
+ * compute; dash_attn_bwd_costs gives the costs a launch uses), and returns the one
  * with the smallest makespan (ties: SHIFT, then DESCENDING, then NAIVE).
  * (DASH_SCHED_AUTO in dash_attn_bwd makes the same choice with each
  * candidate predicted under the launch's placement, dash_attn_bwd_predict.)
@@ -459,8 +469,11 @@ dash_status dash_attn_bwd_calibrate(const dash_attn_desc* desc, const void* q, c
 
 /*
  * The costs DASH_SCHED_AUTO uses on the current device for the
- * descriptor's dtype and head dimension: {1, 0.5, 0.05, 0.05} until
- * dash_attn_bwd_calibrate fitted others.  Queries the current device only.
+ * descriptor's dtype and head dimension until dash_attn_bwd_calibrate fits
+ * others: {1, 0.5, 0.3, 0.3} for bf16 with d = 128 (the two-stage pipeline,
+ * which overlaps the products so that the ordered adds weigh more), else
+ * {1, 0.5, 0.05, 0.05} (the one-stage kernel).  Queries the current device
+ * only.
  */
 dash_status dash_attn_bwd_costs(const dash_attn_desc* desc, double cost_out[4]);
 
@@ -484,8 +497,10 @@ dash_status dash_schedule_fit_costs(const dash_attn_desc* desc, int32_t slots,
 
 /*
  * The schedule dash_attn_bwd runs for `schedule` on the current device:
- * DASH_SCHED_AUTO resolves to dash_schedule_choose's pick for the
- * problem's tile count, B*H heads and the launch's co-resident workgroups;
+ * DASH_SCHED_AUTO resolves to the DAG model's pick (as dash_schedule_choose,
+ * each candidate predicted under the launch's placement with the costs
+ * dash_attn_bwd_costs reports) for the problem's mask, B*H heads and the
+ * launch's co-resident workgroups, or to dash_attn_bwd_tune's measured pick;
  * other schedules come back unchanged.  Queries the device (occupancy),
  * launches nothing.  Errors as dash_attn_bwd's argument checks.
  */

@@ -20,10 +20,17 @@ def _free_bytes():
 
 def test_first_seen_shapes_allocate_no_device_memory():
     require_gpu()
-    # load the kernels once (code-object loading is the runtime's, not ours)
-    dev, _ = device_inputs(1, 2, 512, 128, "bf16", 3100)
-    o, lse = D.attn_fwd(dev["q"], dev["k"], dev["v"], causal=True)
-    D.backward(dev["q"], dev["k"], dev["v"], o, dev["do"], lse, schedule="shift", causal=True)
+    # load every kernel the cases run once (code-object loading and the
+    # scratch a kernel's first launch sets up are the runtime's, not ours):
+    # d = 128 runs the two-stage pipeline, d = 64 the one-stage kernel, each
+    # with and without masked pairs, ordered and atomic
+    for d in (64, 128):
+        dev, _ = device_inputs(1, 2, 512, d, "bf16", 3100)
+        for causal in (True, False):
+            o, lse = D.attn_fwd(dev["q"], dev["k"], dev["v"], causal=causal)
+            for sched in ("shift", "atomic"):
+                D.backward(dev["q"], dev["k"], dev["v"], o, dev["do"], lse, schedule=sched,
+                           causal=causal)
     torch.cuda.synchronize()
     block = np.random.default_rng(5).random((6, 6)) < 0.5
     cases = [dict(causal=True), dict(causal=False), dict(causal=True, window=300),

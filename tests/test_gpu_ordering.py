@@ -239,10 +239,23 @@ def test_auto_runs_its_resolved_schedule(shape, causal):
     assert picked in ORDERED
     for s in ORDERED + ["atomic"]:
         assert D.resolve_schedule(B, H, N, d, "bf16", causal, s) == s
-    n = N // D.tile(B, H, N, d, "bf16")
     cus = torch.cuda.get_device_properties(0).multi_processor_count
-    # one or two workgroups per compute unit, by the kernel's occupancy
-    assert picked in {D.schedule_choose(n, causal, B * H, k * cus)[0] for k in (1, 2)}
+    # the DAG model's pick under the costs the library uses for this dtype
+    # and head dim, on one or two workgroups per compute unit (the kernel's
+    # occupancy); ties go to shift, then descending
+    cost = D.bwd_costs(B, H, N, d, "bf16", causal)
+    picks = set()
+    for k in (1, 2):
+        pred = {}
+        for s in ORDERED:
+            try:
+                pred[s] = D.bwd_predict(B, H, N, d, "bf16", causal, s, slots=k * cus,
+                                        cost=cost)[0][0]
+            except D.DashError as e:  # a schedule that cannot run (causal shift, odd n)
+                assert e.code == 2 and s == "shift", (s, e.code)
+        best = min(pred.values())
+        picks.add([s for s in reversed(ORDERED) if pred.get(s) == best][0])
+    assert picked in picks
     dev, lse, delta = _prep(B, H, N, d, "bf16", causal, 8200)
     ref = _bwd(dev, lse, delta, picked, causal)
     for _ in range(3):
@@ -297,7 +310,8 @@ def test_phase_timer_changes_no_bit(causal):
     for sched in ORDERED + ["atomic"]:
         ws = D.alloc_workspace(dev["q"], causal, sched)
         st = torch.zeros(16 * 4096 * 4, dtype=torch.int64, device="cuda")
-        timed = _bwd(dev, lse, delta, sched, causal, ws, debug={"phase_stats": st})
+        # the one-stage kernel's phases (the pipeline's have their own test)
+        timed = _bwd(dev, lse, delta, sched, causal, ws, debug={"layout": 3, "phase_stats": st})
         D.attn_bwd_status(ws)
         a = st.view(-1, 16).cpu().numpy()
         a = a[a[:, 15] > 0]
@@ -307,7 +321,7 @@ def test_phase_timer_changes_no_bit(causal):
         ran = a[:, :11].sum(axis=1) > 0
         assert ran.any() and (a[ran, 1] > 0).all() and (a[ran, 4] > 0).all()
         if sched != "atomic":
-            plain = _bwd(dev, lse, delta, sched, causal, ws)
+            plain = _bwd(dev, lse, delta, sched, causal, ws, debug={"layout": 3})
             for x, y in zip(timed, plain):
                 assert torch.equal(x.view(torch.int16), y.view(torch.int16)), sched
         log(f"  {sched}: {len(a)} waves, ordered-add share "
