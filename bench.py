@@ -37,8 +37,6 @@ sys.path.insert(0, ROOT)
 
 METRIC = "deterministic attn-bwd TFLOP/s + % bf16 MFMA peak; det/non-det throughput ratio"
 PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}   # MI355X dense MFMA (bf16), fp32 MFMA
-# the library's default DAG costs: full item, partial item, dQ add, hand-off
-DAG_COST = (1.0, 0.5, 0.05, 0.05)
 def kernel_source_hash() -> str:
     """Hash of the backward kernel's sources and build flags, as recorded in
     the committed traffic summaries."""
@@ -170,11 +168,13 @@ def dag_prediction(D, w, causal, sched, mkw, coresident):
     schedule's units fit one, the library's unit order): predicted makespan
     and its lower bound in units of one full item, for one group's share,
     and the predicted share of slot time spent waiting for ordered-add
-    turns, with the library's default costs (full item 1, partial item 0.5,
-    dQ add 0.05, hand-off 0.05).  None if the launch cannot run it."""
+    turns, with the costs the library's "auto" uses for this dtype and head
+    dim (dash_attn_bwd_costs: full item, partial item, dQ add, hand-off).
+    None if the launch cannot run it."""
     try:
+        cost = D.bwd_costs(w.B, w.H, w.N, w.d, w.dtype, causal)
         (mk, wait, _, lb), info = D.bwd_predict(w.B, w.H, w.N, w.d, w.dtype, causal, sched,
-                                                slots=coresident, cost=DAG_COST, **mkw)
+                                                slots=coresident, cost=cost, **mkw)
     except D.DashError:
         return None
     slots = info["slots"]
@@ -426,7 +426,7 @@ def main():
                        "traffic": traffic,
                        "hbm_GBps": (round(traffic / (prim["kernel_ms"] * 1e-3) / 1e9, 1)
                                     if traffic else None),
-                       "kernel": f"bwd_kernel ({ran})"}
+                       "kernel": f"{'bwd_pipe_kernel' if kind == 'pipe' else 'bwd_kernel'} ({ran})"}
     if fwd_stats:
         out.update(fwd_stats)
     if tuned:

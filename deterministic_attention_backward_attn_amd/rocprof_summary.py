@@ -8,7 +8,7 @@
   python -m deterministic_attention_backward_attn_amd.rocprof_summary traffic \\
       --fetch-csv <dir>/<prefix>_counter_collection.csv \\
       --write-csv <dir>/<prefix>_counter_collection.csv \\
-      --copy-bytes N --kernel bwd_kernel --flops F [--dispatches A:B] \\
+      --copy-bytes N [--kernel NAME|NAME] --flops F [--dispatches A:B] \\
       --cmd-fetch "<command>" --cmd-write "<command>" --out profiles/<name>.md
 
 With --trace, the backward kernel's dispatches (in dispatch order) are cut
@@ -51,11 +51,20 @@ import statistics
 import sys
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
-# every source the backward kernel's translation unit includes
+# every source of the backward kernels' translation units (the one-stage
+# kernel and the two-stage pipeline that bf16 with d = 128 runs) and what
+# they include
 KERNEL_SOURCES = ["deterministic_attention_backward_attn_amd/csrc/kernels/attn_bwd.hip",
+                  "deterministic_attention_backward_attn_amd/csrc/kernels/attn_bwd_pipe.hip",
                   "deterministic_attention_backward_attn_amd/csrc/kernels/common.hpp",
                   "deterministic_attention_backward_attn_amd/csrc/kernels/launch.hpp",
                   "deterministic_attention_backward_attn_amd/csrc/kernels/placement.hpp"]
+# names of the backward kernels' dispatches
+BWD_KERNELS = ("bwd_kernel", "bwd_pipe_kernel", "bwd_pair_kernel")
+
+
+def is_bwd(name: str) -> bool:
+    return any(k in name for k in BWD_KERNELS)
 
 
 def kernel_source_hash() -> str:
@@ -65,7 +74,8 @@ def kernel_source_hash() -> str:
     for rel in KERNEL_SOURCES:
         with open(os.path.join(ROOT, rel), "rb") as f:
             h.update(f.read())
-    h.update(" ".join(B.DEVICE + B.PER_FILE.get("kernels/attn_bwd.hip", [])).encode())
+    h.update(" ".join(B.DEVICE + B.PER_FILE.get("kernels/attn_bwd.hip", [])
+                      + B.PER_FILE.get("kernels/attn_bwd_pipe.hip", [])).encode())
     return h.hexdigest()[:16]
 
 
@@ -86,7 +96,7 @@ def stats(args):
     if args.trace:
         rows = sorted(csv.DictReader(open(args.trace)), key=lambda r: int(r["Dispatch_Id"]))
         bwd = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3
-               for r in rows if "bwd_kernel" in r["Kernel_Name"]]
+               for r in rows if is_bwd(r["Kernel_Name"])]
         names = [b for b in args.blocks.split(",") if b]
         if len(bwd) != len(names) * args.block_size:
             raise SystemExit(f"{len(bwd)} backward dispatches, expected "
@@ -131,7 +141,7 @@ def traffic(args):
     f_fac = known_kib / copy_kib(fetch)
     w_fac = known_kib / copy_kib(write)
     def pick(d, i):
-        vals = [d[k][i] for k in sorted(d) if args.kernel in d[k][0]]
+        vals = [d[k][i] for k in sorted(d) if any(n in d[k][0] for n in args.kernel.split("|"))]
         if args.dispatches:
             a, b = (int(x) for x in args.dispatches.split(":"))
             vals = vals[a:b]
@@ -228,8 +238,12 @@ def phases(args):
     for n in names:
         lines.append(f"| {n} | " + " | ".join(f"{run['schedules'][s]['phases'][n]:.3f}"
                                               for s in scheds) + " |")
-    lines.append("| sum | " + " | ".join(f"{sum(run['schedules'][s]['phases'].values()):.3f}"
-                                        for s in scheds) + " |")
+    # the 8-wave layouts time each role's waves separately ("A: ...", "B: ...")
+    groups = sorted({n.split(": ")[0] for n in names if ": " in n}) or [None]
+    for g in groups:
+        keys = [n for n in names if g is None or n.startswith(g + ": ")]
+        lines.append(f"| sum{'' if g is None else ' ' + g} | " + " | ".join(
+            f"{sum(run['schedules'][s]['phases'][k] for k in keys):.3f}" for s in scheds) + " |")
     lines.append("| kernel ms (timed launches, no timer) | " + " | ".join(
         f"{run['schedules'][s]['kernel_ms']:.3f}" for s in scheds) + " |")
     lines += ["", f"kernel_source_sha256: {kernel_source_hash()}", ""]
@@ -256,14 +270,14 @@ def main(argv=None):
     c.add_argument("--csv", required=True)
     c.add_argument("--cmd", required=True)
     c.add_argument("--out")
-    c.add_argument("--kernel", default="bwd_kernel")
+    c.add_argument("--kernel", default="|".join(BWD_KERNELS))
     c.add_argument("--blocks", default="atomic,descending")
     c.add_argument("--block-size", type=int, default=3)
     t = sub.add_parser("traffic")
     t.add_argument("--fetch-csv", required=True)
     t.add_argument("--write-csv", required=True)
     t.add_argument("--copy-bytes", type=int, required=True)
-    t.add_argument("--kernel", default="bwd_kernel")
+    t.add_argument("--kernel", default="|".join(BWD_KERNELS))
     t.add_argument("--flops", type=float, default=0.0)
     t.add_argument("--dispatches", default="",
                    help="a:b = only the backward dispatches a..b-1 (dispatch order), e.g. one "
