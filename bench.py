@@ -162,17 +162,19 @@ def phase_shares(D, dev, lse, delta, sched, causal, ws, out, mkw, lay=None, kind
     return res
 
 
-def dag_prediction(D, w, causal, sched, mkw, coresident):
+def dag_prediction(D, w, causal, sched, mkw, coresident, cost=None):
     """The host DAG model's view of one ordered schedule on this workload, as
     the launch places it (dash_attn_bwd_predict: XCD groups when the
     schedule's units fit one, the library's unit order): predicted makespan
     and its lower bound in units of one full item, for one group's share,
     and the predicted share of slot time spent waiting for ordered-add
-    turns, with the costs the library's "auto" uses for this dtype and head
-    dim (dash_attn_bwd_costs: full item, partial item, dQ add, hand-off).
-    None if the launch cannot run it."""
+    turns, with `cost` (full item, partial item, dQ add, hand-off), by
+    default the costs the library's "auto" uses for this dtype and head dim
+    (dash_attn_bwd_costs, a device query).  None if the launch cannot run
+    it."""
     try:
-        cost = D.bwd_costs(w.B, w.H, w.N, w.d, w.dtype, causal)
+        if cost is None:
+            cost = D.bwd_costs(w.B, w.H, w.N, w.d, w.dtype, causal)
         (mk, wait, _, lb), info = D.bwd_predict(w.B, w.H, w.N, w.d, w.dtype, causal, sched,
                                                 slots=coresident, cost=cost, **mkw)
     except D.DashError:

@@ -316,12 +316,13 @@ def test_noalloc_refusals_happen_before_any_device_call():
 
 
 def test_profile_hash_covers_every_kernel_include():
-    """The freshness hash of the committed traffic summaries covers every
-    file the backward kernel's source includes from this package."""
+    """The freshness hash of the committed traffic summaries covers the
+    backward kernels' sources (the one-stage kernel and the two-stage
+    pipeline) and every file they include from this package."""
     import re
     from deterministic_attention_backward_attn_amd import rocprof_summary as RS
     kdir = "deterministic_attention_backward_attn_amd/csrc/kernels/"
-    seen, todo = set(), ["attn_bwd.hip"]
+    seen, todo = set(), ["attn_bwd.hip", "attn_bwd_pipe.hip"]
     while todo:
         f = todo.pop()
         if f in seen:

@@ -7,6 +7,8 @@ exactly; SHIFT (the timed shift) exactly against the oracle's own timed
 shift and against the timing certificate; the DAG prediction on the
 library's own tables against the oracle's DAG.
 """
+import itertools
+
 import numpy as np
 import pytest
 
@@ -283,10 +285,13 @@ def test_bench_dag_prediction_on_the_plain_workloads():
     a group (32 at 4K full, 64 at 16K causal: device-wide)."""
     import bench
     from synth import WORKLOADS
-    for name in ("b1h32_n16k_d128_causal", "b4h32_n4k_d128_full", "b2h16_n2k_d128_causal"):
+    # the default costs of the one-stage kernel and of the two-stage pipeline
+    for name, cost in itertools.product(
+            ("b1h32_n16k_d128_causal", "b4h32_n4k_d128_full", "b2h16_n2k_d128_causal"),
+            ((1.0, 0.5, 0.05, 0.05), (1.0, 0.5, 0.3, 0.3))):
         w = WORKLOADS[name]
         causal = w.masks[0] == "causal"
-        pred = {s: bench.dag_prediction(D, w, causal, s, w.mask_args(), 256)
+        pred = {s: bench.dag_prediction(D, w, causal, s, w.mask_args(), 256, cost)
                 for s in ("naive", "descending", "shift")}
         for p in pred.values():
             assert p is not None
