@@ -47,6 +47,34 @@
 
 namespace dash {
 
+// Direct global -> LDS loads (lane i of a 16-byte load writes LDS bytes
+// [16 i, 16 i + 16) above the LDS address in M0, of a 4-byte load [4 i,
+// 4 i + 4)), written as assembly so that the compiler neither counts them in
+// its own waits nor makes later reads of other LDS buffers wait for them:
+// the caller waits for them (vmcnt) before the barrier after which they are
+// read.  No register receives data; the leading no-ops cover a scalar
+// operand written by a vector instruction just before.  M0 is written here
+// and used by no other instruction of this kernel.
+__device__ __forceinline__ uint32_t lds_offset(const void* p) { return (uint32_t)(uintptr_t)p; }
+__device__ __forceinline__ void dma_b128(const void* gbase, uint32_t voff, const void* lds) {
+  // the base address and the LDS address are the same in every lane
+  // (readfirstlane returns a signed int: widen through uint32_t, never
+  // sign-extend the low half)
+  const uint64_t b = (uint64_t)(uintptr_t)gbase;
+  const uint32_t lo = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)b);
+  const uint32_t hi = (uint32_t)__builtin_amdgcn_readfirstlane((int)(uint32_t)(b >> 32));
+  const uint64_t bs = ((uint64_t)hi << 32) | (uint64_t)lo;
+  const uint32_t ls = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_offset(lds));
+  asm volatile(
+      "s_nop 4\n\ts_mov_b32 m0, %2\n\ts_nop 4\n\tglobal_load_lds_dwordx4 %0, %1"
+      :: "v"(voff), "s"(bs), "s"(ls) : "memory", "m0");
+}
+__device__ __forceinline__ void dma_b32(const void* gaddr, const void* lds) {
+  const uint32_t ls = (uint32_t)__builtin_amdgcn_readfirstlane((int)lds_offset(lds));
+  asm volatile("s_nop 4\n\ts_mov_b32 m0, %1\n\ts_nop 4\n\tglobal_load_lds_dword %0, off"
+               :: "v"(gaddr), "s"(ls) : "memory", "m0");
+}
+
 template <bool MASKED, bool ORDERED, bool DEBUG>
 __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
   using T = bf16_t;
@@ -66,15 +94,16 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
   constexpr int CPT = BR * D / VEC / NA;  // 16-byte chunks per A thread per tensor (2)
   static_assert(CPT * VEC * NA == BR * D, "sub-tile load must split evenly");
 
-  // Q / dO / LSE / delta sub-tiles: sub-tile g in buffer g % 3 (A reads t,
-  // B reads t - 1, A stages t + 1).  dS^T of sub-tile g in buffer g % 2
-  // (A writes t, B reads t - 1).
-  __shared__ __align__(16) T sQ[3][BR * LQ];
-  __shared__ __align__(16) T sdO[3][BR * LQ];
+  // Q / dO / LSE / delta sub-tiles: sub-tile g in buffer g % 4 (A reads t,
+  // B reads t - 1, the loads of t + 1 and t + 2 in flight).  dS^T of
+  // sub-tile g in buffer g % 2 (A writes t, B reads t - 1).
+  constexpr int NQB = 4;
+  __shared__ __align__(16) T sQ[NQB][BR * LQ];
+  __shared__ __align__(16) T sdO[NQB][BR * LQ];
   __shared__ __align__(16) T sdSt[2][BC * LS];
   __shared__ __align__(16) T sK[BC * LQ];
   // LSE (unscaled) in [0, BR), delta in [BR, 2 BR) of each buffer
-  __shared__ __align__(16) float sStat[3][2 * BR];
+  __shared__ __align__(16) float sStat[NQB][2 * BR];
   __shared__ int2 sItems[kMaxUnitItems];
   constexpr int LR = 32;
   __shared__ __align__(16) float sRow[ORDERED ? NW : 1][ORDERED ? 32 * LR : 4];
@@ -186,14 +215,21 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
         const float* stat_src = lane < BR ? lse_g + lane : del_g + (lane - BR);
         auto dma = [&](int g, int buf) {
           const int q0 = qtile_of(g) * BR;
+          const T* qs = Qg + (size_t)q0 * D;
+          const T* os = dOg + (size_t)q0 * D;
 #pragma unroll
           for (int m = 0; m < 2; ++m) {
-            __builtin_amdgcn_global_load_lds(Qg + (size_t)q0 * D + doff[m],
-                                             &sQ[buf][(8 * wu + 4 * m) * LQ], 16, 0, 0);
-            __builtin_amdgcn_global_load_lds(dOg + (size_t)q0 * D + doff[m],
-                                             &sdO[buf][(8 * wu + 4 * m) * LQ], 16, 0, 0);
+            dma_b128(qs, doff[m] * (uint32_t)sizeof(T), &sQ[buf][(8 * wu + 4 * m) * LQ]);
+            dma_b128(os, doff[m] * (uint32_t)sizeof(T), &sdO[buf][(8 * wu + 4 * m) * LQ]);
           }
-          if (wu == 0) __builtin_amdgcn_global_load_lds(stat_src + q0, &sStat[buf][0], 4, 0, 0);
+          if (wu == 0) dma_b32(stat_src + q0, &sStat[buf][0]);
+        };
+        // Wait for this wave's loads of the sub-tile read after the next
+        // barrier: only the loads issued after them (4 or 5 when sub-tile
+        // t + 2 was staged this period) may stay in flight.
+        auto wait_staged = [&](bool newer) {
+          if (newer) __builtin_amdgcn_s_waitcnt(0x0F74);  // vmcnt(4)
+          else __builtin_amdgcn_s_waitcnt(0x0F70);        // vmcnt(0)
         };
         frag Kreg[DK], Vreg[DK];
         f32x16 accdV[NTD];
@@ -208,16 +244,14 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
                   E::from_f32(accdV[nt][r]);
         };
         if (n_steps > 0) dma(0, 0);
+        if (n_steps > 1) dma(1, 1);
+        wait_staged(n_steps > 1);
         __syncthreads();  // sub-tile 0 in LDS
 
         for (int t = 0; t <= n_steps; ++t) {
           PHASE(4);
-          // Nothing of this stage is in flight here (the barrier waited for
-          // the sub-tile loads); saying so keeps the compiler from waiting
-          // on the next loads for a value it last loaded before the loop.
-          __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
           if (t < n_steps) {
-            const int b3 = t % 3;
+            const int b3 = t % NQB;
             const int b2 = t & 1;
             const int2 itm = sItems[t / RHO];
             const int kv = itm.x & 0xFFFF;
@@ -249,9 +283,9 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
               // after it
               __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
             }
-            // sub-tile t + 1 into its buffer (its previous contents, sub-tile
+            // sub-tile t + 2 into its buffer (its previous contents, sub-tile
             // t - 2, were last read by stage B in the previous period)
-            if (t + 1 < n_steps) dma(t + 1, (t + 1) % 3);
+            if (t + 2 < n_steps) dma(t + 2, (t + 2) % NQB);
             PHASE(0);
             const T* cQ = sQ[b3];
             const T* cdO = sdO[b3];
@@ -332,6 +366,8 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
             __builtin_amdgcn_sched_barrier(0);
             PHASE(3);
           }
+          // sub-tile t + 1 complete in LDS (every A wave its part)
+          wait_staged(t + 2 < n_steps);
           __syncthreads();  // end of period t
         }
         if (a_kv >= 0) flush_dv();
@@ -430,7 +466,7 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
           PHASE(6);
           {
             const int g = t - 1;
-            const int b3 = g % 3;
+            const int b3 = g % NQB;
             const int b2 = g & 1;
             const int2 itm = sItems[g / RHO];
             const int kv = itm.x & 0xFFFF;
