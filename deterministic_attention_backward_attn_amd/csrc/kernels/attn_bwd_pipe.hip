@@ -558,19 +558,54 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
               for (int gq = 0; gq < 4; ++gq)
                 *reinterpret_cast<f32x4*>(&row[rix(l32, 8 * gq + 4 * hh)]) =
                     f32x4{accQ[4 * gq], accQ[4 * gq + 1], accQ[4 * gq + 2], accQ[4 * gq + 3]};
+              typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+              if constexpr (!XL) {
+                // device-coherent accumulator: all four sums first, then
+                // four stores from their own registers (rewriting a store's
+                // data registers waits for the store), either the
+                // accumulator or (the last contributor, a uniform branch)
+                // the scaled dQ in the output dtype; four stores either
+                // way, so the waits after them count the same operations
+                f32x4 v[4];
 #pragma unroll
-              for (int gq = 0; gq < 4; ++gq) {
-                f32x4 v = *reinterpret_cast<const f32x4*>(&row[rix((lane >> 3) + 8 * gq, 4 * (lane & 7))]);
-                if (rank > 0) v = lv[gq] + v;
-                const uint32_t off = chunk_off(q0, gq);
-                // both stores issued, the one not wanted out of range: the
-                // accumulator (not last) or the scaled bf16 dQ (last)
-                const f32x4 vs = v * a.scale;
-                coherent_store4<POL>(dq_rs, last ? kOutOfRange : 4 * off, v);
-                typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-                __builtin_amdgcn_raw_buffer_store_b64(
-                    u32x2{pack2_bf16(vs[0], vs[1]), pack2_bf16(vs[2], vs[3])}, dqo_rs,
-                    last ? 2 * off : kOutOfRange, 0, 0);
+                for (int gq = 0; gq < 4; ++gq) {
+                  v[gq] = *reinterpret_cast<const f32x4*>(&row[rix((lane >> 3) + 8 * gq, 4 * (lane & 7))]);
+                  if (rank > 0) v[gq] = lv[gq] + v[gq];
+                }
+                if (!last) {
+                  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                  for (int gq = 0; gq < 4; ++gq) coherent_store4<POL>(dq_rs, 4 * chunk_off(q0, gq), v[gq]);
+                  __builtin_amdgcn_sched_barrier(0);
+                } else {
+                  u32x2 pk[4];
+#pragma unroll
+                  for (int gq = 0; gq < 4; ++gq) {
+                    const f32x4 vs = v[gq] * a.scale;
+                    pk[gq] = u32x2{pack2_bf16(vs[0], vs[1]), pack2_bf16(vs[2], vs[3])};
+                  }
+                  __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+                  for (int gq = 0; gq < 4; ++gq)
+                    __builtin_amdgcn_raw_buffer_store_b64(pk[gq], dqo_rs, 2 * chunk_off(q0, gq), 0, 0);
+                  __builtin_amdgcn_sched_barrier(0);
+                }
+              } else {
+                // L2-coherent accumulator (XCD groups): both stores issued
+                // every period, the one not wanted out of range (the
+                // branch above measured slower here for naive and
+                // descending under the causal mask)
+#pragma unroll
+                for (int gq = 0; gq < 4; ++gq) {
+                  f32x4 v = *reinterpret_cast<const f32x4*>(&row[rix((lane >> 3) + 8 * gq, 4 * (lane & 7))]);
+                  if (rank > 0) v = lv[gq] + v;
+                  const uint32_t off = chunk_off(q0, gq);
+                  const f32x4 vs = v * a.scale;
+                  coherent_store4<POL>(dq_rs, last ? kOutOfRange : 4 * off, v);
+                  __builtin_amdgcn_raw_buffer_store_b64(
+                      u32x2{pack2_bf16(vs[0], vs[1]), pack2_bf16(vs[2], vs[3])}, dqo_rs,
+                      last ? 2 * off : kOutOfRange, 0, 0);
+                }
               }
               if (!last) {
                 rel_pending = true;
