@@ -286,7 +286,12 @@ __global__ void __launch_bounds__(NW * 64, QN == 1 ? 8 / NW : 1) fwd_bf16_kernel
     j_lo = k_min > 0 ? k_min / BN : 0;
     j_hi = k_max < N - 1 ? k_max / BN + 1 : N / BN;
   }
+  // Without a block mask every key tile in [j_lo, j_hi) is needed by some
+  // row of the workgroup (each row sees one contiguous key range, and the
+  // ranges of consecutive rows overlap or adjoin), so the next tile is the
+  // following one; a block mask needs the search.
   const auto next_tile = [&](int j) {
+    if (!(MASKED && a.live)) return j + 1 < j_hi ? j + 1 : j_hi;
     for (++j; j < j_hi; ++j)
       if (need_any(j)) return j;
     return j_hi;
