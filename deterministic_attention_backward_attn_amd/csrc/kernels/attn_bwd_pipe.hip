@@ -75,6 +75,25 @@ __device__ __forceinline__ void dma_b32(const void* gaddr, const void* lds) {
                :: "v"(gaddr), "s"(ls) : "memory", "m0");
 }
 
+// `p` advanced by `bytes`
+template <typename P>
+__device__ __forceinline__ P* at(P* p, uint32_t bytes) {
+  return reinterpret_cast<P*>(reinterpret_cast<char*>(const_cast<void*>(static_cast<const void*>(p))) + bytes);
+}
+// Transposing fragment read (as tr_frag) from two given addresses: K slots
+// 0..3 from `pa`, 4..7 from `pb`.
+__device__ __forceinline__ bf16x8 tr_frag_at(const bf16_t* pa, const bf16_t* pb) {
+  const u16x4 x = lds_tr16(pa);
+  const u16x4 y = lds_tr16(pb);
+  u16x8 u;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    u[s] = x[s];
+    u[s + 4] = y[s];
+  }
+  return __builtin_bit_cast(bf16x8, u);
+}
+
 template <bool MASKED, bool ORDERED, bool DEBUG>
 __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
   using T = bf16_t;
@@ -98,17 +117,35 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
   // B reads t - 1, the loads of t + 1 and t + 2 in flight).  dS^T of
   // sub-tile g in buffer g % 2 (A writes t, B reads t - 1).
   constexpr int NQB = 4;
-  __shared__ __align__(16) T sQ[NQB][BR * LQ];
-  __shared__ __align__(16) T sdO[NQB][BR * LQ];
-  __shared__ __align__(16) T sdSt[2][BC * LS];
-  __shared__ __align__(16) T sK[BC * LQ];
-  // LSE (unscaled) in [0, BR), delta in [BR, 2 BR) of each buffer
-  __shared__ __align__(16) float sStat[NQB][2 * BR];
-  __shared__ int2 sItems[kMaxUnitItems];
   constexpr int LR = 32;
-  __shared__ __align__(16) float sRow[ORDERED ? NW : 1][ORDERED ? 32 * LR : 4];
-  __shared__ int sUnit;
-  __shared__ int sPlace[5];
+  // One LDS block, so that the layout is fixed: a dO buffer lies 32 KB
+  // after the Q buffer of the same index, a distance the LDS instructions
+  // take as an immediate offset (one address register per Q/dO pair of
+  // operand reads).
+  struct __align__(16) Lds {
+    T q[NQB][BR * LQ];
+    T dO[NQB][BR * LQ];
+    T dSt[2][BC * LS];
+    T k[BC * LQ];
+    // LSE (unscaled) in [0, BR), delta in [BR, 2 BR) of each buffer
+    float stat[NQB][2 * BR];
+    float row[ORDERED ? NW : 1][ORDERED ? 32 * LR : 4];
+    int2 items[kMaxUnitItems];
+    int unit;
+    int place[5];
+  };
+  __shared__ Lds L;
+  auto& sQ = L.q;
+  auto& sdO = L.dO;
+  auto& sdSt = L.dSt;
+  auto& sK = L.k;
+  auto& sStat = L.stat;
+  auto& sItems = L.items;
+  auto& sRow = L.row;
+  auto& sUnit = L.unit;
+  auto& sPlace = L.place;
+  // a dO buffer lies this many bytes after the Q buffer of the same index
+  constexpr uint32_t kQtoDO = (uint32_t)(offsetof(Lds, dO) - offsetof(Lds, q));
   const auto qix = [](int r, int c) { return r * LQ + (((c >> 3) ^ swz<D>(r)) << 3) + (c & 7); };
   const auto six = [](int r, int c) { return r * LS + c; };
   const auto rix = [](int r, int c) { return r * LR + (((c >> 2) ^ ((r >> 1) & 7)) << 2) + (c & 3); };
@@ -157,6 +194,20 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
   const int stride_static = grouped ? (W / U) * U : a.p_eff;
   uint32_t* work_counter = grouped ? &a.header[20 + grp] : &a.header[1];
   const int unit0 = (a.dynamic == 0 && li >= stride_static) ? n_units : li;
+
+  // Per-lane byte offsets of the transposing reads of a Q or dO sub-tile
+  // (rows 4 hh + 8 h + j16 / 4, columns 32 nt + gcol + 4 (j16 % 4)); rows
+  // 16 further lie 16 LQ elements further (the swizzle repeats every 16
+  // rows), a constant offset.
+  uint32_t oT[2][NTD];
+#pragma unroll
+  for (int h = 0; h < 2; ++h)
+#pragma unroll
+    for (int nt = 0; nt < NTD; ++nt)
+      oT[h][nt] = (uint32_t)(2 * qix(4 * hh + 8 * h + (j16 >> 2), nt * 32 + gcol + 4 * (j16 & 3)));
+  const auto tr_sub = [&](const T* base, int cc, int nt) {
+    return tr_frag_at(at(base, oT[0][nt] + 2 * 16 * cc * LQ), at(base, oT[1][nt] + 2 * 16 * cc * LQ));
+  };
 
   // One copy of the unit loop per stage, so that each stage's registers are
   // allocated for its own values only; both copies pass the same barriers
@@ -299,7 +350,7 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
               for (int k2 = 0; k2 < DK / 2; ++k2) {
                 const int off = qix(l32, (h2 * DK / 2 + k2) * KSTEP + hh * KPL);
                 qa[k2] = load_frag(&cQ[off]);
-                oa[k2] = load_frag(&cdO[off]);
+                oa[k2] = load_frag(at(&cQ[off], kQtoDO));
               }
               __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -354,7 +405,7 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
             for (int cc = 0; cc < 2; ++cc)
 #pragma unroll
               for (int nt = 0; nt < NTD; ++nt)
-                bo[cc][nt] = tr_frag(cdO, qix, 16 * cc + 4 * hh, 16 * cc + 4 * hh + 8, nt * 32 + gcol, j16);
+                bo[cc][nt] = tr_sub(cdO, cc, nt);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int cc = 0; cc < 2; ++cc) {
@@ -521,7 +572,7 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
               da[cc] = __builtin_bit_cast(bf16x8, make_uint4(d0.x, d0.y, d1.x, d1.y));
 #pragma unroll
               for (int nt = 0; nt < NTD; ++nt)
-                bq[cc][nt] = tr_frag(cQ, qix, r0, r0 + 8, nt * 32 + gcol, j16);
+                bq[cc][nt] = tr_sub(cQ, cc, nt);
             }
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -559,6 +610,9 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
                 *reinterpret_cast<f32x4*>(&row[rix(l32, 8 * gq + 4 * hh)]) =
                     f32x4{accQ[4 * gq], accQ[4 * gq + 1], accQ[4 * gq + 2], accQ[4 * gq + 3]};
               typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+              // The first contributor's accumulator values are zeros (its
+              // reads were out of range) and adding them changes no value:
+              // the partial is never -0, its MFMA sums starting from +0.
               if constexpr (!XL) {
                 // device-coherent accumulator: all four sums first, then
                 // four stores from their own registers (rewriting a store's
@@ -570,7 +624,7 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
 #pragma unroll
                 for (int gq = 0; gq < 4; ++gq) {
                   v[gq] = *reinterpret_cast<const f32x4*>(&row[rix((lane >> 3) + 8 * gq, 4 * (lane & 7))]);
-                  if (rank > 0) v[gq] = lv[gq] + v[gq];
+                  v[gq] = lv[gq] + v[gq];
                 }
                 if (!last) {
                   __builtin_amdgcn_sched_barrier(0);
@@ -598,7 +652,7 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
 #pragma unroll
                 for (int gq = 0; gq < 4; ++gq) {
                   f32x4 v = *reinterpret_cast<const f32x4*>(&row[rix((lane >> 3) + 8 * gq, 4 * (lane & 7))]);
-                  if (rank > 0) v = lv[gq] + v;
+                  v = lv[gq] + v;
                   const uint32_t off = chunk_off(q0, gq);
                   const f32x4 vs = v * a.scale;
                   coherent_store4<POL>(dq_rs, last ? kOutOfRange : 4 * off, v);
