@@ -310,7 +310,7 @@ float scale_of(const dash_attn_desc* d) {
 // units, one item per live pair), so the size is the same for every
 // schedule.
 struct WsLayout {
-  size_t counters_off, counters_words, unit_off_off, items_off, dead_off, acc_off, total;
+  size_t counters_off, counters_words, unit_off_off, items_off, dead_off, lse2_off, acc_off, total;
 };
 
 WsLayout layout(const dash_attn_desc* d, long live_pairs) {
@@ -324,7 +324,8 @@ WsLayout layout(const dash_attn_desc* d, long live_pairs) {
   w.unit_off_off = align256(w.counters_off + 4 * w.counters_words);
   w.items_off = align256(w.unit_off_off + 4 * (size_t)(n + 1));
   w.dead_off = align256(w.items_off + 8 * (size_t)std::max<long>(live_pairs, 1));
-  w.acc_off = align256(w.dead_off + 4 * (size_t)(2 * n));
+  w.lse2_off = align256(w.dead_off + 4 * (size_t)(2 * n));
+  w.acc_off = align256(w.lse2_off + 4 * heads * (size_t)d->N);
   w.total = w.acc_off + 4 * heads * (size_t)d->N * d->d;
   return w;
 }
@@ -766,6 +767,10 @@ dash_status run_bwd(const dash_attn_desc* desc, dash_schedule schedule, const vo
   pa.items = plain ? dash::plain::items(n, mkey.causal != 0) : 0;
   pa.unit_off = (int*)(ws + w.unit_off_off);
   pa.item = (int2*)(ws + w.items_off);
+  // the pipeline layout reads LSE * log2(e), one product per row
+  pa.lse = lse;
+  pa.lse2 = (float*)(ws + w.lse2_off);
+  pa.lse_count = pipe ? (size_t)heads * desc->N : 0;
   if (dash::launch_bwd_prologue(pa, strm) != hipSuccess) return DASH_ERR_HIP;
   if (!plain) {
     // special masks: the host-built tables, copied on the caller's stream
@@ -782,6 +787,7 @@ dash_status run_bwd(const dash_attn_desc* desc, dash_schedule schedule, const vo
   a.v = v;
   a.dout = dout;
   a.lse = lse;
+  a.lse2 = (const float*)(ws + w.lse2_off);
   a.delta = delta;
   a.dq = dq;
   a.dk = dk;

@@ -127,7 +127,7 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
     T dO[NQB][BR * LQ];
     T dSt[2][BC * LS];
     T k[BC * LQ];
-    // LSE (unscaled) in [0, BR), delta in [BR, 2 BR) of each buffer
+    // LSE * log2(e) in [0, BR), delta in [BR, 2 BR) of each buffer
     float stat[NQB][2 * BR];
     float row[ORDERED ? NW : 1][ORDERED ? 32 * LR : 4];
     int2 items[kMaxUnitItems];
@@ -208,6 +208,9 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
   const auto tr_sub = [&](const T* base, int cc, int nt) {
     return tr_frag_at(at(base, oT[0][nt] + 2 * 16 * cc * LQ), at(base, oT[1][nt] + 2 * 16 * cc * LQ));
   };
+  // ... and of dS^T (rows 8 hh + j16 / 4, columns gcol + 4 (j16 % 4)), the
+  // rows of KV step i and the second half's 4 rows a constant further
+  const uint32_t oF = (uint32_t)(2 * six(8 * hh + (j16 >> 2), gcol + 4 * (j16 & 3)));
 
   // One copy of the unit loop per stage, so that each stage's registers are
   // allocated for its own values only; both copies pass the same barriers
@@ -242,7 +245,7 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
         // ---------------------------------------------------------- stage A
         const T* Kg = reinterpret_cast<const T*>(a.k) + hoff;
         const T* Vg = reinterpret_cast<const T*>(a.v) + hoff;
-        const float* lse_g = a.lse + (size_t)head * N;
+        const float* lse_g = a.lse2 + (size_t)head * N;  // LSE * log2(e)
         const float* del_g = a.delta + (size_t)head * N;
         // Sub-tile g into buffer `buf` by direct loads to LDS (no registers:
         // lane i of a 16-byte load writes LDS bytes [16 i, 16 i + 16) of the
@@ -377,11 +380,11 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
               const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sStat[b3][BR + qb]);
               float p[4], ds[4];
               // exp2(s log2(e) S - log2(e) LSE): both products rounded to
-              // fp32 once, the first fused into the subtraction
+              // fp32 once (the second by the workspace prologue, once per
+              // row), the first fused into the subtraction
 #pragma unroll
               for (int e = 0; e < 4; ++e)
-                p[e] = __builtin_amdgcn_exp2f(
-                    __builtin_fmaf(accS[4 * gq + e], a.scale_log2, -__fmul_rn(l4[e], kLog2e)));
+                p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(accS[4 * gq + e], a.scale_log2, -l4[e]));
               if (emask) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -578,7 +581,7 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
 #pragma unroll
             for (int i = 0; i < KK; ++i) {
               accdK[i % NTD] = E::mma(da[i / NTD], bq[i / NTD][i % NTD], accdK[i % NTD]);
-              fa[i] = tr_frag(cdSt, six, i * 16 + 8 * hh, i * 16 + 8 * hh + 4, gcol, j16);
+              fa[i] = tr_frag_at(at(cdSt, oF + 2 * i * 16 * LS), at(cdSt, oF + 2 * (i * 16 + 4) * LS));
             }
             __builtin_amdgcn_sched_barrier(0);
             f32x16 accQ = zero16();

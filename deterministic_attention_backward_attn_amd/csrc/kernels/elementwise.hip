@@ -90,6 +90,7 @@ __global__ void __launch_bounds__(256) bwd_prologue_kernel(PrologueArgs a) {
   for (size_t i = t0; i < a.clear_words / 4; i += stride) c1[i] = make_uint4(0u, 0u, 0u, 0u);
   uint4* c2 = reinterpret_cast<uint4*>(a.clear2);
   for (size_t i = t0; i < a.clear2_words / 4; i += stride) c2[i] = make_uint4(0u, 0u, 0u, 0u);
+  for (size_t i = t0; i < a.lse_count; i += stride) a.lse2[i] = __fmul_rn(a.lse[i], kLog2e);
   if (a.n <= 0) return;
   const bool causal = a.causal != 0;
   for (size_t u = t0; u <= (size_t)a.units; u += stride)
@@ -104,6 +105,7 @@ hipError_t launch_bwd_prologue(const PrologueArgs& a, hipStream_t stream) {
   if (a.clear2_words / 4 > work) work = a.clear2_words / 4;
   if ((size_t)a.items > work) work = (size_t)a.items;
   if ((size_t)a.units + 1 > work) work = (size_t)a.units + 1;
+  if (a.lse_count > work) work = a.lse_count;
   size_t blocks = (work + 255) / 256;
   if (blocks > 8192) blocks = 8192;
   if (blocks == 0) blocks = 1;

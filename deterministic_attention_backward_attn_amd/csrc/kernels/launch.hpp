@@ -18,6 +18,7 @@ struct BwdArgs {
   const void* v;
   const void* dout;
   const float* lse;
+  const float* lse2;      // [BH, N] LSE * log2(e) (two-stage pipeline only)
   const float* delta;
   void* dq;               // final dQ (ordered schedules write it directly)
   void* dk;
@@ -112,6 +113,10 @@ struct PrologueArgs {
   long items = 0;
   int* unit_off = nullptr;
   int2* item = nullptr;
+  // lse2[i] = lse[i] * log2(e), rounded once, for i < lse_count
+  const float* lse = nullptr;
+  float* lse2 = nullptr;
+  size_t lse_count = 0;
 };
 hipError_t launch_bwd_prologue(const PrologueArgs& a, hipStream_t stream);
 // Zero rows [t * rows, t * rows + rows) of every head of a [BH, N, d] tensor
