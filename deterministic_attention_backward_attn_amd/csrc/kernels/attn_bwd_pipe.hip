@@ -152,7 +152,7 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int wv = tid >> 6;              // 0..7
+  const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);  // 0..7, a scalar
   const bool isA = wv < NW;
   const int w = wv & 3;                 // KV slice
   const int l32 = lane & 31;
@@ -186,7 +186,11 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
 
   const Placement pl = place_units(a, tid, sPlace);
   const int U = a.units_per_head;
-  const int grp = pl.grp, n_grp = pl.n_grp, li = pl.li, W = pl.W;
+  // (read from LDS, the same in every lane: scalar registers)
+  const int grp = __builtin_amdgcn_readfirstlane(pl.grp);
+  const int n_grp = __builtin_amdgcn_readfirstlane(pl.n_grp);
+  const int li = __builtin_amdgcn_readfirstlane(pl.li);
+  const int W = __builtin_amdgcn_readfirstlane(pl.W);
   const bool grouped = pl.grouped;
   const int BH = a.total_units / U;
   const int hg = (BH - grp + n_grp - 1) / n_grp;
@@ -239,7 +243,14 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
       for (int i = tid; i < n_items; i += NT) sItems[i] = a.items[it0 + i];
       __syncthreads();
 
-      auto qtile_of = [&](int g) { return (sItems[g / RHO].x >> 16) * RHO + (g % RHO); };
+      // work-list entry i, the same in every lane: moved to scalar registers,
+      // so that what is derived from it (tile indices, addresses, flags) is
+      // computed by scalar instructions
+      auto item_at = [&](int i) {
+        const int2 v = sItems[i];
+        return make_int2(__builtin_amdgcn_readfirstlane(v.x), __builtin_amdgcn_readfirstlane(v.y));
+      };
+      auto qtile_of = [&](int g) { return (item_at(g / RHO).x >> 16) * RHO + (g % RHO); };
 
       if constexpr (IS_A) {
         // ---------------------------------------------------------- stage A
@@ -307,7 +318,7 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
           if (t < n_steps) {
             const int b3 = t % NQB;
             const int b2 = t & 1;
-            const int2 itm = sItems[t / RHO];
+            const int2 itm = item_at(t / RHO);
             const int kv = itm.x & 0xFFFF;
             const int qblk = itm.x >> 16;
             const int rsub = t % RHO;
@@ -522,7 +533,7 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
             const int g = t - 1;
             const int b3 = g % NQB;
             const int b2 = g & 1;
-            const int2 itm = sItems[g / RHO];
+            const int2 itm = item_at(g / RHO);
             const int kv = itm.x & 0xFFFF;
             const int rank = itm.y & 0xFFFF;
             const bool last = ((itm.y >> 30) & 1) != 0;
@@ -687,7 +698,7 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
           sUnit = (int)__hip_atomic_fetch_add(work_counter, 1u, __ATOMIC_RELAXED,
                                               __HIP_MEMORY_SCOPE_AGENT) + W;
         __syncthreads();
-        unit = sUnit;
+        unit = __builtin_amdgcn_readfirstlane(sUnit);
         __syncthreads();
       } else {
         unit += stride_static;
