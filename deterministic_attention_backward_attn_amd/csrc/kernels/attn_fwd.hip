@@ -230,7 +230,7 @@ __global__ void __launch_bounds__(NW * 64, QN == 1 ? 8 / NW : 1) fwd_bf16_kernel
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
-  const int w = tid >> 6;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // a scalar
   const int l32 = lane & 31;
   const int hh = lane >> 5;
   const int j16 = lane & 15;
