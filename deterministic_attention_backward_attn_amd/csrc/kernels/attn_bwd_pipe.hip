@@ -148,7 +148,9 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
   constexpr uint32_t kQtoDO = (uint32_t)(offsetof(Lds, dO) - offsetof(Lds, q));
   const auto qix = [](int r, int c) { return r * LQ + (((c >> 3) ^ swz<D>(r)) << 3) + (c & 7); };
   const auto six = [](int r, int c) { return r * LS + c; };
-  const auto rix = [](int r, int c) { return r * LR + (((c >> 2) ^ ((r >> 1) & 7)) << 2) + (c & 3); };
+  // partial rows, 16-byte chunk c of row r at chunk c ^ (r % 8) (measured
+  // 2 % faster for descending than c ^ (r / 2 % 8))
+  const auto rix = [](int r, int c) { return r * LR + (((c >> 2) ^ (r & 7)) << 2) + (c & 3); };
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -246,11 +248,16 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
       // work-list entry i, the same in every lane: moved to scalar registers,
       // so that what is derived from it (tile indices, addresses, flags) is
       // computed by scalar instructions
-      auto item_at = [&](int i) {
-        const int2 v = sItems[i];
+      const auto uniform = [](int2 v) {
         return make_int2(__builtin_amdgcn_readfirstlane(v.x), __builtin_amdgcn_readfirstlane(v.y));
       };
-      auto qtile_of = [&](int g) { return (item_at(g / RHO).x >> 16) * RHO + (g % RHO); };
+      // Stage A reads its entries one period before it uses them (into
+      // vector registers, made scalar at the start of the period that uses
+      // them), so that its periods do not start by waiting for an LDS round
+      // trip (stage B doing the same measured slower for naive).  Entry i
+      // clamped to the list (the read past its end, at the last period, is
+      // never used).
+      const auto raw_item = [&](int i) { return sItems[i < n_items ? i : (n_items > 0 ? n_items - 1 : 0)]; };
 
       if constexpr (IS_A) {
         // ---------------------------------------------------------- stage A
@@ -278,8 +285,8 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
         }
         // LSE for lanes < BR, delta for the others
         const float* stat_src = lane < BR ? lse_g + lane : del_g + (lane - BR);
-        auto dma = [&](int g, int buf) {
-          const int q0 = qtile_of(g) * BR;
+        auto dma = [&](int qtile, int buf) {
+          const int q0 = qtile * BR;
           const T* qs = Qg + (size_t)q0 * D;
           const T* os = dOg + (size_t)q0 * D;
 #pragma unroll
@@ -308,8 +315,11 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
               dVg[(uint32_t)((a_kv * BC + 32 * w + crow(r, hh)) * D + nt * 32 + l32)] =
                   E::from_f32(accdV[nt][r]);
         };
-        if (n_steps > 0) dma(0, 0);
-        if (n_steps > 1) dma(1, 1);
+        if (n_steps > 0) dma((uniform(raw_item(0)).x >> 16) * RHO, 0);
+        if (n_steps > 1) dma((uniform(raw_item(0)).x >> 16) * RHO + 1, 1);
+        // the entry of sub-tile t and that of sub-tile t + 2 (staged at t)
+        int2 pf_itm = raw_item(0);
+        int2 pf_st = raw_item(2 / RHO);
         wait_staged(n_steps > 1);
         __syncthreads();  // sub-tile 0 in LDS
 
@@ -318,7 +328,7 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
           if (t < n_steps) {
             const int b3 = t % NQB;
             const int b2 = t & 1;
-            const int2 itm = item_at(t / RHO);
+            const int2 itm = uniform(pf_itm);
             const int kv = itm.x & 0xFFFF;
             const int qblk = itm.x >> 16;
             const int rsub = t % RHO;
@@ -350,7 +360,7 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
             }
             // sub-tile t + 2 into its buffer (its previous contents, sub-tile
             // t - 2, were last read by stage B in the previous period)
-            if (t + 2 < n_steps) dma(t + 2, (t + 2) % NQB);
+            if (t + 2 < n_steps) dma((uniform(pf_st).x >> 16) * RHO + (t + 2) % RHO, (t + 2) % NQB);
             PHASE(0);
             const T* cQ = sQ[b3];
             const T* cdO = sdO[b3];
@@ -374,6 +384,8 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
               }
               __builtin_amdgcn_sched_barrier(0);
             }
+            pf_itm = raw_item((t + 1) / RHO);
+            pf_st = raw_item((t + 3) / RHO);
 
             PHASE(1);
             // P and dS (pairs flagged partial hide the elements outside
@@ -533,7 +545,7 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
             const int g = t - 1;
             const int b3 = g % NQB;
             const int b2 = g & 1;
-            const int2 itm = item_at(g / RHO);
+            const int2 itm = uniform(raw_item(g / RHO));
             const int kv = itm.x & 0xFFFF;
             const int rank = itm.y & 0xFFFF;
             const bool last = ((itm.y >> 30) & 1) != 0;
@@ -564,7 +576,8 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
                 wait_turn(qtile, rank);
               }
               load_acc(qtile, rank > 0);
-              p_seen = load_relaxed_agent(counter(qtile_of(g + 1 < n_steps ? g + 1 : g)));
+              const int gn = g + 1 < n_steps ? g + 1 : g;
+              p_seen = load_relaxed_agent(counter((uniform(raw_item(gn / RHO)).x >> 16) * RHO + gn % RHO));
             }
 
             PHASE(1);
