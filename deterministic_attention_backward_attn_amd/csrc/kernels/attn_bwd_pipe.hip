@@ -109,7 +109,7 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
   constexpr int KK = BC / KSTEP;        // 8 MFMA steps over the KV tile
   constexpr int NTD = D / 32;           // 4 column tiles over d
   constexpr int LQ = D;
-  constexpr int LS = BR + 4;            // row stride of sdSt ([kv][q])
+  constexpr int LS = BR;                // row stride of sdSt ([kv][q], swizzled)
   constexpr int CPT = BR * D / VEC / NA;  // 16-byte chunks per A thread per tensor (2)
   static_assert(CPT * VEC * NA == BR * D, "sub-tile load must split evenly");
 
@@ -147,7 +147,12 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
   // a dO buffer lies this many bytes after the Q buffer of the same index
   constexpr uint32_t kQtoDO = (uint32_t)(offsetof(Lds, dO) - offsetof(Lds, q));
   const auto qix = [](int r, int c) { return r * LQ + (((c >> 3) ^ swz<D>(r)) << 3) + (c & 7); };
-  const auto six = [](int r, int c) { return r * LS + c; };
+  // dS^T rows: 8-byte unit u (4 elements) of row r at unit u ^ dsw(r), so
+  // that the 16 lanes of a write step (16 consecutive rows, one unit), the
+  // 32 lanes of a row read (32 consecutive rows) and the transposing reads
+  // (4 whole rows) each touch distinct banks
+  const auto dsw = [](int r) { return ((r >> 1) & 7) ^ ((r >> 4) & 1); };
+  const auto six = [=](int r, int c) { return r * LS + ((((c >> 2) ^ dsw(r)) << 2) | (c & 3)); };
   // partial rows, 16-byte chunk c of row r at chunk c ^ (r % 8) (measured
   // 2 % faster for descending than c ^ (r / 2 % 8))
   const auto rix = [](int r, int c) { return r * LR + (((c >> 2) ^ (r & 7)) << 2) + (c & 3); };
@@ -216,7 +221,23 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
   };
   // ... and of dS^T (rows 8 hh + j16 / 4, columns gcol + 4 (j16 % 4)), the
   // rows of KV step i and the second half's 4 rows a constant further
-  const uint32_t oF = (uint32_t)(2 * six(8 * hh + (j16 >> 2), gcol + 4 * (j16 & 3)));
+  // (the swizzle of rows 16 i + r' depends on i only through i % 2, and
+  // rows 4 further need their own offsets)
+  uint32_t oF[2][2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p)
+#pragma unroll
+    for (int e = 0; e < 2; ++e)
+      oF[p][e] = (uint32_t)(2 * six(16 * p + 8 * hh + 4 * e + (j16 >> 2), gcol + 4 * (j16 & 3)) - 2 * 16 * p * LS);
+  // dS^T writes (unit 2 gq + hh of row kvl) and row reads (units 4 cc + hh
+  // and 4 cc + hh + 2), byte offsets within a buffer
+  uint32_t oDw[4], oDr[2][2];
+#pragma unroll
+  for (int gq = 0; gq < 4; ++gq) oDw[gq] = (uint32_t)(2 * six(kvl, 8 * gq + 4 * hh));
+#pragma unroll
+  for (int cc = 0; cc < 2; ++cc)
+#pragma unroll
+    for (int e = 0; e < 2; ++e) oDr[cc][e] = (uint32_t)(2 * six(kvl, 16 * cc + 4 * hh + 8 * e));
 
   // One copy of the unit loop per stage, so that each stage's registers are
   // allocated for its own values only; both copies pass the same barriers
@@ -419,7 +440,7 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
               for (int e = 0; e < 4; ++e) ds[e] = p[e] * (accP[4 * gq + e] - d4[e]);
               pw[2 * gq] = pack2_bf16(p[0], p[1]);
               pw[2 * gq + 1] = pack2_bf16(p[2], p[3]);
-              *reinterpret_cast<uint2*>(&cdSt[kvl * LS + qb]) =
+              *reinterpret_cast<uint2*>(at(cdSt, oDw[gq])) =
                   make_uint2(pack2_bf16(ds[0], ds[1]), pack2_bf16(ds[2], ds[3]));
             }
             PHASE(2);
@@ -593,9 +614,8 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
             frag da[2], bq[2][NTD], fa[KK];
 #pragma unroll
             for (int cc = 0; cc < 2; ++cc) {
-              const int r0 = 16 * cc + 4 * hh;
-              const uint2 d0 = *reinterpret_cast<const uint2*>(&cdSt[kvl * LS + r0]);
-              const uint2 d1 = *reinterpret_cast<const uint2*>(&cdSt[kvl * LS + r0 + 8]);
+              const uint2 d0 = *reinterpret_cast<const uint2*>(at(cdSt, oDr[cc][0]));
+              const uint2 d1 = *reinterpret_cast<const uint2*>(at(cdSt, oDr[cc][1]));
               da[cc] = __builtin_bit_cast(bf16x8, make_uint4(d0.x, d0.y, d1.x, d1.y));
 #pragma unroll
               for (int nt = 0; nt < NTD; ++nt)
@@ -605,7 +625,7 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
 #pragma unroll
             for (int i = 0; i < KK; ++i) {
               accdK[i % NTD] = E::mma(da[i / NTD], bq[i / NTD][i % NTD], accdK[i % NTD]);
-              fa[i] = tr_frag_at(at(cdSt, oF + 2 * i * 16 * LS), at(cdSt, oF + 2 * (i * 16 + 4) * LS));
+              fa[i] = tr_frag_at(at(cdSt, oF[i & 1][0] + 2 * i * 16 * LS), at(cdSt, oF[i & 1][1] + 2 * i * 16 * LS));
             }
             __builtin_amdgcn_sched_barrier(0);
             f32x16 accQ = zero16();
