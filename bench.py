@@ -210,7 +210,7 @@ def main():
                     help="skip the forward and forward+backward timings")
     ap.add_argument("--layout", choices=["auto", "single", "pairs", "pipe"], default="auto",
                     help="backward kernel layout: default, wave pairs or the two-stage "
-                         "pipeline (bf16 d=128; bit-identical results)")
+                         "pipeline (bf16 d=128 or 64; bit-identical results)")
     ap.add_argument("--phases", action="store_true",
                     help="one extra launch per schedule with the phase timer: share of wave "
                          "cycles per phase of a Q sub-tile")
@@ -270,9 +270,9 @@ def main():
     lay = {"auto": {}, "single": {"layout": 3}, "pairs": {"layout": 1},
            "pipe": {"layout": 2}}[args.layout]
     # the kernel that runs (the library's automatic choice: the pipeline for
-    # bf16 with d = 128), for the phase names and the report
+    # bf16 with d = 128 or 64), for the phase names and the report
     kind = args.layout if args.layout != "auto" else (
-        "pipe" if w.dtype == "bf16" and w.d == 128 else "single")
+        "pipe" if w.dtype == "bf16" and w.d in (128, 64) else "single")
 
     def step(sched, events=None):
         D.attn_bwd_preprocess(o, dev["do"], out=delta)

@@ -204,8 +204,8 @@ def attn_bwd(q, k, v, do, lse, delta, *, schedule="naive", causal=False, scale=N
     kernel_events (two raw hipEvent_t handles), wait_stats (int64 tensor of
     at least 4*4096*4 entries), phase_stats (int64 tensor of at least
     16*4096*4 entries: cycles per phase of each wave's sub-tiles, see the
-    header), layout (0 automatic: the two-stage pipeline for bf16 d=128, else
-    the one-stage kernel; 1 wave pairs, 2 pipeline: bf16 d=128 only; 3
+    header), layout (0 automatic: the two-stage pipeline for bf16 d=128 or 64, else
+    the one-stage kernel; 1 wave pairs: bf16 d=128 only, 2 pipeline: bf16 d=128 or 64; 3
     one-stage kernel; bit-identical results), placement (0 automatic, 1 device-wide, 2 XCD
     groups with L2-coherent accumulator, 3 XCD groups device-coherent),
     unit_order (0 automatic, 1 head by head, 2 unit-major).

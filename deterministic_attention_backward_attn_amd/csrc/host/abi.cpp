@@ -49,9 +49,9 @@ typedef std::array<double, 4> Cost;
 // pairs, 2 two-stage pipeline, 3 one-stage kernel.
 constexpr int kLayoutPairs = 1, kLayoutPipe = 2, kLayoutOneStage = 3;
 // The layout an automatic launch runs: the pipeline where it exists (bf16,
-// d = 128), else the one-stage kernel.
+// d = 128 or 64), else the one-stage kernel.
 int auto_layout(int dtype, int d) {
-  return dtype == DASH_BF16 && d == 128 ? kLayoutPipe : kLayoutOneStage;
+  return dtype == DASH_BF16 && (d == 128 || d == 64) ? kLayoutPipe : kLayoutOneStage;
 }
 
 constexpr int kXcds = 8;  // XCDs of an MI355X: the workgroup groups of the placement
@@ -672,7 +672,8 @@ dash_status run_bwd(const dash_attn_desc* desc, dash_schedule schedule, const vo
   if (lay < 0 || lay > kLayoutOneStage) return DASH_ERR_INVALID_ARG;
   const bool auto_lay = lay == 0;
   if (auto_lay) lay = auto_layout(desc->dtype, desc->d);
-  if ((lay == kLayoutPairs || lay == kLayoutPipe) && (desc->dtype != DASH_BF16 || desc->d != 128))
+  if (lay == kLayoutPairs && (desc->dtype != DASH_BF16 || desc->d != 128)) return DASH_ERR_UNSUPPORTED;
+  if (lay == kLayoutPipe && (desc->dtype != DASH_BF16 || (desc->d != 128 && desc->d != 64)))
     return DASH_ERR_UNSUPPORTED;
 
   const MaskKey mkey = mask_key(desc);
@@ -700,7 +701,7 @@ dash_status run_bwd(const dash_attn_desc* desc, dash_schedule schedule, const vo
     // that finds fewer runs the one-stage kernel instead
     int pb = 0;
     if ((lay == kLayoutPairs ? dash::bwd_pair_max_coresident(masked, ordered, &pb)
-                             : dash::bwd_pipe_max_coresident(masked, ordered, &pb)) != hipSuccess)
+                             : dash::bwd_pipe_max_coresident(desc->d, masked, ordered, &pb)) != hipSuccess)
       return DASH_ERR_HIP;
     if (pb < maxco) {
       if (!auto_lay) return DASH_ERR_UNSUPPORTED;
@@ -826,7 +827,7 @@ dash_status run_bwd(const dash_attn_desc* desc, dash_schedule schedule, const vo
   hipEvent_t ev1 = dbg ? (hipEvent_t)dbg->kernel_events[1] : nullptr;
   if (ev0 && hipEventRecord(ev0, strm) != hipSuccess) return DASH_ERR_HIP;
   if (U > 0 && (pairs  ? dash::launch_bwd_pair(masked, ordered, a, grid, strm)
-                : pipe ? dash::launch_bwd_pipe(masked, ordered, a, grid, strm)
+                : pipe ? dash::launch_bwd_pipe(desc->d, masked, ordered, a, grid, strm)
                        : dash::launch_bwd(desc->dtype, desc->d, masked, ordered, a, grid, strm)) !=
                    hipSuccess)
     return DASH_ERR_HIP;

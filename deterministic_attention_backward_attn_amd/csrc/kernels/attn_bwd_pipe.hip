@@ -1,4 +1,5 @@
-// Deterministic attention backward, two-stage pipeline (bf16, d = 128).
+// Deterministic attention backward, two-stage pipeline (bf16, d = 128 with
+// Q sub-tiles of 32 rows, d = 64 with Q sub-tiles of 64 rows).
 //
 // The same method, schedules, tables and ordered dQ hand-off as the
 // one-wave-per-slice kernel (attn_bwd.hip), with the work of each 32-row KV
@@ -94,12 +95,17 @@ __device__ __forceinline__ bf16x8 tr_frag_at(const bf16_t* pa, const bf16_t* pb)
   return __builtin_bit_cast(bf16x8, u);
 }
 
-template <bool MASKED, bool ORDERED, bool DEBUG>
+template <int D, bool MASKED, bool ORDERED, bool DEBUG>
 __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
   using T = bf16_t;
   using E = Elt<T>;
   using frag = typename E::frag;
-  constexpr int D = 128, BC = 128, BR = 32;
+  static_assert(D == 128 || D == 64, "head dim");
+  // Q sub-tiles of 32 rows at d = 128, 64 at d = 64: the same MFMA work per
+  // period (A 24, B 16 products) and the same 8 KB per staged sub-tile
+  constexpr int BC = 128, BR = D == 128 ? 32 : 64;
+  constexpr int QT = BR / 32;           // 32-row Q tiles per sub-tile
+  constexpr int CS = BR / 16;           // MFMA steps over a sub-tile's Q rows
   constexpr int NW = 4;                 // KV slices (counter layout: one per slice)
   constexpr int NT = 512;
   constexpr int NA = 256;               // threads of stage A
@@ -107,11 +113,14 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
   constexpr int KPL = 8, KSTEP = 16, VEC = 8;
   constexpr int DK = D / KSTEP;         // 8 MFMA steps over d
   constexpr int KK = BC / KSTEP;        // 8 MFMA steps over the KV tile
-  constexpr int NTD = D / 32;           // 4 column tiles over d
+  constexpr int NTD = D / 32;           // column tiles over d
   constexpr int LQ = D;
   constexpr int LS = BR;                // row stride of sdSt ([kv][q], swizzled)
   constexpr int CPT = BR * D / VEC / NA;  // 16-byte chunks per A thread per tensor (2)
-  static_assert(CPT * VEC * NA == BR * D, "sub-tile load must split evenly");
+  static_assert(CPT == 2, "sub-tile load: two 1 KB loads per A wave and tensor");
+  static_assert(CS * NTD == KK, "dK steps pair with the dQ operand reads");
+  // B wave w: dQ columns [32 DT, 32 DT + 32) of the sub-tile's Q rows
+  // [32 QW, 32 QW + 32) (d = 128: DT = w; d = 64: DT = w % 2, QW = w / 2)
 
   // Q / dO / LSE / delta sub-tiles: sub-tile g in buffer g % 4 (A reads t,
   // B reads t - 1, the loads of t + 1 and t + 2 in flight).  dS^T of
@@ -150,8 +159,11 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
   // dS^T rows: 8-byte unit u (4 elements) of row r at unit u ^ dsw(r), so
   // that the 16 lanes of a write step (16 consecutive rows, one unit), the
   // 32 lanes of a row read (32 consecutive rows) and the transposing reads
-  // (4 whole rows) each touch distinct banks
-  const auto dsw = [](int r) { return ((r >> 1) & 7) ^ ((r >> 4) & 1); };
+  // (4 rows, 64 bytes of each) each touch distinct banks
+  const auto dsw = [](int r) {
+    if constexpr (BR == 32) return ((r >> 1) & 7) ^ ((r >> 4) & 1);
+    else return ((r & 1) ^ ((r >> 4) & 1)) | (((r >> 2) & 1) << 1) | (((r >> 3) & 1) << 2) | (((r >> 1) & 1) << 3);
+  };
   const auto six = [=](int r, int c) { return r * LS + ((((c >> 2) ^ dsw(r)) << 2) | (c & 3)); };
   // partial rows, 16-byte chunk c of row r at chunk c ^ (r % 8) (measured
   // 2 % faster for descending than c ^ (r / 2 % 8))
@@ -171,6 +183,7 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
   uint32_t* status = a.header;
   const uint32_t spin_limit = a.spin_limit;
   const int kvl = 32 * w + l32;         // this lane's KV row within the tile
+  const int DT = w % NTD, QW = w / NTD;
 
   uint64_t st_wait = 0, st_waits = 0, st_spun = 0;
   const uint64_t st_t0 = (DEBUG && a.wait_stats) ? (uint64_t)clock64() : 0;
@@ -228,14 +241,17 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
   for (int p = 0; p < 2; ++p)
 #pragma unroll
     for (int e = 0; e < 2; ++e)
-      oF[p][e] = (uint32_t)(2 * six(16 * p + 8 * hh + 4 * e + (j16 >> 2), gcol + 4 * (j16 & 3)) - 2 * 16 * p * LS);
-  // dS^T writes (unit 2 gq + hh of row kvl) and row reads (units 4 cc + hh
-  // and 4 cc + hh + 2), byte offsets within a buffer
-  uint32_t oDw[4], oDr[2][2];
+      oF[p][e] = (uint32_t)(2 * six(16 * p + 8 * hh + 4 * e + (j16 >> 2), 32 * QW + gcol + 4 * (j16 & 3)) -
+                            2 * 16 * p * LS);
+  // dS^T writes (Q tile m: unit 8 m + 2 gq + hh of row kvl) and row reads
+  // (units 4 cc + hh and 4 cc + hh + 2), byte offsets within a buffer
+  uint32_t oDw[QT][4], oDr[CS][2];
 #pragma unroll
-  for (int gq = 0; gq < 4; ++gq) oDw[gq] = (uint32_t)(2 * six(kvl, 8 * gq + 4 * hh));
+  for (int m = 0; m < QT; ++m)
 #pragma unroll
-  for (int cc = 0; cc < 2; ++cc)
+    for (int gq = 0; gq < 4; ++gq) oDw[m][gq] = (uint32_t)(2 * six(kvl, 32 * m + 8 * gq + 4 * hh));
+#pragma unroll
+  for (int cc = 0; cc < CS; ++cc)
 #pragma unroll
     for (int e = 0; e < 2; ++e) oDr[cc][e] = (uint32_t)(2 * six(kvl, 16 * cc + 4 * hh + 8 * e));
 
@@ -288,34 +304,36 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
         const float* del_g = a.delta + (size_t)head * N;
         // Sub-tile g into buffer `buf` by direct loads to LDS (no registers:
         // lane i of a 16-byte load writes LDS bytes [16 i, 16 i + 16) of the
-        // instruction's 1 KB).  Wave w loads LDS chunks [128 w, 128 w + 128)
-        // of sQ and of sdO, i.e. rows 8w .. 8w + 7: lane i of instruction m
-        // fills row 8w + 4m + i / 16, 16-byte slot i % 16, which holds the
-        // row's global chunk (slot ^ swz(row)).  Wave 0 also loads LSE and
-        // delta (one dword per lane).  The loads complete before the barrier
-        // that ends the period (the compiler waits for them there).
+        // instruction's 1 KB).  Wave w loads LDS bytes [2048 w, 2048 w + 2048)
+        // of sQ and of sdO, i.e. rows RW w .. RW w + RW - 1: lane i of
+        // instruction m fills row RW w + RI m + i / (D / 8), 16-byte slot
+        // i % (D / 8), which holds the row's global chunk (slot ^ swz(row)).
+        // Waves 0 (and 1 at d = 64) also load LSE and delta (one dword per
+        // lane).  The loads complete before the barrier that ends the period
+        // (the compiler waits for them there).
+        constexpr int RW = BR / 4, RI = 512 / D, CPR = D / 8;
         const int wu = __builtin_amdgcn_readfirstlane(w);
-        // per-lane element offsets within a sub-tile of the two 16-byte
-        // loads (rows 8w + 4m + lane / 16, m = 0, 1; swz depends on the row
-        // only through lane / 16 and 2w + m)
+        // per-lane element offsets within a sub-tile of the two 16-byte loads
         uint32_t doff[2];
 #pragma unroll
         for (int m = 0; m < 2; ++m) {
-          const int row = 8 * w + 4 * m + (lane >> 4);
-          doff[m] = (uint32_t)(row * D + ((lane & 15) ^ swz<D>(row)) * VEC);
+          const int row = RW * w + RI * m + lane / CPR;
+          doff[m] = (uint32_t)(row * D + ((lane % CPR) ^ swz<D>(row)) * VEC);
         }
-        // LSE for lanes < BR, delta for the others
-        const float* stat_src = lane < BR ? lse_g + lane : del_g + (lane - BR);
+        // stat dword 64 wu + lane: LSE of rows < BR, then delta
+        const int sidx = 64 * w + lane;
+        const bool stat_wave = 64 * wu < 2 * BR;
+        const float* stat_src = sidx < BR ? lse_g + sidx : del_g + (sidx < 2 * BR ? sidx - BR : 0);
         auto dma = [&](int qtile, int buf) {
           const int q0 = qtile * BR;
           const T* qs = Qg + (size_t)q0 * D;
           const T* os = dOg + (size_t)q0 * D;
 #pragma unroll
           for (int m = 0; m < 2; ++m) {
-            dma_b128(qs, doff[m] * (uint32_t)sizeof(T), &sQ[buf][(8 * wu + 4 * m) * LQ]);
-            dma_b128(os, doff[m] * (uint32_t)sizeof(T), &sdO[buf][(8 * wu + 4 * m) * LQ]);
+            dma_b128(qs, doff[m] * (uint32_t)sizeof(T), &sQ[buf][(RW * wu + RI * m) * LQ]);
+            dma_b128(os, doff[m] * (uint32_t)sizeof(T), &sdO[buf][(RW * wu + RI * m) * LQ]);
           }
-          if (wu == 0) dma_b32(stat_src + q0, &sStat[buf][0]);
+          if (stat_wave) dma_b32(stat_src + q0, &sStat[buf][64 * wu]);
         };
         // Wait for this wave's loads of the sub-tile read after the next
         // barrier: only the loads issued after them (4 or 5 when sub-tile
@@ -385,24 +403,32 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
             PHASE(0);
             const T* cQ = sQ[b3];
             const T* cdO = sdO[b3];
-            f32x16 accS = zero16(), accP = zero16();
+            // S and dP of Q tile m (rows 32 m .. 32 m + 31; the swizzle
+            // repeats every 16 rows, so tile m lies 32 m LQ elements further)
+            f32x16 accS[QT], accP[QT];
+#pragma unroll
+            for (int m = 0; m < QT; ++m) accS[m] = accP[m] = zero16();
             // in two halves over d: all A fragments of a half are read
             // first, then its MFMAs (the scheduling barriers keep them apart)
 #pragma unroll
             for (int h2 = 0; h2 < 2; ++h2) {
-              frag qa[DK / 2], oa[DK / 2];
+              frag qa[QT][DK / 2], oa[QT][DK / 2];
 #pragma unroll
-              for (int k2 = 0; k2 < DK / 2; ++k2) {
-                const int off = qix(l32, (h2 * DK / 2 + k2) * KSTEP + hh * KPL);
-                qa[k2] = load_frag(&cQ[off]);
-                oa[k2] = load_frag(at(&cQ[off], kQtoDO));
-              }
+              for (int m = 0; m < QT; ++m)
+#pragma unroll
+                for (int k2 = 0; k2 < DK / 2; ++k2) {
+                  const int off = qix(l32, (h2 * DK / 2 + k2) * KSTEP + hh * KPL) + 32 * m * LQ;
+                  qa[m][k2] = load_frag(&cQ[off]);
+                  oa[m][k2] = load_frag(at(&cQ[off], kQtoDO));
+                }
               __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-              for (int k2 = 0; k2 < DK / 2; ++k2) {
-                accS = E::mma(qa[k2], Kreg[h2 * DK / 2 + k2], accS);
-                accP = E::mma(oa[k2], Vreg[h2 * DK / 2 + k2], accP);
-              }
+              for (int k2 = 0; k2 < DK / 2; ++k2)
+#pragma unroll
+                for (int m = 0; m < QT; ++m) {
+                  accS[m] = E::mma(qa[m][k2], Kreg[h2 * DK / 2 + k2], accS[m]);
+                  accP[m] = E::mma(oa[m][k2], Vreg[h2 * DK / 2 + k2], accP[m]);
+                }
               __builtin_amdgcn_sched_barrier(0);
             }
             pf_itm = raw_item((t + 1) / RHO);
@@ -416,10 +442,12 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
             const bool emask = MASKED && ((itm.y >> 29) & 1);
             const int mbase = (qblk - kv) * BC + rsub * BR - kvl;  // i - j = mbase + row
             T* cdSt = sdSt[b2];
-            uint32_t pw[8];
+            uint32_t pw[QT][8];
+#pragma unroll
+            for (int m = 0; m < QT; ++m)
 #pragma unroll
             for (int gq = 0; gq < 4; ++gq) {
-              const int qb = 8 * gq + 4 * hh;  // 4 consecutive Q rows
+              const int qb = 32 * m + 8 * gq + 4 * hh;  // 4 consecutive Q rows
               const f32x4 l4 = *reinterpret_cast<const f32x4*>(&sStat[b3][qb]);
               const f32x4 d4 = *reinterpret_cast<const f32x4*>(&sStat[b3][BR + qb]);
               float p[4], ds[4];
@@ -428,7 +456,7 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
               // row), the first fused into the subtraction
 #pragma unroll
               for (int e = 0; e < 4; ++e)
-                p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(accS[4 * gq + e], a.scale_log2, -l4[e]));
+                p[e] = __builtin_amdgcn_exp2f(__builtin_fmaf(accS[m][4 * gq + e], a.scale_log2, -l4[e]));
               if (emask) {
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
@@ -437,27 +465,27 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
                 }
               }
 #pragma unroll
-              for (int e = 0; e < 4; ++e) ds[e] = p[e] * (accP[4 * gq + e] - d4[e]);
-              pw[2 * gq] = pack2_bf16(p[0], p[1]);
-              pw[2 * gq + 1] = pack2_bf16(p[2], p[3]);
-              *reinterpret_cast<uint2*>(at(cdSt, oDw[gq])) =
+              for (int e = 0; e < 4; ++e) ds[e] = p[e] * (accP[m][4 * gq + e] - d4[e]);
+              pw[m][2 * gq] = pack2_bf16(p[0], p[1]);
+              pw[m][2 * gq + 1] = pack2_bf16(p[2], p[3]);
+              *reinterpret_cast<uint2*>(at(cdSt, oDw[m][gq])) =
                   make_uint2(pack2_bf16(ds[0], ds[1]), pack2_bf16(ds[2], ds[3]));
             }
             PHASE(2);
             // dV += P^T dO (contraction over the sub-tile's Q rows; K slots:
             // Q rows r0 + {0..3}, r0 + 8 + {0..3}); the dO operands are read
             // before the first product
-            frag bo[2][NTD];
+            frag bo[CS][NTD];
 #pragma unroll
-            for (int cc = 0; cc < 2; ++cc)
+            for (int cc = 0; cc < CS; ++cc)
 #pragma unroll
               for (int nt = 0; nt < NTD; ++nt)
                 bo[cc][nt] = tr_sub(cdO, cc, nt);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-            for (int cc = 0; cc < 2; ++cc) {
-              const frag pa = __builtin_bit_cast(
-                  bf16x8, make_uint4(pw[4 * cc], pw[4 * cc + 1], pw[4 * cc + 2], pw[4 * cc + 3]));
+            for (int cc = 0; cc < CS; ++cc) {
+              const uint32_t* pc = &pw[cc / 2][4 * (cc % 2)];
+              const frag pa = __builtin_bit_cast(bf16x8, make_uint4(pc[0], pc[1], pc[2], pc[3]));
 #pragma unroll
               for (int nt = 0; nt < NTD; ++nt) accdV[nt] = E::mma(pa, bo[cc][nt], accdV[nt]);
             }
@@ -490,14 +518,15 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
         const __amdgpu_buffer_rsrc_t dq_rs = make_rsrc(dqa, (uint32_t)(N * D * 4));
         const __amdgpu_buffer_rsrc_t dqo_rs = make_rsrc(dqo, (uint32_t)(N * D * 2));
         const __amdgpu_buffer_rsrc_t cnt_rs = make_rsrc(cnt_h, (uint32_t)(n_sub * NW * 4));
-        // row-major chunk k (0..3) of this slice's 32 x 32 output tile:
-        // 4 consecutive columns of one row; 8 lanes cover a 128-byte row
+        // row-major chunk k (0..3) of this wave's 32 x 32 output tile (Q
+        // rows 32 QW.., d columns 32 DT..): 4 consecutive columns of one
+        // row; 8 lanes cover a 128-byte row
         auto chunk_off = [&](int q0, int k) {
-          return (uint32_t)((q0 + (lane >> 3) + 8 * k) * D + w * 32 + 4 * (lane & 7));
+          return (uint32_t)((q0 + 32 * QW + (lane >> 3) + 8 * k) * D + DT * 32 + 4 * (lane & 7));
         };
         auto dq_off = [&](int q0, int r) {
-          if constexpr (ORDERED) return (uint32_t)((q0 + l32) * D + w * 32 + crow(r, hh));
-          else return (uint32_t)((q0 + crow(r, hh)) * D + w * 32 + l32);
+          if constexpr (ORDERED) return (uint32_t)((q0 + 32 * QW + l32) * D + DT * 32 + crow(r, hh));
+          else return (uint32_t)((q0 + 32 * QW + crow(r, hh)) * D + DT * 32 + l32);
         };
         f32x4 lv[4];
         auto load_acc = [&](int qtile, bool live) {
@@ -581,7 +610,7 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
               b_kv = kv;
 #pragma unroll
               for (int ks = 0; ks < KK; ++ks)
-                KT[ks] = tr_frag(sK, qix, ks * 16 + 8 * hh, ks * 16 + 8 * hh + 4, w * 32 + gcol, j16);
+                KT[ks] = tr_frag(sK, qix, ks * 16 + 8 * hh, ks * 16 + 8 * hh + 4, DT * 32 + gcol, j16);
 #pragma unroll
               for (int nt = 0; nt < NTD; ++nt) accdK[nt] = zero16();
             }
@@ -611,9 +640,9 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
             // latency once rather than once each.
             const T* cQ = sQ[b3];
             const T* cdSt = sdSt[b2];
-            frag da[2], bq[2][NTD], fa[KK];
+            frag da[CS], bq[CS][NTD], fa[KK];
 #pragma unroll
-            for (int cc = 0; cc < 2; ++cc) {
+            for (int cc = 0; cc < CS; ++cc) {
               const uint2 d0 = *reinterpret_cast<const uint2*>(at(cdSt, oDr[cc][0]));
               const uint2 d1 = *reinterpret_cast<const uint2*>(at(cdSt, oDr[cc][1]));
               da[cc] = __builtin_bit_cast(bf16x8, make_uint4(d0.x, d0.y, d1.x, d1.y));
@@ -757,17 +786,24 @@ __global__ void __launch_bounds__(512, 1) bwd_pipe_kernel(BwdArgs a) {
 #undef PHASE
 }
 
-template <bool DEBUG>
-static void* pick_pipe(bool masked, bool ordered) {
+template <int D, bool DEBUG>
+static void* pick_pipe_d(bool masked, bool ordered) {
   if (masked)
-    return ordered ? (void*)bwd_pipe_kernel<true, true, DEBUG> : (void*)bwd_pipe_kernel<true, false, DEBUG>;
-  return ordered ? (void*)bwd_pipe_kernel<false, true, DEBUG> : (void*)bwd_pipe_kernel<false, false, DEBUG>;
+    return ordered ? (void*)bwd_pipe_kernel<D, true, true, DEBUG> : (void*)bwd_pipe_kernel<D, true, false, DEBUG>;
+  return ordered ? (void*)bwd_pipe_kernel<D, false, true, DEBUG> : (void*)bwd_pipe_kernel<D, false, false, DEBUG>;
+}
+template <bool DEBUG>
+static void* pick_pipe(int d, bool masked, bool ordered) {
+  if (d == 128) return pick_pipe_d<128, DEBUG>(masked, ordered);
+  if (d == 64) return pick_pipe_d<64, DEBUG>(masked, ordered);
+  return nullptr;
 }
 
-hipError_t bwd_pipe_max_coresident(bool masked, bool ordered, int* blocks) {
+hipError_t bwd_pipe_max_coresident(int d, bool masked, bool ordered, int* blocks) {
+  if (d != 128 && d != 64) return hipErrorInvalidValue;
   int per_cu = 0;
   for (int dbg = 0; dbg < 2; ++dbg) {
-    void* f = dbg ? pick_pipe<true>(masked, ordered) : pick_pipe<false>(masked, ordered);
+    void* f = dbg ? pick_pipe<true>(d, masked, ordered) : pick_pipe<false>(d, masked, ordered);
     int n = 0;
     hipError_t e = hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, f, 512, 0);
     if (e != hipSuccess) return e;
@@ -782,11 +818,12 @@ hipError_t bwd_pipe_max_coresident(bool masked, bool ordered, int* blocks) {
   return hipSuccess;
 }
 
-hipError_t launch_bwd_pipe(bool masked, bool ordered, const BwdArgs& a, int grid,
+hipError_t launch_bwd_pipe(int d, bool masked, bool ordered, const BwdArgs& a, int grid,
                            hipStream_t stream) {
   const bool debug = a.jitter_seed != 0u || a.poison_q >= 0 || a.partials != nullptr ||
                      a.wait_stats != nullptr || a.phase_stats != nullptr;
-  void* f = debug ? pick_pipe<true>(masked, ordered) : pick_pipe<false>(masked, ordered);
+  void* f = debug ? pick_pipe<true>(d, masked, ordered) : pick_pipe<false>(d, masked, ordered);
+  if (f == nullptr) return hipErrorInvalidValue;
   BwdArgs copy = a;
   void* args[] = {&copy};
   // cooperative: every workgroup resident, which the ordered waits rely on

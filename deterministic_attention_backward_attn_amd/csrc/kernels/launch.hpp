@@ -77,11 +77,11 @@ hipError_t bwd_max_coresident(int dtype, int d, bool masked, bool ordered, int* 
 hipError_t launch_bwd_pair(bool masked, bool ordered, const BwdArgs& a, int grid,
                            hipStream_t stream);
 hipError_t bwd_pair_max_coresident(bool masked, bool ordered, int* blocks);
-// Two-stage pipeline layout of the backward (bf16, d = 128 only): same
-// arguments, 512 threads per workgroup; no phase timer.
-hipError_t launch_bwd_pipe(bool masked, bool ordered, const BwdArgs& a, int grid,
+// Two-stage pipeline layout of the backward (bf16, d = 128 or 64): same
+// arguments plus the head dim, 512 threads per workgroup.
+hipError_t launch_bwd_pipe(int d, bool masked, bool ordered, const BwdArgs& a, int grid,
                            hipStream_t stream);
-hipError_t bwd_pipe_max_coresident(bool masked, bool ordered, int* blocks);
+hipError_t bwd_pipe_max_coresident(int d, bool masked, bool ordered, int* blocks);
 // Tile sizes of the backward kernel: KV tile (BC) and Q sub-tile (BR).
 void bwd_tiles(int dtype, int d, int* bc, int* br);
 // Waves per workgroup of the backward kernel (one order counter each).

@@ -321,7 +321,7 @@ dash_status dash_attn_bwd_status(const void* workspace, void* stream);
  *   layout          which backward kernel runs; results are bit-identical
  *                   for every value (the ATOMIC schedule's unordered adds
  *                   aside).  0 = automatic: the two-stage pipeline for bf16
- *                   with d = 128, the one-stage kernel otherwise;
+ *                   with d = 128 or 64, the one-stage kernel otherwise;
  *                   1 = the wave-pair layout (two waves per SIMD, each KV
  *                   slice split between a wave for S, P, dV and the dQ
  *                   product and a wave for dP, dS, dK and the ordered add);
@@ -329,10 +329,10 @@ dash_status dash_attn_bwd_status(const void* workspace, void* stream);
  *                   S, dP, P, dS and dV of a Q sub-tile while another
  *                   computes dK, dQ and the ordered dQ add of the sub-tile
  *                   before it); 3 = the one-stage kernel (one wave per KV
- *                   slice does every product of a sub-tile).  1 and 2 exist
- *                   for bf16 with d = 128 only: another dtype or head dim
- *                   gives DASH_ERR_UNSUPPORTED; other values:
- *                   DASH_ERR_INVALID_ARG.
+ *                   slice does every product of a sub-tile).  1 exists for
+ *                   bf16 with d = 128 only, 2 for bf16 with d = 128 or 64:
+ *                   another dtype or head dim gives DASH_ERR_UNSUPPORTED;
+ *                   other values: DASH_ERR_INVALID_ARG.
  */
 typedef struct {
   uint32_t spin_limit;
@@ -470,7 +470,7 @@ dash_status dash_attn_bwd_calibrate(const dash_attn_desc* desc, const void* q, c
 /*
  * The costs DASH_SCHED_AUTO uses on the current device for the
  * descriptor's dtype and head dimension until dash_attn_bwd_calibrate fits
- * others: {1, 0.5, 0.3, 0.3} for bf16 with d = 128 (the two-stage pipeline,
+ * others: {1, 0.5, 0.3, 0.3} for bf16 with d = 128 or 64 (the two-stage pipeline,
  * which overlaps the products so that the ordered adds weigh more), else
  * {1, 0.5, 0.05, 0.05} (the one-stage kernel).  Queries the current device
  * only.

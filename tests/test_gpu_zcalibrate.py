@@ -47,10 +47,12 @@ def test_calibrate_records_the_costs_auto_uses():
         # ties go to shift, then descending
         picks.add([s for s in reversed(SCHED) if pred[s] == best][0])
     assert picked in picks
-    # other dtypes and head dims keep their costs (bf16 with d = 128 runs
-    # the two-stage pipeline, whose default model weighs the ordered add more)
+    # other dtypes and head dims keep their costs (bf16 with d = 128 or 64
+    # runs the two-stage pipeline, whose default model weighs the ordered add
+    # more; fp32 with d = 128 the one-stage kernel)
     assert D.bwd_costs(B, H, N, 128, "bf16", True) == (1.0, 0.5, 0.3, 0.3)
-    assert D.bwd_costs(B, H, N, 64, "bf16", True) == (1.0, 0.5, 0.05, 0.05)
+    assert D.bwd_costs(B, H, N, 64, "bf16", True) == (1.0, 0.5, 0.3, 0.3)
+    assert D.bwd_costs(B, H, N, 128, "f32", True) == (1.0, 0.5, 0.05, 0.05)
     # a measured pick keeps precedence
     tuned, _ = D.attn_bwd_tune(dev["q"], dev["k"], dev["v"], dev["do"], lse, delta, causal=True,
                                reps=2)
