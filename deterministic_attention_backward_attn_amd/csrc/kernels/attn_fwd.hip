@@ -355,8 +355,11 @@ __global__ void __launch_bounds__(NW * 64, QN == 1 ? 8 / NW : 1) fwd_bf16_kernel
     if (jn < j_hi) fetch(jn);
   }
   __syncthreads();
-  int buf = 0;
-  while (j < j_hi) {
+  // One key tile; the loop below alternates the two buffers with the
+  // buffer index a constant in each copy, so that every LDS address is a
+  // per-lane offset plus an immediate.
+  const auto tile = [&](auto buf_tag) {
+    constexpr int buf = decltype(buf_tag)::value;
     bool emask = false;
     if (need(w, j, &emask)) {
       const bf16_t* cK = sK[buf];
@@ -478,7 +481,11 @@ __global__ void __launch_bounds__(NW * 64, QN == 1 ? 8 / NW : 1) fwd_bf16_kernel
     __syncthreads();
     j = jn;
     jn = jnn;
-    buf ^= 1;
+  };
+  while (j < j_hi) {
+    tile(std::integral_constant<int, 0>{});
+    if (j >= j_hi) break;
+    tile(std::integral_constant<int, 1>{});
   }
 
   if (qw >= N) return;
