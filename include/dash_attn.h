@@ -214,9 +214,10 @@ dash_status dash_attn_bwd(const dash_attn_desc* desc, dash_schedule schedule, co
  * library's code object (allocated when the code object is loaded, held
  * until the process ends).  The call allocates nothing.
  *   Limits    the workspace dash_attn_bwd_workspace_size reports must fit
- *             the array (else DASH_ERR_WORKSPACE, before any launch; e.g.
- *             bf16 d = 128 fits up to about 14.6e6 query rows x heads,
- *             B*H*N <= 120k); full and causal masks only (a window or
+ *             the array (else DASH_ERR_WORKSPACE, before any launch; the
+ *             workspace holds about 4 d + 5 bytes per query row and head,
+ *             so bf16 d = 128 fits B*H*N up to about 129k, d = 64 up to
+ *             about 258k); full and causal masks only (a window or
  *             block mask gives DASH_ERR_UNSUPPORTED: their tables need
  *             host memory allocated on first use).
  *   Sharing   every call on a GPU uses that GPU's one array and leaves its
