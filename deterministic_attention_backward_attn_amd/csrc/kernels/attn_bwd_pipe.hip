@@ -26,9 +26,11 @@
 // computed with the same operands in the same order.
 //
 // The ordered add (explainer section 1, a fixed accumulation order for dQ)
-// keeps the other kernel's protocol: wave B of slice s owns dQ columns
-// [32s, 32s+32) in every workgroup and hands off to slice s of the next
-// contributor through the sub-tile's counter for s.  Its timing per period
+// keeps the other kernel's protocol: wave B of slice s owns one 32 x 32
+// block of the sub-tile's dQ (d = 128: columns [32s, 32s+32); d = 64: Q
+// rows [32 (s / 2), +32), columns [32 (s % 2), +32)) in every workgroup and
+// hands off to slice s of the next contributor through the sub-tile's
+// counter for s.  Its timing per period
 // (B processing sub-tile g):
 //   1. the counter value read one period earlier shows whether this
 //      contributor's turn has come; if it has not, the previous add is
